@@ -1,0 +1,77 @@
+"""ctypes declarations of the C ABI in include/cb.h.
+
+The shared library is built in-tree (``python -m csr_constrained_beam_amd.build``).
+There is no fallback: if it is missing, importing the package's API raises.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsrbeam.so")
+
+CB_OK, CB_EINVAL, CB_ENOMEM, CB_EHIP, CB_EUNSUPPORTED, CB_ECAPACITY = 0, -1, -2, -3, -4, -5
+CB_F32, CB_BF16 = 0, 1
+CB_PATH_AUTO, CB_PATH_DENSE, CB_PATH_SPARSE = 0, 1, 2
+CB_STORE_AUTO, CB_STORE_CSR, CB_STORE_BITMAP = 0, 1, 2
+
+STATUS_NAMES = {0: "CB_OK", -1: "CB_EINVAL", -2: "CB_ENOMEM", -3: "CB_EHIP", -4: "CB_EUNSUPPORTED",
+                -5: "CB_ECAPACITY"}
+
+# every symbol the header declares, with (restype, argtypes)
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+
+class StepInfo(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_int64), ("n_edges", ctypes.c_int64), ("max_fanout", ctypes.c_int32),
+                ("storage", ctypes.c_int32), ("bytes", ctypes.c_int64)]
+
+
+SIGNATURES = {
+    "cb_build_index": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _I32, _PP]),
+    "cb_index_shape": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "cb_index_info": (ctypes.c_int, [_P, _I32, ctypes.POINTER(StepInfo)]),
+    "cb_index_row": (ctypes.c_int, [_P, _I32, _I64, _P, _P, _I32, _P]),
+    "cb_free_index": (None, [_P]),
+    "cb_plan_create": (ctypes.c_int, [_P, _I32, _I32, _I32, ctypes.c_int, _PP]),
+    "cb_set_path": (ctypes.c_int, [_P, _I32, ctypes.c_int]),
+    "cb_get_path": (ctypes.c_int, [_P, _I32, _P]),
+    "cb_step": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "cb_decode": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "cb_tune": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P]),
+    "cb_tune_times": (ctypes.c_int, [_P, _I32, _P, _P]),
+    "cb_plan_destroy": (None, [_P]),
+    "cb_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class CbError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__("%s failed: %s: %s" % (fn, STATUS_NAMES.get(status, status), msg))
+        self.status = status
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libcsrbeam.so is not built; run `python -m csr_constrained_beam_amd.build` "
+                              "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def check(fn, status):
+    if status != CB_OK:
+        raise CbError(fn, status, lib().cb_last_error().decode(errors="replace"))

@@ -1,0 +1,192 @@
+"""Python binding of the C ABI: argument marshalling only.
+
+Every step of the decoding path runs in the HIP library; this module checks
+shapes and dtypes, passes raw device pointers and the current HIP stream, and
+allocates output tensors with PyTorch.
+"""
+
+import ctypes
+
+import numpy as np
+
+from . import _lib as C
+
+_PATHS = {"auto": C.CB_PATH_AUTO, "dense": C.CB_PATH_DENSE, "sparse": C.CB_PATH_SPARSE}
+_PATH_NAMES = {v: k for k, v in _PATHS.items()}
+_STORES = {"auto": C.CB_STORE_AUTO, "csr": C.CB_STORE_CSR, "bitmap": C.CB_STORE_BITMAP}
+_STORE_NAMES = {v: k for k, v in _STORES.items()}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+class Index:
+    """Step-sliced prefix index of a catalog, resident on ``device``.
+
+    sids: int array [n_items][L] with tokens in [0, V).  ``device=-1`` builds
+    host tables only (inspection, no stepping)."""
+
+    def __init__(self, sids, V, device=0, store="auto"):
+        sids = np.ascontiguousarray(sids, dtype=np.int32)
+        if sids.ndim != 2:
+            raise ValueError("sids must be a 2-D [n_items][L] array")
+        self._lib = C.lib()
+        h = ctypes.c_void_p()
+        C.check("cb_build_index", self._lib.cb_build_index(sids.ctypes.data, sids.shape[0], sids.shape[1], int(V),
+                                                            int(device), _STORES[store], ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.cb_free_index(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @property
+    def shape(self):
+        L, V, dev = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        n = ctypes.c_int64()
+        C.check("cb_index_shape", self._lib.cb_index_shape(self._h, ctypes.byref(L), ctypes.byref(V), ctypes.byref(n),
+                                                            ctypes.byref(dev)))
+        return {"L": L.value, "V": V.value, "n_items": n.value, "device": dev.value}
+
+    @property
+    def L(self):
+        return self.shape["L"]
+
+    def info(self, t):
+        si = C.StepInfo()
+        C.check("cb_index_info", self._lib.cb_index_info(self._h, int(t), ctypes.byref(si)))
+        return {"n_rows": si.n_rows, "n_edges": si.n_edges, "max_fanout": si.max_fanout,
+                "storage": _STORE_NAMES[si.storage], "bytes": si.bytes}
+
+    def row(self, t, r):
+        """(tokens, next_rows) of row r of step t, read back to the host."""
+        n = ctypes.c_int32()
+        C.check("cb_index_row", self._lib.cb_index_row(self._h, int(t), int(r), None, None, 0, ctypes.byref(n)))
+        tok = np.empty(n.value, np.int32)
+        nxt = np.empty(n.value, np.int64)
+        C.check("cb_index_row", self._lib.cb_index_row(self._h, int(t), int(r), tok.ctypes.data, nxt.ctypes.data,
+                                                        n.value, ctypes.byref(n)))
+        return tok, nxt
+
+    def plan(self, Q_max, K, d, dtype):
+        return Plan(self, Q_max, K, d, dtype)
+
+
+def _dtype_code(dtype):
+    torch = _torch()
+    if dtype in ("bf16", torch.bfloat16):
+        return C.CB_BF16, torch.bfloat16
+    if dtype in ("f32", torch.float32):
+        return C.CB_F32, torch.float32
+    raise ValueError("dtype must be 'f32' or 'bf16'")
+
+
+class Plan:
+    """Workspace and per-step path choice for up to Q_max queries of beam K."""
+
+    def __init__(self, index, Q_max, K, d, dtype):
+        self.index = index  # keeps the index alive
+        self._lib = index._lib
+        self.code, self.tdtype = _dtype_code(dtype)
+        self.Q_max, self.K, self.d = int(Q_max), int(K), int(d)
+        self.L = index.L
+        self.V = index.shape["V"]
+        self.device = index.shape["device"]
+        h = ctypes.c_void_p()
+        C.check("cb_plan_create", self._lib.cb_plan_create(index._h, self.Q_max, self.K, self.d, self.code,
+                                                            ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.cb_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def set_path(self, t, path):
+        C.check("cb_set_path", self._lib.cb_set_path(self._h, int(t), _PATHS[path]))
+
+    def get_path(self, t):
+        v = ctypes.c_int()
+        C.check("cb_get_path", self._lib.cb_get_path(self._h, int(t), ctypes.byref(v)))
+        return _PATH_NAMES[v.value]
+
+    def _stream(self):
+        torch = _torch()
+        return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+
+    def _check_tensor(self, name, x, dtype, shape):
+        torch = _torch()
+        if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.device.index != self.device:
+            raise ValueError("%s must be a tensor on cuda:%d" % (name, self.device))
+        if x.dtype != dtype or tuple(x.shape) != tuple(shape) or not x.is_contiguous():
+            raise ValueError("%s must be a contiguous %s tensor of shape %s (got %s %s)"
+                             % (name, dtype, tuple(shape), x.dtype, tuple(x.shape)))
+        return ctypes.c_void_p(x.data_ptr())
+
+    def step(self, t, hidden, W_t, rows, acc, out=None):
+        """One decoding step (cb_step).  Returns (tokens, parents, rows, logp)."""
+        torch = _torch()
+        R = rows.shape[0]
+        if R % self.K:
+            raise ValueError("rows length must be a multiple of K")
+        Q = R // self.K
+        ph = self._check_tensor("hidden", hidden, self.tdtype, (R, self.d))
+        pw = self._check_tensor("W_t", W_t, self.tdtype, (self.V, self.d))
+        pr = self._check_tensor("rows", rows, torch.int32, (R,))
+        pa = self._check_tensor("acc", acc, torch.float32, (R,))
+        if out is None:
+            dev = rows.device
+            out = (torch.empty(R, dtype=torch.int32, device=dev), torch.empty(R, dtype=torch.int32, device=dev),
+                   torch.empty(R, dtype=torch.int32, device=dev), torch.empty(R, dtype=torch.float32, device=dev))
+        ot, op, orow, ol = out
+        C.check("cb_step", self._lib.cb_step(self._h, int(t), Q, ph, pw, pr, pa, ctypes.c_void_p(ot.data_ptr()),
+                                             ctypes.c_void_p(op.data_ptr()), ctypes.c_void_p(orow.data_ptr()),
+                                             ctypes.c_void_p(ol.data_ptr()), self._stream()))
+        return out
+
+    def decode(self, q, P, W, trace=False):
+        """Full decode (cb_decode).  q [Q][d] f32, P [L-1][V][d] f32, W [L][V][d]."""
+        torch = _torch()
+        Q = q.shape[0]
+        R = Q * self.K
+        dev = q.device
+        pq = self._check_tensor("q", q, torch.float32, (Q, self.d))
+        pp = self._check_tensor("P", P, torch.float32, (self.L - 1, self.V, self.d)) if self.L > 1 else None
+        pw = self._check_tensor("W", W, self.tdtype, (self.L, self.V, self.d))
+        out = {"seqs": torch.empty((R, self.L), dtype=torch.int32, device=dev),
+               "logp": torch.empty(R, dtype=torch.float32, device=dev),
+               "rows": torch.empty(R, dtype=torch.int32, device=dev)}
+        tr = [None, None, None]
+        if trace:
+            out["trace_h"] = torch.empty((self.L, R, self.d), dtype=self.tdtype, device=dev)
+            out["trace_rows"] = torch.empty((self.L, R), dtype=torch.int32, device=dev)
+            out["trace_acc"] = torch.empty((self.L, R), dtype=torch.float32, device=dev)
+            tr = [ctypes.c_void_p(out[k].data_ptr()) for k in ("trace_h", "trace_rows", "trace_acc")]
+        C.check("cb_decode", self._lib.cb_decode(self._h, Q, pq, pp, pw, ctypes.c_void_p(out["seqs"].data_ptr()),
+                                                 ctypes.c_void_p(out["logp"].data_ptr()),
+                                                 ctypes.c_void_p(out["rows"].data_ptr()), *tr, self._stream()))
+        return out
+
+    def tune(self, q, P, W, reps=5):
+        """Pre-measured path switch (cb_tune); returns per-step timings."""
+        torch = _torch()
+        Q = q.shape[0]
+        pq = self._check_tensor("q", q, torch.float32, (Q, self.d))
+        pp = self._check_tensor("P", P, torch.float32, (self.L - 1, self.V, self.d)) if self.L > 1 else None
+        pw = self._check_tensor("W", W, self.tdtype, (self.L, self.V, self.d))
+        C.check("cb_tune", self._lib.cb_tune(self._h, Q, pq, pp, pw, int(reps), self._stream()))
+        res = []
+        for t in range(self.L):
+            dus, sus = ctypes.c_float(), ctypes.c_float()
+            C.check("cb_tune_times", self._lib.cb_tune_times(self._h, t, ctypes.byref(dus), ctypes.byref(sus)))
+            res.append({"t": t, "dense_us": dus.value, "sparse_us": sus.value, "path": self.get_path(t)})
+        return res

@@ -1,0 +1,577 @@
+// C-ABI entry points of the constrained beam-search library.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "cb_internal.h"
+
+namespace cb {
+
+namespace {
+thread_local std::string g_err;
+}
+
+void set_error(const std::string& msg) { g_err = msg; }
+void clear_error() { g_err.clear(); }
+
+size_t expand_lds_bytes(int S, int Kc, int d, bool dense);  // kernels.hip
+
+namespace {
+
+// Make `dev` current for the scope, restoring the caller's device after.
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev) {
+        if (dev < 0) return;  // host-only work: leave the runtime alone
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+cb_status hip_fail(const char* where, hipError_t e) {
+    set_error(std::string(where) + ": " + hipGetErrorString(e));
+    return CB_EHIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dtype_size(cb_dtype dt) { return dt == CB_BF16 ? 2 : 4; }
+
+template <class T>
+cb_status dev_alloc(T** p, size_t count, const char* what) {
+    *p = nullptr;
+    if (count == 0) return CB_OK;
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(p), count * sizeof(T));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        *p = nullptr;
+        set_error(std::string("device allocation failed: ") + what);
+        return CB_ENOMEM;
+    }
+    return CB_OK;
+}
+
+void dev_free(void* p) {
+    if (p) (void)hipFree(p);
+}
+
+bool dense_available(const cb_plan* p) { return p->dtype == CB_F32 || (p->d % 64) == 0; }
+
+int32_t resolve_path(const cb_plan* p, int t) {
+    int32_t f = p->forced[(size_t)t];
+    if (f == CB_PATH_DENSE || f == CB_PATH_SPARSE) return f;
+    int32_t tu = p->tuned[(size_t)t];
+    if (tu == CB_PATH_DENSE || tu == CB_PATH_SPARSE) return tu;
+    const cb::StepTable& T = p->idx->steps[(size_t)t];
+    return (T.store == CB_STORE_BITMAP && dense_available(p)) ? CB_PATH_DENSE : CB_PATH_SPARSE;
+}
+
+// Enqueue one step (no validation).
+cb_status run_step(cb_plan* p, int t, int Q, int32_t path, const void* hidden, const void* Wt, const int32_t* rows,
+                   const float* acc, int32_t* ot, int32_t* op, int32_t* orow, float* ol, hipStream_t s) {
+    const cb_index* idx = p->idx;
+    const cb::StepTable& T = idx->steps[(size_t)t];
+    const cb::StepDev sd = T.dev(idx->words);
+    const int R = Q * p->K;
+    const int Kc = std::min(p->K, std::max(T.S, 1));
+    hipError_t e;
+    if (path == CB_PATH_DENSE) {
+        e = launch_gemm_scores(p->dtype, R, idx->V, p->d, hidden, Wt, p->Z, s);
+        if (e != hipSuccess) return hip_fail("cb_step: full-codebook scores", e);
+        e = launch_beam_expand(sd, true, p->dtype, R, p->K, Kc, p->d, hidden, Wt, p->Z, idx->V, rows, acc, p->keys, s);
+    } else {
+        e = launch_beam_expand(sd, false, p->dtype, R, p->K, Kc, p->d, hidden, Wt, nullptr, 0, rows, acc, p->keys, s);
+    }
+    if (e != hipSuccess) return hip_fail("cb_step: beam expansion", e);
+    e = launch_query_merge(sd, Q, p->K, Kc, p->keys, rows, ot, op, orow, ol, s);
+    if (e != hipSuccess) return hip_fail("cb_step: query merge", e);
+    return CB_OK;
+}
+
+cb_status check_plan(const cb_plan* p, int32_t Q, const char* fn) {
+    if (!p) {
+        set_error(std::string(fn) + ": plan is NULL");
+        return CB_EINVAL;
+    }
+    if (Q < 0 || Q > p->Q_max) {
+        set_error(std::string(fn) + ": Q out of [0, Q_max]");
+        return CB_EINVAL;
+    }
+    if (p->idx->device < 0) {
+        set_error(std::string(fn) + ": index was built host-only (device -1)");
+        return CB_EINVAL;
+    }
+    return CB_OK;
+}
+
+}  // namespace
+}  // namespace cb
+
+using namespace cb;
+
+extern "C" {
+
+const char* cb_last_error(void) { return g_err.c_str(); }
+
+cb_status cb_build_index(const int32_t* sids, int64_t n_items, int32_t L, int32_t V, int32_t device, int32_t store,
+                         cb_index** out) {
+    clear_error();
+    if (!out) {
+        set_error("cb_build_index: out is NULL");
+        return CB_EINVAL;
+    }
+    *out = nullptr;
+    if (!sids || n_items < 1 || n_items >= (int64_t(1) << 31) || L < 1 || L > 64 || V < 2) {
+        set_error("cb_build_index: need sids != NULL, 1 <= n_items < 2^31, 1 <= L <= 64, V >= 2");
+        return CB_EINVAL;
+    }
+    if (V > 65535) {
+        set_error("cb_build_index: V > 65535 is not supported (tokens are stored as 16-bit)");
+        return CB_EUNSUPPORTED;
+    }
+    if (store < CB_STORE_AUTO || store > CB_STORE_BITMAP) {
+        set_error("cb_build_index: unknown storage policy");
+        return CB_EINVAL;
+    }
+    for (int64_t i = 0; i < n_items * L; ++i)
+        if (sids[i] < 0 || sids[i] >= V) {
+            set_error("cb_build_index: token out of [0, V) at item " + std::to_string(i / L));
+            return CB_EINVAL;
+        }
+    cb_index* idx = new (std::nothrow) cb_index();
+    if (!idx) {
+        set_error("cb_build_index: host allocation failed");
+        return CB_ENOMEM;
+    }
+    idx->device = device;
+    cb_status st = build_host_tables(sids, n_items, L, V, store, idx);
+    if (st != CB_OK) {
+        delete idx;
+        return st;
+    }
+    if (device >= 0) {
+        DeviceGuard g(device);
+        if (!g.ok) {
+            delete idx;
+            set_error("cb_build_index: cannot select device " + std::to_string(device));
+            return CB_EHIP;
+        }
+        for (auto& T : idx->steps) {
+            st = dev_alloc(&T.d_row_ptr, T.row_ptr.size(), "row_ptr");
+            if (st == CB_OK) st = dev_alloc(&T.d_tok, T.tok.size(), "tokens");
+            if (st == CB_OK) st = dev_alloc(&T.d_bits, T.bits.size(), "bitmap");
+            hipError_t e = hipSuccess;
+            if (st == CB_OK && T.d_row_ptr)
+                e = hipMemcpy(T.d_row_ptr, T.row_ptr.data(), T.row_ptr.size() * 4, hipMemcpyHostToDevice);
+            if (st == CB_OK && e == hipSuccess && T.d_tok)
+                e = hipMemcpy(T.d_tok, T.tok.data(), T.tok.size() * 2, hipMemcpyHostToDevice);
+            if (st == CB_OK && e == hipSuccess && T.d_bits)
+                e = hipMemcpy(T.d_bits, T.bits.data(), T.bits.size() * 4, hipMemcpyHostToDevice);
+            if (st == CB_OK && e != hipSuccess) st = hip_fail("cb_build_index: upload", e);
+            if (st != CB_OK) {
+                cb_free_index(idx);
+                return st;
+            }
+            std::vector<uint32_t>().swap(T.row_ptr);
+            std::vector<uint16_t>().swap(T.tok);
+            std::vector<uint32_t>().swap(T.bits);
+        }
+    }
+    *out = idx;
+    return CB_OK;
+}
+
+cb_status cb_index_shape(const cb_index* idx, int32_t* L, int32_t* V, int64_t* n_items, int32_t* device) {
+    clear_error();
+    if (!idx) {
+        set_error("cb_index_shape: index is NULL");
+        return CB_EINVAL;
+    }
+    if (L) *L = idx->L;
+    if (V) *V = idx->V;
+    if (n_items) *n_items = idx->n_items;
+    if (device) *device = idx->device;
+    return CB_OK;
+}
+
+cb_status cb_index_info(const cb_index* idx, int32_t t, cb_step_info* out) {
+    clear_error();
+    if (!idx || !out || t < 0 || t >= idx->L) {
+        set_error("cb_index_info: bad index, step or output");
+        return CB_EINVAL;
+    }
+    const auto& T = idx->steps[(size_t)t];
+    out->n_rows = T.n_rows;
+    out->n_edges = T.n_edges;
+    out->max_fanout = T.S;
+    out->storage = T.store;
+    out->bytes = T.bytes;
+    return CB_OK;
+}
+
+cb_status cb_index_row(const cb_index* idx, int32_t t, int64_t row, int32_t* tokens, int64_t* next_rows, int32_t cap,
+                       int32_t* n) {
+    clear_error();
+    if (!idx || !n || t < 0 || t >= idx->L) {
+        set_error("cb_index_row: bad index, step or output");
+        return CB_EINVAL;
+    }
+    const auto& T = idx->steps[(size_t)t];
+    if (row < 0 || row >= T.n_rows) {
+        set_error("cb_index_row: row out of range");
+        return CB_EINVAL;
+    }
+    uint32_t rp[2];
+    std::vector<uint16_t> tk;
+    std::vector<uint32_t> bits;
+    const bool host = !T.row_ptr.empty();
+    if (!host && idx->device < 0) {
+        set_error("cb_index_row: index holds no tables");
+        return CB_EINVAL;
+    }
+    DeviceGuard g(host ? -1 : idx->device);
+    if (host) {
+        rp[0] = T.row_ptr[(size_t)row];
+        rp[1] = T.row_ptr[(size_t)row + 1];
+    } else {
+        hipError_t e = hipMemcpy(rp, T.d_row_ptr + row, 8, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail("cb_index_row", e);
+    }
+    const uint32_t cnt = rp[1] - rp[0];
+    if (T.store == CB_STORE_CSR) {
+        tk.resize(cnt);
+        if (host) {
+            std::copy(T.tok.begin() + rp[0], T.tok.begin() + rp[1], tk.begin());
+        } else if (cnt) {
+            hipError_t e = hipMemcpy(tk.data(), T.d_tok + rp[0], cnt * 2, hipMemcpyDeviceToHost);
+            if (e != hipSuccess) return hip_fail("cb_index_row", e);
+        }
+    } else {
+        bits.resize((size_t)idx->words);
+        if (host) {
+            std::copy(T.bits.begin() + row * idx->words, T.bits.begin() + (row + 1) * idx->words, bits.begin());
+        } else {
+            hipError_t e = hipMemcpy(bits.data(), T.d_bits + row * idx->words, (size_t)idx->words * 4,
+                                     hipMemcpyDeviceToHost);
+            if (e != hipSuccess) return hip_fail("cb_index_row", e);
+        }
+        for (int w = 0; w < idx->words; ++w)
+            for (int b = 0; b < 32; ++b)
+                if (bits[(size_t)w] >> b & 1u) tk.push_back((uint16_t)(w * 32 + b));
+    }
+    *n = (int32_t)tk.size();
+    for (int32_t j = 0; j < (int32_t)tk.size() && j < cap; ++j) {
+        if (tokens) tokens[j] = tk[(size_t)j];
+        if (next_rows) next_rows[j] = (int64_t)rp[0] + j;
+    }
+    return CB_OK;
+}
+
+void cb_free_index(cb_index* idx) {
+    if (!idx) return;
+    if (idx->device >= 0) {
+        DeviceGuard g(idx->device);
+        for (auto& T : idx->steps) {
+            dev_free(T.d_row_ptr);
+            dev_free(T.d_tok);
+            dev_free(T.d_bits);
+        }
+    }
+    delete idx;
+}
+
+cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_dtype dtype, cb_plan** out) {
+    clear_error();
+    if (!out) {
+        set_error("cb_plan_create: out is NULL");
+        return CB_EINVAL;
+    }
+    *out = nullptr;
+    if (!idx || Q_max < 1 || K < 1 || d < 8 || (d % 8) != 0 || (dtype != CB_F32 && dtype != CB_BF16)) {
+        set_error("cb_plan_create: need an index, Q_max >= 1, K >= 1, d a positive multiple of 8, dtype F32/BF16");
+        return CB_EINVAL;
+    }
+    if (idx->device < 0) {
+        set_error("cb_plan_create: index was built host-only (device -1)");
+        return CB_EINVAL;
+    }
+    if (K > kMaxK) {
+        set_error("cb_plan_create: K > 1024 is not supported");
+        return CB_ECAPACITY;
+    }
+    int32_t Smax = 1;
+    for (const auto& T : idx->steps) Smax = std::max(Smax, T.S);
+    if (Smax > kMaxRowSlots) {
+        set_error("cb_plan_create: a step has a row wider than " + std::to_string(kMaxRowSlots) + " valid tokens");
+        return CB_ECAPACITY;
+    }
+    const int32_t Kc = std::min(K, Smax);
+    if ((int64_t)K * Kc > kMaxMergeKeys) {
+        set_error("cb_plan_create: K * min(K, widest row) exceeds the per-query merge capacity");
+        return CB_ECAPACITY;
+    }
+    if (expand_lds_bytes(Smax, Kc, d, false) > 65536) {
+        set_error("cb_plan_create: per-beam workspace exceeds 64 KiB of LDS");
+        return CB_ECAPACITY;
+    }
+    DeviceGuard g(idx->device);
+    if (!g.ok) {
+        set_error("cb_plan_create: cannot select the index's device");
+        return CB_EHIP;
+    }
+    cb_plan* p = new (std::nothrow) cb_plan();
+    if (!p) {
+        set_error("cb_plan_create: host allocation failed");
+        return CB_ENOMEM;
+    }
+    p->idx = idx;
+    p->Q_max = Q_max;
+    p->K = K;
+    p->d = d;
+    p->dtype = dtype;
+    p->Kc_max = Kc;
+    p->forced.assign((size_t)idx->L, CB_PATH_AUTO);
+    p->tuned.assign((size_t)idx->L, 0);
+    p->tune_dense_us.assign((size_t)idx->L, -1.f);
+    p->tune_sparse_us.assign((size_t)idx->L, -1.f);
+    const size_t R = (size_t)Q_max * K;
+    cb_status st = dev_alloc(&p->keys, R * Kc, "candidate keys");
+    if (st == CB_OK) st = dev_alloc(&p->Z, R * (size_t)idx->V, "full-codebook scores");
+    for (int i = 0; i < 2 && st == CB_OK; ++i) {
+        st = dev_alloc(&p->s[i], R * d, "state");
+        if (st == CB_OK) st = dev_alloc(&p->rows[i], R, "rows");
+        if (st == CB_OK) st = dev_alloc(&p->acc[i], R, "acc");
+    }
+    if (st == CB_OK) {
+        unsigned char* h = nullptr;
+        st = dev_alloc(&h, R * d * dtype_size(dtype), "hidden");
+        p->h = h;
+    }
+    if (st == CB_OK) st = dev_alloc(&p->hist_tok, R * idx->L, "token history");
+    if (st == CB_OK) st = dev_alloc(&p->hist_par, R * idx->L, "parent history");
+    if (st == CB_OK) st = dev_alloc(&p->scratch_rows, R, "scratch");
+    if (st == CB_OK) st = dev_alloc(&p->scratch_logp, R, "scratch");
+    if (st == CB_OK) st = dev_alloc(&p->scratch_tok, R, "scratch");
+    if (st == CB_OK) st = dev_alloc(&p->scratch_par, R, "scratch");
+    if (st != CB_OK) {
+        cb_plan_destroy(p);
+        return st;
+    }
+    *out = p;
+    return CB_OK;
+}
+
+cb_status cb_set_path(cb_plan* p, int32_t t, cb_path path) {
+    clear_error();
+    if (!p || t < 0 || t >= p->idx->L || path < CB_PATH_AUTO || path > CB_PATH_SPARSE) {
+        set_error("cb_set_path: bad plan, step or path");
+        return CB_EINVAL;
+    }
+    if (path == CB_PATH_DENSE && !dense_available(p)) {
+        set_error("cb_set_path: the dense path needs d to be a multiple of 64 for bf16");
+        return CB_EUNSUPPORTED;
+    }
+    p->forced[(size_t)t] = path;
+    return CB_OK;
+}
+
+cb_status cb_get_path(const cb_plan* p, int32_t t, cb_path* path) {
+    clear_error();
+    if (!p || !path || t < 0 || t >= p->idx->L) {
+        set_error("cb_get_path: bad plan, step or output");
+        return CB_EINVAL;
+    }
+    *path = (cb_path)resolve_path(p, t);
+    return CB_OK;
+}
+
+cb_status cb_step(cb_plan* p, int32_t t, int32_t Q, const void* hidden, const void* W_t, const int32_t* beam_rows,
+                  const float* acc_logp, int32_t* out_tokens, int32_t* out_parents, int32_t* out_rows,
+                  float* out_logp, void* stream) {
+    clear_error();
+    cb_status st = check_plan(p, Q, "cb_step");
+    if (st != CB_OK) return st;
+    if (t < 0 || t >= p->idx->L) {
+        set_error("cb_step: t out of [0, L)");
+        return CB_EINVAL;
+    }
+    if (Q == 0) return CB_OK;
+    const void* ptrs[] = {hidden, W_t, beam_rows, acc_logp, out_tokens, out_parents, out_rows, out_logp};
+    for (const void* x : ptrs)
+        if (!x || !aligned16(x)) {
+            set_error("cb_step: a device pointer is NULL or not 16-byte aligned");
+            return CB_EINVAL;
+        }
+    DeviceGuard g(p->idx->device);
+    return run_step(p, t, Q, resolve_path(p, t), hidden, W_t, beam_rows, acc_logp, out_tokens, out_parents, out_rows,
+                    out_logp, (hipStream_t)stream);
+}
+
+static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float* P, const void* W, int32_t* out_seqs,
+                             float* out_logp, int32_t* out_rows, void* tr_h, int32_t* tr_rows, float* tr_acc,
+                             hipStream_t s, int reps) {
+    const cb_index* idx = p->idx;
+    const int L = idx->L, K = p->K, d = p->d, V = idx->V;
+    const int R = Q * K;
+    const size_t es = dtype_size(p->dtype);
+    hipError_t e = launch_decode_init(Q, K, d, p->dtype, q, p->s[0], p->h, p->rows[0], p->acc[0], s);
+    if (e != hipSuccess) return hip_fail("cb_decode: init", e);
+    int cur = 0;
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    if (reps > 0) {
+        if ((e = hipEventCreate(&ev0)) != hipSuccess || (e = hipEventCreate(&ev1)) != hipSuccess)
+            return hip_fail("cb_tune: events", e);
+    }
+    cb_status st = CB_OK;
+    for (int t = 0; t < L && st == CB_OK; ++t) {
+        const void* Wt = static_cast<const unsigned char*>(W) + (size_t)t * V * d * es;
+        if (tr_h) {
+            e = hipMemcpyAsync(static_cast<unsigned char*>(tr_h) + (size_t)t * R * d * es, p->h, (size_t)R * d * es,
+                               hipMemcpyDeviceToDevice, s);
+            if (e == hipSuccess && tr_rows)
+                e = hipMemcpyAsync(tr_rows + (size_t)t * R, p->rows[cur], (size_t)R * 4, hipMemcpyDeviceToDevice, s);
+            if (e == hipSuccess && tr_acc)
+                e = hipMemcpyAsync(tr_acc + (size_t)t * R, p->acc[cur], (size_t)R * 4, hipMemcpyDeviceToDevice, s);
+            if (e != hipSuccess) {
+                st = hip_fail("cb_decode: trace copy", e);
+                break;
+            }
+        } else if (tr_rows || tr_acc) {
+            if (tr_rows) e = hipMemcpyAsync(tr_rows + (size_t)t * R, p->rows[cur], (size_t)R * 4, hipMemcpyDeviceToDevice, s);
+            if (e == hipSuccess && tr_acc)
+                e = hipMemcpyAsync(tr_acc + (size_t)t * R, p->acc[cur], (size_t)R * 4, hipMemcpyDeviceToDevice, s);
+            if (e != hipSuccess) {
+                st = hip_fail("cb_decode: trace copy", e);
+                break;
+            }
+        }
+        if (reps > 0 && p->forced[(size_t)t] == CB_PATH_AUTO) {
+            // time both paths on this step's inputs, outputs to scratch
+            float us[2] = {-1.f, -1.f};
+            const int32_t paths[2] = {CB_PATH_DENSE, CB_PATH_SPARSE};
+            for (int k = 0; k < 2 && st == CB_OK; ++k) {
+                if (paths[k] == CB_PATH_DENSE && !dense_available(p)) continue;
+                st = run_step(p, t, Q, paths[k], p->h, Wt, p->rows[cur], p->acc[cur], p->scratch_tok, p->scratch_par,
+                              p->scratch_rows, p->scratch_logp, s);
+                if (st != CB_OK) break;
+                (void)hipEventRecord(ev0, s);
+                for (int r = 0; r < reps && st == CB_OK; ++r)
+                    st = run_step(p, t, Q, paths[k], p->h, Wt, p->rows[cur], p->acc[cur], p->scratch_tok,
+                                  p->scratch_par, p->scratch_rows, p->scratch_logp, s);
+                (void)hipEventRecord(ev1, s);
+                if ((e = hipEventSynchronize(ev1)) != hipSuccess) {
+                    st = hip_fail("cb_tune: synchronise", e);
+                    break;
+                }
+                float ms = 0.f;
+                (void)hipEventElapsedTime(&ms, ev0, ev1);
+                us[k] = ms * 1000.f / (float)reps;
+            }
+            if (st != CB_OK) break;
+            p->tune_dense_us[(size_t)t] = us[0];
+            p->tune_sparse_us[(size_t)t] = us[1];
+            p->tuned[(size_t)t] = (us[0] >= 0.f && us[0] < us[1]) ? CB_PATH_DENSE : CB_PATH_SPARSE;
+        }
+        st = run_step(p, t, Q, resolve_path(p, t), p->h, Wt, p->rows[cur], p->acc[cur], p->hist_tok + (size_t)t * R,
+                      p->hist_par + (size_t)t * R, p->rows[1 - cur], p->acc[1 - cur], s);
+        if (st != CB_OK) break;
+        if (t + 1 < L) {
+            e = launch_hidden_update(R, K, d, p->dtype, p->s[cur], P + (size_t)t * V * d, p->hist_tok + (size_t)t * R,
+                                     p->hist_par + (size_t)t * R, p->s[1 - cur], p->h, s);
+            if (e != hipSuccess) st = hip_fail("cb_decode: hidden update", e);
+        }
+        cur = 1 - cur;
+    }
+    if (ev0) (void)hipEventDestroy(ev0);
+    if (ev1) (void)hipEventDestroy(ev1);
+    if (st != CB_OK) return st;
+    if (out_seqs) {
+        e = launch_backtrace(R, K, L, p->hist_tok, p->hist_par, out_seqs, s);
+        if (e != hipSuccess) return hip_fail("cb_decode: backtrace", e);
+    }
+    if (out_rows && (e = hipMemcpyAsync(out_rows, p->rows[cur], (size_t)R * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return hip_fail("cb_decode: output copy", e);
+    if (out_logp && (e = hipMemcpyAsync(out_logp, p->acc[cur], (size_t)R * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return hip_fail("cb_decode: output copy", e);
+    return CB_OK;
+}
+
+cb_status cb_decode(cb_plan* p, int32_t Q, const float* q, const float* P, const void* W, int32_t* out_seqs,
+                    float* out_logp, int32_t* out_rows, void* trace_hidden, int32_t* trace_rows, float* trace_acc,
+                    void* stream) {
+    clear_error();
+    cb_status st = check_plan(p, Q, "cb_decode");
+    if (st != CB_OK) return st;
+    if (Q == 0) return CB_OK;
+    if (!q || !W || (p->idx->L > 1 && !P) || !out_seqs || !out_logp || !out_rows) {
+        set_error("cb_decode: q, W, out_* (and P when L > 1) must be device pointers");
+        return CB_EINVAL;
+    }
+    const void* ptrs[] = {q, P, W, out_seqs, out_logp, out_rows, trace_hidden, trace_rows, trace_acc};
+    for (const void* x : ptrs)
+        if (x && !aligned16(x)) {
+            set_error("cb_decode: a device pointer is not 16-byte aligned");
+            return CB_EINVAL;
+        }
+    DeviceGuard g(p->idx->device);
+    return decode_impl(p, Q, q, P, W, out_seqs, out_logp, out_rows, trace_hidden, trace_rows, trace_acc,
+                       (hipStream_t)stream, 0);
+}
+
+cb_status cb_tune(cb_plan* p, int32_t Q, const float* q, const float* P, const void* W, int32_t reps, void* stream) {
+    clear_error();
+    cb_status st = check_plan(p, Q, "cb_tune");
+    if (st != CB_OK) return st;
+    if (!q || !W || (p->idx->L > 1 && !P) || reps < 1 || Q < 1) {
+        set_error("cb_tune: need q, W, P (L > 1), Q >= 1 and reps >= 1");
+        return CB_EINVAL;
+    }
+    DeviceGuard g(p->idx->device);
+    st = decode_impl(p, Q, q, P, W, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, (hipStream_t)stream, reps);
+    if (st != CB_OK) return st;
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail("cb_tune: synchronise", e);
+    return CB_OK;
+}
+
+cb_status cb_tune_times(const cb_plan* p, int32_t t, float* dense_us, float* sparse_us) {
+    clear_error();
+    if (!p || t < 0 || t >= p->idx->L) {
+        set_error("cb_tune_times: bad plan or step");
+        return CB_EINVAL;
+    }
+    if (dense_us) *dense_us = p->tune_dense_us[(size_t)t];
+    if (sparse_us) *sparse_us = p->tune_sparse_us[(size_t)t];
+    return CB_OK;
+}
+
+void cb_plan_destroy(cb_plan* p) {
+    if (!p) return;
+    DeviceGuard g(p->idx->device);
+    dev_free(p->keys);
+    dev_free(p->Z);
+    for (int i = 0; i < 2; ++i) {
+        dev_free(p->s[i]);
+        dev_free(p->rows[i]);
+        dev_free(p->acc[i]);
+    }
+    dev_free(p->h);
+    dev_free(p->hist_tok);
+    dev_free(p->hist_par);
+    dev_free(p->scratch_rows);
+    dev_free(p->scratch_logp);
+    dev_free(p->scratch_tok);
+    dev_free(p->scratch_par);
+    delete p;
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Internal types of the constrained beam-search library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "cb.h"
+
+namespace cb {
+
+// Thread-local error message behind cb_last_error().
+void set_error(const std::string& msg);
+void clear_error();
+
+// Device view of one step table.  Rows are the distinct length-t prefixes in
+// lexicographic order; row r's edges are row_ptr[r] .. row_ptr[r+1]-1, ascending
+// token, and edge e leads to row e of the next step.
+struct StepDev {
+    const uint32_t* row_ptr;  // [n_rows + 1]
+    const uint16_t* tok;      // CSR: token of every edge [n_edges]; nullptr for bitmap steps
+    const uint32_t* bits;     // bitmap: [n_rows][words], bit v of a row set iff token v is valid
+    int64_t n_rows;
+    int32_t words;            // 32-bit words per bitmap row = ceil(V / 32)
+    int32_t store;            // CB_STORE_CSR or CB_STORE_BITMAP
+    int32_t S;                // widest row (fixed slot count of the step)
+};
+
+struct StepTable {
+    int64_t n_rows = 0, n_edges = 0;
+    int32_t S = 0;
+    int32_t store = CB_STORE_CSR;
+    int64_t bytes = 0;
+    // host copies (kept for host-only indexes; released after upload otherwise)
+    std::vector<uint32_t> row_ptr;
+    std::vector<uint16_t> tok;
+    std::vector<uint32_t> bits;
+    // device copies
+    uint32_t* d_row_ptr = nullptr;
+    uint16_t* d_tok = nullptr;
+    uint32_t* d_bits = nullptr;
+
+    StepDev dev(int32_t words) const {
+        return StepDev{d_row_ptr, d_tok, d_bits, n_rows, words, store, S};
+    }
+};
+
+}  // namespace cb
+
+struct cb_index {
+    int32_t L = 0, V = 0, device = -1, words = 0;
+    int64_t n_items = 0;
+    std::vector<cb::StepTable> steps;
+};
+
+// Limits of the kernels in this build.
+namespace cb {
+constexpr int kMaxK = 1024;          // parent slot fits the 10-bit key field
+constexpr int kMaxRowSlots = 4096;   // widest row one workgroup holds in LDS
+constexpr int kMaxMergeKeys = 8192;  // K * min(K, S_t) keys merged in LDS per query
+}
+
+struct cb_plan {
+    cb_index* idx = nullptr;
+    int32_t Q_max = 0, K = 0, d = 0;
+    cb_dtype dtype = CB_F32;
+    int32_t Kc_max = 0;           // per-beam survivors kept: min(K, widest step)
+    std::vector<int32_t> forced;  // per step: CB_PATH_* set by the caller
+    std::vector<int32_t> tuned;   // per step: measured choice (0 = none)
+    std::vector<float> tune_dense_us, tune_sparse_us;
+    // workspace (allocated once)
+    uint64_t* keys = nullptr;     // [Q_max*K][Kc_max] per-beam survivors
+    float* Z = nullptr;           // [Q_max*K][V] full-codebook scores (dense path)
+    // decode state
+    float* s[2] = {nullptr, nullptr};    // [R][d] float32 state vectors
+    void* h = nullptr;                    // [R][d] dtype hidden vectors
+    int32_t* rows[2] = {nullptr, nullptr};
+    float* acc[2] = {nullptr, nullptr};
+    int32_t* hist_tok = nullptr;          // [L][R]
+    int32_t* hist_par = nullptr;          // [L][R]
+    int32_t* scratch_rows = nullptr;      // [R] (tuning)
+    float* scratch_logp = nullptr;        // [R]
+    int32_t* scratch_tok = nullptr;       // [R]
+    int32_t* scratch_par = nullptr;       // [R]
+};
+
+namespace cb {
+
+// Kernel launchers (kernels.hip).  All enqueue on `stream`; return hipError_t of the launch.
+hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R, int K, int Kc, int d,
+                              const void* hidden, const void* W, const float* Z, int64_t ldz,
+                              const int32_t* beam_rows, const float* acc, uint64_t* keys, hipStream_t s);
+hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uint64_t* keys,
+                              const int32_t* beam_rows, int32_t* tok, int32_t* par, int32_t* rows, float* logp,
+                              hipStream_t s);
+hipError_t launch_gemm_scores(cb_dtype dt, int R, int V, int d, const void* H, const void* W, float* Z,
+                              hipStream_t s);
+hipError_t launch_decode_init(int Q, int K, int d, cb_dtype dt, const float* q, float* s_out, void* h_out,
+                              int32_t* rows, float* acc, hipStream_t st);
+hipError_t launch_hidden_update(int R, int K, int d, cb_dtype dt, const float* s_old, const float* P_t,
+                                const int32_t* tok, const int32_t* par, float* s_new, void* h_out,
+                                hipStream_t st);
+hipError_t launch_backtrace(int R, int K, int L, const int32_t* hist_tok, const int32_t* hist_par,
+                            int32_t* seqs, hipStream_t s);
+
+// Index construction (index_build.cpp).
+cb_status build_host_tables(const int32_t* sids, int64_t n_items, int32_t L, int32_t V, int32_t store,
+                            cb_index* idx);
+
+}  // namespace cb

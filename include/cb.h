@@ -1,0 +1,193 @@
+/*
+ * cb.h - C ABI of the catalog-constrained beam-search library for AMD MI355X
+ * (gfx950).
+ *
+ * One decoding step of beam search over a catalog of Semantic-ID token
+ * sequences, filter first:
+ *   (1) a per-step sliced prefix index gives every beam its valid next tokens
+ *       and the row each extension maps to in the next step's table
+ *       (ZeroGR summary, "Why slice the index by decoding step?");
+ *   (2) only those tokens are scored against the beam's hidden vector, or the
+ *       whole codebook is scored and the valid columns picked out, the choice
+ *       made per step by a measurement taken in advance (ZeroGR summary, "Why
+ *       fewer scores are not automatically faster");
+ *   (3) log-softmax over the valid tokens only, added to the beam's
+ *       accumulated log-probability (ZeroGR summary, "The pipeline", stage 4);
+ *   (4) the K best candidates of each query become its next beams, each
+ *       carrying its next-step row (same passage; STATIC sec. 4.3 BeamSearch and
+ *       Gather).
+ *
+ * Conventions used by every entry point
+ *   - Steps are numbered t = 0 .. L-1; step t extends prefixes of length t.
+ *   - "Row" r of step t is the r-th smallest distinct length-t prefix of the
+ *     catalog in lexicographic order (row 0 of step 0 is the empty prefix).
+ *     The rows of step t+1 are the edges of step t in order, so an edge's
+ *     position is its next row (ZeroGR: in sparse tables a token's position is
+ *     its next-step row).  At the last step the next row is the item's rank in
+ *     the sorted, duplicate-free catalog.
+ *   - A query owns K consecutive beam slots; slot b = q*K + k.  A dead slot
+ *     has row -1 and accumulated log-prob -inf.  At t = 0 the caller passes
+ *     row 0 and 0.0 in slot k = 0 of each query and dead slots elsewhere.
+ *   - Outputs of a step are, per query, the K best candidates best first by
+ *     (new log-prob descending, parent slot ascending, token ascending);
+ *     fewer than K valid candidates leave sentinel slots (token = parent =
+ *     row = -1, log-prob = -inf).  `parent` is the slot k (0..K-1) within
+ *     the same query.
+ *   - Device pointers are HIP device addresses; `stream` is a hipStream_t
+ *     (NULL = the default stream).  Calls on a stream are asynchronous and
+ *     stream ordered; errors detected on the host are returned before any
+ *     launch, device faults surface at the caller's next synchronisation.
+ *   - Every function returns a cb_status; on failure cb_last_error() gives a
+ *     message (thread local, valid until the next call on that thread).
+ *   - Floating point: scores accumulate in float32 (bf16 x bf16 products are
+ *     exact in float32); the softmax and the accumulated log-prob are float32.
+ */
+#ifndef CB_H
+#define CB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CB_OK = 0,
+    CB_EINVAL = -1,        /* an argument is out of range, misaligned or inconsistent */
+    CB_ENOMEM = -2,        /* host or device allocation failed */
+    CB_EHIP = -3,          /* a HIP runtime call failed */
+    CB_EUNSUPPORTED = -4,  /* a shape this build does not handle (e.g. V > 65535) */
+    CB_ECAPACITY = -5      /* beam width or step width beyond what the kernels hold */
+} cb_status;
+
+typedef enum { CB_F32 = 0, CB_BF16 = 1 } cb_dtype;
+
+/* Scoring path of a step: full-codebook MFMA product then a gather of the
+ * valid columns (DENSE), or a gather-dot over the valid tokens only (SPARSE).
+ * AUTO uses the measured choice of cb_tune, else a width rule. */
+typedef enum { CB_PATH_AUTO = 0, CB_PATH_DENSE = 1, CB_PATH_SPARSE = 2 } cb_path;
+
+/* Storage of a step table: CSR (row_ptr + tokens) for narrow steps, a per-row
+ * bitmap (+ row_ptr) for wide steps (ZeroGR: dense tables where many tokens
+ * are valid, sparse ones where few are; STATIC sec. 5.1 / App. B: dense masks
+ * for the first levels, CSR below).  AUTO picks the smaller of the two. */
+typedef enum { CB_STORE_AUTO = 0, CB_STORE_CSR = 1, CB_STORE_BITMAP = 2 } cb_store;
+
+typedef struct cb_index cb_index; /* owns the device-resident step tables */
+typedef struct cb_plan cb_plan;   /* owns the workspace for (Q_max, K, d, dtype) and the per-step path */
+
+typedef struct {
+    int64_t n_rows;      /* distinct length-t prefixes */
+    int64_t n_edges;     /* distinct length-(t+1) prefixes (= rows of step t+1) */
+    int32_t max_fanout;  /* the widest row: fixed slot count of the step (ZeroGR, fixed candidate slots) */
+    int32_t storage;     /* CB_STORE_CSR or CB_STORE_BITMAP */
+    int64_t bytes;       /* device bytes of this step's table */
+} cb_step_info;
+
+/* Build the step-sliced index of a catalog and upload it to `device`.
+ *   sids      host int32 [n_items][L], row-major; tokens in [0, V).  Read only
+ *             during the call.  Repeated items are removed (the catalog is a
+ *             set: STATIC sec. 4.1).
+ *   L >= 1, 2 <= V <= 65535, 1 <= n_items < 2^31.
+ *   device    HIP device ordinal, or -1 to build host tables only (for
+ *             inspection with cb_index_info / cb_index_row; such an index
+ *             cannot be stepped).
+ *   store     a cb_store policy applied to every step (AUTO per step).
+ *   *out      receives the index; release with cb_free_index.
+ * Errors: CB_EINVAL (shape, token out of range), CB_EUNSUPPORTED, CB_ENOMEM,
+ * CB_EHIP.  Synchronous. */
+cb_status cb_build_index(const int32_t* sids, int64_t n_items, int32_t L, int32_t V,
+                         int32_t device, int32_t store, cb_index** out);
+
+/* Shape of an index: L, V, distinct items and device (-1 = host only).
+ * Any output pointer may be NULL. */
+cb_status cb_index_shape(const cb_index* idx, int32_t* L, int32_t* V, int64_t* n_items, int32_t* device);
+
+/* Per-step statistics of the table of step t (0 <= t < L). */
+cb_status cb_index_info(const cb_index* idx, int32_t t, cb_step_info* out);
+
+/* Host-side lookup of one row: its valid tokens (ascending) and their next
+ * rows.  Writes at most `cap` entries to tokens / next_rows (either may be
+ * NULL) and the row's full count to *n.  Synchronous (reads device tables
+ * back when the host copy was released). */
+cb_status cb_index_row(const cb_index* idx, int32_t t, int64_t row,
+                       int32_t* tokens, int64_t* next_rows, int32_t cap, int32_t* n);
+
+/* Release an index (frees device tables).  NULL is ignored.  Plans created
+ * from it must be destroyed first. */
+void cb_free_index(cb_index* idx);
+
+/* Create a plan: allocates, once, every device buffer the step and decode
+ * need for up to Q_max queries of beam width K, hidden width d (multiple of 8)
+ * and element type dtype (of W and of the hidden vectors).  Nothing is
+ * allocated later by cb_step / cb_decode (FlashTrie App. D: per-batch state
+ * allocated once).  The index must stay alive while the plan exists.
+ * Errors: CB_EINVAL, CB_ECAPACITY (K > 1024 or a step too wide for the
+ * per-beam selection), CB_ENOMEM, CB_EHIP. */
+cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_dtype dtype, cb_plan** out);
+
+/* Force the scoring path of step t (tests run both ways).  CB_PATH_AUTO
+ * restores the measured or default choice. */
+cb_status cb_set_path(cb_plan* plan, int32_t t, cb_path path);
+
+/* The path step t will take (never CB_PATH_AUTO). */
+cb_status cb_get_path(const cb_plan* plan, int32_t t, cb_path* path);
+
+/* One decoding step (the hot path) for Q <= Q_max queries at step t.
+ *   hidden     device [Q*K][d] of dtype: each slot's hidden vector (ignored
+ *              for dead slots).  bf16 plans take the vectors already rounded.
+ *   W_t        device [V][d] of dtype: output layer of step t, row-major.
+ *   beam_rows  device int32 [Q*K]: row of each slot in step t's table, -1 dead
+ *              (a row outside the table is treated as dead).
+ *   acc_logp   device float [Q*K]: accumulated log-prob, -inf dead.
+ *   out_*      device [Q*K]: tokens, parent slots, next rows, new accumulated
+ *              log-probs, best first per query, sentinel padded.  Must not
+ *              alias the inputs.
+ * All device pointers 16-byte aligned.  Enqueued on `stream`; returns after
+ * the launches.  Concurrent calls on one plan from different streams race.
+ * Errors: CB_EINVAL (t, Q, pointers, host-only index), CB_EHIP. */
+cb_status cb_step(cb_plan* plan, int32_t t, int32_t Q, const void* hidden, const void* W_t,
+                  const int32_t* beam_rows, const float* acc_logp,
+                  int32_t* out_tokens, int32_t* out_parents, int32_t* out_rows, float* out_logp,
+                  void* stream);
+
+/* Full decode of all L steps with the stand-in model whose hidden vector
+ * before step t is h = s / ||s||_2, s = q + sum_{j<t} P_j[token_j] (s in
+ * float32; norm and division in double; rounded to float32 and then to bf16
+ * for bf16 plans).  The hidden update runs between steps on the device.
+ *   q     device float [Q][d];  P  device float [L-1][V][d] (may be NULL when
+ *         L == 1);  W  device [L][V][d] of dtype.
+ *   out_seqs  device int32 [Q*K][L] (-1 rows for dead slots);
+ *   out_logp  device float [Q*K];  out_rows device int32 [Q*K] (item rank).
+ *   trace_hidden / trace_rows / trace_acc: optional (NULL) device buffers
+ *   [L][Q*K][d] dtype, [L][Q*K] int32, [L][Q*K] float receiving the inputs
+ *   of every step.
+ * Enqueued on `stream`; nothing is allocated.  Errors as cb_step. */
+cb_status cb_decode(cb_plan* plan, int32_t Q, const float* q, const float* P, const void* W,
+                    int32_t* out_seqs, float* out_logp, int32_t* out_rows,
+                    void* trace_hidden, int32_t* trace_rows, float* trace_acc, void* stream);
+
+/* Pre-measured path switch (ZeroGR: warm-up requests try every option per
+ * step and keep the fastest).  Runs one warm-up decode on the given inputs;
+ * at every step whose path is AUTO it times the dense and the sparse path
+ * (`reps` launches each, HIP events) and records the faster; the decode then
+ * continues on the recorded path.  Synchronises `stream`.  Arguments as
+ * cb_decode. */
+cb_status cb_tune(cb_plan* plan, int32_t Q, const float* q, const float* P, const void* W,
+                  int32_t reps, void* stream);
+
+/* Measured mean time (microseconds) of each path at step t from the last
+ * cb_tune (negative when not measured). */
+cb_status cb_tune_times(const cb_plan* plan, int32_t t, float* dense_us, float* sparse_us);
+
+/* Release a plan and its workspace.  NULL is ignored. */
+void cb_plan_destroy(cb_plan* plan);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char* cb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CB_H */

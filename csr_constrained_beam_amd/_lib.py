@@ -30,6 +30,13 @@ class StepInfo(ctypes.Structure):
                 ("storage", ctypes.c_int32), ("bytes", ctypes.c_int64)]
 
 
+class KernelTime(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int32), ("kernel", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("blocks", ctypes.c_int32), ("us", ctypes.c_float)]
+
+
+KERNEL_NAMES = {0: "gemm_bf16", 1: "gemm_f32", 2: "expand_sparse", 3: "expand_dense", 4: "merge"}
+
 SIGNATURES = {
     "cb_build_index": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _I32, _PP]),
     "cb_index_shape": (ctypes.c_int, [_P, _P, _P, _P, _P]),
@@ -43,6 +50,8 @@ SIGNATURES = {
     "cb_decode": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "cb_tune": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P]),
     "cb_tune_times": (ctypes.c_int, [_P, _I32, _P, _P]),
+    "cb_profile_start": (ctypes.c_int, [_P, _I32]),
+    "cb_profile_stop": (ctypes.c_int, [_P, _P, _I32, _P]),
     "cb_plan_destroy": (None, [_P]),
     "cb_last_error": (ctypes.c_char_p, []),
 }

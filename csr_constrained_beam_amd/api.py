@@ -190,3 +190,17 @@ class Plan:
             C.check("cb_tune_times", self._lib.cb_tune_times(self._h, t, ctypes.byref(dus), ctypes.byref(sus)))
             res.append({"t": t, "dense_us": dus.value, "sparse_us": sus.value, "path": self.get_path(t)})
         return res
+
+    def profile_start(self, capacity=4096):
+        """Record HIP events around every kernel launch from now on."""
+        C.check("cb_profile_start", self._lib.cb_profile_start(self._h, int(capacity)))
+        self._prof_cap = int(capacity)
+
+    def profile_stop(self):
+        """Stop recording; returns one dict per recorded launch."""
+        cap = getattr(self, "_prof_cap", 0)
+        buf = (C.KernelTime * max(cap, 1))()
+        n = ctypes.c_int32()
+        C.check("cb_profile_stop", self._lib.cb_profile_stop(self._h, buf, cap, ctypes.byref(n)))
+        return [{"step": r.step, "kernel": C.KERNEL_NAMES[r.kernel], "threads": r.threads, "blocks": r.blocks,
+                 "us": r.us} for r in buf[:min(n.value, cap)]]

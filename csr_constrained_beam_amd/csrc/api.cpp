@@ -75,6 +75,22 @@ int32_t resolve_path(const cb_plan* p, int t) {
     return (T.store == CB_STORE_BITMAP && dense_available(p)) ? CB_PATH_DENSE : CB_PATH_SPARSE;
 }
 
+// Records an event pair around a launch while profiling is on.
+struct ProfMark {
+    cb_plan* p;
+    hipStream_t s;
+    int idx = -1;
+    ProfMark(cb_plan* p_, hipStream_t s_, int t, int kernel, int threads, int blocks) : p(p_), s(s_) {
+        if (!p->prof_on || (int)p->prof_rec.size() >= p->prof_cap) return;
+        idx = (int)p->prof_rec.size();
+        p->prof_rec.push_back(cb_kernel_time{t, kernel, threads, blocks, 0.f});
+        (void)hipEventRecord(p->prof_ev[(size_t)idx * 2], s);
+    }
+    void done() {
+        if (idx >= 0) (void)hipEventRecord(p->prof_ev[(size_t)idx * 2 + 1], s);
+    }
+};
+
 // Enqueue one step (no validation).
 cb_status run_step(cb_plan* p, int t, int Q, int32_t path, const void* hidden, const void* Wt, const int32_t* rows,
                    const float* acc, int32_t* ot, int32_t* op, int32_t* orow, float* ol, hipStream_t s) {
@@ -84,17 +100,37 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, const void* hidden, c
     const int R = Q * p->K;
     const int Kc = std::min(p->K, std::max(T.S, 1));
     hipError_t e;
+    const int ent = expand_threads(sd);
     if (path == CB_PATH_DENSE) {
+        const bool bf = p->dtype == CB_BF16;
+        const int gblocks = bf ? ((idx->V + 127) / 128) * ((R + 127) / 128) : ((idx->V + 15) / 16) * ((R + 15) / 16);
+        ProfMark m0(p, s, t, bf ? CB_KERNEL_GEMM_BF16 : CB_KERNEL_GEMM_F32, 256, gblocks);
         e = launch_gemm_scores(p->dtype, R, idx->V, p->d, hidden, Wt, p->Z, s);
+        m0.done();
         if (e != hipSuccess) return hip_fail("cb_step: full-codebook scores", e);
+        ProfMark m1(p, s, t, CB_KERNEL_EXPAND_DENSE, ent, R);
         e = launch_beam_expand(sd, true, p->dtype, R, p->K, Kc, p->d, hidden, Wt, p->Z, idx->V, rows, acc, p->keys, s);
+        m1.done();
     } else {
+        ProfMark m1(p, s, t, CB_KERNEL_EXPAND_SPARSE, ent, R);
         e = launch_beam_expand(sd, false, p->dtype, R, p->K, Kc, p->d, hidden, Wt, nullptr, 0, rows, acc, p->keys, s);
+        m1.done();
     }
     if (e != hipSuccess) return hip_fail("cb_step: beam expansion", e);
+    ProfMark m2(p, s, t, CB_KERNEL_MERGE, kMergeThreads, Q);
     e = launch_query_merge(sd, Q, p->K, Kc, p->keys, rows, ot, op, orow, ol, s);
+    m2.done();
     if (e != hipSuccess) return hip_fail("cb_step: query merge", e);
     return CB_OK;
+}
+
+void profile_release(cb_plan* p) {
+    for (hipEvent_t ev : p->prof_ev)
+        if (ev) (void)hipEventDestroy(ev);
+    p->prof_ev.clear();
+    p->prof_rec.clear();
+    p->prof_on = false;
+    p->prof_cap = 0;
 }
 
 cb_status check_plan(const cb_plan* p, int32_t Q, const char* fn) {
@@ -554,9 +590,57 @@ cb_status cb_tune_times(const cb_plan* p, int32_t t, float* dense_us, float* spa
     return CB_OK;
 }
 
+cb_status cb_profile_start(cb_plan* p, int32_t capacity) {
+    clear_error();
+    if (!p || capacity < 1 || p->idx->device < 0) {
+        set_error("cb_profile_start: need a device plan and capacity >= 1");
+        return CB_EINVAL;
+    }
+    DeviceGuard g(p->idx->device);
+    profile_release(p);
+    p->prof_ev.assign((size_t)capacity * 2, nullptr);
+    for (auto& ev : p->prof_ev) {
+        hipError_t e = hipEventCreate(&ev);
+        if (e != hipSuccess) {
+            profile_release(p);
+            return hip_fail("cb_profile_start: events", e);
+        }
+    }
+    p->prof_rec.reserve((size_t)capacity);
+    p->prof_cap = capacity;
+    p->prof_on = true;
+    return CB_OK;
+}
+
+cb_status cb_profile_stop(cb_plan* p, cb_kernel_time* out, int32_t cap, int32_t* n) {
+    clear_error();
+    if (!p || !n) {
+        set_error("cb_profile_stop: bad plan or output");
+        return CB_EINVAL;
+    }
+    DeviceGuard g(p->idx->device);
+    cb_status st = CB_OK;
+    for (size_t i = 0; i < p->prof_rec.size(); ++i) {
+        hipError_t e = hipEventSynchronize(p->prof_ev[i * 2 + 1]);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, p->prof_ev[i * 2], p->prof_ev[i * 2 + 1]);
+        if (e != hipSuccess) {
+            st = hip_fail("cb_profile_stop", e);
+            break;
+        }
+        p->prof_rec[i].us = ms * 1000.f;
+    }
+    *n = (int32_t)p->prof_rec.size();
+    if (out)
+        for (int32_t i = 0; i < *n && i < cap; ++i) out[i] = p->prof_rec[(size_t)i];
+    profile_release(p);
+    return st;
+}
+
 void cb_plan_destroy(cb_plan* p) {
     if (!p) return;
     DeviceGuard g(p->idx->device);
+    profile_release(p);
     dev_free(p->keys);
     dev_free(p->Z);
     for (int i = 0; i < 2; ++i) {

@@ -84,11 +84,20 @@ struct cb_plan {
     float* scratch_logp = nullptr;        // [R]
     int32_t* scratch_tok = nullptr;       // [R]
     int32_t* scratch_par = nullptr;       // [R]
+    // kernel timing (cb_profile_start / cb_profile_stop)
+    bool prof_on = false;
+    int32_t prof_cap = 0;
+    std::vector<hipEvent_t> prof_ev;      // 2 per record
+    std::vector<cb_kernel_time> prof_rec;
 };
 
 namespace cb {
 
 // Kernel launchers (kernels.hip).  All enqueue on `stream`; return hipError_t of the launch.
+// Workgroup size the step kernels use for a table.
+int expand_threads(const StepDev& st);
+constexpr int kMergeThreads = 256;
+
 hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R, int K, int Kc, int d,
                               const void* hidden, const void* W, const float* Z, int64_t ldz,
                               const int32_t* beam_rows, const float* acc, uint64_t* keys, hipStream_t s);

@@ -507,12 +507,14 @@ __global__ void k_backtrace(int R, int K, int L, const int32_t* __restrict__ his
 
 }  // namespace
 
+int expand_threads(const StepDev& st) { return (st.S <= 8 && st.store == CB_STORE_CSR) ? 64 : 256; }
+
 hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R, int K, int Kc, int d,
                               const void* hidden, const void* W, const float* Z, int64_t ldz,
                               const int32_t* beam_rows, const float* acc, uint64_t* keys, hipStream_t s) {
     if (R <= 0) return hipSuccess;
     const ExpandLds lay = expand_lds(st.S, Kc, d, dense);
-    const bool narrow = st.S <= 8 && st.store == CB_STORE_CSR;
+    const bool narrow = expand_threads(st) == 64;
     const dim3 grid(R);
 #define CB_EXPAND(DT, DENSE, NT)                                                                      \
     hipLaunchKernelGGL((k_beam_expand<DT, DENSE, NT>), grid, dim3(NT), lay.total, s, st, K, Kc, d,   \
@@ -533,7 +535,7 @@ hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uin
                               hipStream_t s) {
     if (Q <= 0) return hipSuccess;
     const int P2 = next_pow2(K * Kc);
-    hipLaunchKernelGGL((k_query_merge<256>), dim3(Q), dim3(256), (size_t)P2 * 8, s, st, K, Kc, P2, keys, beam_rows,
+    hipLaunchKernelGGL((k_query_merge<kMergeThreads>), dim3(Q), dim3(kMergeThreads), (size_t)P2 * 8, s, st, K, Kc, P2, keys, beam_rows,
                        tok, par, rows, logp);
     return hipGetLastError();
 }

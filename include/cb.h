@@ -180,6 +180,35 @@ cb_status cb_tune(cb_plan* plan, int32_t Q, const float* q, const float* P, cons
  * cb_tune (negative when not measured). */
 cb_status cb_tune_times(const cb_plan* plan, int32_t t, float* dense_us, float* sparse_us);
 
+/* Kernel timing (measurement support).  While profiling is on, every step
+ * records a HIP event before and after each kernel it launches, on the step's
+ * stream; cb_profile_stop synchronises those events and reports one record
+ * per launch.  `kernel` is one of CB_KERNEL_*; `threads` the workgroup size. */
+typedef enum {
+    CB_KERNEL_GEMM_BF16 = 0,      /* full-codebook scores, bf16 MFMA */
+    CB_KERNEL_GEMM_F32 = 1,       /* full-codebook scores, float32 */
+    CB_KERNEL_EXPAND_SPARSE = 2,  /* slot fill + gather-dot + softmax + per-beam top-K */
+    CB_KERNEL_EXPAND_DENSE = 3,   /* slot fill + column gather + softmax + per-beam top-K */
+    CB_KERNEL_MERGE = 4           /* per-query top-K and next rows */
+} cb_kernel;
+
+typedef struct {
+    int32_t step;     /* decoding step t */
+    int32_t kernel;   /* cb_kernel */
+    int32_t threads;  /* workgroup size */
+    int32_t blocks;   /* workgroups launched */
+    float us;         /* duration between the events around the launch */
+} cb_kernel_time;
+
+/* Start recording up to `capacity` launches (creates 2*capacity events;
+ * launches beyond capacity are not recorded).  Restarting discards records. */
+cb_status cb_profile_start(cb_plan* plan, int32_t capacity);
+
+/* Stop recording, synchronise the recorded events and copy up to `cap`
+ * records to `out` (may be NULL); *n receives the number recorded.  Releases
+ * the events. */
+cb_status cb_profile_stop(cb_plan* plan, cb_kernel_time* out, int32_t cap, int32_t* n);
+
 /* Release a plan and its workspace.  NULL is ignored. */
 void cb_plan_destroy(cb_plan* plan);
 

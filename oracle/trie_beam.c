@@ -53,11 +53,11 @@
 #include <string.h>
 
 typedef struct node {
-    int32_t token;      /* label of the edge from the parent (-1 at the root) */
-    int32_t n, cap;     /* children count / capacity */
-    int32_t depth;
-    int64_t rank;       /* breadth-first number among nodes of the same depth */
-    struct node** kid;  /* children, ascending token */
+    int32_t token;       /* label of the edge from the parent (-1 at the root) */
+    int32_t n;           /* number of children */
+    int64_t rank;        /* breadth-first number among nodes of the same depth */
+    struct node* first;  /* first child (smallest token) */
+    struct node* next;   /* next sibling (next larger token) */
 } node;
 
 typedef struct or_trie {
@@ -67,12 +67,12 @@ typedef struct or_trie {
     node** pools;       /* node storage, in blocks */
     int64_t n_pools, pool_fill, pool_cap;
     int64_t* count;     /* nodes per depth, [L+1] */
-    node*** level;      /* level[t][rank] */
+    node*** level;      /* level[t][rank] for t < L */
 } or_trie;
 
 #define POOL_BLOCK (1 << 20)
 
-static node* new_node(or_trie* T, int32_t token, int32_t depth) {
+static node* new_node(or_trie* T, int32_t token) {
     if (T->n_pools == 0 || T->pool_fill == POOL_BLOCK) {
         if (T->n_pools == T->pool_cap) {
             int64_t nc = T->pool_cap ? T->pool_cap * 2 : 64;
@@ -88,52 +88,23 @@ static node* new_node(or_trie* T, int32_t token, int32_t depth) {
     }
     node* x = &T->pools[T->n_pools - 1][T->pool_fill++];
     x->token = token;
-    x->n = x->cap = 0;
-    x->depth = depth;
+    x->n = 0;
     x->rank = -1;
-    x->kid = NULL;
+    x->first = NULL;
+    x->next = NULL;
     return x;
 }
 
-/* Position of the first child with token >= tok. */
-static int32_t lower_bound_kid(const node* x, int32_t tok) {
-    int32_t lo = 0, hi = x->n;
-    while (lo < hi) {
-        int32_t mid = (lo + hi) >> 1;
-        if (x->kid[mid]->token < tok) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
-
-/* Child of x labelled tok; created (in sorted position) when absent.
- * *created tells whether it was new.  NULL on allocation failure. */
-static node* child_insert(or_trie* T, node* x, int32_t tok, int* created) {
-    int32_t i = lower_bound_kid(x, tok);
-    *created = 0;
-    if (i < x->n && x->kid[i]->token == tok) return x->kid[i];
-    if (x->n == x->cap) {
-        int32_t nc = x->cap ? x->cap * 2 : 2;
-        node** nk = (node**)realloc(x->kid, sizeof(node*) * (size_t)nc);
-        if (!nk) return NULL;
-        x->kid = nk;
-        x->cap = nc;
-    }
-    node* c = new_node(T, tok, x->depth + 1);
-    if (!c) return NULL;
-    memmove(x->kid + i + 1, x->kid + i, sizeof(node*) * (size_t)(x->n - i));
-    x->kid[i] = c;
-    x->n++;
-    *created = 1;
-    return c;
+/* Child of x labelled tok, or NULL. */
+static const node* find_child(const node* x, int32_t tok) {
+    for (const node* c = x->first; c; c = c->next)
+        if (c->token == tok) return c;
+    return NULL;
 }
 
 void or_free(or_trie* T) {
     if (!T) return;
-    for (int64_t p = 0; p < T->n_pools; ++p) {
-        int64_t m = (p == T->n_pools - 1) ? T->pool_fill : POOL_BLOCK;
-        for (int64_t j = 0; j < m; ++j) free(T->pools[p][j].kid);
-        free(T->pools[p]);
-    }
+    for (int64_t p = 0; p < T->n_pools; ++p) free(T->pools[p]);
     free(T->pools);
     if (T->level)
         for (int t = 0; t <= T->L; ++t) free(T->level[t]);
@@ -143,7 +114,14 @@ void or_free(or_trie* T) {
 }
 
 /* Build the trie of the catalog sids[n][L] (tokens in [0, V)).  Returns NULL
- * on a token out of range, L < 1, V < 1 or allocation failure. */
+ * on a token out of range, L < 1, V < 1 or allocation failure.
+ *
+ * Items are inserted in lexicographic order (a stable counting sort per token
+ * position, last position first).  In that order an item shares with the
+ * previous one the path down to the first position where they differ; below
+ * it every node is new, and the new child at the divergence point has a larger
+ * token than every existing sibling, so it is appended as the last child.  An
+ * item equal to the previous one is a repeat and adds nothing. */
 or_trie* or_build(const int32_t* sids, int64_t n, int L, int V) {
     if (L < 1 || V < 1 || n < 0) return NULL;
     for (int64_t i = 0; i < n * L; ++i)
@@ -152,17 +130,48 @@ or_trie* or_build(const int32_t* sids, int64_t n, int L, int V) {
     if (!T) return NULL;
     T->L = L;
     T->V = V;
-    T->root = new_node(T, -1, 0);
+    T->root = new_node(T, -1);
     if (!T->root) { or_free(T); return NULL; }
-    for (int64_t i = 0; i < n; ++i) {
-        node* x = T->root;
-        int created = 0;
-        for (int t = 0; t < L; ++t) {
-            x = child_insert(T, x, sids[i * L + t], &created);
-            if (!x) { or_free(T); return NULL; }
-        }
-        if (created) T->n_items++;  /* a new leaf is a new distinct item */
+    int64_t* order = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n ? n : 1));
+    int64_t* tmp = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n ? n : 1));
+    int64_t* cnt = (int64_t*)malloc(sizeof(int64_t) * ((size_t)V + 1));
+    node** path = (node**)malloc(sizeof(node*) * ((size_t)L + 1));
+    if (!order || !tmp || !cnt || !path) {
+        free(order); free(tmp); free(cnt); free(path); or_free(T);
+        return NULL;
     }
+    for (int64_t i = 0; i < n; ++i) order[i] = i;
+    for (int t = L - 1; t >= 0; --t) {
+        memset(cnt, 0, sizeof(int64_t) * ((size_t)V + 1));
+        for (int64_t k = 0; k < n; ++k) cnt[sids[order[k] * L + t] + 1]++;
+        for (int v = 0; v < V; ++v) cnt[v + 1] += cnt[v];
+        for (int64_t k = 0; k < n; ++k) tmp[cnt[sids[order[k] * L + t]]++] = order[k];
+        int64_t* sw = order; order = tmp; tmp = sw;
+    }
+    free(tmp);
+    free(cnt);
+    path[0] = T->root;
+    int64_t prev = -1;
+    for (int64_t k = 0; k < n; ++k) {
+        const int64_t i = order[k];
+        int t0 = 0;
+        if (prev >= 0)
+            while (t0 < L && sids[i * L + t0] == sids[prev * L + t0]) ++t0;
+        if (t0 == L) continue;  /* repeated item */
+        for (int t = t0; t < L; ++t) {
+            node* c = new_node(T, sids[i * L + t]);
+            if (!c) { free(order); free(path); or_free(T); return NULL; }
+            node* parent = path[t];
+            if (parent->n == 0) parent->first = c;
+            else path[t + 1]->next = c;  /* path[t+1] is parent's last child */
+            parent->n++;
+            path[t + 1] = c;
+        }
+        T->n_items++;
+        prev = i;
+    }
+    free(order);
+    free(path);
     /* breadth-first numbering, children in ascending token order */
     T->count = (int64_t*)calloc((size_t)L + 1, sizeof(int64_t));
     T->level = (node***)calloc((size_t)L + 1, sizeof(node**));
@@ -175,16 +184,18 @@ or_trie* or_build(const int32_t* sids, int64_t n, int L, int V) {
     for (int t = 0; t < L; ++t) {
         int64_t m = 0;
         for (int64_t r = 0; r < T->count[t]; ++r) m += T->level[t][r]->n;
-        T->level[t + 1] = (node**)malloc(sizeof(node*) * (size_t)(m ? m : 1));
-        if (!T->level[t + 1]) { or_free(T); return NULL; }
-        int64_t k = 0;
-        for (int64_t r = 0; r < T->count[t]; ++r) {
-            node* x = T->level[t][r];
-            for (int32_t j = 0; j < x->n; ++j) {
-                x->kid[j]->rank = k;
-                T->level[t + 1][k++] = x->kid[j];
-            }
+        const int keep = t + 1 < L;  /* leaves need no rank -> node table */
+        if (keep) {
+            T->level[t + 1] = (node**)malloc(sizeof(node*) * (size_t)(m ? m : 1));
+            if (!T->level[t + 1]) { or_free(T); return NULL; }
         }
+        int64_t k = 0;
+        for (int64_t r = 0; r < T->count[t]; ++r)
+            for (node* c = T->level[t][r]->first; c; c = c->next) {
+                c->rank = k;
+                if (keep) T->level[t + 1][k] = c;
+                ++k;
+            }
         T->count[t + 1] = m;
     }
     return T;
@@ -199,10 +210,12 @@ int64_t or_level_count(const or_trie* T, int depth) {
 }
 
 static int fill_children(const node* x, int32_t* tokens, int64_t* ranks, int64_t cap) {
-    for (int32_t j = 0; j < x->n && j < cap; ++j) {
-        if (tokens) tokens[j] = x->kid[j]->token;
-        if (ranks) ranks[j] = x->kid[j]->rank;
-    }
+    int64_t j = 0;
+    for (const node* c = x->first; c; c = c->next, ++j)
+        if (j < cap) {
+            if (tokens) tokens[j] = c->token;
+            if (ranks) ranks[j] = c->rank;
+        }
     return x->n;
 }
 
@@ -210,36 +223,30 @@ static int fill_children(const node* x, int32_t* tokens, int64_t* ranks, int64_t
  * numbers at depth len+1.  Returns the child count, -1 if the prefix is not
  * in the catalog. */
 int or_children(const or_trie* T, const int32_t* prefix, int len, int32_t* tokens, int64_t* ranks, int64_t cap) {
-    if (len < 0 || len > T->L) return -1;
+    if (len < 0 || len >= T->L) return -1;
     const node* x = T->root;
-    for (int t = 0; t < len; ++t) {
-        int32_t i = lower_bound_kid(x, prefix[t]);
-        if (i >= x->n || x->kid[i]->token != prefix[t]) return -1;
-        x = x->kid[i];
-    }
+    for (int t = 0; t < len && x; ++t) x = find_child(x, prefix[t]);
+    if (!x) return -1;
     return fill_children(x, tokens, ranks, cap);
 }
 
-/* Children of the node with number `row` at depth `depth`. */
+/* Children of the node with number `row` at depth `depth` (< L). */
 int or_children_of_row(const or_trie* T, int depth, int64_t row, int32_t* tokens, int64_t* ranks, int64_t cap) {
-    if (depth < 0 || depth > T->L || row < 0 || row >= T->count[depth]) return -1;
+    if (depth < 0 || depth >= T->L || row < 0 || row >= T->count[depth]) return -1;
     return fill_children(T->level[depth][row], tokens, ranks, cap);
 }
 
-/* The prefix (tokens from the root) of node `row` at depth `depth`. */
+/* The prefix (tokens from the root) of node `row` at depth `depth` (< L).
+ * Plain and slow: each parent is found by scanning the level above. */
 int or_prefix_of_row(const or_trie* T, int depth, int64_t row, int32_t* out) {
-    if (depth < 0 || depth > T->L || row < 0 || row >= T->count[depth]) return -1;
-    /* walk down: find the path by searching each level's parent (plain and
-     * slow: scan the parent level for the node that owns this child) */
+    if (depth < 0 || depth >= T->L || row < 0 || row >= T->count[depth]) return -1;
     const node* target = T->level[depth][row];
     for (int t = depth; t > 0; --t) {
         out[t - 1] = target->token;
         const node* parent = NULL;
-        for (int64_t r = 0; r < T->count[t - 1] && !parent; ++r) {
-            const node* x = T->level[t - 1][r];
-            int32_t i = lower_bound_kid(x, target->token);
-            if (i < x->n && x->kid[i] == target) parent = x;
-        }
+        for (int64_t r = 0; r < T->count[t - 1] && !parent; ++r)
+            for (const node* c = T->level[t - 1][r]->first; c; c = c->next)
+                if (c == target) { parent = T->level[t - 1][r]; break; }
         if (!parent) return -1;
         target = parent;
     }
@@ -288,22 +295,24 @@ static int64_t query_candidates(const or_trie* T, int t, int K, int d, const flo
         }
         const float* hb = h + (int64_t)k * d;
         double zmax = -INFINITY;
-        for (int32_t j = 0; j < x->n; ++j) {
-            const float* w = Wt + (int64_t)x->kid[j]->token * d;
+        int32_t j = 0;
+        for (const node* ch = x->first; ch; ch = ch->next, ++j) {
+            const float* w = Wt + (int64_t)ch->token * d;
             double s = 0.0;
             for (int i = 0; i < d; ++i) s += (double)hb[i] * (double)w[i];
             z[j] = s;
             if (s > zmax) zmax = s;
         }
         double se = 0.0;
-        for (int32_t j = 0; j < x->n; ++j) se += exp(z[j] - zmax);
+        for (j = 0; j < x->n; ++j) se += exp(z[j] - zmax);
         double lse = zmax + log(se);
-        for (int32_t j = 0; j < x->n; ++j) {
+        j = 0;
+        for (const node* ch = x->first; ch; ch = ch->next, ++j) {
             float logp = (float)(z[j] - lse);
             c[m].score = (float)((double)acc[k] + (double)logp);
             c[m].parent = k;
-            c[m].token = x->kid[j]->token;
-            c[m].child = x->kid[j];
+            c[m].token = ch->token;
+            c[m].child = ch;
             ++m;
         }
     }

@@ -129,12 +129,15 @@ def main():
             "expansions": n_exp, "max_fanout": S, "mean_fanout": float(fan.mean()) if len(fan) else 0.0,
             "valid_fraction": n_exp / max(1, len(live) * V), "distinct_tokens": len(toks),
             "bytes": {
+                "step_query": (R * 8 + idx_bytes + len(live) * d * es + len(toks) * d * es + R * 16
+                               + min(R, n_exp) * 8),
                 "expand_sparse": state_bytes + idx_bytes + len(live) * d * es + len(toks) * d * es,
                 "expand_dense": state_bytes + idx_bytes + n_exp * 4,
                 "merge": Q * K * Kc * 8 + R * 4 + R * 16 + min(R, n_exp) * 8,
                 "gemm_" + cfg.dtype: R * d * es + V * d * es + R * V * 4,
             },
-            "flops": {"gemm_" + cfg.dtype: 2 * len(live) * V * d, "expand_sparse": 2 * d * n_exp},
+            "flops": {"gemm_" + cfg.dtype: 2 * len(live) * V * d, "expand_sparse": 2 * d * n_exp,
+                      "step_query": 2 * d * n_exp},
         })
     expansions = sum(s["expansions"] for s in steps)
     del hidx
@@ -197,10 +200,14 @@ def main():
         k["bytes"] += steps[r["step"]]["bytes"].get(r["kernel"], 0)
         k["flops"] += steps[r["step"]]["flops"].get(r["kernel"], 0)
     per_step_us = [0.0] * L
+    per_step_k = [dict() for _ in range(L)]
     for r in recs:
         per_step_us[r["step"]] += r["us"] / args.steps
+        kk = per_step_k[r["step"]]
+        kk[r["kernel"]] = kk.get(r["kernel"], 0.0) + r["us"] / args.steps
     for s_ in steps:
         s_["kernel_us"] = round(per_step_us[s_["t"]], 3)
+        s_["kernels_us"] = {k: round(v, 3) for k, v in per_step_k[s_["t"]].items()}
     for name, k in kern.items():
         k["mean_us"] = k["us"] / k["launches"]
         k["share"] = k["us"] / sum(x["us"] for x in kern.values())

@@ -35,7 +35,8 @@ class KernelTime(ctypes.Structure):
                 ("blocks", ctypes.c_int32), ("us", ctypes.c_float)]
 
 
-KERNEL_NAMES = {0: "gemm_bf16", 1: "gemm_f32", 2: "expand_sparse", 3: "expand_dense", 4: "merge"}
+KERNEL_NAMES = {0: "gemm_bf16", 1: "gemm_f32", 2: "expand_sparse", 3: "expand_dense", 4: "merge",
+                5: "step_query", 6: "live_rows"}
 
 SIGNATURES = {
     "cb_build_index": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _I32, _PP]),

@@ -18,7 +18,6 @@ thread_local std::string g_err;
 void set_error(const std::string& msg) { g_err = msg; }
 void clear_error() { g_err.clear(); }
 
-size_t expand_lds_bytes(int S, int Kc, int d, bool dense);  // kernels.hip
 
 namespace {
 
@@ -100,27 +99,39 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, const void* hidden, c
     const int R = Q * p->K;
     const int Kc = std::min(p->K, std::max(T.S, 1));
     hipError_t e;
-    const int ent = expand_threads(sd);
-    if (path == CB_PATH_DENSE) {
-        const bool bf = p->dtype == CB_BF16;
-        const int gblocks = bf ? ((idx->V + 127) / 128) * ((R + 127) / 128) : ((idx->V + 15) / 16) * ((R + 15) / 16);
-        ProfMark m0(p, s, t, bf ? CB_KERNEL_GEMM_BF16 : CB_KERNEL_GEMM_F32, 256, gblocks);
-        e = launch_gemm_scores(p->dtype, R, idx->V, p->d, hidden, Wt, p->Z, s);
-        m0.done();
-        if (e != hipSuccess) return hip_fail("cb_step: full-codebook scores", e);
-        ProfMark m1(p, s, t, CB_KERNEL_EXPAND_DENSE, ent, R);
-        e = launch_beam_expand(sd, true, p->dtype, R, p->K, Kc, p->d, hidden, Wt, p->Z, idx->V, rows, acc, p->keys, s);
-        m1.done();
-    } else {
-        ProfMark m1(p, s, t, CB_KERNEL_EXPAND_SPARSE, ent, R);
-        e = launch_beam_expand(sd, false, p->dtype, R, p->K, Kc, p->d, hidden, Wt, nullptr, 0, rows, acc, p->keys, s);
-        m1.done();
+    if (path == CB_PATH_SPARSE) {
+        ProfMark m(p, s, t, CB_KERNEL_STEP_QUERY, query_threads(p->K), Q);
+        e = launch_step_query(sd, p->dtype, Q, p->K, Kc, p->d, hidden, Wt, rows, acc, ot, op, orow, ol, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: sparse step", e);
+        return CB_OK;
     }
-    if (e != hipSuccess) return hip_fail("cb_step: beam expansion", e);
-    ProfMark m2(p, s, t, CB_KERNEL_MERGE, kMergeThreads, Q);
-    e = launch_query_merge(sd, Q, p->K, Kc, p->keys, rows, ot, op, orow, ol, s);
-    m2.done();
-    if (e != hipSuccess) return hip_fail("cb_step: query merge", e);
+    {
+        ProfMark m(p, s, t, CB_KERNEL_LIVE_ROWS, 1024, 1);
+        e = launch_live_rows(sd, R, rows, acc, p->live, p->n_live, p->ci_of, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: live beams", e);
+    }
+    {
+        const bool bf = p->dtype == CB_BF16;
+        ProfMark m(p, s, t, bf ? CB_KERNEL_GEMM_BF16 : CB_KERNEL_GEMM_F32, 256, gemm_blocks(p->dtype, R, idx->V));
+        e = launch_gemm_scores(p->dtype, R, idx->V, p->d, p->live, p->n_live, hidden, Wt, p->Z, p->Zp, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: full-codebook scores", e);
+    }
+    {
+        ProfMark m(p, s, t, CB_KERNEL_EXPAND_DENSE, expand_threads(sd), R);
+        e = launch_beam_expand(sd, true, p->dtype, R, p->K, Kc, p->d, hidden, Wt, p->Z, p->Zp, idx->V, p->n_live,
+                               p->ci_of, rows, acc, p->keys, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: beam expansion", e);
+    }
+    {
+        ProfMark m(p, s, t, CB_KERNEL_MERGE, kMergeThreads, Q);
+        e = launch_query_merge(sd, Q, p->K, Kc, p->keys, rows, ot, op, orow, ol, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: query merge", e);
+    }
     return CB_OK;
 }
 
@@ -341,24 +352,20 @@ cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_
         return CB_EINVAL;
     }
     if (K > kMaxK) {
-        set_error("cb_plan_create: K > 1024 is not supported");
+        set_error("cb_plan_create: K > " + std::to_string(kMaxK) + " is not supported");
         return CB_ECAPACITY;
     }
     int32_t Smax = 1;
-    for (const auto& T : idx->steps) Smax = std::max(Smax, T.S);
-    if (Smax > kMaxRowSlots) {
-        set_error("cb_plan_create: a step has a row wider than " + std::to_string(kMaxRowSlots) + " valid tokens");
-        return CB_ECAPACITY;
+    for (const auto& T : idx->steps) {
+        Smax = std::max(Smax, T.S);
+        const int Kc_t = std::min(K, std::max(T.S, 1));
+        if (query_lds_bytes(T.S, K, Kc_t, d) > (size_t)kMaxLds || expand_lds_bytes(T.S, d, true) > (size_t)kMaxLds) {
+            set_error("cb_plan_create: a step with a row of " + std::to_string(T.S) +
+                      " valid tokens exceeds the step kernels' LDS");
+            return CB_ECAPACITY;
+        }
     }
     const int32_t Kc = std::min(K, Smax);
-    if ((int64_t)K * Kc > kMaxMergeKeys) {
-        set_error("cb_plan_create: K * min(K, widest row) exceeds the per-query merge capacity");
-        return CB_ECAPACITY;
-    }
-    if (expand_lds_bytes(Smax, Kc, d, false) > 65536) {
-        set_error("cb_plan_create: per-beam workspace exceeds 64 KiB of LDS");
-        return CB_ECAPACITY;
-    }
     DeviceGuard g(idx->device);
     if (!g.ok) {
         set_error("cb_plan_create: cannot select the index's device");
@@ -382,6 +389,10 @@ cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_
     const size_t R = (size_t)Q_max * K;
     cb_status st = dev_alloc(&p->keys, R * Kc, "candidate keys");
     if (st == CB_OK) st = dev_alloc(&p->Z, R * (size_t)idx->V, "full-codebook scores");
+    if (st == CB_OK && dtype == CB_BF16) st = dev_alloc(&p->Zp, split_scores_floats(idx->V), "partial scores");
+    if (st == CB_OK) st = dev_alloc(&p->live, R, "live beams");
+    if (st == CB_OK) st = dev_alloc(&p->ci_of, R, "compact index");
+    if (st == CB_OK) st = dev_alloc(&p->n_live, 1, "live count");
     for (int i = 0; i < 2 && st == CB_OK; ++i) {
         st = dev_alloc(&p->s[i], R * d, "state");
         if (st == CB_OK) st = dev_alloc(&p->rows[i], R, "rows");
@@ -643,6 +654,10 @@ void cb_plan_destroy(cb_plan* p) {
     profile_release(p);
     dev_free(p->keys);
     dev_free(p->Z);
+    dev_free(p->Zp);
+    dev_free(p->live);
+    dev_free(p->ci_of);
+    dev_free(p->n_live);
     for (int i = 0; i < 2; ++i) {
         dev_free(p->s[i]);
         dev_free(p->rows[i]);

@@ -57,9 +57,10 @@ struct cb_index {
 
 // Limits of the kernels in this build.
 namespace cb {
-constexpr int kMaxK = 1024;          // parent slot fits the 10-bit key field
-constexpr int kMaxRowSlots = 4096;   // widest row one workgroup holds in LDS
-constexpr int kMaxMergeKeys = 8192;  // K * min(K, S_t) keys merged in LDS per query
+constexpr int kMaxK = 64;            // beam width held by the per-query selection (one wave)
+constexpr int kMaxLds = 65536;       // LDS one workgroup may use
+constexpr int kExpandThreads = 256;  // per-beam expansion workgroup
+constexpr int kMergeThreads = 256;   // per-query merge workgroup (dense path)
 }
 
 struct cb_plan {
@@ -71,8 +72,12 @@ struct cb_plan {
     std::vector<int32_t> tuned;   // per step: measured choice (0 = none)
     std::vector<float> tune_dense_us, tune_sparse_us;
     // workspace (allocated once)
-    uint64_t* keys = nullptr;     // [Q_max*K][Kc_max] per-beam survivors
+    uint64_t* keys = nullptr;     // [Q_max*K][Kc_max] per-beam survivors (dense path)
     float* Z = nullptr;           // [Q_max*K][V] full-codebook scores (dense path)
+    float* Zp = nullptr;          // [k-slices][rows][V] partial scores (dense path, few live beams)
+    int32_t* live = nullptr;      // [Q_max*K] live beam slots (dense path)
+    int32_t* ci_of = nullptr;     // [Q_max*K] compact index of each slot, -1 dead
+    int32_t* n_live = nullptr;    // [1]
     // decode state
     float* s[2] = {nullptr, nullptr};    // [R][d] float32 state vectors
     void* h = nullptr;                    // [R][d] dtype hidden vectors
@@ -94,17 +99,29 @@ struct cb_plan {
 namespace cb {
 
 // Kernel launchers (kernels.hip).  All enqueue on `stream`; return hipError_t of the launch.
-// Workgroup size the step kernels use for a table.
+// Workgroup sizes and LDS bytes of the step kernels.
 int expand_threads(const StepDev& st);
-constexpr int kMergeThreads = 256;
+int query_threads(int K);
+size_t expand_lds_bytes(int S, int d, bool dense);
+size_t query_lds_bytes(int S, int K, int Kc, int d);
+int gemm_blocks(cb_dtype dt, int R, int V);
 
+// Sparse path: the whole step in one launch, one workgroup per query.
+hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int Kc, int d, const void* hidden,
+                             const void* W, const int32_t* beam_rows, const float* acc, int32_t* tok, int32_t* par,
+                             int32_t* rows, float* logp, hipStream_t s);
+// Dense path: live-beam list, full-codebook scores, per-beam expansion, per-query merge.
+hipError_t launch_live_rows(const StepDev& st, int R, const int32_t* beam_rows, const float* acc, int32_t* live,
+                            int32_t* n_live, int32_t* ci_of, hipStream_t s);
+hipError_t launch_gemm_scores(cb_dtype dt, int R, int V, int d, const int32_t* live, const int32_t* n_live,
+                              const void* H, const void* W, float* Z, float* Zp, hipStream_t s);
+size_t split_scores_floats(int V);
 hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R, int K, int Kc, int d,
-                              const void* hidden, const void* W, const float* Z, int64_t ldz,
-                              const int32_t* beam_rows, const float* acc, uint64_t* keys, hipStream_t s);
+                              const void* hidden, const void* W, const float* Z, const float* Zp, int64_t ldz,
+                              const int32_t* n_live, const int32_t* ci_of, const int32_t* beam_rows,
+                              const float* acc, uint64_t* keys, hipStream_t s);
 hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uint64_t* keys,
                               const int32_t* beam_rows, int32_t* tok, int32_t* par, int32_t* rows, float* logp,
-                              hipStream_t s);
-hipError_t launch_gemm_scores(cb_dtype dt, int R, int V, int d, const void* H, const void* W, float* Z,
                               hipStream_t s);
 hipError_t launch_decode_init(int Q, int K, int d, cb_dtype dt, const float* q, float* s_out, void* h_out,
                               int32_t* rows, float* acc, hipStream_t st);

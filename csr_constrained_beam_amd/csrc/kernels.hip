@@ -1,29 +1,37 @@
 // Device kernels of one constrained beam-search step on gfx950 (wave64).
 //
-// Step layout (one decoding step t over R = Q*K beam slots):
-//   [dense path only] k_gemm_bf16 / k_gemm_f32: Z = H * W_t^T over the whole
-//       codebook (ZeroGR: "full scoring" = one regular matrix product).
-//   k_beam_expand: one workgroup per beam slot.
-//       a1 slot fill: the beam's row gives its valid tokens, written in order
-//          into LDS slots 0..n-1 (CSR rows are copied, bitmap rows are
-//          enumerated with a block-wide popcount scan).  Slots depend only on
-//          the beam and the position (ZeroGR: fixed candidate slots, valid
-//          tokens filling from the front).
-//       a2 scores: sparse path = one wavefront per token, W_t row read in
-//          place (coalesced 16-byte lanes), hidden vector staged in LDS,
-//          fixed-order wave reduction; dense path = gather of the valid
-//          columns of Z.
-//       a3 log-softmax over the n valid slots only, added to the beam's
-//          accumulated log-prob (ZeroGR "The pipeline", stage 4).
-//       a4 (first half) the beam's best min(K, n) candidates as 64-bit keys
-//          (a beam cannot place more than K candidates among the K best).
-//   k_query_merge: one workgroup per query; bitonic sort of its K*min(K,S)
-//       keys in LDS, the best K become the next beams; each survivor's next
-//       row is the edge position of its token in the parent's row.
+// Sparse path (one launch per step), k_step_query: one workgroup per query.
+//   Phase 1, one wavefront per beam whose row has <= 64 valid tokens:
+//     a1 slot fill  - lane j holds the row's j-th token (CSR rows, ascending);
+//     a2 scores     - for each token the whole wave reads its W_t row in place
+//                     (16-byte coalesced lanes) against the hidden vector held in
+//                     registers, fixed-order butterfly sum; lane j keeps z_j;
+//     a3 softmax    - wave max / sum over the valid lanes only (ZeroGR "The
+//                     pipeline", stage 4: log-softmax over valid tokens, added to
+//                     the accumulated log-prob);
+//     a4 (beam)     - the beam's best min(K, n) candidate keys, written to the
+//                     beam's fixed slots in LDS (ZeroGR: fixed candidate slots;
+//                     a beam cannot place more than K candidates among its
+//                     query's K best).
+//   Phase 2, rows with more than 64 tokens (and bitmap rows): the whole
+//     workgroup per beam (tokens, hidden vector and scores staged in LDS).
+//   Phase 3 (a4 query): the K best keys of the query, their next rows.
+//
+// Dense path: k_live_rows (compact list of live beams), k_gemm_bf16 / k_gemm_f32
+// (scores of the live beams against the whole codebook; ZeroGR "full
+// scoring"), k_beam_expand (one workgroup per beam: gather of the valid
+// columns, softmax, best min(K, n) keys) and k_query_merge (per query K best).
 //
 // Candidate key: [63:32] order-preserving bits of the float32 score,
-// [25:16] 1023 - parent slot, [15:0] 65535 - token.  Sorting keys descending
-// orders by (score desc, parent asc, token asc); key 0 marks an empty slot.
+// [25:16] 1023 - parent slot, [15:0] 65535 - token.  Keys are unique within a
+// query; descending key order is (score desc, parent asc, token asc); 0 marks
+// an empty slot.
+//
+// Selection of the best Kc (<= 64) of n keys in a workgroup: tau = the Kc-th
+// largest of the per-thread maxima is a lower bound of the true Kc-th largest
+// key (the maxima are a subset of the keys), so the keys >= tau contain the
+// answer; usually only about Kc of them survive, and those are sorted with
+// register-resident wave64 bitonic networks.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -35,6 +43,7 @@ namespace cb {
 namespace {
 
 constexpr int kWave = 64;
+constexpr int kSmallRow = 64;  // rows up to this many tokens take the one-wave path
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
@@ -60,6 +69,8 @@ __device__ __forceinline__ uint64_t make_key(float score, int parent, int token)
            (uint64_t)(65535 - token);
 }
 
+// ---- wave and block primitives ----------------------------------------------
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
@@ -71,6 +82,49 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
     return v;
+}
+
+__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
+    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src);
+    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+// Bitonic sort of the wave's 64 keys (one per lane), descending across lanes.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint64_t o = shfl_xor64(v, j);
+            const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
+            v = take_max ? umax64(v, o) : umin64(v, o);
+        }
+    return v;
+}
+
+// a, b sorted descending across lanes: the 64 largest of a and b, descending.
+// (max(a[l], b[63-l]) is a bitonic sequence holding them; a half-cleaner
+// cascade sorts it.)
+__device__ __forceinline__ uint64_t wave_merge_top(uint64_t a, uint64_t b) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint64_t c = umax64(a, shfl64(b, kWave - 1 - lane));
+#pragma unroll
+    for (int j = kWave / 2; j > 0; j >>= 1) {
+        const uint64_t o = shfl_xor64(c, j);
+        c = ((lane & j) == 0) ? umax64(c, o) : umin64(c, o);
+    }
+    return c;
 }
 
 // Block reductions in a fixed order (deterministic); every thread gets the result.
@@ -122,49 +176,57 @@ __device__ int block_exclusive_scan(int c, int* red, int* total) {
     return off + x - c;
 }
 
-// Bitonic sort of n (power of two) keys in LDS, descending.  Caller syncs before.
+// The 64 largest of one key per thread, descending, in the lanes of wave 0.
+// The waves' sorted lists are merged pairwise as a tree.  stage: LDS [NT/2].
+// All threads call.
 template <int NT>
-__device__ void bitonic_sort_desc(uint64_t* a, int n) {
-    for (int k = 2; k <= n; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < n; i += NT) {
-                int ixj = i ^ j;
-                if (ixj > i) {
-                    uint64_t x = a[i], y = a[ixj];
-                    bool desc = (i & k) == 0;
-                    if (desc ? (x < y) : (x > y)) {
-                        a[i] = y;
-                        a[ixj] = x;
-                    }
-                }
-            }
-            __syncthreads();
-        }
+__device__ uint64_t block_top64(uint64_t v, uint64_t* stage) {
+    v = wave_sort_desc(v);
+    const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int half = NT / kWave / 2; half >= 1; half >>= 1) {
+        if (w >= half && w < 2 * half) stage[(w - half) * kWave + lane] = v;
+        __syncthreads();
+        if (w < half) v = wave_merge_top(v, stage[w * kWave + lane]);
+        __syncthreads();
     }
+    return v;
 }
 
-__host__ __device__ inline int next_pow2(int x) {
-    int p = 1;
-    while (p < x) p <<= 1;
-    return p;
+// The Kc (<= 64) largest of the n keys key(0..n-1) (0 = empty), descending,
+// written by wave 0 to out[0..Kc) (0-padded).  stage: LDS [NT]; list: LDS
+// int [n].  All threads call; out is complete after the next barrier.
+template <int NT, class KeyF>
+__device__ void block_select_top(int n, int Kc, KeyF key, uint64_t* out, uint64_t* stage, int* list, int* red_i,
+                                 uint64_t* bcast) {
+    const int tid = threadIdx.x;
+    if (n <= NT) {
+        const uint64_t top = block_top64<NT>(tid < n ? key(tid) : 0ull, stage);
+        if (tid < Kc) out[tid] = top;
+        return;
+    }
+    uint64_t mx = 0;
+    for (int j = tid; j < n; j += NT) mx = umax64(mx, key(j));
+    const uint64_t t = block_top64<NT>(mx, stage);
+    if (tid == Kc - 1) *bcast = t;
+    __syncthreads();
+    const uint64_t tau = umax64(*bcast, 1ull);
+    int c = 0;
+    for (int j = tid; j < n; j += NT) c += key(j) >= tau;
+    int total;
+    int pos = block_exclusive_scan<NT>(c, red_i, &total);
+    for (int j = tid; j < n; j += NT)
+        if (key(j) >= tau) list[pos++] = j;
+    __syncthreads();
+    uint64_t best = 0;
+    for (int base = 0; base < total; base += NT) {
+        const uint64_t top = block_top64<NT>(base + tid < total ? key(list[base + tid]) : 0ull, stage);
+        if (tid < kWave) best = base == 0 ? top : wave_merge_top(best, top);
+    }
+    if (tid < Kc) out[tid] = best;
 }
 
-// LDS layout of k_beam_expand (bytes), shared by host launcher and kernel.
-struct ExpandLds {
-    int keys, z, h, tok, total;
-};
-__host__ __device__ inline ExpandLds expand_lds(int S, int Kc, int d, bool dense) {
-    ExpandLds l;
-    int nk = S > Kc ? next_pow2(S) : 0;
-    l.keys = 0;
-    l.z = l.keys + nk * 8;
-    l.h = l.z + ((S * 4 + 15) & ~15);
-    l.tok = l.h + (dense ? 0 : d * 4);
-    l.total = l.tok + ((S * 2 + 15) & ~15);
-    return l;
-}
-
-// 8 consecutive elements of a W_t row (16-byte aligned) as float.
+// 8 consecutive elements (16-byte aligned) as float.
 __device__ __forceinline__ void load8(const uint16_t* p, float* o) {
     uint4 v = *reinterpret_cast<const uint4*>(p);
     o[0] = __uint_as_float(v.x << 16);
@@ -185,108 +247,91 @@ __device__ __forceinline__ void load8(const float* p, float* o) {
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 
-template <typename DT, bool DENSE, int NT>
-__global__ __launch_bounds__(NT) void k_beam_expand(StepDev st, int K, int Kc, int d,
-                                                    const DT* __restrict__ hidden, const DT* __restrict__ W,
-                                                    const float* __restrict__ Z, int64_t ldz,
-                                                    const int32_t* __restrict__ beam_rows,
-                                                    const float* __restrict__ acc, uint64_t* __restrict__ keys_out) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ float red_f[NT / kWave];
-    __shared__ int red_i[NT / kWave];
-    const ExpandLds lay = expand_lds(st.S, Kc, d, DENSE);
-    uint64_t* keys_s = reinterpret_cast<uint64_t*>(smem + lay.keys);
-    float* z_s = reinterpret_cast<float*>(smem + lay.z);
-    float* h_s = reinterpret_cast<float*>(smem + lay.h);
-    uint16_t* tok_s = reinterpret_cast<uint16_t*>(smem + lay.tok);
+__device__ __forceinline__ float dot8(const float* h, const float* w, float s) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = fmaf(h[i], w[i], s);
+    return s;
+}
 
-    const int b = blockIdx.x;
-    const int tid = threadIdx.x;
-    uint64_t* out = keys_out + (int64_t)b * Kc;
-    const int32_t r = beam_rows[b];
-    const float a = acc[b];
-    if (r < 0 || (int64_t)r >= st.n_rows || !(a > -INFINITY)) {
-        for (int j = tid; j < Kc; j += NT) out[j] = 0;
+__device__ __forceinline__ bool beam_live(const StepDev& st, int32_t r, float a) {
+    return r >= 0 && (int64_t)r < st.n_rows && a > -INFINITY;
+}
+
+// a1 for one beam, whole block: the row's valid tokens in ascending order into
+// tok_s[0..n).
+template <int NT>
+__device__ void block_fill_tokens(const StepDev& st, int32_t r, uint32_t e0, int n, uint16_t* tok_s, int* red_i) {
+    if (st.store == CB_STORE_CSR) {
+        for (int j = threadIdx.x; j < n; j += NT) tok_s[j] = st.tok[e0 + j];
         return;
     }
-    const uint32_t e0 = st.row_ptr[r];
-    const int n = (int)(st.row_ptr[r + 1] - e0);
+    const uint32_t* rb = st.bits + (int64_t)r * st.words;
+    int base = 0;
+    for (int w0 = 0; w0 < st.words; w0 += NT) {
+        const int w = w0 + threadIdx.x;
+        uint32_t word = w < st.words ? rb[w] : 0u;
+        int tot;
+        int pos = base + block_exclusive_scan<NT>(__popc(word), red_i, &tot);
+        while (word) {
+            const int bit = __ffs(word) - 1;
+            tok_s[pos++] = (uint16_t)(w * 32 + bit);
+            word &= word - 1;
+        }
+        base += tot;
+    }
+}
 
-    // a1: slot fill
-    if (st.store == CB_STORE_CSR) {
-        for (int j = tid; j < n; j += NT) tok_s[j] = st.tok[e0 + j];
-    } else {
-        const uint32_t* rb = st.bits + (int64_t)r * st.words;
-        int base = 0;
-        for (int w0 = 0; w0 < st.words; w0 += NT) {
-            const int w = w0 + tid;
-            uint32_t word = w < st.words ? rb[w] : 0u;
-            int tot;
-            int pos = base + block_exclusive_scan<NT>(__popc(word), red_i, &tot);
-            while (word) {
-                const int bit = __ffs(word) - 1;
-                tok_s[pos++] = (uint16_t)(w * 32 + bit);
-                word &= word - 1;
-            }
-            base += tot;
+// a2 (sparse) for one beam, whole block: z_s[j] = <h, W_t[tok_s[j]]>, one wave
+// per token, two tokens in flight per wave.
+template <typename DT, int NT>
+__device__ void block_scores(const float* h_s, const DT* __restrict__ W, int d, const uint16_t* tok_s, int n,
+                             float* z_s) {
+    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int NW = NT / kWave;
+    int j = threadIdx.x / kWave;
+    for (; j + NW < n; j += 2 * NW) {
+        const DT* w0 = W + (int64_t)tok_s[j] * d;
+        const DT* w1 = W + (int64_t)tok_s[j + NW] * d;
+        float s0 = 0.f, s1 = 0.f;
+        for (int i = lane * 8; i < d; i += kWave * 8) {
+            float a[8], b[8], h[8];
+            load8(w0 + i, a);
+            load8(w1 + i, b);
+            load8(h_s + i, h);
+            s0 = dot8(h, a, s0);
+            s1 = dot8(h, b, s1);
+        }
+        s0 = wave_sum(s0);
+        s1 = wave_sum(s1);
+        if (lane == 0) {
+            z_s[j] = s0;
+            z_s[j + NW] = s1;
         }
     }
-    if (!DENSE) {
-        const DT* hb = hidden + (int64_t)b * d;
-        for (int i = tid; i < d; i += NT) h_s[i] = to_f32(hb[i]);
-    }
-    __syncthreads();
-
-    // a2: scores of the valid slots
-    if (DENSE) {
-        const float* zb = Z + (int64_t)b * ldz;
-        for (int j = tid; j < n; j += NT) z_s[j] = zb[tok_s[j]];
-    } else {
-        const int lane = tid & (kWave - 1);
-        for (int j = tid / kWave; j < n; j += NT / kWave) {
-            const DT* wr = W + (int64_t)tok_s[j] * d;
-            float s = 0.f;
-            for (int i = lane * 8; i < d; i += kWave * 8) {
-                float w8[8];
-                load8(wr + i, w8);
-                const float4 h0 = *reinterpret_cast<const float4*>(h_s + i);
-                const float4 h1 = *reinterpret_cast<const float4*>(h_s + i + 4);
-                s = fmaf(h0.x, w8[0], s);
-                s = fmaf(h0.y, w8[1], s);
-                s = fmaf(h0.z, w8[2], s);
-                s = fmaf(h0.w, w8[3], s);
-                s = fmaf(h1.x, w8[4], s);
-                s = fmaf(h1.y, w8[5], s);
-                s = fmaf(h1.z, w8[6], s);
-                s = fmaf(h1.w, w8[7], s);
-            }
-            s = wave_sum(s);
-            if (lane == 0) z_s[j] = s;
+    for (; j < n; j += NW) {
+        const DT* w0 = W + (int64_t)tok_s[j] * d;
+        float s0 = 0.f;
+        for (int i = lane * 8; i < d; i += kWave * 8) {
+            float a[8], h[8];
+            load8(w0 + i, a);
+            load8(h_s + i, h);
+            s0 = dot8(h, a, s0);
         }
+        s0 = wave_sum(s0);
+        if (lane == 0) z_s[j] = s0;
     }
-    __syncthreads();
+}
 
-    // a3: log-softmax over the valid slots, plus the accumulated log-prob
+// a3 for one beam, whole block: log-sum-exp of z_s[0..n).
+template <int NT>
+__device__ float block_lse(const float* z_s, int n, float* red_f) {
     float m = -INFINITY;
-    for (int j = tid; j < n; j += NT) m = fmaxf(m, z_s[j]);
+    for (int j = threadIdx.x; j < n; j += NT) m = fmaxf(m, z_s[j]);
     m = block_max<NT>(m, red_f);
     float se = 0.f;
-    for (int j = tid; j < n; j += NT) se += expf(z_s[j] - m);
+    for (int j = threadIdx.x; j < n; j += NT) se += expf(z_s[j] - m);
     se = block_sum<NT>(se, red_f);
-    const float lse = m + logf(se);
-    const int parent = b % K;
-
-    // a4 (per beam): best min(K, n) candidates
-    if (n <= Kc) {
-        for (int j = tid; j < Kc; j += NT)
-            out[j] = j < n ? make_key(a + (z_s[j] - lse), parent, tok_s[j]) : 0ull;
-        return;
-    }
-    const int n2 = next_pow2(n);
-    for (int j = tid; j < n2; j += NT) keys_s[j] = j < n ? make_key(a + (z_s[j] - lse), parent, tok_s[j]) : 0ull;
-    __syncthreads();
-    bitonic_sort_desc<NT>(keys_s, n2);
-    for (int j = tid; j < Kc; j += NT) out[j] = keys_s[j];
+    return m + logf(se);
 }
 
 // Next-step row of `token` in row r: its edge position.
@@ -308,57 +353,391 @@ __device__ int32_t edge_of(const StepDev& st, int32_t r, int token) {
     return (int32_t)(e0 + c);
 }
 
+// Output slot i of query q from its key.
+__device__ void emit(const StepDev& st, int q, int K, int i, uint64_t key, const int32_t* __restrict__ beam_rows,
+                     int32_t* out_tok, int32_t* out_par, int32_t* out_rows, float* out_logp) {
+    const int64_t o = (int64_t)q * K + i;
+    if (key == 0ull) {
+        out_tok[o] = -1;
+        out_par[o] = -1;
+        out_rows[o] = -1;
+        out_logp[o] = -INFINITY;
+        return;
+    }
+    const int parent = 1023 - (int)((key >> 16) & 1023u);
+    const int token = 65535 - (int)(key & 0xFFFFu);
+    out_tok[o] = token;
+    out_par[o] = parent;
+    out_rows[o] = edge_of(st, beam_rows[(int64_t)q * K + parent], token);
+    out_logp[o] = score_from_order_bits((uint32_t)(key >> 32));
+}
+
+// ---- LDS layouts (shared by launchers and kernels) --------------------------
+
+struct ExpandLds {
+    int z, h, tok, list, stage, total;
+};
+__host__ __device__ inline ExpandLds expand_lds(int S, int d, bool dense, int NT) {
+    ExpandLds l;
+    l.stage = 0;
+    l.z = l.stage + NT * 8;
+    l.list = l.z + ((S * 4 + 15) & ~15);
+    l.h = l.list + ((S * 4 + 15) & ~15);
+    l.tok = l.h + (dense ? 0 : ((d * 4 + 15) & ~15));
+    l.total = l.tok + ((S * 2 + 15) & ~15);
+    return l;
+}
+
+struct QueryLds {
+    int qkeys, stage, list, z, h, tok, total;
+};
+__host__ __device__ inline QueryLds query_lds(int S, int K, int Kc, int d, int NT) {
+    QueryLds l;
+    const int M = K * Kc;
+    l.qkeys = 0;
+    l.stage = l.qkeys + M * 8;
+    l.list = l.stage + NT * 8;
+    l.z = l.list + (((S > M ? S : M) * 4 + 15) & ~15);
+    l.h = l.z + ((S * 4 + 15) & ~15);
+    l.tok = l.h + ((d * 4 + 15) & ~15);
+    l.total = l.tok + ((S * 2 + 15) & ~15);
+    return l;
+}
+
+// ---- sparse step: one workgroup per query ----------------------------------
+
+template <typename DT, int NT, int CH>
+__global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, int d,
+                                                   const DT* __restrict__ hidden, const DT* __restrict__ W,
+                                                   const int32_t* __restrict__ beam_rows,
+                                                   const float* __restrict__ acc, int32_t* __restrict__ out_tok,
+                                                   int32_t* __restrict__ out_par, int32_t* __restrict__ out_rows,
+                                                   float* __restrict__ out_logp) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ float red_f[NT / kWave];
+    __shared__ int red_i[NT / kWave];
+    __shared__ uint64_t bcast;
+    __shared__ uint64_t best[kWave];
+    __shared__ int nbig;
+    __shared__ int big[kWave];
+    const QueryLds lay = query_lds(st.S, K, Kc, d, NT);
+    uint64_t* qkeys = reinterpret_cast<uint64_t*>(smem + lay.qkeys);
+    uint64_t* stage = reinterpret_cast<uint64_t*>(smem + lay.stage);
+    int* list = reinterpret_cast<int*>(smem + lay.list);
+    float* z_s = reinterpret_cast<float*>(smem + lay.z);
+    float* h_s = reinterpret_cast<float*>(smem + lay.h);
+    uint16_t* tok_s = reinterpret_cast<uint16_t*>(smem + lay.tok);
+
+    const int q = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    constexpr int NW = NT / kWave;
+    if (tid == 0) nbig = 0;
+    __syncthreads();
+
+    // phase 1: one wave per beam with a narrow CSR row; each wave takes two
+    // beams at a time so that their chains of dependent loads overlap
+    for (int k0 = wv; k0 < K; k0 += 2 * NW) {
+        int kk[2], tk[2], n[2];
+        int64_t b[2];
+        float a[2];
+        bool small[2];
+        uint32_t e0[2];
+        int32_t r[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            kk[u] = k0 + u * NW;
+            b[u] = (int64_t)q * K + kk[u];
+            r[u] = kk[u] < K ? beam_rows[b[u]] : -1;
+            a[u] = kk[u] < K ? acc[b[u]] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bool live = kk[u] < K && beam_live(st, r[u], a[u]);
+            e0[u] = live ? st.row_ptr[r[u]] : 0u;
+            n[u] = live ? (int)(st.row_ptr[r[u] + 1] - e0[u]) : 0;
+            small[u] = live && n[u] <= kSmallRow && st.store == CB_STORE_CSR;
+            if (kk[u] < K) {
+                if (!live) {
+                    if (lane < Kc) qkeys[kk[u] * Kc + lane] = 0ull;
+                } else if (!small[u]) {
+                    if (lane == 0) big[atomicAdd(&nbig, 1)] = kk[u];
+                }
+            }
+            tk[u] = small[u] && lane < n[u] ? (int)st.tok[e0[u] + lane] : 0;
+        }
+        if (!small[0] && !small[1]) continue;
+        float hr[2][CH][8];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int i = c * kWave * 8 + lane * 8;
+                if (small[u] && i < d) load8(hidden + b[u] * d + i, hr[u][c]);
+                else
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) hr[u][c][e] = 0.f;
+            }
+        float z[2] = {-INFINITY, -INFINITY};
+        const int nmax = max(small[0] ? n[0] : 0, small[1] ? n[1] : 0);
+        for (int j = 0; j < nmax; ++j) {
+            float sv[2] = {0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int tj = __shfl(tk[u], j);
+                if (small[u] && j < n[u]) {
+                    const DT* wr = W + (int64_t)tj * d;
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) {
+                        const int i = c * kWave * 8 + lane * 8;
+                        if (i < d) {
+                            float w8[8];
+                            load8(wr + i, w8);
+                            sv[u] = dot8(hr[u][c], w8, sv[u]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const float t = wave_sum(sv[u]);
+                if (lane == j) z[u] = t;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (!small[u]) continue;
+            const bool on = lane < n[u];
+            const float m = wave_max(on ? z[u] : -INFINITY);
+            const float se = wave_sum(on ? expf(z[u] - m) : 0.f);
+            const float lse = m + logf(se);
+            uint64_t key = on ? make_key(a[u] + (z[u] - lse), kk[u], tk[u]) : 0ull;
+            if (n[u] > Kc) key = wave_sort_desc(key);
+            if (lane < Kc) qkeys[kk[u] * Kc + lane] = key;
+        }
+    }
+    __syncthreads();
+
+    // phase 2: wide rows and bitmap rows, the whole block per beam
+    const int nb = nbig;
+    for (int i = 0; i < nb; ++i) {
+        const int k = big[i];
+        const int64_t b = (int64_t)q * K + k;
+        const int32_t r = beam_rows[b];
+        const float a = acc[b];
+        const uint32_t e0 = st.row_ptr[r];
+        const int n = (int)(st.row_ptr[r + 1] - e0);
+        block_fill_tokens<NT>(st, r, e0, n, tok_s, red_i);
+        for (int x = tid; x < d; x += NT) h_s[x] = to_f32(hidden[b * d + x]);
+        __syncthreads();
+        block_scores<DT, NT>(h_s, W, d, tok_s, n, z_s);
+        __syncthreads();
+        const float lse = block_lse<NT>(z_s, n, red_f);
+        auto keyf = [&](int j) { return make_key(a + (z_s[j] - lse), k, (int)tok_s[j]); };
+        uint64_t* slot = qkeys + k * Kc;
+        if (n <= Kc) {
+            for (int j = tid; j < Kc; j += NT) slot[j] = j < n ? keyf(j) : 0ull;
+        } else {
+            block_select_top<NT>(n, Kc, keyf, slot, stage, list, red_i, &bcast);
+        }
+        __syncthreads();
+    }
+
+    // phase 3: the query's K best
+    block_select_top<NT>(K * Kc, K, [&](int j) { return qkeys[j]; }, best, stage, list, red_i, &bcast);
+    __syncthreads();
+    for (int i = tid; i < K; i += NT) emit(st, q, K, i, best[i], beam_rows, out_tok, out_par, out_rows, out_logp);
+}
+
+// ---- dense step: per-beam expansion and per-query merge --------------------
+
+constexpr int kBM = 128, kBN = 128, kBK = 32, kLDP = kBK + 8;
+constexpr int kSplitMax = 8;   // k-slices for steps with few live beams
+constexpr int kSplitRows = 2 * kBM;
+constexpr int kCUs = 256;
+
+// Number of k-slices the full-codebook product uses for n_live live beams:
+// more than one only when the tiles alone would leave most compute units idle.
+// The slices' partial sums are added in slice order by the consumer.
+__host__ __device__ inline int gemm_split(int n_live, int V, int d) {
+    const int tiles = ((n_live + kBM - 1) / kBM) * ((V + kBN - 1) / kBN);
+    int s = 1;
+    if (n_live > kSplitRows) return 1;
+    while (s < kSplitMax && tiles * s * 2 <= kCUs && (d / kBK) % (s * 2) == 0) s *= 2;
+    return s;
+}
+
+__host__ __device__ inline int gemm_grid(int R, int V) {
+    const int nt = (V + kBN - 1) / kBN;
+    const int full = ((R + kBM - 1) / kBM) * nt;
+    const int split = kSplitMax * ((kSplitRows + kBM - 1) / kBM) * nt;
+    return full > split ? full : split;
+}
+
+
+template <typename DT, bool DENSE, int NT>
+__global__ __launch_bounds__(NT) void k_beam_expand(StepDev st, int K, int Kc, int d,
+                                                    const DT* __restrict__ hidden, const DT* __restrict__ W,
+                                                    const float* __restrict__ Z, const float* __restrict__ Zp,
+                                                    int64_t ldz, const int32_t* __restrict__ n_live,
+                                                    const int32_t* __restrict__ ci_of, int split_ok,
+                                                    const int32_t* __restrict__ beam_rows,
+                                                    const float* __restrict__ acc, uint64_t* __restrict__ keys_out) {
+    auto split_of = [&](const int32_t* nl) { return split_ok ? gemm_split(*nl, (int)ldz, d) : 1; };
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ float red_f[NT / kWave];
+    __shared__ int red_i[NT / kWave];
+    __shared__ uint64_t bcast;
+    const ExpandLds lay = expand_lds(st.S, d, DENSE, NT);
+    uint64_t* stage = reinterpret_cast<uint64_t*>(smem + lay.stage);
+    float* z_s = reinterpret_cast<float*>(smem + lay.z);
+    int* list = reinterpret_cast<int*>(smem + lay.list);
+    float* h_s = reinterpret_cast<float*>(smem + lay.h);
+    uint16_t* tok_s = reinterpret_cast<uint16_t*>(smem + lay.tok);
+
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    uint64_t* out = keys_out + (int64_t)b * Kc;
+    const int32_t r = beam_rows[b];
+    const float a = acc[b];
+    if (!beam_live(st, r, a)) {
+        for (int j = tid; j < Kc; j += NT) out[j] = 0;
+        return;
+    }
+    const uint32_t e0 = st.row_ptr[r];
+    const int n = (int)(st.row_ptr[r + 1] - e0);
+    block_fill_tokens<NT>(st, r, e0, n, tok_s, red_i);
+    if (!DENSE)
+        for (int i = tid; i < d; i += NT) h_s[i] = to_f32(hidden[(int64_t)b * d + i]);
+    __syncthreads();
+    if (DENSE) {
+        const int split = split_of(n_live);
+        if (split == 1) {
+            const float* zb = Z + (int64_t)b * ldz;
+            for (int j = tid; j < n; j += NT) z_s[j] = zb[tok_s[j]];
+        } else {
+            const float* zb = Zp + (int64_t)ci_of[b] * ldz;
+            for (int j = tid; j < n; j += NT) {
+                float z = 0.f;
+                for (int x = 0; x < split; ++x) z += zb[(int64_t)x * kSplitRows * ldz + tok_s[j]];
+                z_s[j] = z;
+            }
+        }
+    } else {
+        block_scores<DT, NT>(h_s, W, d, tok_s, n, z_s);
+    }
+    __syncthreads();
+    const float lse = block_lse<NT>(z_s, n, red_f);
+    const int parent = b % K;
+    auto keyf = [&](int j) { return make_key(a + (z_s[j] - lse), parent, (int)tok_s[j]); };
+    if (n <= Kc) {
+        for (int j = tid; j < Kc; j += NT) out[j] = j < n ? keyf(j) : 0ull;
+        return;
+    }
+    block_select_top<NT>(n, Kc, keyf, out, stage, list, red_i, &bcast);
+}
+
 template <int NT>
-__global__ __launch_bounds__(NT) void k_query_merge(StepDev st, int K, int Kc, int P2,
-                                                    const uint64_t* __restrict__ keys,
+__global__ __launch_bounds__(NT) void k_query_merge(StepDev st, int K, int Kc, const uint64_t* __restrict__ keys,
                                                     const int32_t* __restrict__ beam_rows,
                                                     int32_t* __restrict__ out_tok, int32_t* __restrict__ out_par,
                                                     int32_t* __restrict__ out_rows, float* __restrict__ out_logp) {
     extern __shared__ __align__(16) unsigned char smem[];
-    uint64_t* sk = reinterpret_cast<uint64_t*>(smem);
+    __shared__ int red_i[NT / kWave];
+    __shared__ uint64_t bcast;
+    __shared__ uint64_t best[kWave];
+    uint64_t* stage = reinterpret_cast<uint64_t*>(smem);
+    int* list = reinterpret_cast<int*>(smem + NT * 8);
     const int q = blockIdx.x;
-    const int M = K * Kc;
-    const uint64_t* src = keys + (int64_t)q * M;
-    for (int i = threadIdx.x; i < P2; i += NT) sk[i] = i < M ? src[i] : 0ull;
+    const uint64_t* src = keys + (int64_t)q * K * Kc;
+    block_select_top<NT>(K * Kc, K, [&](int j) { return src[j]; }, best, stage, list, red_i, &bcast);
     __syncthreads();
-    bitonic_sort_desc<NT>(sk, P2);
-    for (int i = threadIdx.x; i < K; i += NT) {
-        const int64_t o = (int64_t)q * K + i;
-        const uint64_t key = sk[i];
-        if (key == 0ull) {
-            out_tok[o] = -1;
-            out_par[o] = -1;
-            out_rows[o] = -1;
-            out_logp[o] = -INFINITY;
-            continue;
-        }
-        const int parent = 1023 - (int)((key >> 16) & 1023u);
-        const int token = 65535 - (int)(key & 0xFFFFu);
-        const int32_t r = beam_rows[(int64_t)q * K + parent];
-        out_tok[o] = token;
-        out_par[o] = parent;
-        out_rows[o] = edge_of(st, r, token);
-        out_logp[o] = score_from_order_bits((uint32_t)(key >> 32));
-    }
+    for (int i = threadIdx.x; i < K; i += NT)
+        emit(st, q, K, i, best[i], beam_rows, out_tok, out_par, out_rows, out_logp);
 }
 
-// ---- full-codebook scores (dense path) ------------------------------------
+// ---- full-codebook scores of the live beams (dense path) ------------------
+
+// Compact list of the live beam slots (ascending), their count, and the
+// compact index of every slot (-1 when dead).
+template <int NT>
+__global__ __launch_bounds__(NT) void k_live_rows(StepDev st, int R, const int32_t* __restrict__ beam_rows,
+                                                  const float* __restrict__ acc, int32_t* __restrict__ live,
+                                                  int32_t* __restrict__ n_live, int32_t* __restrict__ ci_of) {
+    __shared__ int red_i[NT / kWave];
+    int base = 0;
+    for (int b0 = 0; b0 < R; b0 += NT) {
+        const int b = b0 + threadIdx.x;
+        const int on = b < R && beam_live(st, beam_rows[b], acc[b]);
+        int tot;
+        const int pos = base + block_exclusive_scan<NT>(on, red_i, &tot);
+        if (on) live[pos] = b;
+        if (b < R) ci_of[b] = on ? pos : -1;
+        base += tot;
+    }
+    if (threadIdx.x == 0) *n_live = base;
+}
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 64, kLDP = kBK + 8;
-
-// Z[R][V] (row pitch ldz) = H[R][d] * W[V][d]^T, bf16 in, float32 accumulate on
-// MFMA 32x32x16.  256 threads = 4 waves, each a 64x64 quarter of the tile.
-__global__ __launch_bounds__(256) void k_gemm_bf16(int R, int V, int d, const uint16_t* __restrict__ H,
+// Scores of the live beams against the whole codebook, bf16 in, float32
+// accumulate on MFMA 32x32x16: one 128x128 tile (4 waves of 64x64) of one
+// k-slice per workgroup; LDS double buffered with the next k-tile prefetched
+// into registers.  With one slice, Z[beam][v]; with several, Zp[slice][compact
+// row][v].  Consecutive tiles on one XCD share W columns.
+__global__ __launch_bounds__(256) void k_gemm_bf16(int V, int d, const int32_t* __restrict__ live,
+                                                   const int32_t* __restrict__ n_live, const uint16_t* __restrict__ H,
                                                    const uint16_t* __restrict__ W, float* __restrict__ Z,
-                                                   int64_t ldz) {
-    __shared__ __align__(16) uint16_t As[kBM * kLDP];
-    __shared__ __align__(16) uint16_t Bs[kBN * kLDP];
-    const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+                                                   float* __restrict__ Zp, int64_t ldz) {
+    __shared__ __align__(16) uint16_t As[2][kBM * kLDP];
+    __shared__ __align__(16) uint16_t Bs[2][kBN * kLDP];
+    __shared__ int rows_s[kBM];
+    const int nl = *n_live;
+    const int split = gemm_split(nl, V, d);
+    const int mt = (nl + kBM - 1) / kBM, nt = (V + kBN - 1) / kBN;
+    const int N = mt * nt * split;
+    const int L = blockIdx.x;
+    if (L >= N) return;
+    const int full = (N / 8) * 8;
+    const int lin = L < full ? (L % 8) * (full / 8) + L / 8 : L;
+    const int zs = lin % split, tile = lin / split;
+    const int m0 = (tile % mt) * kBM, n0 = (tile / mt) * kBN;
+    const int klen = d / split, kbeg = zs * klen;
+
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (tid < kBM) rows_s[tid] = m0 + tid < nl ? live[m0 + tid] : -1;
+    __syncthreads();
     const int wm = (wv >> 1) * 64, wn = (wv & 1) * 64;
+
+    // this thread's two 16-byte chunks of each k-tile of A and B
+    int crow[2], ccol[2];
+    const uint16_t* pa[2];
+    const uint16_t* pb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int c = tid + u * 256;
+        crow[u] = c / (kBK / 8);
+        ccol[u] = (c % (kBK / 8)) * 8;
+        const int hb = rows_s[crow[u]];
+        pa[u] = hb >= 0 ? H + (int64_t)hb * d + kbeg + ccol[u] : nullptr;
+        pb[u] = n0 + crow[u] < V ? W + (int64_t)(n0 + crow[u]) * d + kbeg + ccol[u] : nullptr;
+    }
+    uint4 ra[2], rb[2];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            ra[u] = pa[u] ? *reinterpret_cast<const uint4*>(pa[u] + k0) : make_uint4(0, 0, 0, 0);
+            rb[u] = pb[u] ? *reinterpret_cast<const uint4*>(pb[u] + k0) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            *reinterpret_cast<uint4*>(&As[buf][crow[u] * kLDP + ccol[u]]) = ra[u];
+            *reinterpret_cast<uint4*>(&Bs[buf][crow[u] * kLDP + ccol[u]]) = rb[u];
+        }
+    };
+
     f32x16_t acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -367,67 +746,71 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(int R, int V, int d, const ui
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    for (int k0 = 0; k0 < d; k0 += kBK) {
-        for (int c = tid; c < kBM * kBK / 8; c += 256) {
-            const int rr = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
-            uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
-            if (m0 + rr < R) va = *reinterpret_cast<const uint4*>(H + (int64_t)(m0 + rr) * d + k0 + kc);
-            if (n0 + rr < V) vb = *reinterpret_cast<const uint4*>(W + (int64_t)(n0 + rr) * d + k0 + kc);
-            *reinterpret_cast<uint4*>(As + rr * kLDP + kc) = va;
-            *reinterpret_cast<uint4*>(Bs + rr * kLDP + kc) = vb;
-        }
-        __syncthreads();
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    const int nk = klen / kBK;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) fetch((kt + 1) * kBK);
 #pragma unroll
         for (int kk = 0; kk < kBK; kk += 16) {
             bf16x8_t av[2], bv[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                uint4 u = *reinterpret_cast<const uint4*>(As + (wm + i * 32 + (lane & 31)) * kLDP + kk + (lane >> 5) * 8);
-                av[i] = __builtin_bit_cast(bf16x8_t, u);
-            }
+            for (int i = 0; i < 2; ++i)
+                av[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                                                         &As[buf][(wm + i * 32 + (lane & 31)) * kLDP + kk + (lane >> 5) * 8]));
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                uint4 u = *reinterpret_cast<const uint4*>(Bs + (wn + j * 32 + (lane & 31)) * kLDP + kk + (lane >> 5) * 8);
-                bv[j] = __builtin_bit_cast(bf16x8_t, u);
-            }
+            for (int j = 0; j < 2; ++j)
+                bv[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                                                         &Bs[buf][(wn + j * 32 + (lane & 31)) * kLDP + kk + (lane >> 5) * 8]));
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
         }
+        if (kt + 1 < nk) stash(buf ^ 1);
         __syncthreads();
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int e = 0; e < 16; ++e) {
+            const int rr = wm + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+            const int hb = rows_s[rr];
+            if (hb < 0) continue;
+            float* dst = split == 1 ? Z + (int64_t)hb * ldz : Zp + ((int64_t)zs * kSplitRows + m0 + rr) * ldz;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = m0 + wm + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+            for (int j = 0; j < 2; ++j) {
                 const int col = n0 + wn + j * 32 + (lane & 31);
-                if (row < R && col < V) Z[(int64_t)row * ldz + col] = acc[i][j][e];
+                if (col < V) dst[col] = acc[i][j][e];
             }
+        }
 }
 
-// float32 full-codebook scores: 16x16 output tile per workgroup, one output
-// per thread, the k loop in ascending order.
-__global__ __launch_bounds__(256) void k_gemm_f32(int R, int V, int d, const float* __restrict__ H,
+// float32 full-codebook scores of the live beams: 16x16 output tile per
+// workgroup, one output per thread, the k loop in ascending order.
+__global__ __launch_bounds__(256) void k_gemm_f32(int V, int d, const int32_t* __restrict__ live,
+                                                  const int32_t* __restrict__ n_live, const float* __restrict__ H,
                                                   const float* __restrict__ W, float* __restrict__ Z, int64_t ldz) {
     __shared__ float As[16][17], Bs[16][17];
+    const int nl = *n_live;
+    if ((int)blockIdx.y * 16 >= nl) return;
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    const int row = blockIdx.y * 16 + ty, col = blockIdx.x * 16 + tx;
+    const int ri = blockIdx.y * 16 + ty, col = blockIdx.x * 16 + tx;
+    const int ar = blockIdx.y * 16 + ty < nl ? live[blockIdx.y * 16 + ty] : -1;
+    const int bc = blockIdx.x * 16 + ty;
     float s = 0.f;
     for (int k0 = 0; k0 < d; k0 += 16) {
-        const int ar = blockIdx.y * 16 + ty, bc = blockIdx.x * 16 + ty;
-        As[ty][tx] = (ar < R && k0 + tx < d) ? H[(int64_t)ar * d + k0 + tx] : 0.f;
+        As[ty][tx] = (ar >= 0 && k0 + tx < d) ? H[(int64_t)ar * d + k0 + tx] : 0.f;
         Bs[ty][tx] = (bc < V && k0 + tx < d) ? W[(int64_t)bc * d + k0 + tx] : 0.f;
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < 16; ++k) s = fmaf(As[ty][k], Bs[tx][k], s);
         __syncthreads();
     }
-    if (row < R && col < V) Z[(int64_t)row * ldz + col] = s;
+    if (ri < nl && col < V) Z[(int64_t)live[ri] * ldz + col] = s;
 }
 
 // ---- stand-in model between steps (decode only) ---------------------------
@@ -507,24 +890,59 @@ __global__ void k_backtrace(int R, int K, int L, const int32_t* __restrict__ his
 
 }  // namespace
 
-int expand_threads(const StepDev& st) { return (st.S <= 8 && st.store == CB_STORE_CSR) ? 64 : 256; }
+// ---- launchers -----------------------------------------------------------------
+
+int expand_threads(const StepDev&) { return kExpandThreads; }
+
+int query_threads(int K) { return K >= 16 ? 1024 : 512; }
+
+size_t expand_lds_bytes(int S, int d, bool dense) { return (size_t)expand_lds(S, d, dense, kExpandThreads).total; }
+
+size_t query_lds_bytes(int S, int K, int Kc, int d) {
+    return (size_t)query_lds(S, K, Kc, d, query_threads(K)).total;
+}
+
+hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int Kc, int d, const void* hidden,
+                             const void* W, const int32_t* beam_rows, const float* acc, int32_t* tok, int32_t* par,
+                             int32_t* rows, float* logp, hipStream_t s) {
+    if (Q <= 0) return hipSuccess;
+    const int NT = query_threads(K);
+    const QueryLds lay = query_lds(st.S, K, Kc, d, NT);
+    const int CH = (d + kWave * 8 - 1) / (kWave * 8);
+#define CB_QUERY(DT, NTV, CHV)                                                                           \
+    hipLaunchKernelGGL((k_step_query<DT, NTV, CHV>), dim3(Q), dim3(NTV), lay.total, s, st, K, Kc, d,     \
+                       (const DT*)hidden, (const DT*)W, beam_rows, acc, tok, par, rows, logp)
+#define CB_QUERY_NT(DT, CHV) \
+    do { if (NT == 1024) CB_QUERY(DT, 1024, CHV); else CB_QUERY(DT, 512, CHV); } while (0)
+    if (dt == CB_BF16) {
+        if (CH <= 1) CB_QUERY_NT(uint16_t, 1);
+        else if (CH == 2) CB_QUERY_NT(uint16_t, 2);
+        else CB_QUERY_NT(uint16_t, 4);
+    } else {
+        if (CH <= 1) CB_QUERY_NT(float, 1);
+        else if (CH == 2) CB_QUERY_NT(float, 2);
+        else CB_QUERY_NT(float, 4);
+    }
+#undef CB_QUERY_NT
+#undef CB_QUERY
+    return hipGetLastError();
+}
 
 hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R, int K, int Kc, int d,
-                              const void* hidden, const void* W, const float* Z, int64_t ldz,
-                              const int32_t* beam_rows, const float* acc, uint64_t* keys, hipStream_t s) {
+                              const void* hidden, const void* W, const float* Z, const float* Zp, int64_t ldz,
+                              const int32_t* n_live, const int32_t* ci_of, const int32_t* beam_rows,
+                              const float* acc, uint64_t* keys, hipStream_t s) {
     if (R <= 0) return hipSuccess;
-    const ExpandLds lay = expand_lds(st.S, Kc, d, dense);
-    const bool narrow = expand_threads(st) == 64;
-    const dim3 grid(R);
-#define CB_EXPAND(DT, DENSE, NT)                                                                      \
-    hipLaunchKernelGGL((k_beam_expand<DT, DENSE, NT>), grid, dim3(NT), lay.total, s, st, K, Kc, d,   \
-                       (const DT*)hidden, (const DT*)W, Z, ldz, beam_rows, acc, keys)
+    const ExpandLds lay = expand_lds(st.S, d, dense, kExpandThreads);
+    const int split_ok = dt == CB_BF16 ? 1 : 0;
+#define CB_EXPAND(DT, DENSE)                                                                                     \
+    hipLaunchKernelGGL((k_beam_expand<DT, DENSE, kExpandThreads>), dim3(R), dim3(kExpandThreads), lay.total, s, \
+                       st, K, Kc, d, (const DT*)hidden, (const DT*)W, Z, Zp, ldz, n_live, ci_of, split_ok,        \
+                       beam_rows, acc, keys)
     if (dt == CB_BF16) {
-        if (dense) { if (narrow) CB_EXPAND(uint16_t, true, 64); else CB_EXPAND(uint16_t, true, 256); }
-        else { if (narrow) CB_EXPAND(uint16_t, false, 64); else CB_EXPAND(uint16_t, false, 256); }
+        if (dense) CB_EXPAND(uint16_t, true); else CB_EXPAND(uint16_t, false);
     } else {
-        if (dense) { if (narrow) CB_EXPAND(float, true, 64); else CB_EXPAND(float, true, 256); }
-        else { if (narrow) CB_EXPAND(float, false, 64); else CB_EXPAND(float, false, 256); }
+        if (dense) CB_EXPAND(float, true); else CB_EXPAND(float, false);
     }
 #undef CB_EXPAND
     return hipGetLastError();
@@ -534,26 +952,37 @@ hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uin
                               const int32_t* beam_rows, int32_t* tok, int32_t* par, int32_t* rows, float* logp,
                               hipStream_t s) {
     if (Q <= 0) return hipSuccess;
-    const int P2 = next_pow2(K * Kc);
-    hipLaunchKernelGGL((k_query_merge<kMergeThreads>), dim3(Q), dim3(kMergeThreads), (size_t)P2 * 8, s, st, K, Kc, P2, keys, beam_rows,
-                       tok, par, rows, logp);
+    const size_t lds = (size_t)kMergeThreads * 8 + (size_t)K * Kc * 4;
+    hipLaunchKernelGGL((k_query_merge<kMergeThreads>), dim3(Q), dim3(kMergeThreads), lds, s, st, K, Kc, keys,
+                       beam_rows, tok, par, rows, logp);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_scores(cb_dtype dt, int R, int V, int d, const void* H, const void* W, float* Z,
-                              hipStream_t s) {
+hipError_t launch_live_rows(const StepDev& st, int R, const int32_t* beam_rows, const float* acc, int32_t* live,
+                            int32_t* n_live, int32_t* ci_of, hipStream_t s) {
+    hipLaunchKernelGGL((k_live_rows<1024>), dim3(1), dim3(1024), 0, s, st, R, beam_rows, acc, live, n_live, ci_of);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_scores(cb_dtype dt, int R, int V, int d, const int32_t* live, const int32_t* n_live,
+                              const void* H, const void* W, float* Z, float* Zp, hipStream_t s) {
     if (R <= 0) return hipSuccess;
     if (dt == CB_BF16) {
-        dim3 grid((V + kBN - 1) / kBN, (R + kBM - 1) / kBM);
-        hipLaunchKernelGGL(k_gemm_bf16, grid, dim3(256), 0, s, R, V, d, (const uint16_t*)H, (const uint16_t*)W, Z,
-                           (int64_t)V);
+        hipLaunchKernelGGL(k_gemm_bf16, dim3(gemm_grid(R, V)), dim3(256), 0, s, V, d, live, n_live,
+                           (const uint16_t*)H, (const uint16_t*)W, Z, Zp, (int64_t)V);
     } else {
         dim3 grid((V + 15) / 16, (R + 15) / 16);
-        hipLaunchKernelGGL(k_gemm_f32, grid, dim3(256), 0, s, R, V, d, (const float*)H, (const float*)W, Z,
-                           (int64_t)V);
+        hipLaunchKernelGGL(k_gemm_f32, grid, dim3(256), 0, s, V, d, live, n_live, (const float*)H, (const float*)W,
+                           Z, (int64_t)V);
     }
     return hipGetLastError();
 }
+
+int gemm_blocks(cb_dtype dt, int R, int V) {
+    return dt == CB_BF16 ? gemm_grid(R, V) : ((V + 15) / 16) * ((R + 15) / 16);
+}
+
+size_t split_scores_floats(int V) { return (size_t)kSplitMax * kSplitRows * (size_t)V; }
 
 hipError_t launch_decode_init(int Q, int K, int d, cb_dtype dt, const float* q, float* s_out, void* h_out,
                               int32_t* rows, float* acc, hipStream_t st) {
@@ -587,7 +1016,5 @@ hipError_t launch_backtrace(int R, int K, int L, const int32_t* hist_tok, const 
     hipLaunchKernelGGL(k_backtrace, dim3((R + 255) / 256), dim3(256), 0, s, R, K, L, hist_tok, hist_par, seqs);
     return hipGetLastError();
 }
-
-size_t expand_lds_bytes(int S, int Kc, int d, bool dense) { return (size_t)expand_lds(S, Kc, d, dense).total; }
 
 }  // namespace cb

@@ -122,8 +122,8 @@ void cb_free_index(cb_index* idx);
  * and element type dtype (of W and of the hidden vectors).  Nothing is
  * allocated later by cb_step / cb_decode (FlashTrie App. D: per-batch state
  * allocated once).  The index must stay alive while the plan exists.
- * Errors: CB_EINVAL, CB_ECAPACITY (K > 1024 or a step too wide for the
- * per-beam selection), CB_ENOMEM, CB_EHIP. */
+ * Errors: CB_EINVAL, CB_ECAPACITY (K > 64, or a step too wide for the
+ * per-workgroup LDS of the step kernels), CB_ENOMEM, CB_EHIP. */
 cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_dtype dtype, cb_plan** out);
 
 /* Force the scoring path of step t (tests run both ways).  CB_PATH_AUTO
@@ -189,7 +189,9 @@ typedef enum {
     CB_KERNEL_GEMM_F32 = 1,       /* full-codebook scores, float32 */
     CB_KERNEL_EXPAND_SPARSE = 2,  /* slot fill + gather-dot + softmax + per-beam top-K */
     CB_KERNEL_EXPAND_DENSE = 3,   /* slot fill + column gather + softmax + per-beam top-K */
-    CB_KERNEL_MERGE = 4           /* per-query top-K and next rows */
+    CB_KERNEL_MERGE = 4,          /* per-query top-K and next rows (after the dense expansion) */
+    CB_KERNEL_STEP_QUERY = 5,     /* the whole sparse step, one workgroup per query */
+    CB_KERNEL_LIVE_ROWS = 6       /* list of live beams for the full-codebook scores */
 } cb_kernel;
 
 typedef struct {

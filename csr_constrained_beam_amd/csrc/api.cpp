@@ -216,6 +216,7 @@ cb_status cb_build_index(const int32_t* sids, int64_t n_items, int32_t L, int32_
             st = dev_alloc(&T.d_row_ptr, T.row_ptr.size(), "row_ptr");
             if (st == CB_OK) st = dev_alloc(&T.d_tok, T.tok.size(), "tokens");
             if (st == CB_OK) st = dev_alloc(&T.d_bits, T.bits.size(), "bitmap");
+            if (st == CB_OK) st = dev_alloc(&T.d_rank, T.rank.size(), "rank directory");
             hipError_t e = hipSuccess;
             if (st == CB_OK && T.d_row_ptr)
                 e = hipMemcpy(T.d_row_ptr, T.row_ptr.data(), T.row_ptr.size() * 4, hipMemcpyHostToDevice);
@@ -223,6 +224,8 @@ cb_status cb_build_index(const int32_t* sids, int64_t n_items, int32_t L, int32_
                 e = hipMemcpy(T.d_tok, T.tok.data(), T.tok.size() * 2, hipMemcpyHostToDevice);
             if (st == CB_OK && e == hipSuccess && T.d_bits)
                 e = hipMemcpy(T.d_bits, T.bits.data(), T.bits.size() * 4, hipMemcpyHostToDevice);
+            if (st == CB_OK && e == hipSuccess && T.d_rank)
+                e = hipMemcpy(T.d_rank, T.rank.data(), T.rank.size() * 2, hipMemcpyHostToDevice);
             if (st == CB_OK && e != hipSuccess) st = hip_fail("cb_build_index: upload", e);
             if (st != CB_OK) {
                 cb_free_index(idx);
@@ -231,6 +234,7 @@ cb_status cb_build_index(const int32_t* sids, int64_t n_items, int32_t L, int32_
             std::vector<uint32_t>().swap(T.row_ptr);
             std::vector<uint16_t>().swap(T.tok);
             std::vector<uint32_t>().swap(T.bits);
+            std::vector<uint16_t>().swap(T.rank);
         }
     }
     *out = idx;
@@ -331,6 +335,7 @@ void cb_free_index(cb_index* idx) {
             dev_free(T.d_row_ptr);
             dev_free(T.d_tok);
             dev_free(T.d_bits);
+            dev_free(T.d_rank);
         }
     }
     delete idx;

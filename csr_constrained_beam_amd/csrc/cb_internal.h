@@ -22,6 +22,7 @@ struct StepDev {
     const uint32_t* row_ptr;  // [n_rows + 1]
     const uint16_t* tok;      // CSR: token of every edge [n_edges]; nullptr for bitmap steps
     const uint32_t* bits;     // bitmap: [n_rows][words], bit v of a row set iff token v is valid
+    const uint16_t* rank;     // bitmap: [n_rows][words], set bits of the row in the words before
     int64_t n_rows;
     int32_t words;            // 32-bit words per bitmap row = ceil(V / 32)
     int32_t store;            // CB_STORE_CSR or CB_STORE_BITMAP
@@ -37,13 +38,15 @@ struct StepTable {
     std::vector<uint32_t> row_ptr;
     std::vector<uint16_t> tok;
     std::vector<uint32_t> bits;
+    std::vector<uint16_t> rank;
     // device copies
     uint32_t* d_row_ptr = nullptr;
     uint16_t* d_tok = nullptr;
     uint32_t* d_bits = nullptr;
+    uint16_t* d_rank = nullptr;
 
     StepDev dev(int32_t words) const {
-        return StepDev{d_row_ptr, d_tok, d_bits, n_rows, words, store, S};
+        return StepDev{d_row_ptr, d_tok, d_bits, d_rank, n_rows, words, store, S};
     }
 };
 
@@ -103,6 +106,7 @@ namespace cb {
 int expand_threads(const StepDev& st);
 int query_threads(int K);
 size_t expand_lds_bytes(int S, int d, bool dense);
+int expand_bitmap_max_v();
 size_t query_lds_bytes(int S, int K, int Kc, int d);
 int gemm_blocks(cb_dtype dt, int R, int V);
 

@@ -159,7 +159,7 @@ cb_status build_impl(const int32_t* sids, int64_t n, int32_t L, int32_t V, int32
         int32_t S = 0;
         for (int64_t k = 0; k < nr; ++k) S = std::max<int32_t>(S, (int32_t)(T.row_ptr[(size_t)k + 1] - T.row_ptr[(size_t)k]));
         T.S = S;
-        const int64_t bitmap_bytes = nr * (int64_t)idx->words * 4;
+        const int64_t bitmap_bytes = nr * (int64_t)idx->words * 6;  // bits + rank directory
         const int64_t csr_bytes = ne * 2;
         bool bitmap = store == CB_STORE_BITMAP ||
                       (store == CB_STORE_AUTO && bitmap_bytes < csr_bytes);
@@ -175,6 +175,19 @@ cb_status build_impl(const int32_t* sids, int64_t n, int32_t L, int32_t V, int32
                     uint32_t v = T.tok[x];
                     T.bits[(size_t)(k * idx->words + (v >> 5))] |= 1u << (v & 31);
                 }
+            try {
+                T.rank.assign((size_t)(nr * idx->words), 0);
+            } catch (...) {
+                st = CB_ENOMEM;
+                return;
+            }
+            for (int64_t k = 0; k < nr; ++k) {
+                uint32_t c = 0;
+                for (int w = 0; w < idx->words; ++w) {
+                    T.rank[(size_t)(k * idx->words + w)] = (uint16_t)c;
+                    c += (uint32_t)__builtin_popcount(T.bits[(size_t)(k * idx->words + w)]);
+                }
+            }
             std::vector<uint16_t>().swap(T.tok);
             T.store = CB_STORE_BITMAP;
             T.bytes = (nr + 1) * 4 + bitmap_bytes;

@@ -127,6 +127,77 @@ __device__ __forceinline__ uint64_t wave_merge_top(uint64_t a, uint64_t b) {
     return c;
 }
 
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Bitonic sort of the wave's 64 values (one per lane), descending across lanes.
+__device__ __forceinline__ uint32_t wave_sort_desc32(uint32_t v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)v, j);
+            const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
+            v = take_max ? (v > o ? v : o) : (v < o ? v : o);
+        }
+    return v;
+}
+
+constexpr int kWaveListCap = 256;
+
+// The Kc (<= 64) largest keys of the wave, descending in lanes 0..Kc-1 (0 when
+// fewer).  Lane l owns M candidates; score(i) is the high half of candidate i's
+// key (the order bits of its score, 0 = empty) and key(i) the full key.  tau =
+// the Kc-th largest lane maximum of the scores bounds the answer from below
+// (every key of the answer has a score >= tau); the candidates with score >=
+// tau get their full keys compacted (ballot order) into the wave's LDS list wl
+// [kWaveListCap], a window at a time, and are sorted with wave64 bitonic
+// networks.  No block barriers.
+template <int M, class ScoreF, class KeyF>
+__device__ uint64_t wave_top(int Kc, ScoreF score, KeyF key, uint64_t* wl) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) mx = max(mx, score(i));
+    uint32_t tau = (uint32_t)__shfl((int)wave_sort_desc32(mx), Kc - 1);
+    if (tau == 0) tau = 1;
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) cnt += score(i) >= tau;
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    const int total = __shfl(incl, kWave - 1);
+    uint64_t best = 0;
+    bool first = true;
+    for (int s0 = 0; s0 < total; s0 += kWaveListCap) {
+        int pos = incl - cnt;
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            if (score(i) >= tau) {
+                if (pos >= s0 && pos < s0 + kWaveListCap) wl[pos - s0] = key(i);
+                ++pos;
+            }
+        }
+        wave_lds_sync();
+        const int w = min(kWaveListCap, total - s0);
+        for (int c0 = 0; c0 < w; c0 += kWave) {
+            const uint64_t v = wave_sort_desc(c0 + lane < w ? wl[c0 + lane] : 0ull);
+            best = first ? v : wave_merge_top(best, v);
+            first = false;
+        }
+        wave_lds_sync();
+    }
+    return best;
+}
+
 // Block reductions in a fixed order (deterministic); every thread gets the result.
 template <int NT>
 __device__ float block_max(float v, float* red) {
@@ -282,43 +353,39 @@ __device__ void block_fill_tokens(const StepDev& st, int32_t r, uint32_t e0, int
 }
 
 // a2 (sparse) for one beam, whole block: z_s[j] = <h, W_t[tok_s[j]]>, one wave
-// per token, two tokens in flight per wave.
+// per token, up to four tokens in flight per wave.
 template <typename DT, int NT>
 __device__ void block_scores(const float* h_s, const DT* __restrict__ W, int d, const uint16_t* tok_s, int n,
                              float* z_s) {
     const int lane = threadIdx.x & (kWave - 1);
     constexpr int NW = NT / kWave;
-    int j = threadIdx.x / kWave;
-    for (; j + NW < n; j += 2 * NW) {
-        const DT* w0 = W + (int64_t)tok_s[j] * d;
-        const DT* w1 = W + (int64_t)tok_s[j + NW] * d;
-        float s0 = 0.f, s1 = 0.f;
+    constexpr int U = 4;
+    for (int j0 = threadIdx.x / kWave; j0 < n; j0 += U * NW) {
+        const DT* wr[U];
+        float s[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * NW;
+            wr[u] = W + (int64_t)tok_s[j < n ? j : j0] * d;
+            s[u] = 0.f;
+        }
         for (int i = lane * 8; i < d; i += kWave * 8) {
-            float a[8], b[8], h[8];
-            load8(w0 + i, a);
-            load8(w1 + i, b);
+            float h[8];
             load8(h_s + i, h);
-            s0 = dot8(h, a, s0);
-            s1 = dot8(h, b, s1);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (j0 + u * NW < n) {
+                    float w8[8];
+                    load8(wr[u] + i, w8);
+                    s[u] = dot8(h, w8, s[u]);
+                }
+            }
         }
-        s0 = wave_sum(s0);
-        s1 = wave_sum(s1);
-        if (lane == 0) {
-            z_s[j] = s0;
-            z_s[j + NW] = s1;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float t = wave_sum(s[u]);
+            if (lane == 0 && j0 + u * NW < n) z_s[j0 + u * NW] = t;
         }
-    }
-    for (; j < n; j += NW) {
-        const DT* w0 = W + (int64_t)tok_s[j] * d;
-        float s0 = 0.f;
-        for (int i = lane * 8; i < d; i += kWave * 8) {
-            float a[8], h[8];
-            load8(w0 + i, a);
-            load8(h_s + i, h);
-            s0 = dot8(h, a, s0);
-        }
-        s0 = wave_sum(s0);
-        if (lane == 0) z_s[j] = s0;
     }
 }
 
@@ -345,12 +412,8 @@ __device__ int32_t edge_of(const StepDev& st, int32_t r, int token) {
         }
         return (int32_t)(e0 + lo);
     }
-    const uint32_t* rb = st.bits + (int64_t)r * st.words;
-    const int w = token >> 5;
-    uint32_t c = 0;
-    for (int i = 0; i < w; ++i) c += __popc(rb[i]);
-    c += __popc(rb[w] & ((1u << (token & 31)) - 1u));
-    return (int32_t)(e0 + c);
+    const int64_t x = (int64_t)r * st.words + (token >> 5);
+    return (int32_t)(e0 + st.rank[x] + __popc(st.bits[x] & ((1u << (token & 31)) - 1u)));
 }
 
 // Output slot i of query q from its key.
@@ -636,6 +699,112 @@ __global__ __launch_bounds__(NT) void k_beam_expand(StepDev st, int K, int Kc, i
     block_select_top<NT>(n, Kc, keyf, out, stage, list, red_i, &bcast);
 }
 
+// Dense path on a bitmap step: one wavefront per beam, four beams per
+// workgroup.  Lane l owns the M consecutive columns l*M .. l*M+M-1: their
+// scores (16-byte loads, summed over the k-slices, if any) and validity bits
+// stay in registers; softmax and the beam's best min(K, n) keys use wave
+// reductions only.  Requires V <= 64*M and V % 4 == 0.
+template <int M>
+__global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K, int Kc, int V, int d,
+                                                       const float* __restrict__ Z, const float* __restrict__ Zp,
+                                                       const int32_t* __restrict__ n_live,
+                                                       const int32_t* __restrict__ ci_of,
+                                                       const int32_t* __restrict__ beam_rows,
+                                                       const float* __restrict__ acc, uint64_t* __restrict__ keys_out) {
+    static_assert(M % 4 == 0, "columns are read 4 at a time");
+    __shared__ uint64_t wl_all[4][kWaveListCap];
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    const int b = blockIdx.x * 4 + wv;
+    if (b >= R) return;
+    uint64_t* out = keys_out + (int64_t)b * Kc;
+    const int32_t r = beam_rows[b];
+    const float a = acc[b];
+    if (!beam_live(st, r, a)) {
+        if (lane < Kc) out[lane] = 0;
+        return;
+    }
+    const int c0 = lane * M;
+    const uint32_t* rb = st.bits + (int64_t)r * st.words;
+    const int split = gemm_split(*n_live, V, d);
+    const float* zb = (split == 1 ? Z + (int64_t)b * V : Zp + (int64_t)ci_of[b] * V) + c0;
+    float z[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) z[i] = 0.f;
+#pragma unroll
+    for (int x = 0; x < kSplitMax; ++x) {
+        if (x < split) {
+#pragma unroll
+            for (int i = 0; i < M; i += 4) {
+                if (c0 + i < V) {
+                    const float4 v4 = *reinterpret_cast<const float4*>(zb + (int64_t)x * kSplitRows * V + i);
+                    z[i] += v4.x;
+                    z[i + 1] += v4.y;
+                    z[i + 2] += v4.z;
+                    z[i + 3] += v4.w;
+                }
+            }
+        }
+    }
+    uint32_t on = 0;  // validity of this lane's columns, bit i for column c0 + i (M <= 32 per word)
+    uint32_t on_hi = 0;
+#pragma unroll
+    for (int i = 0; i < M; i += 32) {
+        // columns c0+i .. c0+i+31 lie in at most two bitmap words
+        const int c = c0 + i;
+        const int w = c >> 5, sh = c & 31;
+        uint32_t lo = c < V ? rb[w] : 0u;
+        uint32_t hi = (sh && c + 32 - sh < V) ? rb[w + 1] : 0u;
+        uint32_t bits = sh ? ((lo >> sh) | (hi << (32 - sh))) : lo;
+        if (M - i < 32) bits &= (1u << (M - i)) - 1u;
+        if (i == 0) on = bits; else on_hi = bits;
+    }
+    auto valid = [&](int i) { return ((i < 32 ? on >> i : on_hi >> (i - 32)) & 1u) != 0; };
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < M; ++i)
+        if (valid(i)) m = fmaxf(m, z[i]);
+    m = wave_max(m);
+    float se = 0.f;
+#pragma unroll
+    for (int i = 0; i < M; ++i)
+        if (valid(i)) se += expf(z[i] - m);
+    const float lse = m + logf(wave_sum(se));
+    const int parent = b % K;
+    uint32_t sc[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) sc[i] = valid(i) ? score_order_bits(a + (z[i] - lse)) : 0u;
+    const uint64_t best = wave_top<M>(
+        Kc, [&](int i) { return sc[i]; },
+        [&](int i) { return ((uint64_t)sc[i] << 32) | ((uint64_t)(1023 - parent) << 16) | (uint64_t)(65535 - (c0 + i)); },
+        wl_all[wv]);
+    if (lane < Kc) out[lane] = best;
+}
+
+// Dense path, per query: one wavefront per query, four queries per workgroup;
+// lane l owns keys l + 64 i (i < M) of the query's K*Kc.
+template <int M>
+__global__ __launch_bounds__(256) void k_query_merge_w(StepDev st, int Q, int K, int Kc,
+                                                       const uint64_t* __restrict__ keys,
+                                                       const int32_t* __restrict__ beam_rows,
+                                                       int32_t* __restrict__ out_tok, int32_t* __restrict__ out_par,
+                                                       int32_t* __restrict__ out_rows, float* __restrict__ out_logp) {
+    __shared__ uint64_t wl_all[4][kWaveListCap];
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    const int q = blockIdx.x * 4 + wv;
+    if (q >= Q) return;
+    const int n = K * Kc;
+    const uint64_t* src = keys + (int64_t)q * n;
+    uint64_t kv[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const int c = lane + kWave * i;
+        kv[i] = c < n ? src[c] : 0ull;
+    }
+    const uint64_t best = wave_top<M>(K, [&](int i) { return (uint32_t)(kv[i] >> 32); }, [&](int i) { return kv[i]; },
+                                      wl_all[wv]);
+    if (lane < K) emit(st, q, K, lane, best, beam_rows, out_tok, out_par, out_rows, out_logp);
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void k_query_merge(StepDev st, int K, int Kc, const uint64_t* __restrict__ keys,
                                                     const int32_t* __restrict__ beam_rows,
@@ -898,6 +1067,8 @@ int query_threads(int K) { return K >= 16 ? 1024 : 512; }
 
 size_t expand_lds_bytes(int S, int d, bool dense) { return (size_t)expand_lds(S, d, dense, kExpandThreads).total; }
 
+int expand_bitmap_max_v() { return 64 * kWave; }
+
 size_t query_lds_bytes(int S, int K, int Kc, int d) {
     return (size_t)query_lds(S, K, Kc, d, query_threads(K)).total;
 }
@@ -933,8 +1104,22 @@ hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R,
                               const int32_t* n_live, const int32_t* ci_of, const int32_t* beam_rows,
                               const float* acc, uint64_t* keys, hipStream_t s) {
     if (R <= 0) return hipSuccess;
-    const ExpandLds lay = expand_lds(st.S, d, dense, kExpandThreads);
     const int split_ok = dt == CB_BF16 ? 1 : 0;
+    if (dense && split_ok && st.store == CB_STORE_BITMAP && ldz <= 64 * kWave && ldz % 4 == 0) {
+        const int M = (int)((ldz + kWave - 1) / kWave);
+        const dim3 grid((R + 3) / 4);
+#define CB_EXPAND_BM(MV)                                                                                        \
+    hipLaunchKernelGGL((k_expand_bitmap<MV>), grid, dim3(256), 0, s, st, R, K, Kc, (int)ldz, d, Z, Zp, n_live, \
+                       ci_of, beam_rows, acc, keys)
+        if (M <= 4) CB_EXPAND_BM(4);
+        else if (M <= 8) CB_EXPAND_BM(8);
+        else if (M <= 16) CB_EXPAND_BM(16);
+        else if (M <= 32) CB_EXPAND_BM(32);
+        else CB_EXPAND_BM(64);
+#undef CB_EXPAND_BM
+        return hipGetLastError();
+    }
+    const ExpandLds lay = expand_lds(st.S, d, dense, kExpandThreads);
 #define CB_EXPAND(DT, DENSE)                                                                                     \
     hipLaunchKernelGGL((k_beam_expand<DT, DENSE, kExpandThreads>), dim3(R), dim3(kExpandThreads), lay.total, s, \
                        st, K, Kc, d, (const DT*)hidden, (const DT*)W, Z, Zp, ldz, n_live, ci_of, split_ok,        \
@@ -952,9 +1137,16 @@ hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uin
                               const int32_t* beam_rows, int32_t* tok, int32_t* par, int32_t* rows, float* logp,
                               hipStream_t s) {
     if (Q <= 0) return hipSuccess;
-    const size_t lds = (size_t)kMergeThreads * 8 + (size_t)K * Kc * 4;
-    hipLaunchKernelGGL((k_query_merge<kMergeThreads>), dim3(Q), dim3(kMergeThreads), lds, s, st, K, Kc, keys,
-                       beam_rows, tok, par, rows, logp);
+    const int M = (K * Kc + kWave - 1) / kWave;
+    const dim3 grid((Q + 3) / 4);
+#define CB_MERGE(MV)                                                                                      \
+    hipLaunchKernelGGL((k_query_merge_w<MV>), grid, dim3(256), 0, s, st, Q, K, Kc, keys, beam_rows, tok, par, \
+                       rows, logp)
+    if (M <= 1) CB_MERGE(1);
+    else if (M <= 4) CB_MERGE(4);
+    else if (M <= 16) CB_MERGE(16);
+    else CB_MERGE(64);
+#undef CB_MERGE
     return hipGetLastError();
 }
 

@@ -41,7 +41,30 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--path", default="tuned", choices=["tuned", "auto", "dense", "sparse"])
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 256 MiB five times (counter calibration)")
     return ap.parse_args()
+
+
+def kernels_sha1():
+    import hashlib
+    h = hashlib.sha1()
+    with open(os.path.join(ROOT, "csr_constrained_beam_amd", "csrc", "kernels.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from a committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE measurement of the current kernel source, else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernels_sha1") != kernels_sha1():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def log(*a):
@@ -56,6 +79,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}))
+        return
 
     import csr_constrained_beam_amd as cb
     from synth import get_config, make_catalog, make_dense
@@ -217,12 +250,13 @@ def main():
         ach = kd["flops"] / (kd["us"] * 1e-6) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": MFMA_PEAK_TFLOPS[cfg.dtype],
                 "unit": "TFLOP/s", "frac": ach / MFMA_PEAK_TFLOPS[cfg.dtype],
-                "per_launch": kd["flops"] / kd["launches"], "mean_us": kd["mean_us"], "traffic": None}
+                "per_launch": kd["flops"] / kd["launches"], "mean_us": kd["mean_us"],
+                "traffic": committed_traffic(dom, cfg.name)}
     else:
         ach = kd["bytes"] / (kd["us"] * 1e-6) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": ach / HBM_PEAK_GBS, "per_launch": kd["bytes"] / kd["launches"], "mean_us": kd["mean_us"],
-                "traffic": None}
+                "traffic": committed_traffic(dom, cfg.name)}
     kernels = {n: {"launches_per_pass": k["launches"] // args.steps, "mean_us": round(k["mean_us"], 3),
                    "share": round(k["share"], 4),
                    "GB/s": round(k["bytes"] / (k["us"] * 1e-6) / 1e9, 1),

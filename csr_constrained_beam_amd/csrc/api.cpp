@@ -114,7 +114,7 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, const void* hidden, c
     }
     {
         const bool bf = p->dtype == CB_BF16;
-        ProfMark m(p, s, t, bf ? CB_KERNEL_GEMM_BF16 : CB_KERNEL_GEMM_F32, 256, gemm_blocks(p->dtype, R, idx->V));
+        ProfMark m(p, s, t, bf ? CB_KERNEL_GEMM_BF16 : CB_KERNEL_GEMM_F32, bf ? 512 : 256, gemm_blocks(p->dtype, R, idx->V));
         e = launch_gemm_scores(p->dtype, R, idx->V, p->d, p->live, p->n_live, hidden, Wt, p->Z, p->Zp, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: full-codebook scores", e);

@@ -613,7 +613,10 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
 
 // ---- dense step: per-beam expansion and per-query merge --------------------
 
-constexpr int kBM = 128, kBN = 128, kBK = 32, kLDP = kBK + 8;
+constexpr int kBM = 128, kBN = 128, kBK = 64, kLDP = kBK + 8;
+constexpr int kWM = 32, kWN = 64;  // per-wave tile: 1 x 2 MFMA 32x32 blocks
+constexpr int kGemmThreads = (kBM / kWM) * (kBN / kWN) * 64;
+constexpr int kGemmLds = 2 * (kBM + kBN) * kLDP * 2;  // double-buffered A and B tiles (bytes)
 constexpr int kSplitMax = 8;   // k-slices for steps with few live beams
 constexpr int kSplitRows = 2 * kBM;
 constexpr int kCUs = 256;
@@ -850,17 +853,25 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // Scores of the live beams against the whole codebook, bf16 in, float32
-// accumulate on MFMA 32x32x16: one 128x128 tile (4 waves of 64x64) of one
-// k-slice per workgroup; LDS double buffered with the next k-tile prefetched
-// into registers.  With one slice, Z[beam][v]; with several, Zp[slice][compact
+// accumulate on MFMA 32x32x16: one 128x128 tile of one k-slice per workgroup,
+// 8 waves of 32x64; LDS double buffered (dynamic, 72 KiB) with the next k-tile
+// prefetched into registers (native vector types, so the staging stays in
+// VGPRs).  With one slice, Z[beam][v]; with several, Zp[slice][compact
 // row][v].  Consecutive tiles on one XCD share W columns.
-__global__ __launch_bounds__(256) void k_gemm_bf16(int V, int d, const int32_t* __restrict__ live,
-                                                   const int32_t* __restrict__ n_live, const uint16_t* __restrict__ H,
-                                                   const uint16_t* __restrict__ W, float* __restrict__ Z,
-                                                   float* __restrict__ Zp, int64_t ldz) {
-    __shared__ __align__(16) uint16_t As[2][kBM * kLDP];
-    __shared__ __align__(16) uint16_t Bs[2][kBN * kLDP];
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kGemmThreads) void k_gemm_bf16(int V, int d, const int32_t* __restrict__ live,
+                                                            const int32_t* __restrict__ n_live,
+                                                            const uint16_t* __restrict__ H,
+                                                            const uint16_t* __restrict__ W, float* __restrict__ Z,
+                                                            float* __restrict__ Zp, int64_t ldz) {
+    extern __shared__ __align__(16) uint16_t gsm[];
+    uint16_t* As = gsm;                     // [2][kBM * kLDP]
+    uint16_t* Bs = gsm + 2 * kBM * kLDP;    // [2][kBN * kLDP]
     __shared__ int rows_s[kBM];
+    constexpr int NT = kGemmThreads;
+    constexpr int CA = kBM * kBK / 8 / NT, CB = kBN * kBK / 8 / NT;  // 16-byte chunks per thread
+    constexpr int TJ = kWN / 32;
     const int nl = *n_live;
     const int split = gemm_split(nl, V, d);
     const int mt = (nl + kBM - 1) / kBM, nt = (V + kBN - 1) / kBN;
@@ -876,86 +887,85 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(int V, int d, const int32_t* 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     if (tid < kBM) rows_s[tid] = m0 + tid < nl ? live[m0 + tid] : -1;
     __syncthreads();
-    const int wm = (wv >> 1) * 64, wn = (wv & 1) * 64;
+    const int wm = (wv / (kBN / kWN)) * kWM, wn = (wv % (kBN / kWN)) * kWN;
 
-    // this thread's two 16-byte chunks of each k-tile of A and B
-    int crow[2], ccol[2];
-    const uint16_t* pa[2];
-    const uint16_t* pb[2];
+    const uint16_t* pa[CA];
+    const uint16_t* pb[CB];
+    int oa[CA], ob[CB];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int c = tid + u * 256;
-        crow[u] = c / (kBK / 8);
-        ccol[u] = (c % (kBK / 8)) * 8;
-        const int hb = rows_s[crow[u]];
-        pa[u] = hb >= 0 ? H + (int64_t)hb * d + kbeg + ccol[u] : nullptr;
-        pb[u] = n0 + crow[u] < V ? W + (int64_t)(n0 + crow[u]) * d + kbeg + ccol[u] : nullptr;
+    for (int u = 0; u < CA; ++u) {
+        const int c = tid + u * NT, r = c / (kBK / 8), cc = (c % (kBK / 8)) * 8;
+        const int hb = rows_s[r];
+        pa[u] = hb >= 0 ? H + (int64_t)hb * d + kbeg + cc : nullptr;
+        oa[u] = r * kLDP + cc;
     }
-    uint4 ra[2], rb[2];
-    auto fetch = [&](int k0) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            ra[u] = pa[u] ? *reinterpret_cast<const uint4*>(pa[u] + k0) : make_uint4(0, 0, 0, 0);
-            rb[u] = pb[u] ? *reinterpret_cast<const uint4*>(pb[u] + k0) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            *reinterpret_cast<uint4*>(&As[buf][crow[u] * kLDP + ccol[u]]) = ra[u];
-            *reinterpret_cast<uint4*>(&Bs[buf][crow[u] * kLDP + ccol[u]]) = rb[u];
-        }
-    };
+    for (int u = 0; u < CB; ++u) {
+        const int c = tid + u * NT, r = c / (kBK / 8), cc = (c % (kBK / 8)) * 8;
+        pb[u] = n0 + r < V ? W + (int64_t)(n0 + r) * d + kbeg + cc : nullptr;
+        ob[u] = r * kLDP + cc;
+    }
+    u32x4_t ra[CA], rb[CB];
+    const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+#define CB_GEMM_FETCH(k0)                                                                         \
+    _Pragma("unroll") for (int u = 0; u < CA; ++u) ra[u] =                                        \
+        pa[u] ? *reinterpret_cast<const u32x4_t*>(pa[u] + (k0)) : zero4;                          \
+    _Pragma("unroll") for (int u = 0; u < CB; ++u) rb[u] =                                        \
+        pb[u] ? *reinterpret_cast<const u32x4_t*>(pb[u] + (k0)) : zero4;
+#define CB_GEMM_STASH(buf)                                                                        \
+    _Pragma("unroll") for (int u = 0; u < CA; ++u)                                                \
+        *reinterpret_cast<u32x4_t*>(&As[(buf) * kBM * kLDP + oa[u]]) = ra[u];                      \
+    _Pragma("unroll") for (int u = 0; u < CB; ++u)                                                \
+        *reinterpret_cast<u32x4_t*>(&Bs[(buf) * kBN * kLDP + ob[u]]) = rb[u];
 
-    f32x16_t acc[2][2];
+    f32x16_t acc[TJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+        for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
 
-    fetch(0);
-    stash(0);
+    CB_GEMM_FETCH(0)
+    CB_GEMM_STASH(0)
     __syncthreads();
     const int nk = klen / kBK;
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) fetch((kt + 1) * kBK);
+        if (kt + 1 < nk) {
+            CB_GEMM_FETCH((kt + 1) * kBK)
+        }
+        const uint16_t* Ab = As + buf * kBM * kLDP;
+        const uint16_t* Bb = Bs + buf * kBN * kLDP;
 #pragma unroll
         for (int kk = 0; kk < kBK; kk += 16) {
-            bf16x8_t av[2], bv[2];
+            const bf16x8_t av = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const u32x4_t*>(&Ab[(wm + (lane & 31)) * kLDP + kk + (lane >> 5) * 8]));
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                av[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                                                         &As[buf][(wm + i * 32 + (lane & 31)) * kLDP + kk + (lane >> 5) * 8]));
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bv[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                                                         &Bs[buf][(wn + j * 32 + (lane & 31)) * kLDP + kk + (lane >> 5) * 8]));
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-        }
-        if (kt + 1 < nk) stash(buf ^ 1);
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int rr = wm + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-            const int hb = rows_s[rr];
-            if (hb < 0) continue;
-            float* dst = split == 1 ? Z + (int64_t)hb * ldz : Zp + ((int64_t)zs * kSplitRows + m0 + rr) * ldz;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int col = n0 + wn + j * 32 + (lane & 31);
-                if (col < V) dst[col] = acc[i][j][e];
+            for (int j = 0; j < TJ; ++j) {
+                const bf16x8_t bv = __builtin_bit_cast(
+                    bf16x8_t,
+                    *reinterpret_cast<const u32x4_t*>(&Bb[(wn + j * 32 + (lane & 31)) * kLDP + kk + (lane >> 5) * 8]));
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[j], 0, 0, 0);
             }
         }
+        if (kt + 1 < nk) {
+            CB_GEMM_STASH(buf ^ 1)
+        }
+        __syncthreads();
+    }
+#undef CB_GEMM_FETCH
+#undef CB_GEMM_STASH
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int rr = wm + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+        const int hb = rows_s[rr];
+        if (hb < 0) continue;
+        float* dst = split == 1 ? Z + (int64_t)hb * ldz : Zp + ((int64_t)zs * kSplitRows + m0 + rr) * ldz;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+            const int col = n0 + wn + j * 32 + (lane & 31);
+            if (col < V) dst[col] = acc[j][e];
+        }
+    }
 }
 
 // float32 full-codebook scores of the live beams: 16x16 output tile per
@@ -1160,7 +1170,10 @@ hipError_t launch_gemm_scores(cb_dtype dt, int R, int V, int d, const int32_t* l
                               const void* H, const void* W, float* Z, float* Zp, hipStream_t s) {
     if (R <= 0) return hipSuccess;
     if (dt == CB_BF16) {
-        hipLaunchKernelGGL(k_gemm_bf16, dim3(gemm_grid(R, V)), dim3(256), 0, s, V, d, live, n_live,
+        static const hipError_t lds_ok = hipFuncSetAttribute(
+            (const void*)k_gemm_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
+        if (lds_ok != hipSuccess) return lds_ok;
+        hipLaunchKernelGGL(k_gemm_bf16, dim3(gemm_grid(R, V)), dim3(kGemmThreads), kGemmLds, s, V, d, live, n_live,
                            (const uint16_t*)H, (const uint16_t*)W, Z, Zp, (int64_t)V);
     } else {
         dim3 grid((V + 15) / 16, (R + 15) / 16);

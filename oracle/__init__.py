@@ -3,8 +3,9 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  It shares no code with the HIP library
 ``csr_constrained_beam_amd``: the trie, the step and the decode live in
-``trie_beam.c`` (compiled here with gcc); ``brute.py`` is an independent
-pure-Python enumerator for tiny catalogs.
+``trie_beam.c``, a second trie-free construction in ``range_beam.c`` (both
+compiled here with gcc); ``brute.py`` is an independent pure-Python
+enumerator for tiny catalogs.
 
 Parity status of each function (what pins it; see ``tests/test_oracle_pins.py``):
 
@@ -21,6 +22,12 @@ Parity status of each function (what pins it; see ``tests/test_oracle_pins.py``)
   decode invariants.
 * ``Trie.hidden``: the stand-in model's rule is defined by the workload, not by
   the pages; it is pinned by a closed form (unit norm, direction of s) only.
+* ``SortedRange`` (``range_beam.c``): the same definition computed over the
+  sorted catalog without a trie, light enough for 100M-item catalogs.  Pinned
+  by a catalog scan of every prefix, brute-force path scores, the W = 0 closed
+  form, and equality with the trie oracle (tables, step candidates, decode
+  traces) on the tiny, small and hybrid generators
+  (``tests/test_oracle_range.py``).
 """
 
 import ctypes
@@ -30,7 +37,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "trie_beam.c")
+_SRCS = [os.path.join(_HERE, "trie_beam.c"), os.path.join(_HERE, "range_beam.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
@@ -38,10 +45,11 @@ _i32p = ctypes.c_void_p
 
 
 def build(force=False):
-    """Compile trie_beam.c -> liboracle.so (gcc, OpenMP over queries)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    """Compile trie_beam.c and range_beam.c -> liboracle.so (gcc, OpenMP)."""
+    stale = not os.path.exists(_LIB) or any(os.path.getmtime(_LIB) < os.path.getmtime(x) for x in _SRCS)
+    if force or stale:
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"])
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-o", tmp, *_SRCS, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -73,6 +81,20 @@ def _load():
                                   P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
         lib.or_hidden.restype = None
         lib.or_hidden.argtypes = [P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P]
+        lib.orr_build.restype = P
+        lib.orr_build.argtypes = [P, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+        lib.orr_free.restype = None
+        lib.orr_free.argtypes = [P]
+        lib.orr_n_items.restype = ctypes.c_int64
+        lib.orr_n_items.argtypes = [P]
+        lib.orr_level_count.restype = ctypes.c_int64
+        lib.orr_level_count.argtypes = [P, ctypes.c_int]
+        lib.orr_children_of_row.restype = ctypes.c_int
+        lib.orr_children_of_row.argtypes = [P, ctypes.c_int, ctypes.c_int64, P, P, ctypes.c_int64]
+        lib.orr_step.restype = ctypes.c_int
+        lib.orr_step.argtypes = lib.or_step.argtypes
+        lib.orr_decode.restype = ctypes.c_int
+        lib.orr_decode.argtypes = lib.or_decode.argtypes
         _lib = lib
     return _lib
 
@@ -84,6 +106,8 @@ def _ptr(a):
 class Trie:
     """Pointer trie of a catalog (int array [n][L], tokens in [0, V))."""
 
+    _p = "or_"
+
     def __init__(self, sids, V):
         sids = np.ascontiguousarray(sids, dtype=np.int32)
         if sids.ndim != 2:
@@ -91,22 +115,25 @@ class Trie:
         self.L = int(sids.shape[1])
         self.V = int(V)
         self._lib = _load()
-        self._h = self._lib.or_build(_ptr(sids), sids.shape[0], self.L, self.V)
+        self._h = self._fn("build")(_ptr(sids), sids.shape[0], self.L, self.V)
         if not self._h:
-            raise ValueError("oracle trie build failed (token out of range, bad shape or out of memory)")
+            raise ValueError("oracle build failed (token out of range, bad shape or out of memory)")
+
+    def _fn(self, name):
+        return getattr(self._lib, self._p + name)
 
     def __del__(self):
         h = getattr(self, "_h", None)
         if h:
-            self._lib.or_free(h)
+            self._fn("free")(h)
             self._h = None
 
     @property
     def n_items(self):
-        return int(self._lib.or_n_items(self._h))
+        return int(self._fn("n_items")(self._h))
 
     def level_count(self, depth):
-        return int(self._lib.or_level_count(self._h, depth))
+        return int(self._fn("level_count")(self._h, depth))
 
     def children(self, prefix):
         """(tokens, rows) of the children of ``prefix`` (None if absent)."""
@@ -120,12 +147,13 @@ class Trie:
         return tok, rows
 
     def children_of_row(self, depth, row):
-        n = self._lib.or_children_of_row(self._h, depth, row, None, None, 0)
+        f = self._fn("children_of_row")
+        n = f(self._h, depth, row, None, None, 0)
         if n < 0:
             return None
         tok = np.empty(n, dtype=np.int32)
         rows = np.empty(n, dtype=np.int64)
-        self._lib.or_children_of_row(self._h, depth, row, _ptr(tok), _ptr(rows), n)
+        f(self._h, depth, row, _ptr(tok), _ptr(rows), n)
         return tok, rows
 
     def prefix_of_row(self, depth, row):
@@ -161,14 +189,14 @@ class Trie:
             # capacity: the widest query's candidate count
             fan = np.zeros(R, dtype=np.int64)
             for b in np.nonzero(rows >= 0)[0]:
-                fan[b] = self._lib.or_children_of_row(self._h, t, int(rows[b]), None, None, 0)
+                fan[b] = self._fn("children_of_row")(self._h, t, int(rows[b]), None, None, 0)
             cap = int(max(1, fan.reshape(Q, K).sum(axis=1).max() if Q else 1))
             cc = np.zeros(Q, np.int64)
             ct = np.full((Q, cap), -1, np.int32)
             cp = np.full((Q, cap), -1, np.int32)
             cr = np.full((Q, cap), -1, np.int64)
             cs = np.full((Q, cap), -np.inf, np.float32)
-        r = self._lib.or_step(self._h, t, Q, K, d, _ptr(h), _ptr(Wt), _ptr(rows), _ptr(acc),
+        r = self._fn("step")(self._h, t, Q, K, d, _ptr(h), _ptr(Wt), _ptr(rows), _ptr(acc),
                               _ptr(out["tokens"]), _ptr(out["parents"]), _ptr(out["rows"]), _ptr(out["logp"]),
                               cap, _ptr(cc), _ptr(ct), _ptr(cp), _ptr(cr), _ptr(cs), threads)
         if r != 0:
@@ -194,7 +222,7 @@ class Trie:
             tr = [np.zeros((L, R, d), np.float32), np.empty((L, R), np.int64), np.empty((L, R), np.float32),
                   np.empty((L, R), np.int32), np.empty((L, R), np.int32), np.empty((L, R), np.int64),
                   np.empty((L, R), np.float32)]
-        r = self._lib.or_decode(self._h, Q, K, d, 1 if bf16 else 0, _ptr(q), _ptr(P), _ptr(W),
+        r = self._fn("decode")(self._h, Q, K, d, 1 if bf16 else 0, _ptr(q), _ptr(P), _ptr(W),
                                 _ptr(out["seqs"]), _ptr(out["logp"]), _ptr(out["rows"]),
                                 *[_ptr(a) for a in tr], threads)
         if r != 0:
@@ -209,3 +237,17 @@ class Trie:
         h = np.empty_like(s)
         self._lib.or_hidden(_ptr(s), s.shape[0], s.shape[1], 1 if bf16 else 0, _ptr(h))
         return h
+
+
+class SortedRange(Trie):
+    """Second oracle over the sorted catalog: a prefix is a range of sorted
+    items, its children the distinct tokens found by binary search.  Same
+    interface as Trie (children(prefix), prefix_of_row and hidden excepted)."""
+
+    _p = "orr_"
+
+    def children(self, prefix):
+        raise NotImplementedError
+
+    def prefix_of_row(self, depth, row):
+        raise NotImplementedError

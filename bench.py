@@ -46,11 +46,18 @@ def parse():
     return ap.parse_args()
 
 
-def kernels_sha1():
+def kernel_sources(kernel):
+    """Source files that define `kernel` (by its bench name)."""
+    main = "radix.hip" if kernel.startswith("radix_") else "kernels.hip"
+    return [os.path.join(ROOT, "csr_constrained_beam_amd", "csrc", f) for f in ("device.h", main)]
+
+
+def kernels_sha1(kernel):
     import hashlib
     h = hashlib.sha1()
-    with open(os.path.join(ROOT, "csr_constrained_beam_amd", "csrc", "kernels.hip"), "rb") as f:
-        h.update(f.read())
+    for path in kernel_sources(kernel):
+        with open(path, "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -62,7 +69,7 @@ def committed_traffic(kernel, workload):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernels_sha1") != kernels_sha1():
+    if rec.get("kernels_sha1") != kernels_sha1(kernel):
         return None
     return rec.get("bytes_per_launch")
 

@@ -14,6 +14,7 @@ CB_OK, CB_EINVAL, CB_ENOMEM, CB_EHIP, CB_EUNSUPPORTED, CB_ECAPACITY = 0, -1, -2,
 CB_F32, CB_BF16 = 0, 1
 CB_PATH_AUTO, CB_PATH_DENSE, CB_PATH_SPARSE = 0, 1, 2
 CB_STORE_AUTO, CB_STORE_CSR, CB_STORE_BITMAP = 0, 1, 2
+CB_SELECT_AUTO, CB_SELECT_LDS, CB_SELECT_RADIX = 0, 1, 2
 
 STATUS_NAMES = {0: "CB_OK", -1: "CB_EINVAL", -2: "CB_ENOMEM", -3: "CB_EHIP", -4: "CB_EUNSUPPORTED",
                 -5: "CB_ECAPACITY"}
@@ -36,7 +37,9 @@ class KernelTime(ctypes.Structure):
 
 
 KERNEL_NAMES = {0: "gemm_bf16", 1: "gemm_f32", 2: "expand_sparse", 3: "expand_dense", 4: "merge",
-                5: "step_query", 6: "live_rows"}
+                5: "step_query", 6: "live_rows", 7: "radix_plan", 8: "radix_score_sparse",
+                9: "radix_score_dense", 10: "radix_keys", 11: "radix_refine", 12: "radix_collect",
+                13: "radix_sort"}
 
 SIGNATURES = {
     "cb_build_index": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _I32, _PP]),
@@ -47,6 +50,8 @@ SIGNATURES = {
     "cb_plan_create": (ctypes.c_int, [_P, _I32, _I32, _I32, ctypes.c_int, _PP]),
     "cb_set_path": (ctypes.c_int, [_P, _I32, ctypes.c_int]),
     "cb_get_path": (ctypes.c_int, [_P, _I32, _P]),
+    "cb_set_select": (ctypes.c_int, [_P, _I32, ctypes.c_int]),
+    "cb_get_select": (ctypes.c_int, [_P, _I32, _P]),
     "cb_step": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "cb_decode": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "cb_tune": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P]),

@@ -13,6 +13,8 @@ from . import _lib as C
 
 _PATHS = {"auto": C.CB_PATH_AUTO, "dense": C.CB_PATH_DENSE, "sparse": C.CB_PATH_SPARSE}
 _PATH_NAMES = {v: k for k, v in _PATHS.items()}
+_SELECTS = {"auto": C.CB_SELECT_AUTO, "lds": C.CB_SELECT_LDS, "radix": C.CB_SELECT_RADIX}
+_SELECT_NAMES = {v: k for k, v in _SELECTS.items()}
 _STORES = {"auto": C.CB_STORE_AUTO, "csr": C.CB_STORE_CSR, "bitmap": C.CB_STORE_BITMAP}
 _STORE_NAMES = {v: k for k, v in _STORES.items()}
 
@@ -118,6 +120,15 @@ class Plan:
         v = ctypes.c_int()
         C.check("cb_get_path", self._lib.cb_get_path(self._h, int(t), ctypes.byref(v)))
         return _PATH_NAMES[v.value]
+
+    def set_select(self, t, select):
+        """Top-K selection of step t: "auto", "lds" (K <= 64) or "radix"."""
+        C.check("cb_set_select", self._lib.cb_set_select(self._h, int(t), _SELECTS[select]))
+
+    def get_select(self, t):
+        v = ctypes.c_int()
+        C.check("cb_get_select", self._lib.cb_get_select(self._h, int(t), ctypes.byref(v)))
+        return _SELECT_NAMES[v.value]
 
     def _stream(self):
         torch = _torch()

@@ -74,6 +74,71 @@ int32_t resolve_path(const cb_plan* p, int t) {
     return (T.store == CB_STORE_BITMAP && dense_available(p)) ? CB_PATH_DENSE : CB_PATH_SPARSE;
 }
 
+// Whether the LDS selection (fused sparse step, or dense expansion + merge)
+// holds step t of this plan.
+bool lds_select_ok(const cb_plan* p, int t) {
+    if (p->K > kMaxK) return false;
+    const cb::StepTable& T = p->idx->steps[(size_t)t];
+    const int Kc = std::min(p->K, std::max(T.S, 1));
+    return query_lds_bytes(T.S, p->K, Kc, p->d) <= (size_t)kMaxLds &&
+           expand_lds_bytes(T.S, p->d, true) <= (size_t)kMaxLds;
+}
+
+int32_t resolve_select(const cb_plan* p, int t) {
+    const int32_t f = p->select[(size_t)t];
+    if (f == CB_SELECT_LDS || f == CB_SELECT_RADIX) return f;
+    return lds_select_ok(p, t) ? CB_SELECT_LDS : CB_SELECT_RADIX;
+}
+
+void wide_release(cb_plan* p) {
+    WideDev& w = p->wide;
+    dev_free(w.cand_off);
+    dev_free(w.chunk_off);
+    dev_free(w.cand);
+    dev_free(w.cms);
+    dev_free(w.hist);
+    dev_free(w.sel);
+    dev_free(w.surv_n);
+    dev_free(w.surv);
+    w = WideDev();
+    p->wide_S = 0;
+}
+
+// Radix-selection workspace sized for the plan's widest row.
+cb_status wide_alloc(cb_plan* p) {
+    if (p->wide.cand) return CB_OK;
+    int32_t S = 1;
+    for (const auto& T : p->idx->steps) S = std::max(S, T.S);
+    const int64_t cap = (int64_t)p->K * S;
+    const int64_t chunk_cap = (int64_t)p->K * ((S + wide_chunk() - 1) / wide_chunk());
+    if (cap >= (int64_t(1) << 31)) {
+        set_error("radix selection: K * widest row exceeds 2^31 candidates per query");
+        return CB_ECAPACITY;
+    }
+    const size_t Q = (size_t)p->Q_max;
+    WideDev& w = p->wide;
+    w.cap = cap;
+    w.chunk_cap = chunk_cap;
+    cb_status st = dev_alloc(&w.cand_off, Q * (p->K + 1), "radix offsets");
+    if (st == CB_OK) st = dev_alloc(&w.chunk_off, Q * (p->K + 1), "radix chunk offsets");
+    if (st == CB_OK) st = dev_alloc(&w.cand, Q * (size_t)cap, "radix candidates");
+    if (st == CB_OK) st = dev_alloc(&w.cms, Q * (size_t)chunk_cap * 2, "radix chunk softmax");
+    if (st == CB_OK) st = dev_alloc(&w.hist, Q * 2 * (size_t)wide_bins(), "radix histograms");
+    if (st == CB_OK) {
+        unsigned char* sel = nullptr;
+        st = dev_alloc(&sel, Q * wide_sel_bytes(), "radix state");
+        w.sel = sel;
+    }
+    if (st == CB_OK) st = dev_alloc(&w.surv_n, Q, "radix survivor counts");
+    if (st == CB_OK) st = dev_alloc(&w.surv, Q * (size_t)wide_surv_cap(), "radix survivors");
+    if (st != CB_OK) {
+        wide_release(p);
+        return st;
+    }
+    p->wide_S = S;
+    return CB_OK;
+}
+
 // Records an event pair around a launch while profiling is on.
 struct ProfMark {
     cb_plan* p;
@@ -90,6 +155,76 @@ struct ProfMark {
     }
 };
 
+// Enqueue one step on the radix selection (no validation).
+cb_status run_step_radix(cb_plan* p, int t, int Q, int32_t path, const void* hidden, const void* Wt,
+                         const int32_t* rows, const float* acc, int32_t* ot, int32_t* op, int32_t* orow, float* ol,
+                         hipStream_t s) {
+    const cb_index* idx = p->idx;
+    const cb::StepDev sd = idx->steps[(size_t)t].dev(idx->words);
+    const int R = Q * p->K;
+    WideDev w = p->wide;
+    if (!w.cand) {
+        set_error("cb_step: radix workspace missing");
+        return CB_EINVAL;
+    }
+    w.G = wide_blocks_per_query(Q);
+    const int GQ = w.G * Q;
+    const bool dense = path == CB_PATH_DENSE;
+    hipError_t e;
+    {
+        ProfMark m(p, s, t, CB_KERNEL_RADIX_PLAN, 1024, Q);
+        e = launch_wide_plan(sd, Q, p->K, rows, acc, w, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: radix offsets", e);
+    }
+    if (dense) {
+        {
+            ProfMark m(p, s, t, CB_KERNEL_LIVE_ROWS, 1024, 1);
+            e = launch_live_rows(sd, R, rows, acc, p->live, p->n_live, p->ci_of, s);
+            m.done();
+            if (e != hipSuccess) return hip_fail("cb_step: live beams", e);
+        }
+        const bool bf = p->dtype == CB_BF16;
+        ProfMark m(p, s, t, bf ? CB_KERNEL_GEMM_BF16 : CB_KERNEL_GEMM_F32, bf ? 512 : 256,
+                   gemm_blocks(p->dtype, R, idx->V));
+        e = launch_gemm_scores(p->dtype, R, idx->V, p->d, p->live, p->n_live, hidden, Wt, p->Z, p->Zp, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: full-codebook scores", e);
+    }
+    {
+        ProfMark m(p, s, t, dense ? CB_KERNEL_RADIX_SCORE_DENSE : CB_KERNEL_RADIX_SCORE_SPARSE, 256, GQ);
+        e = launch_wide_score(sd, dense, p->dtype, Q, p->K, p->d, hidden, Wt, p->Z, p->Zp, idx->V, p->n_live,
+                              p->ci_of, rows, w, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: radix scores", e);
+    }
+    {
+        ProfMark m(p, s, t, CB_KERNEL_RADIX_KEYS, 256, GQ);
+        e = launch_wide_keys(Q, p->K, acc, w, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: radix keys", e);
+    }
+    {
+        ProfMark m(p, s, t, CB_KERNEL_RADIX_REFINE, 256, GQ);
+        e = launch_wide_refine(Q, p->K, w, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: radix refine", e);
+    }
+    {
+        ProfMark m(p, s, t, CB_KERNEL_RADIX_COLLECT, 256, GQ);
+        e = launch_wide_collect(Q, w, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: radix collect", e);
+    }
+    {
+        ProfMark m(p, s, t, CB_KERNEL_RADIX_SORT, 1024, Q);
+        e = launch_wide_sort(sd, Q, p->K, rows, w, ot, op, orow, ol, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: radix sort", e);
+    }
+    return CB_OK;
+}
+
 // Enqueue one step (no validation).
 cb_status run_step(cb_plan* p, int t, int Q, int32_t path, const void* hidden, const void* Wt, const int32_t* rows,
                    const float* acc, int32_t* ot, int32_t* op, int32_t* orow, float* ol, hipStream_t s) {
@@ -99,6 +234,7 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, const void* hidden, c
     const int R = Q * p->K;
     const int Kc = std::min(p->K, std::max(T.S, 1));
     hipError_t e;
+    if (resolve_select(p, t) == CB_SELECT_RADIX) return run_step_radix(p, t, Q, path, hidden, Wt, rows, acc, ot, op, orow, ol, s);
     if (path == CB_PATH_SPARSE) {
         ProfMark m(p, s, t, CB_KERNEL_STEP_QUERY, query_threads(p->K), Q);
         e = launch_step_query(sd, p->dtype, Q, p->K, Kc, p->d, hidden, Wt, rows, acc, ot, op, orow, ol, s);
@@ -356,20 +492,16 @@ cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_
         set_error("cb_plan_create: index was built host-only (device -1)");
         return CB_EINVAL;
     }
-    if (K > kMaxK) {
-        set_error("cb_plan_create: K > " + std::to_string(kMaxK) + " is not supported");
+    if (K > kMaxKRadix) {
+        set_error("cb_plan_create: K > " + std::to_string(kMaxKRadix) + " is not supported");
+        return CB_ECAPACITY;
+    }
+    if (d > 16384) {
+        set_error("cb_plan_create: d > 16384 is not supported (hidden vector staged in LDS)");
         return CB_ECAPACITY;
     }
     int32_t Smax = 1;
-    for (const auto& T : idx->steps) {
-        Smax = std::max(Smax, T.S);
-        const int Kc_t = std::min(K, std::max(T.S, 1));
-        if (query_lds_bytes(T.S, K, Kc_t, d) > (size_t)kMaxLds || expand_lds_bytes(T.S, d, true) > (size_t)kMaxLds) {
-            set_error("cb_plan_create: a step with a row of " + std::to_string(T.S) +
-                      " valid tokens exceeds the step kernels' LDS");
-            return CB_ECAPACITY;
-        }
-    }
+    for (const auto& T : idx->steps) Smax = std::max(Smax, T.S);
     const int32_t Kc = std::min(K, Smax);
     DeviceGuard g(idx->device);
     if (!g.ok) {
@@ -382,6 +514,7 @@ cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_
         return CB_ENOMEM;
     }
     p->idx = idx;
+    p->device = idx->device;
     p->Q_max = Q_max;
     p->K = K;
     p->d = d;
@@ -391,6 +524,7 @@ cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_
     p->tuned.assign((size_t)idx->L, 0);
     p->tune_dense_us.assign((size_t)idx->L, -1.f);
     p->tune_sparse_us.assign((size_t)idx->L, -1.f);
+    p->select.assign((size_t)idx->L, CB_SELECT_AUTO);
     const size_t R = (size_t)Q_max * K;
     cb_status st = dev_alloc(&p->keys, R * Kc, "candidate keys");
     if (st == CB_OK) st = dev_alloc(&p->Z, R * (size_t)idx->V, "full-codebook scores");
@@ -414,6 +548,9 @@ cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_
     if (st == CB_OK) st = dev_alloc(&p->scratch_logp, R, "scratch");
     if (st == CB_OK) st = dev_alloc(&p->scratch_tok, R, "scratch");
     if (st == CB_OK) st = dev_alloc(&p->scratch_par, R, "scratch");
+    bool need_radix = false;
+    for (int t = 0; t < idx->L; ++t) need_radix = need_radix || !lds_select_ok(p, t);
+    if (st == CB_OK && need_radix) st = wide_alloc(p);
     if (st != CB_OK) {
         cb_plan_destroy(p);
         return st;
@@ -433,6 +570,35 @@ cb_status cb_set_path(cb_plan* p, int32_t t, cb_path path) {
         return CB_EUNSUPPORTED;
     }
     p->forced[(size_t)t] = path;
+    return CB_OK;
+}
+
+cb_status cb_set_select(cb_plan* p, int32_t t, cb_select sel) {
+    clear_error();
+    if (!p || t < 0 || t >= p->idx->L || sel < CB_SELECT_AUTO || sel > CB_SELECT_RADIX) {
+        set_error("cb_set_select: bad plan, step or selection");
+        return CB_EINVAL;
+    }
+    if (sel == CB_SELECT_LDS && !lds_select_ok(p, t)) {
+        set_error("cb_set_select: the LDS selection holds K <= 64 and rows that fit its LDS");
+        return CB_ECAPACITY;
+    }
+    if (sel == CB_SELECT_RADIX) {
+        DeviceGuard g(p->idx->device);
+        cb_status st = wide_alloc(p);
+        if (st != CB_OK) return st;
+    }
+    p->select[(size_t)t] = sel;
+    return CB_OK;
+}
+
+cb_status cb_get_select(const cb_plan* p, int32_t t, cb_select* sel) {
+    clear_error();
+    if (!p || !sel || t < 0 || t >= p->idx->L) {
+        set_error("cb_get_select: bad plan, step or output");
+        return CB_EINVAL;
+    }
+    *sel = (cb_select)resolve_select(p, t);
     return CB_OK;
 }
 
@@ -655,8 +821,9 @@ cb_status cb_profile_stop(cb_plan* p, cb_kernel_time* out, int32_t cap, int32_t*
 
 void cb_plan_destroy(cb_plan* p) {
     if (!p) return;
-    DeviceGuard g(p->idx->device);
+    DeviceGuard g(p->device);  // the index may already be freed
     profile_release(p);
+    wide_release(p);
     dev_free(p->keys);
     dev_free(p->Z);
     dev_free(p->Zp);

@@ -61,13 +61,31 @@ struct cb_index {
 // Limits of the kernels in this build.
 namespace cb {
 constexpr int kMaxK = 64;            // beam width held by the per-query selection (one wave)
+constexpr int kMaxKRadix = 1024;     // beam width of the radix-select path (10-bit parent field of a key)
 constexpr int kMaxLds = 65536;       // LDS one workgroup may use
 constexpr int kExpandThreads = 256;  // per-beam expansion workgroup
 constexpr int kMergeThreads = 256;   // per-query merge workgroup (dense path)
 }
 
+namespace cb {
+// Workspace of the radix-select path (device pointers; sizes per query).
+struct WideDev {
+    int32_t* cand_off = nullptr;   // [Q_max][K+1] first candidate of each slot within its query
+    int32_t* chunk_off = nullptr;  // [Q_max][K+1] first chunk of each slot within its query
+    uint64_t* cand = nullptr;      // [Q_max][cap] candidates: z bits | parent | token, then keys
+    float* cms = nullptr;          // [Q_max][chunk_cap][2] (max z, sum exp(z - max)) per chunk
+    uint32_t* hist = nullptr;      // [Q_max][2][radix bins] digit histograms of the two GPU-wide passes
+    void* sel = nullptr;           // [Q_max] selection state
+    int32_t* surv_n = nullptr;     // [Q_max] survivors collected
+    uint64_t* surv = nullptr;      // [Q_max][survivor cap]
+    int64_t cap = 0, chunk_cap = 0;
+    int32_t G = 1;                 // workgroups per query in the chunk kernels
+};
+}  // namespace cb
+
 struct cb_plan {
     cb_index* idx = nullptr;
+    int32_t device = -1;          // device of the workspace (destroy needs no index)
     int32_t Q_max = 0, K = 0, d = 0;
     cb_dtype dtype = CB_F32;
     int32_t Kc_max = 0;           // per-beam survivors kept: min(K, widest step)
@@ -81,6 +99,9 @@ struct cb_plan {
     int32_t* live = nullptr;      // [Q_max*K] live beam slots (dense path)
     int32_t* ci_of = nullptr;     // [Q_max*K] compact index of each slot, -1 dead
     int32_t* n_live = nullptr;    // [1]
+    std::vector<int32_t> select;  // per step: CB_SELECT_* set by the caller
+    cb::WideDev wide;             // radix-select workspace (allocated when a step may use it)
+    int32_t wide_S = 0;           // widest row the radix workspace was sized for
     // decode state
     float* s[2] = {nullptr, nullptr};    // [R][d] float32 state vectors
     void* h = nullptr;                    // [R][d] dtype hidden vectors
@@ -134,6 +155,27 @@ hipError_t launch_hidden_update(int R, int K, int d, cb_dtype dt, const float* s
                                 hipStream_t st);
 hipError_t launch_backtrace(int R, int K, int L, const int32_t* hist_tok, const int32_t* hist_par,
                             int32_t* seqs, hipStream_t s);
+
+// Radix-select path (any beam width up to kMaxKRadix): per-slot offsets,
+// scores of every candidate (sparse dot or full-codebook gather), keys and
+// the first digit histogram, the second digit, survivor collection, and the
+// survivors' sort with the outputs.
+int wide_chunk();
+int wide_bins();
+int wide_surv_cap();
+size_t wide_sel_bytes();
+int wide_blocks_per_query(int Q);
+size_t wide_score_lds_bytes(int d, bool dense);
+hipError_t launch_wide_plan(const StepDev& st, int Q, int K, const int32_t* beam_rows, const float* acc,
+                            const WideDev& w, hipStream_t s);
+hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, int K, int d, const void* hidden,
+                             const void* W, const float* Z, const float* Zp, int64_t ldz, const int32_t* n_live,
+                             const int32_t* ci_of, const int32_t* beam_rows, const WideDev& w, hipStream_t s);
+hipError_t launch_wide_keys(int Q, int K, const float* acc, const WideDev& w, hipStream_t s);
+hipError_t launch_wide_refine(int Q, int K, const WideDev& w, hipStream_t s);
+hipError_t launch_wide_collect(int Q, const WideDev& w, hipStream_t s);
+hipError_t launch_wide_sort(const StepDev& st, int Q, int K, const int32_t* beam_rows, const WideDev& w,
+                            int32_t* tok, int32_t* par, int32_t* rows, float* logp, hipStream_t s);
 
 // Index construction (index_build.cpp).
 cb_status build_host_tables(const int32_t* sids, int64_t n_items, int32_t L, int32_t V, int32_t store,

@@ -1,0 +1,439 @@
+// Device primitives shared by the step kernels (wave64, gfx950): number
+// formats and candidate keys, wave and workgroup reductions, sorting
+// networks, scoring of valid tokens, next rows, output slots, and the tiling
+// constants of the full-codebook product.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "cb_internal.h"
+
+namespace cb {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kSmallRow = 64;  // rows up to this many tokens take the one-wave path
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// float32 -> bf16, round to nearest, ties to even (inputs finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t score_order_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float score_from_order_bits(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t make_key(float score, int parent, int token) {
+    return ((uint64_t)score_order_bits(score) << 32) | ((uint64_t)(1023 - parent) << 16) |
+           (uint64_t)(65535 - token);
+}
+
+// ---- wave and block primitives ----------------------------------------------
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
+    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src);
+    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+// Bitonic sort of the wave's 64 keys (one per lane), descending across lanes.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint64_t o = shfl_xor64(v, j);
+            const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
+            v = take_max ? umax64(v, o) : umin64(v, o);
+        }
+    return v;
+}
+
+// a, b sorted descending across lanes: the 64 largest of a and b, descending.
+// (max(a[l], b[63-l]) is a bitonic sequence holding them; a half-cleaner
+// cascade sorts it.)
+__device__ __forceinline__ uint64_t wave_merge_top(uint64_t a, uint64_t b) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint64_t c = umax64(a, shfl64(b, kWave - 1 - lane));
+#pragma unroll
+    for (int j = kWave / 2; j > 0; j >>= 1) {
+        const uint64_t o = shfl_xor64(c, j);
+        c = ((lane & j) == 0) ? umax64(c, o) : umin64(c, o);
+    }
+    return c;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Bitonic sort of the wave's 64 values (one per lane), descending across lanes.
+__device__ __forceinline__ uint32_t wave_sort_desc32(uint32_t v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)v, j);
+            const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
+            v = take_max ? (v > o ? v : o) : (v < o ? v : o);
+        }
+    return v;
+}
+
+constexpr int kWaveListCap = 256;
+
+// The Kc (<= 64) largest keys of the wave, descending in lanes 0..Kc-1 (0 when
+// fewer).  Lane l owns M candidates; score(i) is the high half of candidate i's
+// key (the order bits of its score, 0 = empty) and key(i) the full key.  tau =
+// the Kc-th largest lane maximum of the scores bounds the answer from below
+// (every key of the answer has a score >= tau); the candidates with score >=
+// tau get their full keys compacted (ballot order) into the wave's LDS list wl
+// [kWaveListCap], a window at a time, and are sorted with wave64 bitonic
+// networks.  No block barriers.
+template <int M, class ScoreF, class KeyF>
+__device__ uint64_t wave_top(int Kc, ScoreF score, KeyF key, uint64_t* wl) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t mx = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) mx = max(mx, score(i));
+    uint32_t tau = (uint32_t)__shfl((int)wave_sort_desc32(mx), Kc - 1);
+    if (tau == 0) tau = 1;
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) cnt += score(i) >= tau;
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    const int total = __shfl(incl, kWave - 1);
+    uint64_t best = 0;
+    bool first = true;
+    for (int s0 = 0; s0 < total; s0 += kWaveListCap) {
+        int pos = incl - cnt;
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            if (score(i) >= tau) {
+                if (pos >= s0 && pos < s0 + kWaveListCap) wl[pos - s0] = key(i);
+                ++pos;
+            }
+        }
+        wave_lds_sync();
+        const int w = min(kWaveListCap, total - s0);
+        for (int c0 = 0; c0 < w; c0 += kWave) {
+            const uint64_t v = wave_sort_desc(c0 + lane < w ? wl[c0 + lane] : 0ull);
+            best = first ? v : wave_merge_top(best, v);
+            first = false;
+        }
+        wave_lds_sync();
+    }
+    return best;
+}
+
+// Block reductions in a fixed order (deterministic); every thread gets the result.
+template <int NT>
+__device__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / kWave; ++i) r = fmaxf(r, red[i]);
+    __syncthreads();
+    return r;
+}
+
+template <int NT, typename T>
+__device__ T block_sum(T v, T* red) {
+    v = wave_sum(v);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+    __syncthreads();
+    T r = red[0];
+#pragma unroll
+    for (int i = 1; i < NT / kWave; ++i) r += red[i];
+    __syncthreads();
+    return r;
+}
+
+// Exclusive prefix sum of c over the block; *total receives the block sum.
+template <int NT>
+__device__ int block_exclusive_scan(int c, int* red, int* total) {
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    int x = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) red[w] = x;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; ++i) {
+        int v = red[i];
+        off += (i < w) ? v : 0;
+        tot += v;
+    }
+    __syncthreads();
+    *total = tot;
+    return off + x - c;
+}
+
+// The 64 largest of one key per thread, descending, in the lanes of wave 0.
+// The waves' sorted lists are merged pairwise as a tree.  stage: LDS [NT/2].
+// All threads call.
+template <int NT>
+__device__ uint64_t block_top64(uint64_t v, uint64_t* stage) {
+    v = wave_sort_desc(v);
+    const int w = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int half = NT / kWave / 2; half >= 1; half >>= 1) {
+        if (w >= half && w < 2 * half) stage[(w - half) * kWave + lane] = v;
+        __syncthreads();
+        if (w < half) v = wave_merge_top(v, stage[w * kWave + lane]);
+        __syncthreads();
+    }
+    return v;
+}
+
+// The Kc (<= 64) largest of the n keys key(0..n-1) (0 = empty), descending,
+// written by wave 0 to out[0..Kc) (0-padded).  stage: LDS [NT]; list: LDS
+// int [n].  All threads call; out is complete after the next barrier.
+template <int NT, class KeyF>
+__device__ void block_select_top(int n, int Kc, KeyF key, uint64_t* out, uint64_t* stage, int* list, int* red_i,
+                                 uint64_t* bcast) {
+    const int tid = threadIdx.x;
+    if (n <= NT) {
+        const uint64_t top = block_top64<NT>(tid < n ? key(tid) : 0ull, stage);
+        if (tid < Kc) out[tid] = top;
+        return;
+    }
+    uint64_t mx = 0;
+    for (int j = tid; j < n; j += NT) mx = umax64(mx, key(j));
+    const uint64_t t = block_top64<NT>(mx, stage);
+    if (tid == Kc - 1) *bcast = t;
+    __syncthreads();
+    const uint64_t tau = umax64(*bcast, 1ull);
+    int c = 0;
+    for (int j = tid; j < n; j += NT) c += key(j) >= tau;
+    int total;
+    int pos = block_exclusive_scan<NT>(c, red_i, &total);
+    for (int j = tid; j < n; j += NT)
+        if (key(j) >= tau) list[pos++] = j;
+    __syncthreads();
+    uint64_t best = 0;
+    for (int base = 0; base < total; base += NT) {
+        const uint64_t top = block_top64<NT>(base + tid < total ? key(list[base + tid]) : 0ull, stage);
+        if (tid < kWave) best = base == 0 ? top : wave_merge_top(best, top);
+    }
+    if (tid < Kc) out[tid] = best;
+}
+
+// 8 consecutive elements (16-byte aligned) as float.
+__device__ __forceinline__ void load8(const uint16_t* p, float* o) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    o[0] = __uint_as_float(v.x << 16);
+    o[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    o[2] = __uint_as_float(v.y << 16);
+    o[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    o[4] = __uint_as_float(v.z << 16);
+    o[5] = __uint_as_float(v.z & 0xFFFF0000u);
+    o[6] = __uint_as_float(v.w << 16);
+    o[7] = __uint_as_float(v.w & 0xFFFF0000u);
+}
+__device__ __forceinline__ void load8(const float* p, float* o) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+__device__ __forceinline__ float dot8(const float* h, const float* w, float s) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = fmaf(h[i], w[i], s);
+    return s;
+}
+
+__device__ __forceinline__ bool beam_live(const StepDev& st, int32_t r, float a) {
+    return r >= 0 && (int64_t)r < st.n_rows && a > -INFINITY;
+}
+
+// a1 for one beam, whole block: the row's valid tokens in ascending order into
+// tok_s[0..n).
+template <int NT>
+__device__ void block_fill_tokens(const StepDev& st, int32_t r, uint32_t e0, int n, uint16_t* tok_s, int* red_i) {
+    if (st.store == CB_STORE_CSR) {
+        for (int j = threadIdx.x; j < n; j += NT) tok_s[j] = st.tok[e0 + j];
+        return;
+    }
+    const uint32_t* rb = st.bits + (int64_t)r * st.words;
+    int base = 0;
+    for (int w0 = 0; w0 < st.words; w0 += NT) {
+        const int w = w0 + threadIdx.x;
+        uint32_t word = w < st.words ? rb[w] : 0u;
+        int tot;
+        int pos = base + block_exclusive_scan<NT>(__popc(word), red_i, &tot);
+        while (word) {
+            const int bit = __ffs(word) - 1;
+            tok_s[pos++] = (uint16_t)(w * 32 + bit);
+            word &= word - 1;
+        }
+        base += tot;
+    }
+}
+
+// a2 (sparse) for one beam, whole block: z_s[j] = <h, W_t[tok_s[j]]>, one wave
+// per token, up to four tokens in flight per wave.
+template <typename DT, int NT>
+__device__ void block_scores(const float* h_s, const DT* __restrict__ W, int d, const uint16_t* tok_s, int n,
+                             float* z_s) {
+    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int NW = NT / kWave;
+    constexpr int U = 4;
+    for (int j0 = threadIdx.x / kWave; j0 < n; j0 += U * NW) {
+        const DT* wr[U];
+        float s[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * NW;
+            wr[u] = W + (int64_t)tok_s[j < n ? j : j0] * d;
+            s[u] = 0.f;
+        }
+        for (int i = lane * 8; i < d; i += kWave * 8) {
+            float h[8];
+            load8(h_s + i, h);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (j0 + u * NW < n) {
+                    float w8[8];
+                    load8(wr[u] + i, w8);
+                    s[u] = dot8(h, w8, s[u]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float t = wave_sum(s[u]);
+            if (lane == 0 && j0 + u * NW < n) z_s[j0 + u * NW] = t;
+        }
+    }
+}
+
+// a3 for one beam, whole block: log-sum-exp of z_s[0..n).
+template <int NT>
+__device__ float block_lse(const float* z_s, int n, float* red_f) {
+    float m = -INFINITY;
+    for (int j = threadIdx.x; j < n; j += NT) m = fmaxf(m, z_s[j]);
+    m = block_max<NT>(m, red_f);
+    float se = 0.f;
+    for (int j = threadIdx.x; j < n; j += NT) se += expf(z_s[j] - m);
+    se = block_sum<NT>(se, red_f);
+    return m + logf(se);
+}
+
+// Next-step row of `token` in row r: its edge position.
+__device__ int32_t edge_of(const StepDev& st, int32_t r, int token) {
+    const uint32_t e0 = st.row_ptr[r];
+    if (st.store == CB_STORE_CSR) {
+        uint32_t lo = 0, hi = st.row_ptr[r + 1] - e0;
+        while (lo < hi) {
+            uint32_t mid = (lo + hi) >> 1;
+            if ((int)st.tok[e0 + mid] < token) lo = mid + 1; else hi = mid;
+        }
+        return (int32_t)(e0 + lo);
+    }
+    const int64_t x = (int64_t)r * st.words + (token >> 5);
+    return (int32_t)(e0 + st.rank[x] + __popc(st.bits[x] & ((1u << (token & 31)) - 1u)));
+}
+
+// Output slot i of query q from its key.
+__device__ void emit(const StepDev& st, int q, int K, int i, uint64_t key, const int32_t* __restrict__ beam_rows,
+                     int32_t* out_tok, int32_t* out_par, int32_t* out_rows, float* out_logp) {
+    const int64_t o = (int64_t)q * K + i;
+    if (key == 0ull) {
+        out_tok[o] = -1;
+        out_par[o] = -1;
+        out_rows[o] = -1;
+        out_logp[o] = -INFINITY;
+        return;
+    }
+    const int parent = 1023 - (int)((key >> 16) & 1023u);
+    const int token = 65535 - (int)(key & 0xFFFFu);
+    out_tok[o] = token;
+    out_par[o] = parent;
+    out_rows[o] = edge_of(st, beam_rows[(int64_t)q * K + parent], token);
+    out_logp[o] = score_from_order_bits((uint32_t)(key >> 32));
+}
+
+// ---- full-codebook product tiling (shared with its consumers) ---------------
+
+constexpr int kBM = 128, kBN = 128, kBK = 64, kLDP = kBK + 8;
+constexpr int kWM = 32, kWN = 64;  // per-wave tile: 1 x 2 MFMA 32x32 blocks
+constexpr int kGemmThreads = (kBM / kWM) * (kBN / kWN) * 64;
+constexpr int kGemmLds = 2 * (kBM + kBN) * kLDP * 2;  // double-buffered A and B tiles (bytes)
+constexpr int kSplitMax = 8;   // k-slices for steps with few live beams
+constexpr int kSplitRows = 2 * kBM;
+constexpr int kCUs = 256;
+
+// Number of k-slices the full-codebook product uses for n_live live beams:
+// more than one only when the tiles alone would leave most compute units idle.
+// The slices' partial sums are added in slice order by the consumer.
+__host__ __device__ inline int gemm_split(int n_live, int V, int d) {
+    const int tiles = ((n_live + kBM - 1) / kBM) * ((V + kBN - 1) / kBN);
+    int s = 1;
+    if (n_live > kSplitRows) return 1;
+    while (s < kSplitMax && tiles * s * 2 <= kCUs && (d / kBK) % (s * 2) == 0) s *= 2;
+    return s;
+}
+
+__host__ __device__ inline int gemm_grid(int R, int V) {
+    const int nt = (V + kBN - 1) / kBN;
+    const int full = ((R + kBM - 1) / kBM) * nt;
+    const int split = kSplitMax * ((kSplitRows + kBM - 1) / kBM) * nt;
+    return full > split ? full : split;
+}
+
+}  // namespace
+}  // namespace cb

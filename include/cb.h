@@ -73,6 +73,15 @@ typedef enum { CB_PATH_AUTO = 0, CB_PATH_DENSE = 1, CB_PATH_SPARSE = 2 } cb_path
  * for the first levels, CSR below).  AUTO picks the smaller of the two. */
 typedef enum { CB_STORE_AUTO = 0, CB_STORE_CSR = 1, CB_STORE_BITMAP = 2 } cb_store;
 
+/* Per-query top-K of a step (the segmented top-K with the (score desc,
+ * parent asc, token asc) tie-break; ZeroGR "The pipeline", FlashTrie App. D.3
+ * block merge).  LDS: the query's best keys are kept by one wavefront in
+ * registers and LDS, K <= 64, rows no wider than the fused kernels' LDS.
+ * RADIX: every candidate's key is written to HBM and the K-th largest is
+ * found by radix select over the whole GPU, K <= 1024, any row width.  AUTO
+ * takes LDS where it applies, else RADIX.  Both give identical outputs. */
+typedef enum { CB_SELECT_AUTO = 0, CB_SELECT_LDS = 1, CB_SELECT_RADIX = 2 } cb_select;
+
 typedef struct cb_index cb_index; /* owns the device-resident step tables */
 typedef struct cb_plan cb_plan;   /* owns the workspace for (Q_max, K, d, dtype) and the per-step path */
 
@@ -114,7 +123,7 @@ cb_status cb_index_row(const cb_index* idx, int32_t t, int64_t row,
                        int32_t* tokens, int64_t* next_rows, int32_t cap, int32_t* n);
 
 /* Release an index (frees device tables).  NULL is ignored.  Plans created
- * from it must be destroyed first. */
+ * from it must not be used afterwards (destroying them is still allowed). */
 void cb_free_index(cb_index* idx);
 
 /* Create a plan: allocates, once, every device buffer the step and decode
@@ -122,9 +131,24 @@ void cb_free_index(cb_index* idx);
  * and element type dtype (of W and of the hidden vectors).  Nothing is
  * allocated later by cb_step / cb_decode (FlashTrie App. D: per-batch state
  * allocated once).  The index must stay alive while the plan exists.
- * Errors: CB_EINVAL, CB_ECAPACITY (K > 64, or a step too wide for the
- * per-workgroup LDS of the step kernels), CB_ENOMEM, CB_EHIP. */
+ * Beam widths up to 64 use the LDS selection on every step whose rows fit
+ * it; wider beams and wider rows use the radix selection, whose candidate
+ * workspace (12 bytes per candidate slot: Q_max * K * widest row) is
+ * allocated here when some step needs it, else on the first
+ * cb_set_select(..., CB_SELECT_RADIX).
+ * Errors: CB_EINVAL, CB_ECAPACITY (K > 1024, d > 16384, or a candidate
+ * workspace beyond 2^31 slots per query), CB_ENOMEM, CB_EHIP. */
 cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_dtype dtype, cb_plan** out);
+
+/* Force the top-K selection of step t (tests run both ways).  CB_SELECT_LDS
+ * where it does not apply returns CB_ECAPACITY; CB_SELECT_RADIX may allocate
+ * the radix workspace (CB_ENOMEM).  CB_SELECT_AUTO restores the default.
+ * Synchronous with respect to the host; do not call while steps of this plan
+ * are being captured. */
+cb_status cb_set_select(cb_plan* plan, int32_t t, cb_select select);
+
+/* The selection step t will use (never CB_SELECT_AUTO). */
+cb_status cb_get_select(const cb_plan* plan, int32_t t, cb_select* select);
 
 /* Force the scoring path of step t (tests run both ways).  CB_PATH_AUTO
  * restores the measured or default choice. */
@@ -191,7 +215,14 @@ typedef enum {
     CB_KERNEL_EXPAND_DENSE = 3,   /* slot fill + column gather + softmax + per-beam top-K */
     CB_KERNEL_MERGE = 4,          /* per-query top-K and next rows (after the dense expansion) */
     CB_KERNEL_STEP_QUERY = 5,     /* the whole sparse step, one workgroup per query */
-    CB_KERNEL_LIVE_ROWS = 6       /* list of live beams for the full-codebook scores */
+    CB_KERNEL_LIVE_ROWS = 6,      /* list of live beams for the full-codebook scores */
+    CB_KERNEL_RADIX_PLAN = 7,     /* radix selection: per-slot candidate offsets, state reset */
+    CB_KERNEL_RADIX_SCORE_SPARSE = 8, /* radix selection: slot fill + gather-dot of every candidate */
+    CB_KERNEL_RADIX_SCORE_DENSE = 9,  /* radix selection: slot fill + column gather of every candidate */
+    CB_KERNEL_RADIX_KEYS = 10,    /* radix selection: softmax, keys, first digit */
+    CB_KERNEL_RADIX_REFINE = 11,  /* radix selection: second digit */
+    CB_KERNEL_RADIX_COLLECT = 12, /* radix selection: survivors */
+    CB_KERNEL_RADIX_SORT = 13     /* radix selection: survivors sorted, outputs and next rows */
 } cb_kernel;
 
 typedef struct {

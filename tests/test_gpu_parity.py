@@ -257,3 +257,14 @@ def test_step_argument_errors():
     with pytest.raises(cb.CbError) as e:
         idx.plan(1, 2000, cfg.d, cfg.dtype)
     assert e.value.status == -5
+
+
+def test_plan_released_after_its_index():
+    """Destroying a plan after its index (as a garbage collector may order
+    them) touches nothing of the index and leaves no HIP error pending."""
+    w = workload("tiny")
+    cfg = w["cfg"]
+    idx = cb.Index(w["items"], cfg.V, device=0)
+    plan = idx.plan(cfg.Q, cfg.K, cfg.d, cfg.dtype)
+    idx.close()
+    plan.close()

@@ -36,6 +36,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50, help="timed passes")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="production")
+    ap.add_argument("--K", type=int, default=None, help="beam width other than the workload's (sweeps)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
     ap.add_argument("--no-graph", action="store_true")
@@ -100,7 +101,7 @@ def main():
     import csr_constrained_beam_amd as cb
     from synth import get_config, make_catalog, make_dense
 
-    cfg = get_config(args.config)
+    cfg = get_config(args.config, K=args.K) if args.K else get_config(args.config)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
@@ -147,8 +148,7 @@ def main():
     trace_h, trace_rows, trace_acc = rec["trace_h"], rec["trace_rows"], rec["trace_acc"]
     rows_np = trace_rows.cpu().numpy()
 
-    # workload accounting from the library's own tables (a host-side copy of the index)
-    hidx = cb.Index(items, cfg.V, device=-1)
+    # workload accounting from the library's own tables (rows read back from the device)
     words = (V + 31) // 32
     steps = []
     for t in range(L):
@@ -156,14 +156,16 @@ def main():
         fan = np.zeros(len(live), np.int64)
         toks = set()
         for i, b in enumerate(live):
-            tk, _ = hidx.row(t, int(rows_np[t][b]))
+            tk, _ = idx.row(t, int(rows_np[t][b]))
             fan[i] = len(tk)
             toks.update(tk.tolist())
         S = info[t]["max_fanout"]
         Kc = min(K, max(S, 1))
         n_exp = int(fan.sum())
+        chunks = int(((fan + 63) // 64).sum())
         idx_bytes = len(live) * 8 + (n_exp * 2 if info[t]["storage"] == "csr" else len(live) * words * 4)
         state_bytes = R * 8 + R * Kc * 8
+        w_bytes = len(live) * d * es + len(toks) * d * es  # hidden vectors and distinct W_t rows
         steps.append({
             "t": t, "path": paths[t], "storage": info[t]["storage"], "live_beams": int(len(live)),
             "expansions": n_exp, "max_fanout": S, "mean_fanout": float(fan.mean()) if len(fan) else 0.0,
@@ -175,12 +177,19 @@ def main():
                 "expand_dense": state_bytes + idx_bytes + n_exp * 4,
                 "merge": Q * K * Kc * 8 + R * 4 + R * 16 + min(R, n_exp) * 8,
                 "gemm_" + cfg.dtype: R * d * es + V * d * es + R * V * 4,
+                # radix path: candidates written to HBM as 8-byte keys
+                "radix_score_sparse": R * 8 + idx_bytes + w_bytes + n_exp * 8 + chunks * 8,
+                "radix_score_dense": R * 8 + idx_bytes + n_exp * 4 + n_exp * 8 + chunks * 8,
+                "radix_keys": n_exp * 16 + chunks * 8 + len(live) * 4,
+                "radix_refine": n_exp * 8,
+                "radix_collect": n_exp * 8,
+                "radix_sort": min(n_exp, K) * 8 + R * 24,
             },
             "flops": {"gemm_" + cfg.dtype: 2 * len(live) * V * d, "expand_sparse": 2 * d * n_exp,
-                      "step_query": 2 * d * n_exp},
+                      "step_query": 2 * d * n_exp, "radix_score_sparse": 2 * d * n_exp},
+            "selection": plan.get_select(t),
         })
     expansions = sum(s["expansions"] for s in steps)
-    del hidx
 
     # teacher-forced pass over all L steps, outputs into fixed buffers
     outs = [tuple(torch.empty(R, dtype=dt, device=dev) for dt in (torch.int32, torch.int32, torch.int32,
@@ -228,7 +237,7 @@ def main():
     ms_per_pass = e0.elapsed_time(e1) / args.steps
 
     # per-kernel durations: HIP events around every launch, eager passes
-    plan.profile_start(capacity=args.steps * L * 4 + 16)
+    plan.profile_start(capacity=args.steps * L * 10 + 16)
     for _ in range(args.steps):
         one_pass()
     recs = plan.profile_stop()
@@ -276,7 +285,9 @@ def main():
         import oracle
         threads = min(16, os.cpu_count() or 1)
         t0 = time.time()
-        T = oracle.Trie(items, cfg.V)
+        # the pointer trie of 100M 12-token items does not fit the host: sorted ranges instead
+        kind = "sorted-range" if cfg.n_items > 50_000_000 else "pointer-trie"
+        T = oracle.SortedRange(items, cfg.V) if kind == "sorted-range" else oracle.Trie(items, cfg.V)
         trie_s = time.time() - t0
         bf16 = cfg.dtype == "bf16"
         r0 = T.decode(K, dense["q"], dense["P"], dense["W"], bf16=bf16, trace=True, threads=threads)
@@ -293,7 +304,7 @@ def main():
             reps += 1
         cpu = {"value": cexp * reps / el, "unit": "beam-expansions/s", "cores": threads, "kind": "oracle",
                "sample": "the full batch (%d queries x %d steps, %d expansions per pass), %d passes, %.1f s; "
-                         "pointer-trie build (%.1f s) excluded" % (Q, L, cexp, reps, el, trie_s),
+                         "%s build (%.1f s) excluded" % (Q, L, cexp, reps, el, kind, trie_s),
                "ms_per_pass": 1000 * el / reps}
         del T
 

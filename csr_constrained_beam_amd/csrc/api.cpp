@@ -42,6 +42,7 @@ cb_status hip_fail(const char* where, hipError_t e) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 size_t dtype_size(cb_dtype dt) { return dt == CB_BF16 ? 2 : 4; }
 
@@ -87,6 +88,8 @@ bool lds_select_ok(const cb_plan* p, int t) {
 int32_t resolve_select(const cb_plan* p, int t) {
     const int32_t f = p->select[(size_t)t];
     if (f == CB_SELECT_LDS || f == CB_SELECT_RADIX) return f;
+    const int32_t tu = p->tuned_select[(size_t)t];
+    if (tu == CB_SELECT_RADIX || (tu == CB_SELECT_LDS && lds_select_ok(p, t))) return tu;
     return lds_select_ok(p, t) ? CB_SELECT_LDS : CB_SELECT_RADIX;
 }
 
@@ -95,6 +98,7 @@ void wide_release(cb_plan* p) {
     dev_free(w.cand_off);
     dev_free(w.chunk_off);
     dev_free(w.cand);
+    dev_free(w.info);
     dev_free(w.cms);
     dev_free(w.hist);
     dev_free(w.sel);
@@ -122,6 +126,7 @@ cb_status wide_alloc(cb_plan* p) {
     cb_status st = dev_alloc(&w.cand_off, Q * (p->K + 1), "radix offsets");
     if (st == CB_OK) st = dev_alloc(&w.chunk_off, Q * (p->K + 1), "radix chunk offsets");
     if (st == CB_OK) st = dev_alloc(&w.cand, Q * (size_t)cap, "radix candidates");
+    if (st == CB_OK) st = dev_alloc(&w.info, Q * (size_t)cap, "radix candidate rows");
     if (st == CB_OK) st = dev_alloc(&w.cms, Q * (size_t)chunk_cap * 2, "radix chunk softmax");
     if (st == CB_OK) st = dev_alloc(&w.hist, Q * 2 * (size_t)wide_bins(), "radix histograms");
     if (st == CB_OK) {
@@ -162,21 +167,14 @@ cb_status run_step_radix(cb_plan* p, int t, int Q, int32_t path, const void* hid
     const cb_index* idx = p->idx;
     const cb::StepDev sd = idx->steps[(size_t)t].dev(idx->words);
     const int R = Q * p->K;
-    WideDev w = p->wide;
+    const WideDev& w = p->wide;
     if (!w.cand) {
         set_error("cb_step: radix workspace missing");
         return CB_EINVAL;
     }
-    w.G = wide_blocks_per_query(Q);
-    const int GQ = w.G * Q;
+    const int GS = wide_blocks_per_query(Q) * Q, GH = wide_hist_blocks_per_query(Q) * Q;
     const bool dense = path == CB_PATH_DENSE;
     hipError_t e;
-    {
-        ProfMark m(p, s, t, CB_KERNEL_RADIX_PLAN, 1024, Q);
-        e = launch_wide_plan(sd, Q, p->K, rows, acc, w, s);
-        m.done();
-        if (e != hipSuccess) return hip_fail("cb_step: radix offsets", e);
-    }
     if (dense) {
         {
             ProfMark m(p, s, t, CB_KERNEL_LIVE_ROWS, 1024, 1);
@@ -192,27 +190,27 @@ cb_status run_step_radix(cb_plan* p, int t, int Q, int32_t path, const void* hid
         if (e != hipSuccess) return hip_fail("cb_step: full-codebook scores", e);
     }
     {
-        ProfMark m(p, s, t, dense ? CB_KERNEL_RADIX_SCORE_DENSE : CB_KERNEL_RADIX_SCORE_SPARSE, 256, GQ);
+        ProfMark m(p, s, t, dense ? CB_KERNEL_RADIX_SCORE_DENSE : CB_KERNEL_RADIX_SCORE_SPARSE, 256, GS);
         e = launch_wide_score(sd, dense, p->dtype, Q, p->K, p->d, hidden, Wt, p->Z, p->Zp, idx->V, p->n_live,
-                              p->ci_of, rows, w, s);
+                              p->ci_of, rows, acc, w, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: radix scores", e);
     }
     {
-        ProfMark m(p, s, t, CB_KERNEL_RADIX_KEYS, 256, GQ);
+        ProfMark m(p, s, t, CB_KERNEL_RADIX_KEYS, 256, GH);
         e = launch_wide_keys(Q, p->K, acc, w, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: radix keys", e);
     }
     {
-        ProfMark m(p, s, t, CB_KERNEL_RADIX_REFINE, 256, GQ);
+        ProfMark m(p, s, t, CB_KERNEL_RADIX_REFINE, 256, GH);
         e = launch_wide_refine(Q, p->K, w, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: radix refine", e);
     }
     {
-        ProfMark m(p, s, t, CB_KERNEL_RADIX_COLLECT, 256, GQ);
-        e = launch_wide_collect(Q, w, s);
+        ProfMark m(p, s, t, CB_KERNEL_RADIX_COLLECT, 256, GH);
+        e = launch_wide_collect(Q, p->K, w, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: radix collect", e);
     }
@@ -226,15 +224,16 @@ cb_status run_step_radix(cb_plan* p, int t, int Q, int32_t path, const void* hid
 }
 
 // Enqueue one step (no validation).
-cb_status run_step(cb_plan* p, int t, int Q, int32_t path, const void* hidden, const void* Wt, const int32_t* rows,
-                   const float* acc, int32_t* ot, int32_t* op, int32_t* orow, float* ol, hipStream_t s) {
+cb_status run_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const void* hidden, const void* Wt,
+                   const int32_t* rows, const float* acc, int32_t* ot, int32_t* op, int32_t* orow, float* ol,
+                   hipStream_t s) {
     const cb_index* idx = p->idx;
     const cb::StepTable& T = idx->steps[(size_t)t];
     const cb::StepDev sd = T.dev(idx->words);
     const int R = Q * p->K;
     const int Kc = std::min(p->K, std::max(T.S, 1));
     hipError_t e;
-    if (resolve_select(p, t) == CB_SELECT_RADIX) return run_step_radix(p, t, Q, path, hidden, Wt, rows, acc, ot, op, orow, ol, s);
+    if (sel == CB_SELECT_RADIX) return run_step_radix(p, t, Q, path, hidden, Wt, rows, acc, ot, op, orow, ol, s);
     if (path == CB_PATH_SPARSE) {
         ProfMark m(p, s, t, CB_KERNEL_STEP_QUERY, query_threads(p->K), Q);
         e = launch_step_query(sd, p->dtype, Q, p->K, Kc, p->d, hidden, Wt, rows, acc, ot, op, orow, ol, s);
@@ -525,6 +524,7 @@ cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_
     p->tune_dense_us.assign((size_t)idx->L, -1.f);
     p->tune_sparse_us.assign((size_t)idx->L, -1.f);
     p->select.assign((size_t)idx->L, CB_SELECT_AUTO);
+    p->tuned_select.assign((size_t)idx->L, 0);
     const size_t R = (size_t)Q_max * K;
     cb_status st = dev_alloc(&p->keys, R * Kc, "candidate keys");
     if (st == CB_OK) st = dev_alloc(&p->Z, R * (size_t)idx->V, "full-codebook scores");
@@ -623,15 +623,22 @@ cb_status cb_step(cb_plan* p, int32_t t, int32_t Q, const void* hidden, const vo
         return CB_EINVAL;
     }
     if (Q == 0) return CB_OK;
-    const void* ptrs[] = {hidden, W_t, beam_rows, acc_logp, out_tokens, out_parents, out_rows, out_logp};
-    for (const void* x : ptrs)
+    // hidden vectors and W_t rows are read 16 bytes at a time; the per-slot arrays element-wise
+    const void* vec[] = {hidden, W_t};
+    const void* ptrs[] = {beam_rows, acc_logp, out_tokens, out_parents, out_rows, out_logp};
+    for (const void* x : vec)
         if (!x || !aligned16(x)) {
-            set_error("cb_step: a device pointer is NULL or not 16-byte aligned");
+            set_error("cb_step: hidden or W_t is NULL or not 16-byte aligned");
+            return CB_EINVAL;
+        }
+    for (const void* x : ptrs)
+        if (!x || !aligned4(x)) {
+            set_error("cb_step: a per-slot array is NULL or not 4-byte aligned");
             return CB_EINVAL;
         }
     DeviceGuard g(p->idx->device);
-    return run_step(p, t, Q, resolve_path(p, t), hidden, W_t, beam_rows, acc_logp, out_tokens, out_parents, out_rows,
-                    out_logp, (hipStream_t)stream);
+    return run_step(p, t, Q, resolve_path(p, t), resolve_select(p, t), hidden, W_t, beam_rows, acc_logp, out_tokens,
+                    out_parents, out_rows, out_logp, (hipStream_t)stream);
 }
 
 static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float* P, const void* W, int32_t* out_seqs,
@@ -672,35 +679,57 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
                 break;
             }
         }
-        if (reps > 0 && p->forced[(size_t)t] == CB_PATH_AUTO) {
-            // time both paths on this step's inputs, outputs to scratch
-            float us[2] = {-1.f, -1.f};
+        const bool path_free = p->forced[(size_t)t] == CB_PATH_AUTO;
+        const bool sel_free = p->select[(size_t)t] == CB_SELECT_AUTO;
+        if (reps > 0 && (path_free || sel_free)) {
+            // time every allowed (scoring path, selection) pair on this step's inputs, outputs to scratch
+            float best_us[2] = {-1.f, -1.f};  // per path, best over the selections
+            float best = -1.f;
+            int32_t best_path = 0, best_sel = 0;
             const int32_t paths[2] = {CB_PATH_DENSE, CB_PATH_SPARSE};
+            const int32_t sels[2] = {CB_SELECT_LDS, CB_SELECT_RADIX};
             for (int k = 0; k < 2 && st == CB_OK; ++k) {
+                if (!path_free && paths[k] != resolve_path(p, t)) continue;
                 if (paths[k] == CB_PATH_DENSE && !dense_available(p)) continue;
-                st = run_step(p, t, Q, paths[k], p->h, Wt, p->rows[cur], p->acc[cur], p->scratch_tok, p->scratch_par,
-                              p->scratch_rows, p->scratch_logp, s);
-                if (st != CB_OK) break;
-                (void)hipEventRecord(ev0, s);
-                for (int r = 0; r < reps && st == CB_OK; ++r)
-                    st = run_step(p, t, Q, paths[k], p->h, Wt, p->rows[cur], p->acc[cur], p->scratch_tok,
+                for (int m = 0; m < 2 && st == CB_OK; ++m) {
+                    if (!sel_free && sels[m] != p->select[(size_t)t]) continue;
+                    if (sels[m] == CB_SELECT_LDS && !lds_select_ok(p, t)) continue;
+                    if (sels[m] == CB_SELECT_RADIX && wide_alloc(p) != CB_OK) {
+                        (void)hipGetLastError();
+                        clear_error();
+                        continue;
+                    }
+                    st = run_step(p, t, Q, paths[k], sels[m], p->h, Wt, p->rows[cur], p->acc[cur], p->scratch_tok,
                                   p->scratch_par, p->scratch_rows, p->scratch_logp, s);
-                (void)hipEventRecord(ev1, s);
-                if ((e = hipEventSynchronize(ev1)) != hipSuccess) {
-                    st = hip_fail("cb_tune: synchronise", e);
-                    break;
+                    if (st != CB_OK) break;
+                    (void)hipEventRecord(ev0, s);
+                    for (int r = 0; r < reps && st == CB_OK; ++r)
+                        st = run_step(p, t, Q, paths[k], sels[m], p->h, Wt, p->rows[cur], p->acc[cur],
+                                      p->scratch_tok, p->scratch_par, p->scratch_rows, p->scratch_logp, s);
+                    (void)hipEventRecord(ev1, s);
+                    if ((e = hipEventSynchronize(ev1)) != hipSuccess) {
+                        st = hip_fail("cb_tune: synchronise", e);
+                        break;
+                    }
+                    float ms = 0.f;
+                    (void)hipEventElapsedTime(&ms, ev0, ev1);
+                    const float us = ms * 1000.f / (float)reps;
+                    if (best_us[k] < 0.f || us < best_us[k]) best_us[k] = us;
+                    if (best < 0.f || us < best) {
+                        best = us;
+                        best_path = paths[k];
+                        best_sel = sels[m];
+                    }
                 }
-                float ms = 0.f;
-                (void)hipEventElapsedTime(&ms, ev0, ev1);
-                us[k] = ms * 1000.f / (float)reps;
             }
             if (st != CB_OK) break;
-            p->tune_dense_us[(size_t)t] = us[0];
-            p->tune_sparse_us[(size_t)t] = us[1];
-            p->tuned[(size_t)t] = (us[0] >= 0.f && us[0] < us[1]) ? CB_PATH_DENSE : CB_PATH_SPARSE;
+            p->tune_dense_us[(size_t)t] = best_us[0];
+            p->tune_sparse_us[(size_t)t] = best_us[1];
+            if (best_path) p->tuned[(size_t)t] = best_path;
+            if (best_sel) p->tuned_select[(size_t)t] = best_sel;
         }
-        st = run_step(p, t, Q, resolve_path(p, t), p->h, Wt, p->rows[cur], p->acc[cur], p->hist_tok + (size_t)t * R,
-                      p->hist_par + (size_t)t * R, p->rows[1 - cur], p->acc[1 - cur], s);
+        st = run_step(p, t, Q, resolve_path(p, t), resolve_select(p, t), p->h, Wt, p->rows[cur], p->acc[cur],
+                      p->hist_tok + (size_t)t * R, p->hist_par + (size_t)t * R, p->rows[1 - cur], p->acc[1 - cur], s);
         if (st != CB_OK) break;
         if (t + 1 < L) {
             e = launch_hidden_update(R, K, d, p->dtype, p->s[cur], P + (size_t)t * V * d, p->hist_tok + (size_t)t * R,
@@ -734,10 +763,14 @@ cb_status cb_decode(cb_plan* p, int32_t Q, const float* q, const float* P, const
         set_error("cb_decode: q, W, out_* (and P when L > 1) must be device pointers");
         return CB_EINVAL;
     }
-    const void* ptrs[] = {q, P, W, out_seqs, out_logp, out_rows, trace_hidden, trace_rows, trace_acc};
+    const void* ptrs[] = {q, P, out_seqs, out_logp, out_rows, trace_hidden, trace_rows, trace_acc};
+    if (!aligned16(W)) {
+        set_error("cb_decode: W is not 16-byte aligned");
+        return CB_EINVAL;
+    }
     for (const void* x : ptrs)
-        if (x && !aligned16(x)) {
-            set_error("cb_decode: a device pointer is not 16-byte aligned");
+        if (x && !aligned4(x)) {
+            set_error("cb_decode: a device pointer is not 4-byte aligned");
             return CB_EINVAL;
         }
     DeviceGuard g(p->idx->device);

@@ -72,14 +72,14 @@ namespace cb {
 struct WideDev {
     int32_t* cand_off = nullptr;   // [Q_max][K+1] first candidate of each slot within its query
     int32_t* chunk_off = nullptr;  // [Q_max][K+1] first chunk of each slot within its query
-    uint64_t* cand = nullptr;      // [Q_max][cap] candidates: z bits | parent | token, then keys
+    uint64_t* cand = nullptr;      // [Q_max][cap] candidates: z bits | ~index, then keys
+    uint64_t* info = nullptr;      // [Q_max][cap] per candidate: next row | token | parent slot
     float* cms = nullptr;          // [Q_max][chunk_cap][2] (max z, sum exp(z - max)) per chunk
     uint32_t* hist = nullptr;      // [Q_max][2][radix bins] digit histograms of the two GPU-wide passes
     void* sel = nullptr;           // [Q_max] selection state
     int32_t* surv_n = nullptr;     // [Q_max] survivors collected
     uint64_t* surv = nullptr;      // [Q_max][survivor cap]
     int64_t cap = 0, chunk_cap = 0;
-    int32_t G = 1;                 // workgroups per query in the chunk kernels
 };
 }  // namespace cb
 
@@ -100,6 +100,7 @@ struct cb_plan {
     int32_t* ci_of = nullptr;     // [Q_max*K] compact index of each slot, -1 dead
     int32_t* n_live = nullptr;    // [1]
     std::vector<int32_t> select;  // per step: CB_SELECT_* set by the caller
+    std::vector<int32_t> tuned_select;  // per step: measured choice (0 = none)
     cb::WideDev wide;             // radix-select workspace (allocated when a step may use it)
     int32_t wide_S = 0;           // widest row the radix workspace was sized for
     // decode state
@@ -156,24 +157,24 @@ hipError_t launch_hidden_update(int R, int K, int d, cb_dtype dt, const float* s
 hipError_t launch_backtrace(int R, int K, int L, const int32_t* hist_tok, const int32_t* hist_par,
                             int32_t* seqs, hipStream_t s);
 
-// Radix-select path (any beam width up to kMaxKRadix): per-slot offsets,
-// scores of every candidate (sparse dot or full-codebook gather), keys and
-// the first digit histogram, the second digit, survivor collection, and the
-// survivors' sort with the outputs.
+// Radix-select path (any beam width up to kMaxKRadix): slot offsets and
+// scores of every candidate (sparse dot or full-codebook gather), keys and the
+// first digit, the second digit, survivor collection, and the survivors' sort
+// with the outputs.
 int wide_chunk();
 int wide_bins();
 int wide_surv_cap();
 size_t wide_sel_bytes();
 int wide_blocks_per_query(int Q);
+int wide_hist_blocks_per_query(int Q);
 size_t wide_score_lds_bytes(int d, bool dense);
-hipError_t launch_wide_plan(const StepDev& st, int Q, int K, const int32_t* beam_rows, const float* acc,
-                            const WideDev& w, hipStream_t s);
 hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, int K, int d, const void* hidden,
                              const void* W, const float* Z, const float* Zp, int64_t ldz, const int32_t* n_live,
-                             const int32_t* ci_of, const int32_t* beam_rows, const WideDev& w, hipStream_t s);
+                             const int32_t* ci_of, const int32_t* beam_rows, const float* acc, const WideDev& w,
+                             hipStream_t s);
 hipError_t launch_wide_keys(int Q, int K, const float* acc, const WideDev& w, hipStream_t s);
 hipError_t launch_wide_refine(int Q, int K, const WideDev& w, hipStream_t s);
-hipError_t launch_wide_collect(int Q, const WideDev& w, hipStream_t s);
+hipError_t launch_wide_collect(int Q, int K, const WideDev& w, hipStream_t s);
 hipError_t launch_wide_sort(const StepDev& st, int Q, int K, const int32_t* beam_rows, const WideDev& w,
                             int32_t* tok, int32_t* par, int32_t* rows, float* logp, hipStream_t s);
 

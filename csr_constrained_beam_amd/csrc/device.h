@@ -373,39 +373,6 @@ __device__ float block_lse(const float* z_s, int n, float* red_f) {
     return m + logf(se);
 }
 
-// Next-step row of `token` in row r: its edge position.
-__device__ int32_t edge_of(const StepDev& st, int32_t r, int token) {
-    const uint32_t e0 = st.row_ptr[r];
-    if (st.store == CB_STORE_CSR) {
-        uint32_t lo = 0, hi = st.row_ptr[r + 1] - e0;
-        while (lo < hi) {
-            uint32_t mid = (lo + hi) >> 1;
-            if ((int)st.tok[e0 + mid] < token) lo = mid + 1; else hi = mid;
-        }
-        return (int32_t)(e0 + lo);
-    }
-    const int64_t x = (int64_t)r * st.words + (token >> 5);
-    return (int32_t)(e0 + st.rank[x] + __popc(st.bits[x] & ((1u << (token & 31)) - 1u)));
-}
-
-// Output slot i of query q from its key.
-__device__ void emit(const StepDev& st, int q, int K, int i, uint64_t key, const int32_t* __restrict__ beam_rows,
-                     int32_t* out_tok, int32_t* out_par, int32_t* out_rows, float* out_logp) {
-    const int64_t o = (int64_t)q * K + i;
-    if (key == 0ull) {
-        out_tok[o] = -1;
-        out_par[o] = -1;
-        out_rows[o] = -1;
-        out_logp[o] = -INFINITY;
-        return;
-    }
-    const int parent = 1023 - (int)((key >> 16) & 1023u);
-    const int token = 65535 - (int)(key & 0xFFFFu);
-    out_tok[o] = token;
-    out_par[o] = parent;
-    out_rows[o] = edge_of(st, beam_rows[(int64_t)q * K + parent], token);
-    out_logp[o] = score_from_order_bits((uint32_t)(key >> 32));
-}
 
 // ---- full-codebook product tiling (shared with its consumers) ---------------
 

@@ -1,5 +1,35 @@
 // Radix-select path of one constrained beam-search step (gfx950, wave64):
 // beam widths up to 1024 and rows of any width.
+//
+// The per-query selection of kernels.hip holds a query's best keys in one
+// wavefront, which bounds K by 64.  For wider beams (FlashTrie's beam widths
+// of 100 to 1000, sec. 4.2) every candidate of a query is written to HBM as
+// its 64-bit key and the query's K-th largest key is found by radix select on
+// the high bits: 12-bit digits counted across the whole GPU (LDS histograms
+// per workgroup, added into the query's global histogram; the next kernel's
+// workgroups each read the finished histogram and pick the digit), after
+// which the survivors (keys >= the threshold) are sorted by one workgroup and
+// emitted.  Keys are distinct
+// within a query (parent, token), so the selection is exact and the order is
+// the (score desc, parent asc, token asc) order of the key.  If more than
+// kSurvCap keys still share the two digits (massive exact score ties), the
+// sort workgroup finishes the radix select on its own, 8 bits a pass.
+//
+// A query's candidates are laid out slot by slot, each slot's in ascending
+// token order, so a candidate's index within its query orders exactly as
+// (parent asc, token asc).  The radix keys therefore carry [63:32] the
+// order-preserving score bits and [31:0] the complement of that index (unique,
+// and descending key order is the tie-break); the candidate's token, parent
+// and next row (the edge position row_ptr[r] + j of its j-th valid token) sit
+// in a parallel array written when it is scored, so the outputs need one load.
+//
+// Work is cut into chunks of kWCH consecutive valid tokens of one beam; a
+// beam's log-sum-exp is combined from its chunks' (max, sum exp) pairs.
+//
+// Kernels per step: k_wide_score (slot offsets, scores, chunk softmax
+// partials), k_wide_keys (keys, first-digit histogram), k_wide_refine (first
+// digit, second-digit histogram), k_wide_collect (digits, survivors),
+// k_wide_sort (sort, outputs, next rows).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -10,40 +40,25 @@
 
 namespace cb {
 namespace {
-// ---- radix-select path: beam widths up to 1024 -----------------------------
-//
-// The per-query selection above holds a query's best keys in one wavefront,
-// which bounds K by 64.  For wider beams (FlashTrie's beam widths of 100 to
-// 1000, sec. 4.2) every candidate of a query is written to HBM as its 64-bit
-// key and the query's K-th largest key is found by radix select on the high
-// bits: two 12-bit digits counted across the whole GPU (LDS histograms per
-// workgroup, added into the query's global histogram; the last workgroup of
-// the query to finish picks the digit), after which the survivors (keys >=
-// the threshold, at most kSurvCap) are sorted in LDS and emitted.  Keys are
-// distinct within a query (parent, token), so the selection is exact and the
-// order is the (score desc, parent asc, token asc) order of the key.  If more
-// than kSurvCap keys still share the two digits (massive exact score ties),
-// the sort workgroup finishes the radix select on its own, 8 bits a pass.
-//
-// Work is cut into chunks of kWCH consecutive valid tokens of one beam; a
-// beam's log-sum-exp is combined from its chunks' (max, sum exp) pairs.
 
 constexpr int kWCH = 64;
 constexpr int kWThreads = 256;
 constexpr int kRBits = 12;
 constexpr int kRBins = 1 << kRBits;
-constexpr int kSurvCap = 8192;
+constexpr int kSurvCap = 8192;   // survivors the sort workgroup holds
+constexpr int kSurvCap1 = 2048;  // stop after the first digit only below this
 constexpr int kSortThreads = 1024;
 
-enum : int32_t { kSelPending = 0, kSelThreshold = 1, kSelUnresolved = 2 };
+enum : int32_t { kSelPending = 0, kSelThreshold = 1, kSelUnresolved = 2, kSelAll = 3 };
 
+// Per query, written by the scoring kernel (n_cand, state) and by the collect
+// kernel (the resolved selection) for the sort kernel.
 struct WideSel {
     uint64_t prefix;  // decided high bits of the query's K-th largest key
-    uint64_t thr;     // state kSelThreshold: the survivors are the keys >= thr
     int32_t need;     // keys still to take among those sharing `prefix`
-    int32_t state;
+    int32_t state;    // kSelAll: no more candidates than K, all survive
     int32_t n_cand;   // candidates of the query
-    uint32_t done;    // workgroups of the query finished with the current pass
+    int32_t pad;
 };
 
 // j-th valid token (ascending) of row r.
@@ -60,7 +75,7 @@ __device__ int nth_token(const StepDev& st, int32_t r, uint32_t e0, int j) {
     return lo * 32 + __ffs(x) - 1;
 }
 
-// Slot of the query whose chunks contain chunk c (offs[0] <= c < offs[K]).
+// Slot whose chunks contain chunk c (offs[0] <= c < offs[K]).
 __device__ __forceinline__ int slot_of_chunk(const int32_t* offs, int K, int c) {
     int lo = 0, hi = K;
     while (hi - lo > 1) {
@@ -70,25 +85,65 @@ __device__ __forceinline__ int slot_of_chunk(const int32_t* offs, int K, int c) 
     return lo;
 }
 
-__device__ __forceinline__ uint32_t load_count(const uint32_t* p, bool coherent) {
-    return coherent ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *p;
+// Candidate and chunk offsets of the query's K slots into co_s / ho_s [K+1]
+// (exclusive prefix sums of the slots' valid-token counts and chunk counts).
+// All threads call.
+template <int NT>
+__device__ void slot_offsets(const StepDev& st, int q, int K, const int32_t* __restrict__ beam_rows,
+                             const float* __restrict__ acc, int32_t* co_s, int32_t* ho_s, int* red_i) {
+    constexpr int PER = (kMaxKRadix + NT - 1) / NT;
+    const int k0 = threadIdx.x * PER;
+    int n[PER];
+    int sc = 0, sh = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int k = k0 + u;
+        int x = 0;
+        if (k < K) {
+            const int64_t b = (int64_t)q * K + k;
+            const int32_t r = beam_rows[b];
+            if (beam_live(st, r, acc[b])) x = (int)(st.row_ptr[r + 1] - st.row_ptr[r]);
+        }
+        n[u] = x;
+        sc += x;
+        sh += (x + kWCH - 1) / kWCH;
+    }
+    int tc, th;
+    int oc = block_exclusive_scan<NT>(sc, red_i, &tc);
+    int oh = block_exclusive_scan<NT>(sh, red_i, &th);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int k = k0 + u;
+        if (k < K) {
+            co_s[k] = oc;
+            ho_s[k] = oh;
+        }
+        oc += n[u];
+        oh += (n[u] + kWCH - 1) / kWCH;
+    }
+    if (threadIdx.x == 0) {
+        co_s[K] = tc;
+        ho_s[K] = th;
+    }
+    __syncthreads();
 }
 
-// Digit (bin) holding the need-th largest key, from the counts of nbins
-// digits (bin index = digit value).  pick[0] = digit, pick[1] = keys in
+
+// Digit (bin) holding the need-th largest key, from the LDS counts h of
+// nbins digits (bin index = digit value).  pick[0] = digit, pick[1] = keys in
 // higher bins, pick[2] = keys in the bin.  All threads call.
 template <int NT>
-__device__ void block_pick(const uint32_t* h, int nbins, bool coherent, int need, int* red_i, int* pick) {
+__device__ void block_pick(const uint32_t* h, int nbins, int need, int* red_i, int* pick) {
     const int per = (nbins + NT - 1) / NT;
     const int top = nbins - 1 - (int)threadIdx.x * per;  // this thread's bins: top, top-1, ... (highest first)
     int s = 0;
     for (int i = 0; i < per; ++i)
-        if (top - i >= 0) s += (int)load_count(h + top - i, coherent);
+        if (top - i >= 0) s += (int)h[top - i];
     int tot;
     int above = block_exclusive_scan<NT>(s, red_i, &tot);
     if (above < need && above + s >= need) {
         for (int i = 0; i < per; ++i) {
-            const int c = (int)load_count(h + top - i, coherent);
+            const int c = (int)h[top - i];
             if (above + c >= need) {
                 pick[0] = top - i;
                 pick[1] = above;
@@ -101,102 +156,97 @@ __device__ void block_pick(const uint32_t* h, int nbins, bool coherent, int need
     __syncthreads();
 }
 
-// After a digit at bit `shift` is picked: survivors if we stopped here are the
-// keys above the boundary bin plus the whole bin.
-__device__ void sel_advance(WideSel* sel, int K, const int* pick, int shift, bool last_pass) {
-    const int kt = min(K, sel->n_cand);
-    const int need = sel->need - pick[1];
-    const uint64_t prefix = sel->prefix | ((uint64_t)pick[0] << shift);
-    sel->prefix = prefix;
-    sel->need = need;
-    if (kt - need + pick[2] <= kSurvCap) {
-        sel->thr = prefix;
-        sel->state = kSelThreshold;
-    } else if (last_pass) {
-        sel->state = kSelUnresolved;
-    }
-}
+// Selection of a query as far as its digit histograms decide it, recomputed
+// by every workgroup that needs it (the histograms are complete when the
+// kernel that reads them starts, so no workgroup waits for another).  Digits
+// are resolved one after the other; after each, the survivors if we stopped
+// there are the keys above the boundary bin plus the whole bin.
+struct SelView {
+    uint64_t prefix;  // decided high bits of the K-th largest key
+    int need;         // keys still to take among those sharing `prefix`
+    int state;
+};
 
-// True in the last workgroup of the query to reach this point (its earlier
-// global atomics are then visible to it).
-__device__ bool last_of_query(WideSel* sel, int G, int* flag) {
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev = atomicAdd(&sel->done, 1u);
-        *flag = prev == (uint32_t)(G - 1);
-        if (*flag) sel->done = 0;  // ready for the next pass
+template <int NT>
+__device__ SelView resolve_digits(const WideDev& w, int q, int K, int n_cand, int passes, uint32_t* hs, int* red_i,
+                                  int* pick) {
+    SelView v;
+    v.prefix = 0;
+    v.need = min(K, n_cand);
+    v.state = n_cand <= K ? kSelAll : kSelPending;
+    if (v.state == kSelAll) return v;
+    const int kt = v.need;
+    for (int p = 0; p < passes; ++p) {
+        const uint4* src = reinterpret_cast<const uint4*>(w.hist + ((int64_t)q * 2 + p) * kRBins);
+        uint4* dst = reinterpret_cast<uint4*>(hs);
+        for (int i = threadIdx.x; i < kRBins / 4; i += NT) dst[i] = src[i];
+        __syncthreads();
+        block_pick<NT>(hs, kRBins, v.need, red_i, pick);
+        v.need -= pick[1];
+        v.prefix |= (uint64_t)pick[0] << (64 - (p + 1) * kRBits);
+        const int surv = kt - v.need + pick[2];
+        __syncthreads();  // pick and hs are reused
+        if (surv <= (p == 0 ? kSurvCap1 : kSurvCap)) {
+            v.state = kSelThreshold;
+            return v;
+        }
     }
-    __syncthreads();
-    if (*flag) __threadfence();
-    return *flag != 0;
-}
-
-// Per query: candidate and chunk offsets of every slot, selection state, and
-// cleared histograms.  One workgroup per query, one thread per slot.
-__global__ __launch_bounds__(1024) void k_wide_plan(StepDev st, int K, const int32_t* __restrict__ beam_rows,
-                                                    const float* __restrict__ acc, WideDev w) {
-    __shared__ int red_i[1024 / kWave];
-    const int q = blockIdx.x, k = threadIdx.x;
-    int n = 0;
-    if (k < K) {
-        const int64_t b = (int64_t)q * K + k;
-        const int32_t r = beam_rows[b];
-        if (beam_live(st, r, acc[b])) n = (int)(st.row_ptr[r + 1] - st.row_ptr[r]);
-    }
-    int tc, th;
-    const int oc = block_exclusive_scan<1024>(n, red_i, &tc);
-    const int oh = block_exclusive_scan<1024>((n + kWCH - 1) / kWCH, red_i, &th);
-    int32_t* co = w.cand_off + (int64_t)q * (K + 1);
-    int32_t* ho = w.chunk_off + (int64_t)q * (K + 1);
-    if (k < K) {
-        co[k] = oc;
-        ho[k] = oh;
-    }
-    if (k == 0) {
-        co[K] = tc;
-        ho[K] = th;
-        WideSel* sel = reinterpret_cast<WideSel*>(w.sel) + q;
-        sel->prefix = 0;
-        sel->need = min(K, tc);
-        sel->n_cand = tc;
-        sel->done = 0;
-        sel->state = tc <= K ? kSelThreshold : kSelPending;
-        sel->thr = 1;  // every candidate key is nonzero
-        w.surv_n[q] = 0;
-    }
-    uint32_t* hq = w.hist + (int64_t)q * 2 * kRBins;
-    for (int i = k; i < 2 * kRBins; i += 1024) hq[i] = 0;
+    v.state = passes == 2 ? kSelUnresolved : kSelPending;
+    return v;
 }
 
 // Scores of every candidate, one chunk per workgroup iteration: z (sparse
 // gather-dot against the beam's hidden vector staged in LDS, or the
 // full-codebook score of the column), stored as z's bits over the key's low
-// half (parent, token), and the chunk's (max, sum exp).
+// half (parent, token), and the chunk's (max, sum exp).  Every workgroup
+// derives the slot offsets itself; the query's first one also publishes them
+// and resets the query's selection state for the kernels that follow.
 template <typename DT, bool DENSE>
 __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int d, const DT* __restrict__ hidden,
                                                           const DT* __restrict__ W, const float* __restrict__ Z,
                                                           const float* __restrict__ Zp, int64_t ldz,
                                                           const int32_t* __restrict__ n_live,
                                                           const int32_t* __restrict__ ci_of, int split_ok,
-                                                          const int32_t* __restrict__ beam_rows, WideDev w) {
+                                                          const int32_t* __restrict__ beam_rows,
+                                                          const float* __restrict__ acc, WideDev w, int G) {
     extern __shared__ __align__(16) float h_s[];  // [d], sparse scoring only
     __shared__ float z_s[kWCH];
     __shared__ uint16_t tok_s[kWCH];
-    const int q = blockIdx.x / w.G, g = blockIdx.x % w.G, tid = threadIdx.x;
-    const int32_t* co = w.cand_off + (int64_t)q * (K + 1);
-    const int32_t* ho = w.chunk_off + (int64_t)q * (K + 1);
-    const int nch = ho[K];
+    __shared__ int32_t co_s[kMaxKRadix + 1], ho_s[kMaxKRadix + 1];
+    __shared__ int red_i[kWThreads / kWave];
+    const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
+    slot_offsets<kWThreads>(st, q, K, beam_rows, acc, co_s, ho_s, red_i);
+    if (g == 0) {
+        int32_t* co = w.cand_off + (int64_t)q * (K + 1);
+        int32_t* ho = w.chunk_off + (int64_t)q * (K + 1);
+        for (int k = tid; k <= K; k += kWThreads) {
+            co[k] = co_s[k];
+            ho[k] = ho_s[k];
+        }
+        uint32_t* hq = w.hist + (int64_t)q * 2 * kRBins;
+        for (int i = tid; i < 2 * kRBins; i += kWThreads) hq[i] = 0;
+        if (tid == 0) {
+            const int tc = co_s[K];
+            WideSel* sel = reinterpret_cast<WideSel*>(w.sel) + q;
+            sel->prefix = 0;
+            sel->need = min(K, tc);
+            sel->n_cand = tc;
+            sel->pad = 0;
+            sel->state = tc <= K ? kSelAll : kSelPending;
+            w.surv_n[q] = 0;
+        }
+    }
+    const int nch = ho_s[K];
     int split = 1;
     if (DENSE && split_ok) split = gemm_split(*n_live, (int)ldz, d);
     int staged = -1;
-    for (int c = g; c < nch; c += w.G) {
-        const int k = slot_of_chunk(ho, K, c);
+    for (int c = g; c < nch; c += G) {
+        const int k = slot_of_chunk(ho_s, K, c);
         const int64_t b = (int64_t)q * K + k;
         const int32_t r = beam_rows[b];
         const uint32_t e0 = st.row_ptr[r];
-        const int n = co[k + 1] - co[k];
-        const int j0 = (c - ho[k]) * kWCH;
+        const int n = co_s[k + 1] - co_s[k];
+        const int j0 = (c - ho_s[k]) * kWCH;
         const int cnt = min(kWCH, n - j0);
         if (tid < cnt) tok_s[tid] = (uint16_t)nth_token(st, r, e0, j0 + tid);
         if (!DENSE && staged != k) {
@@ -229,10 +279,13 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
                 p[0] = m;
                 p[1] = s;
             }
-            if (tid < cnt)
-                w.cand[(int64_t)q * w.cap + co[k] + j0 + tid] = ((uint64_t)__float_as_uint(z) << 32) |
-                                                                 ((uint64_t)(1023 - k) << 16) |
-                                                                 (uint64_t)(65535 - tok_s[tid]);
+            if (tid < cnt) {
+                const uint32_t c_ix = (uint32_t)(co_s[k] + j0 + tid);
+                const int64_t o = (int64_t)q * w.cap + c_ix;
+                w.cand[o] = ((uint64_t)__float_as_uint(z) << 32) | (uint64_t)(0xFFFFFFFFu - c_ix);
+                w.info[o] = ((uint64_t)(e0 + (uint32_t)(j0 + tid)) << 32) | ((uint64_t)tok_s[tid] << 16) |
+                            (uint64_t)k;
+            }
         }
         __syncthreads();
     }
@@ -240,26 +293,30 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
 
 // Keys of every candidate (one chunk per wavefront): the beam's log-sum-exp
 // from its chunks, score = acc + (z - lse) in float32, and the histogram of
-// the keys' top digit; the query's last workgroup picks that digit.
-__global__ __launch_bounds__(kWThreads) void k_wide_keys(int K, const float* __restrict__ acc, WideDev w) {
-    __shared__ uint32_t hs[kRBins];
-    __shared__ int red_i[kWThreads / kWave];
-    __shared__ int pick[3];
-    __shared__ int flag;
-    const int q = blockIdx.x / w.G, g = blockIdx.x % w.G, tid = threadIdx.x;
+// the keys' top digit.
+__global__ __launch_bounds__(kWThreads) void k_wide_keys(int K, const float* __restrict__ acc, WideDev w, int G) {
+    __shared__ __align__(16) uint32_t hs[kRBins];
+    __shared__ int32_t co_s[kMaxKRadix + 1], ho_s[kMaxKRadix + 1];
+    const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wv = tid / kWave;
     constexpr int NWV = kWThreads / kWave;
+    const WideSel* sel = reinterpret_cast<const WideSel*>(w.sel) + q;
+    const bool pending = sel->state == kSelPending;  // uniform over the query's workgroups
     for (int i = tid; i < kRBins; i += kWThreads) hs[i] = 0;
-    __syncthreads();
     const int32_t* co = w.cand_off + (int64_t)q * (K + 1);
     const int32_t* ho = w.chunk_off + (int64_t)q * (K + 1);
-    const int nch = ho[K];
+    for (int k = tid; k <= K; k += kWThreads) {
+        co_s[k] = co[k];
+        ho_s[k] = ho[k];
+    }
+    __syncthreads();
+    const int nch = ho_s[K];
     const float* cms = w.cms + (int64_t)q * w.chunk_cap * 2;
     uint64_t* cq = w.cand + (int64_t)q * w.cap;
-    for (int c = g * NWV + wv; c < nch; c += w.G * NWV) {
-        const int k = slot_of_chunk(ho, K, c);
+    for (int c = g * NWV + wv; c < nch; c += G * NWV) {
+        const int k = slot_of_chunk(ho_s, K, c);
         float m = -INFINITY, s = 0.f;
-        for (int x = ho[k] + lane; x < ho[k + 1]; x += kWave) {
+        for (int x = ho_s[k] + lane; x < ho_s[k + 1]; x += kWave) {
             const float cm = cms[2 * x], cs = cms[2 * x + 1];
             if (cm > m) {
                 s = s * expf(m - cm) + cs;
@@ -272,43 +329,41 @@ __global__ __launch_bounds__(kWThreads) void k_wide_keys(int K, const float* __r
         const float S = wave_sum(m == -INFINITY ? 0.f : s * expf(m - M));
         const float lse = M + logf(S);
         const float a = acc[(int64_t)q * K + k];
-        const int j0 = (c - ho[k]) * kWCH;
-        const int cnt = min(kWCH, co[k + 1] - co[k] - j0);
+        const int j0 = (c - ho_s[k]) * kWCH;
+        const int cnt = min(kWCH, co_s[k + 1] - co_s[k] - j0);
         if (lane < cnt) {
-            uint64_t* p = cq + co[k] + j0 + lane;
+            uint64_t* p = cq + co_s[k] + j0 + lane;
             const uint64_t v = *p;
             const float z = __uint_as_float((uint32_t)(v >> 32));
             const uint64_t key = ((uint64_t)score_order_bits(a + (z - lse)) << 32) | (v & 0xFFFFFFFFull);
             *p = key;
-            atomicAdd(&hs[key >> (64 - kRBits)], 1u);
+            if (pending) atomicAdd(&hs[key >> (64 - kRBits)], 1u);
         }
     }
+    if (!pending) return;
     __syncthreads();
-    WideSel* sel = reinterpret_cast<WideSel*>(w.sel) + q;
-    if (sel->state != kSelPending) return;  // uniform over the query's workgroups
     uint32_t* h1 = w.hist + (int64_t)q * 2 * kRBins;
     for (int i = tid; i < kRBins; i += kWThreads)
         if (hs[i]) atomicAdd(&h1[i], hs[i]);
-    if (!last_of_query(sel, w.G, &flag)) return;
-    block_pick<kWThreads>(h1, kRBins, true, sel->need, red_i, pick);
-    if (tid == 0) sel_advance(sel, K, pick, 64 - kRBits, false);
 }
 
-// Second digit, over the keys that share the first.
-__global__ __launch_bounds__(kWThreads) void k_wide_refine(int K, WideDev w) {
-    __shared__ uint32_t hs[kRBins];
+// Second digit, over the keys that share the first (queries the first digit
+// left open).
+__global__ __launch_bounds__(kWThreads) void k_wide_refine(int K, WideDev w, int G) {
+    __shared__ __align__(16) uint32_t hs[kRBins];
     __shared__ int red_i[kWThreads / kWave];
     __shared__ int pick[3];
-    __shared__ int flag;
-    const int q = blockIdx.x / w.G, g = blockIdx.x % w.G, tid = threadIdx.x;
-    WideSel* sel = reinterpret_cast<WideSel*>(w.sel) + q;
+    const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
+    const WideSel* sel = reinterpret_cast<const WideSel*>(w.sel) + q;
     if (sel->state != kSelPending) return;  // uniform over the query's workgroups
+    const int n = sel->n_cand;
+    const SelView v = resolve_digits<kWThreads>(w, q, K, n, 1, hs, red_i, pick);
+    if (v.state != kSelPending) return;
     for (int i = tid; i < kRBins; i += kWThreads) hs[i] = 0;
     __syncthreads();
-    const uint64_t pre = sel->prefix >> (64 - kRBits);
-    const int n = sel->n_cand;
+    const uint64_t pre = v.prefix >> (64 - kRBits);
     const uint64_t* cq = w.cand + (int64_t)q * w.cap;
-    for (int i = g * kWThreads + tid; i < n; i += w.G * kWThreads) {
+    for (int i = g * kWThreads + tid; i < n; i += G * kWThreads) {
         const uint64_t key = cq[i];
         if ((key >> (64 - kRBits)) == pre) atomicAdd(&hs[(key >> (64 - 2 * kRBits)) & (kRBins - 1)], 1u);
     }
@@ -316,22 +371,30 @@ __global__ __launch_bounds__(kWThreads) void k_wide_refine(int K, WideDev w) {
     uint32_t* h2 = w.hist + (int64_t)q * 2 * kRBins + kRBins;
     for (int i = tid; i < kRBins; i += kWThreads)
         if (hs[i]) atomicAdd(&h2[i], hs[i]);
-    if (!last_of_query(sel, w.G, &flag)) return;
-    block_pick<kWThreads>(h2, kRBins, true, sel->need, red_i, pick);
-    if (tid == 0) sel_advance(sel, K, pick, 64 - 2 * kRBits, true);
 }
 
-// Survivors (keys >= the query's threshold) appended to the query's list.
-__global__ __launch_bounds__(kWThreads) void k_wide_collect(WideDev w) {
-    const int q = blockIdx.x / w.G, g = blockIdx.x % w.G, tid = threadIdx.x;
+// Survivors (keys >= the query's threshold) appended to the query's list;
+// the query's first workgroup records the resolved selection for the sort.
+__global__ __launch_bounds__(kWThreads) void k_wide_collect(int K, WideDev w, int G) {
+    __shared__ __align__(16) uint32_t hs[kRBins];
+    __shared__ int red_i[kWThreads / kWave];
+    __shared__ int pick[3];
+    const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const WideSel* sel = reinterpret_cast<const WideSel*>(w.sel) + q;
-    if (sel->state != kSelThreshold) return;
-    const uint64_t thr = sel->thr;
+    WideSel* sel = reinterpret_cast<WideSel*>(w.sel) + q;
     const int n = sel->n_cand;
+    if (n <= K) return;  // every candidate survives (sel->state is rewritten below, so not read here)
+    const SelView v = resolve_digits<kWThreads>(w, q, K, n, 2, hs, red_i, pick);
+    if (g == 0 && tid == 0) {
+        sel->prefix = v.prefix;
+        sel->need = v.need;
+        sel->state = v.state;
+    }
+    if (v.state != kSelThreshold) return;
+    const uint64_t thr = v.prefix;  // every key >= the prefix with zero low bits survives
     const uint64_t* cq = w.cand + (int64_t)q * w.cap;
     uint64_t* out = w.surv + (int64_t)q * kSurvCap;
-    for (int i0 = g * kWThreads; i0 < n; i0 += w.G * kWThreads) {
+    for (int i0 = g * kWThreads; i0 < n; i0 += G * kWThreads) {
         const int i = i0 + tid;
         const uint64_t key = i < n ? cq[i] : 0ull;
         const bool take = i < n && key >= thr;
@@ -346,11 +409,108 @@ __global__ __launch_bounds__(kWThreads) void k_wide_collect(WideDev w) {
     }
 }
 
-// Per query: the survivors sorted descending in LDS (bitonic), the best K
-// emitted.  A query whose threshold is still open after the two GPU-wide
-// digits finishes the radix select here, 8 bits a pass.
-__global__ __launch_bounds__(kSortThreads) void k_wide_sort(StepDev st, int K, const int32_t* __restrict__ beam_rows,
-                                                            WideDev w, int32_t* __restrict__ out_tok,
+// In-register stage of the block bitonic sort: registers r and r ^ RJ hold
+// the partners (element i = r * kSortThreads + thread).
+template <int E, int RJ>
+__device__ __forceinline__ void sort_reg_stage(uint64_t (&v)[E], int k) {
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const int r2 = r ^ RJ;
+        if (r2 > r && r2 < E) {
+            const bool desc = ((r * kSortThreads) & k) == 0;
+            const uint64_t a = v[r], b = v[r2];
+            const bool sw = desc ? a < b : a > b;
+            v[r] = sw ? b : a;
+            v[r2] = sw ? a : b;
+        }
+    }
+}
+
+// Bitonic sort, descending, of the E * kSortThreads keys held as v[r] =
+// element r * kSortThreads + thread.  Partners closer than a wavefront are
+// exchanged by lane shuffles, partners in other wavefronts through LDS (xch:
+// E * kSortThreads keys), partners in other registers of the same thread in
+// place.  All threads call.
+template <int E>
+__device__ void block_sort_desc(uint64_t (&v)[E], uint64_t* xch) {
+    constexpr int NT = kSortThreads;
+    constexpr int P = NT * E;
+    const int tid = threadIdx.x;
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            if (j >= NT) {
+                const int rj = j / NT;
+                if (rj == 1) sort_reg_stage<E, 1>(v, k);
+                else if (rj == 2) sort_reg_stage<E, 2>(v, k);
+                else sort_reg_stage<E, 4>(v, k);
+            } else if (j >= kWave) {
+#pragma unroll
+                for (int r = 0; r < E; ++r) xch[r * NT + tid] = v[r];
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    const uint64_t o = xch[r * NT + (tid ^ j)];
+                    const int i = r * NT + tid;
+                    const bool take_max = ((i & j) == 0) == ((i & k) == 0);
+                    v[r] = take_max ? umax64(v[r], o) : umin64(v[r], o);
+                }
+                __syncthreads();
+            } else {
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    const uint64_t o = shfl_xor64(v[r], j);
+                    const int i = r * NT + tid;
+                    const bool take_max = ((i & j) == 0) == ((i & k) == 0);
+                    v[r] = take_max ? umax64(v[r], o) : umin64(v[r], o);
+                }
+            }
+        }
+    }
+}
+
+// Output slot i of query q from a radix key (0 = sentinel).
+__device__ void emit_radix(const WideDev& w, int q, int K, int i, uint64_t key, int32_t* out_tok, int32_t* out_par,
+                           int32_t* out_rows, float* out_logp) {
+    const int64_t o = (int64_t)q * K + i;
+    if (key == 0ull) {
+        out_tok[o] = -1;
+        out_par[o] = -1;
+        out_rows[o] = -1;
+        out_logp[o] = -INFINITY;
+        return;
+    }
+    const uint32_t c_ix = 0xFFFFFFFFu - (uint32_t)key;
+    const uint64_t inf = w.info[(int64_t)q * w.cap + c_ix];
+    out_tok[o] = (int32_t)((inf >> 16) & 0xFFFFu);
+    out_par[o] = (int32_t)(inf & 0xFFFFu);
+    out_rows[o] = (int32_t)(uint32_t)(inf >> 32);
+    out_logp[o] = score_from_order_bits((uint32_t)(key >> 32));
+}
+
+// Survivors src[0..n) (n <= E * kSortThreads) sorted; the best K emitted.
+template <int E>
+__device__ void sort_and_emit(const WideDev& w, int q, int K, const uint64_t* src, int n, uint64_t* xch,
+                              int32_t* out_tok, int32_t* out_par, int32_t* out_rows, float* out_logp) {
+    const int tid = threadIdx.x;
+    uint64_t v[E];
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const int i = r * kSortThreads + tid;
+        v[r] = i < n ? src[i] : 0ull;
+    }
+    __syncthreads();  // src may alias xch
+    block_sort_desc<E>(v, xch);
+#pragma unroll
+    for (int r = 0; r < E; ++r) {
+        const int i = r * kSortThreads + tid;
+        if (i < K) emit_radix(w, q, K, i, v[r], out_tok, out_par, out_rows, out_logp);
+    }
+}
+
+// Per query: the survivors sorted descending, the best K emitted.  A query
+// whose threshold is still open after the two GPU-wide digits finishes the
+// radix select here, 8 bits a pass.
+__global__ __launch_bounds__(kSortThreads) void k_wide_sort(int K, WideDev w, int32_t* __restrict__ out_tok,
                                                             int32_t* __restrict__ out_par,
                                                             int32_t* __restrict__ out_rows,
                                                             float* __restrict__ out_logp) {
@@ -359,13 +519,14 @@ __global__ __launch_bounds__(kSortThreads) void k_wide_sort(StepDev st, int K, c
     __shared__ int red_i[kSortThreads / kWave];
     __shared__ int pick[3];
     __shared__ int cnt_s;
-    __shared__ uint64_t thr_s;
     const int q = blockIdx.x, tid = threadIdx.x;
     const WideSel* sel = reinterpret_cast<const WideSel*>(w.sel) + q;
     const int n_cand = sel->n_cand;
+    const int state = sel->state;
     const uint64_t* cq = w.cand + (int64_t)q * w.cap;
+    const uint64_t* src;
     int n;
-    if (sel->state == kSelUnresolved) {
+    if (state == kSelUnresolved) {
         uint64_t prefix = sel->prefix;
         int need = sel->need;
         const int kt = min(K, n_cand);
@@ -377,55 +538,40 @@ __global__ __launch_bounds__(kSortThreads) void k_wide_sort(StepDev st, int K, c
                 if ((key >> (shift + 8)) == (prefix >> (shift + 8))) atomicAdd(&h8[(key >> shift) & 255u], 1u);
             }
             __syncthreads();
-            block_pick<kSortThreads>(h8, 256, false, need, red_i, pick);
+            block_pick<kSortThreads>(h8, 256, need, red_i, pick);
             need -= pick[1];
             prefix |= (uint64_t)pick[0] << shift;
             const bool done = kt - need + pick[2] <= kSurvCap || shift == 0;
             __syncthreads();
             if (done) break;
         }
-        if (tid == 0) {
-            thr_s = prefix;
-            cnt_s = 0;
-        }
+        if (tid == 0) cnt_s = 0;
         __syncthreads();
-        const uint64_t thr = thr_s;
         for (int i = tid; i < n_cand; i += kSortThreads) {
             const uint64_t key = cq[i];
-            if (key >= thr) {
+            if (key >= prefix) {
                 const int pos = atomicAdd(&cnt_s, 1);
                 if (pos < kSurvCap) ks[pos] = key;
             }
         }
         __syncthreads();
         n = min(cnt_s, kSurvCap);
+        src = ks;
+    } else if (state == kSelAll) {
+        n = n_cand;  // <= K <= kSortThreads
+        src = cq;
     } else {
         n = min(w.surv_n[q], kSurvCap);
-        const uint64_t* src = w.surv + (int64_t)q * kSurvCap;
-        for (int i = tid; i < n; i += kSortThreads) ks[i] = src[i];
+        src = w.surv + (int64_t)q * kSurvCap;
     }
-    int P = kWave;
-    while (P < n) P <<= 1;
-    for (int i = n + tid; i < P; i += kSortThreads) ks[i] = 0ull;
-    __syncthreads();
-    for (int k = 2; k <= P; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < P; i += kSortThreads) {
-                const int o = i ^ j;
-                if (o > i) {
-                    const uint64_t a = ks[i], b = ks[o];
-                    const bool desc = (i & k) == 0;
-                    if (desc ? a < b : a > b) {
-                        ks[i] = b;
-                        ks[o] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-    for (int i = tid; i < K; i += kSortThreads)
-        emit(st, q, K, i, i < n ? ks[i] : 0ull, beam_rows, out_tok, out_par, out_rows, out_logp);
+    if (n <= kSortThreads)
+        sort_and_emit<1>(w, q, K, src, n, ks, out_tok, out_par, out_rows, out_logp);
+    else if (n <= 2 * kSortThreads)
+        sort_and_emit<2>(w, q, K, src, n, ks, out_tok, out_par, out_rows, out_logp);
+    else if (n <= 4 * kSortThreads)
+        sort_and_emit<4>(w, q, K, src, n, ks, out_tok, out_par, out_rows, out_logp);
+    else
+        sort_and_emit<8>(w, q, K, src, n, ks, out_tok, out_par, out_rows, out_logp);
 }
 
 }  // namespace
@@ -436,26 +582,24 @@ int wide_chunk() { return kWCH; }
 int wide_bins() { return kRBins; }
 int wide_surv_cap() { return kSurvCap; }
 size_t wide_sel_bytes() { return sizeof(WideSel); }
+// Workgroups per query: the scoring kernel spreads a query's chunks over up
+// to 1024 workgroups; the histogram kernels use up to 256 (one per CU).
 int wide_blocks_per_query(int Q) { return Q >= 2048 ? 1 : (2048 / (Q > 0 ? Q : 1) > 1024 ? 1024 : 2048 / Q); }
+int wide_hist_blocks_per_query(int Q) { return Q >= 256 ? 1 : 256 / (Q > 0 ? Q : 1); }
 size_t wide_score_lds_bytes(int d, bool dense) { return dense ? 0 : (size_t)d * 4; }
-
-hipError_t launch_wide_plan(const StepDev& st, int Q, int K, const int32_t* beam_rows, const float* acc,
-                            const WideDev& w, hipStream_t s) {
-    if (Q <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_wide_plan, dim3(Q), dim3(1024), 0, s, st, K, beam_rows, acc, w);
-    return hipGetLastError();
-}
 
 hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, int K, int d, const void* hidden,
                              const void* W, const float* Z, const float* Zp, int64_t ldz, const int32_t* n_live,
-                             const int32_t* ci_of, const int32_t* beam_rows, const WideDev& w, hipStream_t s) {
+                             const int32_t* ci_of, const int32_t* beam_rows, const float* acc, const WideDev& w,
+                             hipStream_t s) {
     if (Q <= 0) return hipSuccess;
-    const dim3 grid(Q * w.G);
+    const int G = wide_blocks_per_query(Q);
+    const dim3 grid(Q * G);
     const size_t lds = wide_score_lds_bytes(d, dense);
     const int split_ok = dt == CB_BF16 ? 1 : 0;
 #define CB_WSCORE(DT, DENSE)                                                                                  \
     hipLaunchKernelGGL((k_wide_score<DT, DENSE>), grid, dim3(kWThreads), lds, s, st, K, d, (const DT*)hidden, \
-                       (const DT*)W, Z, Zp, ldz, n_live, ci_of, split_ok, beam_rows, w)
+                       (const DT*)W, Z, Zp, ldz, n_live, ci_of, split_ok, beam_rows, acc, w, G)
     if (dt == CB_BF16) {
         if (dense) CB_WSCORE(uint16_t, true); else CB_WSCORE(uint16_t, false);
     } else {
@@ -467,19 +611,22 @@ hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, 
 
 hipError_t launch_wide_keys(int Q, int K, const float* acc, const WideDev& w, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_wide_keys, dim3(Q * w.G), dim3(kWThreads), 0, s, K, acc, w);
+    const int G = wide_hist_blocks_per_query(Q);
+    hipLaunchKernelGGL(k_wide_keys, dim3(Q * G), dim3(kWThreads), 0, s, K, acc, w, G);
     return hipGetLastError();
 }
 
 hipError_t launch_wide_refine(int Q, int K, const WideDev& w, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_wide_refine, dim3(Q * w.G), dim3(kWThreads), 0, s, K, w);
+    const int G = wide_hist_blocks_per_query(Q);
+    hipLaunchKernelGGL(k_wide_refine, dim3(Q * G), dim3(kWThreads), 0, s, K, w, G);
     return hipGetLastError();
 }
 
-hipError_t launch_wide_collect(int Q, const WideDev& w, hipStream_t s) {
+hipError_t launch_wide_collect(int Q, int K, const WideDev& w, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_wide_collect, dim3(Q * w.G), dim3(kWThreads), 0, s, w);
+    const int G = wide_hist_blocks_per_query(Q);
+    hipLaunchKernelGGL(k_wide_collect, dim3(Q * G), dim3(kWThreads), 0, s, K, w, G);
     return hipGetLastError();
 }
 
@@ -490,7 +637,7 @@ hipError_t launch_wide_sort(const StepDev& st, int Q, int K, const int32_t* beam
     static const hipError_t lds_ok =
         hipFuncSetAttribute((const void*)k_wide_sort, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (lds_ok != hipSuccess) return lds_ok;
-    hipLaunchKernelGGL(k_wide_sort, dim3(Q), dim3(kSortThreads), lds, s, st, K, beam_rows, w, tok, par, rows, logp);
+    hipLaunchKernelGGL(k_wide_sort, dim3(Q), dim3(kSortThreads), lds, s, K, w, tok, par, rows, logp);
     return hipGetLastError();
 }
 

@@ -167,7 +167,8 @@ cb_status cb_get_path(const cb_plan* plan, int32_t t, cb_path* path);
  *   out_*      device [Q*K]: tokens, parent slots, next rows, new accumulated
  *              log-probs, best first per query, sentinel padded.  Must not
  *              alias the inputs.
- * All device pointers 16-byte aligned.  Enqueued on `stream`; returns after
+ * hidden and W_t 16-byte aligned (d is a multiple of 8, so every row is);
+ * the per-slot arrays 4-byte aligned.  Enqueued on `stream`; returns after
  * the launches.  Concurrent calls on one plan from different streams race.
  * Errors: CB_EINVAL (t, Q, pointers, host-only index), CB_EHIP. */
 cb_status cb_step(cb_plan* plan, int32_t t, int32_t Q, const void* hidden, const void* W_t,
@@ -186,6 +187,7 @@ cb_status cb_step(cb_plan* plan, int32_t t, int32_t Q, const void* hidden, const
  *   trace_hidden / trace_rows / trace_acc: optional (NULL) device buffers
  *   [L][Q*K][d] dtype, [L][Q*K] int32, [L][Q*K] float receiving the inputs
  *   of every step.
+ * W 16-byte aligned, the other arrays 4-byte aligned.
  * Enqueued on `stream`; nothing is allocated.  Errors as cb_step. */
 cb_status cb_decode(cb_plan* plan, int32_t Q, const float* q, const float* P, const void* W,
                     int32_t* out_seqs, float* out_logp, int32_t* out_rows,
@@ -216,13 +218,12 @@ typedef enum {
     CB_KERNEL_MERGE = 4,          /* per-query top-K and next rows (after the dense expansion) */
     CB_KERNEL_STEP_QUERY = 5,     /* the whole sparse step, one workgroup per query */
     CB_KERNEL_LIVE_ROWS = 6,      /* list of live beams for the full-codebook scores */
-    CB_KERNEL_RADIX_PLAN = 7,     /* radix selection: per-slot candidate offsets, state reset */
-    CB_KERNEL_RADIX_SCORE_SPARSE = 8, /* radix selection: slot fill + gather-dot of every candidate */
-    CB_KERNEL_RADIX_SCORE_DENSE = 9,  /* radix selection: slot fill + column gather of every candidate */
-    CB_KERNEL_RADIX_KEYS = 10,    /* radix selection: softmax, keys, first digit */
-    CB_KERNEL_RADIX_REFINE = 11,  /* radix selection: second digit */
-    CB_KERNEL_RADIX_COLLECT = 12, /* radix selection: survivors */
-    CB_KERNEL_RADIX_SORT = 13     /* radix selection: survivors sorted, outputs and next rows */
+    CB_KERNEL_RADIX_SCORE_SPARSE = 7, /* radix selection: offsets, slot fill, gather-dot of every candidate */
+    CB_KERNEL_RADIX_SCORE_DENSE = 8,  /* radix selection: offsets, slot fill, column gather of every candidate */
+    CB_KERNEL_RADIX_KEYS = 9,     /* radix selection: softmax, keys, first digit */
+    CB_KERNEL_RADIX_REFINE = 10,  /* radix selection: second digit */
+    CB_KERNEL_RADIX_COLLECT = 11, /* radix selection: survivors */
+    CB_KERNEL_RADIX_SORT = 12     /* radix selection: survivors sorted, outputs and next rows */
 } cb_kernel;
 
 typedef struct {

@@ -123,9 +123,10 @@ def check_decode(w, out, K, plan):
     cfg, ref, T = w["cfg"], w["ref"], w["T"]
     seqs, logp, rows = (out[k].cpu().numpy() for k in ("seqs", "logp", "rows"))
     tr = out["trace_rows"].cpu().numpy()
-    catalog = {tuple(r) for r in w["items"].tolist()}
-    for s_ in seqs[rows >= 0][:3000].tolist():
-        assert tuple(s_) in catalog
+    if len(w["items"]) <= 10_000_000:  # (larger catalogs: outputs equal to the oracle's are in it)
+        catalog = {tuple(r) for r in w["items"].tolist()}
+        for s_ in seqs[rows >= 0][:3000].tolist():
+            assert tuple(s_) in catalog
     diverged = 0
     for qi in range(cfg.Q):
         sl = slice(qi * K, (qi + 1) * K)

@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_HERE, "libcsrbeam.so")
 
 CB_OK, CB_EINVAL, CB_ENOMEM, CB_EHIP, CB_EUNSUPPORTED, CB_ECAPACITY = 0, -1, -2, -3, -4, -5
 CB_F32, CB_BF16 = 0, 1
-CB_PATH_AUTO, CB_PATH_DENSE, CB_PATH_SPARSE = 0, 1, 2
+CB_PATH_AUTO, CB_PATH_DENSE, CB_PATH_SPARSE, CB_PATH_SPARSE_SPLIT = 0, 1, 2, 3
 CB_STORE_AUTO, CB_STORE_CSR, CB_STORE_BITMAP = 0, 1, 2
 CB_SELECT_AUTO, CB_SELECT_LDS, CB_SELECT_RADIX = 0, 1, 2
 

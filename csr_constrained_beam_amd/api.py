@@ -11,7 +11,8 @@ import numpy as np
 
 from . import _lib as C
 
-_PATHS = {"auto": C.CB_PATH_AUTO, "dense": C.CB_PATH_DENSE, "sparse": C.CB_PATH_SPARSE}
+_PATHS = {"auto": C.CB_PATH_AUTO, "dense": C.CB_PATH_DENSE, "sparse": C.CB_PATH_SPARSE,
+          "sparse_split": C.CB_PATH_SPARSE_SPLIT}
 _PATH_NAMES = {v: k for k, v in _PATHS.items()}
 _SELECTS = {"auto": C.CB_SELECT_AUTO, "lds": C.CB_SELECT_LDS, "radix": C.CB_SELECT_RADIX}
 _SELECT_NAMES = {v: k for k, v in _SELECTS.items()}

@@ -68,9 +68,9 @@ bool dense_available(const cb_plan* p) { return p->dtype == CB_F32 || (p->d % 64
 
 int32_t resolve_path(const cb_plan* p, int t) {
     int32_t f = p->forced[(size_t)t];
-    if (f == CB_PATH_DENSE || f == CB_PATH_SPARSE) return f;
+    if (f == CB_PATH_DENSE || f == CB_PATH_SPARSE || f == CB_PATH_SPARSE_SPLIT) return f;
     int32_t tu = p->tuned[(size_t)t];
-    if (tu == CB_PATH_DENSE || tu == CB_PATH_SPARSE) return tu;
+    if (tu == CB_PATH_DENSE || tu == CB_PATH_SPARSE || tu == CB_PATH_SPARSE_SPLIT) return tu;
     const cb::StepTable& T = p->idx->steps[(size_t)t];
     return (T.store == CB_STORE_BITMAP && dense_available(p)) ? CB_PATH_DENSE : CB_PATH_SPARSE;
 }
@@ -192,7 +192,7 @@ cb_status run_step_radix(cb_plan* p, int t, int Q, int32_t path, const void* hid
     {
         ProfMark m(p, s, t, dense ? CB_KERNEL_RADIX_SCORE_DENSE : CB_KERNEL_RADIX_SCORE_SPARSE, 256, GS);
         e = launch_wide_score(sd, dense, p->dtype, Q, p->K, p->d, hidden, Wt, p->Z, p->Zp, idx->V, p->n_live,
-                              p->ci_of, rows, acc, w, s);
+                              p->ci_of, rows, acc, 0, w, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: radix scores", e);
     }
@@ -234,9 +234,19 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const vo
     const int Kc = std::min(p->K, std::max(T.S, 1));
     hipError_t e;
     if (sel == CB_SELECT_RADIX) return run_step_radix(p, t, Q, path, hidden, Wt, rows, acc, ot, op, orow, ol, s);
-    if (path == CB_PATH_SPARSE) {
+    if (path == CB_PATH_SPARSE || path == CB_PATH_SPARSE_SPLIT) {
+        const WideDev& w = p->wide;
+        const bool split = path == CB_PATH_SPARSE_SPLIT && w.cand;
+        if (split) {  // rows too wide for one wavefront: scored across many workgroups first
+            ProfMark m(p, s, t, CB_KERNEL_RADIX_SCORE_SPARSE, 256, wide_blocks_per_query(Q) * Q);
+            e = launch_wide_score(sd, false, p->dtype, Q, p->K, p->d, hidden, Wt, nullptr, nullptr, idx->V, nullptr,
+                                  nullptr, rows, acc, 1, w, s);
+            m.done();
+            if (e != hipSuccess) return hip_fail("cb_step: wide-row scores", e);
+        }
         ProfMark m(p, s, t, CB_KERNEL_STEP_QUERY, query_threads(p->K), Q);
-        e = launch_step_query(sd, p->dtype, Q, p->K, Kc, p->d, hidden, Wt, rows, acc, ot, op, orow, ol, s);
+        e = launch_step_query(sd, p->dtype, Q, p->K, Kc, p->d, hidden, Wt, rows, acc, split ? w.cand : nullptr,
+                              split ? w.cand_off : nullptr, split ? w.cap : 0, ot, op, orow, ol, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: sparse step", e);
         return CB_OK;
@@ -561,9 +571,14 @@ cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_
 
 cb_status cb_set_path(cb_plan* p, int32_t t, cb_path path) {
     clear_error();
-    if (!p || t < 0 || t >= p->idx->L || path < CB_PATH_AUTO || path > CB_PATH_SPARSE) {
+    if (!p || t < 0 || t >= p->idx->L || path < CB_PATH_AUTO || path > CB_PATH_SPARSE_SPLIT) {
         set_error("cb_set_path: bad plan, step or path");
         return CB_EINVAL;
+    }
+    if (path == CB_PATH_SPARSE_SPLIT) {
+        DeviceGuard g(p->device);
+        cb_status st = wide_alloc(p);
+        if (st != CB_OK) return st;
     }
     if (path == CB_PATH_DENSE && !dense_available(p)) {
         set_error("cb_set_path: the dense path needs d to be a multiple of 64 for bf16");
@@ -683,18 +698,22 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
         const bool sel_free = p->select[(size_t)t] == CB_SELECT_AUTO;
         if (reps > 0 && (path_free || sel_free)) {
             // time every allowed (scoring path, selection) pair on this step's inputs, outputs to scratch
-            float best_us[2] = {-1.f, -1.f};  // per path, best over the selections
+            float best_us[2] = {-1.f, -1.f};  // dense, sparse (either variant): best over the selections
             float best = -1.f;
             int32_t best_path = 0, best_sel = 0;
-            const int32_t paths[2] = {CB_PATH_DENSE, CB_PATH_SPARSE};
+            const int32_t paths[3] = {CB_PATH_DENSE, CB_PATH_SPARSE, CB_PATH_SPARSE_SPLIT};
             const int32_t sels[2] = {CB_SELECT_LDS, CB_SELECT_RADIX};
-            for (int k = 0; k < 2 && st == CB_OK; ++k) {
+            const cb::StepTable& T = idx->steps[(size_t)t];
+            const bool has_wide = T.store == CB_STORE_BITMAP || T.S > 64;
+            for (int k = 0; k < 3 && st == CB_OK; ++k) {
                 if (!path_free && paths[k] != resolve_path(p, t)) continue;
                 if (paths[k] == CB_PATH_DENSE && !dense_available(p)) continue;
                 for (int m = 0; m < 2 && st == CB_OK; ++m) {
                     if (!sel_free && sels[m] != p->select[(size_t)t]) continue;
                     if (sels[m] == CB_SELECT_LDS && !lds_select_ok(p, t)) continue;
-                    if (sels[m] == CB_SELECT_RADIX && wide_alloc(p) != CB_OK) {
+                    // the split variant differs from plain sparse only on LDS steps with wide rows
+                    if (paths[k] == CB_PATH_SPARSE_SPLIT && (sels[m] != CB_SELECT_LDS || !has_wide)) continue;
+                    if ((paths[k] == CB_PATH_SPARSE_SPLIT || sels[m] == CB_SELECT_RADIX) && wide_alloc(p) != CB_OK) {
                         (void)hipGetLastError();
                         clear_error();
                         continue;
@@ -714,7 +733,8 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
                     float ms = 0.f;
                     (void)hipEventElapsedTime(&ms, ev0, ev1);
                     const float us = ms * 1000.f / (float)reps;
-                    if (best_us[k] < 0.f || us < best_us[k]) best_us[k] = us;
+                    const int slot = paths[k] == CB_PATH_DENSE ? 0 : 1;
+                    if (best_us[slot] < 0.f || us < best_us[slot]) best_us[slot] = us;
                     if (best < 0.f || us < best) {
                         best = us;
                         best_path = paths[k];

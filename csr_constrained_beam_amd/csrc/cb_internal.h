@@ -133,9 +133,13 @@ size_t query_lds_bytes(int S, int K, int Kc, int d);
 int gemm_blocks(cb_dtype dt, int R, int V);
 
 // Sparse path: the whole step in one launch, one workgroup per query.
+// pre / pre_off / pre_cap: scores of the wide rows from launch_wide_score(...,
+// wide_only = 1, ...) (candidate z bits in the high half, per-query offsets
+// [K+1], per-query capacity), or null to score them in the step kernel.
 hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int Kc, int d, const void* hidden,
-                             const void* W, const int32_t* beam_rows, const float* acc, int32_t* tok, int32_t* par,
-                             int32_t* rows, float* logp, hipStream_t s);
+                             const void* W, const int32_t* beam_rows, const float* acc, const uint64_t* pre,
+                             const int32_t* pre_off, int64_t pre_cap, int32_t* tok, int32_t* par, int32_t* rows,
+                             float* logp, hipStream_t s);
 // Dense path: live-beam list, full-codebook scores, per-beam expansion, per-query merge.
 hipError_t launch_live_rows(const StepDev& st, int R, const int32_t* beam_rows, const float* acc, int32_t* live,
                             int32_t* n_live, int32_t* ci_of, hipStream_t s);
@@ -170,8 +174,8 @@ int wide_hist_blocks_per_query(int Q);
 size_t wide_score_lds_bytes(int d, bool dense);
 hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, int K, int d, const void* hidden,
                              const void* W, const float* Z, const float* Zp, int64_t ldz, const int32_t* n_live,
-                             const int32_t* ci_of, const int32_t* beam_rows, const float* acc, const WideDev& w,
-                             hipStream_t s);
+                             const int32_t* ci_of, const int32_t* beam_rows, const float* acc, int wide_only,
+                             const WideDev& w, hipStream_t s);
 hipError_t launch_wide_keys(int Q, int K, const float* acc, const WideDev& w, hipStream_t s);
 hipError_t launch_wide_refine(int Q, int K, const WideDev& w, hipStream_t s);
 hipError_t launch_wide_collect(int Q, int K, const WideDev& w, hipStream_t s);

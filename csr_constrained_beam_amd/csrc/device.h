@@ -42,30 +42,98 @@ __device__ __forceinline__ uint64_t make_key(float score, int parent, int token)
 }
 
 // ---- wave and block primitives ----------------------------------------------
+//
+// Cross-lane exchanges avoid the LDS crossbar (ds_bpermute, ~100 cycles each,
+// serialised by the dependent chains of sorting networks): partner lane^1 and
+// lane^2 by DPP quad permutes, lane^4 and lane^8 by DPP row shifts (one per
+// direction, selected by the lane's bit), lane^16 and lane^32 by the gfx950
+// permlane16/permlane32 swaps.  Broadcasts from a uniform lane use readlane.
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+    static_assert(J == 1 || J == 2 || J == 4 || J == 8 || J == 16 || J == 32, "lane_xor: J is a power of two < 64");
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    } else if constexpr (J == 4 || J == 8) {
+        const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x100 | J, 0xF, 0xF, false);  // lane+J
+        const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x110 | J, 0xF, 0xF, false);  // lane-J
+        return (lane_id() & J) ? dn : up;
+    } else if constexpr (J == 16) {
+        const auto q = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane_id() & 16) ? q[0] : q[1];
+    } else {
+        const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane_id() & 32) ? q[0] : q[1];
+    }
+}
+
+// When j is a compile-time constant after unrolling the switch folds away;
+// otherwise (loops over runtime sizes) one ds_bpermute beats a runtime switch.
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int j) {
+    if (!__builtin_constant_p(j)) return (uint32_t)__shfl_xor((int)v, j);
+    switch (j) {
+        case 1: return lane_xor<1>(v);
+        case 2: return lane_xor<2>(v);
+        case 4: return lane_xor<4>(v);
+        case 8: return lane_xor<8>(v);
+        case 16: return lane_xor<16>(v);
+        default: return lane_xor<32>(v);
+    }
+}
+__device__ __forceinline__ int lane_xor(int v, int j) { return (int)lane_xor((uint32_t)v, j); }
+__device__ __forceinline__ float lane_xor(float v, int j) { return __uint_as_float(lane_xor(__float_as_uint(v), j)); }
+__device__ __forceinline__ double lane_xor(double v, int j) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint64_t r = ((uint64_t)lane_xor((uint32_t)(u >> 32), j) << 32) | lane_xor((uint32_t)u, j);
+    return __longlong_as_double((long long)r);
+}
+
+// Value of lane 63 - lane: mirror within each row of 16, then swap rows.
+__device__ __forceinline__ uint32_t lane_reverse(uint32_t v) {
+    const uint32_t m = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);  // row_mirror
+    return lane_xor<32>(lane_xor<16>(m));
+}
+
+// Broadcast from a lane index that is the same for the whole wave.
+__device__ __forceinline__ int lane_bcast(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
 
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    for (int o = kWave / 2; o > 0; o >>= 1) v += lane_xor(v, o);
     return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, lane_xor(v, o));
     return v;
 }
 
-__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
-    const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src);
-    const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src);
-    return ((uint64_t)hi << 32) | lo;
+// Inclusive prefix sum over the wave (butterfly: after the step with distance
+// o every lane knows the total of its aligned block of 2o lanes).
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    int pre = x, sum = x;
+    const int lane = lane_id();
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int t = lane_xor(sum, o);
+        if (lane & o) pre += t;
+        sum += t;
+    }
+    return pre;
+}
+
+__device__ __forceinline__ uint64_t lane_reverse64(uint64_t v) {
+    return ((uint64_t)lane_reverse((uint32_t)(v >> 32)) << 32) | lane_reverse((uint32_t)v);
 }
 
 __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
-    return ((uint64_t)hi << 32) | lo;
+    return ((uint64_t)lane_xor((uint32_t)(v >> 32), m) << 32) | lane_xor((uint32_t)v, m);
 }
 
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
@@ -90,7 +158,7 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
 // cascade sorts it.)
 __device__ __forceinline__ uint64_t wave_merge_top(uint64_t a, uint64_t b) {
     const int lane = threadIdx.x & (kWave - 1);
-    uint64_t c = umax64(a, shfl64(b, kWave - 1 - lane));
+    uint64_t c = umax64(a, lane_reverse64(b));
 #pragma unroll
     for (int j = kWave / 2; j > 0; j >>= 1) {
         const uint64_t o = shfl_xor64(c, j);
@@ -112,7 +180,7 @@ __device__ __forceinline__ uint32_t wave_sort_desc32(uint32_t v) {
     for (int k = 2; k <= kWave; k <<= 1)
 #pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint32_t o = (uint32_t)__shfl_xor((int)v, j);
+            const uint32_t o = lane_xor(v, j);
             const bool take_max = ((lane & j) == 0) == ((lane & k) == 0);
             v = take_max ? (v > o ? v : o) : (v < o ? v : o);
         }
@@ -135,18 +203,13 @@ __device__ uint64_t wave_top(int Kc, ScoreF score, KeyF key, uint64_t* wl) {
     uint32_t mx = 0;
 #pragma unroll
     for (int i = 0; i < M; ++i) mx = max(mx, score(i));
-    uint32_t tau = (uint32_t)__shfl((int)wave_sort_desc32(mx), Kc - 1);
+    uint32_t tau = (uint32_t)lane_bcast((int)wave_sort_desc32(mx), Kc - 1);
     if (tau == 0) tau = 1;
     int cnt = 0;
 #pragma unroll
     for (int i = 0; i < M; ++i) cnt += score(i) >= tau;
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-    }
-    const int total = __shfl(incl, kWave - 1);
+    const int incl = wave_inclusive_scan(cnt);
+    const int total = lane_bcast(incl, kWave - 1);
     uint64_t best = 0;
     bool first = true;
     for (int s0 = 0; s0 < total; s0 += kWaveListCap) {
@@ -199,12 +262,7 @@ __device__ T block_sum(T v, T* red) {
 template <int NT>
 __device__ int block_exclusive_scan(int c, int* red, int* total) {
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-    int x = c;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_inclusive_scan(c);
     if (lane == kWave - 1) red[w] = x;
     __syncthreads();
     int off = 0, tot = 0;
@@ -287,6 +345,41 @@ __device__ __forceinline__ void load8(const float* p, float* o) {
     o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
     o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
 }
+// 8 consecutive elements kept raw in registers (loaded now, converted later),
+// so that several rows' loads can be in flight before any is used.
+typedef unsigned int cb_u32x4 __attribute__((ext_vector_type(4)));
+typedef float cb_f32x8 __attribute__((ext_vector_type(8)));
+template <typename DT>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+    cb_u32x4 v;
+    __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const cb_u32x4*>(p); }
+    __device__ __forceinline__ void zero() { v = cb_u32x4{0u, 0u, 0u, 0u}; }
+    __device__ __forceinline__ float dot(const float* h, float s) const {
+        s = fmaf(h[0], __uint_as_float(v.x << 16), s);
+        s = fmaf(h[1], __uint_as_float(v.x & 0xFFFF0000u), s);
+        s = fmaf(h[2], __uint_as_float(v.y << 16), s);
+        s = fmaf(h[3], __uint_as_float(v.y & 0xFFFF0000u), s);
+        s = fmaf(h[4], __uint_as_float(v.z << 16), s);
+        s = fmaf(h[5], __uint_as_float(v.z & 0xFFFF0000u), s);
+        s = fmaf(h[6], __uint_as_float(v.w << 16), s);
+        s = fmaf(h[7], __uint_as_float(v.w & 0xFFFF0000u), s);
+        return s;
+    }
+};
+template <>
+struct Raw8<float> {
+    cb_f32x8 v;
+    __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const cb_f32x8*>(p); }
+    __device__ __forceinline__ void zero() { v = cb_f32x8{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}; }
+    __device__ __forceinline__ float dot(const float* h, float s) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = fmaf(h[i], v[i], s);
+        return s;
+    }
+};
+
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 

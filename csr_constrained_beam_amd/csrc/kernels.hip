@@ -118,7 +118,9 @@ template <typename DT, int NT, int CH>
 __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, int d,
                                                    const DT* __restrict__ hidden, const DT* __restrict__ W,
                                                    const int32_t* __restrict__ beam_rows,
-                                                   const float* __restrict__ acc, int32_t* __restrict__ out_tok,
+                                                   const float* __restrict__ acc, const uint64_t* __restrict__ pre,
+                                                   const int32_t* __restrict__ pre_off, int64_t pre_cap,
+                                                   int32_t* __restrict__ out_tok,
                                                    int32_t* __restrict__ out_par, int32_t* __restrict__ out_rows,
                                                    float* __restrict__ out_logp) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -187,29 +189,37 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
             }
         float z[2] = {-INFINITY, -INFINITY};
         const int nmax = max(small[0] ? n[0] : 0, small[1] ? n[1] : 0);
-        for (int j = 0; j < nmax; ++j) {
-            float sv[2] = {0.f, 0.f};
+        // kTok tokens of each of the two beams at a time: all their W_t row
+        // loads are issued before any is reduced, so the latencies overlap
+        // (as many as the register budget of a 1024-thread workgroup allows)
+        constexpr int kTok = CH >= 4 ? 1 : 4 / CH;
+        for (int j0 = 0; j0 < nmax; j0 += kTok) {
+            Raw8<DT> wr8[2][kTok][CH];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int tj = __shfl(tk[u], j);
-                if (small[u] && j < n[u]) {
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int jj = 0; jj < kTok; ++jj) {
+                    const int j = j0 + jj;
+                    const int tj = lane_bcast(tk[u], j < kWave ? j : 0);
+                    const bool on = small[u] && j < n[u];
                     const DT* wr = W + (int64_t)tj * d;
 #pragma unroll
                     for (int c = 0; c < CH; ++c) {
                         const int i = c * kWave * 8 + lane * 8;
-                        if (i < d) {
-                            float w8[8];
-                            load8(wr + i, w8);
-                            sv[u] = dot8(hr[u][c], w8, sv[u]);
-                        }
+                        if (on && i < d) wr8[u][jj][c].load(wr + i);
+                        else wr8[u][jj][c].zero();
                     }
                 }
-            }
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const float t = wave_sum(sv[u]);
-                if (lane == j) z[u] = t;
-            }
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int jj = 0; jj < kTok; ++jj) {
+                    float sv = 0.f;
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) sv = wr8[u][jj][c].dot(hr[u][c], sv);
+                    const float t = wave_sum(sv);
+                    if (lane == j0 + jj) z[u] = t;
+                }
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -235,10 +245,16 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
         const uint32_t e0 = st.row_ptr[r];
         const int n = (int)(st.row_ptr[r + 1] - e0);
         block_fill_tokens<NT>(st, r, e0, n, tok_s, red_i);
-        for (int x = tid; x < d; x += NT) h_s[x] = to_f32(hidden[b * d + x]);
-        __syncthreads();
-        block_scores<DT, NT>(h_s, W, d, tok_s, n, z_s);
-        __syncthreads();
+        if (pre) {  // scored apart, across many workgroups
+            const uint64_t* zp = pre + (int64_t)q * pre_cap + pre_off[(int64_t)q * (K + 1) + k];
+            for (int j = tid; j < n; j += NT) z_s[j] = __uint_as_float((uint32_t)(zp[j] >> 32));
+            __syncthreads();
+        } else {
+            for (int x = tid; x < d; x += NT) h_s[x] = to_f32(hidden[b * d + x]);
+            __syncthreads();
+            block_scores<DT, NT>(h_s, W, d, tok_s, n, z_s);
+            __syncthreads();
+        }
         const float lse = block_lse<NT>(z_s, n, red_f);
         auto keyf = [&](int j) { return make_key(a + (z_s[j] - lse), k, (int)tok_s[j]); };
         uint64_t* slot = qkeys + k * Kc;
@@ -488,34 +504,41 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_bf16(int V, int d, const 
     __syncthreads();
     const int wm = (wv / (kBN / kWN)) * kWM, wn = (wv % (kBN / kWN)) * kWN;
 
+    // Rows past the live list or the codebook read a valid row instead (the
+    // tile's first live beam, the last codebook row): their products are
+    // never stored, and unconditional loads keep the prefetch ring free of
+    // branches, so the compiler waits only for the tile it stashes.
     const uint16_t* pa[CA];
     const uint16_t* pb[CB];
     int oa[CA], ob[CB];
 #pragma unroll
     for (int u = 0; u < CA; ++u) {
         const int c = tid + u * NT, r = c / (kBK / 8), cc = (c % (kBK / 8)) * 8;
-        const int hb = rows_s[r];
-        pa[u] = hb >= 0 ? H + (int64_t)hb * d + kbeg + cc : nullptr;
+        const int hb = rows_s[r] >= 0 ? rows_s[r] : rows_s[0];
+        pa[u] = H + (int64_t)hb * d + kbeg + cc;
         oa[u] = r * kLDP + cc;
     }
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
         const int c = tid + u * NT, r = c / (kBK / 8), cc = (c % (kBK / 8)) * 8;
-        pb[u] = n0 + r < V ? W + (int64_t)(n0 + r) * d + kbeg + cc : nullptr;
+        pb[u] = W + (int64_t)min(n0 + r, V - 1) * d + kbeg + cc;
         ob[u] = r * kLDP + cc;
     }
-    u32x4_t ra[CA], rb[CB];
-    const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-#define CB_GEMM_FETCH(k0)                                                                         \
-    _Pragma("unroll") for (int u = 0; u < CA; ++u) ra[u] =                                        \
-        pa[u] ? *reinterpret_cast<const u32x4_t*>(pa[u] + (k0)) : zero4;                          \
-    _Pragma("unroll") for (int u = 0; u < CB; ++u) rb[u] =                                        \
-        pb[u] ? *reinterpret_cast<const u32x4_t*>(pb[u] + (k0)) : zero4;
-#define CB_GEMM_STASH(buf)                                                                        \
-    _Pragma("unroll") for (int u = 0; u < CA; ++u)                                                \
-        *reinterpret_cast<u32x4_t*>(&As[(buf) * kBM * kLDP + oa[u]]) = ra[u];                      \
-    _Pragma("unroll") for (int u = 0; u < CB; ++u)                                                \
-        *reinterpret_cast<u32x4_t*>(&Bs[(buf) * kBN * kLDP + ob[u]]) = rb[u];
+    // Register ring of kPF k-tiles: tile kt+kPF is requested while tile kt is
+    // computed, so kPF-1 global round trips are always in flight (the loop is
+    // otherwise bound by one global latency per k-tile).
+    constexpr int kPF = 4;
+    u32x4_t ra[kPF][CA], rb[kPF][CB];
+#define CB_GEMM_FETCH(slot, k0)                                                                   \
+    _Pragma("unroll") for (int x_ = 0; x_ < CA; ++x_) ra[slot][x_] =                              \
+        *reinterpret_cast<const u32x4_t*>(pa[x_] + (k0));                                          \
+    _Pragma("unroll") for (int x_ = 0; x_ < CB; ++x_) rb[slot][x_] =                              \
+        *reinterpret_cast<const u32x4_t*>(pb[x_] + (k0));
+#define CB_GEMM_STASH(slot, buf)                                                                  \
+    _Pragma("unroll") for (int x_ = 0; x_ < CA; ++x_)                                             \
+        *reinterpret_cast<u32x4_t*>(&As[(buf) * kBM * kLDP + oa[x_]]) = ra[slot][x_];             \
+    _Pragma("unroll") for (int x_ = 0; x_ < CB; ++x_)                                             \
+        *reinterpret_cast<u32x4_t*>(&Bs[(buf) * kBN * kLDP + ob[x_]]) = rb[slot][x_];
 
     f32x16_t acc[TJ];
 #pragma unroll
@@ -523,33 +546,63 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_bf16(int V, int d, const 
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
 
-    CB_GEMM_FETCH(0)
-    CB_GEMM_STASH(0)
-    __syncthreads();
     const int nk = klen / kBK;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) {
-            CB_GEMM_FETCH((kt + 1) * kBK)
-        }
+    // all fragments of the LDS k-tile first, then the MFMAs back to back
+    auto compute = [&](int buf) {
         const uint16_t* Ab = As + buf * kBM * kLDP;
         const uint16_t* Bb = Bs + buf * kBN * kLDP;
+        constexpr int NKK = kBK / 16;
+        u32x4_t af[NKK], bf[NKK][TJ];
 #pragma unroll
-        for (int kk = 0; kk < kBK; kk += 16) {
-            const bf16x8_t av = __builtin_bit_cast(
-                bf16x8_t, *reinterpret_cast<const u32x4_t*>(&Ab[(wm + (lane & 31)) * kLDP + kk + (lane >> 5) * 8]));
+        for (int x = 0; x < NKK; ++x) {
+            af[x] = *reinterpret_cast<const u32x4_t*>(&Ab[(wm + (lane & 31)) * kLDP + x * 16 + (lane >> 5) * 8]);
 #pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-                const bf16x8_t bv = __builtin_bit_cast(
-                    bf16x8_t,
-                    *reinterpret_cast<const u32x4_t*>(&Bb[(wn + j * 32 + (lane & 31)) * kLDP + kk + (lane >> 5) * 8]));
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[j], 0, 0, 0);
+            for (int j = 0; j < TJ; ++j)
+                bf[x][j] = *reinterpret_cast<const u32x4_t*>(
+                    &Bb[(wn + j * 32 + (lane & 31)) * kLDP + x * 16 + (lane >> 5) * 8]);
+        }
+#pragma unroll
+        for (int x = 0; x < NKK; ++x)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[x]),
+                                                                 __builtin_bit_cast(bf16x8_t, bf[x][j]), acc[j],
+                                                                 0, 0, 0);
+    };
+    if (nk % kPF == 0) {
+        // Every fetch and stash unconditional (tiles past the end re-read the
+        // last one, and the final stash fills an unused buffer), so the waits
+        // the compiler inserts cover only the tile being stashed.
+#pragma unroll
+        for (int u = 0; u < kPF; ++u) {
+            CB_GEMM_FETCH(u, u * kBK)
+        }
+        CB_GEMM_STASH(0, 0)
+        __syncthreads();
+        for (int kt0 = 0; kt0 < nk; kt0 += kPF) {
+#pragma unroll
+            for (int u = 0; u < kPF; ++u) {
+                const int kt = kt0 + u;  // tile kt is in LDS buffer kt & 1; its register slot u is free
+                compute(kt & 1);
+                CB_GEMM_STASH((u + 1) % kPF, (kt & 1) ^ 1)
+                CB_GEMM_FETCH(u, min(kt + kPF, nk - 1) * kBK)
+                __syncthreads();
             }
         }
-        if (kt + 1 < nk) {
-            CB_GEMM_STASH(buf ^ 1)
-        }
+    } else {
+        CB_GEMM_FETCH(0, 0)
+        CB_GEMM_STASH(0, 0)
         __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            if (kt + 1 < nk) {
+                CB_GEMM_FETCH(0, (kt + 1) * kBK)
+            }
+            compute(kt & 1);
+            if (kt + 1 < nk) {
+                CB_GEMM_STASH(0, (kt & 1) ^ 1)
+            }
+            __syncthreads();
+        }
     }
 #undef CB_GEMM_FETCH
 #undef CB_GEMM_STASH
@@ -683,15 +736,16 @@ size_t query_lds_bytes(int S, int K, int Kc, int d) {
 }
 
 hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int Kc, int d, const void* hidden,
-                             const void* W, const int32_t* beam_rows, const float* acc, int32_t* tok, int32_t* par,
-                             int32_t* rows, float* logp, hipStream_t s) {
+                             const void* W, const int32_t* beam_rows, const float* acc, const uint64_t* pre,
+                             const int32_t* pre_off, int64_t pre_cap, int32_t* tok, int32_t* par, int32_t* rows,
+                             float* logp, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
     const int NT = query_threads(K);
     const QueryLds lay = query_lds(st.S, K, Kc, d, NT);
     const int CH = (d + kWave * 8 - 1) / (kWave * 8);
 #define CB_QUERY(DT, NTV, CHV)                                                                           \
     hipLaunchKernelGGL((k_step_query<DT, NTV, CHV>), dim3(Q), dim3(NTV), lay.total, s, st, K, Kc, d,     \
-                       (const DT*)hidden, (const DT*)W, beam_rows, acc, tok, par, rows, logp)
+                       (const DT*)hidden, (const DT*)W, beam_rows, acc, pre, pre_off, pre_cap, tok, par, rows, logp)
 #define CB_QUERY_NT(DT, CHV) \
     do { if (NT == 1024) CB_QUERY(DT, 1024, CHV); else CB_QUERY(DT, 512, CHV); } while (0)
     if (dt == CB_BF16) {

@@ -26,6 +26,11 @@
 // Work is cut into chunks of kWCH consecutive valid tokens of one beam; a
 // beam's log-sum-exp is combined from its chunks' (max, sum exp) pairs.
 //
+// k_wide_score also serves the per-query (LDS) sparse step: with wide_only it
+// scores just the rows that step would give a whole workgroup (rows of more
+// than 64 tokens and bitmap rows), spread over many workgroups, and the step
+// kernel then reads their scores instead of computing them.
+//
 // Kernels per step: k_wide_score (slot offsets, scores, chunk softmax
 // partials), k_wide_keys (keys, first-digit histogram), k_wide_refine (first
 // digit, second-digit histogram), k_wide_collect (digits, survivors),
@@ -90,7 +95,7 @@ __device__ __forceinline__ int slot_of_chunk(const int32_t* offs, int K, int c) 
 // All threads call.
 template <int NT>
 __device__ void slot_offsets(const StepDev& st, int q, int K, const int32_t* __restrict__ beam_rows,
-                             const float* __restrict__ acc, int32_t* co_s, int32_t* ho_s, int* red_i) {
+                             const float* __restrict__ acc, int wide_only, int32_t* co_s, int32_t* ho_s, int* red_i) {
     constexpr int PER = (kMaxKRadix + NT - 1) / NT;
     const int k0 = threadIdx.x * PER;
     int n[PER];
@@ -103,6 +108,8 @@ __device__ void slot_offsets(const StepDev& st, int q, int K, const int32_t* __r
             const int64_t b = (int64_t)q * K + k;
             const int32_t r = beam_rows[b];
             if (beam_live(st, r, acc[b])) x = (int)(st.row_ptr[r + 1] - st.row_ptr[r]);
+            // wide_only: only the rows the per-query kernel would score with a whole workgroup
+            if (wide_only && st.store == CB_STORE_CSR && x <= kSmallRow) x = 0;
         }
         n[u] = x;
         sc += x;
@@ -208,14 +215,15 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
                                                           const int32_t* __restrict__ n_live,
                                                           const int32_t* __restrict__ ci_of, int split_ok,
                                                           const int32_t* __restrict__ beam_rows,
-                                                          const float* __restrict__ acc, WideDev w, int G) {
+                                                          const float* __restrict__ acc, int wide_only, WideDev w,
+                                                          int G) {
     extern __shared__ __align__(16) float h_s[];  // [d], sparse scoring only
     __shared__ float z_s[kWCH];
     __shared__ uint16_t tok_s[kWCH];
     __shared__ int32_t co_s[kMaxKRadix + 1], ho_s[kMaxKRadix + 1];
     __shared__ int red_i[kWThreads / kWave];
     const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
-    slot_offsets<kWThreads>(st, q, K, beam_rows, acc, co_s, ho_s, red_i);
+    slot_offsets<kWThreads>(st, q, K, beam_rows, acc, wide_only, co_s, ho_s, red_i);
     if (g == 0) {
         int32_t* co = w.cand_off + (int64_t)q * (K + 1);
         int32_t* ho = w.chunk_off + (int64_t)q * (K + 1);
@@ -401,7 +409,7 @@ __global__ __launch_bounds__(kWThreads) void k_wide_collect(int K, WideDev w, in
         const uint64_t mask = __ballot(take);
         int base = 0;
         if (lane == 0 && mask) base = atomicAdd(&w.surv_n[q], (int)__popcll(mask));
-        base = __shfl(base, 0);
+        base = lane_bcast(base, 0);
         if (take) {
             const int pos = base + (int)__popcll(mask & ((1ull << lane) - 1ull));
             if (pos < kSurvCap) out[pos] = key;
@@ -590,8 +598,8 @@ size_t wide_score_lds_bytes(int d, bool dense) { return dense ? 0 : (size_t)d * 
 
 hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, int K, int d, const void* hidden,
                              const void* W, const float* Z, const float* Zp, int64_t ldz, const int32_t* n_live,
-                             const int32_t* ci_of, const int32_t* beam_rows, const float* acc, const WideDev& w,
-                             hipStream_t s) {
+                             const int32_t* ci_of, const int32_t* beam_rows, const float* acc, int wide_only,
+                             const WideDev& w, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
     const int G = wide_blocks_per_query(Q);
     const dim3 grid(Q * G);
@@ -599,7 +607,7 @@ hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, 
     const int split_ok = dt == CB_BF16 ? 1 : 0;
 #define CB_WSCORE(DT, DENSE)                                                                                  \
     hipLaunchKernelGGL((k_wide_score<DT, DENSE>), grid, dim3(kWThreads), lds, s, st, K, d, (const DT*)hidden, \
-                       (const DT*)W, Z, Zp, ldz, n_live, ci_of, split_ok, beam_rows, acc, w, G)
+                       (const DT*)W, Z, Zp, ldz, n_live, ci_of, split_ok, beam_rows, acc, wide_only, w, G)
     if (dt == CB_BF16) {
         if (dense) CB_WSCORE(uint16_t, true); else CB_WSCORE(uint16_t, false);
     } else {

@@ -64,8 +64,11 @@ typedef enum { CB_F32 = 0, CB_BF16 = 1 } cb_dtype;
 
 /* Scoring path of a step: full-codebook MFMA product then a gather of the
  * valid columns (DENSE), or a gather-dot over the valid tokens only (SPARSE).
- * AUTO uses the measured choice of cb_tune, else a width rule. */
-typedef enum { CB_PATH_AUTO = 0, CB_PATH_DENSE = 1, CB_PATH_SPARSE = 2 } cb_path;
+ * SPARSE_SPLIT is SPARSE with the rows too wide for one wavefront scored
+ * first by a separate pass spread over many workgroups (same results; it
+ * differs from SPARSE only under the LDS selection).  AUTO uses the measured
+ * choice of cb_tune, else a width rule. */
+typedef enum { CB_PATH_AUTO = 0, CB_PATH_DENSE = 1, CB_PATH_SPARSE = 2, CB_PATH_SPARSE_SPLIT = 3 } cb_path;
 
 /* Storage of a step table: CSR (row_ptr + tokens) for narrow steps, a per-row
  * bitmap (+ row_ptr) for wide steps (ZeroGR: dense tables where many tokens
@@ -151,7 +154,8 @@ cb_status cb_set_select(cb_plan* plan, int32_t t, cb_select select);
 cb_status cb_get_select(const cb_plan* plan, int32_t t, cb_select* select);
 
 /* Force the scoring path of step t (tests run both ways).  CB_PATH_AUTO
- * restores the measured or default choice. */
+ * restores the measured or default choice.  CB_PATH_SPARSE_SPLIT may allocate
+ * the radix-selection workspace (CB_ENOMEM). */
 cb_status cb_set_path(cb_plan* plan, int32_t t, cb_path path);
 
 /* The path step t will take (never CB_PATH_AUTO). */

@@ -95,7 +95,7 @@ def test_fullsize_decode(name):
 
 
 @pytest.mark.parametrize("name", ["production", "hybrid"])
-@pytest.mark.parametrize("path", ["tuned", "dense", "sparse"])
+@pytest.mark.parametrize("path", ["tuned", "dense", "sparse", "sparse_split"])
 def test_fullsize_teacher_forced(name, path):
     w = big(name)
     cfg, ref, plan, T = w["cfg"], w["ref"], w["plan"], w["T"]

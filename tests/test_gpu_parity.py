@@ -56,7 +56,7 @@ def gpu_step(plan, t, h, Wt, rows, acc):
 
 
 @pytest.mark.parametrize("name", ["tiny", "small"])
-@pytest.mark.parametrize("path", ["sparse", "dense", "auto"])
+@pytest.mark.parametrize("path", ["sparse", "dense", "auto", "sparse_split"])
 @pytest.mark.parametrize("store", ["auto", "csr", "bitmap"])
 def test_step_parity_teacher_forced(name, path, store):
     w = workload(name)

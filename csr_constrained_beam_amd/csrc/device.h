@@ -16,6 +16,7 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kSmallRow = 64;  // rows up to this many tokens take the one-wave path
+constexpr int kPreMin = 16;    // with scores computed apart: rows above this many tokens read them
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 

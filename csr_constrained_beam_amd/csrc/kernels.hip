@@ -176,19 +176,29 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
             tk[u] = small[u] && lane < n[u] ? (int)st.tok[e0[u] + lane] : 0;
         }
         if (!small[0] && !small[1]) continue;
+        // rows whose scores were computed apart are read, the others scored here
+        bool dots[2];
+        float z[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const bool ready = pre && small[u] && n[u] > kPreMin;
+            dots[u] = small[u] && !ready;
+            if (ready && lane < n[u])
+                z[u] = __uint_as_float((uint32_t)(pre[(int64_t)q * pre_cap + pre_off[(int64_t)q * (K + 1) + kk[u]] +
+                                                      lane] >> 32));
+        }
         float hr[2][CH][8];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
                 const int i = c * kWave * 8 + lane * 8;
-                if (small[u] && i < d) load8(hidden + b[u] * d + i, hr[u][c]);
+                if (dots[u] && i < d) load8(hidden + b[u] * d + i, hr[u][c]);
                 else
 #pragma unroll
                     for (int e = 0; e < 8; ++e) hr[u][c][e] = 0.f;
             }
-        float z[2] = {-INFINITY, -INFINITY};
-        const int nmax = max(small[0] ? n[0] : 0, small[1] ? n[1] : 0);
+        const int nmax = max(dots[0] ? n[0] : 0, dots[1] ? n[1] : 0);
         // kTok tokens of each of the two beams at a time: all their W_t row
         // loads are issued before any is reduced, so the latencies overlap
         // (as many as the register budget of a 1024-thread workgroup allows)
@@ -201,7 +211,7 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
                 for (int jj = 0; jj < kTok; ++jj) {
                     const int j = j0 + jj;
                     const int tj = lane_bcast(tk[u], j < kWave ? j : 0);
-                    const bool on = small[u] && j < n[u];
+                    const bool on = dots[u] && j < n[u];
                     const DT* wr = W + (int64_t)tj * d;
 #pragma unroll
                     for (int c = 0; c < CH; ++c) {
@@ -218,7 +228,7 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
 #pragma unroll
                     for (int c = 0; c < CH; ++c) sv = wr8[u][jj][c].dot(hr[u][c], sv);
                     const float t = wave_sum(sv);
-                    if (lane == j0 + jj) z[u] = t;
+                    if (dots[u] && lane == j0 + jj) z[u] = t;
                 }
         }
 #pragma unroll

@@ -27,9 +27,9 @@
 // beam's log-sum-exp is combined from its chunks' (max, sum exp) pairs.
 //
 // k_wide_score also serves the per-query (LDS) sparse step: with wide_only it
-// scores just the rows that step would give a whole workgroup (rows of more
-// than 64 tokens and bitmap rows), spread over many workgroups, and the step
-// kernel then reads their scores instead of computing them.
+// scores just the rows of more than kPreMin tokens (and bitmap rows), spread
+// over many workgroups, and the step kernel then reads their scores instead of
+// computing them one wavefront or one workgroup per row.
 //
 // Kernels per step: k_wide_score (slot offsets, scores, chunk softmax
 // partials), k_wide_keys (keys, first-digit histogram), k_wide_refine (first
@@ -108,8 +108,8 @@ __device__ void slot_offsets(const StepDev& st, int q, int K, const int32_t* __r
             const int64_t b = (int64_t)q * K + k;
             const int32_t r = beam_rows[b];
             if (beam_live(st, r, acc[b])) x = (int)(st.row_ptr[r + 1] - st.row_ptr[r]);
-            // wide_only: only the rows the per-query kernel would score with a whole workgroup
-            if (wide_only && st.store == CB_STORE_CSR && x <= kSmallRow) x = 0;
+            // wide_only: only the rows the per-query kernel reads scores for (more than kPreMin tokens)
+            if (wide_only && st.store == CB_STORE_CSR && x <= kPreMin) x = 0;
         }
         n[u] = x;
         sc += x;
@@ -224,7 +224,10 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
     __shared__ int red_i[kWThreads / kWave];
     const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
     slot_offsets<kWThreads>(st, q, K, beam_rows, acc, wide_only, co_s, ho_s, red_i);
-    if (g == 0) {
+    if (g == 0 && wide_only) {
+        int32_t* co = w.cand_off + (int64_t)q * (K + 1);
+        for (int k = tid; k <= K; k += kWThreads) co[k] = co_s[k];
+    } else if (g == 0) {
         int32_t* co = w.cand_off + (int64_t)q * (K + 1);
         int32_t* ho = w.chunk_off + (int64_t)q * (K + 1);
         for (int k = tid; k <= K; k += kWThreads) {

@@ -148,7 +148,9 @@ def main():
     trace_h, trace_rows, trace_acc = rec["trace_h"], rec["trace_rows"], rec["trace_acc"]
     rows_np = trace_rows.cpu().numpy()
 
-    # workload accounting from the library's own tables (rows read back from the device)
+    # workload accounting from the library's own tables: a host-side copy of the
+    # index, or (catalogs too large to build twice) rows read back from the device
+    hidx = cb.Index(items, cfg.V, device=-1) if cfg.n_items <= 50_000_000 else idx
     words = (V + 31) // 32
     steps = []
     for t in range(L):
@@ -156,7 +158,7 @@ def main():
         fan = np.zeros(len(live), np.int64)
         toks = set()
         for i, b in enumerate(live):
-            tk, _ = idx.row(t, int(rows_np[t][b]))
+            tk, _ = hidx.row(t, int(rows_np[t][b]))
             fan[i] = len(tk)
             toks.update(tk.tolist())
         S = info[t]["max_fanout"]
@@ -190,6 +192,7 @@ def main():
             "selection": plan.get_select(t),
         })
     expansions = sum(s["expansions"] for s in steps)
+    del hidx
 
     # teacher-forced pass over all L steps, outputs into fixed buffers
     outs = [tuple(torch.empty(R, dtype=dt, device=dev) for dt in (torch.int32, torch.int32, torch.int32,

@@ -136,13 +136,32 @@ def main():
     # free-running decode: records every step's inputs; also times the full decode
     rec = plan.decode(q, P, W, trace=True)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(5):
-        plan.decode(q, P, W)
-    ev1.record()
-    torch.cuda.synchronize()
-    decode_ms = ev0.elapsed_time(ev1) / 5
+
+    def time_decodes(fused, n=10):
+        plan.set_decode_fusion(fused)
+        a = plan.decode(q, P, W)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(n):
+            plan.decode(q, P, W)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n, a
+
+    decode_ms_steps, dec_a = time_decodes(False)
+    decode_ms, dec_b = time_decodes(True)
+    for k in ("seqs", "logp", "rows"):
+        assert torch.equal(dec_a[k], dec_b[k]), "persistent decode differs from the step-by-step decode"
+    plan.profile_start(capacity=4 * cfg.L * 10)
+    plan.decode(q, P, W)
+    tail_recs = [r for r in plan.profile_stop() if r["kernel"] == "decode_tail"]
+    tail = [r["step"] for r in tail_recs]
+    phases = plan.profile_phases()
+    log("decode: %.4f ms step by step, %.4f ms with the persistent tail (from step %s)"
+        % (decode_ms_steps, decode_ms, tail[0] if tail else "-"))
+    for ph in phases:
+        log("  persistent step %d: selection %.2f us, hidden update %.2f us" % (ph["step"], ph["select_us"],
+                                                                             ph["update_us"]))
 
     L, R, K, Q, d, V = cfg.L, cfg.Q * cfg.K, cfg.K, cfg.Q, cfg.d, cfg.V
     trace_h, trace_rows, trace_acc = rec["trace_h"], rec["trace_rows"], rec["trace_acc"]
@@ -336,6 +355,10 @@ def main():
         "us_per_decode_step": ms_per_pass * 1000.0 / L,
         "expansions_per_pass": expansions,
         "decode_ms_with_model_standin": decode_ms,
+        "decode_ms_step_by_step": decode_ms_steps,
+        "decode_persistent_from_step": tail[0] if tail else None,
+        "decode_persistent_us": tail_recs[0]["us"] if tail_recs else None,
+        "decode_persistent_phases": phases,
         "index": {"build_s": round(build_s, 2), "bytes": sum(i["bytes"] for i in info),
                   "rows": [i["n_rows"] for i in info], "storage": [i["storage"] for i in info]},
         "per_step": steps,

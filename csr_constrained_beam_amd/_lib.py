@@ -36,9 +36,14 @@ class KernelTime(ctypes.Structure):
                 ("blocks", ctypes.c_int32), ("us", ctypes.c_float)]
 
 
+class PhaseTime(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int32), ("select_us", ctypes.c_float), ("update_us", ctypes.c_float)]
+
+
 KERNEL_NAMES = {0: "gemm_bf16", 1: "gemm_f32", 2: "expand_sparse", 3: "expand_dense", 4: "merge",
                 5: "step_query", 6: "live_rows", 7: "radix_score_sparse", 8: "radix_score_dense",
-                9: "radix_keys", 10: "radix_refine", 11: "radix_collect", 12: "radix_sort"}
+                9: "radix_keys", 10: "radix_refine", 11: "radix_collect", 12: "radix_sort",
+                13: "decode_tail"}
 
 SIGNATURES = {
     "cb_build_index": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _I32, _PP]),
@@ -51,12 +56,15 @@ SIGNATURES = {
     "cb_get_path": (ctypes.c_int, [_P, _I32, _P]),
     "cb_set_select": (ctypes.c_int, [_P, _I32, ctypes.c_int]),
     "cb_get_select": (ctypes.c_int, [_P, _I32, _P]),
+    "cb_set_decode_fusion": (ctypes.c_int, [_P, _I32]),
+    "cb_get_decode_fusion": (ctypes.c_int, [_P, _P]),
     "cb_step": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "cb_decode": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "cb_tune": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P]),
     "cb_tune_times": (ctypes.c_int, [_P, _I32, _P, _P]),
     "cb_profile_start": (ctypes.c_int, [_P, _I32]),
     "cb_profile_stop": (ctypes.c_int, [_P, _P, _I32, _P]),
+    "cb_profile_phases": (ctypes.c_int, [_P, _P, _I32, _P]),
     "cb_plan_destroy": (None, [_P]),
     "cb_last_error": (ctypes.c_char_p, []),
 }

@@ -131,6 +131,15 @@ class Plan:
         C.check("cb_get_select", self._lib.cb_get_select(self._h, int(t), ctypes.byref(v)))
         return _SELECT_NAMES[v.value]
 
+    def set_decode_fusion(self, enable):
+        """Persistent decode of the trailing sparse steps (on by default)."""
+        C.check("cb_set_decode_fusion", self._lib.cb_set_decode_fusion(self._h, 1 if enable else 0))
+
+    def get_decode_fusion(self):
+        v = ctypes.c_int()
+        C.check("cb_get_decode_fusion", self._lib.cb_get_decode_fusion(self._h, ctypes.byref(v)))
+        return bool(v.value)
+
     def _stream(self):
         torch = _torch()
         return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
@@ -216,3 +225,12 @@ class Plan:
         C.check("cb_profile_stop", self._lib.cb_profile_stop(self._h, buf, cap, ctypes.byref(n)))
         return [{"step": r.step, "kernel": C.KERNEL_NAMES[r.kernel], "threads": r.threads, "blocks": r.blocks,
                  "us": r.us} for r in buf[:min(n.value, cap)]]
+
+    def profile_phases(self):
+        """Per-step phase times (mean over queries, device wall clock) of the
+        last persistent decode run while profiling was on, as of the last
+        profile_stop: [{"step", "select_us", "update_us"}]."""
+        buf = (C.PhaseTime * max(self.L, 1))()
+        n = ctypes.c_int32()
+        C.check("cb_profile_phases", self._lib.cb_profile_phases(self._h, buf, self.L, ctypes.byref(n)))
+        return [{"step": r.step, "select_us": r.select_us, "update_us": r.update_us} for r in buf[:n.value]]

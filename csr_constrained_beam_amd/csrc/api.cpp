@@ -283,6 +283,9 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const vo
 void profile_release(cb_plan* p) {
     for (hipEvent_t ev : p->prof_ev)
         if (ev) (void)hipEventDestroy(ev);
+    dev_free(p->phase_clk);
+    p->phase_clk = nullptr;
+    p->phase_t0 = -1;
     p->prof_ev.clear();
     p->prof_rec.clear();
     p->prof_on = false;
@@ -380,6 +383,18 @@ cb_status cb_build_index(const int32_t* sids, int64_t n_items, int32_t L, int32_
             std::vector<uint16_t>().swap(T.tok);
             std::vector<uint32_t>().swap(T.bits);
             std::vector<uint16_t>().swap(T.rank);
+        }
+        std::vector<cb::StepDev> descs;
+        for (const auto& T : idx->steps) descs.push_back(T.dev(idx->words));
+        st = dev_alloc(&idx->d_steps, descs.size(), "step descriptors");
+        if (st == CB_OK) {
+            hipError_t e = hipMemcpy(idx->d_steps, descs.data(), descs.size() * sizeof(cb::StepDev),
+                                     hipMemcpyHostToDevice);
+            if (e != hipSuccess) st = hip_fail("cb_build_index: upload", e);
+        }
+        if (st != CB_OK) {
+            cb_free_index(idx);
+            return st;
         }
     }
     *out = idx;
@@ -482,6 +497,7 @@ void cb_free_index(cb_index* idx) {
             dev_free(T.d_bits);
             dev_free(T.d_rank);
         }
+        dev_free(idx->d_steps);
     }
     delete idx;
 }
@@ -671,8 +687,17 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
         if ((e = hipEventCreate(&ev0)) != hipSuccess || (e = hipEventCreate(&ev1)) != hipSuccess)
             return hip_fail("cb_tune: events", e);
     }
+    // persistent tail: the trailing steps on the fused sparse step with LDS
+    // selection run in one launch (untraced, untuned decodes only)
+    int t_fuse = L;
+    if (p->fuse && reps == 0 && !tr_h && !tr_rows && !tr_acc && idx->d_steps) {
+        while (t_fuse > 0 && resolve_path(p, t_fuse - 1) == CB_PATH_SPARSE &&
+               resolve_select(p, t_fuse - 1) == CB_SELECT_LDS)
+            --t_fuse;
+        if (L - t_fuse < 2) t_fuse = L;
+    }
     cb_status st = CB_OK;
-    for (int t = 0; t < L && st == CB_OK; ++t) {
+    for (int t = 0; t < t_fuse && st == CB_OK; ++t) {
         const void* Wt = static_cast<const unsigned char*>(W) + (size_t)t * V * d * es;
         if (tr_h) {
             e = hipMemcpyAsync(static_cast<unsigned char*>(tr_h) + (size_t)t * R * d * es, p->h, (size_t)R * d * es,
@@ -761,6 +786,25 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
     if (ev0) (void)hipEventDestroy(ev0);
     if (ev1) (void)hipEventDestroy(ev1);
     if (st != CB_OK) return st;
+    if (t_fuse < L) {
+        size_t lds = 0;
+        for (int t = t_fuse; t < L; ++t) {
+            const cb::StepTable& T = idx->steps[(size_t)t];
+            lds = std::max(lds, query_lds_bytes(T.S, K, std::min(K, std::max(T.S, 1)), d));
+        }
+        ProfMark m(p, s, t_fuse, CB_KERNEL_DECODE_TAIL, query_threads(K), Q);
+        uint64_t* clk = p->prof_on ? p->phase_clk : nullptr;
+        e = launch_decode_tail(idx->d_steps, lds, t_fuse, L, Q, K, d, V, p->dtype, W, P, p->s[cur], p->s[1 - cur],
+                               p->h, p->rows[cur], p->rows[1 - cur], p->acc[cur], p->acc[1 - cur], p->hist_tok,
+                               p->hist_par, clk, s);
+        m.done();
+        if (clk) {
+            p->phase_t0 = t_fuse;
+            p->phase_Q = Q;
+        }
+        if (e != hipSuccess) return hip_fail("cb_decode: persistent steps", e);
+        if ((L - t_fuse) & 1) cur = 1 - cur;
+    }
     if (out_seqs) {
         e = launch_backtrace(R, K, L, p->hist_tok, p->hist_par, out_seqs, s);
         if (e != hipSuccess) return hip_fail("cb_decode: backtrace", e);
@@ -769,6 +813,26 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
         return hip_fail("cb_decode: output copy", e);
     if (out_logp && (e = hipMemcpyAsync(out_logp, p->acc[cur], (size_t)R * 4, hipMemcpyDeviceToDevice, s)) != hipSuccess)
         return hip_fail("cb_decode: output copy", e);
+    return CB_OK;
+}
+
+cb_status cb_set_decode_fusion(cb_plan* p, int32_t enable) {
+    clear_error();
+    if (!p) {
+        set_error("cb_set_decode_fusion: plan is NULL");
+        return CB_EINVAL;
+    }
+    p->fuse = enable != 0;
+    return CB_OK;
+}
+
+cb_status cb_get_decode_fusion(const cb_plan* p, int32_t* enabled) {
+    clear_error();
+    if (!p || !enabled) {
+        set_error("cb_get_decode_fusion: plan or output is NULL");
+        return CB_EINVAL;
+    }
+    *enabled = p->fuse ? 1 : 0;
     return CB_OK;
 }
 
@@ -843,6 +907,13 @@ cb_status cb_profile_start(cb_plan* p, int32_t capacity) {
     }
     p->prof_rec.reserve((size_t)capacity);
     p->prof_cap = capacity;
+    cb_status st = dev_alloc(&p->phase_clk, (size_t)p->Q_max * p->idx->L * 2, "phase clock");
+    if (st != CB_OK) {
+        profile_release(p);
+        return st;
+    }
+    p->phase_t0 = -1;
+    p->phases.clear();
     p->prof_on = true;
     return CB_OK;
 }
@@ -868,8 +939,43 @@ cb_status cb_profile_stop(cb_plan* p, cb_kernel_time* out, int32_t cap, int32_t*
     *n = (int32_t)p->prof_rec.size();
     if (out)
         for (int32_t i = 0; i < *n && i < cap; ++i) out[i] = p->prof_rec[(size_t)i];
+    p->phases.clear();
+    if (st == CB_OK && p->phase_t0 >= 0 && p->phase_clk) {
+        const int L = p->idx->L, t0 = p->phase_t0, Q = p->phase_Q;
+        std::vector<uint64_t> clk((size_t)Q * L * 2);
+        int rate_khz = 0;
+        hipError_t e = hipDeviceSynchronize();  // the decode may sit on any stream
+        if (e == hipSuccess) e = hipMemcpy(clk.data(), p->phase_clk, clk.size() * 8, hipMemcpyDeviceToHost);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, p->idx->device);
+        if (e != hipSuccess || rate_khz <= 0) {
+            st = hip_fail("cb_profile_stop: phase clock", e == hipSuccess ? hipErrorUnknown : e);
+        } else {
+            const double us_per_tick = 1000.0 / rate_khz;
+            for (int t = t0; t < L; ++t) {
+                double sel = 0.0, upd = 0.0;
+                for (int q = 0; q < Q; ++q) {
+                    const uint64_t* c = clk.data() + ((size_t)q * L + t) * 2;
+                    sel += (double)(int64_t)(c[1] - c[0]);
+                    if (t + 1 < L) upd += (double)(int64_t)(c[2] - c[1]);
+                }
+                p->phases.push_back(cb_phase_time{t, (float)(sel / Q * us_per_tick), (float)(upd / Q * us_per_tick)});
+            }
+        }
+    }
     profile_release(p);
     return st;
+}
+
+cb_status cb_profile_phases(const cb_plan* p, cb_phase_time* out, int32_t cap, int32_t* n) {
+    clear_error();
+    if (!p || !n) {
+        set_error("cb_profile_phases: bad plan or output");
+        return CB_EINVAL;
+    }
+    *n = (int32_t)p->phases.size();
+    if (out)
+        for (int32_t i = 0; i < *n && i < cap; ++i) out[i] = p->phases[(size_t)i];
+    return CB_OK;
 }
 
 void cb_plan_destroy(cb_plan* p) {

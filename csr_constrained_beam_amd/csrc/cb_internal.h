@@ -56,6 +56,7 @@ struct cb_index {
     int32_t L = 0, V = 0, device = -1, words = 0;
     int64_t n_items = 0;
     std::vector<cb::StepTable> steps;
+    cb::StepDev* d_steps = nullptr;  // device copy of every step's descriptor [L]
 };
 
 // Limits of the kernels in this build.
@@ -114,11 +115,15 @@ struct cb_plan {
     float* scratch_logp = nullptr;        // [R]
     int32_t* scratch_tok = nullptr;       // [R]
     int32_t* scratch_par = nullptr;       // [R]
+    bool fuse = true;                     // persistent decode of the trailing sparse steps
     // kernel timing (cb_profile_start / cb_profile_stop)
     bool prof_on = false;
     int32_t prof_cap = 0;
     std::vector<hipEvent_t> prof_ev;      // 2 per record
     std::vector<cb_kernel_time> prof_rec;
+    uint64_t* phase_clk = nullptr;        // [Q_max][L][2] ticks of the persistent decode (while profiling)
+    int32_t phase_t0 = -1, phase_Q = 0;   // its first step and query count (-1: none recorded)
+    std::vector<cb_phase_time> phases;    // results at the last cb_profile_stop
 };
 
 namespace cb {
@@ -160,6 +165,13 @@ hipError_t launch_hidden_update(int R, int K, int d, cb_dtype dt, const float* s
                                 hipStream_t st);
 hipError_t launch_backtrace(int R, int K, int L, const int32_t* hist_tok, const int32_t* hist_par,
                             int32_t* seqs, hipStream_t s);
+// Steps t0..L-1 of a decode (sparse, LDS selection) with the hidden updates
+// in between, one persistent workgroup per query.  d_steps: device array [L];
+// clk: NULL, or [Q][L][2] device wall-clock ticks (step start, outputs written).
+hipError_t launch_decode_tail(const StepDev* d_steps, size_t lds, int t0, int L, int Q, int K, int d, int V,
+                              cb_dtype dt, const void* W, const float* P, float* s0, float* s1, void* h,
+                              int32_t* rows0, int32_t* rows1, float* acc0, float* acc1, int32_t* hist_tok,
+                              int32_t* hist_par, uint64_t* clk, hipStream_t s);
 
 // Radix-select path (any beam width up to kMaxKRadix): slot offsets and
 // scores of every candidate (sparse dot or full-codebook gather), keys and the

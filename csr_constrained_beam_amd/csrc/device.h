@@ -328,6 +328,44 @@ __device__ void block_select_top(int n, int Kc, KeyF key, uint64_t* out, uint64_
     if (tid < Kc) out[tid] = best;
 }
 
+// Append the keys of the lanes where p holds to the LDS list keys[*count ..]
+// (wave-aggregated: one LDS atomic per wave).  Their order in the list is
+// immaterial (keys are unique).
+__device__ __forceinline__ void wave_append(bool p, uint64_t v, uint64_t* keys, int* count) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t mask = __ballot(p);
+    if (mask == 0ull) return;
+    int base = 0;
+    if (lane == 0) base = atomicAdd(count, __popcll(mask));
+    base = __shfl(base, 0);
+    if (p) keys[base + __popcll(mask & ((1ull << lane) - 1ull))] = v;
+}
+
+// The Kc (<= 64) largest of the m keys in the LDS list keys[0..m), descending,
+// written by wave 0 to out[0..Kc) (0-padded); out is complete after the next
+// barrier.  Up to 64 keys: one wave sorts them.  Up to NT: only the
+// ceil(m / 64) waves that hold keys sort and merge them as a tree.  More: the
+// threshold selection.  stage: LDS [NT]; list: LDS int [m].  All threads call.
+template <int NT>
+__device__ void block_select_list(int m, int Kc, const uint64_t* keys, uint64_t* out, uint64_t* stage, int* list,
+                                  int* red_i, uint64_t* bcast) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    if (m > NT) {
+        block_select_top<NT>(m, Kc, [&](int j) { return keys[j]; }, out, stage, list, red_i, bcast);
+        return;
+    }
+    const int nw = (m + kWave - 1) / kWave;
+    uint64_t v = 0ull;
+    if (w < nw) v = wave_sort_desc(tid < m ? keys[tid] : 0ull);
+    for (int s = 1; s < nw; s <<= 1) {  // uniform: m is the same for every thread
+        if (w < nw && (w & (2 * s - 1)) == s) stage[(w >> 1) * kWave + lane] = v;
+        __syncthreads();
+        if (w + s < nw && (w & (2 * s - 1)) == 0) v = wave_merge_top(v, stage[((w + s) >> 1) * kWave + lane]);
+        __syncthreads();
+    }
+    if (w == 0 && lane < Kc) out[lane] = v;
+}
+
 // 8 consecutive elements (16-byte aligned) as float.
 __device__ __forceinline__ void load8(const uint16_t* p, float* o) {
     uint4 v = *reinterpret_cast<const uint4*>(p);

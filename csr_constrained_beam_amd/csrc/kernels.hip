@@ -80,6 +80,62 @@ __device__ void emit(const StepDev& st, int q, int K, int i, uint64_t key, const
     out_logp[o] = score_from_order_bits((uint32_t)(key >> 32));
 }
 
+// Output slot i of query q from its key, in the fused sparse step: the
+// parent's row start, width and (narrow CSR rows) sorted tokens were kept in
+// LDS when the row was read, so the next row needs no global reads there.
+// n_s[p] >= 0: narrow row of n_s[p] tokens in tokq[p * 64 ...]; otherwise a
+// wide row of -1 - n_s[p] tokens, searched in the step table.  nrows / nacc
+// (may be NULL): LDS copies of the next rows and log-probs, per slot.
+__device__ void emit_query(const StepDev& st, int q, int K, int i, uint64_t key, const int32_t* r_s,
+                           const uint32_t* e0_s, const int* n_s, const uint16_t* tokq, int32_t* out_tok,
+                           int32_t* out_par, int32_t* out_rows, float* out_logp, int32_t* nrows, float* nacc) {
+    const int64_t o = (int64_t)q * K + i;
+    if (key == 0ull) {
+        out_tok[o] = -1;
+        out_par[o] = -1;
+        out_rows[o] = -1;
+        out_logp[o] = -INFINITY;
+        if (nrows) {
+            nrows[i] = -1;
+            nacc[i] = -INFINITY;
+        }
+        return;
+    }
+    const int parent = 1023 - (int)((key >> 16) & 1023u);
+    const int token = 65535 - (int)(key & 0xFFFFu);
+    const uint32_t e0 = e0_s[parent];
+    const int nn = n_s[parent];
+    int32_t row;
+    if (nn >= 0) {
+        const uint16_t* tq = tokq + parent * kWave;
+        int lo = 0, hi = nn;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((int)tq[mid] < token) lo = mid + 1; else hi = mid;
+        }
+        row = (int32_t)(e0 + lo);
+    } else if (st.store == CB_STORE_CSR) {
+        uint32_t lo = 0, hi = (uint32_t)(-1 - nn);
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if ((int)st.tok[e0 + mid] < token) lo = mid + 1; else hi = mid;
+        }
+        row = (int32_t)(e0 + lo);
+    } else {
+        const int64_t x = (int64_t)r_s[parent] * st.words + (token >> 5);
+        row = (int32_t)(e0 + st.rank[x] + __popc(st.bits[x] & ((1u << (token & 31)) - 1u)));
+    }
+    const float lp = score_from_order_bits((uint32_t)(key >> 32));
+    out_tok[o] = token;
+    out_par[o] = parent;
+    out_rows[o] = row;
+    out_logp[o] = lp;
+    if (nrows) {
+        nrows[i] = row;
+        nacc[i] = lp;
+    }
+}
+
 // ---- LDS layouts (shared by launchers and kernels) --------------------------
 
 struct ExpandLds {
@@ -97,7 +153,7 @@ __host__ __device__ inline ExpandLds expand_lds(int S, int d, bool dense, int NT
 }
 
 struct QueryLds {
-    int qkeys, stage, list, z, h, tok, total;
+    int qkeys, stage, list, z, h, tok, tokq, total;
 };
 __host__ __device__ inline QueryLds query_lds(int S, int K, int Kc, int d, int NT) {
     QueryLds l;
@@ -108,28 +164,39 @@ __host__ __device__ inline QueryLds query_lds(int S, int K, int Kc, int d, int N
     l.z = l.list + (((S > M ? S : M) * 4 + 15) & ~15);
     l.h = l.z + ((S * 4 + 15) & ~15);
     l.tok = l.h + ((d * 4 + 15) & ~15);
-    l.total = l.tok + ((S * 2 + 15) & ~15);
+    l.tokq = l.tok + ((S * 2 + 15) & ~15);
+    l.total = l.tokq + ((K * kWave * 2 + 15) & ~15);
     return l;
 }
 
 // ---- sparse step: one workgroup per query ----------------------------------
 
+// The whole sparse step of query q by one workgroup (body of k_step_query and
+// of each step of k_decode_tail).  rows_q / acc_q: the query's K beam rows
+// and accumulated log-probs (global or LDS).  smem: the query_lds layout of
+// this step; best: LDS [64], left holding the query's K winning keys;
+// nrows / nacc: NULL, or LDS [K] receiving the next rows and log-probs.
 template <typename DT, int NT, int CH>
-__global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, int d,
-                                                   const DT* __restrict__ hidden, const DT* __restrict__ W,
-                                                   const int32_t* __restrict__ beam_rows,
-                                                   const float* __restrict__ acc, const uint64_t* __restrict__ pre,
-                                                   const int32_t* __restrict__ pre_off, int64_t pre_cap,
-                                                   int32_t* __restrict__ out_tok,
-                                                   int32_t* __restrict__ out_par, int32_t* __restrict__ out_rows,
-                                                   float* __restrict__ out_logp) {
-    extern __shared__ __align__(16) unsigned char smem[];
+__device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d, const DT* __restrict__ hidden,
+                                 const DT* __restrict__ W, const int32_t* __restrict__ rows_q,
+                                 const float* __restrict__ acc_q, const uint64_t* __restrict__ pre,
+                                 const int32_t* __restrict__ pre_off, int64_t pre_cap, int32_t* __restrict__ out_tok,
+                                 int32_t* __restrict__ out_par, int32_t* __restrict__ out_rows,
+                                 float* __restrict__ out_logp, unsigned char* smem, uint64_t* best,
+                                 int32_t* nrows, float* nacc) {
     __shared__ float red_f[NT / kWave];
     __shared__ int red_i[NT / kWave];
     __shared__ uint64_t bcast;
-    __shared__ uint64_t best[kWave];
+    // per beam, from its row: row, accumulated log-prob, row start, width
+    // (negative: -1 - width of a row too wide for phase 1)
+    __shared__ int32_t r_s[kWave];
+    __shared__ float a_s[kWave];
+    __shared__ uint32_t e0_s[kWave];
+    __shared__ int n_s[kWave];
     __shared__ int nbig;
     __shared__ int big[kWave];
+    __shared__ int ncand;             // keys in the candidate list qkeys
+    __shared__ uint64_t slot[kWave];  // survivors of one wide row
     const QueryLds lay = query_lds(st.S, K, Kc, d, NT);
     uint64_t* qkeys = reinterpret_cast<uint64_t*>(smem + lay.qkeys);
     uint64_t* stage = reinterpret_cast<uint64_t*>(smem + lay.stage);
@@ -137,11 +204,14 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
     float* z_s = reinterpret_cast<float*>(smem + lay.z);
     float* h_s = reinterpret_cast<float*>(smem + lay.h);
     uint16_t* tok_s = reinterpret_cast<uint16_t*>(smem + lay.tok);
+    uint16_t* tokq = reinterpret_cast<uint16_t*>(smem + lay.tokq);
 
-    const int q = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
     constexpr int NW = NT / kWave;
-    if (tid == 0) nbig = 0;
+    if (tid == 0) {
+        nbig = 0;
+        ncand = 0;
+    }
     __syncthreads();
 
     // phase 1: one wave per beam with a narrow CSR row; each wave takes two
@@ -157,8 +227,8 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
         for (int u = 0; u < 2; ++u) {
             kk[u] = k0 + u * NW;
             b[u] = (int64_t)q * K + kk[u];
-            r[u] = kk[u] < K ? beam_rows[b[u]] : -1;
-            a[u] = kk[u] < K ? acc[b[u]] : -INFINITY;
+            r[u] = kk[u] < K ? rows_q[kk[u]] : -1;
+            a[u] = kk[u] < K ? acc_q[kk[u]] : -INFINITY;
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -167,13 +237,18 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
             n[u] = live ? (int)(st.row_ptr[r[u] + 1] - e0[u]) : 0;
             small[u] = live && n[u] <= kSmallRow && st.store == CB_STORE_CSR;
             if (kk[u] < K) {
-                if (!live) {
-                    if (lane < Kc) qkeys[kk[u] * Kc + lane] = 0ull;
-                } else if (!small[u]) {
-                    if (lane == 0) big[atomicAdd(&nbig, 1)] = kk[u];
+                if (live) {
+                    if (lane == 0) {
+                        r_s[kk[u]] = r[u];
+                        a_s[kk[u]] = a[u];
+                        e0_s[kk[u]] = e0[u];
+                        n_s[kk[u]] = small[u] ? n[u] : -1 - n[u];
+                    }
+                    if (!small[u] && lane == 0) big[atomicAdd(&nbig, 1)] = kk[u];
                 }
             }
             tk[u] = small[u] && lane < n[u] ? (int)st.tok[e0[u] + lane] : 0;
+            if (small[u] && lane < n[u]) tokq[kk[u] * kWave + lane] = (uint16_t)tk[u];
         }
         if (!small[0] && !small[1]) continue;
         // rows whose scores were computed apart are read, the others scored here
@@ -240,7 +315,8 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
             const float lse = m + logf(se);
             uint64_t key = on ? make_key(a[u] + (z[u] - lse), kk[u], tk[u]) : 0ull;
             if (n[u] > Kc) key = wave_sort_desc(key);
-            if (lane < Kc) qkeys[kk[u] * Kc + lane] = key;
+            // the beam's best min(n, Kc) join the query's candidate list
+            wave_append(lane < min(n[u], Kc), key, qkeys, &ncand);
         }
     }
     __syncthreads();
@@ -250,10 +326,10 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
     for (int i = 0; i < nb; ++i) {
         const int k = big[i];
         const int64_t b = (int64_t)q * K + k;
-        const int32_t r = beam_rows[b];
-        const float a = acc[b];
-        const uint32_t e0 = st.row_ptr[r];
-        const int n = (int)(st.row_ptr[r + 1] - e0);
+        const int32_t r = r_s[k];
+        const float a = a_s[k];
+        const uint32_t e0 = e0_s[k];
+        const int n = -1 - n_s[k];
         block_fill_tokens<NT>(st, r, e0, n, tok_s, red_i);
         if (pre) {  // scored apart, across many workgroups
             const uint64_t* zp = pre + (int64_t)q * pre_cap + pre_off[(int64_t)q * (K + 1) + k];
@@ -267,19 +343,41 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
         }
         const float lse = block_lse<NT>(z_s, n, red_f);
         auto keyf = [&](int j) { return make_key(a + (z_s[j] - lse), k, (int)tok_s[j]); };
-        uint64_t* slot = qkeys + k * Kc;
         if (n <= Kc) {
             for (int j = tid; j < Kc; j += NT) slot[j] = j < n ? keyf(j) : 0ull;
         } else {
             block_select_top<NT>(n, Kc, keyf, slot, stage, list, red_i, &bcast);
         }
         __syncthreads();
+        if (wv == 0) {
+            const uint64_t v = lane < Kc ? slot[lane] : 0ull;
+            wave_append(v != 0ull, v, qkeys, &ncand);
+        }
+        __syncthreads();
     }
 
-    // phase 3: the query's K best
-    block_select_top<NT>(K * Kc, K, [&](int j) { return qkeys[j]; }, best, stage, list, red_i, &bcast);
+    // phase 3: the query's K best of its candidate list
+    block_select_list<NT>(ncand, K, qkeys, best, stage, list, red_i, &bcast);
     __syncthreads();
-    for (int i = tid; i < K; i += NT) emit(st, q, K, i, best[i], beam_rows, out_tok, out_par, out_rows, out_logp);
+    for (int i = tid; i < K; i += NT)
+        emit_query(st, q, K, i, best[i], r_s, e0_s, n_s, tokq, out_tok, out_par, out_rows, out_logp, nrows, nacc);
+}
+
+template <typename DT, int NT, int CH>
+__global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, int d,
+                                                   const DT* __restrict__ hidden, const DT* __restrict__ W,
+                                                   const int32_t* __restrict__ beam_rows,
+                                                   const float* __restrict__ acc, const uint64_t* __restrict__ pre,
+                                                   const int32_t* __restrict__ pre_off, int64_t pre_cap,
+                                                   int32_t* __restrict__ out_tok,
+                                                   int32_t* __restrict__ out_par, int32_t* __restrict__ out_rows,
+                                                   float* __restrict__ out_logp) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ uint64_t best[kWave];
+    const int q = blockIdx.x;
+    step_query_block<DT, NT, CH>(st, q, K, Kc, d, hidden, W, beam_rows + (int64_t)q * K, acc + (int64_t)q * K, pre,
+                                 pre_off, pre_cap, out_tok, out_par, out_rows, out_logp, smem, best, nullptr,
+                                 nullptr);
 }
 
 // ---- dense step: per-beam expansion and per-query merge --------------------
@@ -690,26 +788,176 @@ __global__ __launch_bounds__(NT) void k_decode_init(int K, int d, const float* _
     normalise_into<DT, NT>(sb, d, hb, red);
 }
 
-template <typename DT, int NT>
-__global__ __launch_bounds__(NT) void k_hidden_update(int K, int d, const float* __restrict__ s_old,
-                                                      const float* __restrict__ P_t, const int32_t* __restrict__ tok,
-                                                      const int32_t* __restrict__ par, float* __restrict__ s_new,
-                                                      DT* __restrict__ h_out) {
-    __shared__ double red[NT / kWave];
-    const int b = blockIdx.x;
-    const int tk = tok[b];
-    DT* hb = h_out + (int64_t)b * d;
-    if (tk < 0) {
-        for (int i = threadIdx.x; i < d; i += NT) store_h(hb + i, 0.f);
-        return;
+__device__ __forceinline__ void store_h4(uint16_t* p, float a, float b, float c, float e) {
+    uint2 v;
+    v.x = (uint32_t)f32_to_bf16_rne(a) | (uint32_t)f32_to_bf16_rne(b) << 16;
+    v.y = (uint32_t)f32_to_bf16_rne(c) | (uint32_t)f32_to_bf16_rne(e) << 16;
+    *reinterpret_cast<uint2*>(p) = v;
+}
+__device__ __forceinline__ void store_h4(float* p, float a, float b, float c, float e) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, e);
+}
+
+// Stand-in model update by one wavefront, of NB slots at once (their loads
+// in flight together): s_new = s_old[parent slot] + P_t[token] in float32,
+// h = s_new / ||s_new||_2 with the squares summed in double (fused
+// multiply-adds in element order per lane, then a butterfly), rounded to
+// float32 (then bf16).  Dead slots (token < 0) get h = 0; slots b < 0 are
+// skipped.  REG: d a multiple of 256 and at most 256 * NV, P_t 16-byte
+// aligned; every lane keeps 4 consecutive elements per 256 in registers.
+// Otherwise lane-strided single elements, re-read from s_new.  Both launch
+// forms make the same choice for a given (d, P), so they agree bit for bit.
+template <typename DT, bool REG, int NV, int NB>
+__device__ void hidden_update_wave(const int (&b)[NB], const int (&tk)[NB], const int (&par)[NB], int K, int d,
+                                   const float* __restrict__ s_old, const float* __restrict__ P_t,
+                                   float* __restrict__ s_new, DT* __restrict__ h_out) {
+    const int lane = lane_id();
+    if constexpr (REG) {
+        float4 v[NB][NV];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            if (b[u] < 0 || tk[u] < 0) continue;  // uniform over the wavefront
+            const float* sp = s_old + (int64_t)((b[u] / K) * K + par[u]) * d;
+            const float* pv = P_t + (int64_t)tk[u] * d;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                if (j * kWave * 4 >= d) break;
+                const int i = lane * 4 + j * kWave * 4;
+                const float4 x = *reinterpret_cast<const float4*>(sp + i);
+                const float4 y = *reinterpret_cast<const float4*>(pv + i);
+                v[u][j] = make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            if (b[u] < 0) continue;
+            DT* hb = h_out + (int64_t)b[u] * d;
+            if (tk[u] < 0) {
+                for (int i = lane; i < d; i += kWave) store_h(hb + i, 0.f);
+                continue;
+            }
+            float* sn = s_new + (int64_t)b[u] * d;
+            double ss = 0.0;
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                if (j * kWave * 4 >= d) break;
+                const float4 x = v[u][j];
+                *reinterpret_cast<float4*>(sn + lane * 4 + j * kWave * 4) = x;
+                ss = fma((double)x.x, (double)x.x, ss);
+                ss = fma((double)x.y, (double)x.y, ss);
+                ss = fma((double)x.z, (double)x.z, ss);
+                ss = fma((double)x.w, (double)x.w, ss);
+            }
+            const double nrm = sqrt(wave_sum(ss));
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                if (j * kWave * 4 >= d) break;
+                const float4 x = v[u][j];
+                store_h4(hb + lane * 4 + j * kWave * 4, (float)((double)x.x / nrm), (float)((double)x.y / nrm),
+                         (float)((double)x.z / nrm), (float)((double)x.w / nrm));
+            }
+        }
+    } else {
+        for (int u = 0; u < NB; ++u) {
+            if (b[u] < 0) continue;
+            DT* hb = h_out + (int64_t)b[u] * d;
+            if (tk[u] < 0) {
+                for (int i = lane; i < d; i += kWave) store_h(hb + i, 0.f);
+                continue;
+            }
+            const float* sp = s_old + (int64_t)((b[u] / K) * K + par[u]) * d;
+            const float* pv = P_t + (int64_t)tk[u] * d;
+            float* sn = s_new + (int64_t)b[u] * d;
+            double ss = 0.0;
+            for (int i = lane; i < d; i += kWave) {
+                const float x = sp[i] + pv[i];
+                sn[i] = x;
+                ss = fma((double)x, (double)x, ss);
+            }
+            const double nrm = sqrt(wave_sum(ss));
+            for (int i = lane; i < d; i += kWave) store_h(hb + i, (float)((double)sn[i] / nrm));
+        }
     }
-    const int p = (b / K) * K + par[b];
-    const float* sp = s_old + (int64_t)p * d;
-    const float* pv = P_t + (int64_t)tk * d;
-    float* sn = s_new + (int64_t)b * d;
-    for (int i = threadIdx.x; i < d; i += NT) sn[i] = sp[i] + pv[i];
+}
+
+// Largest d the register-resident update takes.
+constexpr int kRegMaxD = 2048;
+
+template <typename DT, bool REG>
+__global__ __launch_bounds__(256) void k_hidden_update(int R, int K, int d, const float* __restrict__ s_old,
+                                                       const float* __restrict__ P_t, const int32_t* __restrict__ tok,
+                                                       const int32_t* __restrict__ par, float* __restrict__ s_new,
+                                                       DT* __restrict__ h_out) {
+    const int b0 = blockIdx.x * 4 + (int)(threadIdx.x / kWave);
+    if (b0 >= R) return;  // uniform over the wavefront
+    const int b[1] = {b0}, t[1] = {tok[b0]}, p[1] = {par[b0]};
+    hidden_update_wave<DT, REG, kRegMaxD / (kWave * 4), 1>(b, t, p, K, d, s_old, P_t, s_new, h_out);
+}
+
+// Persistent decode of the steps t0..L-1 (all sparse, LDS selection) with the
+// stand-in model between them: one workgroup per query runs every step and
+// every hidden update of its beams, so the steps need no launches in between
+// (queries share nothing, so no workgroup waits for another).  Buffers [0]
+// hold step t0's inputs; outputs of step t go to hist_tok/hist_par [t] and to
+// the other buffer of the pair, which becomes the next step's input.
+template <typename DT, int NT, int CH, bool REG>
+__global__ __launch_bounds__(NT) void k_decode_tail(const StepDev* __restrict__ steps, int t0, int L, int K, int d,
+                                                    int V, int R, const DT* __restrict__ W,
+                                                    const float* __restrict__ P, float* s0, float* s1, DT* h,
+                                                    int32_t* rows0, int32_t* rows1, float* acc0, float* acc1,
+                                                    int32_t* __restrict__ hist_tok, int32_t* __restrict__ hist_par,
+                                                    uint64_t* __restrict__ clk) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ uint64_t best[kWave];
+    __shared__ int32_t rows_l[2][kWave];  // the query's beam rows, current and next step
+    __shared__ float acc_l[2][kWave];
+    const int q = blockIdx.x;
+    const int wv = threadIdx.x / kWave;
+    constexpr int NW = NT / kWave;
+    // values per lane per slot in the register-resident update: d <= 512 * CH
+    constexpr int NV = 2 * CH;
+    constexpr int NB = NV <= 4 ? 2 : 1;
+    float* sb[2] = {s0, s1};
+    int32_t* rb[2] = {rows0, rows1};
+    float* ab[2] = {acc0, acc1};
+    for (int k = threadIdx.x; k < K; k += NT) {
+        rows_l[0][k] = rows0[(int64_t)q * K + k];
+        acc_l[0][k] = acc0[(int64_t)q * K + k];
+    }
     __syncthreads();
-    normalise_into<DT, NT>(sn, d, hb, red);
+    int cur = 0;
+    for (int t = t0; t < L; ++t) {
+        // phase clock (when asked): device wall clock at the step's start and
+        // once its outputs are written
+        if (clk && threadIdx.x == 0) clk[((int64_t)q * L + t) * 2] = wall_clock64();
+        const StepDev st = steps[t];
+        const int Kc = min(K, max(st.S, 1));
+        int32_t* ot = hist_tok + (int64_t)t * R;
+        int32_t* op = hist_par + (int64_t)t * R;
+        step_query_block<DT, NT, CH>(st, q, K, Kc, d, h, W + (int64_t)t * V * d, rows_l[cur], acc_l[cur], nullptr,
+                                     nullptr, 0, ot, op, rb[cur ^ 1], ab[cur ^ 1], smem, best, rows_l[cur ^ 1],
+                                     acc_l[cur ^ 1]);
+        __syncthreads();
+        if (clk && threadIdx.x == 0) clk[((int64_t)q * L + t) * 2 + 1] = wall_clock64();
+        if (t + 1 < L) {
+            // winners from LDS: the same (token, parent) the step wrote out
+            const float* Pt = P + (int64_t)t * V * d;
+            for (int k0 = wv; k0 < K; k0 += NW * NB) {
+                int bb[NB], tt[NB], pp[NB];
+#pragma unroll
+                for (int u = 0; u < NB; ++u) {
+                    const int k = k0 + u * NW;
+                    const uint64_t key = k < K ? best[k] : 0ull;
+                    bb[u] = k < K ? q * K + k : -1;
+                    tt[u] = key ? 65535 - (int)(key & 0xFFFFu) : -1;
+                    pp[u] = key ? 1023 - (int)((key >> 16) & 1023u) : -1;
+                }
+                hidden_update_wave<DT, REG, NV, NB>(bb, tt, pp, K, d, sb[cur], Pt, sb[cur ^ 1], h);
+            }
+            __syncthreads();
+        }
+        cur ^= 1;
+    }
 }
 
 __global__ void k_backtrace(int R, int K, int L, const int32_t* __restrict__ hist_tok,
@@ -865,16 +1113,57 @@ hipError_t launch_decode_init(int Q, int K, int d, cb_dtype dt, const float* q, 
     return hipGetLastError();
 }
 
+// Whether the register-resident hidden update applies: d a multiple of 256,
+// at most kRegMaxD, and P (hence every row of every P_t) 16-byte aligned.
+static bool hidden_vec_ok(int d, const float* P) {
+    return d % (kWave * 4) == 0 && d <= kRegMaxD && (reinterpret_cast<uintptr_t>(P) & 15) == 0;
+}
+
 hipError_t launch_hidden_update(int R, int K, int d, cb_dtype dt, const float* s_old, const float* P_t,
                                 const int32_t* tok, const int32_t* par, float* s_new, void* h_out,
                                 hipStream_t st) {
     if (R <= 0) return hipSuccess;
-    if (dt == CB_BF16)
-        hipLaunchKernelGGL((k_hidden_update<uint16_t, 256>), dim3(R), dim3(256), 0, st, K, d, s_old, P_t, tok, par,
-                           s_new, (uint16_t*)h_out);
-    else
-        hipLaunchKernelGGL((k_hidden_update<float, 256>), dim3(R), dim3(256), 0, st, K, d, s_old, P_t, tok, par,
-                           s_new, (float*)h_out);
+    const dim3 grid((R + 3) / 4);
+    const bool vec = hidden_vec_ok(d, P_t);
+#define CB_HU(DT, V) \
+    hipLaunchKernelGGL((k_hidden_update<DT, V>), grid, dim3(256), 0, st, R, K, d, s_old, P_t, tok, par, s_new, (DT*)h_out)
+    if (dt == CB_BF16) {
+        if (vec) CB_HU(uint16_t, true); else CB_HU(uint16_t, false);
+    } else {
+        if (vec) CB_HU(float, true); else CB_HU(float, false);
+    }
+#undef CB_HU
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_tail(const StepDev* d_steps, size_t lds, int t0, int L, int Q, int K, int d, int V,
+                              cb_dtype dt, const void* W, const float* P, float* s0, float* s1, void* h,
+                              int32_t* rows0, int32_t* rows1, float* acc0, float* acc1, int32_t* hist_tok,
+                              int32_t* hist_par, uint64_t* clk, hipStream_t s) {
+    if (Q <= 0 || t0 >= L) return hipSuccess;
+    const int NT = query_threads(K);
+    const int CH = (d + kWave * 8 - 1) / (kWave * 8);
+    const int R = Q * K;
+    const bool vec = hidden_vec_ok(d, P);
+#define CB_TAIL(DT, NTV, CHV, VV)                                                                                  \
+    hipLaunchKernelGGL((k_decode_tail<DT, NTV, CHV, VV>), dim3(Q), dim3(NTV), lds, s, d_steps, t0, L, K, d, V, R, \
+                       (const DT*)W, P, s0, s1, (DT*)h, rows0, rows1, acc0, acc1, hist_tok, hist_par, clk)
+#define CB_TAIL_V(DT, NTV, CHV) \
+    do { if (vec) CB_TAIL(DT, NTV, CHV, true); else CB_TAIL(DT, NTV, CHV, false); } while (0)
+#define CB_TAIL_NT(DT, CHV) \
+    do { if (NT == 1024) CB_TAIL_V(DT, 1024, CHV); else CB_TAIL_V(DT, 512, CHV); } while (0)
+    if (dt == CB_BF16) {
+        if (CH <= 1) CB_TAIL_NT(uint16_t, 1);
+        else if (CH == 2) CB_TAIL_NT(uint16_t, 2);
+        else CB_TAIL_NT(uint16_t, 4);
+    } else {
+        if (CH <= 1) CB_TAIL_NT(float, 1);
+        else if (CH == 2) CB_TAIL_NT(float, 2);
+        else CB_TAIL_NT(float, 4);
+    }
+#undef CB_TAIL_NT
+#undef CB_TAIL_V
+#undef CB_TAIL
     return hipGetLastError();
 }
 

@@ -197,6 +197,19 @@ cb_status cb_decode(cb_plan* plan, int32_t Q, const float* q, const float* P, co
                     int32_t* out_seqs, float* out_logp, int32_t* out_rows,
                     void* trace_hidden, int32_t* trace_rows, float* trace_acc, void* stream);
 
+/* Persistent decode (FlashTrie, arXiv HTML, sections 2.2 and 4.2: every step
+ * of a query in one launch, paying the launch cost once).  When enabled (the
+ * default) and cb_decode is called without trace buffers, the trailing run
+ * of steps whose path resolves to CB_PATH_SPARSE with CB_SELECT_LDS (at least
+ * two steps) runs as one launch: one workgroup per query performs each of
+ * those steps and the hidden updates between them, so no workgroup waits for
+ * another.  Results equal the step-by-step decode bit for bit.  Disabling
+ * restores one launch per step.  Synchronous with respect to the host. */
+cb_status cb_set_decode_fusion(cb_plan* plan, int32_t enable);
+
+/* Whether the persistent decode is enabled (1) or not (0). */
+cb_status cb_get_decode_fusion(const cb_plan* plan, int32_t* enabled);
+
 /* Pre-measured path switch (ZeroGR: warm-up requests try every option per
  * step and keep the fastest).  Runs one warm-up decode on the given inputs;
  * at every step whose path is AUTO it times the dense and the sparse path
@@ -227,7 +240,8 @@ typedef enum {
     CB_KERNEL_RADIX_KEYS = 9,     /* radix selection: softmax, keys, first digit */
     CB_KERNEL_RADIX_REFINE = 10,  /* radix selection: second digit */
     CB_KERNEL_RADIX_COLLECT = 11, /* radix selection: survivors */
-    CB_KERNEL_RADIX_SORT = 12     /* radix selection: survivors sorted, outputs and next rows */
+    CB_KERNEL_RADIX_SORT = 12,    /* radix selection: survivors sorted, outputs and next rows */
+    CB_KERNEL_DECODE_TAIL = 13    /* persistent decode of the trailing sparse steps (step = first one) */
 } cb_kernel;
 
 typedef struct {
@@ -246,6 +260,23 @@ cb_status cb_profile_start(cb_plan* plan, int32_t capacity);
  * records to `out` (may be NULL); *n receives the number recorded.  Releases
  * the events. */
 cb_status cb_profile_stop(cb_plan* plan, cb_kernel_time* out, int32_t cap, int32_t* n);
+
+/* Phase clock of the persistent decode (FlashTrie, arXiv HTML, section 4.3
+ * and appendix D.4: per-phase device timestamps).  While profiling is on, a
+ * persistent decode also records the device wall clock in every workgroup at
+ * the start of each step and once the step's outputs are written.  After
+ * cb_profile_stop this reports, for each step of the last such decode, the
+ * mean over queries of the selection phase (step start to outputs written:
+ * lookup, scoring, softmax, top-K) and of the hidden update that follows it
+ * (outputs written to the next step's start; 0 for the last step).  *n
+ * receives the number of steps recorded (0 when no persistent decode ran
+ * while profiling was on); up to `cap` are copied to `out`. */
+typedef struct {
+    int32_t step;
+    float select_us;
+    float update_us;
+} cb_phase_time;
+cb_status cb_profile_phases(const cb_plan* plan, cb_phase_time* out, int32_t cap, int32_t* n);
 
 /* Release a plan and its workspace.  NULL is ignored. */
 void cb_plan_destroy(cb_plan* plan);

@@ -95,6 +95,34 @@ def test_fullsize_decode(name):
 
 
 @pytest.mark.parametrize("name", ["production", "hybrid"])
+@pytest.mark.parametrize("paths", ["tuned", "sparse"])
+def test_fullsize_persistent_decode(name, paths):
+    """The untraced decode (trailing sparse steps in one persistent launch)
+    equals the step-by-step decode bit for bit, on the tuned paths and with
+    every step forced sparse."""
+    w = big(name)
+    cfg = w["cfg"]
+    plan = w["plan"] if paths == "tuned" else w["idx"].plan(cfg.Q, cfg.K, cfg.d, cfg.dtype)
+    if paths == "sparse":
+        for t in range(cfg.L):
+            plan.set_path(t, "sparse")
+    plan.set_decode_fusion(False)
+    a = plan.decode(w["q"], w["P"], w["W"])
+    plan.set_decode_fusion(True)
+    plan.profile_start(capacity=1024)
+    b = plan.decode(w["q"], w["P"], w["W"])
+    recs = plan.profile_stop()
+    torch.cuda.synchronize()
+    tail = [r["step"] for r in recs if r["kernel"] == "decode_tail"]
+    print("paths", [plan.get_path(t) + "/" + plan.get_select(t) for t in range(cfg.L)], "tail from", tail,
+          flush=True)
+    if paths == "sparse":
+        assert len(tail) == 1
+    for k in ("seqs", "logp", "rows"):
+        assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("name", ["production", "hybrid"])
 @pytest.mark.parametrize("path", ["tuned", "dense", "sparse", "sparse_split"])
 def test_fullsize_teacher_forced(name, path):
     w = big(name)

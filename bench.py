@@ -157,6 +157,7 @@ def main():
     tail_recs = [r for r in plan.profile_stop() if r["kernel"] == "decode_tail"]
     tail = [r["step"] for r in tail_recs]
     phases = plan.profile_phases()
+    plan.set_decode_fusion("auto")
     log("decode: %.4f ms step by step, %.4f ms with the persistent tail (from step %s)"
         % (decode_ms_steps, decode_ms, tail[0] if tail else "-"))
     for ph in phases:
@@ -356,6 +357,7 @@ def main():
         "expansions_per_pass": expansions,
         "decode_ms_with_model_standin": decode_ms,
         "decode_ms_step_by_step": decode_ms_steps,
+        "decode_persistent_chosen_by_tune": plan.get_decode_fusion() if tune is not None else None,
         "decode_persistent_from_step": tail[0] if tail else None,
         "decode_persistent_us": tail_recs[0]["us"] if tail_recs else None,
         "decode_persistent_phases": phases,

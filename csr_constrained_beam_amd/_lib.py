@@ -58,6 +58,7 @@ SIGNATURES = {
     "cb_get_select": (ctypes.c_int, [_P, _I32, _P]),
     "cb_set_decode_fusion": (ctypes.c_int, [_P, _I32]),
     "cb_get_decode_fusion": (ctypes.c_int, [_P, _P]),
+    "cb_tune_decode_times": (ctypes.c_int, [_P, _P, _P]),
     "cb_step": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "cb_decode": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "cb_tune": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P]),
@@ -65,6 +66,8 @@ SIGNATURES = {
     "cb_profile_start": (ctypes.c_int, [_P, _I32]),
     "cb_profile_stop": (ctypes.c_int, [_P, _P, _I32, _P]),
     "cb_profile_phases": (ctypes.c_int, [_P, _P, _I32, _P]),
+    "cb_index_save": (ctypes.c_int, [_P, ctypes.c_char_p]),
+    "cb_index_load": (ctypes.c_int, [ctypes.c_char_p, _I32, _P]),
     "cb_plan_destroy": (None, [_P]),
     "cb_last_error": (ctypes.c_char_p, []),
 }

@@ -41,6 +41,27 @@ class Index:
                                                             int(device), _STORES[store], ctypes.byref(h)))
         self._h = h
 
+    @classmethod
+    def load(cls, path, device=0):
+        """An index saved by ``save``, uploaded to ``device`` (-1: host only)."""
+        self = cls.__new__(cls)
+        self._lib = C.lib()
+        h = ctypes.c_void_p()
+        C.check("cb_index_load", self._lib.cb_index_load(str(path).encode(), int(device), ctypes.byref(h)))
+        self._h = h
+        return self
+
+    def save(self, path):
+        C.check("cb_index_save", self._lib.cb_index_save(self._h, str(path).encode()))
+
+    def size_report(self):
+        """Bytes per step and in total, with bytes per catalog item."""
+        shape = self.shape
+        steps = [dict(t=t, **self.info(t)) for t in range(shape["L"])]
+        total = sum(s["bytes"] for s in steps)
+        return {"n_items": shape["n_items"], "L": shape["L"], "V": shape["V"], "steps": steps, "bytes": total,
+                "bytes_per_item": total / max(1, shape["n_items"])}
+
     def close(self):
         if getattr(self, "_h", None):
             self._lib.cb_free_index(self._h)
@@ -132,8 +153,16 @@ class Plan:
         return _SELECT_NAMES[v.value]
 
     def set_decode_fusion(self, enable):
-        """Persistent decode of the trailing sparse steps (on by default)."""
-        C.check("cb_set_decode_fusion", self._lib.cb_set_decode_fusion(self._h, 1 if enable else 0))
+        """Persistent decode of the trailing sparse steps: True, False or
+        "auto" (the default: chosen by tune, on until measured)."""
+        v = -1 if enable == "auto" else (1 if enable else 0)
+        C.check("cb_set_decode_fusion", self._lib.cb_set_decode_fusion(self._h, v))
+
+    def tune_decode_times(self):
+        """(step-by-step, persistent) decode microseconds from the last tune."""
+        a, b = ctypes.c_float(), ctypes.c_float()
+        C.check("cb_tune_decode_times", self._lib.cb_tune_decode_times(self._h, ctypes.byref(a), ctypes.byref(b)))
+        return a.value, b.value
 
     def get_decode_fusion(self):
         v = ctypes.c_int()

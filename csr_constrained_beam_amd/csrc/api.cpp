@@ -309,6 +309,60 @@ cb_status check_plan(const cb_plan* p, int32_t Q, const char* fn) {
 }
 
 }  // namespace
+
+// Copy the host tables of idx to idx->device, release the host copies and
+// upload the step descriptors.  On failure idx is freed.
+cb_status upload_index(cb_index* idx) {
+    DeviceGuard g(idx->device);
+    if (!g.ok) {
+        set_error("cb_build_index: cannot select device " + std::to_string(idx->device));
+        idx->device = -1;
+        cb_free_index(idx);
+        return CB_EHIP;
+    }
+    cb_status st = CB_OK;
+    for (auto& T : idx->steps) {
+        st = dev_alloc(&T.d_row_ptr, T.row_ptr.size(), "row_ptr");
+        if (st == CB_OK) st = dev_alloc(&T.d_tok, T.tok.size(), "tokens");
+        if (st == CB_OK) st = dev_alloc(&T.d_bits, T.bits.size(), "bitmap");
+        if (st == CB_OK) st = dev_alloc(&T.d_rank, T.rank.size(), "rank directory");
+        if (st == CB_OK) st = dev_alloc(&T.d_tok0, T.tok0.size(), "first tokens");
+        hipError_t e = hipSuccess;
+        if (st == CB_OK && T.d_row_ptr)
+            e = hipMemcpy(T.d_row_ptr, T.row_ptr.data(), T.row_ptr.size() * 4, hipMemcpyHostToDevice);
+        if (st == CB_OK && e == hipSuccess && T.d_tok)
+            e = hipMemcpy(T.d_tok, T.tok.data(), T.tok.size() * 2, hipMemcpyHostToDevice);
+        if (st == CB_OK && e == hipSuccess && T.d_bits)
+            e = hipMemcpy(T.d_bits, T.bits.data(), T.bits.size() * 4, hipMemcpyHostToDevice);
+        if (st == CB_OK && e == hipSuccess && T.d_rank)
+            e = hipMemcpy(T.d_rank, T.rank.data(), T.rank.size() * 2, hipMemcpyHostToDevice);
+        if (st == CB_OK && e == hipSuccess && T.d_tok0)
+            e = hipMemcpy(T.d_tok0, T.tok0.data(), T.tok0.size() * 2, hipMemcpyHostToDevice);
+        if (st == CB_OK && e != hipSuccess) st = hip_fail("cb_build_index: upload", e);
+        if (st != CB_OK) {
+            cb_free_index(idx);
+            return st;
+        }
+        std::vector<uint32_t>().swap(T.row_ptr);
+        std::vector<uint16_t>().swap(T.tok);
+        std::vector<uint32_t>().swap(T.bits);
+        std::vector<uint16_t>().swap(T.rank);
+        std::vector<uint16_t>().swap(T.tok0);
+    }
+    std::vector<cb::StepDev> descs;
+    for (const auto& T : idx->steps) descs.push_back(T.dev(idx->words));
+    st = dev_alloc(&idx->d_steps, descs.size(), "step descriptors");
+    if (st == CB_OK) {
+        hipError_t e = hipMemcpy(idx->d_steps, descs.data(), descs.size() * sizeof(cb::StepDev), hipMemcpyHostToDevice);
+        if (e != hipSuccess) st = hip_fail("cb_build_index: upload", e);
+    }
+    if (st != CB_OK) {
+        cb_free_index(idx);
+        return st;
+    }
+    return CB_OK;
+}
+
 }  // namespace cb
 
 using namespace cb;
@@ -353,50 +407,7 @@ cb_status cb_build_index(const int32_t* sids, int64_t n_items, int32_t L, int32_
         delete idx;
         return st;
     }
-    if (device >= 0) {
-        DeviceGuard g(device);
-        if (!g.ok) {
-            delete idx;
-            set_error("cb_build_index: cannot select device " + std::to_string(device));
-            return CB_EHIP;
-        }
-        for (auto& T : idx->steps) {
-            st = dev_alloc(&T.d_row_ptr, T.row_ptr.size(), "row_ptr");
-            if (st == CB_OK) st = dev_alloc(&T.d_tok, T.tok.size(), "tokens");
-            if (st == CB_OK) st = dev_alloc(&T.d_bits, T.bits.size(), "bitmap");
-            if (st == CB_OK) st = dev_alloc(&T.d_rank, T.rank.size(), "rank directory");
-            hipError_t e = hipSuccess;
-            if (st == CB_OK && T.d_row_ptr)
-                e = hipMemcpy(T.d_row_ptr, T.row_ptr.data(), T.row_ptr.size() * 4, hipMemcpyHostToDevice);
-            if (st == CB_OK && e == hipSuccess && T.d_tok)
-                e = hipMemcpy(T.d_tok, T.tok.data(), T.tok.size() * 2, hipMemcpyHostToDevice);
-            if (st == CB_OK && e == hipSuccess && T.d_bits)
-                e = hipMemcpy(T.d_bits, T.bits.data(), T.bits.size() * 4, hipMemcpyHostToDevice);
-            if (st == CB_OK && e == hipSuccess && T.d_rank)
-                e = hipMemcpy(T.d_rank, T.rank.data(), T.rank.size() * 2, hipMemcpyHostToDevice);
-            if (st == CB_OK && e != hipSuccess) st = hip_fail("cb_build_index: upload", e);
-            if (st != CB_OK) {
-                cb_free_index(idx);
-                return st;
-            }
-            std::vector<uint32_t>().swap(T.row_ptr);
-            std::vector<uint16_t>().swap(T.tok);
-            std::vector<uint32_t>().swap(T.bits);
-            std::vector<uint16_t>().swap(T.rank);
-        }
-        std::vector<cb::StepDev> descs;
-        for (const auto& T : idx->steps) descs.push_back(T.dev(idx->words));
-        st = dev_alloc(&idx->d_steps, descs.size(), "step descriptors");
-        if (st == CB_OK) {
-            hipError_t e = hipMemcpy(idx->d_steps, descs.data(), descs.size() * sizeof(cb::StepDev),
-                                     hipMemcpyHostToDevice);
-            if (e != hipSuccess) st = hip_fail("cb_build_index: upload", e);
-        }
-        if (st != CB_OK) {
-            cb_free_index(idx);
-            return st;
-        }
-    }
+    if (device >= 0 && (st = upload_index(idx)) != CB_OK) return st;  // frees idx on failure
     *out = idx;
     return CB_OK;
 }
@@ -496,6 +507,7 @@ void cb_free_index(cb_index* idx) {
             dev_free(T.d_tok);
             dev_free(T.d_bits);
             dev_free(T.d_rank);
+            dev_free(T.d_tok0);
         }
         dev_free(idx->d_steps);
     }
@@ -690,7 +702,8 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
     // persistent tail: the trailing steps on the fused sparse step with LDS
     // selection run in one launch (untraced, untuned decodes only)
     int t_fuse = L;
-    if (p->fuse && reps == 0 && !tr_h && !tr_rows && !tr_acc && idx->d_steps) {
+    const bool fuse = p->fuse_mode == 1 || (p->fuse_mode == -1 && p->fuse_tuned);
+    if (fuse && reps == 0 && !tr_h && !tr_rows && !tr_acc && idx->d_steps) {
         while (t_fuse > 0 && resolve_path(p, t_fuse - 1) == CB_PATH_SPARSE &&
                resolve_select(p, t_fuse - 1) == CB_SELECT_LDS)
             --t_fuse;
@@ -818,11 +831,11 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
 
 cb_status cb_set_decode_fusion(cb_plan* p, int32_t enable) {
     clear_error();
-    if (!p) {
-        set_error("cb_set_decode_fusion: plan is NULL");
+    if (!p || enable < -1 || enable > 1) {
+        set_error("cb_set_decode_fusion: plan is NULL or enable not in {-1, 0, 1}");
         return CB_EINVAL;
     }
-    p->fuse = enable != 0;
+    p->fuse_mode = enable;
     return CB_OK;
 }
 
@@ -832,7 +845,18 @@ cb_status cb_get_decode_fusion(const cb_plan* p, int32_t* enabled) {
         set_error("cb_get_decode_fusion: plan or output is NULL");
         return CB_EINVAL;
     }
-    *enabled = p->fuse ? 1 : 0;
+    *enabled = (p->fuse_mode == 1 || (p->fuse_mode == -1 && p->fuse_tuned)) ? 1 : 0;
+    return CB_OK;
+}
+
+cb_status cb_tune_decode_times(const cb_plan* p, float* stepwise_us, float* persistent_us) {
+    clear_error();
+    if (!p) {
+        set_error("cb_tune_decode_times: plan is NULL");
+        return CB_EINVAL;
+    }
+    if (stepwise_us) *stepwise_us = p->fuse_us[0];
+    if (persistent_us) *persistent_us = p->fuse_us[1];
     return CB_OK;
 }
 
@@ -875,6 +899,36 @@ cb_status cb_tune(cb_plan* p, int32_t Q, const float* q, const float* P, const v
     if (st != CB_OK) return st;
     hipError_t e = hipStreamSynchronize((hipStream_t)stream);
     if (e != hipSuccess) return hip_fail("cb_tune: synchronise", e);
+    // the persistent decode against one launch per step, on the chosen paths
+    const hipStream_t s = (hipStream_t)stream;
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    if ((e = hipEventCreate(&ev0)) != hipSuccess || (e = hipEventCreate(&ev1)) != hipSuccess) {
+        if (ev0) (void)hipEventDestroy(ev0);
+        return hip_fail("cb_tune: events", e);
+    }
+    const int32_t mode = p->fuse_mode;
+    p->fuse_us[0] = p->fuse_us[1] = -1.f;
+    for (int f = 0; f < 2 && st == CB_OK; ++f) {
+        p->fuse_mode = f;
+        st = decode_impl(p, Q, q, P, W, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s, 0);  // warm
+        if (st == CB_OK) (void)hipEventRecord(ev0, s);
+        for (int r = 0; r < reps && st == CB_OK; ++r)
+            st = decode_impl(p, Q, q, P, W, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s, 0);
+        if (st != CB_OK) break;
+        (void)hipEventRecord(ev1, s);
+        if ((e = hipEventSynchronize(ev1)) != hipSuccess) {
+            st = hip_fail("cb_tune: synchronise", e);
+            break;
+        }
+        float ms = 0.f;
+        (void)hipEventElapsedTime(&ms, ev0, ev1);
+        p->fuse_us[f] = ms * 1000.f / (float)reps;
+    }
+    p->fuse_mode = mode;
+    (void)hipEventDestroy(ev0);
+    (void)hipEventDestroy(ev1);
+    if (st != CB_OK) return st;
+    p->fuse_tuned = p->fuse_us[1] <= p->fuse_us[0];
     return CB_OK;
 }
 

@@ -27,6 +27,7 @@ struct StepDev {
     int32_t words;            // 32-bit words per bitmap row = ceil(V / 32)
     int32_t store;            // CB_STORE_CSR or CB_STORE_BITMAP
     int32_t S;                // widest row (fixed slot count of the step)
+    const uint16_t* tok0;     // CSR: first token of every row [n_rows] (read with row_ptr); else nullptr
 };
 
 struct StepTable {
@@ -39,14 +40,16 @@ struct StepTable {
     std::vector<uint16_t> tok;
     std::vector<uint32_t> bits;
     std::vector<uint16_t> rank;
+    std::vector<uint16_t> tok0;
     // device copies
     uint32_t* d_row_ptr = nullptr;
     uint16_t* d_tok = nullptr;
     uint32_t* d_bits = nullptr;
     uint16_t* d_rank = nullptr;
+    uint16_t* d_tok0 = nullptr;
 
     StepDev dev(int32_t words) const {
-        return StepDev{d_row_ptr, d_tok, d_bits, d_rank, n_rows, words, store, S};
+        return StepDev{d_row_ptr, d_tok, d_bits, d_rank, n_rows, words, store, S, d_tok0};
     }
 };
 
@@ -115,7 +118,11 @@ struct cb_plan {
     float* scratch_logp = nullptr;        // [R]
     int32_t* scratch_tok = nullptr;       // [R]
     int32_t* scratch_par = nullptr;       // [R]
-    bool fuse = true;                     // persistent decode of the trailing sparse steps
+    // persistent decode of the trailing sparse steps: mode -1 measured by
+    // cb_tune (fuse_tuned, on until measured), 0 off, 1 on
+    int32_t fuse_mode = -1;
+    bool fuse_tuned = true;
+    float fuse_us[2] = {-1.f, -1.f};      // measured decode time without / with it
     // kernel timing (cb_profile_start / cb_profile_stop)
     bool prof_on = false;
     int32_t prof_cap = 0;
@@ -195,6 +202,9 @@ hipError_t launch_wide_sort(const StepDev& st, int Q, int K, const int32_t* beam
                             int32_t* tok, int32_t* par, int32_t* rows, float* logp, hipStream_t s);
 
 // Index construction (index_build.cpp).
+// Upload the host tables of idx to idx->device (release the host copies);
+// frees idx on failure.
+cb_status upload_index(cb_index* idx);
 cb_status build_host_tables(const int32_t* sids, int64_t n_items, int32_t L, int32_t V, int32_t store,
                             cb_index* idx);
 

@@ -347,7 +347,7 @@ __device__ __forceinline__ void wave_append(bool p, uint64_t v, uint64_t* keys, 
 // ceil(m / 64) waves that hold keys sort and merge them as a tree.  More: the
 // threshold selection.  stage: LDS [NT]; list: LDS int [m].  All threads call.
 template <int NT>
-__device__ void block_select_list(int m, int Kc, const uint64_t* keys, uint64_t* out, uint64_t* stage, int* list,
+__device__ __forceinline__ void block_select_list(int m, int Kc, const uint64_t* keys, uint64_t* out, uint64_t* stage, int* list,
                                   int* red_i, uint64_t* bcast) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
     if (m > NT) {

@@ -192,8 +192,17 @@ cb_status build_impl(const int32_t* sids, int64_t n, int32_t L, int32_t V, int32
             T.store = CB_STORE_BITMAP;
             T.bytes = (nr + 1) * 4 + bitmap_bytes;
         } else {
+            // first token of every row, read together with row_ptr so that a
+            // one-token row needs no second dependent read
+            try {
+                T.tok0.resize((size_t)nr);
+            } catch (...) {
+                st = CB_ENOMEM;
+                return;
+            }
+            for (int64_t k = 0; k < nr; ++k) T.tok0[(size_t)k] = T.tok[T.row_ptr[(size_t)k]];
             T.store = CB_STORE_CSR;
-            T.bytes = (nr + 1) * 4 + csr_bytes;
+            T.bytes = (nr + 1) * 4 + csr_bytes + nr * 2;
         }
     };
     {

@@ -235,6 +235,7 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
             const bool live = kk[u] < K && beam_live(st, r[u], a[u]);
             e0[u] = live ? st.row_ptr[r[u]] : 0u;
             n[u] = live ? (int)(st.row_ptr[r[u] + 1] - e0[u]) : 0;
+            const int f0 = live && st.tok0 ? (int)st.tok0[r[u]] : 0;  // in flight with row_ptr
             small[u] = live && n[u] <= kSmallRow && st.store == CB_STORE_CSR;
             if (kk[u] < K) {
                 if (live) {
@@ -247,7 +248,7 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
                     if (!small[u] && lane == 0) big[atomicAdd(&nbig, 1)] = kk[u];
                 }
             }
-            tk[u] = small[u] && lane < n[u] ? (int)st.tok[e0[u] + lane] : 0;
+            tk[u] = small[u] && lane < n[u] ? (lane == 0 && st.tok0 ? f0 : (int)st.tok[e0[u] + lane]) : 0;
             if (small[u] && lane < n[u]) tokq[kk[u] * kWave + lane] = (uint16_t)tk[u];
         }
         if (!small[0] && !small[1]) continue;

@@ -129,6 +129,24 @@ cb_status cb_index_row(const cb_index* idx, int32_t t, int64_t row,
  * from it must not be used afterwards (destroying them is still allowed). */
 void cb_free_index(cb_index* idx);
 
+/* Write the index's tables to a file (host or device index; device tables
+ * are read back).  The file holds the tables exactly as built, so loading it
+ * skips the sort and deduplication of the catalog (ZeroGR summary: the index
+ * is built on the CPU once and streamed to the GPU).  Format: tag
+ * "CBINDEX1", int32 L, V, int64 n_items, per step int64 n_rows, n_edges,
+ * int32 widest row, storage, then row_ptr u32 [n_rows+1] and either tok u16
+ * [n_edges] + first token per row u16 [n_rows] (CSR) or bits u32 and rank u16
+ * [n_rows][ceil(V/32)] (bitmap); last a 64-bit FNV-1a hash of all preceding
+ * bytes; little-endian.  Errors: CB_EINVAL (NULL, cannot write), CB_EHIP. */
+cb_status cb_index_save(const cb_index* idx, const char* path);
+
+/* Read an index written by cb_index_save and upload it to `device` (-1: host
+ * tables only).  Every structural invariant is checked on the host first
+ * (row counts chained across steps, row pointers, ascending in-range tokens,
+ * bitmap rank directory, hash), so a damaged file returns CB_EINVAL and
+ * nothing reaches the device.  Errors: CB_EINVAL, CB_ENOMEM, CB_EHIP. */
+cb_status cb_index_load(const char* path, int32_t device, cb_index** out);
+
 /* Create a plan: allocates, once, every device buffer the step and decode
  * need for up to Q_max queries of beam width K, hidden width d (multiple of 8)
  * and element type dtype (of W and of the hidden vectors).  Nothing is
@@ -198,24 +216,31 @@ cb_status cb_decode(cb_plan* plan, int32_t Q, const float* q, const float* P, co
                     void* trace_hidden, int32_t* trace_rows, float* trace_acc, void* stream);
 
 /* Persistent decode (FlashTrie, arXiv HTML, sections 2.2 and 4.2: every step
- * of a query in one launch, paying the launch cost once).  When enabled (the
- * default) and cb_decode is called without trace buffers, the trailing run
- * of steps whose path resolves to CB_PATH_SPARSE with CB_SELECT_LDS (at least
- * two steps) runs as one launch: one workgroup per query performs each of
- * those steps and the hidden updates between them, so no workgroup waits for
- * another.  Results equal the step-by-step decode bit for bit.  Disabling
- * restores one launch per step.  Synchronous with respect to the host. */
+ * of a query in one launch, paying the launch cost once).  When enabled and
+ * cb_decode is called without trace buffers, the trailing run of steps whose
+ * path resolves to CB_PATH_SPARSE with CB_SELECT_LDS (at least two steps)
+ * runs as one launch: one workgroup per query performs each of those steps
+ * and the hidden updates between them, so no workgroup waits for another.
+ * Results equal the step-by-step decode bit for bit.  enable: 1 on, 0 off
+ * (one launch per step), -1 (the default) automatic: cb_tune times the
+ * decode both ways and keeps the faster (on until measured).  Synchronous
+ * with respect to the host. */
 cb_status cb_set_decode_fusion(cb_plan* plan, int32_t enable);
 
-/* Whether the persistent decode is enabled (1) or not (0). */
+/* Whether the persistent decode is in effect (1) or not (0). */
 cb_status cb_get_decode_fusion(const cb_plan* plan, int32_t* enabled);
+
+/* Mean decode time (microseconds) with one launch per step and with the
+ * persistent tail, from the last cb_tune (negative when not measured). */
+cb_status cb_tune_decode_times(const cb_plan* plan, float* stepwise_us, float* persistent_us);
 
 /* Pre-measured path switch (ZeroGR: warm-up requests try every option per
  * step and keep the fastest).  Runs one warm-up decode on the given inputs;
  * at every step whose path is AUTO it times the dense and the sparse path
  * (`reps` launches each, HIP events) and records the faster; the decode then
- * continues on the recorded path.  Synchronises `stream`.  Arguments as
- * cb_decode. */
+ * continues on the recorded path.  Then, when the persistent decode is
+ * automatic, times `reps` whole decodes with and without it and keeps the
+ * faster.  Synchronises `stream`.  Arguments as cb_decode. */
 cb_status cb_tune(cb_plan* plan, int32_t Q, const float* q, const float* P, const void* W,
                   int32_t reps, void* stream);
 

@@ -159,3 +159,23 @@ def test_fusion_switch_and_traced_decode_unfused():
     torch.cuda.synchronize()
     for k in ("seqs", "logp", "rows"):
         assert torch.equal(tr[k], b[k]), k
+
+
+def test_tune_chooses_the_faster_decode_form():
+    w = workload("small")
+    cfg = w["cfg"]
+    idx = cb.Index(w["items"], cfg.V, device=0)
+    plan = idx.plan(cfg.Q, cfg.K, cfg.d, cfg.dtype)
+    q = torch.from_numpy(w["dense"]["q"]).to(DEV)
+    P = torch.from_numpy(w["dense"]["P"]).to(DEV)
+    assert plan.tune_decode_times() == (-1.0, -1.0)
+    plan.tune(q, P, w["W"], reps=3)
+    stepwise, persistent = plan.tune_decode_times()
+    assert stepwise > 0 and persistent > 0
+    assert plan.get_decode_fusion() == (persistent <= stepwise)
+    plan.set_decode_fusion(True)
+    assert plan.get_decode_fusion() is True
+    plan.set_decode_fusion(False)
+    assert plan.get_decode_fusion() is False
+    plan.set_decode_fusion("auto")
+    assert plan.get_decode_fusion() == (persistent <= stepwise)

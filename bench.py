@@ -30,6 +30,15 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
 
+# Scaling sweeps over the production workload family (L = 8, d = 1024, bf16):
+# catalog size at V = 2048, codebook size at 10M items and batch 32, batch size.
+SWEEPS = {
+    "items": [{"items": n} for n in (100_000, 1_000_000, 10_000_000, 20_000_000, 100_000_000)],
+    "codebook": [{"items": 10_000_000, "Q": 32, "V": v} for v in (256, 1024, 2048, 4096, 8192, 16384, 32768)],
+    "batch": [{"Q": q} for q in (1, 8, 32, 64, 128, 256)],
+}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -37,6 +46,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="production")
     ap.add_argument("--K", type=int, default=None, help="beam width other than the workload's (sweeps)")
+    ap.add_argument("--items", type=int, default=None, help="catalog size other than the workload's (sweeps)")
+    ap.add_argument("--V", type=int, default=None, help="codebook size other than the workload's (sweeps)")
+    ap.add_argument("--Q", type=int, default=None, help="batch (queries) other than the workload's (sweeps)")
+    ap.add_argument("--sweep", default=None, choices=sorted(SWEEPS),
+                    help="run the named scaling sweep, one child process per point, and print a table")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
     ap.add_argument("--no-graph", action="store_true")
@@ -79,12 +93,53 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def run_sweep(args):
+    """One child bench process per sweep point (each builds its own workload);
+    a table on stderr and the list of points as one JSON line."""
+    import subprocess
+    import tempfile
+    rows = []
+    for point in SWEEPS[args.sweep]:
+        with tempfile.NamedTemporaryFile(suffix=".json", delete=False) as f:
+            out = f.name
+        cmd = [sys.executable, os.path.abspath(__file__), "--config", args.config, "--no-cpu", "--steps",
+               str(args.steps), "--warmup", str(args.warmup), "--json-out", out]
+        for k, v in point.items():
+            cmd += ["--" + k, str(v)]
+        log("sweep %s: %s" % (args.sweep, point))
+        rc = subprocess.run(cmd, stdout=subprocess.DEVNULL).returncode
+        if rc != 0:
+            log("sweep point failed (exit %d): %s" % (rc, point))
+            rows.append(dict(point, error=rc))
+            break
+        with open(out) as f:
+            r = json.loads(f.read())
+        os.unlink(out)
+        rows.append(dict(point, workload=r["config"]["workload"], paths=r["config"]["paths"],
+                         ms_per_pass=r["ms_per_step"], us_per_decode_step=r["us_per_decode_step"],
+                         expansions_per_pass=r["expansions_per_pass"], expansions_per_s=r["value"],
+                         decode_ms=r["decode_ms_with_model_standin"],
+                         decode_ms_step_by_step=r["decode_ms_step_by_step"],
+                         index_bytes=r["index"]["bytes"], index_build_s=r["index"]["build_s"],
+                         dominant=r["roofline"]["kernel"], dominant_frac=r["roofline"]["frac"]))
+        x = rows[-1]
+        log("  %s: %.4f ms/pass, %.3g expansions/s, decode %.4f ms, index %.1f MB" % (
+            point, x["ms_per_pass"], x["expansions_per_s"], x["decode_ms"], x["index_bytes"] / 1e6))
+    line = json.dumps({"sweep": args.sweep, "config": args.config, "points": rows})
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    print(line, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
               "(run with --gpus 1)" % args.gpus, flush=True)
         sys.exit(2)
+    if args.sweep:
+        return run_sweep(args)
 
     import torch
 
@@ -101,7 +156,8 @@ def main():
     import csr_constrained_beam_amd as cb
     from synth import get_config, make_catalog, make_dense
 
-    cfg = get_config(args.config, K=args.K) if args.K else get_config(args.config)
+    over = {k: v for k, v in (("K", args.K), ("n_items", args.items), ("V", args.V), ("Q", args.Q)) if v}
+    cfg = get_config(args.config, **over)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()

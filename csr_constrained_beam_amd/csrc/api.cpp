@@ -176,7 +176,7 @@ cb_status run_step_radix(cb_plan* p, int t, int Q, int32_t path, const void* hid
     const bool dense = path == CB_PATH_DENSE;
     hipError_t e;
     if (dense) {
-        {
+        if (!gemm_finds_live(p->dtype, R)) {
             ProfMark m(p, s, t, CB_KERNEL_LIVE_ROWS, 1024, 1);
             e = launch_live_rows(sd, R, rows, acc, p->live, p->n_live, p->ci_of, s);
             m.done();
@@ -185,7 +185,8 @@ cb_status run_step_radix(cb_plan* p, int t, int Q, int32_t path, const void* hid
         const bool bf = p->dtype == CB_BF16;
         ProfMark m(p, s, t, bf ? CB_KERNEL_GEMM_BF16 : CB_KERNEL_GEMM_F32, bf ? 512 : 256,
                    gemm_blocks(p->dtype, R, idx->V));
-        e = launch_gemm_scores(p->dtype, R, idx->V, p->d, p->live, p->n_live, hidden, Wt, p->Z, p->Zp, s);
+        e = launch_gemm_scores(p->dtype, R, idx->V, p->d, p->live, p->n_live, hidden, Wt, p->Z, p->Zp, sd, rows, acc,
+                               p->ci_of, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: full-codebook scores", e);
     }
@@ -251,7 +252,7 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const vo
         if (e != hipSuccess) return hip_fail("cb_step: sparse step", e);
         return CB_OK;
     }
-    {
+    if (!gemm_finds_live(p->dtype, R)) {
         ProfMark m(p, s, t, CB_KERNEL_LIVE_ROWS, 1024, 1);
         e = launch_live_rows(sd, R, rows, acc, p->live, p->n_live, p->ci_of, s);
         m.done();
@@ -260,7 +261,8 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const vo
     {
         const bool bf = p->dtype == CB_BF16;
         ProfMark m(p, s, t, bf ? CB_KERNEL_GEMM_BF16 : CB_KERNEL_GEMM_F32, bf ? 512 : 256, gemm_blocks(p->dtype, R, idx->V));
-        e = launch_gemm_scores(p->dtype, R, idx->V, p->d, p->live, p->n_live, hidden, Wt, p->Z, p->Zp, s);
+        e = launch_gemm_scores(p->dtype, R, idx->V, p->d, p->live, p->n_live, hidden, Wt, p->Z, p->Zp, sd, rows, acc,
+                               p->ci_of, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: full-codebook scores", e);
     }

@@ -155,8 +155,11 @@ hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int K
 // Dense path: live-beam list, full-codebook scores, per-beam expansion, per-query merge.
 hipError_t launch_live_rows(const StepDev& st, int R, const int32_t* beam_rows, const float* acc, int32_t* live,
                             int32_t* n_live, int32_t* ci_of, hipStream_t s);
-hipError_t launch_gemm_scores(cb_dtype dt, int R, int V, int d, const int32_t* live, const int32_t* n_live,
-                              const void* H, const void* W, float* Z, float* Zp, hipStream_t s);
+// Whether the bf16 product finds the live beams itself (no k_live_rows).
+bool gemm_finds_live(cb_dtype dt, int R);
+hipError_t launch_gemm_scores(cb_dtype dt, int R, int V, int d, const int32_t* live, int32_t* n_live,
+                              const void* H, const void* W, float* Z, float* Zp, const StepDev& st,
+                              const int32_t* beam_rows, const float* acc, int32_t* ci_of, hipStream_t s);
 size_t split_scores_floats(int V);
 hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R, int K, int Kc, int d,
                               const void* hidden, const void* W, const float* Z, const float* Zp, int64_t ldz,

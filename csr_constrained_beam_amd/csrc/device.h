@@ -512,7 +512,7 @@ constexpr int kBM = 128, kBN = 128, kBK = 64, kLDP = kBK + 8;
 constexpr int kWM = 32, kWN = 64;  // per-wave tile: 1 x 2 MFMA 32x32 blocks
 constexpr int kGemmThreads = (kBM / kWM) * (kBN / kWN) * 64;
 constexpr int kGemmLds = 2 * (kBM + kBN) * kLDP * 2;  // double-buffered A and B tiles (bytes)
-constexpr int kSplitMax = 8;   // k-slices for steps with few live beams
+constexpr int kSplitMax = 2;   // k-slices for steps with few live beams (more cost the consumer more than they save)
 constexpr int kSplitRows = 2 * kBM;
 constexpr int kCUs = 256;
 

@@ -584,32 +584,76 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // row][v].  Consecutive tiles on one XCD share W columns.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
+// Live beams found in the prologue (R > 0; R <= kFoldSlots): every workgroup
+// marks the live slots (each thread a run of consecutive slots), one block
+// scan gives their compact positions, and the workgroup keeps the slots of
+// its own tile; workgroup 0 also writes n_live and ci_of for the expansion
+// kernel.  Otherwise (R == 0) the list comes from k_live_rows.
+constexpr int kFoldSlots = 16 * kGemmThreads;
+
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_bf16(int V, int d, const int32_t* __restrict__ live,
-                                                            const int32_t* __restrict__ n_live,
+                                                            int32_t* __restrict__ n_live,
                                                             const uint16_t* __restrict__ H,
                                                             const uint16_t* __restrict__ W, float* __restrict__ Z,
-                                                            float* __restrict__ Zp, int64_t ldz) {
+                                                            float* __restrict__ Zp, int64_t ldz, StepDev st, int R,
+                                                            const int32_t* __restrict__ beam_rows,
+                                                            const float* __restrict__ beam_acc,
+                                                            int32_t* __restrict__ ci_of) {
     extern __shared__ __align__(16) uint16_t gsm[];
     uint16_t* As = gsm;                     // [2][kBM * kLDP]
     uint16_t* Bs = gsm + 2 * kBM * kLDP;    // [2][kBN * kLDP]
     __shared__ int rows_s[kBM];
+    __shared__ int red_i[kGemmThreads / kWave];
     constexpr int NT = kGemmThreads;
     constexpr int CA = kBM * kBK / 8 / NT, CB = kBN * kBK / 8 / NT;  // 16-byte chunks per thread
     constexpr int TJ = kWN / 32;
-    const int nl = *n_live;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int L = blockIdx.x;
+    int nl;
+    uint32_t onmask = 0;
+    int pos0 = 0, run = 0, b0 = 0;
+    if (R > 0) {
+        run = (R + NT - 1) / NT;
+        b0 = tid * run;
+        int c = 0;
+        for (int j = 0; j < run; ++j) {
+            const int b = b0 + j;
+            const bool on = b < R && beam_live(st, beam_rows[b], beam_acc[b]);
+            onmask |= (uint32_t)on << j;
+            c += on;
+        }
+        pos0 = block_exclusive_scan<NT>(c, red_i, &nl);
+        if (L == 0) {
+            int p = pos0;
+            for (int j = 0; j < run; ++j)
+                if (b0 + j < R) ci_of[b0 + j] = (onmask >> j & 1u) ? p++ : -1;
+            if (tid == 0) *n_live = nl;
+        }
+    } else {
+        nl = *n_live;
+    }
     const int split = gemm_split(nl, V, d);
     const int mt = (nl + kBM - 1) / kBM, nt = (V + kBN - 1) / kBN;
     const int N = mt * nt * split;
-    const int L = blockIdx.x;
-    if (L >= N) return;
+    if (L >= N) return;  // uniform over the workgroup
     const int full = (N / 8) * 8;
     const int lin = L < full ? (L % 8) * (full / 8) + L / 8 : L;
     const int zs = lin % split, tile = lin / split;
     const int m0 = (tile % mt) * kBM, n0 = (tile / mt) * kBN;
     const int klen = d / split, kbeg = zs * klen;
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    if (tid < kBM) rows_s[tid] = m0 + tid < nl ? live[m0 + tid] : -1;
+    if (R > 0) {
+        if (tid < kBM) rows_s[tid] = -1;
+        __syncthreads();
+        int p = pos0;
+        for (int j = 0; j < run; ++j)
+            if (onmask >> j & 1u) {
+                if (p >= m0 && p < m0 + kBM) rows_s[p - m0] = b0 + j;
+                ++p;
+            }
+    } else if (tid < kBM) {
+        rows_s[tid] = m0 + tid < nl ? live[m0 + tid] : -1;
+    }
     __syncthreads();
     const int wm = (wv / (kBN / kWN)) * kWM, wn = (wv % (kBN / kWN)) * kWN;
 
@@ -1078,15 +1122,20 @@ hipError_t launch_live_rows(const StepDev& st, int R, const int32_t* beam_rows, 
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_scores(cb_dtype dt, int R, int V, int d, const int32_t* live, const int32_t* n_live,
-                              const void* H, const void* W, float* Z, float* Zp, hipStream_t s) {
+bool gemm_finds_live(cb_dtype dt, int R) { return dt == CB_BF16 && R <= kFoldSlots; }
+
+hipError_t launch_gemm_scores(cb_dtype dt, int R, int V, int d, const int32_t* live, int32_t* n_live,
+                              const void* H, const void* W, float* Z, float* Zp, const StepDev& st,
+                              const int32_t* beam_rows, const float* acc, int32_t* ci_of, hipStream_t s) {
     if (R <= 0) return hipSuccess;
     if (dt == CB_BF16) {
         static const hipError_t lds_ok = hipFuncSetAttribute(
             (const void*)k_gemm_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
         if (lds_ok != hipSuccess) return lds_ok;
+        const int fold = gemm_finds_live(dt, R) ? R : 0;
         hipLaunchKernelGGL(k_gemm_bf16, dim3(gemm_grid(R, V)), dim3(kGemmThreads), kGemmLds, s, V, d, live, n_live,
-                           (const uint16_t*)H, (const uint16_t*)W, Z, Zp, (int64_t)V);
+                           (const uint16_t*)H, (const uint16_t*)W, Z, Zp, (int64_t)V, st, fold, beam_rows, acc,
+                           ci_of);
     } else {
         dim3 grid((V + 15) / 16, (R + 15) / 16);
         hipLaunchKernelGGL(k_gemm_f32, grid, dim3(256), 0, s, V, d, live, n_live, (const float*)H, (const float*)W,

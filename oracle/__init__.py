@@ -22,6 +22,14 @@ Parity status of each function (what pins it; see ``tests/test_oracle_pins.py``)
   decode invariants.
 * ``Trie.hidden``: the stand-in model's rule is defined by the workload, not by
   the pages; it is pinned by a closed form (unit norm, direction of s) only.
+* ``Trie.step`` / ``Trie.decode`` with ``mode="score_first"`` (softmax over
+  the whole codebook, valid tokens as candidates) and ``mode="unconstrained"``
+  (every token a candidate, row 0): the brute-force enumerator with the
+  whole codebook as softmax support (every catalog item, resp. every
+  sequence of the codebook product, with its path score when the beam is
+  that wide), equality of the three variants on the full-product catalog,
+  and the per-beam constant shift lse(valid) - lse(all) <= 0 between the two
+  supports (``tests/test_oracle_modes.py``).
 * ``SortedRange`` (``range_beam.c``): the same definition computed over the
   sorted catalog without a trie, light enough for 100M-item catalogs.  Pinned
   by a catalog scan of every prefix, brute-force path scores, the W = 0 closed
@@ -54,6 +62,9 @@ def build(force=False):
     return _LIB
 
 
+_MODES = {"filter_first": 0, "score_first": 1, "unconstrained": 2}
+
+
 def _load():
     global _lib
     if _lib is None:
@@ -79,6 +90,10 @@ def _load():
         lib.or_decode.restype = ctypes.c_int
         lib.or_decode.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P,
                                   P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
+        lib.or_step_mode.restype = ctypes.c_int
+        lib.or_step_mode.argtypes = lib.or_step.argtypes + [ctypes.c_int]
+        lib.or_decode_mode.restype = ctypes.c_int
+        lib.or_decode_mode.argtypes = lib.or_decode.argtypes + [ctypes.c_int]
         lib.or_hidden.restype = None
         lib.or_hidden.argtypes = [P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P]
         lib.orr_build.restype = P
@@ -163,11 +178,16 @@ class Trie:
             return None
         return out[:depth]
 
-    def step(self, t, K, h, Wt, rows, acc, candidates=False, threads=1):
+    def step(self, t, K, h, Wt, rows, acc, candidates=False, threads=1, mode="filter_first"):
         """Teacher-forced step.  h [Q*K][d] f32, Wt [V][d] f32, rows [Q*K]
         (-1 dead), acc [Q*K] f32.  Returns dict of tokens, parents, rows,
         logp (each [Q*K]) and, with ``candidates``, every candidate of every
-        query sorted best first (``cand_*`` [Q][cap], ``cand_count`` [Q])."""
+        query sorted best first (``cand_*`` [Q][cap], ``cand_count`` [Q]).
+        mode: "filter_first", "score_first" (softmax over the whole codebook,
+        valid tokens as candidates) or "unconstrained" (every token, row 0)."""
+        m = _MODES[mode]
+        if m and type(self) is not Trie:
+            raise NotImplementedError("modes other than filter_first: pointer-trie oracle only")
         h = np.ascontiguousarray(h, dtype=np.float32)
         Wt = np.ascontiguousarray(Wt, dtype=np.float32)
         rows = np.ascontiguousarray(rows, dtype=np.int64)
@@ -189,24 +209,29 @@ class Trie:
             # capacity: the widest query's candidate count
             fan = np.zeros(R, dtype=np.int64)
             for b in np.nonzero(rows >= 0)[0]:
-                fan[b] = self._fn("children_of_row")(self._h, t, int(rows[b]), None, None, 0)
+                fan[b] = self.V if m == 2 else self._fn("children_of_row")(self._h, t, int(rows[b]), None, None, 0)
             cap = int(max(1, fan.reshape(Q, K).sum(axis=1).max() if Q else 1))
             cc = np.zeros(Q, np.int64)
             ct = np.full((Q, cap), -1, np.int32)
             cp = np.full((Q, cap), -1, np.int32)
             cr = np.full((Q, cap), -1, np.int64)
             cs = np.full((Q, cap), -np.inf, np.float32)
-        r = self._fn("step")(self._h, t, Q, K, d, _ptr(h), _ptr(Wt), _ptr(rows), _ptr(acc),
-                              _ptr(out["tokens"]), _ptr(out["parents"]), _ptr(out["rows"]), _ptr(out["logp"]),
-                              cap, _ptr(cc), _ptr(ct), _ptr(cp), _ptr(cr), _ptr(cs), threads)
+        args = (self._h, t, Q, K, d, _ptr(h), _ptr(Wt), _ptr(rows), _ptr(acc),
+                _ptr(out["tokens"]), _ptr(out["parents"]), _ptr(out["rows"]), _ptr(out["logp"]),
+                cap, _ptr(cc), _ptr(ct), _ptr(cp), _ptr(cr), _ptr(cs), threads)
+        r = self._lib.or_step_mode(*args, m) if m else self._fn("step")(*args)
         if r != 0:
             raise RuntimeError("or_step failed (%d)" % r)
         if candidates:
             out.update(cand_count=cc, cand_tokens=ct, cand_parents=cp, cand_rows=cr, cand_scores=cs)
         return out
 
-    def decode(self, K, q, P, W, bf16, trace=False, threads=1):
-        """Free-running decode.  q [Q][d], P [L-1][V][d], W [L][V][d] (f32)."""
+    def decode(self, K, q, P, W, bf16, trace=False, threads=1, mode="filter_first"):
+        """Free-running decode.  q [Q][d], P [L-1][V][d], W [L][V][d] (f32).
+        mode as for ``step``."""
+        m = _MODES[mode]
+        if m and type(self) is not Trie:
+            raise NotImplementedError("modes other than filter_first: pointer-trie oracle only")
         q = np.ascontiguousarray(q, dtype=np.float32)
         W = np.ascontiguousarray(W, dtype=np.float32)
         Q, d = q.shape
@@ -222,9 +247,9 @@ class Trie:
             tr = [np.zeros((L, R, d), np.float32), np.empty((L, R), np.int64), np.empty((L, R), np.float32),
                   np.empty((L, R), np.int32), np.empty((L, R), np.int32), np.empty((L, R), np.int64),
                   np.empty((L, R), np.float32)]
-        r = self._fn("decode")(self._h, Q, K, d, 1 if bf16 else 0, _ptr(q), _ptr(P), _ptr(W),
-                                _ptr(out["seqs"]), _ptr(out["logp"]), _ptr(out["rows"]),
-                                *[_ptr(a) for a in tr], threads)
+        args = (self._h, Q, K, d, 1 if bf16 else 0, _ptr(q), _ptr(P), _ptr(W),
+                _ptr(out["seqs"]), _ptr(out["logp"]), _ptr(out["rows"]), *[_ptr(a) for a in tr], threads)
+        r = self._lib.or_decode_mode(*args, m) if m else self._fn("decode")(*args)
         if r != 0:
             raise RuntimeError("or_decode failed (%d)" % r)
         if trace:

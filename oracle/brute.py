@@ -39,20 +39,24 @@ def _hidden(s, bf16):
     return [_bf16(v) for v in h] if bf16 else h
 
 
-def item_scores(items, q, P, W, bf16):
+def item_scores(items, q, P, W, bf16, support="valid"):
     """Accumulated score of every item of the catalog along its own path.
 
     items: list of tuples (distinct); q [d]; P [L-1][V][d]; W [L][V][d].
+    support: the tokens the softmax denominator covers, "valid" (the tokens
+    that continue the prefix in the catalog) or "all" (the whole codebook:
+    score first, or no constraint).
     Returns a list of float32-valued floats, one per item."""
     items = [tuple(int(x) for x in it) for it in items]
     L = len(items[0])
+    V = len(W[0])
     out = []
     for it in items:
         s = [float(v) for v in q]
         acc = 0.0
         for t in range(L):
             h = _hidden(s, bf16)
-            valid = valid_tokens(items, it[:t])
+            valid = valid_tokens(items, it[:t]) if support == "valid" else list(range(V))
             z = {v: sum(h[i] * float(W[t][v][i]) for i in range(len(h))) for v in valid}
             m = max(z.values())
             lse = m + math.log(sum(math.exp(z[v] - m) for v in valid))

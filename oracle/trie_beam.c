@@ -43,6 +43,16 @@
  *    bf16).  Output rows at the last step number the catalog items in
  *    lexicographic order.
  *
+ * Variants (the same step with another softmax support or no constraint):
+ *  - Score first: the softmax denominator covers the whole codebook (lse over
+ *    all V tokens of z_v, in double), and only the valid tokens become
+ *    candidates (ZeroGR "Does filtering first change the recommendations?":
+ *    the two orders differ exactly in the denominator).
+ *  - Unconstrained: every token of the codebook is a candidate and the
+ *    denominator covers all of them; no catalog (ZeroGR summary: decoding
+ *    without constraints as the speed reference).  Beams stay "live" at a
+ *    placeholder node, so every output row is 0.
+ *
  * Floating point: double inside, with float32 rounding at exactly the points
  * listed above (logp, cand, s, h), so that the final selection is made on
  * float32 values, as on the device.
@@ -274,16 +284,66 @@ static int cand_cmp(const void* a, const void* b) {
 /* All candidates of one query, sorted best first.  h: [K][d], nodes: [K]
  * (NULL = dead), acc: [K].  Returns the count, or -1 on allocation failure;
  * *out is malloc'ed. */
+/* Softmax support and candidate set of one step. */
+enum { OR_FILTER_FIRST = 0, OR_SCORE_FIRST = 1, OR_UNCONSTRAINED = 2 };
+
+/* log sum_v exp(z_v) over the whole codebook, z_v = <h, W_t[v]> in double. */
+static double lse_all_tokens(const float* hb, const float* Wt, int V, int d, double* zall) {
+    double zmax = -INFINITY;
+    for (int v = 0; v < V; ++v) {
+        const float* w = Wt + (int64_t)v * d;
+        double s = 0.0;
+        for (int i = 0; i < d; ++i) s += (double)hb[i] * (double)w[i];
+        zall[v] = s;
+        if (s > zmax) zmax = s;
+    }
+    double se = 0.0;
+    for (int v = 0; v < V; ++v) se += exp(zall[v] - zmax);
+    return zmax + log(se);
+}
+
 static int64_t query_candidates(const or_trie* T, int t, int K, int d, const float* h, const float* Wt,
-                                const node* const* nodes, const float* acc, cand_t** out) {
+                                const node* const* nodes, const float* acc, int mode, cand_t** out) {
     int64_t total = 0;
     for (int k = 0; k < K; ++k)
-        if (nodes[k]) total += nodes[k]->n;
+        if (nodes[k]) total += mode == OR_UNCONSTRAINED ? T->V : nodes[k]->n;
     cand_t* c = (cand_t*)malloc(sizeof(cand_t) * (size_t)(total ? total : 1));
     double* z = NULL;
     int32_t zcap = 0;
     if (!c) return -1;
     int64_t m = 0;
+    if (mode != OR_FILTER_FIRST) {
+        double* zall = (double*)malloc(sizeof(double) * (size_t)T->V);
+        if (!zall) { free(c); return -1; }
+        for (int k = 0; k < K; ++k) {
+            const node* x = nodes[k];
+            if (!x) continue;
+            const double lse = lse_all_tokens(h + (int64_t)k * d, Wt, T->V, d, zall);
+            if (mode == OR_UNCONSTRAINED) {
+                for (int v = 0; v < T->V; ++v) {
+                    float logp = (float)(zall[v] - lse);
+                    c[m].score = (float)((double)acc[k] + (double)logp);
+                    c[m].parent = k;
+                    c[m].token = v;
+                    c[m].child = T->root;  /* placeholder: the beam stays live, row 0 */
+                    ++m;
+                }
+            } else {
+                for (const node* ch = x->first; ch; ch = ch->next) {
+                    float logp = (float)(zall[ch->token] - lse);
+                    c[m].score = (float)((double)acc[k] + (double)logp);
+                    c[m].parent = k;
+                    c[m].token = ch->token;
+                    c[m].child = ch;
+                    ++m;
+                }
+            }
+        }
+        free(zall);
+        qsort(c, (size_t)m, sizeof(cand_t), cand_cmp);
+        *out = c;
+        return m;
+    }
     for (int k = 0; k < K; ++k) {
         const node* x = nodes[k];
         if (!x || x->n == 0) continue;
@@ -335,12 +395,12 @@ static int64_t query_candidates(const or_trie* T, int t, int K, int d, const flo
  * Optional full candidate lists (any of c_* may be NULL): cand_count[Q] and
  * [Q][cand_cap] arrays, sorted best first.
  * Returns 0, -1 on bad arguments, -2 on allocation failure. */
-int or_step(const or_trie* T, int t, int Q, int K, int d, const float* h, const float* Wt,
-            const int64_t* rows, const float* acc,
-            int32_t* out_tok, int32_t* out_par, int64_t* out_row, float* out_logp,
-            int64_t cand_cap, int64_t* cand_count, int32_t* c_tok, int32_t* c_par, int64_t* c_row, float* c_score,
-            int nthreads) {
-    if (t < 0 || t >= T->L || Q < 0 || K < 1 || d < 1) return -1;
+int or_step_mode(const or_trie* T, int t, int Q, int K, int d, const float* h, const float* Wt,
+                 const int64_t* rows, const float* acc,
+                 int32_t* out_tok, int32_t* out_par, int64_t* out_row, float* out_logp,
+                 int64_t cand_cap, int64_t* cand_count, int32_t* c_tok, int32_t* c_par, int64_t* c_row,
+                 float* c_score, int nthreads, int mode) {
+    if (t < 0 || t >= T->L || Q < 0 || K < 1 || d < 1 || mode < 0 || mode > 2) return -1;
     for (int64_t b = 0; b < (int64_t)Q * K; ++b)
         if (rows[b] >= T->count[t]) return -1;
     int err = 0;
@@ -355,10 +415,10 @@ int or_step(const or_trie* T, int t, int Q, int K, int d, const float* h, const 
         }
         for (int k = 0; k < K; ++k) {
             int64_t r = rows[(int64_t)q * K + k];
-            np[k] = r >= 0 ? T->level[t][r] : NULL;
+            np[k] = r < 0 ? NULL : (mode == OR_UNCONSTRAINED ? T->root : T->level[t][r]);
         }
         cand_t* c = NULL;
-        int64_t m = query_candidates(T, t, K, d, h + (int64_t)q * K * d, Wt, np, acc + (int64_t)q * K, &c);
+        int64_t m = query_candidates(T, t, K, d, h + (int64_t)q * K * d, Wt, np, acc + (int64_t)q * K, mode, &c);
         if (np != nodes) free(np);
         if (m < 0) {
             #pragma omp atomic write
@@ -392,6 +452,15 @@ int or_step(const or_trie* T, int t, int Q, int K, int d, const float* h, const 
     return err;
 }
 
+int or_step(const or_trie* T, int t, int Q, int K, int d, const float* h, const float* Wt,
+            const int64_t* rows, const float* acc,
+            int32_t* out_tok, int32_t* out_par, int64_t* out_row, float* out_logp,
+            int64_t cand_cap, int64_t* cand_count, int32_t* c_tok, int32_t* c_par, int64_t* c_row, float* c_score,
+            int nthreads) {
+    return or_step_mode(T, t, Q, K, d, h, Wt, rows, acc, out_tok, out_par, out_row, out_logp, cand_cap, cand_count,
+                        c_tok, c_par, c_row, c_score, nthreads, OR_FILTER_FIRST);
+}
+
 /* ---- the stand-in model's hidden vector and the full decode --------------- */
 
 static float round_bf16(float v) {
@@ -422,14 +491,14 @@ static void hidden_of_state(const float* s, int d, int bf16, float* h) {
  *   tr_rows_in / tr_acc_in: beam state fed to step t,
  *   tr_tok / tr_par / tr_rows_out / tr_logp_out: step t's outputs.
  * Returns 0, -1 on bad arguments, -2 on allocation failure. */
-int or_decode(const or_trie* T, int Q, int K, int d, int bf16,
-              const float* q, const float* P, const float* W,
-              int32_t* seqs, float* logp, int64_t* rows,
-              float* tr_h, int64_t* tr_rows_in, float* tr_acc_in,
-              int32_t* tr_tok, int32_t* tr_par, int64_t* tr_rows_out, float* tr_logp_out,
-              int nthreads) {
+int or_decode_mode(const or_trie* T, int Q, int K, int d, int bf16,
+                   const float* q, const float* P, const float* W,
+                   int32_t* seqs, float* logp, int64_t* rows,
+                   float* tr_h, int64_t* tr_rows_in, float* tr_acc_in,
+                   int32_t* tr_tok, int32_t* tr_par, int64_t* tr_rows_out, float* tr_logp_out,
+                   int nthreads, int mode) {
     const int L = T->L, V = T->V;
-    if (Q < 0 || K < 1 || d < 1) return -1;
+    if (Q < 0 || K < 1 || d < 1 || mode < 0 || mode > 2) return -1;
     const int64_t R = (int64_t)Q * K;
     int err = 0;
     #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
@@ -465,7 +534,7 @@ int or_decode(const or_trie* T, int Q, int K, int d, int bf16,
                 if (tr_acc_in) tr_acc_in[o] = acc[k];
             }
             cand_t* c = NULL;
-            int64_t m = query_candidates(T, t, K, d, h, W + (int64_t)t * V * d, nodes, acc, &c);
+            int64_t m = query_candidates(T, t, K, d, h, W + (int64_t)t * V * d, nodes, acc, mode, &c);
             if (m < 0) {
                 #pragma omp atomic write
                 err = -2;
@@ -514,6 +583,16 @@ int or_decode(const or_trie* T, int Q, int K, int d, int bf16,
         free(nodes); free(nn); free(acc); free(acc2); free(s); free(s2); free(h); free(seq); free(seq2);
     }
     return err;
+}
+
+int or_decode(const or_trie* T, int Q, int K, int d, int bf16,
+              const float* q, const float* P, const float* W,
+              int32_t* seqs, float* logp, int64_t* rows,
+              float* tr_h, int64_t* tr_rows_in, float* tr_acc_in,
+              int32_t* tr_tok, int32_t* tr_par, int64_t* tr_rows_out, float* tr_logp_out,
+              int nthreads) {
+    return or_decode_mode(T, Q, K, d, bf16, q, P, W, seqs, logp, rows, tr_h, tr_rows_in, tr_acc_in, tr_tok, tr_par,
+                          tr_rows_out, tr_logp_out, nthreads, OR_FILTER_FIRST);
 }
 
 /* Hidden vector of a float32 state vector, as the decode computes it

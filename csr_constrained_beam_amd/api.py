@@ -18,6 +18,8 @@ _SELECTS = {"auto": C.CB_SELECT_AUTO, "lds": C.CB_SELECT_LDS, "radix": C.CB_SELE
 _SELECT_NAMES = {v: k for k, v in _SELECTS.items()}
 _STORES = {"auto": C.CB_STORE_AUTO, "csr": C.CB_STORE_CSR, "bitmap": C.CB_STORE_BITMAP}
 _STORE_NAMES = {v: k for k, v in _STORES.items()}
+_MODES = {"filter_first": 0, "score_first": 1, "unconstrained": 2}
+_MODE_NAMES = {v: k for k, v in _MODES.items()}
 
 
 def _torch():
@@ -151,6 +153,16 @@ class Plan:
         v = ctypes.c_int()
         C.check("cb_get_select", self._lib.cb_get_select(self._h, int(t), ctypes.byref(v)))
         return _SELECT_NAMES[v.value]
+
+    def set_mode(self, mode):
+        """Decoding variant: "filter_first" (default), "score_first" or
+        "unconstrained" (the last two on the dense path only)."""
+        C.check("cb_set_mode", self._lib.cb_set_mode(self._h, _MODES[mode]))
+
+    def get_mode(self):
+        v = ctypes.c_int()
+        C.check("cb_get_mode", self._lib.cb_get_mode(self._h, ctypes.byref(v)))
+        return _MODE_NAMES[v.value]
 
     def set_decode_fusion(self, enable):
         """Persistent decode of the trailing sparse steps: True, False or

@@ -67,6 +67,7 @@ void dev_free(void* p) {
 bool dense_available(const cb_plan* p) { return p->dtype == CB_F32 || (p->d % 64) == 0; }
 
 int32_t resolve_path(const cb_plan* p, int t) {
+    if (p->mode != CB_MODE_FILTER_FIRST) return CB_PATH_DENSE;  // the variants need full score rows
     int32_t f = p->forced[(size_t)t];
     if (f == CB_PATH_DENSE || f == CB_PATH_SPARSE || f == CB_PATH_SPARSE_SPLIT) return f;
     int32_t tu = p->tuned[(size_t)t];
@@ -86,6 +87,7 @@ bool lds_select_ok(const cb_plan* p, int t) {
 }
 
 int32_t resolve_select(const cb_plan* p, int t) {
+    if (p->mode != CB_MODE_FILTER_FIRST) return CB_SELECT_LDS;
     const int32_t f = p->select[(size_t)t];
     if (f == CB_SELECT_LDS || f == CB_SELECT_RADIX) return f;
     const int32_t tu = p->tuned_select[(size_t)t];
@@ -232,7 +234,8 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const vo
     const cb::StepTable& T = idx->steps[(size_t)t];
     const cb::StepDev sd = T.dev(idx->words);
     const int R = Q * p->K;
-    const int Kc = std::min(p->K, std::max(T.S, 1));
+    // survivors per beam: every token is a candidate without a constraint
+    const int Kc = std::min(p->K, p->mode == CB_MODE_UNCONSTRAINED ? idx->V : std::max(T.S, 1));
     hipError_t e;
     if (sel == CB_SELECT_RADIX) return run_step_radix(p, t, Q, path, hidden, Wt, rows, acc, ot, op, orow, ol, s);
     if (path == CB_PATH_SPARSE || path == CB_PATH_SPARSE_SPLIT) {
@@ -269,13 +272,13 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const vo
     {
         ProfMark m(p, s, t, CB_KERNEL_EXPAND_DENSE, expand_threads(sd), R);
         e = launch_beam_expand(sd, true, p->dtype, R, p->K, Kc, p->d, hidden, Wt, p->Z, p->Zp, idx->V, p->n_live,
-                               p->ci_of, rows, acc, p->keys, s);
+                               p->ci_of, rows, acc, p->keys, p->mode, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: beam expansion", e);
     }
     {
         ProfMark m(p, s, t, CB_KERNEL_MERGE, kMergeThreads, Q);
-        e = launch_query_merge(sd, Q, p->K, Kc, p->keys, rows, ot, op, orow, ol, s);
+        e = launch_query_merge(sd, Q, p->K, Kc, p->keys, rows, ot, op, orow, ol, p->mode, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: query merge", e);
     }
@@ -614,7 +617,54 @@ cb_status cb_set_path(cb_plan* p, int32_t t, cb_path path) {
         set_error("cb_set_path: the dense path needs d to be a multiple of 64 for bf16");
         return CB_EUNSUPPORTED;
     }
+    if (p->mode != CB_MODE_FILTER_FIRST && path != CB_PATH_AUTO && path != CB_PATH_DENSE) {
+        set_error("cb_set_path: the score-first and unconstrained variants take the dense path only");
+        return CB_EUNSUPPORTED;
+    }
     p->forced[(size_t)t] = path;
+    return CB_OK;
+}
+
+cb_status cb_set_mode(cb_plan* p, cb_mode mode) {
+    clear_error();
+    if (!p || mode < CB_MODE_FILTER_FIRST || mode > CB_MODE_UNCONSTRAINED) {
+        set_error("cb_set_mode: bad plan or mode");
+        return CB_EINVAL;
+    }
+    if (mode != CB_MODE_FILTER_FIRST) {
+        const cb_index* idx = p->idx;
+        if (p->K > kMaxK || !dense_available(p)) {
+            set_error("cb_set_mode: the variant needs K <= 64 and the dense path (bf16: d a multiple of 64)");
+            return CB_EUNSUPPORTED;
+        }
+        for (int t = 0; t < idx->L; ++t)
+            if (expand_lds_bytes(idx->steps[(size_t)t].S, p->d, true) > (size_t)kMaxLds) {
+                set_error("cb_set_mode: a step's dense expansion does not fit the LDS");
+                return CB_EUNSUPPORTED;
+            }
+        for (int t = 0; t < idx->L; ++t)
+            if (p->forced[(size_t)t] != CB_PATH_AUTO && p->forced[(size_t)t] != CB_PATH_DENSE) {
+                set_error("cb_set_mode: a step is forced to a sparse path");
+                return CB_EUNSUPPORTED;
+            }
+        if (mode == CB_MODE_UNCONSTRAINED &&
+            (p->dtype != CB_BF16 || idx->V > 64 * 64 || idx->V % 4 != 0 || std::min(p->K, idx->V) > p->Kc_max)) {
+            set_error("cb_set_mode: unconstrained decoding needs a bf16 plan, V <= 4096, V a multiple of 4 "
+                      "and min(K, V) survivors per beam");
+            return CB_EUNSUPPORTED;
+        }
+    }
+    p->mode = mode;
+    return CB_OK;
+}
+
+cb_status cb_get_mode(const cb_plan* p, cb_mode* mode) {
+    clear_error();
+    if (!p || !mode) {
+        set_error("cb_get_mode: plan or output is NULL");
+        return CB_EINVAL;
+    }
+    *mode = (cb_mode)p->mode;
     return CB_OK;
 }
 
@@ -627,6 +677,10 @@ cb_status cb_set_select(cb_plan* p, int32_t t, cb_select sel) {
     if (sel == CB_SELECT_LDS && !lds_select_ok(p, t)) {
         set_error("cb_set_select: the LDS selection holds K <= 64 and rows that fit its LDS");
         return CB_ECAPACITY;
+    }
+    if (sel == CB_SELECT_RADIX && p->mode != CB_MODE_FILTER_FIRST) {
+        set_error("cb_set_select: the score-first and unconstrained variants take the LDS selection only");
+        return CB_EUNSUPPORTED;
     }
     if (sel == CB_SELECT_RADIX) {
         DeviceGuard g(p->idx->device);
@@ -736,7 +790,7 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
         }
         const bool path_free = p->forced[(size_t)t] == CB_PATH_AUTO;
         const bool sel_free = p->select[(size_t)t] == CB_SELECT_AUTO;
-        if (reps > 0 && (path_free || sel_free)) {
+        if (reps > 0 && p->mode == CB_MODE_FILTER_FIRST && (path_free || sel_free)) {
             // time every allowed (scoring path, selection) pair on this step's inputs, outputs to scratch
             float best_us[2] = {-1.f, -1.f};  // dense, sparse (either variant): best over the selections
             float best = -1.f;

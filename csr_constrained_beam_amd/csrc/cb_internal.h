@@ -122,6 +122,7 @@ struct cb_plan {
     // cb_tune (fuse_tuned, on until measured), 0 off, 1 on
     int32_t fuse_mode = -1;
     bool fuse_tuned = true;
+    int32_t mode = CB_MODE_FILTER_FIRST;  // softmax support / constraint (cb_set_mode)
     float fuse_us[2] = {-1.f, -1.f};      // measured decode time without / with it
     // kernel timing (cb_profile_start / cb_profile_stop)
     bool prof_on = false;
@@ -164,10 +165,10 @@ size_t split_scores_floats(int V);
 hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R, int K, int Kc, int d,
                               const void* hidden, const void* W, const float* Z, const float* Zp, int64_t ldz,
                               const int32_t* n_live, const int32_t* ci_of, const int32_t* beam_rows,
-                              const float* acc, uint64_t* keys, hipStream_t s);
+                              const float* acc, uint64_t* keys, int mode, hipStream_t s);
 hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uint64_t* keys,
                               const int32_t* beam_rows, int32_t* tok, int32_t* par, int32_t* rows, float* logp,
-                              hipStream_t s);
+                              int mode, hipStream_t s);
 hipError_t launch_decode_init(int Q, int K, int d, cb_dtype dt, const float* q, float* s_out, void* h_out,
                               int32_t* rows, float* acc, hipStream_t st);
 hipError_t launch_hidden_update(int R, int K, int d, cb_dtype dt, const float* s_old, const float* P_t,

@@ -390,7 +390,8 @@ __global__ __launch_bounds__(NT) void k_beam_expand(StepDev st, int K, int Kc, i
                                                     int64_t ldz, const int32_t* __restrict__ n_live,
                                                     const int32_t* __restrict__ ci_of, int split_ok,
                                                     const int32_t* __restrict__ beam_rows,
-                                                    const float* __restrict__ acc, uint64_t* __restrict__ keys_out) {
+                                                    const float* __restrict__ acc, uint64_t* __restrict__ keys_out,
+                                                    int mode) {
     auto split_of = [&](const int32_t* nl) { return split_ok ? gemm_split(*nl, (int)ldz, d) : 1; };
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float red_f[NT / kWave];
@@ -435,7 +436,25 @@ __global__ __launch_bounds__(NT) void k_beam_expand(StepDev st, int K, int Kc, i
         block_scores<DT, NT>(h_s, W, d, tok_s, n, z_s);
     }
     __syncthreads();
-    const float lse = block_lse<NT>(z_s, n, red_f);
+    float lse;
+    if (DENSE && mode == CB_MODE_SCORE_FIRST) {
+        // score first: the denominator covers every column of the score row
+        const int split = split_of(n_live);
+        const float* zb = split == 1 ? Z + (int64_t)b * ldz : Zp + (int64_t)ci_of[b] * ldz;
+        auto zc = [&](int c) {
+            float z = 0.f;
+            for (int x = 0; x < split; ++x) z += zb[(int64_t)x * kSplitRows * ldz + c];
+            return z;
+        };
+        float m = -INFINITY;
+        for (int c = tid; c < (int)ldz; c += NT) m = fmaxf(m, zc(c));
+        m = block_max<NT>(m, red_f);
+        float se = 0.f;
+        for (int c = tid; c < (int)ldz; c += NT) se += expf(zc(c) - m);
+        lse = m + logf(block_sum<NT>(se, red_f));
+    } else {
+        lse = block_lse<NT>(z_s, n, red_f);
+    }
     const int parent = b % K;
     auto keyf = [&](int j) { return make_key(a + (z_s[j] - lse), parent, (int)tok_s[j]); };
     if (n <= Kc) {
@@ -456,7 +475,8 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
                                                        const int32_t* __restrict__ n_live,
                                                        const int32_t* __restrict__ ci_of,
                                                        const int32_t* __restrict__ beam_rows,
-                                                       const float* __restrict__ acc, uint64_t* __restrict__ keys_out) {
+                                                       const float* __restrict__ acc, uint64_t* __restrict__ keys_out,
+                                                       int mode) {
     static_assert(M % 4 == 0, "columns are read 4 at a time");
     __shared__ uint64_t wl_all[4][kWaveListCap];
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
@@ -470,7 +490,7 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
         return;
     }
     const int c0 = lane * M;
-    const uint32_t* rb = st.bits + (int64_t)r * st.words;
+    const uint32_t* rb = mode == CB_MODE_UNCONSTRAINED ? nullptr : st.bits + (int64_t)r * st.words;
     const int split = gemm_split(*n_live, V, d);
     const float* zb = (split == 1 ? Z + (int64_t)b * V : Zp + (int64_t)ci_of[b] * V) + c0;
     float z[M];
@@ -493,27 +513,35 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
     }
     uint32_t on = 0;  // validity of this lane's columns, bit i for column c0 + i (M <= 32 per word)
     uint32_t on_hi = 0;
+    if (mode != CB_MODE_UNCONSTRAINED) {
 #pragma unroll
-    for (int i = 0; i < M; i += 32) {
-        // columns c0+i .. c0+i+31 lie in at most two bitmap words
-        const int c = c0 + i;
-        const int w = c >> 5, sh = c & 31;
-        uint32_t lo = c < V ? rb[w] : 0u;
-        uint32_t hi = (sh && c + 32 - sh < V) ? rb[w + 1] : 0u;
-        uint32_t bits = sh ? ((lo >> sh) | (hi << (32 - sh))) : lo;
-        if (M - i < 32) bits &= (1u << (M - i)) - 1u;
-        if (i == 0) on = bits; else on_hi = bits;
+        for (int i = 0; i < M; i += 32) {
+            // columns c0+i .. c0+i+31 lie in at most two bitmap words
+            const int c = c0 + i;
+            const int w = c >> 5, sh = c & 31;
+            uint32_t lo = c < V ? rb[w] : 0u;
+            uint32_t hi = (sh && c + 32 - sh < V) ? rb[w + 1] : 0u;
+            uint32_t bits = sh ? ((lo >> sh) | (hi << (32 - sh))) : lo;
+            if (M - i < 32) bits &= (1u << (M - i)) - 1u;
+            if (i == 0) on = bits; else on_hi = bits;
+        }
     }
-    auto valid = [&](int i) { return ((i < 32 ? on >> i : on_hi >> (i - 32)) & 1u) != 0; };
+    // candidates: the row's valid tokens, or (no constraint) every column
+    auto valid = [&](int i) {
+        if (mode == CB_MODE_UNCONSTRAINED) return c0 + i < V;
+        return ((i < 32 ? on >> i : on_hi >> (i - 32)) & 1u) != 0;
+    };
+    // softmax support: the candidates, or (score first) every column
+    auto in_lse = [&](int i) { return mode == CB_MODE_FILTER_FIRST ? valid(i) : c0 + i < V; };
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < M; ++i)
-        if (valid(i)) m = fmaxf(m, z[i]);
+        if (in_lse(i)) m = fmaxf(m, z[i]);
     m = wave_max(m);
     float se = 0.f;
 #pragma unroll
     for (int i = 0; i < M; ++i)
-        if (valid(i)) se += expf(z[i] - m);
+        if (in_lse(i)) se += expf(z[i] - m);
     const float lse = m + logf(wave_sum(se));
     const int parent = b % K;
     uint32_t sc[M];
@@ -533,7 +561,8 @@ __global__ __launch_bounds__(256) void k_query_merge_w(StepDev st, int Q, int K,
                                                        const uint64_t* __restrict__ keys,
                                                        const int32_t* __restrict__ beam_rows,
                                                        int32_t* __restrict__ out_tok, int32_t* __restrict__ out_par,
-                                                       int32_t* __restrict__ out_rows, float* __restrict__ out_logp) {
+                                                       int32_t* __restrict__ out_rows, float* __restrict__ out_logp,
+                                                       int mode) {
     __shared__ uint64_t wl_all[4][kWaveListCap];
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     const int q = blockIdx.x * 4 + wv;
@@ -548,7 +577,18 @@ __global__ __launch_bounds__(256) void k_query_merge_w(StepDev st, int Q, int K,
     }
     const uint64_t best = wave_top<M>(K, [&](int i) { return (uint32_t)(kv[i] >> 32); }, [&](int i) { return kv[i]; },
                                       wl_all[wv]);
-    if (lane < K) emit(st, q, K, lane, best, beam_rows, out_tok, out_par, out_rows, out_logp);
+    if (lane < K) {
+        if (mode == CB_MODE_UNCONSTRAINED) {
+            // no catalog: every live beam sits at row 0 of the next table
+            const int64_t o = (int64_t)q * K + lane;
+            out_tok[o] = best ? 65535 - (int)(best & 0xFFFFu) : -1;
+            out_par[o] = best ? 1023 - (int)((best >> 16) & 1023u) : -1;
+            out_rows[o] = best ? 0 : -1;
+            out_logp[o] = best ? score_from_order_bits((uint32_t)(best >> 32)) : -INFINITY;
+        } else {
+            emit(st, q, K, lane, best, beam_rows, out_tok, out_par, out_rows, out_logp);
+        }
+    }
 }
 
 // ---- full-codebook scores of the live beams (dense path) ------------------
@@ -1068,15 +1108,16 @@ hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int K
 hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R, int K, int Kc, int d,
                               const void* hidden, const void* W, const float* Z, const float* Zp, int64_t ldz,
                               const int32_t* n_live, const int32_t* ci_of, const int32_t* beam_rows,
-                              const float* acc, uint64_t* keys, hipStream_t s) {
+                              const float* acc, uint64_t* keys, int mode, hipStream_t s) {
     if (R <= 0) return hipSuccess;
     const int split_ok = dt == CB_BF16 ? 1 : 0;
-    if (dense && split_ok && st.store == CB_STORE_BITMAP && ldz <= 64 * kWave && ldz % 4 == 0) {
+    if (dense && split_ok && (st.store == CB_STORE_BITMAP || mode == CB_MODE_UNCONSTRAINED) &&
+        ldz <= 64 * kWave && ldz % 4 == 0) {
         const int M = (int)((ldz + kWave - 1) / kWave);
         const dim3 grid((R + 3) / 4);
 #define CB_EXPAND_BM(MV)                                                                                        \
     hipLaunchKernelGGL((k_expand_bitmap<MV>), grid, dim3(256), 0, s, st, R, K, Kc, (int)ldz, d, Z, Zp, n_live, \
-                       ci_of, beam_rows, acc, keys)
+                       ci_of, beam_rows, acc, keys, mode)
         if (M <= 4) CB_EXPAND_BM(4);
         else if (M <= 8) CB_EXPAND_BM(8);
         else if (M <= 16) CB_EXPAND_BM(16);
@@ -1089,7 +1130,7 @@ hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R,
 #define CB_EXPAND(DT, DENSE)                                                                                     \
     hipLaunchKernelGGL((k_beam_expand<DT, DENSE, kExpandThreads>), dim3(R), dim3(kExpandThreads), lay.total, s, \
                        st, K, Kc, d, (const DT*)hidden, (const DT*)W, Z, Zp, ldz, n_live, ci_of, split_ok,        \
-                       beam_rows, acc, keys)
+                       beam_rows, acc, keys, mode)
     if (dt == CB_BF16) {
         if (dense) CB_EXPAND(uint16_t, true); else CB_EXPAND(uint16_t, false);
     } else {
@@ -1101,13 +1142,13 @@ hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R,
 
 hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uint64_t* keys,
                               const int32_t* beam_rows, int32_t* tok, int32_t* par, int32_t* rows, float* logp,
-                              hipStream_t s) {
+                              int mode, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
     const int M = (K * Kc + kWave - 1) / kWave;
     const dim3 grid((Q + 3) / 4);
 #define CB_MERGE(MV)                                                                                      \
     hipLaunchKernelGGL((k_query_merge_w<MV>), grid, dim3(256), 0, s, st, Q, K, Kc, keys, beam_rows, tok, par, \
-                       rows, logp)
+                       rows, logp, mode)
     if (M <= 1) CB_MERGE(1);
     else if (M <= 4) CB_MERGE(4);
     else if (M <= 16) CB_MERGE(16);

@@ -76,6 +76,16 @@ typedef enum { CB_PATH_AUTO = 0, CB_PATH_DENSE = 1, CB_PATH_SPARSE = 2, CB_PATH_
  * for the first levels, CSR below).  AUTO picks the smaller of the two. */
 typedef enum { CB_STORE_AUTO = 0, CB_STORE_CSR = 1, CB_STORE_BITMAP = 2 } cb_store;
 
+/* Decoding variant of a plan (ZeroGR, "Does filtering first change the
+ * recommendations?"; the summary's unconstrained speed reference):
+ *   CB_MODE_FILTER_FIRST   softmax over each beam's valid tokens (default);
+ *   CB_MODE_SCORE_FIRST    softmax over the whole codebook, then only the
+ *                          valid tokens are candidates;
+ *   CB_MODE_UNCONSTRAINED  every token of the codebook is a candidate and
+ *                          the softmax covers all of them; the index only
+ *                          sets L and V, and every live beam's row is 0. */
+typedef enum { CB_MODE_FILTER_FIRST = 0, CB_MODE_SCORE_FIRST = 1, CB_MODE_UNCONSTRAINED = 2 } cb_mode;
+
 /* Per-query top-K of a step (the segmented top-K with the (score desc,
  * parent asc, token asc) tie-break; ZeroGR "The pipeline", FlashTrie App. D.3
  * block merge).  LDS: the query's best keys are kept by one wavefront in
@@ -170,6 +180,20 @@ cb_status cb_set_select(cb_plan* plan, int32_t t, cb_select select);
 
 /* The selection step t will use (never CB_SELECT_AUTO). */
 cb_status cb_get_select(const cb_plan* plan, int32_t t, cb_select* select);
+
+/* Set the decoding variant.  The score-first and unconstrained variants
+ * need every step's full score row: all steps then take the dense path with
+ * the LDS selection (cb_get_path reports CB_PATH_DENSE, cb_tune has nothing
+ * to choose, sparse paths and the radix selection return CB_EUNSUPPORTED).
+ * Errors: CB_EINVAL (unknown mode); CB_EUNSUPPORTED for K > 64, for a bf16
+ * plan with d not a multiple of 64, for a step whose dense expansion does not
+ * fit the LDS, and, unconstrained, for an f32 plan, V > 4096, V not a
+ * multiple of 4, or min(K, V) beyond the plan's per-beam survivor count.
+ * Synchronous with respect to the host. */
+cb_status cb_set_mode(cb_plan* plan, cb_mode mode);
+
+/* The plan's decoding variant. */
+cb_status cb_get_mode(const cb_plan* plan, cb_mode* mode);
 
 /* Force the scoring path of step t (tests run both ways).  CB_PATH_AUTO
  * restores the measured or default choice.  CB_PATH_SPARSE_SPLIT may allocate

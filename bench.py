@@ -55,6 +55,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU oracle time budget")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--path", default="tuned", choices=["tuned", "auto", "dense", "sparse"])
+    ap.add_argument("--paths", default=None,
+                    help="comma-separated path per step (dense/sparse/sparse_split), no tuning: replays a tuned "
+                         "choice without the tuning launches (profiler runs)")
+    ap.add_argument("--mode", default="filter_first", choices=["filter_first", "score_first", "unconstrained"],
+                    help="decoding variant (the last two run the dense path)")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 256 MiB five times (counter calibration)")
@@ -103,7 +108,7 @@ def run_sweep(args):
         with tempfile.NamedTemporaryFile(suffix=".json", delete=False) as f:
             out = f.name
         cmd = [sys.executable, os.path.abspath(__file__), "--config", args.config, "--no-cpu", "--steps",
-               str(args.steps), "--warmup", str(args.warmup), "--json-out", out]
+               str(args.steps), "--warmup", str(args.warmup), "--json-out", out, "--mode", args.mode]
         for k, v in point.items():
             cmd += ["--" + k, str(v)]
         log("sweep %s: %s" % (args.sweep, point))
@@ -178,10 +183,17 @@ def main():
     q = torch.from_numpy(dense["q"]).to(dev)
     P = torch.from_numpy(dense["P"]).to(dev)
     plan = idx.plan(cfg.Q, cfg.K, cfg.d, cfg.dtype)
+    if args.mode != "filter_first":
+        plan.set_mode(args.mode)
 
     # pre-measured path switch (warm-up decode trying both paths per step)
     tune = None
-    if args.path == "tuned":
+    if args.paths:
+        fixed = args.paths.split(",")
+        assert len(fixed) == cfg.L, "--paths needs one path per step"
+        for t, pth in enumerate(fixed):
+            plan.set_path(t, pth)
+    elif args.path == "tuned":
         tune = plan.tune(q, P, W, reps=5)
     elif args.path in ("dense", "sparse"):
         for t in range(cfg.L):
@@ -235,6 +247,8 @@ def main():
         toks = set()
         for i, b in enumerate(live):
             tk, _ = hidx.row(t, int(rows_np[t][b]))
+            if args.mode == "unconstrained":  # every token is a candidate
+                tk = np.arange(V)
             fan[i] = len(tk)
             toks.update(tk.tolist())
         S = info[t]["max_fanout"]
@@ -315,6 +329,26 @@ def main():
     torch.cuda.synchronize()
     ms_per_pass = e0.elapsed_time(e1) / args.steps
 
+    # score first against filter first on the same batch: share of each
+    # query's final items that both orders return (ZeroGR's overlap measure)
+    overlap = None
+    if args.mode == "score_first":
+        ff = idx.plan(cfg.Q, cfg.K, cfg.d, cfg.dtype)
+        a = ff.decode(q, P, W)
+        b = plan.decode(q, P, W)
+        torch.cuda.synchronize()
+        sa, ra = a["seqs"].cpu().numpy(), a["rows"].cpu().numpy()
+        sb, rb_ = b["seqs"].cpu().numpy(), b["rows"].cpu().numpy()
+        fr = []
+        for qi in range(Q):
+            sl = slice(qi * K, (qi + 1) * K)
+            A = {int(x) for x in ra[sl] if x >= 0}
+            B = {int(x) for x in rb_[sl] if x >= 0}
+            fr.append(len(A & B) / max(1, len(A)))
+        overlap = {"mean": float(np.mean(fr)), "min": float(np.min(fr))}
+        del ff
+        log("score-first vs filter-first item overlap: mean %.4f, min %.4f" % (overlap["mean"], overlap["min"]))
+
     # per-kernel durations: HIP events around every launch, eager passes
     plan.profile_start(capacity=args.steps * L * 10 + 16)
     for _ in range(args.steps):
@@ -369,16 +403,17 @@ def main():
         T = oracle.SortedRange(items, cfg.V) if kind == "sorted-range" else oracle.Trie(items, cfg.V)
         trie_s = time.time() - t0
         bf16 = cfg.dtype == "bf16"
-        r0 = T.decode(K, dense["q"], dense["P"], dense["W"], bf16=bf16, trace=True, threads=threads)
+        mkw = {} if args.mode == "filter_first" else {"mode": args.mode}
+        r0 = T.decode(K, dense["q"], dense["P"], dense["W"], bf16=bf16, trace=True, threads=threads, **mkw)
         cexp = 0
         for t in range(L):
             for r in r0["trace_rows_in"][t]:
                 if r >= 0:
-                    cexp += len(T.children_of_row(t, int(r))[0])
+                    cexp += V if args.mode == "unconstrained" else len(T.children_of_row(t, int(r))[0])
         reps, el = 0, 0.0
         while el < args.cpu_seconds and reps < 1000:
             t0 = time.time()
-            T.decode(K, dense["q"], dense["P"], dense["W"], bf16=bf16, threads=threads)
+            T.decode(K, dense["q"], dense["P"], dense["W"], bf16=bf16, threads=threads, **mkw)
             el += time.time() - t0
             reps += 1
         cpu = {"value": cexp * reps / el, "unit": "beam-expansions/s", "cores": threads, "kind": "oracle",
@@ -406,6 +441,7 @@ def main():
                         % (cfg.name, cfg.n_items, cfg.L, cfg.V, cfg.d, cfg.dtype, cfg.Q, cfg.K),
             "seed": cfg.seed,
             "step": "one teacher-forced pass over all %d decoding steps" % cfg.L,
+            "mode": args.mode,
             "graph": graph is not None,
             "paths": paths,
         },
@@ -417,6 +453,7 @@ def main():
         "decode_persistent_from_step": tail[0] if tail else None,
         "decode_persistent_us": tail_recs[0]["us"] if tail_recs else None,
         "decode_persistent_phases": phases,
+        "overlap_with_filter_first": overlap,
         "index": {"build_s": round(build_s, 2), "bytes": sum(i["bytes"] for i in info),
                   "rows": [i["n_rows"] for i in info], "storage": [i["storage"] for i in info]},
         "per_step": steps,

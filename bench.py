@@ -245,27 +245,33 @@ def main():
         live = np.nonzero(rows_np[t] >= 0)[0]
         fan = np.zeros(len(live), np.int64)
         toks = set()
+        toks_scored = set()  # sparse paths read W_t rows only for rows of two or more tokens
         for i, b in enumerate(live):
             tk, _ = hidx.row(t, int(rows_np[t][b]))
             if args.mode == "unconstrained":  # every token is a candidate
                 tk = np.arange(V)
             fan[i] = len(tk)
             toks.update(tk.tolist())
+            if len(tk) > 1:
+                toks_scored.update(tk.tolist())
         S = info[t]["max_fanout"]
         Kc = min(K, max(S, 1))
         n_exp = int(fan.sum())
+        # a row with one valid token has log-softmax 0 whatever its score: the
+        # sparse paths read neither its hidden vector nor its W_t row
+        n_scored = int(fan[fan > 1].sum())
+        live_scored = int((fan > 1).sum())
         chunks = int(((fan + 63) // 64).sum())
         idx_bytes = len(live) * 8 + (n_exp * 2 if info[t]["storage"] == "csr" else len(live) * words * 4)
         state_bytes = R * 8 + R * Kc * 8
-        w_bytes = len(live) * d * es + len(toks) * d * es  # hidden vectors and distinct W_t rows
+        w_bytes = live_scored * d * es + len(toks_scored) * d * es  # hidden vectors and distinct W_t rows
         steps.append({
             "t": t, "path": paths[t], "storage": info[t]["storage"], "live_beams": int(len(live)),
             "expansions": n_exp, "max_fanout": S, "mean_fanout": float(fan.mean()) if len(fan) else 0.0,
             "valid_fraction": n_exp / max(1, len(live) * V), "distinct_tokens": len(toks),
             "bytes": {
-                "step_query": (R * 8 + idx_bytes + len(live) * d * es + len(toks) * d * es + R * 16
-                               + min(R, n_exp) * 8),
-                "expand_sparse": state_bytes + idx_bytes + len(live) * d * es + len(toks) * d * es,
+                "step_query": R * 8 + idx_bytes + w_bytes + R * 16 + min(R, n_exp) * 8,
+                "expand_sparse": state_bytes + idx_bytes + w_bytes,
                 "expand_dense": state_bytes + idx_bytes + n_exp * 4,
                 "merge": Q * K * Kc * 8 + R * 4 + R * 16 + min(R, n_exp) * 8,
                 "gemm_" + cfg.dtype: R * d * es + V * d * es + R * V * 4,
@@ -277,8 +283,8 @@ def main():
                 "radix_collect": n_exp * 8,
                 "radix_sort": min(n_exp, K) * 8 + R * 24,
             },
-            "flops": {"gemm_" + cfg.dtype: 2 * len(live) * V * d, "expand_sparse": 2 * d * n_exp,
-                      "step_query": 2 * d * n_exp, "radix_score_sparse": 2 * d * n_exp},
+            "flops": {"gemm_" + cfg.dtype: 2 * len(live) * V * d, "expand_sparse": 2 * d * n_scored,
+                      "step_query": 2 * d * n_scored, "radix_score_sparse": 2 * d * n_scored},
             "selection": plan.get_select(t),
         })
     expansions = sum(s["expansions"] for s in steps)

@@ -343,7 +343,7 @@ __device__ __forceinline__ void wave_append(bool p, uint64_t v, uint64_t* keys, 
 
 // The Kc (<= 64) largest of the m keys in the LDS list keys[0..m), descending,
 // written by wave 0 to out[0..Kc) (0-padded); out is complete after the next
-// barrier.  Up to 64 keys: one wave sorts them.  Up to NT: only the
+// barrier.  Keys are unique and nonzero.  Up to 64 keys: one wave ranks them.  Up to NT: only the
 // ceil(m / 64) waves that hold keys sort and merge them as a tree.  More: the
 // threshold selection.  stage: LDS [NT]; list: LDS int [m].  All threads call.
 template <int NT>
@@ -352,6 +352,24 @@ __device__ __forceinline__ void block_select_list(int m, int Kc, const uint64_t*
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
     if (m > NT) {
         block_select_top<NT>(m, Kc, [&](int j) { return keys[j]; }, out, stage, list, red_i, bcast);
+        return;
+    }
+    if (m <= kWave) {
+        // one key per lane of wave 0; a key's rank is the number of larger keys
+        // (keys are unique and nonzero), so it lands directly in its output
+        // slot: m independent compares instead of a sorting network
+        if (w == 0) {
+            const uint64_t v = lane < m ? keys[lane] : 0ull;
+            const uint32_t vh = (uint32_t)(v >> 32), vl = (uint32_t)v;
+            int rank = 0;
+            for (int j = 0; j < m; ++j) {
+                const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)vh, j) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane((int)vl, j);
+                rank += o > v;
+            }
+            if (lane < m && rank < Kc) out[rank] = v;
+            if (lane >= m && lane < Kc) out[lane] = 0ull;
+        }
         return;
     }
     const int nw = (m + kWave - 1) / kWave;

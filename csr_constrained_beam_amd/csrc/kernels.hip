@@ -258,7 +258,10 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const bool ready = pre && small[u] && n[u] > kPreMin;
-            dots[u] = small[u] && !ready;
+            // a row with one valid token: its log-softmax is exactly 0 whatever
+            // its score, so neither the hidden vector nor the W_t row is read
+            dots[u] = small[u] && !ready && n[u] > 1;
+            if (small[u] && n[u] == 1) z[u] = 0.f;
             if (ready && lane < n[u])
                 z[u] = __uint_as_float((uint32_t)(pre[(int64_t)q * pre_cap + pre_off[(int64_t)q * (K + 1) + kk[u]] +
                                                       lane] >> 32));
@@ -416,10 +419,13 @@ __global__ __launch_bounds__(NT) void k_beam_expand(StepDev st, int K, int Kc, i
     const uint32_t e0 = st.row_ptr[r];
     const int n = (int)(st.row_ptr[r + 1] - e0);
     block_fill_tokens<NT>(st, r, e0, n, tok_s, red_i);
-    if (!DENSE)
+    if (!DENSE && n > 1)
         for (int i = tid; i < d; i += NT) h_s[i] = to_f32(hidden[(int64_t)b * d + i]);
     __syncthreads();
-    if (DENSE) {
+    if (!DENSE && n == 1) {
+        // one valid token: log-softmax 0 whatever the score (no reads)
+        if (tid == 0) z_s[0] = 0.f;
+    } else if (DENSE) {
         const int split = split_of(n_live);
         if (split == 1) {
             const float* zb = Z + (int64_t)b * ldz;

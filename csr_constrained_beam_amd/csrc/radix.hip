@@ -260,12 +260,15 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
         const int j0 = (c - ho_s[k]) * kWCH;
         const int cnt = min(kWCH, n - j0);
         if (tid < cnt) tok_s[tid] = (uint16_t)nth_token(st, r, e0, j0 + tid);
-        if (!DENSE && staged != k) {
+        if (!DENSE && staged != k && n > 1) {
             for (int i = tid; i < d; i += kWThreads) h_s[i] = to_f32(hidden[b * d + i]);
             staged = k;
         }
         __syncthreads();
-        if (DENSE) {
+        if (!DENSE && n == 1) {
+            // one valid token: log-softmax 0 whatever the score (no reads)
+            if (tid == 0) z_s[0] = 0.f;
+        } else if (DENSE) {
             if (tid < cnt) {
                 const int v = tok_s[tid];
                 float z = 0.f;

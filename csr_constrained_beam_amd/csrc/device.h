@@ -17,6 +17,8 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kSmallRow = 64;  // rows up to this many tokens take the one-wave path
 constexpr int kPreMin = 16;    // with scores computed apart: rows above this many tokens read them
+constexpr int kMidRow = 4;     // rows above this many tokens (up to kSmallRow) are scored by the whole block
+constexpr int kMidTok = 4;     // tokens per task of that block-wide scoring
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
@@ -114,6 +116,25 @@ __device__ __forceinline__ float wave_max(float v) {
     for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, lane_xor(v, o));
     return v;
 }
+
+// Max / sum over the aligned groups of w lanes (w a power of two <= 64,
+// uniform over the wave): only the butterfly steps below w.  When the lanes
+// from n <= w on hold the neutral value, lanes 0..w-1 get the result of all 64
+// lanes, in the same order (the skipped steps would only add the neutral
+// value), so a row of n tokens needs log2(w) steps instead of six.
+__device__ __forceinline__ float wave_max_w(float v, int w) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        if (o < w) v = fmaxf(v, lane_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum_w(float v, int w) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        if (o < w) v += lane_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ int pow2_at_least(int n) { return n <= 1 ? 1 : 1 << (32 - __clz(n - 1)); }
 
 // Inclusive prefix sum over the wave (butterfly: after the step with distance
 // o every lane knows the total of its aligned block of 2o lanes).

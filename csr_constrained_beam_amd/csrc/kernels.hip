@@ -153,7 +153,7 @@ __host__ __device__ inline ExpandLds expand_lds(int S, int d, bool dense, int NT
 }
 
 struct QueryLds {
-    int qkeys, stage, list, z, h, tok, tokq, total;
+    int qkeys, stage, list, z, h, tok, tokq, zmid, total;
 };
 __host__ __device__ inline QueryLds query_lds(int S, int K, int Kc, int d, int NT) {
     QueryLds l;
@@ -165,7 +165,8 @@ __host__ __device__ inline QueryLds query_lds(int S, int K, int Kc, int d, int N
     l.h = l.z + ((S * 4 + 15) & ~15);
     l.tok = l.h + ((d * 4 + 15) & ~15);
     l.tokq = l.tok + ((S * 2 + 15) & ~15);
-    l.total = l.tokq + ((K * kWave * 2 + 15) & ~15);
+    l.zmid = l.tokq + ((K * kWave * 2 + 15) & ~15);
+    l.total = l.zmid + (S > kMidRow ? K * kWave * 4 : 0);
     return l;
 }
 
@@ -195,6 +196,9 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
     __shared__ int n_s[kWave];
     __shared__ int nbig;
     __shared__ int big[kWave];
+    __shared__ int nmid;              // rows scored by the whole block (phase 1b)
+    __shared__ int mid[kWave];
+    __shared__ int moff[kWave + 1];   // their first task
     __shared__ int ncand;             // keys in the candidate list qkeys
     __shared__ uint64_t slot[kWave];  // survivors of one wide row
     const QueryLds lay = query_lds(st.S, K, Kc, d, NT);
@@ -205,11 +209,13 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
     float* h_s = reinterpret_cast<float*>(smem + lay.h);
     uint16_t* tok_s = reinterpret_cast<uint16_t*>(smem + lay.tok);
     uint16_t* tokq = reinterpret_cast<uint16_t*>(smem + lay.tokq);
+    float* zmid = reinterpret_cast<float*>(smem + lay.zmid);
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
     constexpr int NW = NT / kWave;
     if (tid == 0) {
         nbig = 0;
+        nmid = 0;
         ncand = 0;
     }
     __syncthreads();
@@ -220,7 +226,7 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
         int kk[2], tk[2], n[2];
         int64_t b[2];
         float a[2];
-        bool small[2];
+        bool small[2], midr[2];
         uint32_t e0[2];
         int32_t r[2];
 #pragma unroll
@@ -230,25 +236,37 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
             r[u] = kk[u] < K ? rows_q[kk[u]] : -1;
             a[u] = kk[u] < K ? acc_q[kk[u]] : -INFINITY;
         }
+        // every global load of both beams is issued before the LDS bookkeeping
+        // (atomics), which the compiler does not move loads across: the two
+        // chains row -> row_ptr -> token then overlap
+        bool live[2];
+        int f0[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const bool live = kk[u] < K && beam_live(st, r[u], a[u]);
-            e0[u] = live ? st.row_ptr[r[u]] : 0u;
-            n[u] = live ? (int)(st.row_ptr[r[u] + 1] - e0[u]) : 0;
-            const int f0 = live && st.tok0 ? (int)st.tok0[r[u]] : 0;  // in flight with row_ptr
-            small[u] = live && n[u] <= kSmallRow && st.store == CB_STORE_CSR;
-            if (kk[u] < K) {
-                if (live) {
-                    if (lane == 0) {
-                        r_s[kk[u]] = r[u];
-                        a_s[kk[u]] = a[u];
-                        e0_s[kk[u]] = e0[u];
-                        n_s[kk[u]] = small[u] ? n[u] : -1 - n[u];
-                    }
-                    if (!small[u] && lane == 0) big[atomicAdd(&nbig, 1)] = kk[u];
+            live[u] = kk[u] < K && beam_live(st, r[u], a[u]);
+            e0[u] = live[u] ? st.row_ptr[r[u]] : 0u;
+            n[u] = live[u] ? (int)(st.row_ptr[r[u] + 1] - e0[u]) : 0;
+            f0[u] = live[u] && st.tok0 ? (int)st.tok0[r[u]] : 0;  // in flight with row_ptr
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            small[u] = live[u] && n[u] <= kSmallRow && st.store == CB_STORE_CSR;
+            // rows of more than kMidRow tokens (scores not computed apart) go to phase 1b
+            midr[u] = small[u] && n[u] > kMidRow && !(pre && n[u] > kPreMin);
+            tk[u] = small[u] && lane < n[u] ? (lane == 0 && st.tok0 ? f0[u] : (int)st.tok[e0[u] + lane]) : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (midr[u] && lane == 0) mid[atomicAdd(&nmid, 1)] = kk[u];
+            if (live[u]) {
+                if (lane == 0) {
+                    r_s[kk[u]] = r[u];
+                    a_s[kk[u]] = a[u];
+                    e0_s[kk[u]] = e0[u];
+                    n_s[kk[u]] = small[u] ? n[u] : -1 - n[u];
                 }
+                if (!small[u] && lane == 0) big[atomicAdd(&nbig, 1)] = kk[u];
             }
-            tk[u] = small[u] && lane < n[u] ? (lane == 0 && st.tok0 ? f0 : (int)st.tok[e0[u] + lane]) : 0;
             if (small[u] && lane < n[u]) tokq[kk[u] * kWave + lane] = (uint16_t)tk[u];
         }
         if (!small[0] && !small[1]) continue;
@@ -260,7 +278,7 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
             const bool ready = pre && small[u] && n[u] > kPreMin;
             // a row with one valid token: its log-softmax is exactly 0 whatever
             // its score, so neither the hidden vector nor the W_t row is read
-            dots[u] = small[u] && !ready && n[u] > 1;
+            dots[u] = small[u] && !ready && n[u] > 1 && !midr[u];
             if (small[u] && n[u] == 1) z[u] = 0.f;
             if (ready && lane < n[u])
                 z[u] = __uint_as_float((uint32_t)(pre[(int64_t)q * pre_cap + pre_off[(int64_t)q * (K + 1) + kk[u]] +
@@ -312,18 +330,112 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            if (!small[u]) continue;
+            if (!small[u] || midr[u]) continue;
             const bool on = lane < n[u];
-            const float m = wave_max(on ? z[u] : -INFINITY);
-            const float se = wave_sum(on ? expf(z[u] - m) : 0.f);
-            const float lse = m + logf(se);
-            uint64_t key = on ? make_key(a[u] + (z[u] - lse), kk[u], tk[u]) : 0ull;
+            uint64_t key;
+            if (n[u] == 1) {
+                // one valid token: log-softmax exactly 0, no reductions
+                key = on ? make_key(a[u] + 0.f, kk[u], tk[u]) : 0ull;
+            } else {
+                const int w = pow2_at_least(n[u]);
+                const float m = wave_max_w(on ? z[u] : -INFINITY, w);
+                const float se = wave_sum_w(on ? expf(z[u] - m) : 0.f, w);
+                const float lse = m + logf(se);
+                key = on ? make_key(a[u] + (z[u] - lse), kk[u], tk[u]) : 0ull;
+            }
             if (n[u] > Kc) key = wave_sort_desc(key);
             // the beam's best min(n, Kc) join the query's candidate list
             wave_append(lane < min(n[u], Kc), key, qkeys, &ncand);
         }
     }
     __syncthreads();
+
+    // phase 1b: rows of kMidRow+1 .. kSmallRow tokens, scored by the whole
+    // block.  Their tokens form a flat list of tasks of kMidTok consecutive
+    // tokens of one row; each wave takes two tasks at a time, so every wave
+    // has 2 * kMidTok W_t rows in flight (a wave working through one such row
+    // alone would wait a global round trip for every few tokens).  The dot
+    // products are summed in the same order as in phase 1.
+    const int nm = nmid;
+    if (nm > 0) {
+        if (wv == 0) {
+            const int c = lane < nm ? (n_s[mid[lane]] + kMidTok - 1) / kMidTok : 0;
+            const int incl = wave_inclusive_scan(c);
+            if (lane < nm) moff[lane + 1] = incl;
+            if (lane == 0) moff[0] = 0;
+        }
+        __syncthreads();
+        const int ntask = moff[nm];
+        for (int t0 = wv; t0 < ntask; t0 += 2 * NW) {
+            int kq[2], j0[2], nn[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int task = t0 + u * NW;
+                int lo = 0;
+                if (task < ntask) {  // the row whose tasks hold this one: last i with moff[i] <= task
+                    int hi = nm;
+                    while (hi - lo > 1) {
+                        const int md = (lo + hi) >> 1;
+                        if (moff[md] <= task) lo = md; else hi = md;
+                    }
+                }
+                kq[u] = task < ntask ? mid[lo] : 0;
+                j0[u] = task < ntask ? (task - moff[lo]) * kMidTok : 0;
+                nn[u] = task < ntask ? min(kMidTok, n_s[kq[u]] - j0[u]) : 0;
+            }
+            float hr[2][CH][8];
+            Raw8<DT> w8[2][kMidTok][CH];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const int i = c * kWave * 8 + lane * 8;
+                    if (nn[u] > 0 && i < d) load8(hidden + ((int64_t)q * K + kq[u]) * d + i, hr[u][c]);
+                    else
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) hr[u][c][e] = 0.f;
+                }
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int jj = 0; jj < kMidTok; ++jj) {
+                    const bool on = jj < nn[u];
+                    const int tkn = on ? (int)tokq[kq[u] * kWave + j0[u] + jj] : 0;
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) {
+                        const int i = c * kWave * 8 + lane * 8;
+                        if (on && i < d) w8[u][jj][c].load(W + (int64_t)tkn * d + i);
+                        else w8[u][jj][c].zero();
+                    }
+                }
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int jj = 0; jj < kMidTok; ++jj) {
+                    float sv = 0.f;
+#pragma unroll
+                    for (int c = 0; c < CH; ++c) sv = w8[u][jj][c].dot(hr[u][c], sv);
+                    const float t = wave_sum(sv);
+                    if (lane == 0 && jj < nn[u]) zmid[kq[u] * kWave + j0[u] + jj] = t;
+                }
+        }
+        __syncthreads();
+        // phase 1c: softmax and the beam's best min(n, Kc) keys, one wave per row
+        for (int i = wv; i < nm; i += NW) {
+            const int k = mid[i], n = n_s[k];
+            const bool on = lane < n;
+            const float z = on ? zmid[k * kWave + lane] : -INFINITY;
+            const int tk = on ? (int)tokq[k * kWave + lane] : 0;
+            const int w = pow2_at_least(n);
+            const float m = wave_max_w(z, w);
+            const float se = wave_sum_w(on ? expf(z - m) : 0.f, w);
+            const float lse = m + logf(se);
+            uint64_t key = on ? make_key(a_s[k] + (z - lse), k, tk) : 0ull;
+            if (n > Kc) key = wave_sort_desc(key);
+            wave_append(lane < min(n, Kc), key, qkeys, &ncand);
+        }
+        __syncthreads();
+    }
 
     // phase 2: wide rows and bitmap rows, the whole block per beam
     const int nb = nbig;

@@ -29,6 +29,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// e^x for the terms of the softmax sums (x <= 0, or -inf): the hardware
+// base-2 exponential of x * log2(e).  Relative error ~1e-7 (the rounding of
+// the product), exact at x = 0, 0 at -inf; one multiply and one transcendental
+// instead of the library's range reduction.
+__device__ __forceinline__ float exp_sm(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 __device__ __forceinline__ uint32_t score_order_bits(float f) {
     uint32_t u = __float_as_uint(f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -245,6 +251,19 @@ __device__ uint64_t wave_top(int Kc, ScoreF score, KeyF key, uint64_t* wl) {
         }
         wave_lds_sync();
         const int w = min(kWaveListCap, total - s0);
+        if (total <= kWave) {
+            // a single window: each key's rank (number of larger keys; keys
+            // are unique) is its output lane, placed through the LDS list
+            const uint64_t v = lane < w ? wl[lane] : 0ull;
+            int rank = 0;
+            for (int j = 0; j < w; ++j) rank += wl[j] > v;  // broadcast reads
+            wave_lds_sync();
+            if (lane < w) wl[rank] = v;
+            wave_lds_sync();
+            best = lane < w ? wl[lane] : 0ull;
+            wave_lds_sync();
+            break;
+        }
         for (int c0 = 0; c0 < w; c0 += kWave) {
             const uint64_t v = wave_sort_desc(c0 + lane < w ? wl[c0 + lane] : 0ull);
             best = first ? v : wave_merge_top(best, v);
@@ -381,13 +400,8 @@ __device__ __forceinline__ void block_select_list(int m, int Kc, const uint64_t*
         // slot: m independent compares instead of a sorting network
         if (w == 0) {
             const uint64_t v = lane < m ? keys[lane] : 0ull;
-            const uint32_t vh = (uint32_t)(v >> 32), vl = (uint32_t)v;
             int rank = 0;
-            for (int j = 0; j < m; ++j) {
-                const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)vh, j) << 32) |
-                                   (uint32_t)__builtin_amdgcn_readlane((int)vl, j);
-                rank += o > v;
-            }
+            for (int j = 0; j < m; ++j) rank += keys[j] > v;  // broadcast reads
             if (lane < m && rank < Kc) out[rank] = v;
             if (lane >= m && lane < Kc) out[lane] = 0ull;
         }
@@ -539,7 +553,7 @@ __device__ float block_lse(const float* z_s, int n, float* red_f) {
     for (int j = threadIdx.x; j < n; j += NT) m = fmaxf(m, z_s[j]);
     m = block_max<NT>(m, red_f);
     float se = 0.f;
-    for (int j = threadIdx.x; j < n; j += NT) se += expf(z_s[j] - m);
+    for (int j = threadIdx.x; j < n; j += NT) se += exp_sm(z_s[j] - m);
     se = block_sum<NT>(se, red_f);
     return m + logf(se);
 }

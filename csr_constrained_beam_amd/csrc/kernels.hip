@@ -339,7 +339,7 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
             } else {
                 const int w = pow2_at_least(n[u]);
                 const float m = wave_max_w(on ? z[u] : -INFINITY, w);
-                const float se = wave_sum_w(on ? expf(z[u] - m) : 0.f, w);
+                const float se = wave_sum_w(on ? exp_sm(z[u] - m) : 0.f, w);
                 const float lse = m + logf(se);
                 key = on ? make_key(a[u] + (z[u] - lse), kk[u], tk[u]) : 0ull;
             }
@@ -428,7 +428,7 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
             const int tk = on ? (int)tokq[k * kWave + lane] : 0;
             const int w = pow2_at_least(n);
             const float m = wave_max_w(z, w);
-            const float se = wave_sum_w(on ? expf(z - m) : 0.f, w);
+            const float se = wave_sum_w(on ? exp_sm(z - m) : 0.f, w);
             const float lse = m + logf(se);
             uint64_t key = on ? make_key(a_s[k] + (z - lse), k, tk) : 0ull;
             if (n > Kc) key = wave_sort_desc(key);
@@ -568,7 +568,7 @@ __global__ __launch_bounds__(NT) void k_beam_expand(StepDev st, int K, int Kc, i
         for (int c = tid; c < (int)ldz; c += NT) m = fmaxf(m, zc(c));
         m = block_max<NT>(m, red_f);
         float se = 0.f;
-        for (int c = tid; c < (int)ldz; c += NT) se += expf(zc(c) - m);
+        for (int c = tid; c < (int)ldz; c += NT) se += exp_sm(zc(c) - m);
         lse = m + logf(block_sum<NT>(se, red_f));
     } else {
         lse = block_lse<NT>(z_s, n, red_f);
@@ -659,7 +659,7 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
     float se = 0.f;
 #pragma unroll
     for (int i = 0; i < M; ++i)
-        if (in_lse(i)) se += expf(z[i] - m);
+        if (in_lse(i)) se += exp_sm(z[i] - m);
     const float lse = m + logf(wave_sum(se));
     const int parent = b % K;
     uint32_t sc[M];

@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
         if (tid < kWave) {
             const float z = tid < cnt ? z_s[tid] : -INFINITY;
             const float m = wave_max(z);
-            const float s = wave_sum(tid < cnt ? expf(z - m) : 0.f);
+            const float s = wave_sum(tid < cnt ? exp_sm(z - m) : 0.f);
             if (tid == 0) {
                 float* p = w.cms + ((int64_t)q * w.chunk_cap + c) * 2;
                 p[0] = m;
@@ -333,14 +333,14 @@ __global__ __launch_bounds__(kWThreads) void k_wide_keys(int K, const float* __r
         for (int x = ho_s[k] + lane; x < ho_s[k + 1]; x += kWave) {
             const float cm = cms[2 * x], cs = cms[2 * x + 1];
             if (cm > m) {
-                s = s * expf(m - cm) + cs;
+                s = s * exp_sm(m - cm) + cs;
                 m = cm;
             } else {
-                s += cs * expf(cm - m);
+                s += cs * exp_sm(cm - m);
             }
         }
         const float M = wave_max(m);
-        const float S = wave_sum(m == -INFINITY ? 0.f : s * expf(m - M));
+        const float S = wave_sum(m == -INFINITY ? 0.f : s * exp_sm(m - M));
         const float lse = M + logf(S);
         const float a = acc[(int64_t)q * K + k];
         const int j0 = (c - ho_s[k]) * kWCH;

@@ -18,7 +18,6 @@ constexpr int kWave = 64;
 constexpr int kSmallRow = 64;  // rows up to this many tokens take the one-wave path
 constexpr int kPreMin = 16;    // with scores computed apart: rows above this many tokens read them
 constexpr int kMidRow = 4;     // rows above this many tokens (up to kSmallRow) are scored by the whole block
-constexpr int kMidTok = 4;     // tokens per task of that block-wide scoring
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
@@ -541,6 +540,50 @@ __device__ void block_scores(const float* h_s, const DT* __restrict__ W, int d, 
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const float t = wave_sum(s[u]);
+            if (lane == 0 && j0 + u * NW < n) z_s[j0 + u * NW] = t;
+        }
+    }
+}
+
+// block_scores for d <= CH * 512: every wave takes U tokens at a time with all
+// their W_t row chunks in flight at once (the plain version waits one round
+// trip per chunk), h held in registers.  Products summed in the same order as
+// block_scores (chunk by chunk, then the wave butterfly), so z is identical.
+template <typename DT, int NT, int CH>
+__device__ void block_scores_ch(const float* h_s, const DT* __restrict__ W, int d, const uint16_t* tok_s, int n,
+                                float* z_s) {
+    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int NW = NT / kWave;
+    constexpr int kRegs = CH * (sizeof(DT) == 2 ? 4 : 8);  // VGPRs per token in flight
+    constexpr int U = 48 / kRegs > 0 ? 48 / kRegs : 1;
+    float h[CH][8];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int i = c * kWave * 8 + lane * 8;
+        if (i < d) load8(h_s + i, h[c]);
+        else
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[c][e] = 0.f;
+    }
+    for (int j0 = threadIdx.x / kWave; j0 < n; j0 += U * NW) {
+        Raw8<DT> w8[U][CH];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * NW;
+            const DT* wr = W + (int64_t)tok_s[j < n ? j : j0] * d;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int i = c * kWave * 8 + lane * 8;
+                if (j < n && i < d) w8[u][c].load(wr + i);
+                else w8[u][c].zero();
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float sv = 0.f;
+#pragma unroll
+            for (int c = 0; c < CH; ++c) sv = w8[u][c].dot(h[c], sv);
+            const float t = wave_sum(sv);
             if (lane == 0 && j0 + u * NW < n) z_s[j0 + u * NW] = t;
         }
     }

@@ -351,25 +351,29 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
     __syncthreads();
 
     // phase 1b: rows of kMidRow+1 .. kSmallRow tokens, scored by the whole
-    // block.  Their tokens form a flat list of tasks of kMidTok consecutive
-    // tokens of one row; each wave takes two tasks at a time, so every wave
-    // has 2 * kMidTok W_t rows in flight (a wave working through one such row
+    // block.  Their tokens form a flat list of tasks of MT consecutive
+    // tokens of one row; each wave takes TPW tasks at a time, so every wave
+    // has TPW * MT W_t rows in flight (a wave working through one such row
     // alone would wait a global round trip for every few tokens).  The dot
     // products are summed in the same order as in phase 1.
+    // tokens per task and tasks in flight per wave, within a register budget
+    constexpr int kRw = sizeof(DT) == 2 ? 4 : 8;  // VGPRs per 8 elements of a W_t row
+    constexpr int MT = 4 * CH * kRw + CH * 8 <= 96 ? 4 : (2 * CH * kRw + CH * 8 <= 96 ? 2 : 1);
+    constexpr int TPW = 2 * (MT * CH * kRw + CH * 8) <= 96 ? 2 : 1;
     const int nm = nmid;
     if (nm > 0) {
         if (wv == 0) {
-            const int c = lane < nm ? (n_s[mid[lane]] + kMidTok - 1) / kMidTok : 0;
+            const int c = lane < nm ? (n_s[mid[lane]] + MT - 1) / MT : 0;
             const int incl = wave_inclusive_scan(c);
             if (lane < nm) moff[lane + 1] = incl;
             if (lane == 0) moff[0] = 0;
         }
         __syncthreads();
         const int ntask = moff[nm];
-        for (int t0 = wv; t0 < ntask; t0 += 2 * NW) {
-            int kq[2], j0[2], nn[2];
+        for (int t0 = wv; t0 < ntask; t0 += TPW * NW) {
+            int kq[TPW], j0[TPW], nn[TPW];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < TPW; ++u) {
                 const int task = t0 + u * NW;
                 int lo = 0;
                 if (task < ntask) {  // the row whose tasks hold this one: last i with moff[i] <= task
@@ -380,13 +384,13 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
                     }
                 }
                 kq[u] = task < ntask ? mid[lo] : 0;
-                j0[u] = task < ntask ? (task - moff[lo]) * kMidTok : 0;
-                nn[u] = task < ntask ? min(kMidTok, n_s[kq[u]] - j0[u]) : 0;
+                j0[u] = task < ntask ? (task - moff[lo]) * MT : 0;
+                nn[u] = task < ntask ? min(MT, n_s[kq[u]] - j0[u]) : 0;
             }
-            float hr[2][CH][8];
-            Raw8<DT> w8[2][kMidTok][CH];
+            float hr[TPW][CH][8];
+            Raw8<DT> w8[TPW][MT][CH];
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < TPW; ++u)
 #pragma unroll
                 for (int c = 0; c < CH; ++c) {
                     const int i = c * kWave * 8 + lane * 8;
@@ -396,9 +400,9 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
                         for (int e = 0; e < 8; ++e) hr[u][c][e] = 0.f;
                 }
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < TPW; ++u)
 #pragma unroll
-                for (int jj = 0; jj < kMidTok; ++jj) {
+                for (int jj = 0; jj < MT; ++jj) {
                     const bool on = jj < nn[u];
                     const int tkn = on ? (int)tokq[kq[u] * kWave + j0[u] + jj] : 0;
 #pragma unroll
@@ -409,9 +413,9 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
                     }
                 }
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < TPW; ++u)
 #pragma unroll
-                for (int jj = 0; jj < kMidTok; ++jj) {
+                for (int jj = 0; jj < MT; ++jj) {
                     float sv = 0.f;
 #pragma unroll
                     for (int c = 0; c < CH; ++c) sv = w8[u][jj][c].dot(hr[u][c], sv);
@@ -454,7 +458,7 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
         } else {
             for (int x = tid; x < d; x += NT) h_s[x] = to_f32(hidden[b * d + x]);
             __syncthreads();
-            block_scores<DT, NT>(h_s, W, d, tok_s, n, z_s);
+            block_scores_ch<DT, NT, CH>(h_s, W, d, tok_s, n, z_s);
             __syncthreads();
         }
         const float lse = block_lse<NT>(z_s, n, red_f);

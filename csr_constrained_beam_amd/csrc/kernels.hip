@@ -587,10 +587,11 @@ __global__ __launch_bounds__(NT) void k_beam_expand(StepDev st, int K, int Kc, i
 }
 
 // Dense path on a bitmap step: one wavefront per beam, four beams per
-// workgroup.  Lane l owns the M consecutive columns l*M .. l*M+M-1: their
-// scores (16-byte loads, summed over the k-slices, if any) and validity bits
-// stay in registers; softmax and the beam's best min(K, n) keys use wave
-// reductions only.  Requires V <= 64*M and V % 4 == 0.
+// workgroup.  Lane l owns the M columns g*256 + 4l .. g*256 + 4l + 3
+// (g < M/4), so that every 16-byte load of the wave reads 1 KB of the score
+// row contiguously; their scores (summed over the k-slices, if any) and
+// validity bits stay in registers; softmax and the beam's best min(K, n) keys
+// use wave reductions only.  Requires V <= 64*M and V % 4 == 0.
 template <int M>
 __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K, int Kc, int V, int d,
                                                        const float* __restrict__ Z, const float* __restrict__ Zp,
@@ -599,7 +600,8 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
                                                        const int32_t* __restrict__ beam_rows,
                                                        const float* __restrict__ acc, uint64_t* __restrict__ keys_out,
                                                        int mode) {
-    static_assert(M % 4 == 0, "columns are read 4 at a time");
+    static_assert(M % 4 == 0 && M <= 64, "columns are read 4 at a time, at most 64 per lane");
+    constexpr int G = M / 4;
     __shared__ uint64_t wl_all[4][kWaveListCap];
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     const int b = blockIdx.x * 4 + wv;
@@ -611,10 +613,10 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
         if (lane < Kc) out[lane] = 0;
         return;
     }
-    const int c0 = lane * M;
+    auto col = [&](int i) { return (i >> 2) * (kWave * 4) + lane * 4 + (i & 3); };
     const uint32_t* rb = mode == CB_MODE_UNCONSTRAINED ? nullptr : st.bits + (int64_t)r * st.words;
     const int split = gemm_split(*n_live, V, d);
-    const float* zb = (split == 1 ? Z + (int64_t)b * V : Zp + (int64_t)ci_of[b] * V) + c0;
+    const float* zb = split == 1 ? Z + (int64_t)b * V : Zp + (int64_t)ci_of[b] * V;
     float z[M];
 #pragma unroll
     for (int i = 0; i < M; ++i) z[i] = 0.f;
@@ -622,39 +624,40 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
     for (int x = 0; x < kSplitMax; ++x) {
         if (x < split) {
 #pragma unroll
-            for (int i = 0; i < M; i += 4) {
-                if (c0 + i < V) {
-                    const float4 v4 = *reinterpret_cast<const float4*>(zb + (int64_t)x * kSplitRows * V + i);
-                    z[i] += v4.x;
-                    z[i + 1] += v4.y;
-                    z[i + 2] += v4.z;
-                    z[i + 3] += v4.w;
-                }
+            for (int g = 0; g < G; ++g) {
+                // columns past the row re-read its last four (in bounds, no
+                // branch around the loads); their validity bits are 0
+                const int c = min(col(4 * g), V - 4);
+                const float4 v4 = *reinterpret_cast<const float4*>(zb + (int64_t)x * kSplitRows * V + c);
+                z[4 * g] += v4.x;
+                z[4 * g + 1] += v4.y;
+                z[4 * g + 2] += v4.z;
+                z[4 * g + 3] += v4.w;
             }
         }
     }
-    uint32_t on = 0;  // validity of this lane's columns, bit i for column c0 + i (M <= 32 per word)
-    uint32_t on_hi = 0;
+    // validity of this lane's columns: the row's bitmap read once (lane l
+    // holds words l and l + 64), then group g's four bits, which lie in word
+    // 8g + l/8 at bit 4(l%8), fetched from the lane holding that word
+    uint32_t vb[G];
     if (mode != CB_MODE_UNCONSTRAINED) {
+        const int words = (V + 31) >> 5;
+        const uint32_t w0 = rb[min(lane, words - 1)];
+        const uint32_t w1 = G > 8 ? rb[min(lane + kWave, words - 1)] : 0u;
 #pragma unroll
-        for (int i = 0; i < M; i += 32) {
-            // columns c0+i .. c0+i+31 lie in at most two bitmap words
-            const int c = c0 + i;
-            const int w = c >> 5, sh = c & 31;
-            uint32_t lo = c < V ? rb[w] : 0u;
-            uint32_t hi = (sh && c + 32 - sh < V) ? rb[w + 1] : 0u;
-            uint32_t bits = sh ? ((lo >> sh) | (hi << (32 - sh))) : lo;
-            if (M - i < 32) bits &= (1u << (M - i)) - 1u;
-            if (i == 0) on = bits; else on_hi = bits;
+        for (int g = 0; g < G; ++g) {
+            const int src = (g * 8 + (lane >> 3)) & (kWave - 1);
+            const uint32_t w = (uint32_t)__shfl((int)(g < 8 ? w0 : w1), src);
+            vb[g] = col(4 * g) < V ? (w >> ((lane & 7) * 4)) & 0xFu : 0u;
         }
+    } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) vb[g] = col(4 * g) < V ? 0xFu : 0u;
     }
     // candidates: the row's valid tokens, or (no constraint) every column
-    auto valid = [&](int i) {
-        if (mode == CB_MODE_UNCONSTRAINED) return c0 + i < V;
-        return ((i < 32 ? on >> i : on_hi >> (i - 32)) & 1u) != 0;
-    };
+    auto valid = [&](int i) { return ((vb[i >> 2] >> (i & 3)) & 1u) != 0; };
     // softmax support: the candidates, or (score first) every column
-    auto in_lse = [&](int i) { return mode == CB_MODE_FILTER_FIRST ? valid(i) : c0 + i < V; };
+    auto in_lse = [&](int i) { return mode == CB_MODE_FILTER_FIRST ? valid(i) : col(i) < V; };
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < M; ++i)
@@ -671,7 +674,7 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
     for (int i = 0; i < M; ++i) sc[i] = valid(i) ? score_order_bits(a + (z[i] - lse)) : 0u;
     const uint64_t best = wave_top<M>(
         Kc, [&](int i) { return sc[i]; },
-        [&](int i) { return ((uint64_t)sc[i] << 32) | ((uint64_t)(1023 - parent) << 16) | (uint64_t)(65535 - (c0 + i)); },
+        [&](int i) { return ((uint64_t)sc[i] << 32) | ((uint64_t)(1023 - parent) << 16) | (uint64_t)(65535 - col(i)); },
         wl_all[wv]);
     if (lane < Kc) out[lane] = best;
 }

@@ -458,6 +458,20 @@ struct Raw8<uint16_t> {
         s = fmaf(h[7], __uint_as_float(v.w & 0xFFFF0000u), s);
         return s;
     }
+    // the same sum with the hidden values also kept raw (converted here, so
+    // that their loads need not complete before the next loads are issued)
+    __device__ __forceinline__ float dot_raw(const Raw8& h, float s) const {
+        float hf[8];
+        hf[0] = __uint_as_float(h.v.x << 16);
+        hf[1] = __uint_as_float(h.v.x & 0xFFFF0000u);
+        hf[2] = __uint_as_float(h.v.y << 16);
+        hf[3] = __uint_as_float(h.v.y & 0xFFFF0000u);
+        hf[4] = __uint_as_float(h.v.z << 16);
+        hf[5] = __uint_as_float(h.v.z & 0xFFFF0000u);
+        hf[6] = __uint_as_float(h.v.w << 16);
+        hf[7] = __uint_as_float(h.v.w & 0xFFFF0000u);
+        return dot(hf, s);
+    }
 };
 template <>
 struct Raw8<float> {
@@ -467,6 +481,11 @@ struct Raw8<float> {
     __device__ __forceinline__ float dot(const float* h, float s) const {
 #pragma unroll
         for (int i = 0; i < 8; ++i) s = fmaf(h[i], v[i], s);
+        return s;
+    }
+    __device__ __forceinline__ float dot_raw(const Raw8& h, float s) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = fmaf(h.v[i], v[i], s);
         return s;
     }
 };
@@ -528,14 +547,17 @@ __device__ void block_scores(const float* h_s, const DT* __restrict__ W, int d, 
         for (int i = lane * 8; i < d; i += kWave * 8) {
             float h[8];
             load8(h_s + i, h);
+            // raw loads of the U rows first (no use inside the guards), so
+            // that they are in flight together
+            Raw8<DT> w8[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (j0 + u * NW < n) {
-                    float w8[8];
-                    load8(wr[u] + i, w8);
-                    s[u] = dot8(h, w8, s[u]);
-                }
+                if (j0 + u * NW < n) w8[u].load(wr[u] + i);
+                else w8[u].zero();
             }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (j0 + u * NW < n) s[u] = w8[u].dot(h, s[u]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {

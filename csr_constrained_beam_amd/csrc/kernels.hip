@@ -284,16 +284,16 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
                 z[u] = __uint_as_float((uint32_t)(pre[(int64_t)q * pre_cap + pre_off[(int64_t)q * (K + 1) + kk[u]] +
                                                       lane] >> 32));
         }
-        float hr[2][CH][8];
+        // hidden vectors kept raw until used (a conversion right after the
+        // load would make each load wait before the next is issued)
+        Raw8<DT> hr[2][CH];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
                 const int i = c * kWave * 8 + lane * 8;
-                if (dots[u] && i < d) load8(hidden + b[u] * d + i, hr[u][c]);
-                else
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) hr[u][c][e] = 0.f;
+                if (dots[u] && i < d) hr[u][c].load(hidden + b[u] * d + i);
+                else hr[u][c].zero();
             }
         const int nmax = max(dots[0] ? n[0] : 0, dots[1] ? n[1] : 0);
         // kTok tokens of each of the two beams at a time: all their W_t row
@@ -323,7 +323,7 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
                 for (int jj = 0; jj < kTok; ++jj) {
                     float sv = 0.f;
 #pragma unroll
-                    for (int c = 0; c < CH; ++c) sv = wr8[u][jj][c].dot(hr[u][c], sv);
+                    for (int c = 0; c < CH; ++c) sv = wr8[u][jj][c].dot_raw(hr[u][c], sv);
                     const float t = wave_sum(sv);
                     if (dots[u] && lane == j0 + jj) z[u] = t;
                 }
@@ -387,17 +387,15 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
                 j0[u] = task < ntask ? (task - moff[lo]) * MT : 0;
                 nn[u] = task < ntask ? min(MT, n_s[kq[u]] - j0[u]) : 0;
             }
-            float hr[TPW][CH][8];
+            Raw8<DT> hr[TPW][CH];
             Raw8<DT> w8[TPW][MT][CH];
 #pragma unroll
             for (int u = 0; u < TPW; ++u)
 #pragma unroll
                 for (int c = 0; c < CH; ++c) {
                     const int i = c * kWave * 8 + lane * 8;
-                    if (nn[u] > 0 && i < d) load8(hidden + ((int64_t)q * K + kq[u]) * d + i, hr[u][c]);
-                    else
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) hr[u][c][e] = 0.f;
+                    if (nn[u] > 0 && i < d) hr[u][c].load(hidden + ((int64_t)q * K + kq[u]) * d + i);
+                    else hr[u][c].zero();
                 }
 #pragma unroll
             for (int u = 0; u < TPW; ++u)
@@ -418,7 +416,7 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
                 for (int jj = 0; jj < MT; ++jj) {
                     float sv = 0.f;
 #pragma unroll
-                    for (int c = 0; c < CH; ++c) sv = w8[u][jj][c].dot(hr[u][c], sv);
+                    for (int c = 0; c < CH; ++c) sv = w8[u][jj][c].dot_raw(hr[u][c], sv);
                     const float t = wave_sum(sv);
                     if (lane == 0 && jj < nn[u]) zmid[kq[u] * kWave + j0[u] + jj] = t;
                 }
@@ -695,10 +693,13 @@ __global__ __launch_bounds__(256) void k_query_merge_w(StepDev st, int Q, int K,
     const int n = K * Kc;
     const uint64_t* src = keys + (int64_t)q * n;
     uint64_t kv[M];
+    // branch-free loads (indices past the list re-read its last key, then
+    // masked), so that all M loads are in flight together
 #pragma unroll
     for (int i = 0; i < M; ++i) {
         const int c = lane + kWave * i;
-        kv[i] = c < n ? src[c] : 0ull;
+        const uint64_t v = src[min(c, n - 1)];
+        kv[i] = c < n ? v : 0ull;
     }
     const uint64_t best = wave_top<M>(K, [&](int i) { return (uint32_t)(kv[i] >> 32); }, [&](int i) { return kv[i]; },
                                       wl_all[wv]);

@@ -1,0 +1,97 @@
+"""GPU parity of a decoding step at hidden widths of two to four 512-element
+chunks, float32 and bf16, on the sparse path with both workgroup sizes of the
+per-query kernel (512 threads for K < 16, 1024 otherwise) and on the dense
+path (the full-codebook product, then the expansion and merge).
+
+The catalog is built so that the rows of its steps cover every scoring phase
+of the per-query kernel: rows of one token (not scored: log-softmax 0), of
+2-4 tokens (one wavefront), of 5-64 tokens (the block-wide task list) and of
+more than 64 tokens (the block per row).  Each step is teacher forced from the
+oracle's trace and compared with the oracle's candidates; the persistent
+decode must equal the step-by-step decode bit for bit.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.parity import compare_step
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import csr_constrained_beam_amd as cb  # noqa: E402
+from tests.test_gpu_parity import DEV, gpu_step  # noqa: E402
+
+# children of the level-1 prefixes: one of each scoring phase and the edges
+# between them (4 | 5 and 64 | 65 are the phase boundaries)
+FANOUTS = [1, 2, 3, 4, 5, 6, 12, 30, 64, 65, 100, 250]
+
+
+def catalog(seed):
+    rng = np.random.default_rng(seed)
+    V = 300
+    items = []
+    for a, f in enumerate(FANOUTS * 3):
+        for b in rng.choice(V, size=f, replace=False):
+            for c in rng.choice(V, size=int(rng.integers(1, 6)), replace=False):
+                items.append((a, int(b), int(c)))
+    return np.unique(np.array(items, np.int32), axis=0), V
+
+
+def test_catalog_covers_every_phase():
+    items, V = catalog(11)
+    T = oracle.Trie(items, V)
+    fan1 = sorted({len(T.children_of_row(1, r)[0]) for r in range(len(np.unique(items[:, 0])))})
+    assert fan1 == sorted(set(FANOUTS))
+    assert len(T.children_of_row(0, 0)[0]) == 3 * len(FANOUTS)  # the root row: 36 tokens
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 1024), ("f32", 2048), ("bf16", 1536), ("bf16", 2048)])
+@pytest.mark.parametrize("K", [8, 32])
+@pytest.mark.parametrize("path", ["sparse", "dense"])
+def test_step_hidden_widths(dtype, d, K, path):
+    items, V = catalog(11)
+    L, Q = 3, 6
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((Q, d)).astype(np.float32)
+    P = (rng.standard_normal((L - 1, V, d)) / np.sqrt(d)).astype(np.float32)
+    W = (rng.standard_normal((L, V, d)) / np.sqrt(d)).astype(np.float32)
+    Wd = torch.from_numpy(W).to(DEV)
+    if dtype == "bf16":
+        Wd = Wd.bfloat16()
+        W = Wd.float().cpu().numpy()
+    bf16 = dtype == "bf16"
+    T = oracle.Trie(items, V)
+    ref = T.decode(K, q, P, W, bf16=bf16, trace=True, threads=8)
+    idx = cb.Index(items, V, device=0)
+    plan = idx.plan(Q, K, d, dtype)
+    for t in range(L):
+        plan.set_path(t, path)
+        plan.set_select(t, "lds")
+    for t in range(L):
+        print("case", dtype, d, "K", K, path, "step", t, flush=True)
+        h = ref["trace_h"][t]
+        rows = ref["trace_rows_in"][t]
+        acc = ref["trace_acc_in"][t]
+        o = T.step(t, K, h, W[t], rows, acc, candidates=True, threads=8)
+        hd = torch.from_numpy(np.ascontiguousarray(h, np.float32)).to(DEV)
+        if bf16:
+            hd = hd.to(torch.bfloat16)
+        g = gpu_step(plan, t, hd, Wd[t], torch.from_numpy(rows.astype(np.int32)).to(DEV),
+                     torch.from_numpy(acc).to(DEV))
+        ex, gap, fails = compare_step(o, g, K, dtype)
+        assert not fails, "\n".join(fails[:10])
+    # the persistent decode (one launch for every step) against the step-by-step one
+    print("case", dtype, d, "K", K, path, "decode", flush=True)
+    qd, Pd = torch.from_numpy(q).to(DEV), torch.from_numpy(P).to(DEV)
+    plan.set_decode_fusion(False)
+    a = plan.decode(qd, Pd, Wd)
+    plan.set_decode_fusion(True)
+    b = plan.decode(qd, Pd, Wd)
+    torch.cuda.synchronize()
+    for k in ("seqs", "logp", "rows"):
+        assert torch.equal(a[k], b[k]), k

@@ -859,9 +859,9 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
         size_t lds = 0;
         for (int t = t_fuse; t < L; ++t) {
             const cb::StepTable& T = idx->steps[(size_t)t];
-            lds = std::max(lds, query_lds_bytes(T.S, K, std::min(K, std::max(T.S, 1)), d));
+            lds = std::max(lds, tail_lds_bytes(T.S, K, std::min(K, std::max(T.S, 1)), d));
         }
-        ProfMark m(p, s, t_fuse, CB_KERNEL_DECODE_TAIL, query_threads(K), Q);
+        ProfMark m(p, s, t_fuse, CB_KERNEL_DECODE_TAIL, tail_threads(K), Q);
         uint64_t* clk = p->prof_on ? p->phase_clk : nullptr;
         e = launch_decode_tail(idx->d_steps, lds, t_fuse, L, Q, K, d, V, p->dtype, W, P, p->s[cur], p->s[1 - cur],
                                p->h, p->rows[cur], p->rows[1 - cur], p->acc[cur], p->acc[1 - cur], p->hist_tok,

@@ -143,6 +143,8 @@ int query_threads(int K);
 size_t expand_lds_bytes(int S, int d, bool dense);
 int expand_bitmap_max_v();
 size_t query_lds_bytes(int S, int K, int Kc, int d);
+int tail_threads(int K);
+size_t tail_lds_bytes(int S, int K, int Kc, int d);
 int gemm_blocks(cb_dtype dt, int R, int V);
 
 // Sparse path: the whole step in one launch, one workgroup per query.

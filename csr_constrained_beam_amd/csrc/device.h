@@ -611,15 +611,35 @@ __device__ void block_scores_ch(const float* h_s, const DT* __restrict__ W, int 
     }
 }
 
-// a3 for one beam, whole block: log-sum-exp of z_s[0..n).
+// a3 for one beam, whole block: log-sum-exp of z_s[0..n).  Workgroups of at
+// least kLseSlots threads sum over kLseSlots fixed slots (slot s takes the
+// terms s, s + kLseSlots, ...) reduced in a fixed order, so that every such
+// workgroup size gives the same bits (the per-query step of 512 and of 1024
+// threads, and the persistent decode, agree exactly); the maximum is exact in
+// any order.
+constexpr int kLseSlots = 512;
 template <int NT>
 __device__ float block_lse(const float* z_s, int n, float* red_f) {
     float m = -INFINITY;
     for (int j = threadIdx.x; j < n; j += NT) m = fmaxf(m, z_s[j]);
     m = block_max<NT>(m, red_f);
     float se = 0.f;
-    for (int j = threadIdx.x; j < n; j += NT) se += exp_sm(z_s[j] - m);
-    se = block_sum<NT>(se, red_f);
+    if constexpr (NT >= kLseSlots) {
+        if (threadIdx.x < kLseSlots)
+            for (int j = threadIdx.x; j < n; j += kLseSlots) se += exp_sm(z_s[j] - m);
+        se = wave_sum(se);
+        const int w = threadIdx.x / kWave;
+        if ((threadIdx.x & (kWave - 1)) == 0 && w < kLseSlots / kWave) red_f[w] = se;
+        __syncthreads();
+        float r = red_f[0];
+#pragma unroll
+        for (int i = 1; i < kLseSlots / kWave; ++i) r += red_f[i];
+        __syncthreads();
+        se = r;
+    } else {
+        for (int j = threadIdx.x; j < n; j += NT) se += exp_sm(z_s[j] - m);
+        se = block_sum<NT>(se, red_f);
+    }
     return m + logf(se);
 }
 

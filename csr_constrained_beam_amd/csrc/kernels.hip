@@ -1196,6 +1196,12 @@ int expand_threads(const StepDev&) { return kExpandThreads; }
 
 int query_threads(int K) { return K >= 16 ? 1024 : 512; }
 
+// The persistent decode runs every step and every hidden update of a query in
+// one workgroup; with 512 threads its per-wave register budget doubles (the
+// 1024-thread build spills the update's registers).  The per-query step gives
+// the same bits at either size (every sum is per wave or over fixed slots).
+int tail_threads(int) { return 512; }
+
 size_t expand_lds_bytes(int S, int d, bool dense) { return (size_t)expand_lds(S, d, dense, kExpandThreads).total; }
 
 int expand_bitmap_max_v() { return 64 * kWave; }
@@ -1203,6 +1209,8 @@ int expand_bitmap_max_v() { return 64 * kWave; }
 size_t query_lds_bytes(int S, int K, int Kc, int d) {
     return (size_t)query_lds(S, K, Kc, d, query_threads(K)).total;
 }
+
+size_t tail_lds_bytes(int S, int K, int Kc, int d) { return (size_t)query_lds(S, K, Kc, d, tail_threads(K)).total; }
 
 hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int Kc, int d, const void* hidden,
                              const void* W, const int32_t* beam_rows, const float* acc, const uint64_t* pre,
@@ -1358,7 +1366,7 @@ hipError_t launch_decode_tail(const StepDev* d_steps, size_t lds, int t0, int L,
                               int32_t* rows0, int32_t* rows1, float* acc0, float* acc1, int32_t* hist_tok,
                               int32_t* hist_par, uint64_t* clk, hipStream_t s) {
     if (Q <= 0 || t0 >= L) return hipSuccess;
-    const int NT = query_threads(K);
+    const int NT = tail_threads(K);
     const int CH = (d + kWave * 8 - 1) / (kWave * 8);
     const int R = Q * K;
     const bool vec = hidden_vec_ok(d, P);

@@ -21,27 +21,33 @@ void clear_error() { g_err.clear(); }
 
 namespace {
 
-// Make `dev` current for the scope, restoring the caller's device after.
-struct DeviceGuard {
-    int prev = -1;
-    bool ok = true;
-    explicit DeviceGuard(int dev) {
-        if (dev < 0) return;  // host-only work: leave the runtime alone
-        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
-        if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
-    }
-    ~DeviceGuard() {
-        int cur = -1;
-        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
-    }
-};
-
 cb_status hip_fail(const char* where, hipError_t e) {
     set_error(std::string(where) + ": " + hipGetErrorString(e));
     return CB_EHIP;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Whether the byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na && nb && x < y + nb && y < x + na;
+}
+
+// The step's outputs must be four distinct arrays that share no byte with
+// its inputs (the kernels read inputs after other workgroups wrote outputs).
+bool step_outputs_alias(size_t R, size_t d, size_t V, size_t es, const void* hidden, const void* W_t,
+                        const void* rows, const void* acc, void* const outs[4]) {
+    const void* in[4] = {hidden, W_t, rows, acc};
+    const size_t in_n[4] = {R * d * es, V * d * es, R * 4, R * 4};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 4; ++j)
+            if (overlaps(outs[i], R * 4, in[j], in_n[j])) return true;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], R * 4, outs[j], R * 4)) return true;
+    }
+    return false;
+}
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 size_t dtype_size(cb_dtype dt) { return dt == CB_BF16 ? 2 : 4; }
@@ -78,12 +84,17 @@ int32_t resolve_path(const cb_plan* p, int t) {
 
 // Whether the LDS selection (fused sparse step, or dense expansion + merge)
 // holds step t of this plan.
+// Hidden widths above kQueryMaxD take the sparse step as a per-beam
+// expansion (whose scoring loops over the whole width) + per-query merge
+// instead of the fused per-query kernel, which keeps at most kQueryMaxD
+// elements of a hidden vector in registers.
 bool lds_select_ok(const cb_plan* p, int t) {
     if (p->K > kMaxK) return false;
     const cb::StepTable& T = p->idx->steps[(size_t)t];
     const int Kc = std::min(p->K, std::max(T.S, 1));
-    return query_lds_bytes(T.S, p->K, Kc, p->d) <= (size_t)kMaxLds &&
-           expand_lds_bytes(T.S, p->d, true) <= (size_t)kMaxLds;
+    const bool sparse_ok = p->d <= kQueryMaxD ? query_lds_bytes(T.S, p->K, Kc, p->d) <= (size_t)kMaxLds
+                                              : expand_lds_bytes(T.S, p->d, false) <= (size_t)kMaxLds;
+    return sparse_ok && expand_lds_bytes(T.S, p->d, true) <= (size_t)kMaxLds;
 }
 
 int32_t resolve_select(const cb_plan* p, int t) {
@@ -238,6 +249,21 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const vo
     const int Kc = std::min(p->K, p->mode == CB_MODE_UNCONSTRAINED ? idx->V : std::max(T.S, 1));
     hipError_t e;
     if (sel == CB_SELECT_RADIX) return run_step_radix(p, t, Q, path, hidden, Wt, rows, acc, ot, op, orow, ol, s);
+    if ((path == CB_PATH_SPARSE || path == CB_PATH_SPARSE_SPLIT) && p->d > kQueryMaxD) {
+        // wide hidden vectors: per-beam gather-dot expansion, then the per-query merge
+        {
+            ProfMark m(p, s, t, CB_KERNEL_EXPAND_SPARSE, expand_threads(sd), R);
+            e = launch_beam_expand(sd, false, p->dtype, R, p->K, Kc, p->d, hidden, Wt, nullptr, nullptr, idx->V,
+                                   nullptr, nullptr, rows, acc, p->keys, p->mode, s);
+            m.done();
+            if (e != hipSuccess) return hip_fail("cb_step: sparse beam expansion", e);
+        }
+        ProfMark m(p, s, t, CB_KERNEL_MERGE, kMergeThreads, Q);
+        e = launch_query_merge(sd, Q, p->K, Kc, p->keys, rows, ot, op, orow, ol, p->mode, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: query merge", e);
+        return CB_OK;
+    }
     if (path == CB_PATH_SPARSE || path == CB_PATH_SPARSE_SPLIT) {
         const WideDev& w = p->wide;
         const bool split = path == CB_PATH_SPARSE_SPLIT && w.cand;
@@ -314,6 +340,18 @@ cb_status check_plan(const cb_plan* p, int32_t Q, const char* fn) {
 }
 
 }  // namespace
+
+// Entry points shared with the allocation-free step (noalloc.hip).
+cb_status enqueue_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const void* hidden, const void* Wt,
+                       const int32_t* rows, const float* acc, int32_t* ot, int32_t* op, int32_t* orow, float* ol,
+                       hipStream_t s) {
+    return run_step(p, t, Q, path, sel, hidden, Wt, rows, acc, ot, op, orow, ol, s);
+}
+
+bool step_args_alias(size_t R, size_t d, size_t V, cb_dtype dt, const void* hidden, const void* W_t, const void* rows,
+                     const void* acc, void* const outs[4]) {
+    return step_outputs_alias(R, d, V, dtype_size(dt), hidden, W_t, rows, acc, outs);
+}
 
 // Copy the host tables of idx to idx->device, release the host copies and
 // upload the step descriptors.  On failure idx is freed.
@@ -735,6 +773,12 @@ cb_status cb_step(cb_plan* p, int32_t t, int32_t Q, const void* hidden, const vo
             set_error("cb_step: a per-slot array is NULL or not 4-byte aligned");
             return CB_EINVAL;
         }
+    void* const outs[4] = {out_tokens, out_parents, out_rows, out_logp};
+    if (step_outputs_alias((size_t)Q * p->K, (size_t)p->d, (size_t)p->idx->V, dtype_size(p->dtype), hidden, W_t,
+                           beam_rows, acc_logp, outs)) {
+        set_error("cb_step: an output array overlaps an input or another output");
+        return CB_EINVAL;
+    }
     DeviceGuard g(p->idx->device);
     return run_step(p, t, Q, resolve_path(p, t), resolve_select(p, t), hidden, W_t, beam_rows, acc_logp, out_tokens,
                     out_parents, out_rows, out_logp, (hipStream_t)stream);
@@ -759,7 +803,7 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
     // selection run in one launch (untraced, untuned decodes only)
     int t_fuse = L;
     const bool fuse = p->fuse_mode == 1 || (p->fuse_mode == -1 && p->fuse_tuned);
-    if (fuse && reps == 0 && !tr_h && !tr_rows && !tr_acc && idx->d_steps) {
+    if (fuse && reps == 0 && !tr_h && !tr_rows && !tr_acc && idx->d_steps && d <= kQueryMaxD) {
         while (t_fuse > 0 && resolve_path(p, t_fuse - 1) == CB_PATH_SPARSE &&
                resolve_select(p, t_fuse - 1) == CB_SELECT_LDS)
             --t_fuse;

@@ -15,6 +15,24 @@ namespace cb {
 void set_error(const std::string& msg);
 void clear_error();
 
+// Make `dev` current for the scope, restoring the caller's device after
+// (dev < 0: host-only work, the runtime is left alone).
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev) {
+        if (dev < 0) return;
+        if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+        if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+    DeviceGuard(const DeviceGuard&) = delete;
+    DeviceGuard& operator=(const DeviceGuard&) = delete;
+};
+
 // Device view of one step table.  Rows are the distinct length-t prefixes in
 // lexicographic order; row r's edges are row_ptr[r] .. row_ptr[r+1]-1, ascending
 // token, and edge e leads to row e of the next step.
@@ -65,6 +83,8 @@ struct cb_index {
 // Limits of the kernels in this build.
 namespace cb {
 constexpr int kMaxK = 64;            // beam width held by the per-query selection (one wave)
+constexpr int kQueryMaxD = 2048;     // hidden width the fused per-query sparse step holds in registers
+                                     // (wider: per-beam expansion + per-query merge, or the radix path)
 constexpr int kMaxKRadix = 1024;     // beam width of the radix-select path (10-bit parent field of a key)
 constexpr int kMaxLds = 65536;       // LDS one workgroup may use
 constexpr int kExpandThreads = 256;  // per-beam expansion workgroup
@@ -207,6 +227,15 @@ hipError_t launch_wide_collect(int Q, int K, const WideDev& w, hipStream_t s);
 hipError_t launch_wide_sort(const StepDev& st, int Q, int K, const int32_t* beam_rows, const WideDev& w,
                             int32_t* tok, int32_t* par, int32_t* rows, float* logp, hipStream_t s);
 
+// One step on the given plan's workspace and path / selection (api.cpp; no
+// validation).  The allocation-free step passes a plan whose workspace
+// pointers lie in its static device array.
+cb_status enqueue_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const void* hidden, const void* Wt,
+                       const int32_t* rows, const float* acc, int32_t* ot, int32_t* op, int32_t* orow, float* ol,
+                       hipStream_t s);
+// Whether a step's four outputs overlap one another or its inputs.
+bool step_args_alias(size_t R, size_t d, size_t V, cb_dtype dt, const void* hidden, const void* W_t, const void* rows,
+                     const void* acc, void* const outs[4]);
 // Index construction (index_build.cpp).
 // Upload the host tables of idx to idx->device (release the host copies);
 // frees idx on failure.

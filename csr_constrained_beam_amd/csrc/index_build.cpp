@@ -133,8 +133,10 @@ cb_status build_impl(const int32_t* sids, int64_t n, int32_t L, int32_t V, int32
 
     idx->steps.assign((size_t)L, StepTable());
     idx->words = (V + 31) / 32;
-    cb_status st = CB_OK;
+    // one status per step thread (each writes only its own), reduced after the joins
+    std::vector<cb_status> step_st((size_t)L, CB_OK);
     auto build_step = [&](int t) {
+        cb_status& st = step_st[(size_t)t];
         StepTable& T = idx->steps[(size_t)t];
         int64_t nr = 0, ne = 0;
         for (int64_t i = 0; i < N; ++i) {
@@ -210,6 +212,9 @@ cb_status build_impl(const int32_t* sids, int64_t n, int32_t L, int32_t V, int32
         for (int t = 0; t < L; ++t) th.emplace_back(build_step, t);
         for (auto& x : th) x.join();
     }
+    cb_status st = CB_OK;
+    for (cb_status x : step_st)
+        if (x != CB_OK) st = x;
     if (st != CB_OK) {
         set_error("cb_build_index: host allocation failed");
         idx->steps.clear();

@@ -135,7 +135,8 @@ cb_status cb_index_save(const cb_index* idx, const char* path) {
     w.val<int32_t>(idx->L);
     w.val<int32_t>(idx->V);
     w.val<int64_t>(idx->n_items);
-    if (idx->device >= 0 && hipSetDevice(idx->device) != hipSuccess) {
+    DeviceGuard guard(idx->device);  // restores the caller's device on return
+    if (!guard.ok) {
         set_error("cb_index_save: cannot select the index's device");
         return CB_EHIP;
     }

@@ -125,7 +125,11 @@ cb_status cb_build_index(const int32_t* sids, int64_t n_items, int32_t L, int32_
  * Any output pointer may be NULL. */
 cb_status cb_index_shape(const cb_index* idx, int32_t* L, int32_t* V, int64_t* n_items, int32_t* device);
 
-/* Per-step statistics of the table of step t (0 <= t < L). */
+/* Per-step statistics of the table of step t (0 <= t < L): rows, edges, the
+ * widest row (the step's fixed slot count: ZeroGR summary, "Why fewer scores
+ * are not automatically faster", candidates padded to a fixed number of
+ * slots; STATIC sec. 4.2, a static maximum branch factor per level), storage
+ * and device bytes.  Errors: CB_EINVAL (NULL, t out of range). */
 cb_status cb_index_info(const cb_index* idx, int32_t t, cb_step_info* out);
 
 /* Host-side lookup of one row: its valid tokens (ascending) and their next
@@ -166,7 +170,10 @@ cb_status cb_index_load(const char* path, int32_t device, cb_index** out);
  * it; wider beams and wider rows use the radix selection, whose candidate
  * workspace (12 bytes per candidate slot: Q_max * K * widest row) is
  * allocated here when some step needs it, else on the first
- * cb_set_select(..., CB_SELECT_RADIX).
+ * cb_set_select(..., CB_SELECT_RADIX).  The fused per-query sparse step
+ * holds up to 2048 elements of a hidden vector; wider plans take sparse steps
+ * as a per-beam expansion + per-query merge (or the radix selection, whose
+ * scoring loops over any width), and never the persistent decode.
  * Errors: CB_EINVAL, CB_ECAPACITY (K > 1024, d > 16384, or a candidate
  * workspace beyond 2^31 slots per query), CB_ENOMEM, CB_EHIP. */
 cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_dtype dtype, cb_plan** out);
@@ -203,7 +210,13 @@ cb_status cb_set_path(cb_plan* plan, int32_t t, cb_path path);
 /* The path step t will take (never CB_PATH_AUTO). */
 cb_status cb_get_path(const cb_plan* plan, int32_t t, cb_path* path);
 
-/* One decoding step (the hot path) for Q <= Q_max queries at step t.
+/* One decoding step (the hot path) for Q <= Q_max queries at step t, as
+ * ZeroGR's summary states it ("The pipeline": look up each beam's valid next
+ * tokens in the step's table, score them, log-softmax over the valid tokens
+ * only, add to the beam's accumulated log-probability, keep the K best per
+ * query, each carrying its next-step row) with STATIC's beam update (sec.
+ * 4.3: top-K over the flattened candidates of a query, then a gather of the
+ * parents' next states).
  *   hidden     device [Q*K][d] of dtype: each slot's hidden vector (ignored
  *              for dead slots).  bf16 plans take the vectors already rounded.
  *   W_t        device [V][d] of dtype: output layer of step t, row-major.
@@ -216,16 +229,21 @@ cb_status cb_get_path(const cb_plan* plan, int32_t t, cb_path* path);
  * hidden and W_t 16-byte aligned (d is a multiple of 8, so every row is);
  * the per-slot arrays 4-byte aligned.  Enqueued on `stream`; returns after
  * the launches.  Concurrent calls on one plan from different streams race.
- * Errors: CB_EINVAL (t, Q, pointers, host-only index), CB_EHIP. */
+ * Errors: CB_EINVAL (t, Q, NULL or misaligned pointers, an output sharing a
+ * byte with an input or another output, host-only index), CB_EHIP. */
 cb_status cb_step(cb_plan* plan, int32_t t, int32_t Q, const void* hidden, const void* W_t,
                   const int32_t* beam_rows, const float* acc_logp,
                   int32_t* out_tokens, int32_t* out_parents, int32_t* out_rows, float* out_logp,
                   void* stream);
 
-/* Full decode of all L steps with the stand-in model whose hidden vector
- * before step t is h = s / ||s||_2, s = q + sum_{j<t} P_j[token_j] (s in
- * float32; norm and division in double; rounded to float32 and then to bf16
- * for bf16 plans).  The hidden update runs between steps on the device.
+/* Full decode of all L steps (the beam-search loop of FlashTrie, arXiv HTML,
+ * Algorithm 1: expand, prune to the beam, carry the survivors, backtrace the
+ * sequences at the end) with a stand-in model whose hidden vector before
+ * step t is h = s / ||s||_2, s = q + sum_{j<t} P_j[token_j] (s in float32;
+ * norm and division in double; rounded to float32 and then to bf16 for bf16
+ * plans).  The stand-in is not from the pages; it only feeds each step a
+ * hidden vector that depends on the path taken.  The hidden update runs
+ * between steps on the device.
  *   q     device float [Q][d];  P  device float [L-1][V][d] (may be NULL when
  *         L == 1);  W  device [L][V][d] of dtype.
  *   out_seqs  device int32 [Q*K][L] (-1 rows for dead slots);

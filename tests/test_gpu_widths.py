@@ -1,7 +1,10 @@
 """GPU parity of a decoding step at hidden widths of two to four 512-element
 chunks, float32 and bf16, on the sparse path with both workgroup sizes of the
 per-query kernel (512 threads for K < 16, 1024 otherwise) and on the dense
-path (the full-codebook product, then the expansion and merge).
+path (the full-codebook product, then the expansion and merge).  Widths above
+2048 (beyond what the fused per-query kernel keeps in registers) take the
+sparse steps as a per-beam expansion + per-query merge: d = 4096 is checked
+on that route, on the dense path and on the radix selection.
 
 The catalog is built so that the rows of its steps cover every scoring phase
 of the per-query kernel: rows of one token (not scored: log-softmax 0), of
@@ -50,10 +53,20 @@ def test_catalog_covers_every_phase():
     assert len(T.children_of_row(0, 0)[0]) == 3 * len(FANOUTS)  # the root row: 36 tokens
 
 
-@pytest.mark.parametrize("dtype,d", [("f32", 1024), ("f32", 2048), ("bf16", 1536), ("bf16", 2048)])
+@pytest.mark.parametrize("dtype,d", [("f32", 1024), ("f32", 2048), ("bf16", 1536), ("bf16", 2048),
+                                     ("f32", 4096), ("bf16", 4096)])
 @pytest.mark.parametrize("K", [8, 32])
 @pytest.mark.parametrize("path", ["sparse", "dense"])
 def test_step_hidden_widths(dtype, d, K, path):
+    _run_widths(dtype, d, K, path, "lds")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_step_wide_hidden_radix(dtype):
+    _run_widths(dtype, 4096, 32, "sparse", "radix")
+
+
+def _run_widths(dtype, d, K, path, select):
     items, V = catalog(11)
     L, Q = 3, 6
     rng = np.random.default_rng(5)
@@ -71,7 +84,7 @@ def test_step_hidden_widths(dtype, d, K, path):
     plan = idx.plan(Q, K, d, dtype)
     for t in range(L):
         plan.set_path(t, path)
-        plan.set_select(t, "lds")
+        plan.set_select(t, select)
     for t in range(L):
         print("case", dtype, d, "K", K, path, "step", t, flush=True)
         h = ref["trace_h"][t]
@@ -86,7 +99,7 @@ def test_step_hidden_widths(dtype, d, K, path):
         ex, gap, fails = compare_step(o, g, K, dtype)
         assert not fails, "\n".join(fails[:10])
     # the persistent decode (one launch for every step) against the step-by-step one
-    print("case", dtype, d, "K", K, path, "decode", flush=True)
+    print("case", dtype, d, "K", K, path, select, "decode", flush=True)
     qd, Pd = torch.from_numpy(q).to(DEV), torch.from_numpy(P).to(DEV)
     plan.set_decode_fusion(False)
     a = plan.decode(qd, Pd, Wd)

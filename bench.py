@@ -3,16 +3,23 @@
 A bench "step" is one pass of the whole hot path over one batch: all L
 decoding steps (index lookup, scoring, masked log-softmax and per-query
 top-K), teacher forced with the beam states and hidden vectors that a free
-running decode of the same batch produced.  The stand-in model's hidden update
-is outside the timed region (it is timed separately as part of a full decode).
+running decode of the same batch produced, replayed as one HIP graph.  The
+stand-in model's hidden update is outside the timed region (it is timed
+separately as part of a full decode).
 
 Prints one JSON line.  `value` is beam expansions per second: one expansion is
 one (live beam, valid next token) candidate that is scored, normalised and
 offered to the top-K.  `us_per_decode_step` is the mean time of one decoding
-step.  `roofline` covers the kernel with the largest share of the pass time,
-with its algorithmic bytes (or flops) per launch over its mean launch time
-measured here with HIP events.  `cpu_baseline` is the CPU oracle on the host
-cores, on the same batch.
+step; `pass_ms` gives mean / p50 / p95 / p99 / std over the timed replays.
+Per-kernel and per-step times come from event pairs attached to each kernel's
+dispatch (hipExtLaunchKernel), i.e. the kernel's own start and end as the GPU
+records them, the durations a rocprofv3 kernel trace shows; `roofline` covers
+the kernel with the largest share of the pass, with its algorithmic bytes (or
+flops) per launch over that mean duration.  `floor` is the overhead floor
+(empty kernels, graph nodes) and `copy_gbs` a measured device copy rate.
+`cpu_baseline` is the CPU oracle on the host cores (one thread and all the
+threads it may use), and `decode_vs_oracle` compares the free-running GPU
+decode of the benched batch with the oracle's.
 """
 
 import argparse
@@ -327,13 +334,17 @@ def main():
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
+    # the timed region: an event between consecutive replays, so that the
+    # whole region's time and each replay's time come from the same run
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
         run()
-    e1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    ms_per_pass = e0.elapsed_time(e1) / args.steps
+    ms_per_pass = evs[0].elapsed_time(evs[-1]) / args.steps
+    pass_ms = stats([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    log("pass: %.4f ms (p50 %.4f, p99 %.4f)" % (ms_per_pass, pass_ms["p50"], pass_ms["p99"]))
 
     # score first against filter first on the same batch: share of each
     # query's final items that both orders return (ZeroGR's overlap measure)
@@ -355,27 +366,34 @@ def main():
         del ff
         log("score-first vs filter-first item overlap: mean %.4f, min %.4f" % (overlap["mean"], overlap["min"]))
 
-    # per-kernel durations: HIP events around every launch, eager passes
+    # per-kernel durations: event pairs attached to each dispatch (its start
+    # and end on the GPU), over eager passes of the same inputs
     plan.profile_start(capacity=args.steps * L * 10 + 16)
     for _ in range(args.steps):
         one_pass()
     recs = plan.profile_stop()
     kern = {}
+    per_pass_step = np.zeros((args.steps, L))
+    per_step_k = [dict() for _ in range(L)]
+    seen = [0] * L
     for r in recs:
-        k = kern.setdefault(r["kernel"], {"launches": 0, "us": 0.0, "bytes": 0, "flops": 0})
+        t = r["step"]
+        k = kern.setdefault(r["kernel"], {"launches": 0, "us": 0.0, "bytes": 0, "flops": 0, "durations": []})
         k["launches"] += 1
         k["us"] += r["us"]
-        k["bytes"] += steps[r["step"]]["bytes"].get(r["kernel"], 0)
-        k["flops"] += steps[r["step"]]["flops"].get(r["kernel"], 0)
-    per_step_us = [0.0] * L
-    per_step_k = [dict() for _ in range(L)]
-    for r in recs:
-        per_step_us[r["step"]] += r["us"] / args.steps
-        kk = per_step_k[r["step"]]
+        k["durations"].append(r["us"])
+        k["bytes"] += steps[t]["bytes"].get(r["kernel"], 0)
+        k["flops"] += steps[t]["flops"].get(r["kernel"], 0)
+        kk = per_step_k[t]
         kk[r["kernel"]] = kk.get(r["kernel"], 0.0) + r["us"] / args.steps
+    # pass index of each record: records come pass by pass, step by step
+    launches_per_pass = len(recs) // args.steps
+    for i, r in enumerate(recs[:launches_per_pass * args.steps]):
+        per_pass_step[i // launches_per_pass, r["step"]] += r["us"]
     for s_ in steps:
-        s_["kernel_us"] = round(per_step_us[s_["t"]], 3)
-        s_["kernels_us"] = {k: round(v, 3) for k, v in per_step_k[s_["t"]].items()}
+        t = s_["t"]
+        s_["kernel_us"] = stats(per_pass_step[:, t].tolist())
+        s_["kernels_us"] = {k: round(v, 3) for k, v in per_step_k[t].items()}
     for name, k in kern.items():
         k["mean_us"] = k["us"] / k["launches"]
         k["share"] = k["us"] / sum(x["us"] for x in kern.values())
@@ -392,41 +410,28 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": ach / HBM_PEAK_GBS, "per_launch": kd["bytes"] / kd["launches"], "mean_us": kd["mean_us"],
                 "traffic": committed_traffic(dom, cfg.name)}
+    roof["timing"] = "dispatch events (kernel start to end on the GPU), eager passes of the benched inputs"
     kernels = {n: {"launches_per_pass": k["launches"] // args.steps, "mean_us": round(k["mean_us"], 3),
+                   "p50_us": round(float(np.percentile(k["durations"], 50)), 3),
                    "share": round(k["share"], 4),
                    "GB/s": round(k["bytes"] / (k["us"] * 1e-6) / 1e9, 1),
                    "TFLOP/s": round(k["flops"] / (k["us"] * 1e-6) / 1e12, 2) if k["flops"] else None}
                for n, k in kern.items()}
+    kernel_sum_us = sum(k["us"] for k in kern.values()) / args.steps
+    log("kernels: %.1f us of dispatch time per pass; dominant %s %.2f us/launch, %.4g %s (%.4f of peak)"
+        % (kernel_sum_us, dom, kd["mean_us"], roof["achieved"], roof["unit"], roof["frac"]))
 
-    # CPU baseline: the oracle on the host cores, same batch, same L steps
+    floor = measure_floor(torch, cb)
+    copy_gbs = measure_copy(torch)
+    log("floor: graph node of an empty kernel %s; copy %.0f GB/s"
+        % (", ".join("%s %.2f us" % (k[len("graph_node_"):-3], v) for k, v in floor.items()), copy_gbs))
+
+    # CPU baseline: the oracle on the host cores, same batch, same L steps; and
+    # the free-running GPU decode of this batch against the oracle's
     cpu = None
+    vs_oracle = None
     if not args.no_cpu:
-        import oracle
-        threads = min(16, os.cpu_count() or 1)
-        t0 = time.time()
-        # the pointer trie of 100M 12-token items does not fit the host: sorted ranges instead
-        kind = "sorted-range" if cfg.n_items > 50_000_000 else "pointer-trie"
-        T = oracle.SortedRange(items, cfg.V) if kind == "sorted-range" else oracle.Trie(items, cfg.V)
-        trie_s = time.time() - t0
-        bf16 = cfg.dtype == "bf16"
-        mkw = {} if args.mode == "filter_first" else {"mode": args.mode}
-        r0 = T.decode(K, dense["q"], dense["P"], dense["W"], bf16=bf16, trace=True, threads=threads, **mkw)
-        cexp = 0
-        for t in range(L):
-            for r in r0["trace_rows_in"][t]:
-                if r >= 0:
-                    cexp += V if args.mode == "unconstrained" else len(T.children_of_row(t, int(r))[0])
-        reps, el = 0, 0.0
-        while el < args.cpu_seconds and reps < 1000:
-            t0 = time.time()
-            T.decode(K, dense["q"], dense["P"], dense["W"], bf16=bf16, threads=threads, **mkw)
-            el += time.time() - t0
-            reps += 1
-        cpu = {"value": cexp * reps / el, "unit": "beam-expansions/s", "cores": threads, "kind": "oracle",
-               "sample": "the full batch (%d queries x %d steps, %d expansions per pass), %d passes, %.1f s; "
-                         "%s build (%.1f s) excluded" % (Q, L, cexp, reps, el, kind, trie_s),
-               "ms_per_pass": 1000 * el / reps}
-        del T
+        cpu, vs_oracle = cpu_leg(args, cfg, items, dense, rec, L, K, Q, V)
 
     value = expansions / (ms_per_pass * 1e-3)
     line = {
@@ -452,6 +457,8 @@ def main():
             "paths": paths,
         },
         "us_per_decode_step": ms_per_pass * 1000.0 / L,
+        "pass_ms": pass_ms,
+        "kernel_us_per_pass": kernel_sum_us,
         "expansions_per_pass": expansions,
         "decode_ms_with_model_standin": decode_ms,
         "decode_ms_step_by_step": decode_ms_steps,
@@ -459,12 +466,15 @@ def main():
         "decode_persistent_from_step": tail[0] if tail else None,
         "decode_persistent_us": tail_recs[0]["us"] if tail_recs else None,
         "decode_persistent_phases": phases,
+        "decode_vs_oracle": vs_oracle,
         "overlap_with_filter_first": overlap,
         "index": {"build_s": round(build_s, 2), "bytes": sum(i["bytes"] for i in info),
                   "rows": [i["n_rows"] for i in info], "storage": [i["storage"] for i in info]},
         "per_step": steps,
         "kernels": kernels,
         "tune": tune,
+        "floor": floor,
+        "copy_gbs": copy_gbs,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -475,6 +485,172 @@ def main():
         with open(args.json_out, "w") as f:
             f.write(out + "\n")
     print(out, flush=True)
+
+
+def stats(xs):
+    """mean / p50 / p95 / p99 / std / n of a list of times."""
+    a = np.asarray(xs, np.float64)
+    return {"mean": float(a.mean()), "p50": float(np.percentile(a, 50)), "p95": float(np.percentile(a, 95)),
+            "p99": float(np.percentile(a, 99)), "std": float(a.std()), "n": int(a.size)}
+
+
+def measure_floor(torch, cb):
+    """Overhead floor (FlashTrie's fixed per-launch cost): wall time per node
+    of a graph of empty kernels, replayed back to back, at grid shapes the step
+    kernels use (64 workgroups of 64 or 1024 threads, 256 and 2048 of 256).
+    This is the least a kernel of the graph-replayed pass costs."""
+    f = {}
+    nodes, reps = 50, 20
+    for blocks, threads in ((64, 64), (64, 1024), (256, 256), (2048, 256)):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            cb.floor_probe(blocks, threads, nodes, timed=False)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cb.floor_probe(blocks, threads, nodes, timed=False)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        f["graph_node_%dx%d_us" % (blocks, threads)] = e0.elapsed_time(e1) * 1000.0 / (reps * nodes)
+        del g
+    return f
+
+
+def measure_copy(torch):
+    """Device-to-device copy of 1 GiB: bytes read plus written per second (GB/s)."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_leg(args, cfg, items, dense, rec, L, K, Q, V):
+    """The oracle on the host: one thread and all the threads this process may
+    use (at most 16, the host share of one GPU), timed per pass over the same
+    batch; and the GPU's free-running decode of the batch against the oracle's
+    (identical, or diverging only where the step chose between candidates whose
+    oracle scores are within 1e-5 relative)."""
+    import oracle
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    threads = max(1, min(16, avail))
+    t0 = time.time()
+    # the pointer trie of 100M 12-token items does not fit the host: sorted ranges instead
+    kind = "sorted-range" if cfg.n_items > 50_000_000 else "pointer-trie"
+    T = oracle.SortedRange(items, cfg.V) if kind == "sorted-range" else oracle.Trie(items, cfg.V)
+    trie_s = time.time() - t0
+    bf16 = cfg.dtype == "bf16"
+    mkw = {} if args.mode == "filter_first" else {"mode": args.mode}
+    r0 = T.decode(K, dense["q"], dense["P"], dense["W"], bf16=bf16, trace=True, threads=threads, **mkw)
+    cexp = 0
+    for t in range(L):
+        for r in r0["trace_rows_in"][t]:
+            if r >= 0:
+                cexp += V if args.mode == "unconstrained" else len(T.children_of_row(t, int(r))[0])
+    runs = {}
+    for nth in sorted({1, threads}):
+        reps, el = 0, 0.0
+        budget = args.cpu_seconds if nth == threads else args.cpu_seconds / 2
+        while (el < budget and reps < 1000) or reps == 0:
+            t0 = time.time()
+            T.decode(K, dense["q"], dense["P"], dense["W"], bf16=bf16, threads=nth, **mkw)
+            el += time.time() - t0
+            reps += 1
+        runs[nth] = (reps, el)
+        log("cpu oracle, %d thread(s): %.2f ms per pass (%d passes)" % (nth, 1000 * el / reps, reps))
+    reps, el = runs[threads]
+    r1, e1 = runs[1]
+    cpu = {"value": cexp * reps / el, "unit": "beam-expansions/s", "cores": threads, "kind": "oracle",
+           "sample": "the full batch (%d queries x %d steps, %d expansions per pass), %d passes, %.1f s on %d "
+                     "threads; %s build (%.1f s) excluded" % (Q, L, cexp, reps, el, threads, kind, trie_s),
+           "ms_per_pass": 1000 * el / reps,
+           "single_thread": {"value": cexp * r1 / e1, "ms_per_pass": 1000 * e1 / r1, "passes": r1},
+           "host_cpus": os.cpu_count(), "affinity_cpus": avail, "cpu_model": cpu_model()}
+    vs = None
+    if args.mode == "filter_first":
+        vs = decode_vs_oracle(T, r0, rec, dense, L, K, Q)
+        log("decode vs oracle: %s" % vs)
+        assert not vs["unexplained"], "free-running GPU decode differs from the oracle away from a near tie"
+    return cpu, vs
+
+
+def decode_vs_oracle(T, r0, rec, dense, L, K, Q):
+    """Per query: identical item rows and sequences, or the first step where
+    the GPU's outputs differ is checked on the oracle's candidates of that step
+    (same inputs on both sides up to it): every position where the picks
+    differ must be between candidates whose oracle scores lie within
+    1e-5 * max(1, |score|)."""
+    g_rows = [rec["trace_rows"][t].cpu().numpy() for t in range(1, L)] + [rec["rows"].cpu().numpy()]
+    r_rows = [r0["trace_rows_in"][t] for t in range(1, L)] + [r0["rows"]]
+    g_seqs = rec["seqs"].cpu().numpy()
+    identical, tie, bad, max_gap = 0, 0, [], 0.0
+    cand = {}
+    for q in range(Q):
+        sl = slice(q * K, (q + 1) * K)
+        first = next((t for t in range(L) if not np.array_equal(g_rows[t][sl], r_rows[t][sl])), None)
+        if first is None and np.array_equal(g_seqs[sl], r0["seqs"][sl]):
+            identical += 1
+            continue
+        if first is None:
+            bad.append(q)
+            continue
+        if first not in cand:
+            cand[first] = T.step(first, K, r0["trace_h"][first], dense["W"][first], r0["trace_rows_in"][first],
+                                 r0["trace_acc_in"][first], candidates=True, threads=8)
+        o = cand[first]
+        score = {int(o["cand_rows"][q, j]): float(o["cand_scores"][q, j]) for j in range(int(o["cand_count"][q]))}
+        ok = True
+        for i in range(K):
+            a, b = int(g_rows[first][q * K + i]), int(r_rows[first][q * K + i])
+            if a == b:
+                continue
+            if a not in score or b not in score:
+                ok = False
+                break
+            gap = abs(score[a] - score[b])
+            max_gap = max(max_gap, gap)
+            if gap > 1e-5 * max(1.0, abs(score[b])):
+                ok = False
+                break
+        if ok:
+            tie += 1
+        else:
+            bad.append(q)
+    return {"queries": Q, "identical": identical, "near_tie_divergences": tie, "unexplained": bad,
+            "max_tie_gap": max_gap}
 
 
 if __name__ == "__main__":

@@ -54,6 +54,8 @@ SIGNATURES = {
     "cb_plan_create": (ctypes.c_int, [_P, _I32, _I32, _I32, ctypes.c_int, _PP]),
     "cb_set_path": (ctypes.c_int, [_P, _I32, ctypes.c_int]),
     "cb_get_path": (ctypes.c_int, [_P, _I32, _P]),
+    "cb_set_step_threads": (ctypes.c_int, [_P, _I32, _I32]),
+    "cb_get_step_threads": (ctypes.c_int, [_P, _I32, _P]),
     "cb_set_select": (ctypes.c_int, [_P, _I32, ctypes.c_int]),
     "cb_get_select": (ctypes.c_int, [_P, _I32, _P]),
     "cb_set_decode_fusion": (ctypes.c_int, [_P, _I32]),
@@ -70,6 +72,7 @@ SIGNATURES = {
     "cb_profile_phases": (ctypes.c_int, [_P, _P, _I32, _P]),
     "cb_index_save": (ctypes.c_int, [_P, ctypes.c_char_p]),
     "cb_index_load": (ctypes.c_int, [ctypes.c_char_p, _I32, _P]),
+    "cb_floor_probe": (ctypes.c_int, [_I32, _I32, _I32, _P, _P]),
     "cb_plan_destroy": (None, [_P]),
     "cb_last_error": (ctypes.c_char_p, []),
 }

@@ -104,6 +104,17 @@ class Index:
         return Plan(self, Q_max, K, d, dtype)
 
 
+def _check_tensor(device, name, x, dtype, shape):
+    """Raw pointer of a contiguous tensor on cuda:device of the given dtype and shape."""
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.device.index != device:
+        raise ValueError("%s must be a tensor on cuda:%d" % (name, device))
+    if x.dtype != dtype or tuple(x.shape) != tuple(shape) or not x.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor of shape %s (got %s %s)"
+                         % (name, dtype, tuple(shape), x.dtype, tuple(x.shape)))
+    return ctypes.c_void_p(x.data_ptr())
+
+
 def _dtype_code(dtype):
     torch = _torch()
     if dtype in ("bf16", torch.bfloat16):
@@ -144,6 +155,16 @@ class Plan:
         v = ctypes.c_int()
         C.check("cb_get_path", self._lib.cb_get_path(self._h, int(t), ctypes.byref(v)))
         return _PATH_NAMES[v.value]
+
+    def set_step_threads(self, t, threads):
+        """Workgroup size of the per-query sparse step at step t (256, 512,
+        1024, or 0 for the default)."""
+        C.check("cb_set_step_threads", self._lib.cb_set_step_threads(self._h, int(t), int(threads)))
+
+    def get_step_threads(self, t):
+        v = ctypes.c_int32()
+        C.check("cb_get_step_threads", self._lib.cb_get_step_threads(self._h, int(t), ctypes.byref(v)))
+        return v.value
 
     def set_select(self, t, select):
         """Top-K selection of step t: "auto", "lds" (K <= 64) or "radix"."""
@@ -186,13 +207,7 @@ class Plan:
         return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
 
     def _check_tensor(self, name, x, dtype, shape):
-        torch = _torch()
-        if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.device.index != self.device:
-            raise ValueError("%s must be a tensor on cuda:%d" % (name, self.device))
-        if x.dtype != dtype or tuple(x.shape) != tuple(shape) or not x.is_contiguous():
-            raise ValueError("%s must be a contiguous %s tensor of shape %s (got %s %s)"
-                             % (name, dtype, tuple(shape), x.dtype, tuple(x.shape)))
-        return ctypes.c_void_p(x.data_ptr())
+        return _check_tensor(self.device, name, x, dtype, shape)
 
     def step(self, t, hidden, W_t, rows, acc, out=None):
         """One decoding step (cb_step).  Returns (tokens, parents, rows, logp)."""
@@ -275,3 +290,19 @@ class Plan:
         n = ctypes.c_int32()
         C.check("cb_profile_phases", self._lib.cb_profile_phases(self._h, buf, self.L, ctypes.byref(n)))
         return [{"step": r.step, "select_us": r.select_us, "update_us": r.update_us} for r in buf[:n.value]]
+
+
+def floor_probe(blocks, threads, n, timed=True):
+    """Overhead floor (cb_floor_probe): n launches of an empty kernel of
+    ``blocks`` x ``threads`` on the current stream.  timed: returns (mean
+    dispatch duration, mean time per launch back to back) in microseconds;
+    otherwise only enqueues them (capturable) and returns None."""
+    torch = _torch()
+    lib = C.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if not timed:
+        C.check("cb_floor_probe", lib.cb_floor_probe(int(blocks), int(threads), int(n), None, stream))
+        return None
+    us = (ctypes.c_float * 2)()
+    C.check("cb_floor_probe", lib.cb_floor_probe(int(blocks), int(threads), int(n), us, stream))
+    return float(us[0]), float(us[1])

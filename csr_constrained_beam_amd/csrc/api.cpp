@@ -15,6 +15,9 @@ namespace {
 thread_local std::string g_err;
 }
 
+thread_local LaunchEvents g_launch_events;
+LaunchEvents& launch_events() { return g_launch_events; }
+
 void set_error(const std::string& msg) { g_err = msg; }
 void clear_error() { g_err.clear(); }
 
@@ -157,20 +160,20 @@ cb_status wide_alloc(cb_plan* p) {
     return CB_OK;
 }
 
-// Records an event pair around a launch while profiling is on.
+// While profiling is on, attaches an event pair to the dispatch of the one
+// kernel the next launcher call enqueues (its start and end as the GPU
+// records them, not the host's enqueue).
 struct ProfMark {
     cb_plan* p;
-    hipStream_t s;
     int idx = -1;
-    ProfMark(cb_plan* p_, hipStream_t s_, int t, int kernel, int threads, int blocks) : p(p_), s(s_) {
+    ProfMark(cb_plan* p_, hipStream_t, int t, int kernel, int threads, int blocks) : p(p_) {
         if (!p->prof_on || (int)p->prof_rec.size() >= p->prof_cap) return;
         idx = (int)p->prof_rec.size();
         p->prof_rec.push_back(cb_kernel_time{t, kernel, threads, blocks, 0.f});
-        (void)hipEventRecord(p->prof_ev[(size_t)idx * 2], s);
+        launch_events() = LaunchEvents{p->prof_ev[(size_t)idx * 2], p->prof_ev[(size_t)idx * 2 + 1]};
     }
-    void done() {
-        if (idx >= 0) (void)hipEventRecord(p->prof_ev[(size_t)idx * 2 + 1], s);
-    }
+    void done() { launch_events() = LaunchEvents{}; }
+    ~ProfMark() { launch_events() = LaunchEvents{}; }
 };
 
 // Enqueue one step on the radix selection (no validation).
@@ -274,8 +277,10 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const vo
             m.done();
             if (e != hipSuccess) return hip_fail("cb_step: wide-row scores", e);
         }
-        ProfMark m(p, s, t, CB_KERNEL_STEP_QUERY, query_threads(p->K), Q);
-        e = launch_step_query(sd, p->dtype, Q, p->K, Kc, p->d, hidden, Wt, rows, acc, split ? w.cand : nullptr,
+        const int nt = (size_t)t < p->query_nt.size() && query_threads_ok(p->query_nt[(size_t)t])
+                           ? p->query_nt[(size_t)t] : query_threads(p->K);
+        ProfMark m(p, s, t, CB_KERNEL_STEP_QUERY, nt, Q);
+        e = launch_step_query(sd, p->dtype, Q, p->K, Kc, p->d, nt, hidden, Wt, rows, acc, split ? w.cand : nullptr,
                               split ? w.cand_off : nullptr, split ? w.cap : 0, ot, op, orow, ol, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: sparse step", e);
@@ -602,6 +607,7 @@ cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_
     p->Kc_max = Kc;
     p->forced.assign((size_t)idx->L, CB_PATH_AUTO);
     p->tuned.assign((size_t)idx->L, 0);
+    p->query_nt.assign((size_t)idx->L, 0);
     p->tune_dense_us.assign((size_t)idx->L, -1.f);
     p->tune_sparse_us.assign((size_t)idx->L, -1.f);
     p->select.assign((size_t)idx->L, CB_SELECT_AUTO);
@@ -739,6 +745,33 @@ cb_status cb_get_select(const cb_plan* p, int32_t t, cb_select* sel) {
     return CB_OK;
 }
 
+cb_status cb_set_step_threads(cb_plan* p, int32_t t, int32_t threads) {
+    clear_error();
+    if (!p || t < 0 || t >= p->idx->L || (threads != 0 && !query_threads_ok(threads))) {
+        set_error("cb_set_step_threads: bad plan or step, or threads not 0, 256, 512 or 1024");
+        return CB_EINVAL;
+    }
+    const cb::StepTable& T = p->idx->steps[(size_t)t];
+    const int Kc = std::min(p->K, std::max(T.S, 1));
+    if (query_lds_bytes(T.S, p->K, Kc, p->d, threads) > (size_t)kMaxLds) {
+        set_error("cb_set_step_threads: the step's LDS does not fit that workgroup size");
+        return CB_ECAPACITY;
+    }
+    p->query_nt[(size_t)t] = threads;
+    return CB_OK;
+}
+
+cb_status cb_get_step_threads(const cb_plan* p, int32_t t, int32_t* threads) {
+    clear_error();
+    if (!p || !threads || t < 0 || t >= p->idx->L) {
+        set_error("cb_get_step_threads: bad plan, step or output");
+        return CB_EINVAL;
+    }
+    const int32_t v = p->query_nt[(size_t)t];
+    *threads = query_threads_ok(v) ? v : query_threads(p->K);
+    return CB_OK;
+}
+
 cb_status cb_get_path(const cb_plan* p, int32_t t, cb_path* path) {
     clear_error();
     if (!p || !path || t < 0 || t >= p->idx->L) {
@@ -838,7 +871,7 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
             // time every allowed (scoring path, selection) pair on this step's inputs, outputs to scratch
             float best_us[2] = {-1.f, -1.f};  // dense, sparse (either variant): best over the selections
             float best = -1.f;
-            int32_t best_path = 0, best_sel = 0;
+            int32_t best_path = 0, best_sel = 0, best_nt = 0;
             const int32_t paths[3] = {CB_PATH_DENSE, CB_PATH_SPARSE, CB_PATH_SPARSE_SPLIT};
             const int32_t sels[2] = {CB_SELECT_LDS, CB_SELECT_RADIX};
             const cb::StepTable& T = idx->steps[(size_t)t];
@@ -856,28 +889,37 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
                         clear_error();
                         continue;
                     }
-                    st = run_step(p, t, Q, paths[k], sels[m], p->h, Wt, p->rows[cur], p->acc[cur], p->scratch_tok,
-                                  p->scratch_par, p->scratch_rows, p->scratch_logp, s);
-                    if (st != CB_OK) break;
-                    (void)hipEventRecord(ev0, s);
-                    for (int r = 0; r < reps && st == CB_OK; ++r)
+                    // the per-query sparse step at its default workgroup size and at 256 threads
+                    // (same bits either way: a step of few multi-token rows starts faster on the smaller)
+                    const bool per_query = paths[k] != CB_PATH_DENSE && sels[m] == CB_SELECT_LDS && p->d <= kQueryMaxD;
+                    const int nts[2] = {0, 256};
+                    for (int v = 0; v < (per_query ? 2 : 1) && st == CB_OK; ++v) {
+                        p->query_nt[(size_t)t] = nts[v];
                         st = run_step(p, t, Q, paths[k], sels[m], p->h, Wt, p->rows[cur], p->acc[cur],
                                       p->scratch_tok, p->scratch_par, p->scratch_rows, p->scratch_logp, s);
-                    (void)hipEventRecord(ev1, s);
-                    if ((e = hipEventSynchronize(ev1)) != hipSuccess) {
-                        st = hip_fail("cb_tune: synchronise", e);
-                        break;
+                        if (st != CB_OK) break;
+                        (void)hipEventRecord(ev0, s);
+                        for (int r = 0; r < reps && st == CB_OK; ++r)
+                            st = run_step(p, t, Q, paths[k], sels[m], p->h, Wt, p->rows[cur], p->acc[cur],
+                                          p->scratch_tok, p->scratch_par, p->scratch_rows, p->scratch_logp, s);
+                        (void)hipEventRecord(ev1, s);
+                        if ((e = hipEventSynchronize(ev1)) != hipSuccess) {
+                            st = hip_fail("cb_tune: synchronise", e);
+                            break;
+                        }
+                        float ms = 0.f;
+                        (void)hipEventElapsedTime(&ms, ev0, ev1);
+                        const float us = ms * 1000.f / (float)reps;
+                        const int slot = paths[k] == CB_PATH_DENSE ? 0 : 1;
+                        if (best_us[slot] < 0.f || us < best_us[slot]) best_us[slot] = us;
+                        if (best < 0.f || us < best) {
+                            best = us;
+                            best_path = paths[k];
+                            best_sel = sels[m];
+                            best_nt = nts[v];
+                        }
                     }
-                    float ms = 0.f;
-                    (void)hipEventElapsedTime(&ms, ev0, ev1);
-                    const float us = ms * 1000.f / (float)reps;
-                    const int slot = paths[k] == CB_PATH_DENSE ? 0 : 1;
-                    if (best_us[slot] < 0.f || us < best_us[slot]) best_us[slot] = us;
-                    if (best < 0.f || us < best) {
-                        best = us;
-                        best_path = paths[k];
-                        best_sel = sels[m];
-                    }
+                    p->query_nt[(size_t)t] = 0;
                 }
             }
             if (st != CB_OK) break;
@@ -885,6 +927,7 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
             p->tune_sparse_us[(size_t)t] = best_us[1];
             if (best_path) p->tuned[(size_t)t] = best_path;
             if (best_sel) p->tuned_select[(size_t)t] = best_sel;
+            p->query_nt[(size_t)t] = best_nt;
         }
         st = run_step(p, t, Q, resolve_path(p, t), resolve_select(p, t), p->h, Wt, p->rows[cur], p->acc[cur],
                       p->hist_tok + (size_t)t * R, p->hist_par + (size_t)t * R, p->rows[1 - cur], p->acc[1 - cur], s);
@@ -1130,6 +1173,55 @@ cb_status cb_profile_phases(const cb_plan* p, cb_phase_time* out, int32_t cap, i
     if (out)
         for (int32_t i = 0; i < *n && i < cap; ++i) out[i] = p->phases[(size_t)i];
     return CB_OK;
+}
+
+cb_status cb_floor_probe(int32_t blocks, int32_t threads, int32_t n, float* us, void* stream) {
+    clear_error();
+    if (blocks < 1 || blocks > (1 << 20) || threads < 64 || threads > 1024 || threads % 64 || n < 1 || n > 4096) {
+        set_error("cb_floor_probe: need 1 <= blocks <= 2^20, threads a multiple of 64 in [64, 1024], 1 <= n <= 4096");
+        return CB_EINVAL;
+    }
+    const hipStream_t s = (hipStream_t)stream;
+    if (!us) {
+        for (int i = 0; i < n; ++i) {
+            hipError_t e = launch_empty(blocks, threads, s);
+            if (e != hipSuccess) return hip_fail("cb_floor_probe", e);
+        }
+        return CB_OK;
+    }
+    std::vector<hipEvent_t> ev((size_t)n * 2, nullptr);
+    cb_status st = CB_OK;
+    hipError_t e = hipSuccess;
+    for (auto& x : ev)
+        if ((e = hipEventCreate(&x)) != hipSuccess) {
+            st = hip_fail("cb_floor_probe: events", e);
+            break;
+        }
+    for (int i = 0; i < n && st == CB_OK; ++i) {
+        launch_events() = LaunchEvents{ev[(size_t)i * 2], ev[(size_t)i * 2 + 1]};
+        e = launch_empty(blocks, threads, s);
+        launch_events() = LaunchEvents{};
+        if (e != hipSuccess) st = hip_fail("cb_floor_probe", e);
+    }
+    if (st == CB_OK && (e = hipEventSynchronize(ev[(size_t)n * 2 - 1])) != hipSuccess)
+        st = hip_fail("cb_floor_probe: synchronise", e);
+    if (st == CB_OK) {
+        double sum = 0.0;
+        for (int i = 0; i < n && st == CB_OK; ++i) {
+            float ms = 0.f;
+            if ((e = hipEventElapsedTime(&ms, ev[(size_t)i * 2], ev[(size_t)i * 2 + 1])) != hipSuccess)
+                st = hip_fail("cb_floor_probe: elapsed", e);
+            sum += ms;
+        }
+        float all = 0.f;
+        if (st == CB_OK && (e = hipEventElapsedTime(&all, ev[0], ev[(size_t)n * 2 - 1])) != hipSuccess)
+            st = hip_fail("cb_floor_probe: elapsed", e);
+        us[0] = (float)(sum * 1000.0 / n);
+        us[1] = all * 1000.f / (float)n;
+    }
+    for (auto x : ev)
+        if (x) (void)hipEventDestroy(x);
+    return st;
 }
 
 void cb_plan_destroy(cb_plan* p) {

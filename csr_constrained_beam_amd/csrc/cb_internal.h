@@ -33,6 +33,15 @@ struct DeviceGuard {
     DeviceGuard& operator=(const DeviceGuard&) = delete;
 };
 
+// Events the next kernel launch of this thread attaches to its dispatch
+// (hipExtLaunchKernel: the events take the dispatch's own start and end
+// times).  Set by the kernel-timing support around one launcher call; both
+// null otherwise.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+
 // Device view of one step table.  Rows are the distinct length-t prefixes in
 // lexicographic order; row r's edges are row_ptr[r] .. row_ptr[r+1]-1, ascending
 // token, and edge e leads to row e of the next step.
@@ -115,6 +124,7 @@ struct cb_plan {
     int32_t Kc_max = 0;           // per-beam survivors kept: min(K, widest step)
     std::vector<int32_t> forced;  // per step: CB_PATH_* set by the caller
     std::vector<int32_t> tuned;   // per step: measured choice (0 = none)
+    std::vector<int32_t> query_nt;  // per step: workgroup size of the per-query sparse step (0 = default), measured
     std::vector<float> tune_dense_us, tune_sparse_us;
     // workspace (allocated once)
     uint64_t* keys = nullptr;     // [Q_max*K][Kc_max] per-beam survivors (dense path)
@@ -160,9 +170,11 @@ namespace cb {
 // Workgroup sizes and LDS bytes of the step kernels.
 int expand_threads(const StepDev& st);
 int query_threads(int K);
+bool query_threads_ok(int nt);
 size_t expand_lds_bytes(int S, int d, bool dense);
 int expand_bitmap_max_v();
-size_t query_lds_bytes(int S, int K, int Kc, int d);
+// LDS of the per-query sparse step at workgroup size nt (0: the default size).
+size_t query_lds_bytes(int S, int K, int Kc, int d, int nt = 0);
 int tail_threads(int K);
 size_t tail_lds_bytes(int S, int K, int Kc, int d);
 int gemm_blocks(cb_dtype dt, int R, int V);
@@ -171,7 +183,8 @@ int gemm_blocks(cb_dtype dt, int R, int V);
 // pre / pre_off / pre_cap: scores of the wide rows from launch_wide_score(...,
 // wide_only = 1, ...) (candidate z bits in the high half, per-query offsets
 // [K+1], per-query capacity), or null to score them in the step kernel.
-hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int Kc, int d, const void* hidden,
+// nt: workgroup size (256, 512 or 1024; 0 = query_threads(K)); every size gives the same bits.
+hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int Kc, int d, int nt, const void* hidden,
                              const void* W, const int32_t* beam_rows, const float* acc, const uint64_t* pre,
                              const int32_t* pre_off, int64_t pre_cap, int32_t* tok, int32_t* par, int32_t* rows,
                              float* logp, hipStream_t s);
@@ -196,6 +209,7 @@ hipError_t launch_decode_init(int Q, int K, int d, cb_dtype dt, const float* q, 
 hipError_t launch_hidden_update(int R, int K, int d, cb_dtype dt, const float* s_old, const float* P_t,
                                 const int32_t* tok, const int32_t* par, float* s_new, void* h_out,
                                 hipStream_t st);
+hipError_t launch_empty(int blocks, int threads, hipStream_t s);
 hipError_t launch_backtrace(int R, int K, int L, const int32_t* hist_tok, const int32_t* hist_par,
                             int32_t* seqs, hipStream_t s);
 // Steps t0..L-1 of a decode (sparse, LDS selection) with the hidden updates

@@ -4,12 +4,25 @@
 // constants of the full-codebook product.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 
 #include "cb_internal.h"
+
+// Every launch of the library goes through this: an ordinary launch, or,
+// while the thread's timing events are set (eager kernel timing only), the
+// launch with those events attached to its dispatch.
+#define CB_LAUNCH(kernel, grid, block, lds, stream, ...)                                                   \
+    do {                                                                                                   \
+        const ::cb::LaunchEvents cb_ev_ = ::cb::launch_events();                                          \
+        if (cb_ev_.start || cb_ev_.stop)                                                                   \
+            hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, cb_ev_.start, cb_ev_.stop, 0, __VA_ARGS__); \
+        else                                                                                               \
+            hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                             \
+    } while (0)
 
 namespace cb {
 namespace {
@@ -611,36 +624,45 @@ __device__ void block_scores_ch(const float* h_s, const DT* __restrict__ W, int 
     }
 }
 
-// a3 for one beam, whole block: log-sum-exp of z_s[0..n).  Workgroups of at
-// least kLseSlots threads sum over kLseSlots fixed slots (slot s takes the
-// terms s, s + kLseSlots, ...) reduced in a fixed order, so that every such
-// workgroup size gives the same bits (the per-query step of 512 and of 1024
-// threads, and the persistent decode, agree exactly); the maximum is exact in
-// any order.
+// a3 for one beam, whole block: log-sum-exp of z_s[0..n).  The sum runs over
+// kLseSlots fixed slots (slot s takes the terms s, s + kLseSlots, ...); the
+// slots form groups of 64, each summed by one wave's butterfly, and the group
+// sums are added in group order.  Every workgroup size gives the same bits
+// (a wave takes the groups w, w + NW, ...), so the per-query step at any size,
+// the persistent decode and the per-beam expansion agree exactly; the maximum
+// is exact in any order.  red_f: LDS [max(NT / 64, kLseSlots / 64)].
 constexpr int kLseSlots = 512;
+constexpr int kLseGroups = kLseSlots / 64;
 template <int NT>
 __device__ float block_lse(const float* z_s, int n, float* red_f) {
+    constexpr int NW = NT / kWave;
     float m = -INFINITY;
     for (int j = threadIdx.x; j < n; j += NT) m = fmaxf(m, z_s[j]);
     m = block_max<NT>(m, red_f);
-    float se = 0.f;
-    if constexpr (NT >= kLseSlots) {
-        if (threadIdx.x < kLseSlots)
-            for (int j = threadIdx.x; j < n; j += kLseSlots) se += exp_sm(z_s[j] - m);
-        se = wave_sum(se);
-        const int w = threadIdx.x / kWave;
-        if ((threadIdx.x & (kWave - 1)) == 0 && w < kLseSlots / kWave) red_f[w] = se;
-        __syncthreads();
-        float r = red_f[0];
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
 #pragma unroll
-        for (int i = 1; i < kLseSlots / kWave; ++i) r += red_f[i];
-        __syncthreads();
-        se = r;
-    } else {
-        for (int j = threadIdx.x; j < n; j += NT) se += exp_sm(z_s[j] - m);
-        se = block_sum<NT>(se, red_f);
+    for (int g0 = 0; g0 < kLseGroups; g0 += NW) {
+        const int g = g0 + w;
+        if (g < kLseGroups) {  // uniform over the wave
+            float se = 0.f;
+            for (int j = g * kWave + lane; j < n; j += kLseSlots) se += exp_sm(z_s[j] - m);
+            se = wave_sum(se);
+            if (lane == 0) red_f[g] = se;
+        }
     }
-    return m + logf(se);
+    __syncthreads();
+    float r = red_f[0];
+#pragma unroll
+    for (int i = 1; i < kLseGroups; ++i) r += red_f[i];
+    __syncthreads();
+    return m + logf(r);
+}
+
+// Entries of the reduction scratch a block needs (block_max / block_sum /
+// block_lse).
+template <int NT>
+constexpr int red_slots() {
+    return NT / kWave > kLseGroups ? NT / kWave : kLseGroups;
 }
 
 

@@ -177,6 +177,8 @@ __host__ __device__ inline QueryLds query_lds(int S, int K, int Kc, int d, int N
 // and accumulated log-probs (global or LDS).  smem: the query_lds layout of
 // this step; best: LDS [64], left holding the query's K winning keys;
 // nrows / nacc: NULL, or LDS [K] receiving the next rows and log-probs.
+// Every sum is per wave or over fixed slots, so any workgroup size (a
+// multiple of 64) gives the same bits.
 template <typename DT, int NT, int CH>
 __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d, const DT* __restrict__ hidden,
                                  const DT* __restrict__ W, const int32_t* __restrict__ rows_q,
@@ -185,21 +187,24 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
                                  int32_t* __restrict__ out_par, int32_t* __restrict__ out_rows,
                                  float* __restrict__ out_logp, unsigned char* smem, uint64_t* best,
                                  int32_t* nrows, float* nacc) {
-    __shared__ float red_f[NT / kWave];
+    __shared__ float red_f[red_slots<NT>()];
     __shared__ int red_i[NT / kWave];
     __shared__ uint64_t bcast;
     // per beam, from its row: row, accumulated log-prob, row start, width
-    // (negative: -1 - width of a row too wide for phase 1)
+    // (negative: -1 - width of a row too wide for phases 1 / 1b)
     __shared__ int32_t r_s[kWave];
     __shared__ float a_s[kWave];
     __shared__ uint32_t e0_s[kWave];
     __shared__ int n_s[kWave];
     __shared__ int nbig;
     __shared__ int big[kWave];
+    __shared__ int nsm;               // rows of 2..kSmallRow tokens (their tokens are read in phase 1)
+    __shared__ int sml[kWave];
     __shared__ int nmid;              // rows scored by the whole block (phase 1b)
     __shared__ int mid[kWave];
     __shared__ int moff[kWave + 1];   // their first task
     __shared__ int ncand;             // keys in the candidate list qkeys
+    __shared__ int ident;             // the step is the identity (see the prologue)
     __shared__ uint64_t slot[kWave];  // survivors of one wide row
     const QueryLds lay = query_lds(st.S, K, Kc, d, NT);
     uint64_t* qkeys = reinterpret_cast<uint64_t*>(smem + lay.qkeys);
@@ -213,77 +218,111 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
     constexpr int NW = NT / kWave;
-    if (tid == 0) {
-        nbig = 0;
-        nmid = 0;
-        ncand = 0;
+
+    // prologue, one lane per beam (wave 0; K <= 64): the beam's row and
+    // accumulated log-prob, then its row pointers and first token, all beams'
+    // loads in flight together.  A row with one valid token needs nothing
+    // more: its log-softmax is exactly 0 whatever its score (z - (z + log 1)),
+    // so neither its hidden vector nor its W_t row is read and its candidate
+    // key is the beam's accumulated log-prob.  Rows of 2..64 tokens (CSR) go
+    // to phase 1, wider rows and bitmap rows to phase 2.
+    if (wv == 0) {
+        const int k = lane;
+        const int32_t r = k < K ? rows_q[k] : -1;
+        const float a = k < K ? acc_q[k] : -INFINITY;
+        const bool live = k < K && beam_live(st, r, a);
+        const uint32_t e0 = live ? st.row_ptr[r] : 0u;
+        const int n = live ? (int)(st.row_ptr[r + 1] - e0) : 0;
+        const int f0 = live && st.tok0 ? (int)st.tok0[r] : 0;  // in flight with row_ptr
+        const bool csr = st.store == CB_STORE_CSR;
+        const bool one = live && csr && n == 1 && st.tok0;
+        const bool narrow = live && csr && !one && n <= kSmallRow;
+        // rows above kMidRow tokens (scores not computed apart) are scored by the block (phase 1b)
+        const bool midr = narrow && n > kMidRow && !(pre && n > kPreMin);
+        const bool wide = live && !one && !narrow;
+        if (live) {
+            r_s[k] = r;
+            a_s[k] = a;
+            e0_s[k] = e0;
+            n_s[k] = (one || narrow) ? n : -1 - n;
+        }
+        if (one) tokq[k * kWave] = (uint16_t)f0;
+        const uint64_t key = one ? make_key(a + 0.f, k, f0) : 0ull;
+        const uint64_t m_one = __ballot(one), m_nar = __ballot(narrow), m_mid = __ballot(midr),
+                       m_wide = __ballot(wide), m_live = __ballot(live);
+        const uint64_t below = (1ull << lane) - 1ull;
+        if (one) qkeys[__popcll(m_one & below)] = key;
+        if (narrow) sml[__popcll(m_nar & below)] = k;
+        if (midr) mid[__popcll(m_mid & below)] = k;
+        if (wide) big[__popcll(m_wide & below)] = k;
+        // identity: every live row has one token, the live slots come first
+        // and their log-probs do not increase, so the K candidates (acc_k,
+        // k, token) are already in (score desc, parent asc) order and slot i
+        // of the output is beam i
+        const float a_prev = __shfl(a, lane > 0 ? lane - 1 : 0);
+        const bool viol = live && lane > 0 && !(a_prev >= a);
+        const bool id = m_live == m_one && (m_live & (m_live + 1ull)) == 0ull && __ballot(viol) == 0ull;
+        if (id) {
+            best[lane] = key;
+            if (k < K) {
+                const int64_t o = (int64_t)q * K + k;
+                out_tok[o] = one ? f0 : -1;
+                out_par[o] = one ? k : -1;
+                out_rows[o] = one ? (int32_t)e0 : -1;
+                out_logp[o] = one ? a + 0.f : -INFINITY;
+                if (nrows) {
+                    nrows[k] = one ? (int32_t)e0 : -1;
+                    nacc[k] = one ? a + 0.f : -INFINITY;
+                }
+            }
+        }
+        if (lane == 0) {
+            ncand = __popcll(m_one);
+            nsm = __popcll(m_nar);
+            nmid = __popcll(m_mid);
+            nbig = __popcll(m_wide);
+            ident = id;
+        }
     }
     __syncthreads();
+    if (ident) return;  // uniform over the workgroup
 
-    // phase 1: one wave per beam with a narrow CSR row; each wave takes two
-    // beams at a time so that their chains of dependent loads overlap
-    for (int k0 = wv; k0 < K; k0 += 2 * NW) {
+    // phase 1: one wave per row of 2..64 tokens, two rows per wave in flight:
+    // lane j holds the row's token j; rows of up to kMidRow tokens (and rows
+    // whose scores were computed apart) are scored here, the rest in phase 1b
+    const int ns = nsm;
+    for (int i0 = wv; i0 < ns; i0 += 2 * NW) {
         int kk[2], tk[2], n[2];
-        int64_t b[2];
         float a[2];
-        bool small[2], midr[2];
+        bool on2[2], midr[2];
         uint32_t e0[2];
-        int32_t r[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            kk[u] = k0 + u * NW;
-            b[u] = (int64_t)q * K + kk[u];
-            r[u] = kk[u] < K ? rows_q[kk[u]] : -1;
-            a[u] = kk[u] < K ? acc_q[kk[u]] : -INFINITY;
-        }
-        // every global load of both beams is issued before the LDS bookkeeping
-        // (atomics), which the compiler does not move loads across: the two
-        // chains row -> row_ptr -> token then overlap
-        bool live[2];
-        int f0[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            live[u] = kk[u] < K && beam_live(st, r[u], a[u]);
-            e0[u] = live[u] ? st.row_ptr[r[u]] : 0u;
-            n[u] = live[u] ? (int)(st.row_ptr[r[u] + 1] - e0[u]) : 0;
-            f0[u] = live[u] && st.tok0 ? (int)st.tok0[r[u]] : 0;  // in flight with row_ptr
+            const int i = i0 + u * NW;
+            on2[u] = i < ns;
+            kk[u] = on2[u] ? sml[i] : 0;
+            n[u] = on2[u] ? n_s[kk[u]] : 0;
+            e0[u] = on2[u] ? e0_s[kk[u]] : 0u;
+            a[u] = on2[u] ? a_s[kk[u]] : -INFINITY;
+            midr[u] = on2[u] && n[u] > kMidRow && !(pre && n[u] > kPreMin);
+            tk[u] = on2[u] && lane < n[u] ? (int)st.tok[e0[u] + lane] : 0;
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            small[u] = live[u] && n[u] <= kSmallRow && st.store == CB_STORE_CSR;
-            // rows of more than kMidRow tokens (scores not computed apart) go to phase 1b
-            midr[u] = small[u] && n[u] > kMidRow && !(pre && n[u] > kPreMin);
-            tk[u] = small[u] && lane < n[u] ? (lane == 0 && st.tok0 ? f0[u] : (int)st.tok[e0[u] + lane]) : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            if (midr[u] && lane == 0) mid[atomicAdd(&nmid, 1)] = kk[u];
-            if (live[u]) {
-                if (lane == 0) {
-                    r_s[kk[u]] = r[u];
-                    a_s[kk[u]] = a[u];
-                    e0_s[kk[u]] = e0[u];
-                    n_s[kk[u]] = small[u] ? n[u] : -1 - n[u];
-                }
-                if (!small[u] && lane == 0) big[atomicAdd(&nbig, 1)] = kk[u];
-            }
-            if (small[u] && lane < n[u]) tokq[kk[u] * kWave + lane] = (uint16_t)tk[u];
-        }
-        if (!small[0] && !small[1]) continue;
+        for (int u = 0; u < 2; ++u)
+            if (on2[u] && lane < n[u]) tokq[kk[u] * kWave + lane] = (uint16_t)tk[u];
         // rows whose scores were computed apart are read, the others scored here
         bool dots[2];
         float z[2] = {-INFINITY, -INFINITY};
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const bool ready = pre && small[u] && n[u] > kPreMin;
-            // a row with one valid token: its log-softmax is exactly 0 whatever
-            // its score, so neither the hidden vector nor the W_t row is read
-            dots[u] = small[u] && !ready && n[u] > 1 && !midr[u];
-            if (small[u] && n[u] == 1) z[u] = 0.f;
+            const bool ready = pre && on2[u] && n[u] > kPreMin;
+            dots[u] = on2[u] && !ready && !midr[u];
             if (ready && lane < n[u])
                 z[u] = __uint_as_float((uint32_t)(pre[(int64_t)q * pre_cap + pre_off[(int64_t)q * (K + 1) + kk[u]] +
                                                       lane] >> 32));
         }
+        // rows for phase 1b only needed their tokens
+        if (!(on2[0] && !midr[0]) && !(on2[1] && !midr[1])) continue;
         // hidden vectors kept raw until used (a conversion right after the
         // load would make each load wait before the next is issued)
         Raw8<DT> hr[2][CH];
@@ -292,7 +331,7 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
                 const int i = c * kWave * 8 + lane * 8;
-                if (dots[u] && i < d) hr[u][c].load(hidden + b[u] * d + i);
+                if (dots[u] && i < d) hr[u][c].load(hidden + ((int64_t)q * K + kk[u]) * d + i);
                 else hr[u][c].zero();
             }
         const int nmax = max(dots[0] ? n[0] : 0, dots[1] ? n[1] : 0);
@@ -330,19 +369,13 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            if (!small[u] || midr[u]) continue;
+            if (!on2[u] || midr[u]) continue;
             const bool on = lane < n[u];
-            uint64_t key;
-            if (n[u] == 1) {
-                // one valid token: log-softmax exactly 0, no reductions
-                key = on ? make_key(a[u] + 0.f, kk[u], tk[u]) : 0ull;
-            } else {
-                const int w = pow2_at_least(n[u]);
-                const float m = wave_max_w(on ? z[u] : -INFINITY, w);
-                const float se = wave_sum_w(on ? exp_sm(z[u] - m) : 0.f, w);
-                const float lse = m + logf(se);
-                key = on ? make_key(a[u] + (z[u] - lse), kk[u], tk[u]) : 0ull;
-            }
+            const int w = pow2_at_least(n[u]);
+            const float m = wave_max_w(on ? z[u] : -INFINITY, w);
+            const float se = wave_sum_w(on ? exp_sm(z[u] - m) : 0.f, w);
+            const float lse = m + logf(se);
+            uint64_t key = on ? make_key(a[u] + (z[u] - lse), kk[u], tk[u]) : 0ull;
             if (n[u] > Kc) key = wave_sort_desc(key);
             // the beam's best min(n, Kc) join the query's candidate list
             wave_append(lane < min(n[u], Kc), key, qkeys, &ncand);
@@ -511,7 +544,7 @@ __global__ __launch_bounds__(NT) void k_beam_expand(StepDev st, int K, int Kc, i
                                                     int mode) {
     auto split_of = [&](const int32_t* nl) { return split_ok ? gemm_split(*nl, (int)ldz, d) : 1; };
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ float red_f[NT / kWave];
+    __shared__ float red_f[red_slots<NT>()];
     __shared__ int red_i[NT / kWave];
     __shared__ uint64_t bcast;
     const ExpandLds lay = expand_lds(st.S, d, DENSE, NT);
@@ -1171,6 +1204,10 @@ __global__ __launch_bounds__(NT) void k_decode_tail(const StepDev* __restrict__ 
     }
 }
 
+// Does nothing: the fixed cost of a dispatch (launch, wave start and drain)
+// for the overhead floor.
+__global__ void k_empty(int) {}
+
 __global__ void k_backtrace(int R, int K, int L, const int32_t* __restrict__ hist_tok,
                             const int32_t* __restrict__ hist_par, int32_t* __restrict__ seqs) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
@@ -1196,6 +1233,8 @@ int expand_threads(const StepDev&) { return kExpandThreads; }
 
 int query_threads(int K) { return K >= 16 ? 1024 : 512; }
 
+bool query_threads_ok(int nt) { return nt == 256 || nt == 512 || nt == 1024; }
+
 // The persistent decode runs every step and every hidden update of a query in
 // one workgroup; with 512 threads its per-wave register budget doubles (the
 // 1024-thread build spills the update's registers).  The per-query step gives
@@ -1206,25 +1245,29 @@ size_t expand_lds_bytes(int S, int d, bool dense) { return (size_t)expand_lds(S,
 
 int expand_bitmap_max_v() { return 64 * kWave; }
 
-size_t query_lds_bytes(int S, int K, int Kc, int d) {
-    return (size_t)query_lds(S, K, Kc, d, query_threads(K)).total;
+size_t query_lds_bytes(int S, int K, int Kc, int d, int nt) {
+    return (size_t)query_lds(S, K, Kc, d, query_threads_ok(nt) ? nt : query_threads(K)).total;
 }
 
 size_t tail_lds_bytes(int S, int K, int Kc, int d) { return (size_t)query_lds(S, K, Kc, d, tail_threads(K)).total; }
 
-hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int Kc, int d, const void* hidden,
+hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int Kc, int d, int nt, const void* hidden,
                              const void* W, const int32_t* beam_rows, const float* acc, const uint64_t* pre,
                              const int32_t* pre_off, int64_t pre_cap, int32_t* tok, int32_t* par, int32_t* rows,
                              float* logp, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
-    const int NT = query_threads(K);
+    const int NT = nt == 256 || nt == 512 || nt == 1024 ? nt : query_threads(K);
     const QueryLds lay = query_lds(st.S, K, Kc, d, NT);
     const int CH = (d + kWave * 8 - 1) / (kWave * 8);
 #define CB_QUERY(DT, NTV, CHV)                                                                           \
-    hipLaunchKernelGGL((k_step_query<DT, NTV, CHV>), dim3(Q), dim3(NTV), lay.total, s, st, K, Kc, d,     \
+    CB_LAUNCH((k_step_query<DT, NTV, CHV>), dim3(Q), dim3(NTV), lay.total, s, st, K, Kc, d,     \
                        (const DT*)hidden, (const DT*)W, beam_rows, acc, pre, pre_off, pre_cap, tok, par, rows, logp)
-#define CB_QUERY_NT(DT, CHV) \
-    do { if (NT == 1024) CB_QUERY(DT, 1024, CHV); else CB_QUERY(DT, 512, CHV); } while (0)
+#define CB_QUERY_NT(DT, CHV)                              \
+    do {                                                  \
+        if (NT == 1024) CB_QUERY(DT, 1024, CHV);          \
+        else if (NT == 512) CB_QUERY(DT, 512, CHV);       \
+        else CB_QUERY(DT, 256, CHV);                      \
+    } while (0)
     if (dt == CB_BF16) {
         if (CH <= 1) CB_QUERY_NT(uint16_t, 1);
         else if (CH == 2) CB_QUERY_NT(uint16_t, 2);
@@ -1250,7 +1293,7 @@ hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R,
         const int M = (int)((ldz + kWave - 1) / kWave);
         const dim3 grid((R + 3) / 4);
 #define CB_EXPAND_BM(MV)                                                                                        \
-    hipLaunchKernelGGL((k_expand_bitmap<MV>), grid, dim3(256), 0, s, st, R, K, Kc, (int)ldz, d, Z, Zp, n_live, \
+    CB_LAUNCH((k_expand_bitmap<MV>), grid, dim3(256), 0, s, st, R, K, Kc, (int)ldz, d, Z, Zp, n_live, \
                        ci_of, beam_rows, acc, keys, mode)
         if (M <= 4) CB_EXPAND_BM(4);
         else if (M <= 8) CB_EXPAND_BM(8);
@@ -1262,7 +1305,7 @@ hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R,
     }
     const ExpandLds lay = expand_lds(st.S, d, dense, kExpandThreads);
 #define CB_EXPAND(DT, DENSE)                                                                                     \
-    hipLaunchKernelGGL((k_beam_expand<DT, DENSE, kExpandThreads>), dim3(R), dim3(kExpandThreads), lay.total, s, \
+    CB_LAUNCH((k_beam_expand<DT, DENSE, kExpandThreads>), dim3(R), dim3(kExpandThreads), lay.total, s, \
                        st, K, Kc, d, (const DT*)hidden, (const DT*)W, Z, Zp, ldz, n_live, ci_of, split_ok,        \
                        beam_rows, acc, keys, mode)
     if (dt == CB_BF16) {
@@ -1281,7 +1324,7 @@ hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uin
     const int M = (K * Kc + kWave - 1) / kWave;
     const dim3 grid((Q + 3) / 4);
 #define CB_MERGE(MV)                                                                                      \
-    hipLaunchKernelGGL((k_query_merge_w<MV>), grid, dim3(256), 0, s, st, Q, K, Kc, keys, beam_rows, tok, par, \
+    CB_LAUNCH((k_query_merge_w<MV>), grid, dim3(256), 0, s, st, Q, K, Kc, keys, beam_rows, tok, par, \
                        rows, logp, mode)
     if (M <= 1) CB_MERGE(1);
     else if (M <= 4) CB_MERGE(4);
@@ -1293,7 +1336,7 @@ hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uin
 
 hipError_t launch_live_rows(const StepDev& st, int R, const int32_t* beam_rows, const float* acc, int32_t* live,
                             int32_t* n_live, int32_t* ci_of, hipStream_t s) {
-    hipLaunchKernelGGL((k_live_rows<1024>), dim3(1), dim3(1024), 0, s, st, R, beam_rows, acc, live, n_live, ci_of);
+    CB_LAUNCH((k_live_rows<1024>), dim3(1), dim3(1024), 0, s, st, R, beam_rows, acc, live, n_live, ci_of);
     return hipGetLastError();
 }
 
@@ -1308,12 +1351,12 @@ hipError_t launch_gemm_scores(cb_dtype dt, int R, int V, int d, const int32_t* l
             (const void*)k_gemm_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
         if (lds_ok != hipSuccess) return lds_ok;
         const int fold = gemm_finds_live(dt, R) ? R : 0;
-        hipLaunchKernelGGL(k_gemm_bf16, dim3(gemm_grid(R, V)), dim3(kGemmThreads), kGemmLds, s, V, d, live, n_live,
+        CB_LAUNCH(k_gemm_bf16, dim3(gemm_grid(R, V)), dim3(kGemmThreads), kGemmLds, s, V, d, live, n_live,
                            (const uint16_t*)H, (const uint16_t*)W, Z, Zp, (int64_t)V, st, fold, beam_rows, acc,
                            ci_of);
     } else {
         dim3 grid((V + 15) / 16, (R + 15) / 16);
-        hipLaunchKernelGGL(k_gemm_f32, grid, dim3(256), 0, s, V, d, live, n_live, (const float*)H, (const float*)W,
+        CB_LAUNCH(k_gemm_f32, grid, dim3(256), 0, s, V, d, live, n_live, (const float*)H, (const float*)W,
                            Z, (int64_t)V);
     }
     return hipGetLastError();
@@ -1330,10 +1373,10 @@ hipError_t launch_decode_init(int Q, int K, int d, cb_dtype dt, const float* q, 
     const int R = Q * K;
     if (R <= 0) return hipSuccess;
     if (dt == CB_BF16)
-        hipLaunchKernelGGL((k_decode_init<uint16_t, 256>), dim3(R), dim3(256), 0, st, K, d, q, s_out,
+        CB_LAUNCH((k_decode_init<uint16_t, 256>), dim3(R), dim3(256), 0, st, K, d, q, s_out,
                            (uint16_t*)h_out, rows, acc);
     else
-        hipLaunchKernelGGL((k_decode_init<float, 256>), dim3(R), dim3(256), 0, st, K, d, q, s_out, (float*)h_out,
+        CB_LAUNCH((k_decode_init<float, 256>), dim3(R), dim3(256), 0, st, K, d, q, s_out, (float*)h_out,
                            rows, acc);
     return hipGetLastError();
 }
@@ -1351,7 +1394,7 @@ hipError_t launch_hidden_update(int R, int K, int d, cb_dtype dt, const float* s
     const dim3 grid((R + 3) / 4);
     const bool vec = hidden_vec_ok(d, P_t);
 #define CB_HU(DT, V) \
-    hipLaunchKernelGGL((k_hidden_update<DT, V>), grid, dim3(256), 0, st, R, K, d, s_old, P_t, tok, par, s_new, (DT*)h_out)
+    CB_LAUNCH((k_hidden_update<DT, V>), grid, dim3(256), 0, st, R, K, d, s_old, P_t, tok, par, s_new, (DT*)h_out)
     if (dt == CB_BF16) {
         if (vec) CB_HU(uint16_t, true); else CB_HU(uint16_t, false);
     } else {
@@ -1371,7 +1414,7 @@ hipError_t launch_decode_tail(const StepDev* d_steps, size_t lds, int t0, int L,
     const int R = Q * K;
     const bool vec = hidden_vec_ok(d, P);
 #define CB_TAIL(DT, NTV, CHV, VV)                                                                                  \
-    hipLaunchKernelGGL((k_decode_tail<DT, NTV, CHV, VV>), dim3(Q), dim3(NTV), lds, s, d_steps, t0, L, K, d, V, R, \
+    CB_LAUNCH((k_decode_tail<DT, NTV, CHV, VV>), dim3(Q), dim3(NTV), lds, s, d_steps, t0, L, K, d, V, R, \
                        (const DT*)W, P, s0, s1, (DT*)h, rows0, rows1, acc0, acc1, hist_tok, hist_par, clk)
 #define CB_TAIL_V(DT, NTV, CHV) \
     do { if (vec) CB_TAIL(DT, NTV, CHV, true); else CB_TAIL(DT, NTV, CHV, false); } while (0)
@@ -1392,10 +1435,15 @@ hipError_t launch_decode_tail(const StepDev* d_steps, size_t lds, int t0, int L,
     return hipGetLastError();
 }
 
+hipError_t launch_empty(int blocks, int threads, hipStream_t s) {
+    CB_LAUNCH(k_empty, dim3(blocks), dim3(threads), 0, s, 0);
+    return hipGetLastError();
+}
+
 hipError_t launch_backtrace(int R, int K, int L, const int32_t* hist_tok, const int32_t* hist_par, int32_t* seqs,
                             hipStream_t s) {
     if (R <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_backtrace, dim3((R + 255) / 256), dim3(256), 0, s, R, K, L, hist_tok, hist_par, seqs);
+    CB_LAUNCH(k_backtrace, dim3((R + 255) / 256), dim3(256), 0, s, R, K, L, hist_tok, hist_par, seqs);
     return hipGetLastError();
 }
 

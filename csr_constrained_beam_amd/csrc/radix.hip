@@ -612,7 +612,7 @@ hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, 
     const size_t lds = wide_score_lds_bytes(d, dense);
     const int split_ok = dt == CB_BF16 ? 1 : 0;
 #define CB_WSCORE(DT, DENSE)                                                                                  \
-    hipLaunchKernelGGL((k_wide_score<DT, DENSE>), grid, dim3(kWThreads), lds, s, st, K, d, (const DT*)hidden, \
+    CB_LAUNCH((k_wide_score<DT, DENSE>), grid, dim3(kWThreads), lds, s, st, K, d, (const DT*)hidden, \
                        (const DT*)W, Z, Zp, ldz, n_live, ci_of, split_ok, beam_rows, acc, wide_only, w, G)
     if (dt == CB_BF16) {
         if (dense) CB_WSCORE(uint16_t, true); else CB_WSCORE(uint16_t, false);
@@ -626,21 +626,21 @@ hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, 
 hipError_t launch_wide_keys(int Q, int K, const float* acc, const WideDev& w, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
     const int G = wide_hist_blocks_per_query(Q);
-    hipLaunchKernelGGL(k_wide_keys, dim3(Q * G), dim3(kWThreads), 0, s, K, acc, w, G);
+    CB_LAUNCH(k_wide_keys, dim3(Q * G), dim3(kWThreads), 0, s, K, acc, w, G);
     return hipGetLastError();
 }
 
 hipError_t launch_wide_refine(int Q, int K, const WideDev& w, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
     const int G = wide_hist_blocks_per_query(Q);
-    hipLaunchKernelGGL(k_wide_refine, dim3(Q * G), dim3(kWThreads), 0, s, K, w, G);
+    CB_LAUNCH(k_wide_refine, dim3(Q * G), dim3(kWThreads), 0, s, K, w, G);
     return hipGetLastError();
 }
 
 hipError_t launch_wide_collect(int Q, int K, const WideDev& w, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
     const int G = wide_hist_blocks_per_query(Q);
-    hipLaunchKernelGGL(k_wide_collect, dim3(Q * G), dim3(kWThreads), 0, s, K, w, G);
+    CB_LAUNCH(k_wide_collect, dim3(Q * G), dim3(kWThreads), 0, s, K, w, G);
     return hipGetLastError();
 }
 
@@ -651,7 +651,7 @@ hipError_t launch_wide_sort(const StepDev& st, int Q, int K, const int32_t* beam
     static const hipError_t lds_ok =
         hipFuncSetAttribute((const void*)k_wide_sort, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (lds_ok != hipSuccess) return lds_ok;
-    hipLaunchKernelGGL(k_wide_sort, dim3(Q), dim3(kSortThreads), lds, s, K, w, tok, par, rows, logp);
+    CB_LAUNCH(k_wide_sort, dim3(Q), dim3(kSortThreads), lds, s, K, w, tok, par, rows, logp);
     return hipGetLastError();
 }
 

@@ -207,6 +207,16 @@ cb_status cb_get_mode(const cb_plan* plan, cb_mode* mode);
  * the radix-selection workspace (CB_ENOMEM). */
 cb_status cb_set_path(cb_plan* plan, int32_t t, cb_path path);
 
+/* Workgroup size of the per-query sparse step at step t: 256, 512 or 1024
+ * threads, or 0 for the default (1024 for K >= 16, else 512); cb_tune
+ * measures the default against 256 and keeps the faster.  Every size gives
+ * the same bits (each sum is per wavefront or over fixed slots).  Errors:
+ * CB_EINVAL (other sizes), CB_ECAPACITY (the step's LDS would not fit). */
+cb_status cb_set_step_threads(cb_plan* plan, int32_t t, int32_t threads);
+
+/* The workgroup size the per-query sparse step of step t uses. */
+cb_status cb_get_step_threads(const cb_plan* plan, int32_t t, int32_t* threads);
+
 /* The path step t will take (never CB_PATH_AUTO). */
 cb_status cb_get_path(const cb_plan* plan, int32_t t, cb_path* path);
 
@@ -291,9 +301,12 @@ cb_status cb_tune(cb_plan* plan, int32_t Q, const float* q, const float* P, cons
 cb_status cb_tune_times(const cb_plan* plan, int32_t t, float* dense_us, float* sparse_us);
 
 /* Kernel timing (measurement support).  While profiling is on, every step
- * records a HIP event before and after each kernel it launches, on the step's
- * stream; cb_profile_stop synchronises those events and reports one record
- * per launch.  `kernel` is one of CB_KERNEL_*; `threads` the workgroup size. */
+ * attaches an event pair to the dispatch of each kernel it launches
+ * (hipExtLaunchKernel: the events take the kernel's own start and end times
+ * as the GPU records them, the figures a kernel trace shows, without the
+ * host's enqueue); cb_profile_stop synchronises those events and reports one
+ * record per launch.  `kernel` is one of CB_KERNEL_*; `threads` the
+ * workgroup size. */
 typedef enum {
     CB_KERNEL_GEMM_BF16 = 0,      /* full-codebook scores, bf16 MFMA */
     CB_KERNEL_GEMM_F32 = 1,       /* full-codebook scores, float32 */
@@ -344,6 +357,19 @@ typedef struct {
     float update_us;
 } cb_phase_time;
 cb_status cb_profile_phases(const cb_plan* plan, cb_phase_time* out, int32_t cap, int32_t* n);
+
+/* Overhead floor (FlashTrie, arXiv HTML, App. K "GPU Overhead Floor": the
+ * fixed cost of launches, barriers and selection passes below which a pass
+ * cannot go however little work it does): n launches of an empty kernel of
+ * `blocks` workgroups of `threads` threads on `stream` (current device).
+ * With us == NULL they are only enqueued (a caller may capture them in a
+ * graph and time the replays).  Otherwise each dispatch carries its own event
+ * pair, the call synchronises, and us[0] receives the mean dispatch duration
+ * (start to end of the kernel as the GPU records it), us[1] the mean time per
+ * launch of the whole back-to-back sequence (microseconds).
+ * Errors: CB_EINVAL (1 <= blocks <= 2^20, threads a multiple of 64 in
+ * [64, 1024], 1 <= n <= 4096), CB_EHIP. */
+cb_status cb_floor_probe(int32_t blocks, int32_t threads, int32_t n, float* us, void* stream);
 
 /* Release a plan and its workspace.  NULL is ignored. */
 void cb_plan_destroy(cb_plan* plan);

@@ -64,6 +64,8 @@ SIGNATURES = {
     "cb_set_mode": (ctypes.c_int, [_P, ctypes.c_int]),
     "cb_get_mode": (ctypes.c_int, [_P, _P]),
     "cb_step": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "cb_step_noalloc": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, ctypes.c_int, ctypes.c_int, _P, _P, _P, _P, _P,
+                                       _P, _P, _P, _P]),
     "cb_decode": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "cb_tune": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P]),
     "cb_tune_times": (ctypes.c_int, [_P, _I32, _P, _P]),

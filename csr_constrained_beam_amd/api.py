@@ -103,6 +103,36 @@ class Index:
     def plan(self, Q_max, K, d, dtype):
         return Plan(self, Q_max, K, d, dtype)
 
+    def step_noalloc(self, t, K, hidden, W_t, rows, acc, path="auto", out=None):
+        """One decoding step without a plan (cb_step_noalloc): the library
+        allocates nothing; its workspace is a static device array.  hidden
+        [Q*K][d] (f32 or bf16), W_t [V][d] of the same type, rows int32 [Q*K],
+        acc f32 [Q*K].  Returns (tokens, parents, rows, logp)."""
+        torch = _torch()
+        K = int(K)
+        R = rows.shape[0]
+        if R % K:
+            raise ValueError("rows length must be a multiple of K")
+        code, tdt = _dtype_code(hidden.dtype)
+        d = hidden.shape[1]
+        dev = self.shape["device"]
+        ph = _check_tensor(dev, "hidden", hidden, tdt, (R, d))
+        pw = _check_tensor(dev, "W_t", W_t, tdt, (self.shape["V"], d))
+        pr = _check_tensor(dev, "rows", rows, torch.int32, (R,))
+        pa = _check_tensor(dev, "acc", acc, torch.float32, (R,))
+        if out is None:
+            out = (torch.empty(R, dtype=torch.int32, device=rows.device),
+                   torch.empty(R, dtype=torch.int32, device=rows.device),
+                   torch.empty(R, dtype=torch.int32, device=rows.device),
+                   torch.empty(R, dtype=torch.float32, device=rows.device))
+        ot, op, orow, ol = out
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        C.check("cb_step_noalloc", self._lib.cb_step_noalloc(
+            self._h, int(t), R // K, K, int(d), code, _PATHS[path], ph, pw, pr, pa, ctypes.c_void_p(ot.data_ptr()),
+            ctypes.c_void_p(op.data_ptr()), ctypes.c_void_p(orow.data_ptr()), ctypes.c_void_p(ol.data_ptr()),
+            stream))
+        return out
+
 
 def _check_tensor(device, name, x, dtype, shape):
     """Raw pointer of a contiguous tensor on cuda:device of the given dtype and shape."""

@@ -246,6 +246,26 @@ cb_status cb_step(cb_plan* plan, int32_t t, int32_t Q, const void* hidden, const
                   int32_t* out_tokens, int32_t* out_parents, int32_t* out_rows, float* out_logp,
                   void* stream);
 
+/* One decoding step without a plan, allocating nothing: for callers that
+ * cannot allocate device memory at call time (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same kernels and
+ * results as cb_step with CB_SELECT_LDS on the given path (CB_PATH_AUTO:
+ * dense for bitmap steps, sparse for CSR steps; CB_PATH_SPARSE_SPLIT is not
+ * taken).  Arguments as cb_step, plus the plan's K, d and dtype.
+ * Workspace: a static device array of 32 MiB per device (held by each GPU the
+ * library runs on until the process ends), shared by every call on that
+ * device; the fused sparse step needs none of it, the dense path needs
+ * (Q*K*min(K, widest row)*8 + Q*K*V*4 [+ 2*256*V*4 for bf16] + Q*K*8) bytes.
+ * Calls that overlap on one device (e.g. on two streams) race on it.
+ * Errors: CB_EINVAL (as cb_step; t, Q, K, d, dtype, path out of range),
+ * CB_EUNSUPPORTED (dense path with bf16 and d not a multiple of 64),
+ * CB_ECAPACITY (K > 64, a row too wide for the LDS selection, or a workspace
+ * above 32 MiB), CB_EHIP. */
+cb_status cb_step_noalloc(const cb_index* idx, int32_t t, int32_t Q, int32_t K, int32_t d, cb_dtype dtype,
+                          cb_path path, const void* hidden, const void* W_t, const int32_t* beam_rows,
+                          const float* acc_logp, int32_t* out_tokens, int32_t* out_parents, int32_t* out_rows,
+                          float* out_logp, void* stream);
+
 /* Full decode of all L steps (the beam-search loop of FlashTrie, arXiv HTML,
  * Algorithm 1: expand, prune to the beam, carry the survivors, backtrace the
  * sequences at the end) with a stand-in model whose hidden vector before

@@ -43,6 +43,9 @@ SWEEPS = {
     "items": [{"items": n} for n in (100_000, 1_000_000, 10_000_000, 20_000_000, 100_000_000)],
     "codebook": [{"items": 10_000_000, "Q": 32, "V": v} for v in (256, 1024, 2048, 4096, 8192, 16384, 32768)],
     "batch": [{"Q": q} for q in (1, 8, 32, 64, 128, 256)],
+    # STATIC's max-branch-factor scaling at |C| = 10^6: rows below the root
+    # hold exactly B tokens (L = 3, V = 16,384)
+    "branch": [{"config": "branch", "B": b} for b in (8, 16, 32, 64, 128, 256, 512, 1024)],
 }
 
 
@@ -56,6 +59,7 @@ def parse():
     ap.add_argument("--items", type=int, default=None, help="catalog size other than the workload's (sweeps)")
     ap.add_argument("--V", type=int, default=None, help="codebook size other than the workload's (sweeps)")
     ap.add_argument("--Q", type=int, default=None, help="batch (queries) other than the workload's (sweeps)")
+    ap.add_argument("--B", type=int, default=None, help="branch factor of the 'branch' workload (sweeps)")
     ap.add_argument("--sweep", default=None, choices=sorted(SWEEPS),
                     help="run the named scaling sweep, one child process per point, and print a table")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -114,8 +118,10 @@ def run_sweep(args):
     for point in SWEEPS[args.sweep]:
         with tempfile.NamedTemporaryFile(suffix=".json", delete=False) as f:
             out = f.name
-        cmd = [sys.executable, os.path.abspath(__file__), "--config", args.config, "--no-cpu", "--steps",
+        cmd = [sys.executable, os.path.abspath(__file__), "--no-cpu", "--steps",
                str(args.steps), "--warmup", str(args.warmup), "--json-out", out, "--mode", args.mode]
+        if "config" not in point:
+            cmd += ["--config", args.config]
         for k, v in point.items():
             cmd += ["--" + k, str(v)]
         log("sweep %s: %s" % (args.sweep, point))
@@ -133,6 +139,10 @@ def run_sweep(args):
                          decode_ms=r["decode_ms_with_model_standin"],
                          decode_ms_step_by_step=r["decode_ms_step_by_step"],
                          index_bytes=r["index"]["bytes"], index_build_s=r["index"]["build_s"],
+                         n_items=r["index"]["n_items"],
+                         step_us=[round(x["kernel_us"]["mean"], 2) for x in r["per_step"]],
+                         max_fanout=[x["max_fanout"] for x in r["per_step"]],
+                         step_paths=[x["path"] for x in r["per_step"]],
                          dominant=r["roofline"]["kernel"], dominant_frac=r["roofline"]["frac"]))
         x = rows[-1]
         log("  %s: %.4f ms/pass, %.3g expansions/s, decode %.4f ms, index %.1f MB" % (
@@ -169,6 +179,8 @@ def main():
     from synth import get_config, make_catalog, make_dense
 
     over = {k: v for k, v in (("K", args.K), ("n_items", args.items), ("V", args.V), ("Q", args.Q)) if v}
+    if args.B:
+        over["params"] = dict(get_config(args.config).params, B=args.B)
     cfg = get_config(args.config, **over)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -468,8 +480,7 @@ def main():
         "decode_persistent_phases": phases,
         "decode_vs_oracle": vs_oracle,
         "overlap_with_filter_first": overlap,
-        "index": {"build_s": round(build_s, 2), "bytes": sum(i["bytes"] for i in info),
-                  "rows": [i["n_rows"] for i in info], "storage": [i["storage"] for i in info]},
+        "index": index_report(idx, info, build_s, cfg),
         "per_step": steps,
         "kernels": kernels,
         "tune": tune,
@@ -485,6 +496,28 @@ def main():
         with open(args.json_out, "w") as f:
             f.write(out + "\n")
     print(out, flush=True)
+
+
+def static_umax(V, n_items, L, d, K1=12, K2=4):
+    """STATIC (arXiv 2602.22647) sec. 5.3's upper bound on its index bytes:
+    (1/8 + K2) V^d for the d dense-mask levels plus K1 bytes per edge of each
+    later level, at most min(V^l, |C|) edges (K1 = 12, K2 = 4 as in its App.
+    B.3 capacity planning)."""
+    return (0.125 + K2) * float(V) ** d + K1 * sum(min(float(V) ** lv, n_items) for lv in range(d + 1, L + 1))
+
+
+def index_report(idx, info, build_s, cfg):
+    """Index bytes and build time, with STATIC's bound for the same catalog
+    shape (its dense levels = the leading bitmap steps here)."""
+    n = idx.shape["n_items"]
+    total = sum(i["bytes"] for i in info)
+    d = 0
+    while d < len(info) and info[d]["storage"] == "bitmap":
+        d += 1
+    um = static_umax(cfg.V, n, cfg.L, d)
+    return {"build_s": round(build_s, 2), "bytes": total, "n_items": n, "bytes_per_item": total / max(1, n),
+            "rows": [i["n_rows"] for i in info], "storage": [i["storage"] for i in info],
+            "static_umax_bytes": um, "static_umax_per_item": um / max(1, n), "static_umax_dense_levels": d}
 
 
 def stats(xs):
@@ -601,56 +634,12 @@ def cpu_leg(args, cfg, items, dense, rec, L, K, Q, V):
            "host_cpus": os.cpu_count(), "affinity_cpus": avail, "cpu_model": cpu_model()}
     vs = None
     if args.mode == "filter_first":
-        vs = decode_vs_oracle(T, r0, rec, dense, L, K, Q)
+        from tests.parity import decode_vs_oracle
+        vs = decode_vs_oracle(T, r0, {k: v.cpu().numpy() for k, v in rec.items() if k in ("trace_rows", "rows", "seqs")},
+                              dense["W"], L, K, Q)
         log("decode vs oracle: %s" % vs)
         assert not vs["unexplained"], "free-running GPU decode differs from the oracle away from a near tie"
     return cpu, vs
-
-
-def decode_vs_oracle(T, r0, rec, dense, L, K, Q):
-    """Per query: identical item rows and sequences, or the first step where
-    the GPU's outputs differ is checked on the oracle's candidates of that step
-    (same inputs on both sides up to it): every position where the picks
-    differ must be between candidates whose oracle scores lie within
-    1e-5 * max(1, |score|)."""
-    g_rows = [rec["trace_rows"][t].cpu().numpy() for t in range(1, L)] + [rec["rows"].cpu().numpy()]
-    r_rows = [r0["trace_rows_in"][t] for t in range(1, L)] + [r0["rows"]]
-    g_seqs = rec["seqs"].cpu().numpy()
-    identical, tie, bad, max_gap = 0, 0, [], 0.0
-    cand = {}
-    for q in range(Q):
-        sl = slice(q * K, (q + 1) * K)
-        first = next((t for t in range(L) if not np.array_equal(g_rows[t][sl], r_rows[t][sl])), None)
-        if first is None and np.array_equal(g_seqs[sl], r0["seqs"][sl]):
-            identical += 1
-            continue
-        if first is None:
-            bad.append(q)
-            continue
-        if first not in cand:
-            cand[first] = T.step(first, K, r0["trace_h"][first], dense["W"][first], r0["trace_rows_in"][first],
-                                 r0["trace_acc_in"][first], candidates=True, threads=8)
-        o = cand[first]
-        score = {int(o["cand_rows"][q, j]): float(o["cand_scores"][q, j]) for j in range(int(o["cand_count"][q]))}
-        ok = True
-        for i in range(K):
-            a, b = int(g_rows[first][q * K + i]), int(r_rows[first][q * K + i])
-            if a == b:
-                continue
-            if a not in score or b not in score:
-                ok = False
-                break
-            gap = abs(score[a] - score[b])
-            max_gap = max(max_gap, gap)
-            if gap > 1e-5 * max(1.0, abs(score[b])):
-                ok = False
-                break
-        if ok:
-            tie += 1
-        else:
-            bad.append(q)
-    return {"queries": Q, "identical": identical, "near_tie_divergences": tie, "unexplained": bad,
-            "max_tie_gap": max_gap}
 
 
 if __name__ == "__main__":

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build", "csrbeam")
 LIB = os.path.join(PKG, "libcsrbeam.so")
-SOURCES = ["kernels.hip", "radix.hip", "noalloc.hip", "api.cpp", "index_build.cpp", "index_io.cpp"]
+SOURCES = ["kernels.hip", "radix.hip", "noalloc.hip", "api.cpp", "index_build.cpp", "index_io.cpp", "upload.cpp"]
 ARCH = os.environ.get("CB_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

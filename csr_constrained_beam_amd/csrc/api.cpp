@@ -358,57 +358,31 @@ bool step_args_alias(size_t R, size_t d, size_t V, cb_dtype dt, const void* hidd
     return step_outputs_alias(R, d, V, dtype_size(dt), hidden, W_t, rows, acc, outs);
 }
 
-// Copy the host tables of idx to idx->device, release the host copies and
-// upload the step descriptors.  On failure idx is freed.
-cb_status upload_index(cb_index* idx) {
+// Device copy of every step's descriptor (read by the persistent decode).
+cb_status upload_descriptors(cb_index* idx) {
     DeviceGuard g(idx->device);
-    if (!g.ok) {
-        set_error("cb_build_index: cannot select device " + std::to_string(idx->device));
-        idx->device = -1;
-        cb_free_index(idx);
-        return CB_EHIP;
-    }
-    cb_status st = CB_OK;
-    for (auto& T : idx->steps) {
-        st = dev_alloc(&T.d_row_ptr, T.row_ptr.size(), "row_ptr");
-        if (st == CB_OK) st = dev_alloc(&T.d_tok, T.tok.size(), "tokens");
-        if (st == CB_OK) st = dev_alloc(&T.d_bits, T.bits.size(), "bitmap");
-        if (st == CB_OK) st = dev_alloc(&T.d_rank, T.rank.size(), "rank directory");
-        if (st == CB_OK) st = dev_alloc(&T.d_tok0, T.tok0.size(), "first tokens");
-        hipError_t e = hipSuccess;
-        if (st == CB_OK && T.d_row_ptr)
-            e = hipMemcpy(T.d_row_ptr, T.row_ptr.data(), T.row_ptr.size() * 4, hipMemcpyHostToDevice);
-        if (st == CB_OK && e == hipSuccess && T.d_tok)
-            e = hipMemcpy(T.d_tok, T.tok.data(), T.tok.size() * 2, hipMemcpyHostToDevice);
-        if (st == CB_OK && e == hipSuccess && T.d_bits)
-            e = hipMemcpy(T.d_bits, T.bits.data(), T.bits.size() * 4, hipMemcpyHostToDevice);
-        if (st == CB_OK && e == hipSuccess && T.d_rank)
-            e = hipMemcpy(T.d_rank, T.rank.data(), T.rank.size() * 2, hipMemcpyHostToDevice);
-        if (st == CB_OK && e == hipSuccess && T.d_tok0)
-            e = hipMemcpy(T.d_tok0, T.tok0.data(), T.tok0.size() * 2, hipMemcpyHostToDevice);
-        if (st == CB_OK && e != hipSuccess) st = hip_fail("cb_build_index: upload", e);
-        if (st != CB_OK) {
-            cb_free_index(idx);
-            return st;
-        }
-        std::vector<uint32_t>().swap(T.row_ptr);
-        std::vector<uint16_t>().swap(T.tok);
-        std::vector<uint32_t>().swap(T.bits);
-        std::vector<uint16_t>().swap(T.rank);
-        std::vector<uint16_t>().swap(T.tok0);
-    }
     std::vector<cb::StepDev> descs;
     for (const auto& T : idx->steps) descs.push_back(T.dev(idx->words));
-    st = dev_alloc(&idx->d_steps, descs.size(), "step descriptors");
+    cb_status st = dev_alloc(&idx->d_steps, descs.size(), "step descriptors");
     if (st == CB_OK) {
         hipError_t e = hipMemcpy(idx->d_steps, descs.data(), descs.size() * sizeof(cb::StepDev), hipMemcpyHostToDevice);
         if (e != hipSuccess) st = hip_fail("cb_build_index: upload", e);
     }
-    if (st != CB_OK) {
-        cb_free_index(idx);
-        return st;
+    return st;
+}
+
+// Stream the host tables of idx to idx->device (releasing the host copies)
+// and upload the step descriptors.  On failure idx is freed.
+cb_status upload_index(cb_index* idx) {
+    StepUploader up(idx);
+    cb_status st = up.start();
+    if (st == CB_OK) {
+        for (int t = 0; t < idx->L; ++t) up.push(t);
+        st = up.finish();
     }
-    return CB_OK;
+    if (st == CB_OK) st = upload_descriptors(idx);
+    if (st != CB_OK) cb_free_index(idx);
+    return st;
 }
 
 }  // namespace cb
@@ -450,12 +424,28 @@ cb_status cb_build_index(const int32_t* sids, int64_t n_items, int32_t L, int32_
         return CB_ENOMEM;
     }
     idx->device = device;
-    cb_status st = build_host_tables(sids, n_items, L, V, store, idx);
+    if (device < 0) {
+        cb_status st = build_host_tables(sids, n_items, L, V, store, idx, nullptr);
+        if (st != CB_OK) {
+            delete idx;
+            return st;
+        }
+        *out = idx;
+        return CB_OK;
+    }
+    // each finished step streams to the device while the next one is built
+    StepUploader up(idx);
+    cb_status st = up.start();
+    if (st == CB_OK) {
+        st = build_host_tables(sids, n_items, L, V, store, idx, &up);
+        const cb_status su = up.finish();  // joins the upload thread before anything is freed
+        if (st == CB_OK) st = su;
+    }
+    if (st == CB_OK) st = upload_descriptors(idx);
     if (st != CB_OK) {
-        delete idx;
+        cb_free_index(idx);
         return st;
     }
-    if (device >= 0 && (st = upload_index(idx)) != CB_OK) return st;  // frees idx on failure
     *out = idx;
     return CB_OK;
 }

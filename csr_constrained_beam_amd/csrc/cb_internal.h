@@ -3,8 +3,12 @@
 
 #include <hip/hip_runtime.h>
 
+#include <condition_variable>
 #include <cstdint>
+#include <deque>
+#include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "cb.h"
@@ -250,11 +254,54 @@ cb_status enqueue_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, cons
 // Whether a step's four outputs overlap one another or its inputs.
 bool step_args_alias(size_t R, size_t d, size_t V, cb_dtype dt, const void* hidden, const void* W_t, const void* rows,
                      const void* acc, void* const outs[4]);
+// Streams finished step tables of an index to its device (upload.cpp): a
+// host thread of its own copies each pushed step in batches through two
+// alternating pinned staging buffers on a copy stream of its own, then
+// releases the step's host arrays.  Copies only, no kernels.
+class StepUploader {
+   public:
+    explicit StepUploader(cb_index* idx);
+    ~StepUploader();
+    StepUploader(const StepUploader&) = delete;
+    StepUploader& operator=(const StepUploader&) = delete;
+    cb_status start();
+    // step t's host tables are complete: queue them for upload
+    void push(int t);
+    // wait for every queued step; on failure cb_last_error() tells why (the
+    // caller frees the index, whose device arrays may be partly allocated)
+    cb_status finish();
+
+   private:
+    void run();
+    void release();
+    void fail(const std::string& m);
+    bool stream_copy(void* dst, const void* src, size_t n);
+    template <class T>
+    bool upload_array(std::vector<T>& host, T** dev, const char* what);
+    cb_index* idx_;
+    hipStream_t stream_ = nullptr;
+    void* stage_[2] = {nullptr, nullptr};
+    hipEvent_t ev_[2] = {nullptr, nullptr};
+    int cur_ = 0;
+    std::thread thread_;
+    bool started_ = false;
+    std::mutex mu_;
+    std::condition_variable cv_;
+    std::deque<int> queue_;
+    bool closed_ = false;
+    cb_status status_ = CB_OK;  // written by the upload thread; read after the join
+    std::string msg_;
+};
+
 // Index construction (index_build.cpp).
-// Upload the host tables of idx to idx->device (release the host copies);
-// frees idx on failure.
+// Upload the host tables of idx to idx->device (release the host copies) and
+// the step descriptors; frees idx on failure.
 cb_status upload_index(cb_index* idx);
+// Sort and deduplicate the catalog and build every step's host tables; each
+// finished step is pushed to `up` (NULL: host tables only).
 cb_status build_host_tables(const int32_t* sids, int64_t n_items, int32_t L, int32_t V, int32_t store,
-                            cb_index* idx);
+                            cb_index* idx, StepUploader* up);
+// Upload the step descriptors of an index whose tables are on the device.
+cb_status upload_descriptors(cb_index* idx);
 
 }  // namespace cb

@@ -88,7 +88,8 @@ void parallel_sort(std::vector<T>& v) {
 }
 
 template <int NW>
-cb_status build_impl(const int32_t* sids, int64_t n, int32_t L, int32_t V, int32_t store, cb_index* idx) {
+cb_status build_impl(const int32_t* sids, int64_t n, int32_t L, int32_t V, int32_t store, cb_index* idx,
+                     StepUploader* up) {
     const int b = bits_for(V);
     const int per = 64 / b;
     const uint64_t mask = (uint64_t(1) << b) - 1;
@@ -133,109 +134,129 @@ cb_status build_impl(const int32_t* sids, int64_t n, int32_t L, int32_t V, int32
 
     idx->steps.assign((size_t)L, StepTable());
     idx->words = (V + 31) / 32;
-    // one status per step thread (each writes only its own), reduced after the joins
-    std::vector<cb_status> step_st((size_t)L, CB_OK);
-    auto build_step = [&](int t) {
-        cb_status& st = step_st[(size_t)t];
-        StepTable& T = idx->steps[(size_t)t];
-        int64_t nr = 0, ne = 0;
-        for (int64_t i = 0; i < N; ++i) {
-            nr += fd[(size_t)i] < t;
-            ne += fd[(size_t)i] <= t;
-        }
-        T.n_rows = nr;
-        T.n_edges = ne;
-        try {
-            T.row_ptr.resize((size_t)nr + 1);
-            T.tok.resize((size_t)ne);
-        } catch (...) {
-            st = CB_ENOMEM;
+    const int words = idx->words;
+    // chunks of consecutive sorted items; each chunk's first row and first
+    // edge are known in advance (prefix sums of the chunks' counts), so every
+    // chunk fills its own part of the tables independently
+    const int64_t C = std::max<int64_t>(1, std::min<int64_t>(256, N / 4096));
+    std::vector<int64_t> cut((size_t)C + 1);
+    for (int64_t c = 0; c <= C; ++c) cut[(size_t)c] = N * c / C;
+    auto over_chunks = [&](auto&& f) {
+        const int T_ = std::min<int>(n_threads(), (int)C);
+        if (T_ <= 1) {
+            for (int64_t c = 0; c < C; ++c) f(c);
             return;
         }
-        int64_t r = 0, e = 0;
-        for (int64_t i = 0; i < N; ++i) {
-            if (fd[(size_t)i] < t) T.row_ptr[(size_t)r++] = (uint32_t)e;
-            if (fd[(size_t)i] <= t) T.tok[(size_t)e++] = (uint16_t)token_of(keys[(size_t)i], t);
-        }
-        T.row_ptr[(size_t)nr] = (uint32_t)ne;
-        int32_t S = 0;
-        for (int64_t k = 0; k < nr; ++k) S = std::max<int32_t>(S, (int32_t)(T.row_ptr[(size_t)k + 1] - T.row_ptr[(size_t)k]));
-        T.S = S;
-        const int64_t bitmap_bytes = nr * (int64_t)idx->words * 6;  // bits + rank directory
-        const int64_t csr_bytes = ne * 2;
-        bool bitmap = store == CB_STORE_BITMAP ||
-                      (store == CB_STORE_AUTO && bitmap_bytes < csr_bytes);
-        if (bitmap) {
-            try {
-                T.bits.assign((size_t)(nr * idx->words), 0u);
-            } catch (...) {
-                st = CB_ENOMEM;
-                return;
-            }
-            for (int64_t k = 0; k < nr; ++k)
-                for (uint32_t x = T.row_ptr[(size_t)k]; x < T.row_ptr[(size_t)k + 1]; ++x) {
-                    uint32_t v = T.tok[x];
-                    T.bits[(size_t)(k * idx->words + (v >> 5))] |= 1u << (v & 31);
-                }
-            try {
-                T.rank.assign((size_t)(nr * idx->words), 0);
-            } catch (...) {
-                st = CB_ENOMEM;
-                return;
-            }
-            for (int64_t k = 0; k < nr; ++k) {
-                uint32_t c = 0;
-                for (int w = 0; w < idx->words; ++w) {
-                    T.rank[(size_t)(k * idx->words + w)] = (uint16_t)c;
-                    c += (uint32_t)__builtin_popcount(T.bits[(size_t)(k * idx->words + w)]);
-                }
-            }
-            std::vector<uint16_t>().swap(T.tok);
-            T.store = CB_STORE_BITMAP;
-            T.bytes = (nr + 1) * 4 + bitmap_bytes;
-        } else {
-            // first token of every row, read together with row_ptr so that a
-            // one-token row needs no second dependent read
-            try {
-                T.tok0.resize((size_t)nr);
-            } catch (...) {
-                st = CB_ENOMEM;
-                return;
-            }
-            for (int64_t k = 0; k < nr; ++k) T.tok0[(size_t)k] = T.tok[T.row_ptr[(size_t)k]];
-            T.store = CB_STORE_CSR;
-            T.bytes = (nr + 1) * 4 + csr_bytes + nr * 2;
-        }
-    };
-    {
         std::vector<std::thread> th;
-        for (int t = 0; t < L; ++t) th.emplace_back(build_step, t);
+        for (int w = 0; w < T_; ++w)
+            th.emplace_back([&, w] {
+                for (int64_t c = w; c < C; c += T_) f(c);
+            });
         for (auto& x : th) x.join();
+    };
+    std::vector<int64_t> r0((size_t)C + 1), e0((size_t)C + 1);
+    for (int t = 0; t < L; ++t) {
+        StepTable& T = idx->steps[(size_t)t];
+        // pass 1: rows (items where a new length-t prefix starts) and edges
+        // (items where a new length-(t+1) prefix starts) of every chunk
+        over_chunks([&](int64_t c) {
+            int64_t nr = 0, ne = 0;
+            for (int64_t i = cut[(size_t)c]; i < cut[(size_t)c + 1]; ++i) {
+                nr += fd[(size_t)i] < t;
+                ne += fd[(size_t)i] <= t;
+            }
+            r0[(size_t)c + 1] = nr;
+            e0[(size_t)c + 1] = ne;
+        });
+        r0[0] = e0[0] = 0;
+        for (int64_t c = 0; c < C; ++c) {
+            r0[(size_t)c + 1] += r0[(size_t)c];
+            e0[(size_t)c + 1] += e0[(size_t)c];
+        }
+        const int64_t nr = r0[(size_t)C], ne = e0[(size_t)C];
+        T.n_rows = nr;
+        T.n_edges = ne;
+        const int64_t bitmap_bytes = nr * (int64_t)words * 6;  // bits + rank directory
+        const int64_t csr_bytes = ne * 2;
+        const bool bitmap = store == CB_STORE_BITMAP || (store == CB_STORE_AUTO && bitmap_bytes < csr_bytes);
+        try {
+            T.row_ptr.resize((size_t)nr + 1);
+            if (bitmap) {
+                T.bits.assign((size_t)(nr * words), 0u);
+                T.rank.assign((size_t)(nr * words), 0);
+            } else {
+                T.tok.resize((size_t)ne);
+                // first token of every row, read together with row_ptr so that a
+                // one-token row needs no second dependent read
+                T.tok0.resize((size_t)nr);
+            }
+        } catch (...) {
+            // the caller frees the index once the upload thread has stopped
+            set_error("cb_build_index: host allocation failed");
+            return CB_ENOMEM;
+        }
+        // pass 2: every chunk fills its rows and edges at its precomputed
+        // positions (a row whose edges straddle chunks gets its bitmap bits
+        // from both, hence the atomic OR)
+        over_chunks([&](int64_t c) {
+            int64_t r = r0[(size_t)c], e = e0[(size_t)c];
+            for (int64_t i = cut[(size_t)c]; i < cut[(size_t)c + 1]; ++i) {
+                const int f = fd[(size_t)i];
+                if (f > t) continue;
+                const uint32_t v = (uint32_t)token_of(keys[(size_t)i], t);
+                if (f < t) {
+                    T.row_ptr[(size_t)r] = (uint32_t)e;
+                    if (!bitmap) T.tok0[(size_t)r] = (uint16_t)v;
+                    ++r;
+                }
+                if (bitmap)
+                    __atomic_fetch_or(&T.bits[(size_t)((r - 1) * words + (v >> 5))], 1u << (v & 31), __ATOMIC_RELAXED);
+                else
+                    T.tok[(size_t)e] = (uint16_t)v;
+                ++e;
+            }
+        });
+        T.row_ptr[(size_t)nr] = (uint32_t)ne;
+        // pass 3, over the rows of every chunk: the widest row and (bitmap)
+        // the rank directory
+        std::vector<int32_t> Sc((size_t)C, 0);
+        over_chunks([&](int64_t c) {
+            int32_t S = 0;
+            for (int64_t k = nr * c / C; k < nr * (c + 1) / C; ++k) {
+                S = std::max<int32_t>(S, (int32_t)(T.row_ptr[(size_t)k + 1] - T.row_ptr[(size_t)k]));
+                if (bitmap) {
+                    uint32_t cnt = 0;
+                    for (int w = 0; w < words; ++w) {
+                        T.rank[(size_t)(k * words + w)] = (uint16_t)cnt;
+                        cnt += (uint32_t)__builtin_popcount(T.bits[(size_t)(k * words + w)]);
+                    }
+                }
+            }
+            Sc[(size_t)c] = S;
+        });
+        T.S = *std::max_element(Sc.begin(), Sc.end());
+        T.store = bitmap ? CB_STORE_BITMAP : CB_STORE_CSR;
+        T.bytes = bitmap ? (nr + 1) * 4 + bitmap_bytes : (nr + 1) * 4 + csr_bytes + nr * 2;
+        // the finished step is streamed to the device while the next is built
+        if (up) up->push(t);
     }
-    cb_status st = CB_OK;
-    for (cb_status x : step_st)
-        if (x != CB_OK) st = x;
-    if (st != CB_OK) {
-        set_error("cb_build_index: host allocation failed");
-        idx->steps.clear();
-    }
-    return st;
+    return CB_OK;
 }
 
 }  // namespace
 
 cb_status build_host_tables(const int32_t* sids, int64_t n_items, int32_t L, int32_t V, int32_t store,
-                            cb_index* idx) {
+                            cb_index* idx, StepUploader* up) {
     const int b = bits_for(V);
     const int per = 64 / b;
     const int nw = (L + per - 1) / per;
     idx->L = L;
     idx->V = V;
     switch (nw) {
-        case 1: return build_impl<1>(sids, n_items, L, V, store, idx);
-        case 2: return build_impl<2>(sids, n_items, L, V, store, idx);
-        case 3: return build_impl<3>(sids, n_items, L, V, store, idx);
-        case 4: return build_impl<4>(sids, n_items, L, V, store, idx);
+        case 1: return build_impl<1>(sids, n_items, L, V, store, idx, up);
+        case 2: return build_impl<2>(sids, n_items, L, V, store, idx, up);
+        case 3: return build_impl<3>(sids, n_items, L, V, store, idx, up);
+        case 4: return build_impl<4>(sids, n_items, L, V, store, idx, up);
         default:
             set_error("cb_build_index: L * ceil(log2 V) exceeds 256 bits");
             return CB_EUNSUPPORTED;

@@ -157,6 +157,21 @@ def hybrid(n_items, L, V, seed, level2_mean=300.0, later_mean=3.0):
     return np.ascontiguousarray(items[rng.permutation(n_items)])
 
 
+def branch(n_items, L, V, seed, B=64):
+    """Exact branch factor B: the root has n1 = round(n_items / B^(L-1))
+    children (at least 1, at most V), every node below has exactly B children,
+    all uniform random token subsets; the catalog is every leaf, n1 * B^(L-1)
+    items (within a few percent of n_items).  ``n_items`` only sets n1."""
+    rng = np.random.default_rng([seed, 1, B])
+    n1 = int(min(V, max(1, round(n_items / float(B) ** (L - 1)))))
+    prefixes = np.sort(rng.choice(V, size=n1, replace=False)).astype(np.int32)[:, None]
+    for _ in range(1, L):
+        c = np.full(len(prefixes), min(B, V), dtype=np.int64)
+        kids = _random_subsets(rng, c, V).astype(np.int32)
+        prefixes = np.concatenate([np.repeat(prefixes, c, axis=0), kids[:, None]], axis=1)
+    return np.ascontiguousarray(prefixes[rng.permutation(len(prefixes))])
+
+
 def zipf_prefix(n_items, L, V, seed, zipf_s=1.0):
     from ._native import zipf_items
     return zipf_items(seed, n_items, L, V, -1, zipf_s, L, L)
@@ -172,6 +187,7 @@ _GENERATORS = {
     "clustered": clustered,
     "clustered_collision": clustered_collision,
     "hybrid": hybrid,
+    "branch": branch,
     "zipf_prefix": zipf_prefix,
     "zipf_varlen": zipf_varlen,
 }

@@ -35,6 +35,10 @@ CONFIGS = {
     # 20M items, L=8, V=2048, Zipf(1.0) tokens over per-prefix permutations.
     "production": Config("production", 20_000_000, 8, 2048, 1024, "bf16", 64, 32, 104, "zipf_prefix",
                          {"zipf_s": 1.0}),
+    # ~1M items in a tree whose rows below the root all hold exactly B tokens
+    # (the branch-factor sweep at |C| = 10^6); V = 16,384 so that the root of
+    # the smallest B fits.
+    "branch": Config("branch", 1_000_000, 3, 16_384, 1024, "bf16", 64, 32, 106, "branch", {"B": 64}),
     # 100M variable-length items (4..12 tokens) over V=32,000, EOS-padded to 12.
     "large": Config("large", 100_000_000, 12, 32_001, 1024, "bf16", 1, 1000, 105, "zipf_varlen",
                     {"zipf_s": 1.2, "min_len": 4, "max_len": 12, "codebook": 32_000}),

@@ -100,3 +100,52 @@ def compare_step(ref, got, K, dtype, eps_rel=1e-5):
                     fails.append("query %d: candidate %s (%.9g) differs from the oracle's selection away from "
                                  "the boundary %.9g" % (q, c, cands[c][0], kth))
     return exempt, max_gap, fails
+
+
+def decode_vs_oracle(T, r0, rec, W, L, K, Q):
+    """A free-running device decode against the oracle's.  Per query:
+    identical item rows and sequences, or the first step where the device's
+    outputs differ is checked on the oracle's candidates of that step (same
+    inputs on both sides up to it): every position where the picks differ
+    must be between candidates whose oracle scores lie within
+    1e-5 * max(1, |score|).  T: the oracle; r0: its decode with trace=True;
+    rec: the device decode's trace_rows [L][Q*K], rows and seqs (numpy);
+    W: [L][V][d] float32."""
+    g_rows = [np.asarray(rec["trace_rows"][t]) for t in range(1, L)] + [np.asarray(rec["rows"])]
+    r_rows = [r0["trace_rows_in"][t] for t in range(1, L)] + [r0["rows"]]
+    g_seqs = np.asarray(rec["seqs"])
+    identical, tie, bad, max_gap = 0, 0, [], 0.0
+    cand = {}
+    for q in range(Q):
+        sl = slice(q * K, (q + 1) * K)
+        first = next((t for t in range(L) if not np.array_equal(g_rows[t][sl], r_rows[t][sl])), None)
+        if first is None and np.array_equal(g_seqs[sl], r0["seqs"][sl]):
+            identical += 1
+            continue
+        if first is None:
+            bad.append(q)
+            continue
+        if first not in cand:
+            cand[first] = T.step(first, K, r0["trace_h"][first], W[first], r0["trace_rows_in"][first],
+                                 r0["trace_acc_in"][first], candidates=True, threads=8)
+        o = cand[first]
+        score = {int(o["cand_rows"][q, j]): float(o["cand_scores"][q, j]) for j in range(int(o["cand_count"][q]))}
+        ok = True
+        for i in range(K):
+            a, b = int(g_rows[first][q * K + i]), int(r_rows[first][q * K + i])
+            if a == b:
+                continue
+            if a not in score or b not in score:
+                ok = False
+                break
+            gap = abs(score[a] - score[b])
+            max_gap = max(max_gap, gap)
+            if gap > 1e-5 * max(1.0, abs(score[b])):
+                ok = False
+                break
+        if ok:
+            tie += 1
+        else:
+            bad.append(q)
+    return {"queries": Q, "identical": identical, "near_tie_divergences": tie, "unexplained": bad,
+            "max_tie_gap": max_gap}

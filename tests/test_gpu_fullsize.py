@@ -2,9 +2,8 @@
 configuration (all queries of the batch, beam width and hidden width of the
 workload, the tuned per-step paths), plus both scoring paths forced.
 
-The oracle builds its own pointer trie of the whole catalog; outputs are
-compared for a sample of queries (the oracle computes each query on its own,
-so a sample is exact).  Teacher forcing: every step gets the oracle's beam
+The oracle builds its own pointer trie of the whole catalog; every query's
+outputs are compared.  Teacher forcing: every step gets the oracle's beam
 state and hidden vectors.
 """
 
@@ -24,7 +23,6 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 import csr_constrained_beam_amd as cb  # noqa: E402
 
 DEV = torch.device("cuda:0")
-SAMPLE_QUERIES = 16
 _CACHE = {}
 
 
@@ -91,7 +89,8 @@ def test_fullsize_decode(name):
         assert not fails, "\n".join(fails[:5])
         assert ex > 0
     print("queries diverging at a near tie:", diverged, "of", cfg.Q)
-    assert diverged <= cfg.Q // 4
+    # observed on the current kernels: no query diverges on either workload
+    assert diverged == 0
 
 
 @pytest.mark.parametrize("name", ["production", "hybrid"])
@@ -128,7 +127,7 @@ def test_fullsize_teacher_forced(name, path):
     w = big(name)
     cfg, ref, plan, T = w["cfg"], w["ref"], w["plan"], w["T"]
     K = cfg.K
-    S = SAMPLE_QUERIES * K
+    S = cfg.Q * K
     saved = [plan.get_path(t) for t in range(cfg.L)]
     try:
         for t in range(cfg.L):

@@ -150,3 +150,52 @@ def test_null_arguments_rejected(cb):
     assert L.cb_decode(None, 0, None, None, None, None, None, None, None, None, None, None) == -1
     L.cb_free_index(None)
     L.cb_plan_destroy(None)
+
+
+@pytest.mark.parametrize("store", ["auto", "csr", "bitmap"])
+def test_chunked_build_equals_oracle_at_chunk_boundaries(cb, store):
+    """A catalog of 200k items is built in 48 chunks of consecutive sorted
+    items, each filling its rows and edges at positions computed in advance.
+    Every row that holds a chunk's first or last item (rows straddling two
+    chunks included), and a sample of the others, equal the oracle trie's."""
+    rng = np.random.default_rng(17)
+    V, L, n = 96, 4, 200_000
+    items = rng.integers(0, V, size=(n, L)).astype(np.int32)
+    items[:, 0] %= 5  # few wide level-1 rows, so that rows straddle chunks
+    u = np.unique(items, axis=0)
+    N = len(u)
+    C = max(1, min(256, N // 4096))
+    assert C > 8
+    idx = cb.Index(items, V, device=-1, store=store)
+    T = oracle.Trie(items, V)
+    assert idx.shape["n_items"] == N == T.n_items
+    for t in range(L):
+        info = idx.info(t)
+        assert info["n_rows"] == T.level_count(t) and info["n_edges"] == T.level_count(t + 1)
+        if t == 0:
+            row_of = np.zeros(N, np.int64)
+        else:
+            change = np.ones(N, bool)
+            change[1:] = (u[1:, :t] != u[:-1, :t]).any(axis=1)
+            row_of = np.cumsum(change) - 1
+        rows = {int(row_of[b]) for c in range(C + 1) for b in (N * c // C - 1, N * c // C) if 0 <= b < N}
+        rows |= set(rng.integers(0, info["n_rows"], size=200).tolist())
+        fan = max(len(T.children_of_row(t, r)[0]) for r in range(info["n_rows"]))
+        assert info["max_fanout"] == fan
+        for r in sorted(rows):
+            tok, nxt = idx.row(t, r)
+            otok, orow = T.children_of_row(t, r)
+            assert tok.tolist() == otok.tolist(), (t, r)
+            assert nxt.tolist() == orow.tolist(), (t, r)
+
+
+def test_static_umax_reproduces_the_capacity_rule():
+    """The bench compares index bytes with STATIC's bound (sec. 5.3) at
+    K1 = 12, K2 = 4 bytes (App. B.3): the page's own numbers are 17.3 MB for
+    the dense levels at |V| = 2048, d = 2, 72 MB per million items for the
+    six later levels of L = 8, about 90 MB per million in all."""
+    import bench
+    dense = bench.static_umax(2048, 0, 2, 2)
+    assert abs(dense - 17_301_504) < 1
+    assert abs(bench.static_umax(2048, 1_000_000, 8, 2) - dense - 72e6) < 1
+    assert 89e6 < bench.static_umax(2048, 1_000_000, 8, 2) < 90e6

@@ -218,7 +218,8 @@ def main():
         for t in range(cfg.L):
             plan.set_path(t, args.path)
     paths = [plan.get_path(t) for t in range(cfg.L)]
-    log("paths per step:", paths)
+    forms = [plan.get_option(t, "sparse_form") for t in range(cfg.L)]
+    log("paths per step:", paths, "sparse form per step (1: per beam):", forms)
 
     # free-running decode: records every step's inputs; also times the full decode
     rec = plan.decode(q, P, W, trace=True)
@@ -285,14 +286,17 @@ def main():
         state_bytes = R * 8 + R * Kc * 8
         w_bytes = live_scored * d * es + len(toks_scored) * d * es  # hidden vectors and distinct W_t rows
         steps.append({
-            "t": t, "path": paths[t], "storage": info[t]["storage"], "live_beams": int(len(live)),
+            "t": t, "path": paths[t], "sparse_form": forms[t], "storage": info[t]["storage"], "live_beams": int(len(live)),
             "expansions": n_exp, "max_fanout": S, "mean_fanout": float(fan.mean()) if len(fan) else 0.0,
             "valid_fraction": n_exp / max(1, len(live) * V), "distinct_tokens": len(toks),
             "bytes": {
                 "step_query": R * 8 + idx_bytes + w_bytes + R * 16 + min(R, n_exp) * 8,
-                "expand_sparse": state_bytes + idx_bytes + w_bytes,
-                "expand_dense": state_bytes + idx_bytes + n_exp * 4,
-                "merge": Q * K * Kc * 8 + R * 4 + R * 16 + min(R, n_exp) * 8,
+                # per-beam expansions also write each survivor's next row and token
+                "expand_sparse": state_bytes + R * Kc * 8 + idx_bytes + w_bytes,
+                # bitmap rows: the expansion reads whole score rows, writes no side information
+                "expand_dense": (state_bytes + idx_bytes + len(live) * V * 4 if info[t]["storage"] == "bitmap"
+                                 else state_bytes + R * Kc * 8 + idx_bytes + n_exp * 4),
+                "merge": Q * K * Kc * 8 + R * 4 + R * 16 + min(R, n_exp) * 16,
                 "gemm_" + cfg.dtype: R * d * es + V * d * es + R * V * 4,
                 # radix path: candidates written to HBM as 8-byte keys
                 "radix_score_sparse": R * 8 + idx_bytes + w_bytes + n_exp * 8 + chunks * 8,

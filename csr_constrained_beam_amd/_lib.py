@@ -15,6 +15,7 @@ CB_F32, CB_BF16 = 0, 1
 CB_PATH_AUTO, CB_PATH_DENSE, CB_PATH_SPARSE, CB_PATH_SPARSE_SPLIT = 0, 1, 2, 3
 CB_STORE_AUTO, CB_STORE_CSR, CB_STORE_BITMAP = 0, 1, 2
 CB_SELECT_AUTO, CB_SELECT_LDS, CB_SELECT_RADIX = 0, 1, 2
+STEP_OPTIONS = {"step_threads": 0, "split_rows": 1, "sparse_form": 2, "dense_rows": 3, "radix_prepass": 4}
 
 STATUS_NAMES = {0: "CB_OK", -1: "CB_EINVAL", -2: "CB_ENOMEM", -3: "CB_EHIP", -4: "CB_EUNSUPPORTED",
                 -5: "CB_ECAPACITY"}
@@ -43,7 +44,7 @@ class PhaseTime(ctypes.Structure):
 KERNEL_NAMES = {0: "gemm_bf16", 1: "gemm_f32", 2: "expand_sparse", 3: "expand_dense", 4: "merge",
                 5: "step_query", 6: "live_rows", 7: "radix_score_sparse", 8: "radix_score_dense",
                 9: "radix_keys", 10: "radix_refine", 11: "radix_collect", 12: "radix_sort",
-                13: "decode_tail"}
+                13: "decode_tail", 14: "radix_small"}
 
 SIGNATURES = {
     "cb_build_index": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _I32, _PP]),
@@ -54,8 +55,8 @@ SIGNATURES = {
     "cb_plan_create": (ctypes.c_int, [_P, _I32, _I32, _I32, ctypes.c_int, _PP]),
     "cb_set_path": (ctypes.c_int, [_P, _I32, ctypes.c_int]),
     "cb_get_path": (ctypes.c_int, [_P, _I32, _P]),
-    "cb_set_step_threads": (ctypes.c_int, [_P, _I32, _I32]),
-    "cb_get_step_threads": (ctypes.c_int, [_P, _I32, _P]),
+    "cb_set_step_option": (ctypes.c_int, [_P, _I32, ctypes.c_int, _I32]),
+    "cb_get_step_option": (ctypes.c_int, [_P, _I32, ctypes.c_int, _P]),
     "cb_set_select": (ctypes.c_int, [_P, _I32, ctypes.c_int]),
     "cb_get_select": (ctypes.c_int, [_P, _I32, _P]),
     "cb_set_decode_fusion": (ctypes.c_int, [_P, _I32]),

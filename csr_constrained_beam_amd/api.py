@@ -186,15 +186,31 @@ class Plan:
         C.check("cb_get_path", self._lib.cb_get_path(self._h, int(t), ctypes.byref(v)))
         return _PATH_NAMES[v.value]
 
+    def set_option(self, t, option, value):
+        """Force a form of step t's kernels (cb_set_step_option): option is
+        one of "step_threads", "split_rows", "sparse_form", "dense_rows",
+        "radix_prepass"; 0 restores the default or measured choice."""
+        C.check("cb_set_step_option", self._lib.cb_set_step_option(self._h, int(t), C.STEP_OPTIONS[option],
+                                                                    int(value)))
+
+    def get_option(self, t, option):
+        v = ctypes.c_int32()
+        C.check("cb_get_step_option", self._lib.cb_get_step_option(self._h, int(t), C.STEP_OPTIONS[option],
+                                                                    ctypes.byref(v)))
+        return v.value
+
     def set_step_threads(self, t, threads):
         """Workgroup size of the per-query sparse step at step t (256, 512,
         1024, or 0 for the default)."""
-        C.check("cb_set_step_threads", self._lib.cb_set_step_threads(self._h, int(t), int(threads)))
+        self.set_option(t, "step_threads", threads)
 
     def get_step_threads(self, t):
-        v = ctypes.c_int32()
-        C.check("cb_get_step_threads", self._lib.cb_get_step_threads(self._h, int(t), ctypes.byref(v)))
-        return v.value
+        return self.get_option(t, "step_threads")
+
+    def set_split_rows(self, t, min_tokens):
+        """Rows of more than min_tokens tokens that the split sparse path
+        scores apart at step t (0: the default, 16)."""
+        self.set_option(t, "split_rows", min_tokens)
 
     def set_select(self, t, select):
         """Top-K selection of step t: "auto", "lds" (K <= 64) or "radix"."""

@@ -85,6 +85,20 @@ int32_t resolve_path(const cb_plan* p, int t) {
     return (T.store == CB_STORE_BITMAP && dense_available(p)) ? CB_PATH_DENSE : CB_PATH_SPARSE;
 }
 
+// Per-step option value (0 when the plan keeps none, as the allocation-free step's).
+int32_t opt(const std::vector<int32_t>& v, int t) { return (size_t)t < v.size() ? v[(size_t)t] : 0; }
+
+// Whether the full-codebook product of step t runs over every beam slot (no
+// live list) rather than the compact list of live beams: measured by cb_tune,
+// else over every slot after step 0 (beams fill their slots once a query has
+// K candidates) and compact at step 0 (one live slot per query).
+bool gemm_full(const cb_plan* p, int t) {
+    if (!gemm_full_ok(p->dtype)) return false;
+    const int32_t v = opt(p->gemm_rows, t);
+    if (v == 1 || v == 2) return v == 2;
+    return t > 0;
+}
+
 // Whether the LDS selection (fused sparse step, or dense expansion + merge)
 // holds step t of this plan.
 // Hidden widths above kQueryMaxD take the sparse step as a per-beam
@@ -120,6 +134,7 @@ void wide_release(cb_plan* p) {
     dev_free(w.sel);
     dev_free(w.surv_n);
     dev_free(w.surv);
+    dev_free(w.done);
     w = WideDev();
     p->wide_S = 0;
 }
@@ -152,6 +167,7 @@ cb_status wide_alloc(cb_plan* p) {
     }
     if (st == CB_OK) st = dev_alloc(&w.surv_n, Q, "radix survivor counts");
     if (st == CB_OK) st = dev_alloc(&w.surv, Q * (size_t)wide_surv_cap(), "radix survivors");
+    if (st == CB_OK) st = dev_alloc(&w.done, Q, "radix pre-pass flags");
     if (st != CB_OK) {
         wide_release(p);
         return st;
@@ -183,16 +199,27 @@ cb_status run_step_radix(cb_plan* p, int t, int Q, int32_t path, const void* hid
     const cb_index* idx = p->idx;
     const cb::StepDev sd = idx->steps[(size_t)t].dev(idx->words);
     const int R = Q * p->K;
-    const WideDev& w = p->wide;
-    if (!w.cand) {
+    if (!p->wide.cand) {
         set_error("cb_step: radix workspace missing");
         return CB_EINVAL;
     }
     const int GS = wide_blocks_per_query(Q) * Q, GH = wide_hist_blocks_per_query(Q) * Q;
     const bool dense = path == CB_PATH_DENSE;
     hipError_t e;
+    // the one-token pre-pass (sparse scoring only): queries whose live rows
+    // all hold one token are finished there and skipped by the kernels below
+    WideDev w = p->wide;
+    const int32_t pre_v = opt(p->radix_pre, t);
+    w.use_done = !dense && pre_v != 1 ? 1 : 0;
+    if (w.use_done) {
+        ProfMark m(p, s, t, CB_KERNEL_RADIX_SMALL, 1024, Q);
+        e = launch_wide_small(sd, Q, p->K, rows, acc, w, ot, op, orow, ol, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: radix pre-pass", e);
+    }
     if (dense) {
-        if (!gemm_finds_live(p->dtype, R)) {
+        const bool full = gemm_full(p, t);
+        if (!full && !gemm_finds_live(p->dtype, R)) {
             ProfMark m(p, s, t, CB_KERNEL_LIVE_ROWS, 1024, 1);
             e = launch_live_rows(sd, R, rows, acc, p->live, p->n_live, p->ci_of, s);
             m.done();
@@ -200,9 +227,9 @@ cb_status run_step_radix(cb_plan* p, int t, int Q, int32_t path, const void* hid
         }
         const bool bf = p->dtype == CB_BF16;
         ProfMark m(p, s, t, bf ? CB_KERNEL_GEMM_BF16 : CB_KERNEL_GEMM_F32, bf ? 512 : 256,
-                   gemm_blocks(p->dtype, R, idx->V));
+                   gemm_blocks(p->dtype, R, idx->V, full));
         e = launch_gemm_scores(p->dtype, R, idx->V, p->d, p->live, p->n_live, hidden, Wt, p->Z, p->Zp, sd, rows, acc,
-                               p->ci_of, s);
+                               p->ci_of, full, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: full-codebook scores", e);
     }
@@ -252,17 +279,21 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const vo
     const int Kc = std::min(p->K, p->mode == CB_MODE_UNCONSTRAINED ? idx->V : std::max(T.S, 1));
     hipError_t e;
     if (sel == CB_SELECT_RADIX) return run_step_radix(p, t, Q, path, hidden, Wt, rows, acc, ot, op, orow, ol, s);
-    if ((path == CB_PATH_SPARSE || path == CB_PATH_SPARSE_SPLIT) && p->d > kQueryMaxD) {
-        // wide hidden vectors: per-beam gather-dot expansion, then the per-query merge
+    const bool per_beam = p->d > kQueryMaxD || opt(p->sparse_form, t) == 1;
+    if ((path == CB_PATH_SPARSE || path == CB_PATH_SPARSE_SPLIT) && per_beam) {
+        // per-beam gather-dot expansion over the whole GPU, then the per-query
+        // merge (wide hidden vectors, or the measured choice for the step)
+        bool sided = false;
         {
             ProfMark m(p, s, t, CB_KERNEL_EXPAND_SPARSE, expand_threads(sd), R);
             e = launch_beam_expand(sd, false, p->dtype, R, p->K, Kc, p->d, hidden, Wt, nullptr, nullptr, idx->V,
-                                   nullptr, nullptr, rows, acc, p->keys, p->mode, s);
+                                   nullptr, nullptr, rows, acc, p->keys, p->side, &sided, p->mode, s);
             m.done();
             if (e != hipSuccess) return hip_fail("cb_step: sparse beam expansion", e);
         }
         ProfMark m(p, s, t, CB_KERNEL_MERGE, kMergeThreads, Q);
-        e = launch_query_merge(sd, Q, p->K, Kc, p->keys, rows, ot, op, orow, ol, p->mode, s);
+        e = launch_query_merge(sd, Q, p->K, Kc, p->keys, sided ? p->side : nullptr, rows, ot, op, orow, ol, p->mode,
+                               s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: query merge", e);
         return CB_OK;
@@ -270,23 +301,25 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const vo
     if (path == CB_PATH_SPARSE || path == CB_PATH_SPARSE_SPLIT) {
         const WideDev& w = p->wide;
         const bool split = path == CB_PATH_SPARSE_SPLIT && w.cand;
-        if (split) {  // rows too wide for one wavefront: scored across many workgroups first
+        // rows above pre_min tokens scored across many workgroups first (16 unless measured)
+        const int pre_min = opt(p->split_min, t) > 0 ? opt(p->split_min, t) : kPreMin;
+        if (split) {
             ProfMark m(p, s, t, CB_KERNEL_RADIX_SCORE_SPARSE, 256, wide_blocks_per_query(Q) * Q);
             e = launch_wide_score(sd, false, p->dtype, Q, p->K, p->d, hidden, Wt, nullptr, nullptr, idx->V, nullptr,
-                                  nullptr, rows, acc, 1, w, s);
+                                  nullptr, rows, acc, pre_min, w, s);
             m.done();
             if (e != hipSuccess) return hip_fail("cb_step: wide-row scores", e);
         }
-        const int nt = (size_t)t < p->query_nt.size() && query_threads_ok(p->query_nt[(size_t)t])
-                           ? p->query_nt[(size_t)t] : query_threads(p->K);
+        const int nt = query_threads_ok(opt(p->query_nt, t)) ? opt(p->query_nt, t) : query_threads(p->K);
         ProfMark m(p, s, t, CB_KERNEL_STEP_QUERY, nt, Q);
         e = launch_step_query(sd, p->dtype, Q, p->K, Kc, p->d, nt, hidden, Wt, rows, acc, split ? w.cand : nullptr,
-                              split ? w.cand_off : nullptr, split ? w.cap : 0, ot, op, orow, ol, s);
+                              split ? w.cand_off : nullptr, split ? w.cap : 0, pre_min, ot, op, orow, ol, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: sparse step", e);
         return CB_OK;
     }
-    if (!gemm_finds_live(p->dtype, R)) {
+    const bool full = gemm_full(p, t);
+    if (!full && !gemm_finds_live(p->dtype, R)) {
         ProfMark m(p, s, t, CB_KERNEL_LIVE_ROWS, 1024, 1);
         e = launch_live_rows(sd, R, rows, acc, p->live, p->n_live, p->ci_of, s);
         m.done();
@@ -294,22 +327,25 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const vo
     }
     {
         const bool bf = p->dtype == CB_BF16;
-        ProfMark m(p, s, t, bf ? CB_KERNEL_GEMM_BF16 : CB_KERNEL_GEMM_F32, bf ? 512 : 256, gemm_blocks(p->dtype, R, idx->V));
+        ProfMark m(p, s, t, bf ? CB_KERNEL_GEMM_BF16 : CB_KERNEL_GEMM_F32, bf ? 512 : 256,
+                   gemm_blocks(p->dtype, R, idx->V, full));
         e = launch_gemm_scores(p->dtype, R, idx->V, p->d, p->live, p->n_live, hidden, Wt, p->Z, p->Zp, sd, rows, acc,
-                               p->ci_of, s);
+                               p->ci_of, full, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: full-codebook scores", e);
     }
+    bool sided = false;
     {
         ProfMark m(p, s, t, CB_KERNEL_EXPAND_DENSE, expand_threads(sd), R);
         e = launch_beam_expand(sd, true, p->dtype, R, p->K, Kc, p->d, hidden, Wt, p->Z, p->Zp, idx->V, p->n_live,
-                               p->ci_of, rows, acc, p->keys, p->mode, s);
+                               p->ci_of, rows, acc, p->keys, p->side, &sided, p->mode, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: beam expansion", e);
     }
     {
         ProfMark m(p, s, t, CB_KERNEL_MERGE, kMergeThreads, Q);
-        e = launch_query_merge(sd, Q, p->K, Kc, p->keys, rows, ot, op, orow, ol, p->mode, s);
+        e = launch_query_merge(sd, Q, p->K, Kc, p->keys, sided ? p->side : nullptr, rows, ot, op, orow, ol, p->mode,
+                               s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: query merge", e);
     }
@@ -598,12 +634,17 @@ cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_
     p->forced.assign((size_t)idx->L, CB_PATH_AUTO);
     p->tuned.assign((size_t)idx->L, 0);
     p->query_nt.assign((size_t)idx->L, 0);
+    p->gemm_rows.assign((size_t)idx->L, 0);
+    p->radix_pre.assign((size_t)idx->L, 0);
+    p->split_min.assign((size_t)idx->L, 0);
+    p->sparse_form.assign((size_t)idx->L, 0);
     p->tune_dense_us.assign((size_t)idx->L, -1.f);
     p->tune_sparse_us.assign((size_t)idx->L, -1.f);
     p->select.assign((size_t)idx->L, CB_SELECT_AUTO);
     p->tuned_select.assign((size_t)idx->L, 0);
     const size_t R = (size_t)Q_max * K;
     cb_status st = dev_alloc(&p->keys, R * Kc, "candidate keys");
+    if (st == CB_OK) st = dev_alloc(&p->side, R * Kc, "candidate side information");
     if (st == CB_OK) st = dev_alloc(&p->Z, R * (size_t)idx->V, "full-codebook scores");
     if (st == CB_OK && dtype == CB_BF16) st = dev_alloc(&p->Zp, split_scores_floats(idx->V), "partial scores");
     if (st == CB_OK) st = dev_alloc(&p->live, R, "live beams");
@@ -735,31 +776,75 @@ cb_status cb_get_select(const cb_plan* p, int32_t t, cb_select* sel) {
     return CB_OK;
 }
 
-cb_status cb_set_step_threads(cb_plan* p, int32_t t, int32_t threads) {
+cb_status cb_set_step_option(cb_plan* p, int32_t t, cb_step_option o, int32_t value) {
     clear_error();
-    if (!p || t < 0 || t >= p->idx->L || (threads != 0 && !query_threads_ok(threads))) {
-        set_error("cb_set_step_threads: bad plan or step, or threads not 0, 256, 512 or 1024");
+    if (!p || t < 0 || t >= p->idx->L) {
+        set_error("cb_set_step_option: bad plan or step");
         return CB_EINVAL;
     }
     const cb::StepTable& T = p->idx->steps[(size_t)t];
-    const int Kc = std::min(p->K, std::max(T.S, 1));
-    if (query_lds_bytes(T.S, p->K, Kc, p->d, threads) > (size_t)kMaxLds) {
-        set_error("cb_set_step_threads: the step's LDS does not fit that workgroup size");
-        return CB_ECAPACITY;
+    switch (o) {
+        case CB_OPT_STEP_THREADS: {
+            if (value != 0 && !query_threads_ok(value)) {
+                set_error("cb_set_step_option: step threads must be 0, 256, 512 or 1024");
+                return CB_EINVAL;
+            }
+            const int Kc = std::min(p->K, std::max(T.S, 1));
+            if (query_lds_bytes(T.S, p->K, Kc, p->d, value) > (size_t)kMaxLds) {
+                set_error("cb_set_step_option: the step's LDS does not fit that workgroup size");
+                return CB_ECAPACITY;
+            }
+            p->query_nt[(size_t)t] = value;
+            return CB_OK;
+        }
+        case CB_OPT_SPLIT_ROWS:
+            if (value < 0 || value > 64) break;
+            p->split_min[(size_t)t] = value;
+            return CB_OK;
+        case CB_OPT_SPARSE_FORM:
+            if (value < 0 || value > 1) break;
+            if (value == 1 && expand_lds_bytes(T.S, p->d, false) > (size_t)kMaxLds) {
+                set_error("cb_set_step_option: the per-beam expansion of this step does not fit the LDS");
+                return CB_ECAPACITY;
+            }
+            p->sparse_form[(size_t)t] = value;
+            return CB_OK;
+        case CB_OPT_DENSE_ROWS:
+            if (value < 0 || value > 2) break;
+            if (value == 2 && !gemm_full_ok(p->dtype)) {
+                set_error("cb_set_step_option: the product over every slot needs a bf16 plan");
+                return CB_EUNSUPPORTED;
+            }
+            p->gemm_rows[(size_t)t] = value;
+            return CB_OK;
+        case CB_OPT_RADIX_PREPASS:
+            if (value < 0 || value > 2) break;
+            p->radix_pre[(size_t)t] = value;
+            return CB_OK;
     }
-    p->query_nt[(size_t)t] = threads;
-    return CB_OK;
+    set_error("cb_set_step_option: unknown option or value out of range");
+    return CB_EINVAL;
 }
 
-cb_status cb_get_step_threads(const cb_plan* p, int32_t t, int32_t* threads) {
+cb_status cb_get_step_option(const cb_plan* p, int32_t t, cb_step_option o, int32_t* value) {
     clear_error();
-    if (!p || !threads || t < 0 || t >= p->idx->L) {
-        set_error("cb_get_step_threads: bad plan, step or output");
+    if (!p || !value || t < 0 || t >= p->idx->L) {
+        set_error("cb_get_step_option: bad plan, step or output");
         return CB_EINVAL;
     }
-    const int32_t v = p->query_nt[(size_t)t];
-    *threads = query_threads_ok(v) ? v : query_threads(p->K);
-    return CB_OK;
+    switch (o) {
+        case CB_OPT_STEP_THREADS: {
+            const int32_t v = p->query_nt[(size_t)t];
+            *value = query_threads_ok(v) ? v : query_threads(p->K);
+            return CB_OK;
+        }
+        case CB_OPT_SPLIT_ROWS: *value = p->split_min[(size_t)t] > 0 ? p->split_min[(size_t)t] : kPreMin; return CB_OK;
+        case CB_OPT_SPARSE_FORM: *value = (p->d > kQueryMaxD || p->sparse_form[(size_t)t] == 1) ? 1 : 0; return CB_OK;
+        case CB_OPT_DENSE_ROWS: *value = gemm_full(p, t) ? 2 : 1; return CB_OK;
+        case CB_OPT_RADIX_PREPASS: *value = p->radix_pre[(size_t)t] == 1 ? 1 : 2; return CB_OK;
+    }
+    set_error("cb_get_step_option: unknown option");
+    return CB_EINVAL;
 }
 
 cb_status cb_get_path(const cb_plan* p, int32_t t, cb_path* path) {
@@ -861,30 +946,49 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
             // time every allowed (scoring path, selection) pair on this step's inputs, outputs to scratch
             float best_us[2] = {-1.f, -1.f};  // dense, sparse (either variant): best over the selections
             float best = -1.f;
-            int32_t best_path = 0, best_sel = 0, best_nt = 0;
+            int32_t best_path = 0, best_sel = 0, best_nt = 0, best_rows = 0, best_pre = 0, best_min = 0, best_form = 0;
             const int32_t paths[3] = {CB_PATH_DENSE, CB_PATH_SPARSE, CB_PATH_SPARSE_SPLIT};
             const int32_t sels[2] = {CB_SELECT_LDS, CB_SELECT_RADIX};
             const cb::StepTable& T = idx->steps[(size_t)t];
-            const bool has_wide = T.store == CB_STORE_BITMAP || T.S > 64;
+            // the split variant scores rows apart (it differs from plain sparse on any step with multi-token rows)
+            const bool has_wide = T.store == CB_STORE_BITMAP || T.S > 1;
             for (int k = 0; k < 3 && st == CB_OK; ++k) {
                 if (!path_free && paths[k] != resolve_path(p, t)) continue;
                 if (paths[k] == CB_PATH_DENSE && !dense_available(p)) continue;
                 for (int m = 0; m < 2 && st == CB_OK; ++m) {
                     if (!sel_free && sels[m] != p->select[(size_t)t]) continue;
                     if (sels[m] == CB_SELECT_LDS && !lds_select_ok(p, t)) continue;
-                    // the split variant differs from plain sparse only on LDS steps with wide rows
                     if (paths[k] == CB_PATH_SPARSE_SPLIT && (sels[m] != CB_SELECT_LDS || !has_wide)) continue;
                     if ((paths[k] == CB_PATH_SPARSE_SPLIT || sels[m] == CB_SELECT_RADIX) && wide_alloc(p) != CB_OK) {
                         (void)hipGetLastError();
                         clear_error();
                         continue;
                     }
-                    // the per-query sparse step at its default workgroup size and at 256 threads
-                    // (same bits either way: a step of few multi-token rows starts faster on the smaller)
+                    // variants with the same results: the per-query sparse step at its default
+                    // workgroup size and at 256 threads (a step of few multi-token rows starts
+                    // faster on the smaller); the full-codebook product over the live beams or
+                    // over every slot (no live list)
                     const bool per_query = paths[k] != CB_PATH_DENSE && sels[m] == CB_SELECT_LDS && p->d <= kQueryMaxD;
-                    const int nts[2] = {0, 256};
-                    for (int v = 0; v < (per_query ? 2 : 1) && st == CB_OK; ++v) {
-                        p->query_nt[(size_t)t] = nts[v];
+                    const bool rows_var = paths[k] == CB_PATH_DENSE && gemm_full_ok(p->dtype);
+                    // the radix selection with and without its one-token pre-pass (sparse scoring)
+                    const bool pre_var = paths[k] != CB_PATH_DENSE && sels[m] == CB_SELECT_RADIX;
+                    // the split path scoring apart the rows above 16 tokens, or every multi-token row
+                    const bool split_var = paths[k] == CB_PATH_SPARSE_SPLIT && per_query;
+                    // the plain sparse path also in its per-beam form (expansion over the whole
+                    // GPU, then the per-query merge)
+                    const bool form_var = paths[k] == CB_PATH_SPARSE && per_query &&
+                                          expand_lds_bytes(T.S, p->d, false) <= (size_t)kMaxLds;
+                    const int nts[4] = {0, 256, 0, 256};
+                    const int mins[4] = {kPreMin, kPreMin, 1, 1};
+                    const int nv0 = split_var ? 4 : per_query || rows_var || pre_var ? 2 : 1;
+                    const int nv = nv0 + (form_var ? 1 : 0);
+                    for (int v = 0; v < nv && st == CB_OK; ++v) {
+                        const bool beam_form = v == nv0;
+                        p->sparse_form[(size_t)t] = beam_form ? 1 : 0;
+                        p->query_nt[(size_t)t] = per_query && !beam_form ? nts[v] : 0;
+                        p->split_min[(size_t)t] = split_var ? mins[v] : 0;
+                        p->gemm_rows[(size_t)t] = rows_var ? 1 + v : 0;
+                        p->radix_pre[(size_t)t] = pre_var && !beam_form ? 1 + v : 0;
                         st = run_step(p, t, Q, paths[k], sels[m], p->h, Wt, p->rows[cur], p->acc[cur],
                                       p->scratch_tok, p->scratch_par, p->scratch_rows, p->scratch_logp, s);
                         if (st != CB_OK) break;
@@ -906,10 +1010,18 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
                             best = us;
                             best_path = paths[k];
                             best_sel = sels[m];
-                            best_nt = nts[v];
+                            best_nt = p->query_nt[(size_t)t];
+                            best_rows = p->gemm_rows[(size_t)t];
+                            best_pre = p->radix_pre[(size_t)t];
+                            best_min = p->split_min[(size_t)t];
+                            best_form = p->sparse_form[(size_t)t];
                         }
                     }
                     p->query_nt[(size_t)t] = 0;
+                    p->split_min[(size_t)t] = 0;
+                    p->gemm_rows[(size_t)t] = 0;
+                    p->radix_pre[(size_t)t] = 0;
+                    p->sparse_form[(size_t)t] = 0;
                 }
             }
             if (st != CB_OK) break;
@@ -918,6 +1030,10 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
             if (best_path) p->tuned[(size_t)t] = best_path;
             if (best_sel) p->tuned_select[(size_t)t] = best_sel;
             p->query_nt[(size_t)t] = best_nt;
+            p->gemm_rows[(size_t)t] = best_rows;
+            p->radix_pre[(size_t)t] = best_pre;
+            p->split_min[(size_t)t] = best_min;
+            p->sparse_form[(size_t)t] = best_form;
         }
         st = run_step(p, t, Q, resolve_path(p, t), resolve_select(p, t), p->h, Wt, p->rows[cur], p->acc[cur],
                       p->hist_tok + (size_t)t * R, p->hist_par + (size_t)t * R, p->rows[1 - cur], p->acc[1 - cur], s);
@@ -1220,6 +1336,7 @@ void cb_plan_destroy(cb_plan* p) {
     profile_release(p);
     wide_release(p);
     dev_free(p->keys);
+    dev_free(p->side);
     dev_free(p->Z);
     dev_free(p->Zp);
     dev_free(p->live);

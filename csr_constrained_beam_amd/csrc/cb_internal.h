@@ -100,6 +100,7 @@ constexpr int kQueryMaxD = 2048;     // hidden width the fused per-query sparse 
                                      // (wider: per-beam expansion + per-query merge, or the radix path)
 constexpr int kMaxKRadix = 1024;     // beam width of the radix-select path (10-bit parent field of a key)
 constexpr int kMaxLds = 65536;       // LDS one workgroup may use
+constexpr int kPreMin = 16;          // split sparse path: rows above this many tokens scored apart, unless measured
 constexpr int kExpandThreads = 256;  // per-beam expansion workgroup
 constexpr int kMergeThreads = 256;   // per-query merge workgroup (dense path)
 }
@@ -116,6 +117,8 @@ struct WideDev {
     void* sel = nullptr;           // [Q_max] selection state
     int32_t* surv_n = nullptr;     // [Q_max] survivors collected
     uint64_t* surv = nullptr;      // [Q_max][survivor cap]
+    int32_t* done = nullptr;       // [Q_max] 1: the pre-pass (k_wide_small) wrote the query's outputs
+    int32_t use_done = 0;          // the kernels skip the queries marked done (set when the pre-pass ran)
     int64_t cap = 0, chunk_cap = 0;
 };
 }  // namespace cb
@@ -129,9 +132,14 @@ struct cb_plan {
     std::vector<int32_t> forced;  // per step: CB_PATH_* set by the caller
     std::vector<int32_t> tuned;   // per step: measured choice (0 = none)
     std::vector<int32_t> query_nt;  // per step: workgroup size of the per-query sparse step (0 = default), measured
+    std::vector<int32_t> gemm_rows; // per step: product over live beams (1), every slot (2), or 0 = default
+    std::vector<int32_t> radix_pre; // per step: radix selection with (2) or without (1) the one-token pre-pass, 0 = default
+    std::vector<int32_t> split_min; // per step: split sparse path scores apart the rows above this many tokens (0 = 16)
+    std::vector<int32_t> sparse_form; // per step: sparse step as one kernel per query (0) or per-beam expansion + merge (1)
     std::vector<float> tune_dense_us, tune_sparse_us;
     // workspace (allocated once)
-    uint64_t* keys = nullptr;     // [Q_max*K][Kc_max] per-beam survivors (dense path)
+    uint64_t* keys = nullptr;     // [Q_max*K][Kc_max] per-beam survivors (dense path, per-beam sparse form)
+    uint64_t* side = nullptr;     // [Q_max*K][Kc_max] their next row << 16 | token (per-beam expansion)
     float* Z = nullptr;           // [Q_max*K][V] full-codebook scores (dense path)
     float* Zp = nullptr;          // [k-slices][rows][V] partial scores (dense path, few live beams)
     int32_t* live = nullptr;      // [Q_max*K] live beam slots (dense path)
@@ -181,31 +189,39 @@ int expand_bitmap_max_v();
 size_t query_lds_bytes(int S, int K, int Kc, int d, int nt = 0);
 int tail_threads(int K);
 size_t tail_lds_bytes(int S, int K, int Kc, int d);
-int gemm_blocks(cb_dtype dt, int R, int V);
+int gemm_blocks(cb_dtype dt, int R, int V, bool full);
 
 // Sparse path: the whole step in one launch, one workgroup per query.
 // pre / pre_off / pre_cap: scores of the wide rows from launch_wide_score(...,
-// wide_only = 1, ...) (candidate z bits in the high half, per-query offsets
+// wide_only = pre_min, ...) (candidate z bits in the high half, per-query offsets
 // [K+1], per-query capacity), or null to score them in the step kernel.
 // nt: workgroup size (256, 512 or 1024; 0 = query_threads(K)); every size gives the same bits.
+// pre_min: rows of more than pre_min tokens (and bitmap rows) read their scores from pre.
 hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int Kc, int d, int nt, const void* hidden,
                              const void* W, const int32_t* beam_rows, const float* acc, const uint64_t* pre,
-                             const int32_t* pre_off, int64_t pre_cap, int32_t* tok, int32_t* par, int32_t* rows,
-                             float* logp, hipStream_t s);
+                             const int32_t* pre_off, int64_t pre_cap, int pre_min, int32_t* tok, int32_t* par,
+                             int32_t* rows, float* logp, hipStream_t s);
 // Dense path: live-beam list, full-codebook scores, per-beam expansion, per-query merge.
 hipError_t launch_live_rows(const StepDev& st, int R, const int32_t* beam_rows, const float* acc, int32_t* live,
                             int32_t* n_live, int32_t* ci_of, hipStream_t s);
 // Whether the bf16 product finds the live beams itself (no k_live_rows).
 bool gemm_finds_live(cb_dtype dt, int R);
+// Whether the product can run over every beam slot (full = true: no live
+// list, scores indexed by slot; the consumers learn it from n_live = -1).
+bool gemm_full_ok(cb_dtype dt);
 hipError_t launch_gemm_scores(cb_dtype dt, int R, int V, int d, const int32_t* live, int32_t* n_live,
                               const void* H, const void* W, float* Z, float* Zp, const StepDev& st,
-                              const int32_t* beam_rows, const float* acc, int32_t* ci_of, hipStream_t s);
+                              const int32_t* beam_rows, const float* acc, int32_t* ci_of, bool full,
+                              hipStream_t s);
 size_t split_scores_floats(int V);
+// Per-beam expansion (keys [R][Kc]); *sided tells whether the keys carry
+// list places with side information [R][Kc] (then the merge takes `side`).
 hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R, int K, int Kc, int d,
                               const void* hidden, const void* W, const float* Z, const float* Zp, int64_t ldz,
                               const int32_t* n_live, const int32_t* ci_of, const int32_t* beam_rows,
-                              const float* acc, uint64_t* keys, int mode, hipStream_t s);
-hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uint64_t* keys,
+                              const float* acc, uint64_t* keys, uint64_t* side, bool* sided, int mode,
+                              hipStream_t s);
+hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uint64_t* keys, const uint64_t* side,
                               const int32_t* beam_rows, int32_t* tok, int32_t* par, int32_t* rows, float* logp,
                               int mode, hipStream_t s);
 hipError_t launch_decode_init(int Q, int K, int d, cb_dtype dt, const float* q, float* s_out, void* h_out,
@@ -239,6 +255,11 @@ hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, 
                              const void* W, const float* Z, const float* Zp, int64_t ldz, const int32_t* n_live,
                              const int32_t* ci_of, const int32_t* beam_rows, const float* acc, int wide_only,
                              const WideDev& w, hipStream_t s);
+// Pre-pass of the radix selection: one workgroup per query finishes every
+// query whose live rows all hold one token (outputs written, done[q] = 1)
+// and leaves the others to the radix kernels (done[q] = 0).
+hipError_t launch_wide_small(const StepDev& st, int Q, int K, const int32_t* beam_rows, const float* acc,
+                             const WideDev& w, int32_t* tok, int32_t* par, int32_t* rows, float* logp, hipStream_t s);
 hipError_t launch_wide_keys(int Q, int K, const float* acc, const WideDev& w, hipStream_t s);
 hipError_t launch_wide_refine(int Q, int K, const WideDev& w, hipStream_t s);
 hipError_t launch_wide_collect(int Q, int K, const WideDev& w, hipStream_t s);

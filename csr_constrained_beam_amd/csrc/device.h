@@ -29,8 +29,6 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kSmallRow = 64;  // rows up to this many tokens take the one-wave path
-constexpr int kPreMin = 16;    // with scores computed apart: rows above this many tokens read them
-constexpr int kMidRow = 4;     // rows above this many tokens (up to kSmallRow) are scored by the whole block
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
@@ -582,15 +580,16 @@ __device__ void block_scores(const float* h_s, const DT* __restrict__ W, int d, 
 
 // block_scores for d <= CH * 512: every wave takes U tokens at a time with all
 // their W_t row chunks in flight at once (the plain version waits one round
-// trip per chunk), h held in registers.  Products summed in the same order as
-// block_scores (chunk by chunk, then the wave butterfly), so z is identical.
-template <typename DT, int NT, int CH>
+// trip per chunk), h held in registers; U = BUDGET / (VGPRs of one token's
+// raw row chunks).  Products summed in the same order as block_scores (chunk
+// by chunk, then the wave butterfly), so z is identical.
+template <typename DT, int NT, int CH, int BUDGET = 48>
 __device__ void block_scores_ch(const float* h_s, const DT* __restrict__ W, int d, const uint16_t* tok_s, int n,
                                 float* z_s) {
     const int lane = threadIdx.x & (kWave - 1);
     constexpr int NW = NT / kWave;
     constexpr int kRegs = CH * (sizeof(DT) == 2 ? 4 : 8);  // VGPRs per token in flight
-    constexpr int U = 48 / kRegs > 0 ? 48 / kRegs : 1;
+    constexpr int U = BUDGET / kRegs > 0 ? BUDGET / kRegs : 1;
     float h[CH][8];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -679,10 +678,12 @@ constexpr int kCUs = 256;
 // Number of k-slices the full-codebook product uses for n_live live beams:
 // more than one only when the tiles alone would leave most compute units idle.
 // The slices' partial sums are added in slice order by the consumer.
+// A negative count marks a product over every beam slot (no compaction):
+// one slice, scores indexed by slot.
 __host__ __device__ inline int gemm_split(int n_live, int V, int d) {
     const int tiles = ((n_live + kBM - 1) / kBM) * ((V + kBN - 1) / kBN);
     int s = 1;
-    if (n_live > kSplitRows) return 1;
+    if (n_live < 0 || n_live > kSplitRows) return 1;
     while (s < kSplitMax && tiles * s * 2 <= kCUs && (d / kBK) % (s * 2) == 0) s *= 2;
     return s;
 }

@@ -81,14 +81,15 @@ __device__ void emit(const StepDev& st, int q, int K, int i, uint64_t key, const
 }
 
 // Output slot i of query q from its key, in the fused sparse step: the
-// parent's row start, width and (narrow CSR rows) sorted tokens were kept in
-// LDS when the row was read, so the next row needs no global reads there.
-// n_s[p] >= 0: narrow row of n_s[p] tokens in tokq[p * 64 ...]; otherwise a
-// wide row of -1 - n_s[p] tokens, searched in the step table.  nrows / nacc
-// (may be NULL): LDS copies of the next rows and log-probs, per slot.
-__device__ void emit_query(const StepDev& st, int q, int K, int i, uint64_t key, const int32_t* r_s,
-                           const uint32_t* e0_s, const int* n_s, const uint16_t* tokq, int32_t* out_tok,
-                           int32_t* out_par, int32_t* out_rows, float* out_logp, int32_t* nrows, float* nacc) {
+// parent's row start, width and tokens were kept in LDS when the row was
+// read, so the next row needs no global reads.  n_s[p] >= 0: narrow row of
+// n_s[p] tokens, sorted, in tokq[p * 64 ...]; otherwise a wide row of
+// -1 - n_s[p] tokens whose best min(Kc, n) candidates left their tokens in
+// tokq[p * 64 ...] and their positions in the row in jq[p * 64 ...].  nrows /
+// nacc (may be NULL): LDS copies of the next rows and log-probs, per slot.
+__device__ void emit_query(int q, int K, int Kc, int i, uint64_t key, const uint32_t* e0_s, const int* n_s,
+                           const uint16_t* tokq, const int* jq, int32_t* out_tok, int32_t* out_par, int32_t* out_rows,
+                           float* out_logp, int32_t* nrows, float* nacc) {
     const int64_t o = (int64_t)q * K + i;
     if (key == 0ull) {
         out_tok[o] = -1;
@@ -114,16 +115,13 @@ __device__ void emit_query(const StepDev& st, int q, int K, int i, uint64_t key,
             if ((int)tq[mid] < token) lo = mid + 1; else hi = mid;
         }
         row = (int32_t)(e0 + lo);
-    } else if (st.store == CB_STORE_CSR) {
-        uint32_t lo = 0, hi = (uint32_t)(-1 - nn);
-        while (lo < hi) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if ((int)st.tok[e0 + mid] < token) lo = mid + 1; else hi = mid;
-        }
-        row = (int32_t)(e0 + lo);
     } else {
-        const int64_t x = (int64_t)r_s[parent] * st.words + (token >> 5);
-        row = (int32_t)(e0 + st.rank[x] + __popc(st.bits[x] & ((1u << (token & 31)) - 1u)));
+        const int m = min(Kc, -1 - nn);
+        const uint16_t* tq = tokq + parent * kWave;
+        int j = 0;
+        for (int x = 0; x < m; ++x)
+            if ((int)tq[x] == token) j = jq[parent * kWave + x];
+        row = (int32_t)(e0 + j);
     }
     const float lp = score_from_order_bits((uint32_t)(key >> 32));
     out_tok[o] = token;
@@ -166,11 +164,19 @@ __host__ __device__ inline QueryLds query_lds(int S, int K, int Kc, int d, int N
     l.tok = l.h + ((d * 4 + 15) & ~15);
     l.tokq = l.tok + ((S * 2 + 15) & ~15);
     l.zmid = l.tokq + ((K * kWave * 2 + 15) & ~15);
-    l.total = l.zmid + (S > kMidRow ? K * kWave * 4 : 0);
+    l.total = l.zmid + (S > 1 ? K * kWave * 4 : 0);
     return l;
 }
 
 // ---- sparse step: one workgroup per query ----------------------------------
+
+// Tokens per scoring task of the per-query step (phase 1b), within a register
+// budget: the task's W_t row chunks plus the beam's hidden-vector chunks.
+template <typename DT, int CH>
+__host__ __device__ constexpr int kTaskTokens() {
+    constexpr int kRw = sizeof(DT) == 2 ? 4 : 8;
+    return 4 * CH * kRw + CH * 8 <= 96 ? 4 : (2 * CH * kRw + CH * 8 <= 96 ? 2 : 1);
+}
 
 // The whole sparse step of query q by one workgroup (body of k_step_query and
 // of each step of k_decode_tail).  rows_q / acc_q: the query's K beam rows
@@ -183,10 +189,10 @@ template <typename DT, int NT, int CH>
 __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d, const DT* __restrict__ hidden,
                                  const DT* __restrict__ W, const int32_t* __restrict__ rows_q,
                                  const float* __restrict__ acc_q, const uint64_t* __restrict__ pre,
-                                 const int32_t* __restrict__ pre_off, int64_t pre_cap, int32_t* __restrict__ out_tok,
-                                 int32_t* __restrict__ out_par, int32_t* __restrict__ out_rows,
-                                 float* __restrict__ out_logp, unsigned char* smem, uint64_t* best,
-                                 int32_t* nrows, float* nacc) {
+                                 const int32_t* __restrict__ pre_off, int64_t pre_cap, int pre_min,
+                                 int32_t* __restrict__ out_tok, int32_t* __restrict__ out_par,
+                                 int32_t* __restrict__ out_rows, float* __restrict__ out_logp, unsigned char* smem,
+                                 uint64_t* best, int32_t* nrows, float* nacc) {
     __shared__ float red_f[red_slots<NT>()];
     __shared__ int red_i[NT / kWave];
     __shared__ uint64_t bcast;
@@ -198,11 +204,9 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
     __shared__ int n_s[kWave];
     __shared__ int nbig;
     __shared__ int big[kWave];
-    __shared__ int nsm;               // rows of 2..kSmallRow tokens (their tokens are read in phase 1)
+    __shared__ int nsm;               // rows of 2..kSmallRow tokens (phases 1 - 1c)
     __shared__ int sml[kWave];
-    __shared__ int nmid;              // rows scored by the whole block (phase 1b)
-    __shared__ int mid[kWave];
-    __shared__ int moff[kWave + 1];   // their first task
+    __shared__ int moff[kWave + 1];   // their first scoring task
     __shared__ int ncand;             // keys in the candidate list qkeys
     __shared__ int ident;             // the step is the identity (see the prologue)
     __shared__ uint64_t slot[kWave];  // survivors of one wide row
@@ -215,6 +219,7 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
     uint16_t* tok_s = reinterpret_cast<uint16_t*>(smem + lay.tok);
     uint16_t* tokq = reinterpret_cast<uint16_t*>(smem + lay.tokq);
     float* zmid = reinterpret_cast<float*>(smem + lay.zmid);
+    int* jmid = reinterpret_cast<int*>(smem + lay.zmid);  // wide rows: positions of their survivors
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
     constexpr int NW = NT / kWave;
@@ -237,8 +242,6 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
         const bool csr = st.store == CB_STORE_CSR;
         const bool one = live && csr && n == 1 && st.tok0;
         const bool narrow = live && csr && !one && n <= kSmallRow;
-        // rows above kMidRow tokens (scores not computed apart) are scored by the block (phase 1b)
-        const bool midr = narrow && n > kMidRow && !(pre && n > kPreMin);
         const bool wide = live && !one && !narrow;
         if (live) {
             r_s[k] = r;
@@ -248,12 +251,11 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
         }
         if (one) tokq[k * kWave] = (uint16_t)f0;
         const uint64_t key = one ? make_key(a + 0.f, k, f0) : 0ull;
-        const uint64_t m_one = __ballot(one), m_nar = __ballot(narrow), m_mid = __ballot(midr),
-                       m_wide = __ballot(wide), m_live = __ballot(live);
+        const uint64_t m_one = __ballot(one), m_nar = __ballot(narrow), m_wide = __ballot(wide),
+                       m_live = __ballot(live);
         const uint64_t below = (1ull << lane) - 1ull;
         if (one) qkeys[__popcll(m_one & below)] = key;
         if (narrow) sml[__popcll(m_nar & below)] = k;
-        if (midr) mid[__popcll(m_mid & below)] = k;
         if (wide) big[__popcll(m_wide & below)] = k;
         // identity: every live row has one token, the live slots come first
         // and their log-probs do not increase, so the K candidates (acc_k,
@@ -279,7 +281,6 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
         if (lane == 0) {
             ncand = __popcll(m_one);
             nsm = __popcll(m_nar);
-            nmid = __popcll(m_mid);
             nbig = __popcll(m_wide);
             ident = id;
         }
@@ -287,190 +288,108 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
     __syncthreads();
     if (ident) return;  // uniform over the workgroup
 
-    // phase 1: one wave per row of 2..64 tokens, two rows per wave in flight:
-    // lane j holds the row's token j; rows of up to kMidRow tokens (and rows
-    // whose scores were computed apart) are scored here, the rest in phase 1b
+    // phase 1: the tokens of every row of 2..64 tokens (CSR) into the
+    // query's fixed slots tokq[k * 64 + j], all rows at once (one global round
+    // trip); rows whose scores were computed apart get them here too
     const int ns = nsm;
-    for (int i0 = wv; i0 < ns; i0 += 2 * NW) {
-        int kk[2], tk[2], n[2];
-        float a[2];
-        bool on2[2], midr[2];
-        uint32_t e0[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int i = i0 + u * NW;
-            on2[u] = i < ns;
-            kk[u] = on2[u] ? sml[i] : 0;
-            n[u] = on2[u] ? n_s[kk[u]] : 0;
-            e0[u] = on2[u] ? e0_s[kk[u]] : 0u;
-            a[u] = on2[u] ? a_s[kk[u]] : -INFINITY;
-            midr[u] = on2[u] && n[u] > kMidRow && !(pre && n[u] > kPreMin);
-            tk[u] = on2[u] && lane < n[u] ? (int)st.tok[e0[u] + lane] : 0;
+    for (int x = tid; x < ns * kWave; x += NT) {
+        const int k = sml[x / kWave], j = x % kWave, n = n_s[k];
+        if (j < n) {
+            tokq[k * kWave + j] = st.tok[e0_s[k] + j];
+            if (pre && n > pre_min)
+                zmid[k * kWave + j] =
+                    __uint_as_float((uint32_t)(pre[(int64_t)q * pre_cap + pre_off[(int64_t)q * (K + 1) + k] + j] >> 32));
         }
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            if (on2[u] && lane < n[u]) tokq[kk[u] * kWave + lane] = (uint16_t)tk[u];
-        // rows whose scores were computed apart are read, the others scored here
-        bool dots[2];
-        float z[2] = {-INFINITY, -INFINITY};
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const bool ready = pre && on2[u] && n[u] > kPreMin;
-            dots[u] = on2[u] && !ready && !midr[u];
-            if (ready && lane < n[u])
-                z[u] = __uint_as_float((uint32_t)(pre[(int64_t)q * pre_cap + pre_off[(int64_t)q * (K + 1) + kk[u]] +
-                                                      lane] >> 32));
-        }
-        // rows for phase 1b only needed their tokens
-        if (!(on2[0] && !midr[0]) && !(on2[1] && !midr[1])) continue;
-        // hidden vectors kept raw until used (a conversion right after the
-        // load would make each load wait before the next is issued)
-        Raw8<DT> hr[2][CH];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                const int i = c * kWave * 8 + lane * 8;
-                if (dots[u] && i < d) hr[u][c].load(hidden + ((int64_t)q * K + kk[u]) * d + i);
-                else hr[u][c].zero();
-            }
-        const int nmax = max(dots[0] ? n[0] : 0, dots[1] ? n[1] : 0);
-        // kTok tokens of each of the two beams at a time: all their W_t row
-        // loads are issued before any is reduced, so the latencies overlap
-        // (as many as the register budget of a 1024-thread workgroup allows)
-        constexpr int kTok = CH >= 4 ? 1 : 4 / CH;
-        for (int j0 = 0; j0 < nmax; j0 += kTok) {
-            Raw8<DT> wr8[2][kTok][CH];
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int jj = 0; jj < kTok; ++jj) {
-                    const int j = j0 + jj;
-                    const int tj = lane_bcast(tk[u], j < kWave ? j : 0);
-                    const bool on = dots[u] && j < n[u];
-                    const DT* wr = W + (int64_t)tj * d;
-#pragma unroll
-                    for (int c = 0; c < CH; ++c) {
-                        const int i = c * kWave * 8 + lane * 8;
-                        if (on && i < d) wr8[u][jj][c].load(wr + i);
-                        else wr8[u][jj][c].zero();
-                    }
-                }
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int jj = 0; jj < kTok; ++jj) {
-                    float sv = 0.f;
-#pragma unroll
-                    for (int c = 0; c < CH; ++c) sv = wr8[u][jj][c].dot_raw(hr[u][c], sv);
-                    const float t = wave_sum(sv);
-                    if (dots[u] && lane == j0 + jj) z[u] = t;
-                }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            if (!on2[u] || midr[u]) continue;
-            const bool on = lane < n[u];
-            const int w = pow2_at_least(n[u]);
-            const float m = wave_max_w(on ? z[u] : -INFINITY, w);
-            const float se = wave_sum_w(on ? exp_sm(z[u] - m) : 0.f, w);
-            const float lse = m + logf(se);
-            uint64_t key = on ? make_key(a[u] + (z[u] - lse), kk[u], tk[u]) : 0ull;
-            if (n[u] > Kc) key = wave_sort_desc(key);
-            // the beam's best min(n, Kc) join the query's candidate list
-            wave_append(lane < min(n[u], Kc), key, qkeys, &ncand);
-        }
+    }
+    if (wv == 0) {
+        // tasks of MT consecutive tokens of one row, over every row still to score
+        const int k = lane < ns ? sml[lane] : 0;
+        const int n = lane < ns ? n_s[k] : 0;
+        const int c = lane < ns && !(pre && n > pre_min) ? (n + kTaskTokens<DT, CH>() - 1) / kTaskTokens<DT, CH>() : 0;
+        const int incl = wave_inclusive_scan(c);
+        if (lane < ns) moff[lane + 1] = incl;
+        if (lane == 0) moff[0] = 0;
     }
     __syncthreads();
 
-    // phase 1b: rows of kMidRow+1 .. kSmallRow tokens, scored by the whole
-    // block.  Their tokens form a flat list of tasks of MT consecutive
-    // tokens of one row; each wave takes TPW tasks at a time, so every wave
-    // has TPW * MT W_t rows in flight (a wave working through one such row
-    // alone would wait a global round trip for every few tokens).  The dot
-    // products are summed in the same order as in phase 1.
-    // tokens per task and tasks in flight per wave, within a register budget
+    // phase 1b: scores of those rows, by the whole block.  Their tokens form
+    // a flat list of tasks of MT consecutive tokens of one row; each wave
+    // takes TPW tasks at a time, so that every wave has TPW * MT W_t rows in
+    // flight and all the rows of the query are scored in as few global round
+    // trips as the block's width allows.  Per token the products are summed
+    // chunk by chunk, then by the wave butterfly.
     constexpr int kRw = sizeof(DT) == 2 ? 4 : 8;  // VGPRs per 8 elements of a W_t row
-    constexpr int MT = 4 * CH * kRw + CH * 8 <= 96 ? 4 : (2 * CH * kRw + CH * 8 <= 96 ? 2 : 1);
+    constexpr int MT = kTaskTokens<DT, CH>();
     constexpr int TPW = 2 * (MT * CH * kRw + CH * 8) <= 96 ? 2 : 1;
-    const int nm = nmid;
-    if (nm > 0) {
-        if (wv == 0) {
-            const int c = lane < nm ? (n_s[mid[lane]] + MT - 1) / MT : 0;
-            const int incl = wave_inclusive_scan(c);
-            if (lane < nm) moff[lane + 1] = incl;
-            if (lane == 0) moff[0] = 0;
-        }
-        __syncthreads();
-        const int ntask = moff[nm];
-        for (int t0 = wv; t0 < ntask; t0 += TPW * NW) {
-            int kq[TPW], j0[TPW], nn[TPW];
+    const int ntask = moff[ns];
+    for (int t0 = wv; t0 < ntask; t0 += TPW * NW) {
+        int kq[TPW], j0[TPW], nn[TPW];
 #pragma unroll
-            for (int u = 0; u < TPW; ++u) {
-                const int task = t0 + u * NW;
-                int lo = 0;
-                if (task < ntask) {  // the row whose tasks hold this one: last i with moff[i] <= task
-                    int hi = nm;
-                    while (hi - lo > 1) {
-                        const int md = (lo + hi) >> 1;
-                        if (moff[md] <= task) lo = md; else hi = md;
-                    }
+        for (int u = 0; u < TPW; ++u) {
+            const int task = t0 + u * NW;
+            int lo = 0;
+            if (task < ntask) {  // the row whose tasks hold this one: last i with moff[i] <= task
+                int hi = ns;
+                while (hi - lo > 1) {
+                    const int md = (lo + hi) >> 1;
+                    if (moff[md] <= task) lo = md; else hi = md;
                 }
-                kq[u] = task < ntask ? mid[lo] : 0;
-                j0[u] = task < ntask ? (task - moff[lo]) * MT : 0;
-                nn[u] = task < ntask ? min(MT, n_s[kq[u]] - j0[u]) : 0;
             }
-            Raw8<DT> hr[TPW][CH];
-            Raw8<DT> w8[TPW][MT][CH];
+            kq[u] = task < ntask ? sml[lo] : 0;
+            j0[u] = task < ntask ? (task - moff[lo]) * MT : 0;
+            nn[u] = task < ntask ? min(MT, n_s[kq[u]] - j0[u]) : 0;
+        }
+        Raw8<DT> hr[TPW][CH];
+        Raw8<DT> w8[TPW][MT][CH];
 #pragma unroll
-            for (int u = 0; u < TPW; ++u)
+        for (int u = 0; u < TPW; ++u)
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int i2 = c * kWave * 8 + lane * 8;
+                if (nn[u] > 0 && i2 < d) hr[u][c].load(hidden + ((int64_t)q * K + kq[u]) * d + i2);
+                else hr[u][c].zero();
+            }
+#pragma unroll
+        for (int u = 0; u < TPW; ++u)
+#pragma unroll
+            for (int jj = 0; jj < MT; ++jj) {
+                const bool on = jj < nn[u];
+                const int tkn = on ? (int)tokq[kq[u] * kWave + j0[u] + jj] : 0;
 #pragma unroll
                 for (int c = 0; c < CH; ++c) {
-                    const int i = c * kWave * 8 + lane * 8;
-                    if (nn[u] > 0 && i < d) hr[u][c].load(hidden + ((int64_t)q * K + kq[u]) * d + i);
-                    else hr[u][c].zero();
+                    const int i2 = c * kWave * 8 + lane * 8;
+                    if (on && i2 < d) w8[u][jj][c].load(W + (int64_t)tkn * d + i2);
+                    else w8[u][jj][c].zero();
                 }
+            }
 #pragma unroll
-            for (int u = 0; u < TPW; ++u)
+        for (int u = 0; u < TPW; ++u)
 #pragma unroll
-                for (int jj = 0; jj < MT; ++jj) {
-                    const bool on = jj < nn[u];
-                    const int tkn = on ? (int)tokq[kq[u] * kWave + j0[u] + jj] : 0;
+            for (int jj = 0; jj < MT; ++jj) {
+                float sv = 0.f;
 #pragma unroll
-                    for (int c = 0; c < CH; ++c) {
-                        const int i = c * kWave * 8 + lane * 8;
-                        if (on && i < d) w8[u][jj][c].load(W + (int64_t)tkn * d + i);
-                        else w8[u][jj][c].zero();
-                    }
-                }
-#pragma unroll
-            for (int u = 0; u < TPW; ++u)
-#pragma unroll
-                for (int jj = 0; jj < MT; ++jj) {
-                    float sv = 0.f;
-#pragma unroll
-                    for (int c = 0; c < CH; ++c) sv = w8[u][jj][c].dot_raw(hr[u][c], sv);
-                    const float t = wave_sum(sv);
-                    if (lane == 0 && jj < nn[u]) zmid[kq[u] * kWave + j0[u] + jj] = t;
-                }
-        }
-        __syncthreads();
-        // phase 1c: softmax and the beam's best min(n, Kc) keys, one wave per row
-        for (int i = wv; i < nm; i += NW) {
-            const int k = mid[i], n = n_s[k];
-            const bool on = lane < n;
-            const float z = on ? zmid[k * kWave + lane] : -INFINITY;
-            const int tk = on ? (int)tokq[k * kWave + lane] : 0;
-            const int w = pow2_at_least(n);
-            const float m = wave_max_w(z, w);
-            const float se = wave_sum_w(on ? exp_sm(z - m) : 0.f, w);
-            const float lse = m + logf(se);
-            uint64_t key = on ? make_key(a_s[k] + (z - lse), k, tk) : 0ull;
-            if (n > Kc) key = wave_sort_desc(key);
-            wave_append(lane < min(n, Kc), key, qkeys, &ncand);
-        }
-        __syncthreads();
+                for (int c = 0; c < CH; ++c) sv = w8[u][jj][c].dot_raw(hr[u][c], sv);
+                const float t = wave_sum(sv);
+                if (lane == 0 && jj < nn[u]) zmid[kq[u] * kWave + j0[u] + jj] = t;
+            }
     }
+    __syncthreads();
+    // phase 1c: softmax and the beam's best min(n, Kc) keys, one wave per row
+    // (the reductions only over the lanes the row occupies)
+    for (int i = wv; i < ns; i += NW) {
+        const int k = sml[i], n = n_s[k];
+        const bool on = lane < n;
+        const float z = on ? zmid[k * kWave + lane] : -INFINITY;
+        const int tk = on ? (int)tokq[k * kWave + lane] : 0;
+        const int w = pow2_at_least(n);
+        const float m = wave_max_w(z, w);
+        const float se = wave_sum_w(on ? exp_sm(z - m) : 0.f, w);
+        const float lse = m + logf(se);
+        uint64_t key = on ? make_key(a_s[k] + (z - lse), k, tk) : 0ull;
+        if (n > Kc) key = wave_sort_desc(key);
+        wave_append(lane < min(n, Kc), key, qkeys, &ncand);
+    }
+    __syncthreads();
 
     // phase 2: wide rows and bitmap rows, the whole block per beam
     const int nb = nbig;
@@ -502,6 +421,18 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
         __syncthreads();
         if (wv == 0) {
             const uint64_t v = lane < Kc ? slot[lane] : 0ull;
+            if (v) {
+                // the survivor's token and its position in the row (tok_s is
+                // ascending), kept for the next row at emission
+                const int tkn = 65535 - (int)(v & 0xFFFFu);
+                int lo = 0, hi = n;
+                while (lo < hi) {
+                    const int md = (lo + hi) >> 1;
+                    if ((int)tok_s[md] < tkn) lo = md + 1; else hi = md;
+                }
+                tokq[k * kWave + lane] = (uint16_t)tkn;
+                jmid[k * kWave + lane] = lo;
+            }
             wave_append(v != 0ull, v, qkeys, &ncand);
         }
         __syncthreads();
@@ -511,7 +442,7 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
     block_select_list<NT>(ncand, K, qkeys, best, stage, list, red_i, &bcast);
     __syncthreads();
     for (int i = tid; i < K; i += NT)
-        emit_query(st, q, K, i, best[i], r_s, e0_s, n_s, tokq, out_tok, out_par, out_rows, out_logp, nrows, nacc);
+        emit_query(q, K, Kc, i, best[i], e0_s, n_s, tokq, jmid, out_tok, out_par, out_rows, out_logp, nrows, nacc);
 }
 
 template <typename DT, int NT, int CH>
@@ -519,7 +450,7 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
                                                    const DT* __restrict__ hidden, const DT* __restrict__ W,
                                                    const int32_t* __restrict__ beam_rows,
                                                    const float* __restrict__ acc, const uint64_t* __restrict__ pre,
-                                                   const int32_t* __restrict__ pre_off, int64_t pre_cap,
+                                                   const int32_t* __restrict__ pre_off, int64_t pre_cap, int pre_min,
                                                    int32_t* __restrict__ out_tok,
                                                    int32_t* __restrict__ out_par, int32_t* __restrict__ out_rows,
                                                    float* __restrict__ out_logp) {
@@ -527,13 +458,22 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
     __shared__ uint64_t best[kWave];
     const int q = blockIdx.x;
     step_query_block<DT, NT, CH>(st, q, K, Kc, d, hidden, W, beam_rows + (int64_t)q * K, acc + (int64_t)q * K, pre,
-                                 pre_off, pre_cap, out_tok, out_par, out_rows, out_logp, smem, best, nullptr,
+                                 pre_off, pre_cap, pre_min, out_tok, out_par, out_rows, out_logp, smem, best, nullptr,
                                  nullptr);
 }
 
 // ---- dense step: per-beam expansion and per-query merge --------------------
 
-template <typename DT, bool DENSE, int NT>
+// One workgroup per beam: the row's valid tokens, their scores (gather-dot
+// against the hidden vector, or columns of the full-codebook scores), the
+// log-softmax over them and the beam's best min(K, n) candidate keys.  The
+// keys carry the candidate's place i in the beam's list (low 16 bits 65535 -
+// i; within a beam the list is in (score desc, token asc) order, so the key
+// order across beams is still (score desc, parent asc, token asc)); side[b *
+// Kc + i] holds its next row << 16 | token, so that the merge emits without
+// looking anything up in the index.  CH: hidden width in 512-element chunks
+// kept in registers by the scoring loop (0: any width, one chunk at a time).
+template <typename DT, bool DENSE, int NT, int CH>
 __global__ __launch_bounds__(NT) void k_beam_expand(StepDev st, int K, int Kc, int d,
                                                     const DT* __restrict__ hidden, const DT* __restrict__ W,
                                                     const float* __restrict__ Z, const float* __restrict__ Zp,
@@ -541,7 +481,7 @@ __global__ __launch_bounds__(NT) void k_beam_expand(StepDev st, int K, int Kc, i
                                                     const int32_t* __restrict__ ci_of, int split_ok,
                                                     const int32_t* __restrict__ beam_rows,
                                                     const float* __restrict__ acc, uint64_t* __restrict__ keys_out,
-                                                    int mode) {
+                                                    uint64_t* __restrict__ side, int mode) {
     auto split_of = [&](const int32_t* nl) { return split_ok ? gemm_split(*nl, (int)ldz, d) : 1; };
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ float red_f[red_slots<NT>()];
@@ -585,6 +525,9 @@ __global__ __launch_bounds__(NT) void k_beam_expand(StepDev st, int K, int Kc, i
                 z_s[j] = z;
             }
         }
+    } else if constexpr (CH > 0) {
+        // 16 tokens per wave with all their W_t row chunks in flight
+        block_scores_ch<DT, NT, CH, 128>(h_s, W, d, tok_s, n, z_s);
     } else {
         block_scores<DT, NT>(h_s, W, d, tok_s, n, z_s);
     }
@@ -609,12 +552,25 @@ __global__ __launch_bounds__(NT) void k_beam_expand(StepDev st, int K, int Kc, i
         lse = block_lse<NT>(z_s, n, red_f);
     }
     const int parent = b % K;
-    auto keyf = [&](int j) { return make_key(a + (z_s[j] - lse), parent, (int)tok_s[j]); };
+    // selected by the candidate's position j in the row (the same order as by
+    // token: a row's tokens ascend), then re-keyed by its place in the list
+    __shared__ uint64_t sel_s[kWave];
+    auto keyf = [&](int j) { return make_key(a + (z_s[j] - lse), parent, j); };
     if (n <= Kc) {
-        for (int j = tid; j < Kc; j += NT) out[j] = j < n ? keyf(j) : 0ull;
-        return;
+        for (int j = tid; j < Kc; j += NT) sel_s[j] = j < n ? keyf(j) : 0ull;
+    } else {
+        block_select_top<NT>(n, Kc, keyf, sel_s, stage, list, red_i, &bcast);
     }
-    block_select_top<NT>(n, Kc, keyf, out, stage, list, red_i, &bcast);
+    __syncthreads();
+    for (int i = tid; i < Kc; i += NT) {
+        uint64_t key = sel_s[i];
+        if (key) {
+            const int j = 65535 - (int)(key & 0xFFFFu);
+            side[(int64_t)b * Kc + i] = ((uint64_t)(e0 + (uint32_t)j) << 16) | tok_s[j];
+            key = (key & ~0xFFFFull) | (uint64_t)(65535 - i);
+        }
+        out[i] = key;
+    }
 }
 
 // Dense path on a bitmap step: one wavefront per beam, four beams per
@@ -712,9 +668,13 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
 
 // Dense path, per query: one wavefront per query, four queries per workgroup;
 // lane l owns keys l + 64 i (i < M) of the query's K*Kc.
+// side: NULL when the keys carry tokens (the bitmap expansion; the next row
+// comes from the step table), else the per-beam side information of
+// k_beam_expand (keys carry list places).
 template <int M>
 __global__ __launch_bounds__(256) void k_query_merge_w(StepDev st, int Q, int K, int Kc,
                                                        const uint64_t* __restrict__ keys,
+                                                       const uint64_t* __restrict__ side,
                                                        const int32_t* __restrict__ beam_rows,
                                                        int32_t* __restrict__ out_tok, int32_t* __restrict__ out_par,
                                                        int32_t* __restrict__ out_rows, float* __restrict__ out_logp,
@@ -736,7 +696,23 @@ __global__ __launch_bounds__(256) void k_query_merge_w(StepDev st, int Q, int K,
     }
     const uint64_t best = wave_top<M>(K, [&](int i) { return (uint32_t)(kv[i] >> 32); }, [&](int i) { return kv[i]; },
                                       wl_all[wv]);
-    if (lane < K) {
+    if (lane < K && side) {
+        const int64_t o = (int64_t)q * K + lane;
+        if (!best) {
+            out_tok[o] = -1;
+            out_par[o] = -1;
+            out_rows[o] = -1;
+            out_logp[o] = -INFINITY;
+        } else {
+            const int parent = 1023 - (int)((best >> 16) & 1023u);
+            const int i = 65535 - (int)(best & 0xFFFFu);
+            const uint64_t info = side[((int64_t)q * K + parent) * Kc + i];
+            out_tok[o] = (int32_t)(info & 0xFFFFu);
+            out_par[o] = parent;
+            out_rows[o] = (int32_t)(info >> 16);
+            out_logp[o] = score_from_order_bits((uint32_t)(best >> 32));
+        }
+    } else if (lane < K) {
         if (mode == CB_MODE_UNCONSTRAINED) {
             // no catalog: every live beam sits at row 0 of the next table
             const int64_t o = (int64_t)q * K + lane;
@@ -783,12 +759,17 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // row][v].  Consecutive tiles on one XCD share W columns.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-// Live beams found in the prologue (R > 0; R <= kFoldSlots): every workgroup
-// marks the live slots (each thread a run of consecutive slots), one block
-// scan gives their compact positions, and the workgroup keeps the slots of
-// its own tile; workgroup 0 also writes n_live and ci_of for the expansion
-// kernel.  Otherwise (R == 0) the list comes from k_live_rows.
-constexpr int kFoldSlots = 16 * kGemmThreads;
+// Rows of the product, three ways:
+//  - every slot (all_slots = 1, R slots): tile rows are the beam slots, dead
+//    ones included (their scores are never read); no prologue.  Workgroup 0
+//    writes n_live = -1, which tells the consumers that the scores are one
+//    slice indexed by slot.
+//  - live beams found in the prologue (all_slots = 0, 0 < R <= kFoldSlots): every
+//    workgroup marks the live slots (each thread a run of consecutive slots),
+//    one block scan gives their compact positions, and the workgroup keeps
+//    the slots of its own tile; workgroup 0 also writes n_live and ci_of.
+//  - otherwise (R == 0) the compact list comes from k_live_rows.
+constexpr int kFoldSlots = 4 * kGemmThreads;
 
 __global__ __launch_bounds__(kGemmThreads) void k_gemm_bf16(int V, int d, const int32_t* __restrict__ live,
                                                             int32_t* __restrict__ n_live,
@@ -797,7 +778,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_bf16(int V, int d, const 
                                                             float* __restrict__ Zp, int64_t ldz, StepDev st, int R,
                                                             const int32_t* __restrict__ beam_rows,
                                                             const float* __restrict__ beam_acc,
-                                                            int32_t* __restrict__ ci_of) {
+                                                            int32_t* __restrict__ ci_of, int all_slots) {
     extern __shared__ __align__(16) uint16_t gsm[];
     uint16_t* As = gsm;                     // [2][kBM * kLDP]
     uint16_t* Bs = gsm + 2 * kBM * kLDP;    // [2][kBN * kLDP]
@@ -811,7 +792,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_bf16(int V, int d, const 
     int nl;
     uint32_t onmask = 0;
     int pos0 = 0, run = 0, b0 = 0;
-    if (R > 0) {
+    if (all_slots) {
+        nl = -R;  // one slice over every slot (tiles from R below)
+        if (L == 0 && tid == 0) *n_live = -1;
+    } else if (R > 0) {
         run = (R + NT - 1) / NT;
         b0 = tid * run;
         int c = 0;
@@ -832,6 +816,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_bf16(int V, int d, const 
         nl = *n_live;
     }
     const int split = gemm_split(nl, V, d);
+    if (all_slots) nl = R;
     const int mt = (nl + kBM - 1) / kBM, nt = (V + kBN - 1) / kBN;
     const int N = mt * nt * split;
     if (L >= N) return;  // uniform over the workgroup
@@ -841,7 +826,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_bf16(int V, int d, const 
     const int m0 = (tile % mt) * kBM, n0 = (tile / mt) * kBN;
     const int klen = d / split, kbeg = zs * klen;
 
-    if (R > 0) {
+    if (all_slots) {
+        if (tid < kBM) rows_s[tid] = m0 + tid < R ? m0 + tid : -1;
+    } else if (R > 0) {
         if (tid < kBM) rows_s[tid] = -1;
         __syncthreads();
         int p = pos0;
@@ -1179,7 +1166,7 @@ __global__ __launch_bounds__(NT) void k_decode_tail(const StepDev* __restrict__ 
         int32_t* ot = hist_tok + (int64_t)t * R;
         int32_t* op = hist_par + (int64_t)t * R;
         step_query_block<DT, NT, CH>(st, q, K, Kc, d, h, W + (int64_t)t * V * d, rows_l[cur], acc_l[cur], nullptr,
-                                     nullptr, 0, ot, op, rb[cur ^ 1], ab[cur ^ 1], smem, best, rows_l[cur ^ 1],
+                                     nullptr, 0, 0, ot, op, rb[cur ^ 1], ab[cur ^ 1], smem, best, rows_l[cur ^ 1],
                                      acc_l[cur ^ 1]);
         __syncthreads();
         if (clk && threadIdx.x == 0) clk[((int64_t)q * L + t) * 2 + 1] = wall_clock64();
@@ -1253,15 +1240,16 @@ size_t tail_lds_bytes(int S, int K, int Kc, int d) { return (size_t)query_lds(S,
 
 hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int Kc, int d, int nt, const void* hidden,
                              const void* W, const int32_t* beam_rows, const float* acc, const uint64_t* pre,
-                             const int32_t* pre_off, int64_t pre_cap, int32_t* tok, int32_t* par, int32_t* rows,
-                             float* logp, hipStream_t s) {
+                             const int32_t* pre_off, int64_t pre_cap, int pre_min, int32_t* tok, int32_t* par,
+                             int32_t* rows, float* logp, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
     const int NT = nt == 256 || nt == 512 || nt == 1024 ? nt : query_threads(K);
     const QueryLds lay = query_lds(st.S, K, Kc, d, NT);
     const int CH = (d + kWave * 8 - 1) / (kWave * 8);
 #define CB_QUERY(DT, NTV, CHV)                                                                           \
     CB_LAUNCH((k_step_query<DT, NTV, CHV>), dim3(Q), dim3(NTV), lay.total, s, st, K, Kc, d,     \
-                       (const DT*)hidden, (const DT*)W, beam_rows, acc, pre, pre_off, pre_cap, tok, par, rows, logp)
+                       (const DT*)hidden, (const DT*)W, beam_rows, acc, pre, pre_off, pre_cap, pre_min, tok, par, rows, \
+                       logp)
 #define CB_QUERY_NT(DT, CHV)                              \
     do {                                                  \
         if (NT == 1024) CB_QUERY(DT, 1024, CHV);          \
@@ -1285,7 +1273,9 @@ hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int K
 hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R, int K, int Kc, int d,
                               const void* hidden, const void* W, const float* Z, const float* Zp, int64_t ldz,
                               const int32_t* n_live, const int32_t* ci_of, const int32_t* beam_rows,
-                              const float* acc, uint64_t* keys, int mode, hipStream_t s) {
+                              const float* acc, uint64_t* keys, uint64_t* side, bool* sided, int mode,
+                              hipStream_t s) {
+    *sided = false;
     if (R <= 0) return hipSuccess;
     const int split_ok = dt == CB_BF16 ? 1 : 0;
     if (dense && split_ok && (st.store == CB_STORE_BITMAP || mode == CB_MODE_UNCONSTRAINED) &&
@@ -1304,27 +1294,36 @@ hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R,
         return hipGetLastError();
     }
     const ExpandLds lay = expand_lds(st.S, d, dense, kExpandThreads);
-#define CB_EXPAND(DT, DENSE)                                                                                     \
-    CB_LAUNCH((k_beam_expand<DT, DENSE, kExpandThreads>), dim3(R), dim3(kExpandThreads), lay.total, s, \
-                       st, K, Kc, d, (const DT*)hidden, (const DT*)W, Z, Zp, ldz, n_live, ci_of, split_ok,        \
-                       beam_rows, acc, keys, mode)
+    *sided = true;
+#define CB_EXPAND(DT, DENSE, CHV)                                                                            \
+    CB_LAUNCH((k_beam_expand<DT, DENSE, kExpandThreads, CHV>), dim3(R), dim3(kExpandThreads), lay.total, s, \
+              st, K, Kc, d, (const DT*)hidden, (const DT*)W, Z, Zp, ldz, n_live, ci_of, split_ok, beam_rows, acc, \
+              keys, side, mode)
+#define CB_EXPAND_SPARSE(DT)                                   \
+    do {                                                       \
+        if (d <= 512) CB_EXPAND(DT, false, 1);                 \
+        else if (d <= 1024) CB_EXPAND(DT, false, 2);           \
+        else if (d <= 2048) CB_EXPAND(DT, false, 4);           \
+        else CB_EXPAND(DT, false, 0);                          \
+    } while (0)
     if (dt == CB_BF16) {
-        if (dense) CB_EXPAND(uint16_t, true); else CB_EXPAND(uint16_t, false);
+        if (dense) CB_EXPAND(uint16_t, true, 0); else CB_EXPAND_SPARSE(uint16_t);
     } else {
-        if (dense) CB_EXPAND(float, true); else CB_EXPAND(float, false);
+        if (dense) CB_EXPAND(float, true, 0); else CB_EXPAND_SPARSE(float);
     }
+#undef CB_EXPAND_SPARSE
 #undef CB_EXPAND
     return hipGetLastError();
 }
 
-hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uint64_t* keys,
+hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uint64_t* keys, const uint64_t* side,
                               const int32_t* beam_rows, int32_t* tok, int32_t* par, int32_t* rows, float* logp,
                               int mode, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
     const int M = (K * Kc + kWave - 1) / kWave;
     const dim3 grid((Q + 3) / 4);
 #define CB_MERGE(MV)                                                                                      \
-    CB_LAUNCH((k_query_merge_w<MV>), grid, dim3(256), 0, s, st, Q, K, Kc, keys, beam_rows, tok, par, \
+    CB_LAUNCH((k_query_merge_w<MV>), grid, dim3(256), 0, s, st, Q, K, Kc, keys, side, beam_rows, tok, par, \
                        rows, logp, mode)
     if (M <= 1) CB_MERGE(1);
     else if (M <= 4) CB_MERGE(4);
@@ -1342,18 +1341,22 @@ hipError_t launch_live_rows(const StepDev& st, int R, const int32_t* beam_rows, 
 
 bool gemm_finds_live(cb_dtype dt, int R) { return dt == CB_BF16 && R <= kFoldSlots; }
 
+bool gemm_full_ok(cb_dtype dt) { return dt == CB_BF16; }
+
 hipError_t launch_gemm_scores(cb_dtype dt, int R, int V, int d, const int32_t* live, int32_t* n_live,
                               const void* H, const void* W, float* Z, float* Zp, const StepDev& st,
-                              const int32_t* beam_rows, const float* acc, int32_t* ci_of, hipStream_t s) {
+                              const int32_t* beam_rows, const float* acc, int32_t* ci_of, bool full,
+                              hipStream_t s) {
     if (R <= 0) return hipSuccess;
     if (dt == CB_BF16) {
         static const hipError_t lds_ok = hipFuncSetAttribute(
             (const void*)k_gemm_bf16, hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
         if (lds_ok != hipSuccess) return lds_ok;
-        const int fold = gemm_finds_live(dt, R) ? R : 0;
-        CB_LAUNCH(k_gemm_bf16, dim3(gemm_grid(R, V)), dim3(kGemmThreads), kGemmLds, s, V, d, live, n_live,
-                           (const uint16_t*)H, (const uint16_t*)W, Z, Zp, (int64_t)V, st, fold, beam_rows, acc,
-                           ci_of);
+        const int fold = full || gemm_finds_live(dt, R) ? R : 0;
+        const int grid = full ? ((R + kBM - 1) / kBM) * ((V + kBN - 1) / kBN) : gemm_grid(R, V);
+        CB_LAUNCH(k_gemm_bf16, dim3(grid), dim3(kGemmThreads), kGemmLds, s, V, d, live, n_live,
+                  (const uint16_t*)H, (const uint16_t*)W, Z, Zp, (int64_t)V, st, fold, beam_rows, acc, ci_of,
+                  full ? 1 : 0);
     } else {
         dim3 grid((V + 15) / 16, (R + 15) / 16);
         CB_LAUNCH(k_gemm_f32, grid, dim3(256), 0, s, V, d, live, n_live, (const float*)H, (const float*)W,
@@ -1362,7 +1365,8 @@ hipError_t launch_gemm_scores(cb_dtype dt, int R, int V, int d, const int32_t* l
     return hipGetLastError();
 }
 
-int gemm_blocks(cb_dtype dt, int R, int V) {
+int gemm_blocks(cb_dtype dt, int R, int V, bool full) {
+    if (dt == CB_BF16 && full) return ((R + kBM - 1) / kBM) * ((V + kBN - 1) / kBN);
     return dt == CB_BF16 ? gemm_grid(R, V) : ((V + 15) / 16) * ((R + 15) / 16);
 }
 
@@ -1409,7 +1413,7 @@ hipError_t launch_decode_tail(const StepDev* d_steps, size_t lds, int t0, int L,
                               int32_t* rows0, int32_t* rows1, float* acc0, float* acc1, int32_t* hist_tok,
                               int32_t* hist_par, uint64_t* clk, hipStream_t s) {
     if (Q <= 0 || t0 >= L) return hipSuccess;
-    const int NT = tail_threads(K);
+    // built for 512-thread workgroups only (tail_threads)
     const int CH = (d + kWave * 8 - 1) / (kWave * 8);
     const int R = Q * K;
     const bool vec = hidden_vec_ok(d, P);
@@ -1418,8 +1422,7 @@ hipError_t launch_decode_tail(const StepDev* d_steps, size_t lds, int t0, int L,
                        (const DT*)W, P, s0, s1, (DT*)h, rows0, rows1, acc0, acc1, hist_tok, hist_par, clk)
 #define CB_TAIL_V(DT, NTV, CHV) \
     do { if (vec) CB_TAIL(DT, NTV, CHV, true); else CB_TAIL(DT, NTV, CHV, false); } while (0)
-#define CB_TAIL_NT(DT, CHV) \
-    do { if (NT == 1024) CB_TAIL_V(DT, 1024, CHV); else CB_TAIL_V(DT, 512, CHV); } while (0)
+#define CB_TAIL_NT(DT, CHV) CB_TAIL_V(DT, 512, CHV)
     if (dt == CB_BF16) {
         if (CH <= 1) CB_TAIL_NT(uint16_t, 1);
         else if (CH == 2) CB_TAIL_NT(uint16_t, 2);

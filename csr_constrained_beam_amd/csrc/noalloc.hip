@@ -21,7 +21,7 @@ namespace cb {
 namespace {
 
 // 32 MiB: holds the dense path of 2,048 beams over a 2,048-token codebook
-// (keys 0.5 MiB, scores 16 MiB, k-slice partials 4 MiB).
+// (keys and side information 1 MiB, scores 16 MiB, k-slice partials 4 MiB).
 constexpr size_t kScratchBytes = size_t(32) << 20;
 constexpr int kMaxDevices = 64;
 
@@ -117,12 +117,13 @@ extern "C" cb_status cb_step_noalloc(const cb_index* idx, int32_t t, int32_t Q, 
         set_error("cb_step_noalloc: a row of this step is too wide for the LDS selection (use cb_step with a plan)");
         return CB_ECAPACITY;
     }
-    // workspace: per-beam keys on the dense path and on the wide-hidden sparse
-    // route; full-codebook scores, k-slice partials and the live list on the
-    // dense path; none for the fused per-query sparse step
+    // workspace: per-beam keys and their side information on the dense path
+    // and on the wide-hidden sparse route; full-codebook scores, k-slice
+    // partials and the live list on the dense path; none for the fused
+    // per-query sparse step
     const bool need_keys = p == CB_PATH_DENSE || d > kQueryMaxD;
     const bool need_dense = p == CB_PATH_DENSE;
-    const size_t b_keys = need_keys ? round256(R * Kc * 8) : 0;
+    const size_t b_keys = need_keys ? 2 * round256(R * Kc * 8) : 0;
     const size_t b_z = need_dense ? round256(R * (size_t)idx->V * 4) : 0;
     const size_t b_zp = need_dense && dtype == CB_BF16 ? round256(split_scores_floats(idx->V) * 4) : 0;
     const size_t b_live = need_dense ? 2 * round256(R * 4) + 256 : 0;
@@ -153,6 +154,7 @@ extern "C" cb_status cb_step_noalloc(const cb_index* idx, int32_t t, int32_t Q, 
     unsigned char* cur = base;
     if (b_keys) {
         w.keys = reinterpret_cast<uint64_t*>(cur);
+        w.side = reinterpret_cast<uint64_t*>(cur + b_keys / 2);
         cur += b_keys;
     }
     if (need_dense) {

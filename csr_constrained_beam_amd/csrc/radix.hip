@@ -27,7 +27,7 @@
 // beam's log-sum-exp is combined from its chunks' (max, sum exp) pairs.
 //
 // k_wide_score also serves the per-query (LDS) sparse step: with wide_only it
-// scores just the rows of more than kPreMin tokens (and bitmap rows), spread
+// scores just the rows of more than wide_only tokens (and bitmap rows), spread
 // over many workgroups, and the step kernel then reads their scores instead of
 // computing them one wavefront or one workgroup per row.
 //
@@ -108,8 +108,9 @@ __device__ void slot_offsets(const StepDev& st, int q, int K, const int32_t* __r
             const int64_t b = (int64_t)q * K + k;
             const int32_t r = beam_rows[b];
             if (beam_live(st, r, acc[b])) x = (int)(st.row_ptr[r + 1] - st.row_ptr[r]);
-            // wide_only: only the rows the per-query kernel reads scores for (more than kPreMin tokens)
-            if (wide_only && st.store == CB_STORE_CSR && x <= kPreMin) x = 0;
+            // wide_only > 0: only the rows the per-query kernel reads scores for
+            // (more than wide_only tokens, and every bitmap row)
+            if (wide_only && st.store == CB_STORE_CSR && x <= wide_only) x = 0;
         }
         n[u] = x;
         sc += x;
@@ -208,7 +209,9 @@ __device__ SelView resolve_digits(const WideDev& w, int q, int K, int n_cand, in
 // half (parent, token), and the chunk's (max, sum exp).  Every workgroup
 // derives the slot offsets itself; the query's first one also publishes them
 // and resets the query's selection state for the kernels that follow.
-template <typename DT, bool DENSE>
+// CH: hidden width in 512-element chunks held in registers by the scoring
+// loop (1, 2 or 4: d <= 512 * CH), or 0 for any width (one chunk at a time).
+template <typename DT, bool DENSE, int CH>
 __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int d, const DT* __restrict__ hidden,
                                                           const DT* __restrict__ W, const float* __restrict__ Z,
                                                           const float* __restrict__ Zp, int64_t ldz,
@@ -223,6 +226,7 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
     __shared__ int32_t co_s[kMaxKRadix + 1], ho_s[kMaxKRadix + 1];
     __shared__ int red_i[kWThreads / kWave];
     const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
+    if (w.use_done && w.done[q]) return;  // finished by the pre-pass (uniform over the workgroup)
     slot_offsets<kWThreads>(st, q, K, beam_rows, acc, wide_only, co_s, ho_s, red_i);
     if (g == 0 && wide_only) {
         int32_t* co = w.cand_off + (int64_t)q * (K + 1);
@@ -280,6 +284,10 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
                 }
                 z_s[tid] = z;
             }
+        } else if constexpr (CH > 0) {
+            // every W_t row chunk of 16 tokens per wave in flight at once (the
+            // chunk's 64 tokens in one round trip at d <= 1024 bf16)
+            block_scores_ch<DT, kWThreads, CH, 128>(h_s, W, d, tok_s, cnt, z_s);
         } else {
             block_scores<DT, kWThreads>(h_s, W, d, tok_s, cnt, z_s);
         }
@@ -312,6 +320,7 @@ __global__ __launch_bounds__(kWThreads) void k_wide_keys(int K, const float* __r
     __shared__ __align__(16) uint32_t hs[kRBins];
     __shared__ int32_t co_s[kMaxKRadix + 1], ho_s[kMaxKRadix + 1];
     const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
+    if (w.use_done && w.done[q]) return;
     const int lane = tid & (kWave - 1), wv = tid / kWave;
     constexpr int NWV = kWThreads / kWave;
     const WideSel* sel = reinterpret_cast<const WideSel*>(w.sel) + q;
@@ -368,6 +377,7 @@ __global__ __launch_bounds__(kWThreads) void k_wide_refine(int K, WideDev w, int
     __shared__ int red_i[kWThreads / kWave];
     __shared__ int pick[3];
     const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
+    if (w.use_done && w.done[q]) return;
     const WideSel* sel = reinterpret_cast<const WideSel*>(w.sel) + q;
     if (sel->state != kSelPending) return;  // uniform over the query's workgroups
     const int n = sel->n_cand;
@@ -395,6 +405,7 @@ __global__ __launch_bounds__(kWThreads) void k_wide_collect(int K, WideDev w, in
     __shared__ int pick[3];
     const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
+    if (w.use_done && w.done[q]) return;
     WideSel* sel = reinterpret_cast<WideSel*>(w.sel) + q;
     const int n = sel->n_cand;
     if (n <= K) return;  // every candidate survives (sel->state is rewritten below, so not read here)
@@ -534,6 +545,7 @@ __global__ __launch_bounds__(kSortThreads) void k_wide_sort(int K, WideDev w, in
     __shared__ int pick[3];
     __shared__ int cnt_s;
     const int q = blockIdx.x, tid = threadIdx.x;
+    if (w.use_done && w.done[q]) return;
     const WideSel* sel = reinterpret_cast<const WideSel*>(w.sel) + q;
     const int n_cand = sel->n_cand;
     const int state = sel->state;
@@ -588,6 +600,72 @@ __global__ __launch_bounds__(kSortThreads) void k_wide_sort(int K, WideDev w, in
         sort_and_emit<8>(w, q, K, src, n, ks, out_tok, out_par, out_rows, out_logp);
 }
 
+// Pre-pass, one workgroup of kSortThreads threads per query, one thread per
+// beam slot (K <= kSortThreads).  A row with one valid token has log-softmax
+// exactly 0 whatever its score, so when every live row of the query has one
+// token (CSR) its K candidates are (acc_k, k, token) and no score is needed:
+// if the live slots come first and their log-probs do not increase the
+// outputs are the inputs in place (slot i = beam i); otherwise the K keys are
+// sorted (score desc, parent asc).  The query is then marked done for the
+// radix kernels that follow; any other query is left to them (done = 0, so
+// the array needs no clearing between steps).
+__global__ __launch_bounds__(kSortThreads) void k_wide_small(StepDev st, int K, const int32_t* __restrict__ beam_rows,
+                                                             const float* __restrict__ acc, WideDev w,
+                                                             int32_t* __restrict__ out_tok,
+                                                             int32_t* __restrict__ out_par,
+                                                             int32_t* __restrict__ out_rows,
+                                                             float* __restrict__ out_logp) {
+    __shared__ uint64_t xch[kSortThreads];
+    __shared__ float a_s[kSortThreads];
+    __shared__ uint32_t e0_s[kSortThreads];
+    __shared__ uint16_t t_s[kSortThreads];
+    const int q = blockIdx.x, k = threadIdx.x;
+    const int32_t r = k < K ? beam_rows[(int64_t)q * K + k] : -1;
+    const float a = k < K ? acc[(int64_t)q * K + k] : -INFINITY;
+    const bool live = k < K && beam_live(st, r, a);
+    const uint32_t e0 = live ? st.row_ptr[r] : 0u;
+    const int n = live ? (int)(st.row_ptr[r + 1] - e0) : 0;
+    const int f0 = live && st.tok0 ? (int)st.tok0[r] : 0;  // in flight with row_ptr
+    const bool one = live && st.store == CB_STORE_CSR && n == 1 && st.tok0;
+    a_s[k] = live ? a : -INFINITY;
+    e0_s[k] = e0;
+    t_s[k] = (uint16_t)f0;
+    __syncthreads();
+    // a slot that breaks the in-place order: live after a dead slot, or a
+    // log-prob above the previous slot's
+    const bool viol = live && k > 0 && !(a_s[k - 1] >= a);
+    const int n_other = __syncthreads_count(live && !one);
+    const int n_viol = __syncthreads_count(viol);
+    if (n_other > 0) {
+        if (k == 0) w.done[q] = 0;
+        return;  // uniform: the radix kernels take this query
+    }
+    const int64_t base = (int64_t)q * K;
+    if (n_viol == 0) {
+        if (k < K) {
+            out_tok[base + k] = live ? f0 : -1;
+            out_par[base + k] = live ? k : -1;
+            out_rows[base + k] = live ? (int32_t)e0 : -1;
+            out_logp[base + k] = live ? a + 0.f : -INFINITY;
+        }
+    } else {
+        // one key per slot: score bits, then the complement of the slot (so
+        // that equal scores order by parent ascending); 0 = no candidate
+        uint64_t v[1] = {live ? ((uint64_t)score_order_bits(a + 0.f) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)k)
+                              : 0ull};
+        block_sort_desc<1>(v, xch);
+        if (k < K) {
+            const uint64_t key = v[0];
+            const int p = key ? (int)(0xFFFFFFFFu - (uint32_t)key) : -1;
+            out_tok[base + k] = key ? (int32_t)t_s[p] : -1;
+            out_par[base + k] = key ? p : -1;
+            out_rows[base + k] = key ? (int32_t)e0_s[p] : -1;
+            out_logp[base + k] = key ? score_from_order_bits((uint32_t)(key >> 32)) : -INFINITY;
+        }
+    }
+    if (k == 0) w.done[q] = 1;
+}
+
 }  // namespace
 
 // ---- launchers -----------------------------------------------------------------
@@ -611,15 +689,30 @@ hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, 
     const dim3 grid(Q * G);
     const size_t lds = wide_score_lds_bytes(d, dense);
     const int split_ok = dt == CB_BF16 ? 1 : 0;
-#define CB_WSCORE(DT, DENSE)                                                                                  \
-    CB_LAUNCH((k_wide_score<DT, DENSE>), grid, dim3(kWThreads), lds, s, st, K, d, (const DT*)hidden, \
-                       (const DT*)W, Z, Zp, ldz, n_live, ci_of, split_ok, beam_rows, acc, wide_only, w, G)
+#define CB_WSCORE(DT, DENSE, CHV)                                                                        \
+    CB_LAUNCH((k_wide_score<DT, DENSE, CHV>), grid, dim3(kWThreads), lds, s, st, K, d, (const DT*)hidden, \
+              (const DT*)W, Z, Zp, ldz, n_live, ci_of, split_ok, beam_rows, acc, wide_only, w, G)
+#define CB_WSCORE_CH(DT)                                     \
+    do {                                                     \
+        if (d <= 512) CB_WSCORE(DT, false, 1);               \
+        else if (d <= 1024) CB_WSCORE(DT, false, 2);         \
+        else if (d <= 2048) CB_WSCORE(DT, false, 4);         \
+        else CB_WSCORE(DT, false, 0);                        \
+    } while (0)
     if (dt == CB_BF16) {
-        if (dense) CB_WSCORE(uint16_t, true); else CB_WSCORE(uint16_t, false);
+        if (dense) CB_WSCORE(uint16_t, true, 0); else CB_WSCORE_CH(uint16_t);
     } else {
-        if (dense) CB_WSCORE(float, true); else CB_WSCORE(float, false);
+        if (dense) CB_WSCORE(float, true, 0); else CB_WSCORE_CH(float);
     }
+#undef CB_WSCORE_CH
 #undef CB_WSCORE
+    return hipGetLastError();
+}
+
+hipError_t launch_wide_small(const StepDev& st, int Q, int K, const int32_t* beam_rows, const float* acc,
+                             const WideDev& w, int32_t* tok, int32_t* par, int32_t* rows, float* logp, hipStream_t s) {
+    if (Q <= 0) return hipSuccess;
+    CB_LAUNCH(k_wide_small, dim3(Q), dim3(kSortThreads), 0, s, st, K, beam_rows, acc, w, tok, par, rows, logp);
     return hipGetLastError();
 }
 

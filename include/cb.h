@@ -207,15 +207,39 @@ cb_status cb_get_mode(const cb_plan* plan, cb_mode* mode);
  * the radix-selection workspace (CB_ENOMEM). */
 cb_status cb_set_path(cb_plan* plan, int32_t t, cb_path path);
 
-/* Workgroup size of the per-query sparse step at step t: 256, 512 or 1024
- * threads, or 0 for the default (1024 for K >= 16, else 512); cb_tune
- * measures the default against 256 and keeps the faster.  Every size gives
- * the same bits (each sum is per wavefront or over fixed slots).  Errors:
- * CB_EINVAL (other sizes), CB_ECAPACITY (the step's LDS would not fit). */
-cb_status cb_set_step_threads(cb_plan* plan, int32_t t, int32_t threads);
+/* Per-step forms of the kernels, all with the same results (every sum is per
+ * wavefront or over fixed slots, every selection exact); cb_tune measures the
+ * forms that apply to the step's path and selection and keeps the fastest
+ * (ZeroGR summary, "Why fewer scores are not automatically faster": the
+ * choice is measured in advance), replacing what these calls forced before
+ * it; these calls force one, and 0 restores the default.
+ *   CB_OPT_STEP_THREADS   workgroup size of the per-query sparse step: 256,
+ *                         512 or 1024 (default 1024 for K >= 16, else 512)
+ *   CB_OPT_SPLIT_ROWS     split sparse path: rows of more than this many tokens
+ *                         (1..64; default 16) are scored apart, across the GPU
+ *   CB_OPT_SPARSE_FORM    sparse path: 0 one workgroup per query does the whole
+ *                         step; 1 one workgroup per beam expands its row (scores,
+ *                         log-softmax, its best min(K, n)), then one wavefront
+ *                         per query merges (always 1 when d > 2048)
+ *   CB_OPT_DENSE_ROWS     full-codebook product over the live beams (1) or over
+ *                         every beam slot without a live list (2; bf16 plans);
+ *                         default: the live beams at step 0, every slot after
+ *   CB_OPT_RADIX_PREPASS  radix selection with (2, default) or without (1) the
+ *                         pre-pass that finishes queries whose live rows all
+ *                         hold one token
+ * Errors: CB_EINVAL (unknown option or value), CB_ECAPACITY (the form does not
+ * fit the LDS), CB_EUNSUPPORTED (every-slot product of an f32 plan). */
+typedef enum {
+    CB_OPT_STEP_THREADS = 0,
+    CB_OPT_SPLIT_ROWS = 1,
+    CB_OPT_SPARSE_FORM = 2,
+    CB_OPT_DENSE_ROWS = 3,
+    CB_OPT_RADIX_PREPASS = 4
+} cb_step_option;
+cb_status cb_set_step_option(cb_plan* plan, int32_t t, cb_step_option option, int32_t value);
 
-/* The workgroup size the per-query sparse step of step t uses. */
-cb_status cb_get_step_threads(const cb_plan* plan, int32_t t, int32_t* threads);
+/* The form step t will use for `option` (never 0 except CB_OPT_SPARSE_FORM). */
+cb_status cb_get_step_option(const cb_plan* plan, int32_t t, cb_step_option option, int32_t* value);
 
 /* The path step t will take (never CB_PATH_AUTO). */
 cb_status cb_get_path(const cb_plan* plan, int32_t t, cb_path* path);
@@ -341,7 +365,8 @@ typedef enum {
     CB_KERNEL_RADIX_REFINE = 10,  /* radix selection: second digit */
     CB_KERNEL_RADIX_COLLECT = 11, /* radix selection: survivors */
     CB_KERNEL_RADIX_SORT = 12,    /* radix selection: survivors sorted, outputs and next rows */
-    CB_KERNEL_DECODE_TAIL = 13    /* persistent decode of the trailing sparse steps (step = first one) */
+    CB_KERNEL_DECODE_TAIL = 13,   /* persistent decode of the trailing sparse steps (step = first one) */
+    CB_KERNEL_RADIX_SMALL = 14    /* radix selection: pre-pass finishing the queries whose rows hold one token */
 } cb_kernel;
 
 typedef struct {

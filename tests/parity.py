@@ -149,3 +149,17 @@ def decode_vs_oracle(T, r0, rec, W, L, K, Q):
             bad.append(q)
     return {"queries": Q, "identical": identical, "near_tie_divergences": tie, "unexplained": bad,
             "max_tie_gap": max_gap}
+
+
+def force_beam_form(plan, t):
+    """Put the sparse path of step t in its per-beam form (one workgroup per
+    beam, then the per-query merge); False when the step's widest row does
+    not fit that form's LDS (the step then keeps the per-query kernel)."""
+    import csr_constrained_beam_amd as cb
+    try:
+        plan.set_option(t, "sparse_form", 1)
+        return True
+    except cb.CbError as e:
+        if e.status != -5:  # CB_ECAPACITY
+            raise
+        return False

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from synth import get_config, make_catalog, make_dense
-from tests.parity import compare_step, logp_ok
+from tests.parity import compare_step, force_beam_form, logp_ok
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -122,17 +122,21 @@ def test_fullsize_persistent_decode(name, paths):
 
 
 @pytest.mark.parametrize("name", ["production", "hybrid"])
-@pytest.mark.parametrize("path", ["tuned", "dense", "sparse", "sparse_split"])
+@pytest.mark.parametrize("path", ["tuned", "dense", "sparse", "sparse_split", "sparse_beam"])
 def test_fullsize_teacher_forced(name, path):
     w = big(name)
     cfg, ref, plan, T = w["cfg"], w["ref"], w["plan"], w["T"]
     K = cfg.K
     S = cfg.Q * K
-    saved = [plan.get_path(t) for t in range(cfg.L)]
+    forms = [plan.get_option(t, "sparse_form") for t in range(cfg.L)]
     try:
         for t in range(cfg.L):
-            if path != "tuned":
+            if path == "sparse_beam":
+                plan.set_path(t, "sparse")
+                print("per-beam form:", force_beam_form(plan, t), flush=True)
+            elif path != "tuned":
                 plan.set_path(t, path)
+                plan.set_option(t, "sparse_form", 0)
             print(name, path, "step", t, plan.get_path(t), flush=True)
             h = ref["trace_h"][t]
             hd = torch.from_numpy(h).to(DEV)
@@ -150,4 +154,4 @@ def test_fullsize_teacher_forced(name, path):
     finally:
         for t in range(cfg.L):
             plan.set_path(t, "auto")
-        del saved
+            plan.set_option(t, "sparse_form", forms[t])

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from synth import get_config, make_catalog, make_dense
-from tests.parity import compare_step, logp_ok
+from tests.parity import compare_step, force_beam_form, logp_ok
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -56,7 +56,7 @@ def gpu_step(plan, t, h, Wt, rows, acc):
 
 
 @pytest.mark.parametrize("name", ["tiny", "small"])
-@pytest.mark.parametrize("path", ["sparse", "dense", "auto", "sparse_split"])
+@pytest.mark.parametrize("path", ["sparse", "dense", "auto", "sparse_split", "sparse_split_all", "sparse_beam"])
 @pytest.mark.parametrize("store", ["auto", "csr", "bitmap"])
 def test_step_parity_teacher_forced(name, path, store):
     w = workload(name)
@@ -66,7 +66,14 @@ def test_step_parity_teacher_forced(name, path, store):
     total_exempt = 0
     for t in range(cfg.L):
         print("case", name, path, store, "step", t, flush=True)
-        plan.set_path(t, path)
+        if path == "sparse_split_all":  # every multi-token row scored apart
+            plan.set_path(t, "sparse_split")
+            plan.set_split_rows(t, 1)
+        elif path == "sparse_beam":  # one workgroup per beam, then the per-query merge
+            plan.set_path(t, "sparse")
+            force_beam_form(plan, t)
+        else:
+            plan.set_path(t, path)
         h = ref["trace_h"][t]
         rows = ref["trace_rows_in"][t]
         acc = ref["trace_acc_in"][t]

@@ -131,3 +131,56 @@ def test_workgroup_sizes_agree_on_every_phase(K):
         for g in outs[1:]:
             for k in ("tokens", "parents", "rows", "logp"):
                 assert np.array_equal(g[k], outs[0][k]), "workgroup sizes disagree on " + k
+
+
+def wide_catalog(multi):
+    """64 level-1 tokens with 4 children each (256 rows at step 2), then one
+    child per prefix at levels 3 and 4; with ``multi`` one level-3 prefix gets
+    a second child."""
+    rng = np.random.default_rng(6)
+    items = []
+    for a in range(64):
+        for b in rng.choice(64, size=4, replace=False):
+            items.append((a, int(b), int(rng.integers(64)), int(rng.integers(64))))
+    if multi:
+        a, b, c, x = items[11]
+        items.append((a, b, c, (x + 5) % 64))
+    return np.unique(np.array(items, np.int32), axis=0)
+
+
+@pytest.mark.parametrize("multi", [False, True])
+@pytest.mark.parametrize("order", ["sorted", "permuted", "dead_between"])
+def test_single_token_steps_wide_beam(multi, order):
+    """Beam width 100 (radix selection): the one-token pre-pass finishes the
+    query in place (sorted), by a sort of its keys (permuted, dead slot
+    between live ones), or leaves it to the radix kernels (a two-token row)."""
+    items = wide_catalog(multi)
+    V, L, d, K, Q = 64, 4, 256, 100, 2
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((Q, d)).astype(np.float32)
+    P = (rng.standard_normal((L - 1, V, d)) / np.sqrt(d)).astype(np.float32)
+    Wd = (torch.from_numpy((rng.standard_normal((L, V, d)) / np.sqrt(d)).astype(np.float32))).to(DEV).bfloat16()
+    W = Wd.float().cpu().numpy()
+    T = oracle.Trie(items, V)
+    ref = T.decode(K, q, P, W, bf16=True, trace=True)
+    idx = cb.Index(items, V, device=0)
+    plan = idx.plan(Q, K, d, "bf16")
+    for t in (2, 3):
+        h = ref["trace_h"][t].copy()
+        rows = ref["trace_rows_in"][t].copy()
+        acc = ref["trace_acc_in"][t].copy()
+        if order != "sorted":
+            for qq in range(Q):
+                sl = slice(qq * K, (qq + 1) * K)
+                perm = rng.permutation(K) if order == "permuted" else np.arange(K)
+                h[sl], rows[sl], acc[sl] = h[sl][perm], rows[sl][perm], acc[sl][perm]
+                if order == "dead_between":
+                    rows[qq * K + 3], acc[qq * K + 3] = -1, -np.inf
+        print("case wide beam multi", multi, order, "step", t, plan.get_select(t), flush=True)
+        assert plan.get_select(t) == "radix"
+        o = T.step(t, K, h, W[t], rows, acc, candidates=True)
+        plan.set_path(t, "sparse")
+        hd, rd, ad = _device_inputs(h, rows, acc, "bf16")
+        g = gpu_step(plan, t, hd, Wd[t], rd, ad)
+        ex, gap, fails = compare_step(o, g, K, "bf16")
+        assert not fails, "\n".join(fails[:10])

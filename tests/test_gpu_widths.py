@@ -4,7 +4,8 @@ per-query kernel (512 threads for K < 16, 1024 otherwise) and on the dense
 path (the full-codebook product, then the expansion and merge).  Widths above
 2048 (beyond what the fused per-query kernel keeps in registers) take the
 sparse steps as a per-beam expansion + per-query merge: d = 4096 is checked
-on that route, on the dense path and on the radix selection.
+on that route, on the dense path and on the radix selection; the same form,
+forced at every width, is checked as "sparse_beam".
 
 The catalog is built so that the rows of its steps cover every scoring phase
 of the per-query kernel: rows of one token (not scored: log-softmax 0), of
@@ -18,7 +19,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.parity import compare_step
+from tests.parity import compare_step, force_beam_form
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -56,7 +57,7 @@ def test_catalog_covers_every_phase():
 @pytest.mark.parametrize("dtype,d", [("f32", 1024), ("f32", 2048), ("bf16", 1536), ("bf16", 2048),
                                      ("f32", 4096), ("bf16", 4096)])
 @pytest.mark.parametrize("K", [8, 32])
-@pytest.mark.parametrize("path", ["sparse", "dense"])
+@pytest.mark.parametrize("path", ["sparse", "dense", "sparse_beam"])
 def test_step_hidden_widths(dtype, d, K, path):
     _run_widths(dtype, d, K, path, "lds")
 
@@ -66,7 +67,16 @@ def test_step_wide_hidden_radix(dtype):
     _run_widths(dtype, 4096, 32, "sparse", "radix")
 
 
-def _run_widths(dtype, d, K, path, select):
+@pytest.mark.parametrize("dtype,d", [("f32", 1024), ("bf16", 2048)])
+@pytest.mark.parametrize("K", [8, 32])
+@pytest.mark.parametrize("split_rows", [1, 16])
+def test_step_split_scoring(dtype, d, K, split_rows):
+    """Rows above split_rows tokens scored apart across many workgroups, the
+    rest by the per-query kernel, on rows of every scoring phase."""
+    _run_widths(dtype, d, K, "sparse_split", "lds", split_rows=split_rows)
+
+
+def _run_widths(dtype, d, K, path, select, split_rows=0):
     items, V = catalog(11)
     L, Q = 3, 6
     rng = np.random.default_rng(5)
@@ -83,8 +93,12 @@ def _run_widths(dtype, d, K, path, select):
     idx = cb.Index(items, V, device=0)
     plan = idx.plan(Q, K, d, dtype)
     for t in range(L):
-        plan.set_path(t, path)
+        plan.set_path(t, "sparse" if path == "sparse_beam" else path)
         plan.set_select(t, select)
+        if path == "sparse_beam":  # one workgroup per beam, then the per-query merge
+            force_beam_form(plan, t)
+        if split_rows:
+            plan.set_split_rows(t, split_rows)
     for t in range(L):
         print("case", dtype, d, "K", K, path, "step", t, flush=True)
         h = ref["trace_h"][t]

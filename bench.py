@@ -136,13 +136,15 @@ def run_sweep(args):
         rows.append(dict(point, workload=r["config"]["workload"], paths=r["config"]["paths"],
                          ms_per_pass=r["ms_per_step"], us_per_decode_step=r["us_per_decode_step"],
                          expansions_per_pass=r["expansions_per_pass"], expansions_per_s=r["value"],
-                         decode_ms=r["decode_ms_with_model_standin"],
+                         decode_ms=r["decode_ms_as_planned"],
+                         decode_ms_persistent=r["decode_ms_with_model_standin"],
                          decode_ms_step_by_step=r["decode_ms_step_by_step"],
                          index_bytes=r["index"]["bytes"], index_build_s=r["index"]["build_s"],
                          n_items=r["index"]["n_items"],
                          step_us=[round(x["kernel_us"]["mean"], 2) for x in r["per_step"]],
                          max_fanout=[x["max_fanout"] for x in r["per_step"]],
                          step_paths=[x["path"] for x in r["per_step"]],
+                         sparse_forms=[x["sparse_form"] for x in r["per_step"]],
                          dominant=r["roofline"]["kernel"], dominant_frac=r["roofline"]["frac"]))
         x = rows[-1]
         log("  %s: %.4f ms/pass, %.3g expansions/s, decode %.4f ms, index %.1f MB" % (
@@ -246,8 +248,19 @@ def main():
     tail = [r["step"] for r in tail_recs]
     phases = plan.profile_phases()
     plan.set_decode_fusion("auto")
-    log("decode: %.4f ms step by step, %.4f ms with the persistent tail (from step %s)"
-        % (decode_ms_steps, decode_ms, tail[0] if tail else "-"))
+    decode_ms_auto, _ = time_decodes("auto")
+    log("decode: %.4f ms step by step, %.4f ms with the persistent tail (from step %s), %.4f ms as the plan "
+        "decides" % (decode_ms_steps, decode_ms, tail[0] if tail else "-", decode_ms_auto))
+    # wire-format records of the decode's results (one launch after the decode)
+    wire_out, _ = cb.wire_results(dec_a["seqs"], dec_a["logp"], cfg.K, 0.6)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(20):
+        cb.wire_results(dec_a["seqs"], dec_a["logp"], cfg.K, 0.6, out=wire_out)
+    ev1.record()
+    torch.cuda.synchronize()
+    wire_us = ev0.elapsed_time(ev1) * 1000 / 20
+    log("wire-format records: %.2f us per call (%d bytes per query)" % (wire_us, wire_out.shape[1]))
     for ph in phases:
         log("  persistent step %d: selection %.2f us, hidden update %.2f us" % (ph["step"], ph["select_us"],
                                                                              ph["update_us"]))
@@ -478,6 +491,8 @@ def main():
         "expansions_per_pass": expansions,
         "decode_ms_with_model_standin": decode_ms,
         "decode_ms_step_by_step": decode_ms_steps,
+        "decode_ms_as_planned": decode_ms_auto,
+        "wire_records_us": wire_us,
         "decode_persistent_chosen_by_tune": plan.get_decode_fusion() if tune is not None else None,
         "decode_persistent_from_step": tail[0] if tail else None,
         "decode_persistent_us": tail_recs[0]["us"] if tail_recs else None,

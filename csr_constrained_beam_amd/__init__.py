@@ -6,6 +6,6 @@ runs in hand-written HIP kernels for gfx950 behind the C ABI of
 """
 
 from ._lib import CbError, LIB_PATH
-from .api import Index, Plan, floor_probe
+from .api import Index, Plan, floor_probe, wire_bytes, wire_results
 
-__all__ = ["Index", "Plan", "floor_probe", "CbError", "LIB_PATH"]
+__all__ = ["Index", "Plan", "floor_probe", "wire_bytes", "wire_results", "CbError", "LIB_PATH"]

@@ -76,6 +76,8 @@ SIGNATURES = {
     "cb_index_save": (ctypes.c_int, [_P, ctypes.c_char_p]),
     "cb_index_load": (ctypes.c_int, [ctypes.c_char_p, _I32, _P]),
     "cb_floor_probe": (ctypes.c_int, [_I32, _I32, _I32, _P, _P]),
+    "cb_wire_bytes": (ctypes.c_int, [_I32, _I32, _P]),
+    "cb_wire_results": (ctypes.c_int, [_I32, _I32, _I32, _P, _P, ctypes.c_double, _P, ctypes.c_int64, _P, _P]),
     "cb_plan_destroy": (None, [_P]),
     "cb_last_error": (ctypes.c_char_p, []),
 }

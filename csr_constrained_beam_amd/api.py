@@ -352,3 +352,42 @@ def floor_probe(blocks, threads, n, timed=True):
     us = (ctypes.c_float * 2)()
     C.check("cb_floor_probe", lib.cb_floor_probe(int(blocks), int(threads), int(n), us, stream))
     return float(us[0]), float(us[1])
+
+
+def wire_bytes(K, L):
+    """Smallest record stride of the wire format (cb_wire_bytes)."""
+    v = ctypes.c_int64()
+    C.check("cb_wire_bytes", C.lib().cb_wire_bytes(int(K), int(L), ctypes.byref(v)))
+    return v.value
+
+
+def wire_results(seqs, logp, K, alpha=0.0, out=None, stride=None):
+    """Wire-format records of a decode's results (cb_wire_results).
+
+    seqs: device int32 [Q*K][L] and logp: device float32 [Q*K] from
+    Plan.decode.  Returns (out, nbytes): out uint8 [Q][stride] on the same
+    device, query q's record in out[q, :nbytes[q]] (uint64 n_o, float64
+    logp_norm[n_o], uint64 sent_offset[n_o], uint32 tokens[n_o*L]; live beams
+    in ascending order of score)."""
+    torch = _torch()
+    if seqs.dim() != 2 or seqs.dtype != torch.int32 or not seqs.is_contiguous():
+        raise ValueError("seqs must be a contiguous int32 [Q*K][L] tensor")
+    R, L = seqs.shape
+    if R % K:
+        raise ValueError("seqs rows must be a multiple of K")
+    Q = R // K
+    if logp.dtype != torch.float32 or logp.numel() != R or not logp.is_contiguous() or logp.device != seqs.device:
+        raise ValueError("logp must be a contiguous float32 [Q*K] tensor on the device of seqs")
+    if stride is None:
+        stride = wire_bytes(K, L)
+    if out is None:
+        out = torch.empty((Q, stride), dtype=torch.uint8, device=seqs.device)
+    if out.dtype != torch.uint8 or out.numel() < Q * stride or not out.is_contiguous() or out.device != seqs.device:
+        raise ValueError("out must be a contiguous uint8 tensor of Q*stride bytes on the device of seqs")
+    nbytes = torch.empty(Q, dtype=torch.int64, device=seqs.device)
+    with torch.cuda.device(seqs.device):
+        stream = ctypes.c_void_p(torch.cuda.current_stream(seqs.device).cuda_stream)
+        C.check("cb_wire_results", C.lib().cb_wire_results(
+            Q, int(K), int(L), ctypes.c_void_p(seqs.data_ptr()), ctypes.c_void_p(logp.data_ptr()), float(alpha),
+            ctypes.c_void_p(out.data_ptr()), int(stride), ctypes.c_void_p(nbytes.data_ptr()), stream))
+    return out, nbytes

@@ -1281,6 +1281,51 @@ cb_status cb_profile_phases(const cb_plan* p, cb_phase_time* out, int32_t cap, i
     return CB_OK;
 }
 
+cb_status cb_wire_bytes(int32_t K, int32_t L, int64_t* bytes) {
+    clear_error();
+    if (!bytes || K < 1 || L < 1) {
+        set_error("cb_wire_bytes: need K >= 1, L >= 1 and an output");
+        return CB_EINVAL;
+    }
+    *bytes = (8 + 16 * (int64_t)K + 4 * (int64_t)K * L + 7) & ~int64_t(7);
+    return CB_OK;
+}
+
+cb_status cb_wire_results(int32_t Q, int32_t K, int32_t L, const int32_t* seqs, const float* logp, double alpha,
+                          void* out, int64_t stride, int64_t* out_bytes, void* stream) {
+    clear_error();
+    if (Q < 0 || K < 1 || K > kMaxKRadix || L < 1 || !std::isfinite(alpha)) {
+        set_error("cb_wire_results: need Q >= 0, 1 <= K <= 1024, L >= 1 and a finite alpha");
+        return CB_EINVAL;
+    }
+    const int64_t need = 8 + 16 * (int64_t)K + 4 * (int64_t)K * L;
+    if (stride < need || stride % 8) {
+        set_error("cb_wire_results: stride must be a multiple of 8 and at least " + std::to_string(need));
+        return CB_EINVAL;
+    }
+    if (Q == 0) return CB_OK;
+    if (!seqs || !logp || !out || !aligned4(seqs) || !aligned4(logp) ||
+        (reinterpret_cast<uintptr_t>(out) & 7) || (out_bytes && (reinterpret_cast<uintptr_t>(out_bytes) & 7))) {
+        set_error("cb_wire_results: seqs / logp must be 4-byte aligned, out / out_bytes 8-byte aligned, none NULL "
+                  "(out_bytes may be NULL)");
+        return CB_EINVAL;
+    }
+    const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), o1 = o0 + (uintptr_t)(stride * Q);
+    auto overlaps = [&](const void* p, size_t n) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+        return a < o1 && o0 < a + n;
+    };
+    const size_t R = (size_t)Q * K;
+    if (overlaps(seqs, R * L * 4) || overlaps(logp, R * 4) || (out_bytes && overlaps(out_bytes, (size_t)Q * 8))) {
+        set_error("cb_wire_results: out overlaps seqs, logp or out_bytes");
+        return CB_EINVAL;
+    }
+    const double norm = std::pow(6.0 / (5.0 + (double)L), alpha);
+    const hipError_t e = launch_wire(Q, K, L, seqs, logp, norm, out, stride, out_bytes, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail("cb_wire_results", e);
+    return CB_OK;
+}
+
 cb_status cb_floor_probe(int32_t blocks, int32_t threads, int32_t n, float* us, void* stream) {
     clear_error();
     if (blocks < 1 || blocks > (1 << 20) || threads < 64 || threads > 1024 || threads % 64 || n < 1 || n > 4096) {

@@ -232,6 +232,9 @@ hipError_t launch_hidden_update(int R, int K, int d, cb_dtype dt, const float* s
 hipError_t launch_empty(int blocks, int threads, hipStream_t s);
 hipError_t launch_backtrace(int R, int K, int L, const int32_t* hist_tok, const int32_t* hist_par,
                             int32_t* seqs, hipStream_t s);
+// Wire-format results of Q queries (one workgroup each) at out + q * stride.
+hipError_t launch_wire(int Q, int K, int L, const int32_t* seqs, const float* logp, double norm, void* out,
+                       int64_t stride, int64_t* nbytes, hipStream_t s);
 // Steps t0..L-1 of a decode (sparse, LDS selection) with the hidden updates
 // in between, one persistent workgroup per query.  d_steps: device array [L];
 // clk: NULL, or [Q][L][2] device wall-clock ticks (step start, outputs written).

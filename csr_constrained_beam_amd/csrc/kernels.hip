@@ -1212,6 +1212,58 @@ __global__ void k_backtrace(int R, int K, int L, const int32_t* __restrict__ his
         for (int t = 0; t < L; ++t) seqs[(int64_t)b * L + t] = -1;
 }
 
+// Wire-format results, one workgroup per query (FlashTrie App. D.3, "Output
+// serialization"): the live beams (finite log-prob) of the query's best-first
+// slots written in ascending order of score, the beam of live rank r into wire
+// slot n_o - 1 - r; the end offset of each sequence is the running sum of the
+// lengths in wire order, from a block scan over the slots (every live sequence
+// has L tokens); log-probs in float64 times the length normalisation `norm`
+// (FlashTrie App. E, eq. 2).  Layout at out + q * stride: uint64 n_o, float64
+// logp_norm[n_o], uint64 sent_offset[n_o], uint32 tokens[n_o * L].  Each
+// thread owns `run` consecutive slots (K <= 1024, run <= 4 at 256 threads).
+template <int NT>
+__global__ __launch_bounds__(NT) void k_wire(int K, int L, const int32_t* __restrict__ seqs,
+                                             const float* __restrict__ logp, double norm,
+                                             unsigned char* __restrict__ out, int64_t stride,
+                                             int64_t* __restrict__ nbytes) {
+    __shared__ int red_i[NT / kWave];
+    const int q = blockIdx.x, tid = threadIdx.x;
+    const int run = (K + NT - 1) / NT;
+    const int b0 = tid * run;
+    const float* lq = logp + (int64_t)q * K;
+    uint32_t on = 0;
+    int c = 0;
+    for (int j = 0; j < run; ++j) {
+        const int i = b0 + j;
+        const bool live = i < K && lq[i] > -INFINITY;
+        on |= (uint32_t)live << j;
+        c += live;
+    }
+    int n_o;
+    int r = block_exclusive_scan<NT>(c, red_i, &n_o);
+    unsigned char* o = out + (int64_t)q * stride;
+    double* lp = reinterpret_cast<double*>(o + 8);
+    uint64_t* off = reinterpret_cast<uint64_t*>(o + 8 + 8 * (int64_t)n_o);
+    uint32_t* tok = reinterpret_cast<uint32_t*>(o + 8 + 16 * (int64_t)n_o);
+    const int64_t total = (int64_t)n_o * L;
+    for (int j = 0; j < run; ++j) {
+        if (!(on >> j & 1u)) continue;
+        const int i = b0 + j;
+        const int w = n_o - 1 - r;
+        // wire slots 0..w hold the live ranks r..n_o-1
+        const int64_t end = total - (int64_t)r * L;
+        lp[w] = (double)lq[i] * norm;
+        off[w] = (uint64_t)end;
+        const int32_t* sq = seqs + ((int64_t)q * K + i) * L;
+        for (int t = 0; t < L; ++t) tok[end - L + t] = (uint32_t)sq[t];
+        ++r;
+    }
+    if (tid == 0) {
+        *reinterpret_cast<uint64_t*>(o) = (uint64_t)n_o;
+        if (nbytes) nbytes[q] = 8 + 16 * (int64_t)n_o + 4 * total;
+    }
+}
+
 }  // namespace
 
 // ---- launchers -----------------------------------------------------------------
@@ -1447,6 +1499,13 @@ hipError_t launch_backtrace(int R, int K, int L, const int32_t* hist_tok, const 
                             hipStream_t s) {
     if (R <= 0) return hipSuccess;
     CB_LAUNCH(k_backtrace, dim3((R + 255) / 256), dim3(256), 0, s, R, K, L, hist_tok, hist_par, seqs);
+    return hipGetLastError();
+}
+
+hipError_t launch_wire(int Q, int K, int L, const int32_t* seqs, const float* logp, double norm, void* out,
+                       int64_t stride, int64_t* nbytes, hipStream_t s) {
+    if (Q <= 0) return hipSuccess;
+    CB_LAUNCH((k_wire<256>), dim3(Q), dim3(256), 0, s, K, L, seqs, logp, norm, (unsigned char*)out, stride, nbytes);
     return hipGetLastError();
 }
 

@@ -311,6 +311,37 @@ cb_status cb_decode(cb_plan* plan, int32_t Q, const float* q, const float* P, co
                     int32_t* out_seqs, float* out_logp, int32_t* out_rows,
                     void* trace_hidden, int32_t* trace_rows, float* trace_acc, void* stream);
 
+/* The smallest record stride of the wire format below: 8 + 16 K + 4 K L
+ * bytes rounded up to a multiple of 8, written to *bytes.
+ * Errors: CB_EINVAL (NULL, K < 1, L < 1). */
+cb_status cb_wire_bytes(int32_t K, int32_t L, int64_t* bytes);
+
+/* Wire-format results (FlashTrie, arXiv HTML, App. D.3 "Output
+ * serialization"; length normalisation from its App. E, eq. 2, after Wu et
+ * al.): the decode's best-first slots of every query written as the page's
+ * on-wire record, in ascending order of score.  Query q's record starts at
+ * out + q * stride:
+ *   uint64  n_o                       live beams (finite log-prob)
+ *   float64 logp_norm[n_o]            logp * (6 / (5 + L))^alpha
+ *   uint64  sent_offset[n_o]          end offsets into tokens
+ *   uint32  tokens[n_o * L]           sequence i = tokens[sent_offset[i-1],
+ *                                     sent_offset[i]) with sent_offset[-1] = 0
+ * The live beam of best-first rank r goes to wire slot n_o - 1 - r (the worst
+ * live beam first); dead slots are left out.  Little-endian, as the device
+ * stores it.
+ *   seqs      device int32 [Q*K][L] (cb_decode's out_seqs)
+ *   logp      device float [Q*K] (cb_decode's out_logp)
+ *   alpha     length-normalisation strength (0: logp unchanged)
+ *   out       device, 8-byte aligned, [Q][stride] bytes
+ *   stride    >= cb_wire_bytes(K, L), a multiple of 8
+ *   out_bytes optional device int64 [Q]: bytes of each record
+ * All pointers on the current device; enqueued on `stream`; nothing is
+ * allocated.  Errors: CB_EINVAL (Q < 0, K outside [1, 1024], L < 1, alpha
+ * not finite, NULL or misaligned pointers, stride too small, out overlapping
+ * seqs or logp), CB_EHIP. */
+cb_status cb_wire_results(int32_t Q, int32_t K, int32_t L, const int32_t* seqs, const float* logp, double alpha,
+                          void* out, int64_t stride, int64_t* out_bytes, void* stream);
+
 /* Persistent decode (FlashTrie, arXiv HTML, sections 2.2 and 4.2: every step
  * of a query in one launch, paying the launch cost once).  When enabled and
  * cb_decode is called without trace buffers, the trailing run of steps whose

@@ -36,6 +36,11 @@ Parity status of each function (what pins it; see ``tests/test_oracle_pins.py``)
   form, and equality with the trie oracle (tables, step candidates, decode
   traces) on the tiny, small and hybrid generators
   (``tests/test_oracle_range.py``).
+* ``wire_records`` / ``wire_parse`` (``wire.py``): the on-wire record of a
+  decode's results (FlashTrie App. D.3, "Output serialization").  Pinned by
+  byte records written out by hand from the page's layout
+  (``tests/golden/wire_records.txt``) and parse-back invariants
+  (``tests/test_oracle_wire.py``).
 """
 
 import ctypes
@@ -276,3 +281,6 @@ class SortedRange(Trie):
 
     def prefix_of_row(self, depth, row):
         raise NotImplementedError
+
+
+from .wire import length_norm, parse as wire_parse, record as wire_record, records as wire_records  # noqa: E402

@@ -152,6 +152,21 @@ def test_null_arguments_rejected(cb):
     L.cb_plan_destroy(None)
 
 
+def test_wire_arguments_checked_on_the_host(cb):
+    """The wire-format call checks its sizes before touching the device."""
+    L = cb._lib.lib()
+    v = ctypes.c_int64()
+    assert L.cb_wire_bytes(3, 2, ctypes.byref(v)) == 0 and v.value == 80  # 8 + 16*3 + 4*3*2
+    assert L.cb_wire_bytes(1, 7, ctypes.byref(v)) == 0 and v.value == 56  # 52 rounded up to 8
+    assert cb.wire_bytes(1024, 8) == 8 + 16 * 1024 + 4 * 1024 * 8
+    assert L.cb_wire_bytes(0, 2, ctypes.byref(v)) == -1
+    assert L.cb_wire_results(0, 4, 3, None, None, 0.0, None, 8 + 64 + 48, None, None) == 0  # no queries
+    assert L.cb_wire_results(1, 1025, 3, None, None, 0.0, None, 1 << 20, None, None) == -1  # K above 1024
+    assert L.cb_wire_results(1, 4, 3, None, None, 0.0, None, 64, None, None) == -1  # stride too small
+    assert L.cb_wire_results(1, 4, 3, None, None, float("inf"), None, 128, None, None) == -1
+    assert L.cb_wire_results(1, 4, 3, None, None, 0.0, None, 128, None, None) == -1  # NULL arrays
+
+
 @pytest.mark.parametrize("store", ["auto", "csr", "bitmap"])
 def test_chunked_build_equals_oracle_at_chunk_boundaries(cb, store):
     """A catalog of 200k items is built in 48 chunks of consecutive sorted

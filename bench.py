@@ -221,7 +221,10 @@ def main():
             plan.set_path(t, args.path)
     paths = [plan.get_path(t) for t in range(cfg.L)]
     forms = [plan.get_option(t, "sparse_form") for t in range(cfg.L)]
-    log("paths per step:", paths, "sparse form per step (1: per beam):", forms)
+    qsplits = [plan.get_option(t, "query_split") for t in range(cfg.L)]
+    nthreads = [plan.get_option(t, "step_threads") for t in range(cfg.L)]
+    log("paths per step:", paths, "sparse form per step (1: per beam):", forms, "workgroups per query:", qsplits,
+        "threads:", nthreads)
 
     # free-running decode: records every step's inputs; also times the full decode
     rec = plan.decode(q, P, W, trace=True)
@@ -299,7 +302,8 @@ def main():
         state_bytes = R * 8 + R * Kc * 8
         w_bytes = live_scored * d * es + len(toks_scored) * d * es  # hidden vectors and distinct W_t rows
         steps.append({
-            "t": t, "path": paths[t], "sparse_form": forms[t], "storage": info[t]["storage"], "live_beams": int(len(live)),
+            "t": t, "path": paths[t], "sparse_form": forms[t], "query_split": qsplits[t], "step_threads": nthreads[t],
+            "storage": info[t]["storage"], "live_beams": int(len(live)),
             "expansions": n_exp, "max_fanout": S, "mean_fanout": float(fan.mean()) if len(fan) else 0.0,
             "valid_fraction": n_exp / max(1, len(live) * V), "distinct_tokens": len(toks),
             "bytes": {

@@ -15,7 +15,8 @@ CB_F32, CB_BF16 = 0, 1
 CB_PATH_AUTO, CB_PATH_DENSE, CB_PATH_SPARSE, CB_PATH_SPARSE_SPLIT = 0, 1, 2, 3
 CB_STORE_AUTO, CB_STORE_CSR, CB_STORE_BITMAP = 0, 1, 2
 CB_SELECT_AUTO, CB_SELECT_LDS, CB_SELECT_RADIX = 0, 1, 2
-STEP_OPTIONS = {"step_threads": 0, "split_rows": 1, "sparse_form": 2, "dense_rows": 3, "radix_prepass": 4}
+STEP_OPTIONS = {"step_threads": 0, "split_rows": 1, "sparse_form": 2, "dense_rows": 3, "radix_prepass": 4,
+                "query_split": 5}
 
 STATUS_NAMES = {0: "CB_OK", -1: "CB_EINVAL", -2: "CB_ENOMEM", -3: "CB_EHIP", -4: "CB_EUNSUPPORTED",
                 -5: "CB_ECAPACITY"}

@@ -311,9 +311,11 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const vo
             if (e != hipSuccess) return hip_fail("cb_step: wide-row scores", e);
         }
         const int nt = query_threads_ok(opt(p->query_nt, t)) ? opt(p->query_nt, t) : query_threads(p->K);
-        ProfMark m(p, s, t, CB_KERNEL_STEP_QUERY, nt, Q);
+        const int G = p->qz && p->qcnt && opt(p->query_split, t) > 1 ? opt(p->query_split, t) : 1;
+        ProfMark m(p, s, t, CB_KERNEL_STEP_QUERY, nt, Q * G);
         e = launch_step_query(sd, p->dtype, Q, p->K, Kc, p->d, nt, hidden, Wt, rows, acc, split ? w.cand : nullptr,
-                              split ? w.cand_off : nullptr, split ? w.cap : 0, pre_min, ot, op, orow, ol, s);
+                              split ? w.cand_off : nullptr, split ? w.cap : 0, pre_min, ot, op, orow, ol, G, p->qz,
+                              p->qcnt, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: sparse step", e);
         return CB_OK;
@@ -638,6 +640,7 @@ cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_
     p->radix_pre.assign((size_t)idx->L, 0);
     p->split_min.assign((size_t)idx->L, 0);
     p->sparse_form.assign((size_t)idx->L, 0);
+    p->query_split.assign((size_t)idx->L, 0);
     p->tune_dense_us.assign((size_t)idx->L, -1.f);
     p->tune_sparse_us.assign((size_t)idx->L, -1.f);
     p->select.assign((size_t)idx->L, CB_SELECT_AUTO);
@@ -645,6 +648,17 @@ cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_
     const size_t R = (size_t)Q_max * K;
     cb_status st = dev_alloc(&p->keys, R * Kc, "candidate keys");
     if (st == CB_OK) st = dev_alloc(&p->side, R * Kc, "candidate side information");
+    if (st == CB_OK) {
+        int S_max = 1;
+        for (int t = 0; t < idx->L; ++t) S_max = std::max(S_max, idx->steps[(size_t)t].S);
+        st = dev_alloc(&p->qz, (size_t)Q_max * (size_t)query_scores_floats(K, S_max), "per-query score hand-off");
+    }
+    if (st == CB_OK) st = dev_alloc(&p->qcnt, (size_t)Q_max, "per-query arrival counts");
+    if (st == CB_OK && hipMemset(p->qcnt, 0, (size_t)Q_max * 4) != hipSuccess) {
+        (void)hipGetLastError();
+        set_error("cb_plan_create: clearing the arrival counts failed");
+        st = CB_EHIP;
+    }
     if (st == CB_OK) st = dev_alloc(&p->Z, R * (size_t)idx->V, "full-codebook scores");
     if (st == CB_OK && dtype == CB_BF16) st = dev_alloc(&p->Zp, split_scores_floats(idx->V), "partial scores");
     if (st == CB_OK) st = dev_alloc(&p->live, R, "live beams");
@@ -821,6 +835,10 @@ cb_status cb_set_step_option(cb_plan* p, int32_t t, cb_step_option o, int32_t va
             if (value < 0 || value > 2) break;
             p->radix_pre[(size_t)t] = value;
             return CB_OK;
+        case CB_OPT_QUERY_SPLIT:
+            if (value != 0 && value != 1 && value != 2 && value != 4) break;
+            p->query_split[(size_t)t] = value;
+            return CB_OK;
     }
     set_error("cb_set_step_option: unknown option or value out of range");
     return CB_EINVAL;
@@ -842,6 +860,7 @@ cb_status cb_get_step_option(const cb_plan* p, int32_t t, cb_step_option o, int3
         case CB_OPT_SPARSE_FORM: *value = (p->d > kQueryMaxD || p->sparse_form[(size_t)t] == 1) ? 1 : 0; return CB_OK;
         case CB_OPT_DENSE_ROWS: *value = gemm_full(p, t) ? 2 : 1; return CB_OK;
         case CB_OPT_RADIX_PREPASS: *value = p->radix_pre[(size_t)t] == 1 ? 1 : 2; return CB_OK;
+        case CB_OPT_QUERY_SPLIT: *value = p->query_split[(size_t)t] > 1 ? p->query_split[(size_t)t] : 1; return CB_OK;
     }
     set_error("cb_get_step_option: unknown option");
     return CB_EINVAL;
@@ -907,13 +926,15 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
         if ((e = hipEventCreate(&ev0)) != hipSuccess || (e = hipEventCreate(&ev1)) != hipSuccess)
             return hip_fail("cb_tune: events", e);
     }
-    // persistent tail: the trailing steps on the fused sparse step with LDS
-    // selection run in one launch (untraced, untuned decodes only)
+    // persistent tail: the trailing steps on the fused per-query sparse step
+    // with LDS selection run in one launch (untraced, untuned decodes only);
+    // a step in the per-beam form ends the run, since the tail runs the
+    // per-query form and must give the same bits as the step-by-step decode
     int t_fuse = L;
     const bool fuse = p->fuse_mode == 1 || (p->fuse_mode == -1 && p->fuse_tuned);
     if (fuse && reps == 0 && !tr_h && !tr_rows && !tr_acc && idx->d_steps && d <= kQueryMaxD) {
         while (t_fuse > 0 && resolve_path(p, t_fuse - 1) == CB_PATH_SPARSE &&
-               resolve_select(p, t_fuse - 1) == CB_SELECT_LDS)
+               resolve_select(p, t_fuse - 1) == CB_SELECT_LDS && opt(p->sparse_form, t_fuse - 1) != 1)
             --t_fuse;
         if (L - t_fuse < 2) t_fuse = L;
     }
@@ -946,7 +967,8 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
             // time every allowed (scoring path, selection) pair on this step's inputs, outputs to scratch
             float best_us[2] = {-1.f, -1.f};  // dense, sparse (either variant): best over the selections
             float best = -1.f;
-            int32_t best_path = 0, best_sel = 0, best_nt = 0, best_rows = 0, best_pre = 0, best_min = 0, best_form = 0;
+            int32_t best_path = 0, best_sel = 0, best_nt = 0, best_rows = 0, best_pre = 0, best_min = 0, best_form = 0,
+                    best_split = 0;
             const int32_t paths[3] = {CB_PATH_DENSE, CB_PATH_SPARSE, CB_PATH_SPARSE_SPLIT};
             const int32_t sels[2] = {CB_SELECT_LDS, CB_SELECT_RADIX};
             const cb::StepTable& T = idx->steps[(size_t)t];
@@ -980,12 +1002,17 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
                                           expand_lds_bytes(T.S, p->d, false) <= (size_t)kMaxLds;
                     const int nts[4] = {0, 256, 0, 256};
                     const int mins[4] = {kPreMin, kPreMin, 1, 1};
+                    // and the plain sparse path with two and four workgroups per query
+                    const bool qsplit_var = paths[k] == CB_PATH_SPARSE && per_query;
                     const int nv0 = split_var ? 4 : per_query || rows_var || pre_var ? 2 : 1;
-                    const int nv = nv0 + (form_var ? 1 : 0);
+                    const int nv1 = nv0 + (form_var ? 1 : 0);
+                    const int nv = nv1 + (qsplit_var ? 2 : 0);
                     for (int v = 0; v < nv && st == CB_OK; ++v) {
-                        const bool beam_form = v == nv0;
+                        const bool beam_form = form_var && v == nv0;
+                        const int qs = v >= nv1 ? (v == nv1 ? 2 : 4) : 0;
                         p->sparse_form[(size_t)t] = beam_form ? 1 : 0;
-                        p->query_nt[(size_t)t] = per_query && !beam_form ? nts[v] : 0;
+                        p->query_split[(size_t)t] = qs;
+                        p->query_nt[(size_t)t] = per_query && !beam_form && v < nv0 ? nts[v] : 0;
                         p->split_min[(size_t)t] = split_var ? mins[v] : 0;
                         p->gemm_rows[(size_t)t] = rows_var ? 1 + v : 0;
                         p->radix_pre[(size_t)t] = pre_var && !beam_form ? 1 + v : 0;
@@ -1015,6 +1042,7 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
                             best_pre = p->radix_pre[(size_t)t];
                             best_min = p->split_min[(size_t)t];
                             best_form = p->sparse_form[(size_t)t];
+                            best_split = p->query_split[(size_t)t];
                         }
                     }
                     p->query_nt[(size_t)t] = 0;
@@ -1022,6 +1050,7 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
                     p->gemm_rows[(size_t)t] = 0;
                     p->radix_pre[(size_t)t] = 0;
                     p->sparse_form[(size_t)t] = 0;
+                    p->query_split[(size_t)t] = 0;
                 }
             }
             if (st != CB_OK) break;
@@ -1034,6 +1063,7 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
             p->radix_pre[(size_t)t] = best_pre;
             p->split_min[(size_t)t] = best_min;
             p->sparse_form[(size_t)t] = best_form;
+            p->query_split[(size_t)t] = best_split;
         }
         st = run_step(p, t, Q, resolve_path(p, t), resolve_select(p, t), p->h, Wt, p->rows[cur], p->acc[cur],
                       p->hist_tok + (size_t)t * R, p->hist_par + (size_t)t * R, p->rows[1 - cur], p->acc[1 - cur], s);
@@ -1382,6 +1412,8 @@ void cb_plan_destroy(cb_plan* p) {
     wide_release(p);
     dev_free(p->keys);
     dev_free(p->side);
+    dev_free(p->qz);
+    dev_free(p->qcnt);
     dev_free(p->Z);
     dev_free(p->Zp);
     dev_free(p->live);

@@ -136,10 +136,13 @@ struct cb_plan {
     std::vector<int32_t> radix_pre; // per step: radix selection with (2) or without (1) the one-token pre-pass, 0 = default
     std::vector<int32_t> split_min; // per step: split sparse path scores apart the rows above this many tokens (0 = 16)
     std::vector<int32_t> sparse_form; // per step: sparse step as one kernel per query (0) or per-beam expansion + merge (1)
+    std::vector<int32_t> query_split; // per step: workgroups per query of the per-query sparse step (0 = 1), measured
     std::vector<float> tune_dense_us, tune_sparse_us;
     // workspace (allocated once)
     uint64_t* keys = nullptr;     // [Q_max*K][Kc_max] per-beam survivors (dense path, per-beam sparse form)
     uint64_t* side = nullptr;     // [Q_max*K][Kc_max] their next row << 16 | token (per-beam expansion)
+    float* qz = nullptr;          // [Q_max][K*64 + S_max] scores handed between a query's workgroups
+    int32_t* qcnt = nullptr;      // [Q_max] their arrival counts (zero between launches)
     float* Z = nullptr;           // [Q_max*K][V] full-codebook scores (dense path)
     float* Zp = nullptr;          // [k-slices][rows][V] partial scores (dense path, few live beams)
     int32_t* live = nullptr;      // [Q_max*K] live beam slots (dense path)
@@ -197,10 +200,15 @@ int gemm_blocks(cb_dtype dt, int R, int V, bool full);
 // [K+1], per-query capacity), or null to score them in the step kernel.
 // nt: workgroup size (256, 512 or 1024; 0 = query_threads(K)); every size gives the same bits.
 // pre_min: rows of more than pre_min tokens (and bitmap rows) read their scores from pre.
+// G: workgroups per query (1, 2 or 4; 1 when gz or gcnt is null): each scores
+// a share of the query's rows and the last to finish completes the step.
+// gz: [Q][query_scores_floats(K, S)] scores; gcnt: [Q] arrival counts, zero
+// before the first launch and left at zero by every launch.
 hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int Kc, int d, int nt, const void* hidden,
                              const void* W, const int32_t* beam_rows, const float* acc, const uint64_t* pre,
                              const int32_t* pre_off, int64_t pre_cap, int pre_min, int32_t* tok, int32_t* par,
-                             int32_t* rows, float* logp, hipStream_t s);
+                             int32_t* rows, float* logp, int G, float* gz, int* gcnt, hipStream_t s);
+int64_t query_scores_floats(int K, int S);
 // Dense path: live-beam list, full-codebook scores, per-beam expansion, per-query merge.
 hipError_t launch_live_rows(const StepDev& st, int R, const int32_t* beam_rows, const float* acc, int32_t* live,
                             int32_t* n_live, int32_t* ci_of, hipStream_t s);

@@ -233,10 +233,11 @@ constexpr int kWaveListCap = 256;
 // the Kc-th largest lane maximum of the scores bounds the answer from below
 // (every key of the answer has a score >= tau); the candidates with score >=
 // tau get their full keys compacted (ballot order) into the wave's LDS list wl
-// [kWaveListCap], a window at a time, and are sorted with wave64 bitonic
-// networks.  No block barriers.
-template <int M, class ScoreF, class KeyF>
+// [CAP], a window at a time, and are sorted with wave64 bitonic networks (a
+// single window of at most 64 keys is ranked instead).  No block barriers.
+template <int M, int CAP = kWaveListCap, class ScoreF, class KeyF>
 __device__ uint64_t wave_top(int Kc, ScoreF score, KeyF key, uint64_t* wl) {
+    static_assert(CAP >= kWave && CAP % kWave == 0, "windows hold whole waves of keys");
     const int lane = threadIdx.x & (kWave - 1);
     uint32_t mx = 0;
 #pragma unroll
@@ -250,17 +251,17 @@ __device__ uint64_t wave_top(int Kc, ScoreF score, KeyF key, uint64_t* wl) {
     const int total = lane_bcast(incl, kWave - 1);
     uint64_t best = 0;
     bool first = true;
-    for (int s0 = 0; s0 < total; s0 += kWaveListCap) {
+    for (int s0 = 0; s0 < total; s0 += CAP) {
         int pos = incl - cnt;
 #pragma unroll
         for (int i = 0; i < M; ++i) {
             if (score(i) >= tau) {
-                if (pos >= s0 && pos < s0 + kWaveListCap) wl[pos - s0] = key(i);
+                if (pos >= s0 && pos < s0 + CAP) wl[pos - s0] = key(i);
                 ++pos;
             }
         }
         wave_lds_sync();
-        const int w = min(kWaveListCap, total - s0);
+        const int w = min(CAP, total - s0);
         if (total <= kWave) {
             // a single window: each key's rank (number of larger keys; keys
             // are unique) is its output lane, placed through the LDS list

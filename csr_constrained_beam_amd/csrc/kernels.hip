@@ -62,7 +62,7 @@ __device__ int32_t edge_of(const StepDev& st, int32_t r, int token) {
 }
 
 // Output slot i of query q from its key.
-__device__ void emit(const StepDev& st, int q, int K, int i, uint64_t key, const int32_t* __restrict__ beam_rows,
+__device__ __forceinline__ void emit(const StepDev& st, int q, int K, int i, uint64_t key, const int32_t* __restrict__ beam_rows,
                      int32_t* out_tok, int32_t* out_par, int32_t* out_rows, float* out_logp) {
     const int64_t o = (int64_t)q * K + i;
     if (key == 0ull) {
@@ -185,6 +185,12 @@ __host__ __device__ constexpr int kTaskTokens() {
 // nrows / nacc: NULL, or LDS [K] receiving the next rows and log-probs.
 // Every sum is per wave or over fixed slots, so any workgroup size (a
 // multiple of 64) gives the same bits.
+//
+// G > 1 workgroups per query (g = 0..G-1): each scores its share of the
+// query's scoring tasks (phase 1b) and writes the scores to gz [K * 64 + S]
+// as well; the workgroup that finishes last (a per-query arrival count in
+// *gcnt, which it resets) reads the others' scores back and completes the
+// step.  No workgroup waits for another.
 template <typename DT, int NT, int CH>
 __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d, const DT* __restrict__ hidden,
                                  const DT* __restrict__ W, const int32_t* __restrict__ rows_q,
@@ -192,7 +198,8 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
                                  const int32_t* __restrict__ pre_off, int64_t pre_cap, int pre_min,
                                  int32_t* __restrict__ out_tok, int32_t* __restrict__ out_par,
                                  int32_t* __restrict__ out_rows, float* __restrict__ out_logp, unsigned char* smem,
-                                 uint64_t* best, int32_t* nrows, float* nacc) {
+                                 uint64_t* best, int32_t* nrows, float* nacc, int G = 1, int g = 0,
+                                 float* __restrict__ gz = nullptr, int* __restrict__ gcnt = nullptr) {
     __shared__ float red_f[red_slots<NT>()];
     __shared__ int red_i[NT / kWave];
     __shared__ uint64_t bcast;
@@ -204,11 +211,15 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
     __shared__ int n_s[kWave];
     __shared__ int nbig;
     __shared__ int big[kWave];
-    __shared__ int nsm;               // rows of 2..kSmallRow tokens (phases 1 - 1c)
-    __shared__ int sml[kWave];
+    __shared__ int nsm;               // rows scored in phases 1 - 1c: 2..kSmallRow tokens, and wider
+    __shared__ int sml[kWave];        // CSR rows whose tokens fit the flat buffer tok_s / z_s together
+    __shared__ int sn[kWave];         // their widths
+    __shared__ int mbase[kWave];      // -1: fixed slots tokq / zmid; else the row's start in tok_s / z_s
+    __shared__ int nmed;              // rows with mbase >= 0
     __shared__ int moff[kWave + 1];   // their first scoring task
     __shared__ int ncand;             // keys in the candidate list qkeys
     __shared__ int ident;             // the step is the identity (see the prologue)
+    __shared__ int last;              // G > 1: this workgroup completes the step
     __shared__ uint64_t slot[kWave];  // survivors of one wide row
     const QueryLds lay = query_lds(st.S, K, Kc, d, NT);
     uint64_t* qkeys = reinterpret_cast<uint64_t*>(smem + lay.qkeys);
@@ -230,7 +241,8 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
     // more: its log-softmax is exactly 0 whatever its score (z - (z + log 1)),
     // so neither its hidden vector nor its W_t row is read and its candidate
     // key is the beam's accumulated log-prob.  Rows of 2..64 tokens (CSR) go
-    // to phase 1, wider rows and bitmap rows to phase 2.
+    // to phase 1, and so do wider CSR rows while their tokens fit the S slots
+    // of the flat buffer; the rest and bitmap rows go to phase 2.
     if (wv == 0) {
         const int k = lane;
         const int32_t r = k < K ? rows_q[k] : -1;
@@ -242,20 +254,30 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
         const bool csr = st.store == CB_STORE_CSR;
         const bool one = live && csr && n == 1 && st.tok0;
         const bool narrow = live && csr && !one && n <= kSmallRow;
-        const bool wide = live && !one && !narrow;
+        // wider CSR rows, in slot order while their tokens fit the S slots of
+        // tok_s / z_s (free until phase 2): scored with the narrow rows
+        const bool mcand = live && csr && n > kSmallRow;
+        const int mincl = wave_inclusive_scan(mcand ? n : 0);
+        const bool medium = mcand && mincl <= st.S;
+        const bool wide = live && !one && !narrow && !medium;
         if (live) {
             r_s[k] = r;
             a_s[k] = a;
             e0_s[k] = e0;
-            n_s[k] = (one || narrow) ? n : -1 - n;
+            n_s[k] = (one || narrow) ? n : -1 - n;  // negative: survivors listed in tokq / jmid
         }
         if (one) tokq[k * kWave] = (uint16_t)f0;
         const uint64_t key = one ? make_key(a + 0.f, k, f0) : 0ull;
-        const uint64_t m_one = __ballot(one), m_nar = __ballot(narrow), m_wide = __ballot(wide),
-                       m_live = __ballot(live);
+        const uint64_t m_one = __ballot(one), m_nar = __ballot(narrow || medium), m_wide = __ballot(wide),
+                       m_live = __ballot(live), m_med = __ballot(medium);
         const uint64_t below = (1ull << lane) - 1ull;
         if (one) qkeys[__popcll(m_one & below)] = key;
-        if (narrow) sml[__popcll(m_nar & below)] = k;
+        if (narrow || medium) {
+            const int i = __popcll(m_nar & below);
+            sml[i] = k;
+            sn[i] = n;
+            mbase[i] = medium ? mincl - n : -1;
+        }
         if (wide) big[__popcll(m_wide & below)] = k;
         // identity: every live row has one token, the live slots come first
         // and their log-probs do not increase, so the K candidates (acc_k,
@@ -264,7 +286,7 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
         const float a_prev = __shfl(a, lane > 0 ? lane - 1 : 0);
         const bool viol = live && lane > 0 && !(a_prev >= a);
         const bool id = m_live == m_one && (m_live & (m_live + 1ull)) == 0ull && __ballot(viol) == 0ull;
-        if (id) {
+        if (id && g == 0) {
             best[lane] = key;
             if (k < K) {
                 const int64_t o = (int64_t)q * K + k;
@@ -281,6 +303,7 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
         if (lane == 0) {
             ncand = __popcll(m_one);
             nsm = __popcll(m_nar);
+            nmed = __popcll(m_med);
             nbig = __popcll(m_wide);
             ident = id;
         }
@@ -293,18 +316,28 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
     // trip); rows whose scores were computed apart get them here too
     const int ns = nsm;
     for (int x = tid; x < ns * kWave; x += NT) {
-        const int k = sml[x / kWave], j = x % kWave, n = n_s[k];
-        if (j < n) {
+        const int i = x / kWave, k = sml[i], j = x % kWave, n = sn[i];
+        if (j < n && mbase[i] < 0) {
             tokq[k * kWave + j] = st.tok[e0_s[k] + j];
             if (pre && n > pre_min)
                 zmid[k * kWave + j] =
                     __uint_as_float((uint32_t)(pre[(int64_t)q * pre_cap + pre_off[(int64_t)q * (K + 1) + k] + j] >> 32));
         }
     }
+    for (int i = 0; nmed && i < ns; ++i) {  // the wider rows: every token of one row per pass
+        const int base = mbase[i];
+        if (base < 0) continue;
+        const int k = sml[i], n = sn[i];
+        for (int j = tid; j < n; j += NT) {
+            tok_s[base + j] = st.tok[e0_s[k] + j];
+            if (pre && n > pre_min)
+                z_s[base + j] =
+                    __uint_as_float((uint32_t)(pre[(int64_t)q * pre_cap + pre_off[(int64_t)q * (K + 1) + k] + j] >> 32));
+        }
+    }
     if (wv == 0) {
         // tasks of MT consecutive tokens of one row, over every row still to score
-        const int k = lane < ns ? sml[lane] : 0;
-        const int n = lane < ns ? n_s[k] : 0;
+        const int n = lane < ns ? sn[lane] : 0;
         const int c = lane < ns && !(pre && n > pre_min) ? (n + kTaskTokens<DT, CH>() - 1) / kTaskTokens<DT, CH>() : 0;
         const int incl = wave_inclusive_scan(c);
         if (lane < ns) moff[lane + 1] = incl;
@@ -322,22 +355,28 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
     constexpr int MT = kTaskTokens<DT, CH>();
     constexpr int TPW = 2 * (MT * CH * kRw + CH * 8) <= 96 ? 2 : 1;
     const int ntask = moff[ns];
-    for (int t0 = wv; t0 < ntask; t0 += TPW * NW) {
-        int kq[TPW], j0[TPW], nn[TPW];
+    if (G > 1 && ntask == 0 && g != 0) return;  // nothing to share: workgroup 0 does the step alone
+    const bool handoff = G > 1 && ntask > 0;
+    // this workgroup's share of the tasks
+    const int tb = handoff ? (int)((int64_t)ntask * g / G) : 0;
+    const int te = handoff ? (int)((int64_t)ntask * (g + 1) / G) : ntask;
+    for (int t0 = tb + wv; t0 < te; t0 += TPW * NW) {
+        int kq[TPW], j0[TPW], nn[TPW], mb[TPW];
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
             const int task = t0 + u * NW;
             int lo = 0;
-            if (task < ntask) {  // the row whose tasks hold this one: last i with moff[i] <= task
+            if (task < te) {  // the row whose tasks hold this one: last i with moff[i] <= task
                 int hi = ns;
                 while (hi - lo > 1) {
                     const int md = (lo + hi) >> 1;
                     if (moff[md] <= task) lo = md; else hi = md;
                 }
             }
-            kq[u] = task < ntask ? sml[lo] : 0;
-            j0[u] = task < ntask ? (task - moff[lo]) * MT : 0;
-            nn[u] = task < ntask ? min(MT, n_s[kq[u]] - j0[u]) : 0;
+            kq[u] = task < te ? sml[lo] : 0;
+            j0[u] = task < te ? (task - moff[lo]) * MT : 0;
+            nn[u] = task < te ? min(MT, sn[lo] - j0[u]) : 0;
+            mb[u] = task < te ? mbase[lo] : -1;
         }
         Raw8<DT> hr[TPW][CH];
         Raw8<DT> w8[TPW][MT][CH];
@@ -354,7 +393,8 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
 #pragma unroll
             for (int jj = 0; jj < MT; ++jj) {
                 const bool on = jj < nn[u];
-                const int tkn = on ? (int)tokq[kq[u] * kWave + j0[u] + jj] : 0;
+                const int tkn = !on ? 0 : mb[u] < 0 ? (int)tokq[kq[u] * kWave + j0[u] + jj]
+                                                    : (int)tok_s[mb[u] + j0[u] + jj];
 #pragma unroll
                 for (int c = 0; c < CH; ++c) {
                     const int i2 = c * kWave * 8 + lane * 8;
@@ -370,14 +410,92 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
 #pragma unroll
                 for (int c = 0; c < CH; ++c) sv = w8[u][jj][c].dot_raw(hr[u][c], sv);
                 const float t = wave_sum(sv);
-                if (lane == 0 && jj < nn[u]) zmid[kq[u] * kWave + j0[u] + jj] = t;
+                if (lane == 0 && jj < nn[u]) {
+                    const int zi = mb[u] < 0 ? kq[u] * kWave + j0[u] + jj : K * kWave + mb[u] + j0[u] + jj;
+                    if (mb[u] < 0) zmid[zi] = t;
+                    else z_s[mb[u] + j0[u] + jj] = t;
+                    // device-coherent store (no cache write-back needed before the hand-off)
+                    if (handoff) __hip_atomic_store(gz + zi, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
     }
     __syncthreads();
+    if (handoff) {
+        // hand-off: the scores went out as device-coherent stores; every
+        // wave waits until its stores are acknowledged, then one arrival per
+        // workgroup on the query's count (a device-coherent atomic); the
+        // last to arrive resets the count and reads the others' scores with
+        // device-coherent loads, the rest stop
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+            const int prev = __hip_atomic_fetch_add(gcnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = prev == G - 1;
+            if (last) __hip_atomic_store(gcnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!last) return;  // uniform over the workgroup
+        for (int x = tid; x < ns * kWave; x += NT) {
+            const int i = x / kWave, k = sml[i], j = x % kWave, n = sn[i];
+            if (j < n && mbase[i] < 0 && !(pre && n > pre_min))
+                zmid[k * kWave + j] = __hip_atomic_load(gz + k * kWave + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        for (int i = 0; nmed && i < ns; ++i) {
+            const int base = mbase[i], n = sn[i];
+            if (base < 0 || (pre && n > pre_min)) continue;
+            for (int j = tid; j < n; j += NT)
+                z_s[base + j] = __hip_atomic_load(gz + K * kWave + base + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+    }
     // phase 1c: softmax and the beam's best min(n, Kc) keys, one wave per row
     // (the reductions only over the lanes the row occupies)
     for (int i = wv; i < ns; i += NW) {
-        const int k = sml[i], n = n_s[k];
+        const int k = sml[i], n = sn[i], base = mbase[i];
+        if (base >= 0) {
+            // a wider row, 64 tokens at a time: max, then the sum of exps, then
+            // its best min(n, Kc) keys by sorting each 64 and merging
+            const float* zr = z_s + base;
+            const uint16_t* tr = tok_s + base;
+            float m = -INFINITY;
+            for (int c0 = 0; c0 < n; c0 += kWave) m = fmaxf(m, c0 + lane < n ? zr[c0 + lane] : -INFINITY);
+            m = wave_max(m);
+            float se = 0.f;
+            for (int c0 = 0; c0 < n; c0 += kWave) se += c0 + lane < n ? exp_sm(zr[c0 + lane] - m) : 0.f;
+            const float lse = m + logf(wave_sum(se));
+            auto keyj = [&](int j) { return j < n ? make_key(a_s[k] + (zr[j] - lse), k, (int)tr[j]) : 0ull; };
+            uint64_t top = 0ull;
+            if (n <= 4 * kWave) {
+                // up to 4 keys per lane: the threshold selection, ranked in one
+                // window of the wave's 64 stage slots when it holds <= 64 keys
+                uint64_t kv[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) kv[x] = keyj(lane + x * kWave);
+                auto sc = [&](int x) { return (uint32_t)(kv[x] >> 32); };
+                auto kf = [&](int x) { return kv[x]; };
+                if (n <= 2 * kWave) top = wave_top<2, kWave>(Kc, sc, kf, stage + wv * kWave);
+                else top = wave_top<4, kWave>(Kc, sc, kf, stage + wv * kWave);
+            } else {
+                for (int c0 = 0; c0 < n; c0 += kWave) {
+                    const uint64_t key = wave_sort_desc(keyj(c0 + lane));
+                    top = c0 == 0 ? key : wave_merge_top(top, key);
+                }
+            }
+            const bool sv = lane < Kc && top != 0ull;
+            if (sv) {
+                // the survivor's token and its position in the row (ascending tokens)
+                const int tkn = 65535 - (int)(top & 0xFFFFu);
+                int lo = 0, hi = n;
+                while (lo < hi) {
+                    const int md = (lo + hi) >> 1;
+                    if ((int)tr[md] < tkn) lo = md + 1; else hi = md;
+                }
+                tokq[k * kWave + lane] = (uint16_t)tkn;
+                jmid[k * kWave + lane] = lo;
+            }
+            wave_append(sv, top, qkeys, &ncand);
+            continue;
+        }
         const bool on = lane < n;
         const float z = on ? zmid[k * kWave + lane] : -INFINITY;
         const int tk = on ? (int)tokq[k * kWave + lane] : 0;
@@ -386,12 +504,14 @@ __device__ void step_query_block(const StepDev& st, int q, int K, int Kc, int d,
         const float se = wave_sum_w(on ? exp_sm(z - m) : 0.f, w);
         const float lse = m + logf(se);
         uint64_t key = on ? make_key(a_s[k] + (z - lse), k, tk) : 0ull;
-        if (n > Kc) key = wave_sort_desc(key);
+        if (n > Kc)  // the row's Kc best (one key per lane: one window of at most 64 to rank)
+            key = wave_top<1, kWave>(Kc, [&](int) { return (uint32_t)(key >> 32); }, [&](int) { return key; },
+                                     stage + wv * kWave);
         wave_append(lane < min(n, Kc), key, qkeys, &ncand);
     }
     __syncthreads();
 
-    // phase 2: wide rows and bitmap rows, the whole block per beam
+    // phase 2: wide rows left over and bitmap rows, the whole block per beam
     const int nb = nbig;
     for (int i = 0; i < nb; ++i) {
         const int k = big[i];
@@ -453,13 +573,15 @@ __global__ __launch_bounds__(NT) void k_step_query(StepDev st, int K, int Kc, in
                                                    const int32_t* __restrict__ pre_off, int64_t pre_cap, int pre_min,
                                                    int32_t* __restrict__ out_tok,
                                                    int32_t* __restrict__ out_par, int32_t* __restrict__ out_rows,
-                                                   float* __restrict__ out_logp) {
+                                                   float* __restrict__ out_logp, int G, float* __restrict__ gz,
+                                                   int64_t gz_stride, int* __restrict__ gcnt) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ uint64_t best[kWave];
-    const int q = blockIdx.x;
+    const int q = blockIdx.x / G, g = blockIdx.x % G;
     step_query_block<DT, NT, CH>(st, q, K, Kc, d, hidden, W, beam_rows + (int64_t)q * K, acc + (int64_t)q * K, pre,
                                  pre_off, pre_cap, pre_min, out_tok, out_par, out_rows, out_logp, smem, best, nullptr,
-                                 nullptr);
+                                 nullptr, G, g, G > 1 ? gz + (int64_t)q * gz_stride : nullptr,
+                                 G > 1 ? gcnt + q : nullptr);
 }
 
 // ---- dense step: per-beam expansion and per-query merge --------------------
@@ -1272,6 +1394,8 @@ int expand_threads(const StepDev&) { return kExpandThreads; }
 
 int query_threads(int K) { return K >= 16 ? 1024 : 512; }
 
+int64_t query_scores_floats(int K, int S) { return (int64_t)K * kWave + S; }
+
 bool query_threads_ok(int nt) { return nt == 256 || nt == 512 || nt == 1024; }
 
 // The persistent decode runs every step and every hidden update of a query in
@@ -1293,15 +1417,17 @@ size_t tail_lds_bytes(int S, int K, int Kc, int d) { return (size_t)query_lds(S,
 hipError_t launch_step_query(const StepDev& st, cb_dtype dt, int Q, int K, int Kc, int d, int nt, const void* hidden,
                              const void* W, const int32_t* beam_rows, const float* acc, const uint64_t* pre,
                              const int32_t* pre_off, int64_t pre_cap, int pre_min, int32_t* tok, int32_t* par,
-                             int32_t* rows, float* logp, hipStream_t s) {
+                             int32_t* rows, float* logp, int G, float* gz, int* gcnt, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
     const int NT = nt == 256 || nt == 512 || nt == 1024 ? nt : query_threads(K);
     const QueryLds lay = query_lds(st.S, K, Kc, d, NT);
     const int CH = (d + kWave * 8 - 1) / (kWave * 8);
+    if (G < 1 || !gz || !gcnt) G = 1;
+    const int64_t gz_stride = query_scores_floats(K, st.S);
 #define CB_QUERY(DT, NTV, CHV)                                                                           \
-    CB_LAUNCH((k_step_query<DT, NTV, CHV>), dim3(Q), dim3(NTV), lay.total, s, st, K, Kc, d,     \
+    CB_LAUNCH((k_step_query<DT, NTV, CHV>), dim3(Q * G), dim3(NTV), lay.total, s, st, K, Kc, d,     \
                        (const DT*)hidden, (const DT*)W, beam_rows, acc, pre, pre_off, pre_cap, pre_min, tok, par, rows, \
-                       logp)
+                       logp, G, gz, gz_stride, gcnt)
 #define CB_QUERY_NT(DT, CHV)                              \
     do {                                                  \
         if (NT == 1024) CB_QUERY(DT, 1024, CHV);          \

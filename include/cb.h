@@ -227,6 +227,12 @@ cb_status cb_set_path(cb_plan* plan, int32_t t, cb_path path);
  *   CB_OPT_RADIX_PREPASS  radix selection with (2, default) or without (1) the
  *                         pre-pass that finishes queries whose live rows all
  *                         hold one token
+ *   CB_OPT_QUERY_SPLIT    workgroups per query of the per-query sparse step:
+ *                         1 (default), 2 or 4; each scores a share of the
+ *                         query's rows and the last to finish completes the
+ *                         step (ZeroGR summary, "Why fewer scores are not
+ *                         automatically faster": beams read uneven numbers
+ *                         of weight rows; this spreads a heavy query's reads)
  * Errors: CB_EINVAL (unknown option or value), CB_ECAPACITY (the form does not
  * fit the LDS), CB_EUNSUPPORTED (every-slot product of an f32 plan). */
 typedef enum {
@@ -234,7 +240,8 @@ typedef enum {
     CB_OPT_SPLIT_ROWS = 1,
     CB_OPT_SPARSE_FORM = 2,
     CB_OPT_DENSE_ROWS = 3,
-    CB_OPT_RADIX_PREPASS = 4
+    CB_OPT_RADIX_PREPASS = 4,
+    CB_OPT_QUERY_SPLIT = 5
 } cb_step_option;
 cb_status cb_set_step_option(cb_plan* plan, int32_t t, cb_step_option option, int32_t value);
 
@@ -345,8 +352,8 @@ cb_status cb_wire_results(int32_t Q, int32_t K, int32_t L, const int32_t* seqs, 
 /* Persistent decode (FlashTrie, arXiv HTML, sections 2.2 and 4.2: every step
  * of a query in one launch, paying the launch cost once).  When enabled and
  * cb_decode is called without trace buffers, the trailing run of steps whose
- * path resolves to CB_PATH_SPARSE with CB_SELECT_LDS (at least two steps)
- * runs as one launch: one workgroup per query performs each of those steps
+ * path resolves to CB_PATH_SPARSE with CB_SELECT_LDS in the per-query form
+ * (CB_OPT_SPARSE_FORM 0; at least two steps) runs as one launch: one workgroup per query performs each of those steps
  * and the hidden updates between them, so no workgroup waits for another.
  * Results equal the step-by-step decode bit for bit.  enable: 1 on, 0 off
  * (one launch per step), -1 (the default) automatic: cb_tune times the

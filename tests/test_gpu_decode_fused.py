@@ -30,6 +30,9 @@ def set_paths(plan, L, mode):
             plan.set_path(t, "dense" if t == 0 else "sparse")
         elif mode == "middle_dense":
             plan.set_path(t, "dense" if t == L // 2 else "sparse")
+        elif mode == "middle_per_beam":  # one step in the per-beam form splits the trailing run
+            plan.set_path(t, "sparse")
+            plan.set_option(t, "sparse_form", 1 if t == L // 2 else 0)
         else:
             plan.set_path(t, "auto")
 
@@ -58,13 +61,14 @@ def decode_both(plan, q, P, W):
 
 def expected_tail(plan, L):
     t = L
-    while t > 0 and plan.get_path(t - 1) == "sparse" and plan.get_select(t - 1) == "lds":
+    while (t > 0 and plan.get_path(t - 1) == "sparse" and plan.get_select(t - 1) == "lds"
+           and plan.get_option(t - 1, "sparse_form") == 0):
         t -= 1
     return t if L - t >= 2 else L
 
 
 @pytest.mark.parametrize("name", ["tiny", "small"])
-@pytest.mark.parametrize("mode", ["auto", "all_sparse", "first_dense", "middle_dense"])
+@pytest.mark.parametrize("mode", ["auto", "all_sparse", "first_dense", "middle_dense", "middle_per_beam"])
 def test_persistent_decode_equals_step_by_step(name, mode):
     w = workload(name)
     cfg, ref = w["cfg"], w["ref"]

@@ -122,21 +122,27 @@ def test_fullsize_persistent_decode(name, paths):
 
 
 @pytest.mark.parametrize("name", ["production", "hybrid"])
-@pytest.mark.parametrize("path", ["tuned", "dense", "sparse", "sparse_split", "sparse_beam"])
+@pytest.mark.parametrize("path", ["tuned", "dense", "sparse", "sparse_split", "sparse_beam", "sparse_qsplit"])
 def test_fullsize_teacher_forced(name, path):
     w = big(name)
     cfg, ref, plan, T = w["cfg"], w["ref"], w["plan"], w["T"]
     K = cfg.K
     S = cfg.Q * K
     forms = [plan.get_option(t, "sparse_form") for t in range(cfg.L)]
+    splits = [plan.get_option(t, "query_split") for t in range(cfg.L)]
     try:
         for t in range(cfg.L):
             if path == "sparse_beam":
                 plan.set_path(t, "sparse")
                 print("per-beam form:", force_beam_form(plan, t), flush=True)
+            elif path == "sparse_qsplit":
+                plan.set_path(t, "sparse")
+                plan.set_option(t, "sparse_form", 0)
+                plan.set_option(t, "query_split", 4)
             elif path != "tuned":
                 plan.set_path(t, path)
                 plan.set_option(t, "sparse_form", 0)
+                plan.set_option(t, "query_split", 1)
             print(name, path, "step", t, plan.get_path(t), flush=True)
             h = ref["trace_h"][t]
             hd = torch.from_numpy(h).to(DEV)
@@ -155,3 +161,4 @@ def test_fullsize_teacher_forced(name, path):
         for t in range(cfg.L):
             plan.set_path(t, "auto")
             plan.set_option(t, "sparse_form", forms[t])
+            plan.set_option(t, "query_split", splits[t])

@@ -101,7 +101,8 @@ def test_single_token_steps(dtype, multi, order):
 @pytest.mark.parametrize("K", [8, 32])
 def test_workgroup_sizes_agree_on_every_phase(K):
     """Rows of every scoring phase (1, 2-4, 5-64, > 64 tokens): the three
-    workgroup sizes give identical bits, and the oracle's results."""
+    workgroup sizes, and two and four workgroups per query, give identical
+    bits, and the oracle's results."""
     from tests.test_gpu_widths import catalog as wide_catalog
     items, V = wide_catalog(11)
     L, Q, d = 3, 6, 1024
@@ -118,15 +119,17 @@ def test_workgroup_sizes_agree_on_every_phase(K):
         h, rows, acc = ref["trace_h"][t], ref["trace_rows_in"][t], ref["trace_acc_in"][t]
         o = T.step(t, K, h, W[t], rows, acc, candidates=True, threads=8)
         outs = []
-        for nt in (256, 512, 1024):
-            print("case K", K, "step", t, "threads", nt, flush=True)
+        for nt, qs in ((256, 1), (512, 1), (1024, 1), (1024, 2), (256, 4), (1024, 4)):
+            print("case K", K, "step", t, "threads", nt, "workgroups per query", qs, flush=True)
             plan.set_path(t, "sparse")
             plan.set_select(t, "lds")
             plan.set_step_threads(t, nt)
+            plan.set_option(t, "query_split", qs)
             hd, rd, ad = _device_inputs(h, rows, acc, "bf16")
-            g = gpu_step(plan, t, hd, Wd[t], rd, ad)
-            ex, gap, fails = compare_step(o, g, K, "bf16")
-            assert not fails, "\n".join(fails[:10])
+            for rep in range(2):  # the arrival counts are left at zero for the next launch
+                g = gpu_step(plan, t, hd, Wd[t], rd, ad)
+                ex, gap, fails = compare_step(o, g, K, "bf16")
+                assert not fails, "\n".join(fails[:10])
             outs.append(g)
         for g in outs[1:]:
             for k in ("tokens", "parents", "rows", "logp"):

@@ -57,7 +57,7 @@ def test_catalog_covers_every_phase():
 @pytest.mark.parametrize("dtype,d", [("f32", 1024), ("f32", 2048), ("bf16", 1536), ("bf16", 2048),
                                      ("f32", 4096), ("bf16", 4096)])
 @pytest.mark.parametrize("K", [8, 32])
-@pytest.mark.parametrize("path", ["sparse", "dense", "sparse_beam"])
+@pytest.mark.parametrize("path", ["sparse", "dense", "sparse_beam", "sparse_qsplit"])
 def test_step_hidden_widths(dtype, d, K, path):
     _run_widths(dtype, d, K, path, "lds")
 
@@ -93,10 +93,12 @@ def _run_widths(dtype, d, K, path, select, split_rows=0):
     idx = cb.Index(items, V, device=0)
     plan = idx.plan(Q, K, d, dtype)
     for t in range(L):
-        plan.set_path(t, "sparse" if path == "sparse_beam" else path)
+        plan.set_path(t, "sparse" if path in ("sparse_beam", "sparse_qsplit") else path)
         plan.set_select(t, select)
         if path == "sparse_beam":  # one workgroup per beam, then the per-query merge
             force_beam_form(plan, t)
+        if path == "sparse_qsplit":  # four workgroups per query
+            plan.set_option(t, "query_split", 4)
         if split_rows:
             plan.set_split_rows(t, split_rows)
     for t in range(L):

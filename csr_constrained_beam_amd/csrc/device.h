@@ -225,7 +225,7 @@ __device__ __forceinline__ uint32_t wave_sort_desc32(uint32_t v) {
     return v;
 }
 
-constexpr int kWaveListCap = 256;
+constexpr int kWaveListCap = 256;  // keys per window of wave_top (its list holds 64 more)
 
 // The Kc (<= 64) largest keys of the wave, descending in lanes 0..Kc-1 (0 when
 // fewer).  Lane l owns M candidates; score(i) is the high half of candidate i's
@@ -235,7 +235,11 @@ constexpr int kWaveListCap = 256;
 // tau get their full keys compacted (ballot order) into the wave's LDS list wl
 // [CAP], a window at a time, and are sorted with wave64 bitonic networks (a
 // single window of at most 64 keys is ranked instead).  No block barriers.
-template <int M, int CAP = kWaveListCap, class ScoreF, class KeyF>
+// With TRASH, wl holds CAP + 64 entries and the list is filled without
+// branches: a key outside the current window goes to its lane's slot past
+// the window (the per-column loop is otherwise one divergent branch per
+// column).
+template <int M, int CAP = kWaveListCap, bool TRASH = (CAP == kWaveListCap), class ScoreF, class KeyF>
 __device__ uint64_t wave_top(int Kc, ScoreF score, KeyF key, uint64_t* wl) {
     static_assert(CAP >= kWave && CAP % kWave == 0, "windows hold whole waves of keys");
     const int lane = threadIdx.x & (kWave - 1);
@@ -253,11 +257,21 @@ __device__ uint64_t wave_top(int Kc, ScoreF score, KeyF key, uint64_t* wl) {
     bool first = true;
     for (int s0 = 0; s0 < total; s0 += CAP) {
         int pos = incl - cnt;
+        if constexpr (TRASH) {
 #pragma unroll
-        for (int i = 0; i < M; ++i) {
-            if (score(i) >= tau) {
-                if (pos >= s0 && pos < s0 + CAP) wl[pos - s0] = key(i);
-                ++pos;
+            for (int i = 0; i < M; ++i) {
+                const bool take = score(i) >= tau;
+                const unsigned p = (unsigned)(pos - s0);
+                wl[take && p < (unsigned)CAP ? (int)p : CAP + lane] = key(i);
+                pos += take;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < M; ++i) {
+                if (score(i) >= tau) {
+                    if (pos >= s0 && pos < s0 + CAP) wl[pos - s0] = key(i);
+                    ++pos;
+                }
             }
         }
         wave_lds_sync();

@@ -695,23 +695,87 @@ __global__ __launch_bounds__(NT) void k_beam_expand(StepDev st, int K, int Kc, i
     }
 }
 
+// Outputs of a query's merge.
+struct MergeOut {
+    int32_t* tok;
+    int32_t* par;
+    int32_t* rows;
+    float* logp;
+};
+
+// The query's K best of its K * Kc candidate keys, one wavefront: lane l
+// owns keys l + 64 i (i < M).  side: NULL when the keys carry tokens (the
+// bitmap expansion; the next row comes from the step table), else the
+// per-beam side information of k_beam_expand (keys carry list places).
+template <int M>
+__device__ __forceinline__ void merge_query_wave(const StepDev& st, int q, int K, int Kc,
+                                                 const uint64_t* __restrict__ keys,
+                                                 const uint64_t* __restrict__ side,
+                                                 const int32_t* __restrict__ beam_rows, const MergeOut& mo, int mode,
+                                                 uint64_t* wl) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int n = K * Kc;
+    const uint64_t* src = keys + (int64_t)q * n;
+    uint64_t kv[M];
+    // branch-free loads (indices past the list re-read its last key, then
+    // masked), so that all M loads are in flight together
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        const int c = lane + kWave * i;
+        const uint64_t v = src[min(c, n - 1)];
+        kv[i] = c < n ? v : 0ull;
+    }
+    const uint64_t best = wave_top<M>(K, [&](int i) { return (uint32_t)(kv[i] >> 32); }, [&](int i) { return kv[i]; },
+                                      wl);
+    if (lane < K && side) {
+        const int64_t o = (int64_t)q * K + lane;
+        if (!best) {
+            mo.tok[o] = -1;
+            mo.par[o] = -1;
+            mo.rows[o] = -1;
+            mo.logp[o] = -INFINITY;
+        } else {
+            const int parent = 1023 - (int)((best >> 16) & 1023u);
+            const int i = 65535 - (int)(best & 0xFFFFu);
+            const uint64_t info = side[((int64_t)q * K + parent) * Kc + i];
+            mo.tok[o] = (int32_t)(info & 0xFFFFu);
+            mo.par[o] = parent;
+            mo.rows[o] = (int32_t)(info >> 16);
+            mo.logp[o] = score_from_order_bits((uint32_t)(best >> 32));
+        }
+    } else if (lane < K) {
+        if (mode == CB_MODE_UNCONSTRAINED) {
+            // no catalog: every live beam sits at row 0 of the next table
+            const int64_t o = (int64_t)q * K + lane;
+            mo.tok[o] = best ? 65535 - (int)(best & 0xFFFFu) : -1;
+            mo.par[o] = best ? 1023 - (int)((best >> 16) & 1023u) : -1;
+            mo.rows[o] = best ? 0 : -1;
+            mo.logp[o] = best ? score_from_order_bits((uint32_t)(best >> 32)) : -INFINITY;
+        } else {
+            emit(st, q, K, lane, best, beam_rows, mo.tok, mo.par, mo.rows, mo.logp);
+        }
+    }
+}
+
 // Dense path on a bitmap step: one wavefront per beam, four beams per
 // workgroup.  Lane l owns the M columns g*256 + 4l .. g*256 + 4l + 3
 // (g < M/4), so that every 16-byte load of the wave reads 1 KB of the score
 // row contiguously; their scores (summed over the k-slices, if any) and
 // validity bits stay in registers; softmax and the beam's best min(K, n) keys
-// use wave reductions only.  Requires V <= 64*M and V % 4 == 0.
-template <int M>
+// use wave reductions only.  Requires V <= 64*M and V % 4 == 0.  MODE: the
+// decoding variant (a template argument, so that the per-column tests are
+// the variant's own and nothing else: this kernel is bound by the issue of
+// its per-column instructions, four cycles each for a 64-lane wave).
+template <int M, int MODE>
 __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K, int Kc, int V, int d,
                                                        const float* __restrict__ Z, const float* __restrict__ Zp,
                                                        const int32_t* __restrict__ n_live,
                                                        const int32_t* __restrict__ ci_of,
                                                        const int32_t* __restrict__ beam_rows,
-                                                       const float* __restrict__ acc, uint64_t* __restrict__ keys_out,
-                                                       int mode) {
+                                                       const float* __restrict__ acc, uint64_t* __restrict__ keys_out) {
     static_assert(M % 4 == 0 && M <= 64, "columns are read 4 at a time, at most 64 per lane");
     constexpr int G = M / 4;
-    __shared__ uint64_t wl_all[4][kWaveListCap];
+    __shared__ uint64_t wl_all[4][kWaveListCap + kWave];
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     const int b = blockIdx.x * 4 + wv;
     if (b >= R) return;
@@ -723,7 +787,7 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
         return;
     }
     auto col = [&](int i) { return (i >> 2) * (kWave * 4) + lane * 4 + (i & 3); };
-    const uint32_t* rb = mode == CB_MODE_UNCONSTRAINED ? nullptr : st.bits + (int64_t)r * st.words;
+    const uint32_t* rb = MODE == CB_MODE_UNCONSTRAINED ? nullptr : st.bits + (int64_t)r * st.words;
     const int split = gemm_split(*n_live, V, d);
     const float* zb = split == 1 ? Z + (int64_t)b * V : Zp + (int64_t)ci_of[b] * V;
     float z[M];
@@ -749,7 +813,7 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
     // holds words l and l + 64), then group g's four bits, which lie in word
     // 8g + l/8 at bit 4(l%8), fetched from the lane holding that word
     uint32_t vb[G];
-    if (mode != CB_MODE_UNCONSTRAINED) {
+    if constexpr (MODE != CB_MODE_UNCONSTRAINED) {
         const int words = (V + 31) >> 5;
         const uint32_t w0 = rb[min(lane, words - 1)];
         const uint32_t w1 = G > 8 ? rb[min(lane + kWave, words - 1)] : 0u;
@@ -766,16 +830,15 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
     // candidates: the row's valid tokens, or (no constraint) every column
     auto valid = [&](int i) { return ((vb[i >> 2] >> (i & 3)) & 1u) != 0; };
     // softmax support: the candidates, or (score first) every column
-    auto in_lse = [&](int i) { return mode == CB_MODE_FILTER_FIRST ? valid(i) : col(i) < V; };
+    // (columns past V have validity 0, so that filter first needs no bound test)
+    auto in_lse = [&](int i) { return MODE == CB_MODE_FILTER_FIRST ? valid(i) : col(i) < V; };
     float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < M; ++i)
-        if (in_lse(i)) m = fmaxf(m, z[i]);
+    for (int i = 0; i < M; ++i) m = fmaxf(m, in_lse(i) ? z[i] : -INFINITY);
     m = wave_max(m);
     float se = 0.f;
 #pragma unroll
-    for (int i = 0; i < M; ++i)
-        if (in_lse(i)) se += exp_sm(z[i] - m);
+    for (int i = 0; i < M; ++i) se += in_lse(i) ? exp_sm(z[i] - m) : 0.f;
     const float lse = m + logf(wave_sum(se));
     const int parent = b % K;
     uint32_t sc[M];
@@ -788,64 +851,17 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
     if (lane < Kc) out[lane] = best;
 }
 
-// Dense path, per query: one wavefront per query, four queries per workgroup;
-// lane l owns keys l + 64 i (i < M) of the query's K*Kc.
-// side: NULL when the keys carry tokens (the bitmap expansion; the next row
-// comes from the step table), else the per-beam side information of
-// k_beam_expand (keys carry list places).
+// Dense path, per query: one wavefront per query, four queries per workgroup.
 template <int M>
 __global__ __launch_bounds__(256) void k_query_merge_w(StepDev st, int Q, int K, int Kc,
                                                        const uint64_t* __restrict__ keys,
                                                        const uint64_t* __restrict__ side,
-                                                       const int32_t* __restrict__ beam_rows,
-                                                       int32_t* __restrict__ out_tok, int32_t* __restrict__ out_par,
-                                                       int32_t* __restrict__ out_rows, float* __restrict__ out_logp,
-                                                       int mode) {
-    __shared__ uint64_t wl_all[4][kWaveListCap];
-    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+                                                       const int32_t* __restrict__ beam_rows, MergeOut mo, int mode) {
+    __shared__ uint64_t wl_all[4][kWaveListCap + kWave];
+    const int wv = threadIdx.x / kWave;
     const int q = blockIdx.x * 4 + wv;
     if (q >= Q) return;
-    const int n = K * Kc;
-    const uint64_t* src = keys + (int64_t)q * n;
-    uint64_t kv[M];
-    // branch-free loads (indices past the list re-read its last key, then
-    // masked), so that all M loads are in flight together
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-        const int c = lane + kWave * i;
-        const uint64_t v = src[min(c, n - 1)];
-        kv[i] = c < n ? v : 0ull;
-    }
-    const uint64_t best = wave_top<M>(K, [&](int i) { return (uint32_t)(kv[i] >> 32); }, [&](int i) { return kv[i]; },
-                                      wl_all[wv]);
-    if (lane < K && side) {
-        const int64_t o = (int64_t)q * K + lane;
-        if (!best) {
-            out_tok[o] = -1;
-            out_par[o] = -1;
-            out_rows[o] = -1;
-            out_logp[o] = -INFINITY;
-        } else {
-            const int parent = 1023 - (int)((best >> 16) & 1023u);
-            const int i = 65535 - (int)(best & 0xFFFFu);
-            const uint64_t info = side[((int64_t)q * K + parent) * Kc + i];
-            out_tok[o] = (int32_t)(info & 0xFFFFu);
-            out_par[o] = parent;
-            out_rows[o] = (int32_t)(info >> 16);
-            out_logp[o] = score_from_order_bits((uint32_t)(best >> 32));
-        }
-    } else if (lane < K) {
-        if (mode == CB_MODE_UNCONSTRAINED) {
-            // no catalog: every live beam sits at row 0 of the next table
-            const int64_t o = (int64_t)q * K + lane;
-            out_tok[o] = best ? 65535 - (int)(best & 0xFFFFu) : -1;
-            out_par[o] = best ? 1023 - (int)((best >> 16) & 1023u) : -1;
-            out_rows[o] = best ? 0 : -1;
-            out_logp[o] = best ? score_from_order_bits((uint32_t)(best >> 32)) : -INFINITY;
-        } else {
-            emit(st, q, K, lane, best, beam_rows, out_tok, out_par, out_rows, out_logp);
-        }
-    }
+    merge_query_wave<M>(st, q, K, Kc, keys, side, beam_rows, mo, mode, wl_all[wv]);
 }
 
 // ---- full-codebook scores of the live beams (dense path) ------------------
@@ -1460,15 +1476,22 @@ hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R,
         ldz <= 64 * kWave && ldz % 4 == 0) {
         const int M = (int)((ldz + kWave - 1) / kWave);
         const dim3 grid((R + 3) / 4);
-#define CB_EXPAND_BM(MV)                                                                                        \
-    CB_LAUNCH((k_expand_bitmap<MV>), grid, dim3(256), 0, s, st, R, K, Kc, (int)ldz, d, Z, Zp, n_live, \
-                       ci_of, beam_rows, acc, keys, mode)
+#define CB_EXPAND_BM_MODE(MV, MD)                                                                            \
+    CB_LAUNCH((k_expand_bitmap<MV, MD>), grid, dim3(256), 0, s, st, R, K, Kc, (int)ldz, d, Z, Zp, n_live, \
+                       ci_of, beam_rows, acc, keys)
+#define CB_EXPAND_BM(MV)                                                                          \
+    do {                                                                                          \
+        if (mode == CB_MODE_FILTER_FIRST) CB_EXPAND_BM_MODE(MV, CB_MODE_FILTER_FIRST);            \
+        else if (mode == CB_MODE_SCORE_FIRST) CB_EXPAND_BM_MODE(MV, CB_MODE_SCORE_FIRST);         \
+        else CB_EXPAND_BM_MODE(MV, CB_MODE_UNCONSTRAINED);                                        \
+    } while (0)
         if (M <= 4) CB_EXPAND_BM(4);
         else if (M <= 8) CB_EXPAND_BM(8);
         else if (M <= 16) CB_EXPAND_BM(16);
         else if (M <= 32) CB_EXPAND_BM(32);
         else CB_EXPAND_BM(64);
 #undef CB_EXPAND_BM
+#undef CB_EXPAND_BM_MODE
         return hipGetLastError();
     }
     const ExpandLds lay = expand_lds(st.S, d, dense, kExpandThreads);
@@ -1500,9 +1523,9 @@ hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uin
     if (Q <= 0) return hipSuccess;
     const int M = (K * Kc + kWave - 1) / kWave;
     const dim3 grid((Q + 3) / 4);
+    const MergeOut mo{tok, par, rows, logp};
 #define CB_MERGE(MV)                                                                                      \
-    CB_LAUNCH((k_query_merge_w<MV>), grid, dim3(256), 0, s, st, Q, K, Kc, keys, side, beam_rows, tok, par, \
-                       rows, logp, mode)
+    CB_LAUNCH((k_query_merge_w<MV>), grid, dim3(256), 0, s, st, Q, K, Kc, keys, side, beam_rows, mo, mode)
     if (M <= 1) CB_MERGE(1);
     else if (M <= 4) CB_MERGE(4);
     else if (M <= 16) CB_MERGE(16);

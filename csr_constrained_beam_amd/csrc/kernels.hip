@@ -1083,6 +1083,31 @@ __global__ __launch_bounds__(kGemmThreads) void k_gemm_bf16(int V, int d, const 
     }
 #undef CB_GEMM_FETCH
 #undef CB_GEMM_STASH
+    if ((V & 3) == 0 && (ldz & 3) == 0) {
+        // the tile through LDS (the k loop left it free after its last
+        // barrier), then out in 16-byte stores along whole rows: 2 rows of the
+        // tile per wave instruction instead of 2 partial rows of 32 columns
+        constexpr int LDC = kBN + 4;
+        static_assert(kBM * LDC * 4 <= kGemmLds, "the output tile fits the LDS of the A and B tiles");
+        float* Cs = reinterpret_cast<float*>(gsm);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int rr = wm + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) Cs[rr * LDC + wn + j * 32 + (lane & 31)] = acc[j][e];
+        }
+        __syncthreads();
+        constexpr int C4 = kBN / 4;
+#pragma unroll
+        for (int x = tid; x < kBM * C4; x += NT) {
+            const int rr = x / C4, c = (x % C4) * 4, col = n0 + c;
+            const int hb = rows_s[rr];
+            if (hb < 0 || col >= V) continue;
+            float* dst = split == 1 ? Z + (int64_t)hb * ldz : Zp + ((int64_t)zs * kSplitRows + m0 + rr) * ldz;
+            *reinterpret_cast<float4*>(dst + col) = *reinterpret_cast<const float4*>(&Cs[rr * LDC + c]);
+        }
+        return;
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const int rr = wm + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);

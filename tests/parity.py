@@ -102,7 +102,7 @@ def compare_step(ref, got, K, dtype, eps_rel=1e-5):
     return exempt, max_gap, fails
 
 
-def decode_vs_oracle(T, r0, rec, W, L, K, Q):
+def decode_vs_oracle(T, r0, rec, W, L, K, Q, mode=None):
     """A free-running device decode against the oracle's.  Per query:
     identical item rows and sequences, or the first step where the device's
     outputs differ is checked on the oracle's candidates of that step (same
@@ -110,7 +110,8 @@ def decode_vs_oracle(T, r0, rec, W, L, K, Q):
     must be between candidates whose oracle scores lie within
     1e-5 * max(1, |score|).  T: the oracle; r0: its decode with trace=True;
     rec: the device decode's trace_rows [L][Q*K], rows and seqs (numpy);
-    W: [L][V][d] float32."""
+    W: [L][V][d] float32; mode: the oracle's decoding variant (None: filter
+    first)."""
     g_rows = [np.asarray(rec["trace_rows"][t]) for t in range(1, L)] + [np.asarray(rec["rows"])]
     r_rows = [r0["trace_rows_in"][t] for t in range(1, L)] + [r0["rows"]]
     g_seqs = np.asarray(rec["seqs"])
@@ -126,8 +127,9 @@ def decode_vs_oracle(T, r0, rec, W, L, K, Q):
             bad.append(q)
             continue
         if first not in cand:
+            mkw = {"mode": mode} if mode else {}
             cand[first] = T.step(first, K, r0["trace_h"][first], W[first], r0["trace_rows_in"][first],
-                                 r0["trace_acc_in"][first], candidates=True, threads=8)
+                                 r0["trace_acc_in"][first], candidates=True, threads=8, **mkw)
         o = cand[first]
         score = {int(o["cand_rows"][q, j]): float(o["cand_scores"][q, j]) for j in range(int(o["cand_count"][q]))}
         ok = True

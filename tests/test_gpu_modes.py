@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.parity import compare_step, logp_ok
+from tests.parity import decode_vs_oracle, compare_step, logp_ok
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -75,10 +75,20 @@ def test_variant_free_running_decode(name, mode):
             assert ok.all(), (qi, err.max())
         else:
             diverged += 1
+    if mode == "score_first":
+        # every query that diverges does so first at a near tie of the oracle's own scores
+        # (item rows identify the candidates; without a catalog every row is 0, so the
+        # unconstrained decode relies on its teacher-forced steps, each checked exactly)
+        rec = {"trace_rows": out["trace_rows"].cpu().numpy(), "rows": rows, "seqs": seqs}
+        vs = decode_vs_oracle(w["T"], ref, rec, w["dense"]["W"], cfg.L, K, cfg.Q, mode=mode)
+        print("decode vs oracle:", vs, flush=True)
+        assert not vs["unexplained"], vs
+        # a query whose traces differ at a near tie may still end with the same sequences
+        assert vs["identical"] + vs["near_tie_divergences"] == cfg.Q and vs["identical"] <= cfg.Q - diverged
+    else:
+        assert diverged <= max(1, cfg.Q // 20), diverged
     if name == "tiny":
         assert diverged == 0
-    else:  # divergence only after a near tie; the teacher-forced test checks every step exactly
-        assert diverged <= max(1, cfg.Q // 20), diverged
     if mode == "unconstrained":
         assert np.all(rows[logp > -np.inf] == 0)
 

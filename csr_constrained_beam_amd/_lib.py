@@ -45,7 +45,7 @@ class PhaseTime(ctypes.Structure):
 KERNEL_NAMES = {0: "gemm_bf16", 1: "gemm_f32", 2: "expand_sparse", 3: "expand_dense", 4: "merge",
                 5: "step_query", 6: "live_rows", 7: "radix_score_sparse", 8: "radix_score_dense",
                 9: "radix_keys", 10: "radix_refine", 11: "radix_collect", 12: "radix_sort",
-                13: "decode_tail", 14: "radix_small"}
+                13: "decode_tail", 14: "radix_small", 15: "row_lse"}
 
 SIGNATURES = {
     "cb_build_index": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _I32, _PP]),

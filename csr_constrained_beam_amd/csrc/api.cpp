@@ -114,8 +114,22 @@ bool lds_select_ok(const cb_plan* p, int t) {
     return sparse_ok && expand_lds_bytes(T.S, p->d, true) <= (size_t)kMaxLds;
 }
 
+// Whether a decoding variant can take the LDS selection at step t: the
+// dense expansion of every token (without a constraint) is the bitmap kernel,
+// which needs a bf16 plan, V <= 4096 and V a multiple of 4.
+bool variant_lds_ok(const cb_plan* p, int t) {
+    if (!lds_select_ok(p, t)) return false;
+    if (p->mode != CB_MODE_UNCONSTRAINED) return true;
+    const int V = p->idx->V;
+    return p->dtype == CB_BF16 && V <= expand_bitmap_max_v() && V % 4 == 0 && std::min(p->K, V) <= p->Kc_max;
+}
+
 int32_t resolve_select(const cb_plan* p, int t) {
-    if (p->mode != CB_MODE_FILTER_FIRST) return CB_SELECT_LDS;
+    if (p->mode != CB_MODE_FILTER_FIRST) {
+        const int32_t f = p->select[(size_t)t];
+        if (f == CB_SELECT_RADIX || (f == CB_SELECT_LDS && variant_lds_ok(p, t))) return f;
+        return variant_lds_ok(p, t) ? CB_SELECT_LDS : CB_SELECT_RADIX;
+    }
     const int32_t f = p->select[(size_t)t];
     if (f == CB_SELECT_LDS || f == CB_SELECT_RADIX) return f;
     const int32_t tu = p->tuned_select[(size_t)t];
@@ -141,9 +155,12 @@ void wide_release(cb_plan* p) {
 
 // Radix-selection workspace sized for the plan's widest row.
 cb_status wide_alloc(cb_plan* p) {
-    if (p->wide.cand) return CB_OK;
     int32_t S = 1;
     for (const auto& T : p->idx->steps) S = std::max(S, T.S);
+    // without a constraint every token of the codebook is a candidate
+    if (p->mode == CB_MODE_UNCONSTRAINED) S = std::max(S, p->idx->V);
+    if (p->wide.cand && p->wide_S >= S) return CB_OK;
+    if (p->wide.cand) wide_release(p);
     const int64_t cap = (int64_t)p->K * S;
     const int64_t chunk_cap = (int64_t)p->K * ((S + wide_chunk() - 1) / wide_chunk());
     if (cap >= (int64_t(1) << 31)) {
@@ -232,6 +249,16 @@ cb_status run_step_radix(cb_plan* p, int t, int Q, int32_t path, const void* hid
                                p->ci_of, full, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: full-codebook scores", e);
+    }
+    // the variants (dense scoring only): every token a candidate, or the
+    // softmax over each beam's whole score row
+    if (p->mode == CB_MODE_UNCONSTRAINED) w.unc_v = idx->V;
+    if (p->mode == CB_MODE_SCORE_FIRST) {
+        ProfMark m(p, s, t, CB_KERNEL_ROW_LSE, 256, (R + 3) / 4);
+        e = launch_row_lse(sd, p->dtype, R, idx->V, p->d, p->Z, p->Zp, p->n_live, p->ci_of, rows, acc, p->lse_row, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: row log-sum-exp", e);
+        w.lse_row = p->lse_row;
     }
     {
         ProfMark m(p, s, t, dense ? CB_KERNEL_RADIX_SCORE_DENSE : CB_KERNEL_RADIX_SCORE_SPARSE, 256, GS);
@@ -654,6 +681,7 @@ cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_
         st = dev_alloc(&p->qz, (size_t)Q_max * (size_t)query_scores_floats(K, S_max), "per-query score hand-off");
     }
     if (st == CB_OK) st = dev_alloc(&p->qcnt, (size_t)Q_max, "per-query arrival counts");
+    if (st == CB_OK) st = dev_alloc(&p->lse_row, R, "row log-sum-exp");
     if (st == CB_OK && hipMemset(p->qcnt, 0, (size_t)Q_max * 4) != hipSuccess) {
         (void)hipGetLastError();
         set_error("cb_plan_create: clearing the arrival counts failed");
@@ -722,26 +750,38 @@ cb_status cb_set_mode(cb_plan* p, cb_mode mode) {
     }
     if (mode != CB_MODE_FILTER_FIRST) {
         const cb_index* idx = p->idx;
-        if (p->K > kMaxK || !dense_available(p)) {
-            set_error("cb_set_mode: the variant needs K <= 64 and the dense path (bf16: d a multiple of 64)");
+        if (!dense_available(p)) {
+            set_error("cb_set_mode: the variant needs the dense path (bf16: d a multiple of 64)");
             return CB_EUNSUPPORTED;
         }
-        for (int t = 0; t < idx->L; ++t)
-            if (expand_lds_bytes(idx->steps[(size_t)t].S, p->d, true) > (size_t)kMaxLds) {
-                set_error("cb_set_mode: a step's dense expansion does not fit the LDS");
-                return CB_EUNSUPPORTED;
-            }
         for (int t = 0; t < idx->L; ++t)
             if (p->forced[(size_t)t] != CB_PATH_AUTO && p->forced[(size_t)t] != CB_PATH_DENSE) {
                 set_error("cb_set_mode: a step is forced to a sparse path");
                 return CB_EUNSUPPORTED;
             }
-        if (mode == CB_MODE_UNCONSTRAINED &&
-            (p->dtype != CB_BF16 || idx->V > 64 * 64 || idx->V % 4 != 0 || std::min(p->K, idx->V) > p->Kc_max)) {
-            set_error("cb_set_mode: unconstrained decoding needs a bf16 plan, V <= 4096, V a multiple of 4 "
-                      "and min(K, V) survivors per beam");
-            return CB_EUNSUPPORTED;
+        // each step takes the LDS selection where it holds the variant, else
+        // the radix selection (beam widths above 64, rows too wide for the
+        // LDS, every token of a codebook above 4,096 tokens as candidates)
+        const int32_t old = p->mode;
+        p->mode = mode;
+        bool radix = false;
+        for (int t = 0; t < idx->L; ++t) {
+            if (p->select[(size_t)t] == CB_SELECT_LDS && !variant_lds_ok(p, t)) {
+                p->mode = old;
+                set_error("cb_set_mode: a step is forced to the LDS selection, which cannot hold the variant");
+                return CB_EUNSUPPORTED;
+            }
+            radix = radix || resolve_select(p, t) == CB_SELECT_RADIX;
         }
+        if (radix) {
+            DeviceGuard g(p->idx->device);
+            const cb_status st = wide_alloc(p);
+            if (st != CB_OK) {
+                p->mode = old;
+                return st;
+            }
+        }
+        return CB_OK;
     }
     p->mode = mode;
     return CB_OK;
@@ -763,13 +803,10 @@ cb_status cb_set_select(cb_plan* p, int32_t t, cb_select sel) {
         set_error("cb_set_select: bad plan, step or selection");
         return CB_EINVAL;
     }
-    if (sel == CB_SELECT_LDS && !lds_select_ok(p, t)) {
-        set_error("cb_set_select: the LDS selection holds K <= 64 and rows that fit its LDS");
+    if (sel == CB_SELECT_LDS && !(p->mode == CB_MODE_FILTER_FIRST ? lds_select_ok(p, t) : variant_lds_ok(p, t))) {
+        set_error("cb_set_select: the LDS selection holds K <= 64 and rows that fit its LDS (unconstrained: "
+                  "also a bf16 plan with V <= 4096, V a multiple of 4)");
         return CB_ECAPACITY;
-    }
-    if (sel == CB_SELECT_RADIX && p->mode != CB_MODE_FILTER_FIRST) {
-        set_error("cb_set_select: the score-first and unconstrained variants take the LDS selection only");
-        return CB_EUNSUPPORTED;
     }
     if (sel == CB_SELECT_RADIX) {
         DeviceGuard g(p->idx->device);
@@ -1414,6 +1451,7 @@ void cb_plan_destroy(cb_plan* p) {
     dev_free(p->side);
     dev_free(p->qz);
     dev_free(p->qcnt);
+    dev_free(p->lse_row);
     dev_free(p->Z);
     dev_free(p->Zp);
     dev_free(p->live);

@@ -95,7 +95,8 @@ __device__ __forceinline__ int slot_of_chunk(const int32_t* offs, int K, int c) 
 // All threads call.
 template <int NT>
 __device__ void slot_offsets(const StepDev& st, int q, int K, const int32_t* __restrict__ beam_rows,
-                             const float* __restrict__ acc, int wide_only, int32_t* co_s, int32_t* ho_s, int* red_i) {
+                             const float* __restrict__ acc, int wide_only, int32_t* co_s, int32_t* ho_s, int* red_i,
+                             int unc_v = 0) {
     constexpr int PER = (kMaxKRadix + NT - 1) / NT;
     const int k0 = threadIdx.x * PER;
     int n[PER];
@@ -107,7 +108,9 @@ __device__ void slot_offsets(const StepDev& st, int q, int K, const int32_t* __r
         if (k < K) {
             const int64_t b = (int64_t)q * K + k;
             const int32_t r = beam_rows[b];
-            if (beam_live(st, r, acc[b])) x = (int)(st.row_ptr[r + 1] - st.row_ptr[r]);
+            // a live beam's candidates: its row's valid tokens, or (no
+            // constraint) every token of the codebook
+            if (beam_live(st, r, acc[b])) x = unc_v ? unc_v : (int)(st.row_ptr[r + 1] - st.row_ptr[r]);
             // wide_only > 0: only the rows the per-query kernel reads scores for
             // (more than wide_only tokens, and every bitmap row)
             if (wide_only && st.store == CB_STORE_CSR && x <= wide_only) x = 0;
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
     __shared__ int red_i[kWThreads / kWave];
     const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
     if (w.use_done && w.done[q]) return;  // finished by the pre-pass (uniform over the workgroup)
-    slot_offsets<kWThreads>(st, q, K, beam_rows, acc, wide_only, co_s, ho_s, red_i);
+    slot_offsets<kWThreads>(st, q, K, beam_rows, acc, wide_only, co_s, ho_s, red_i, w.unc_v);
     if (g == 0 && wide_only) {
         int32_t* co = w.cand_off + (int64_t)q * (K + 1);
         for (int k = tid; k <= K; k += kWThreads) co[k] = co_s[k];
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
         const int n = co_s[k + 1] - co_s[k];
         const int j0 = (c - ho_s[k]) * kWCH;
         const int cnt = min(kWCH, n - j0);
-        if (tid < cnt) tok_s[tid] = (uint16_t)nth_token(st, r, e0, j0 + tid);
+        if (tid < cnt) tok_s[tid] = (uint16_t)(w.unc_v ? j0 + tid : nth_token(st, r, e0, j0 + tid));
         if (!DENSE && staged != k && n > 1) {
             for (int i = tid; i < d; i += kWThreads) h_s[i] = to_f32(hidden[b * d + i]);
             staged = k;
@@ -305,12 +308,45 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
                 const uint32_t c_ix = (uint32_t)(co_s[k] + j0 + tid);
                 const int64_t o = (int64_t)q * w.cap + c_ix;
                 w.cand[o] = ((uint64_t)__float_as_uint(z) << 32) | (uint64_t)(0xFFFFFFFFu - c_ix);
-                w.info[o] = ((uint64_t)(e0 + (uint32_t)(j0 + tid)) << 32) | ((uint64_t)tok_s[tid] << 16) |
-                            (uint64_t)k;
+                // next row: the edge position, or row 0 of the next table without a constraint
+                const uint32_t nxt = w.unc_v ? 0u : e0 + (uint32_t)(j0 + tid);
+                w.info[o] = ((uint64_t)nxt << 32) | ((uint64_t)tok_s[tid] << 16) | (uint64_t)k;
             }
         }
         __syncthreads();
     }
+}
+
+// Log-sum-exp of every live beam's whole score row, one wavefront per beam
+// (four per workgroup): the max, then the sum of exps, over the V columns of
+// the full-codebook scores (summed over the k-slices, if any, in slice
+// order).  Score first takes its softmax over the whole codebook.
+__global__ __launch_bounds__(256) void k_row_lse(StepDev st, int R, int V, int d, const float* __restrict__ Z,
+                                                 const float* __restrict__ Zp, const int32_t* __restrict__ n_live,
+                                                 const int32_t* __restrict__ ci_of, int split_ok,
+                                                 const int32_t* __restrict__ beam_rows,
+                                                 const float* __restrict__ acc, float* __restrict__ lse_row) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int b = blockIdx.x * 4 + threadIdx.x / kWave;
+    if (b >= R) return;  // uniform over the wave
+    if (!beam_live(st, beam_rows[b], acc[b])) {
+        if (lane == 0) lse_row[b] = -INFINITY;
+        return;
+    }
+    const int split = split_ok ? gemm_split(*n_live, V, d) : 1;
+    const float* zb = split == 1 ? Z + (int64_t)b * V : Zp + (int64_t)ci_of[b] * V;
+    auto zc = [&](int c) {
+        float z = 0.f;
+        for (int x = 0; x < split; ++x) z += zb[(int64_t)x * kSplitRows * V + c];
+        return z;
+    };
+    float m = -INFINITY;
+    for (int c = lane; c < V; c += kWave) m = fmaxf(m, zc(c));
+    m = wave_max(m);
+    float se = 0.f;
+    for (int c = lane; c < V; c += kWave) se += exp_sm(zc(c) - m);
+    se = wave_sum(se);
+    if (lane == 0) lse_row[b] = m + logf(se);
 }
 
 // Keys of every candidate (one chunk per wavefront): the beam's log-sum-exp
@@ -350,7 +386,8 @@ __global__ __launch_bounds__(kWThreads) void k_wide_keys(int K, const float* __r
         }
         const float M = wave_max(m);
         const float S = wave_sum(m == -INFINITY ? 0.f : s * exp_sm(m - M));
-        const float lse = M + logf(S);
+        // the softmax support: the candidates (their chunks), or (score first) the whole row
+        const float lse = w.lse_row ? w.lse_row[(int64_t)q * K + k] : M + logf(S);
         const float a = acc[(int64_t)q * K + k];
         const int j0 = (c - ho_s[k]) * kWCH;
         const int cnt = min(kWCH, co_s[k + 1] - co_s[k] - j0);
@@ -713,6 +750,15 @@ hipError_t launch_wide_small(const StepDev& st, int Q, int K, const int32_t* bea
                              const WideDev& w, int32_t* tok, int32_t* par, int32_t* rows, float* logp, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
     CB_LAUNCH(k_wide_small, dim3(Q), dim3(kSortThreads), 0, s, st, K, beam_rows, acc, w, tok, par, rows, logp);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_lse(const StepDev& st, cb_dtype dt, int R, int V, int d, const float* Z, const float* Zp,
+                          const int32_t* n_live, const int32_t* ci_of, const int32_t* beam_rows, const float* acc,
+                          float* lse_row, hipStream_t s) {
+    if (R <= 0) return hipSuccess;
+    CB_LAUNCH(k_row_lse, dim3((R + 3) / 4), dim3(256), 0, s, st, R, V, d, Z, Zp, n_live, ci_of,
+              dt == CB_BF16 ? 1 : 0, beam_rows, acc, lse_row);
     return hipGetLastError();
 }
 

@@ -188,15 +188,19 @@ cb_status cb_set_select(cb_plan* plan, int32_t t, cb_select select);
 /* The selection step t will use (never CB_SELECT_AUTO). */
 cb_status cb_get_select(const cb_plan* plan, int32_t t, cb_select* select);
 
-/* Set the decoding variant.  The score-first and unconstrained variants
- * need every step's full score row: all steps then take the dense path with
- * the LDS selection (cb_get_path reports CB_PATH_DENSE, cb_tune has nothing
- * to choose, sparse paths and the radix selection return CB_EUNSUPPORTED).
- * Errors: CB_EINVAL (unknown mode); CB_EUNSUPPORTED for K > 64, for a bf16
- * plan with d not a multiple of 64, for a step whose dense expansion does not
- * fit the LDS, and, unconstrained, for an f32 plan, V > 4096, V not a
- * multiple of 4, or min(K, V) beyond the plan's per-beam survivor count.
- * Synchronous with respect to the host. */
+/* Set the decoding variant (STATIC sec. 4.3: log-softmax over the whole
+ * codebook, then the mask — score first; ZeroGR summary, "Does it actually
+ * work better?": unconstrained decoding as the speed reference).  Both need
+ * every step's full score row: all steps take the dense path (cb_get_path
+ * reports CB_PATH_DENSE, cb_tune has nothing to choose, sparse paths return
+ * CB_EUNSUPPORTED).  A step takes the LDS selection where it holds the
+ * variant (K <= 64, rows that fit its LDS; unconstrained also a bf16 plan
+ * with V <= 4096, V a multiple of 4), else the radix selection, whose
+ * workspace is allocated here (unconstrained: K * V candidates per query).
+ * Errors: CB_EINVAL (unknown mode); CB_EUNSUPPORTED for a bf16 plan with d
+ * not a multiple of 64, a step forced to a sparse path or to an LDS
+ * selection that cannot hold the variant; CB_ECAPACITY, CB_ENOMEM from the
+ * radix workspace.  Synchronous with respect to the host. */
 cb_status cb_set_mode(cb_plan* plan, cb_mode mode);
 
 /* The plan's decoding variant. */
@@ -404,7 +408,8 @@ typedef enum {
     CB_KERNEL_RADIX_COLLECT = 11, /* radix selection: survivors */
     CB_KERNEL_RADIX_SORT = 12,    /* radix selection: survivors sorted, outputs and next rows */
     CB_KERNEL_DECODE_TAIL = 13,   /* persistent decode of the trailing sparse steps (step = first one) */
-    CB_KERNEL_RADIX_SMALL = 14    /* radix selection: pre-pass finishing the queries whose rows hold one token */
+    CB_KERNEL_RADIX_SMALL = 14,   /* radix selection: pre-pass finishing the queries whose rows hold one token */
+    CB_KERNEL_ROW_LSE = 15        /* score first on the radix selection: log-sum-exp of every whole score row */
 } cb_kernel;
 
 typedef struct {

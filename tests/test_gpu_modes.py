@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.parity import decode_vs_oracle, compare_step, logp_ok
+from tests.parity import decode_vs_oracle, compare_step, logp_ok, tolerance
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -98,17 +98,80 @@ def test_variant_argument_errors():
     cfg = w["cfg"]
     idx = cb.Index(w["items"], cfg.V, device=0)
     plan = idx.plan(cfg.Q, cfg.K, cfg.d, cfg.dtype)
+    plan.set_mode("unconstrained")  # f32 plan: every step on the radix selection
+    assert [plan.get_select(t) for t in range(cfg.L)] == ["radix"] * cfg.L
     with pytest.raises(cb.CbError):
-        plan.set_mode("unconstrained")  # f32 plan
+        plan.set_select(0, "lds")  # the LDS selection cannot hold it
     plan.set_mode("score_first")
+    assert plan.get_select(0) == "lds"
     with pytest.raises(cb.CbError):
         plan.set_path(0, "sparse")
-    with pytest.raises(cb.CbError):
-        plan.set_select(0, "radix")
+    plan.set_select(0, "radix")
+    assert plan.get_select(0) == "radix"
+    plan.set_select(0, "auto")
     plan.set_mode("filter_first")
     plan.set_path(0, "sparse")
     with pytest.raises(cb.CbError):
         plan.set_mode("score_first")  # a step forced sparse
     wide = idx.plan(cfg.Q, 128, cfg.d, cfg.dtype)
-    with pytest.raises(cb.CbError):
-        wide.set_mode("score_first")  # K > 64
+    wide.set_mode("score_first")  # K > 64: the radix selection
+    assert [wide.get_select(t) for t in range(cfg.L)] == ["radix"] * cfg.L
+
+
+WIDE_CASES = [("small", {"K": 100}, "score_first"), ("small", {"K": 100}, "unconstrained"),
+              ("tiny", {"K": 100}, "score_first"), ("tiny", {"V": 5003, "K": 16}, "unconstrained"),
+              ("tiny", {"V": 5003, "K": 16}, "score_first")]
+
+
+@pytest.mark.parametrize("name,over,mode", WIDE_CASES, ids=lambda x: str(x))
+def test_variant_wide(name, over, mode):
+    """The variants beyond the LDS selection: beam width 100 (radix selection
+    for every step), and a 5,003-token codebook (every token a candidate:
+    the radix selection; score first at K = 16: the LDS selection over a
+    gather of the valid columns).  Every step teacher forced against the
+    oracle's variant, then the free-running decode."""
+    w = workload(name, **over)
+    cfg, T = w["cfg"], w["T"]
+    ref = ref_decode(w, mode)
+    idx = cb.Index(w["items"], cfg.V, device=0)
+    plan = idx.plan(cfg.Q, cfg.K, cfg.d, cfg.dtype)
+    plan.set_mode(mode)
+    sels = [plan.get_select(t) for t in range(cfg.L)]
+    print("case", name, over, mode, "selections", sels, flush=True)
+    if cfg.K > 64 or (mode == "unconstrained" and cfg.V > 4096):
+        assert sels == ["radix"] * cfg.L
+    for t in range(cfg.L):
+        print("case", name, over, mode, "step", t, flush=True)
+        h, rows, acc = ref["trace_h"][t], ref["trace_rows_in"][t], ref["trace_acc_in"][t]
+        o = T.step(t, cfg.K, h, w["dense"]["W"][t], rows, acc, candidates=True, threads=8, mode=mode)
+        g = gpu_step(plan, t, to_dev_h(h, cfg), w["W"][t], torch.from_numpy(rows.astype(np.int32)).to(DEV),
+                     torch.from_numpy(acc).to(DEV))
+        ex, gap, fails = compare_step(o, g, cfg.K, cfg.dtype)
+        assert not fails, "\n".join(fails[:10])
+    q = torch.from_numpy(w["dense"]["q"]).to(DEV)
+    P = torch.from_numpy(w["dense"]["P"]).to(DEV)
+    out = plan.decode(q, P, w["W"], trace=True)
+    torch.cuda.synchronize()
+    seqs, logp, rows = (out[k].cpu().numpy() for k in ("seqs", "logp", "rows"))
+    if mode == "score_first":
+        rec = {"trace_rows": out["trace_rows"].cpu().numpy(), "rows": rows, "seqs": seqs}
+        vs = decode_vs_oracle(T, ref, rec, w["dense"]["W"], cfg.L, cfg.K, cfg.Q, mode=mode)
+        print("decode vs oracle:", vs, flush=True)
+        assert not vs["unexplained"], vs
+    else:
+        # without a catalog every row is 0, so divergences cannot be traced by
+        # rows: a query that differs must still end with the oracle's scores
+        # (near ties swap candidates of nearly equal score), each step having
+        # been checked exactly above
+        assert np.all(rows[logp > -np.inf] == 0)
+        rel, _ = tolerance(cfg.dtype)
+        same = 0
+        for i in range(cfg.Q):
+            sl = slice(i * cfg.K, (i + 1) * cfg.K)
+            if np.array_equal(seqs[sl], ref["seqs"][sl]):
+                same += 1
+                continue
+            a = np.sort(logp[sl].astype(np.float64))[::-1]
+            b = np.sort(ref["logp"][sl].astype(np.float64))[::-1]
+            assert np.all(np.abs(a - b) <= cfg.L * rel * np.maximum(1.0, np.abs(b))), (i, np.abs(a - b).max())
+        print("identical queries:", same, "of", cfg.Q, flush=True)

@@ -254,7 +254,7 @@ cb_status run_step_radix(cb_plan* p, int t, int Q, int32_t path, const void* hid
     // softmax over each beam's whole score row
     if (p->mode == CB_MODE_UNCONSTRAINED) w.unc_v = idx->V;
     if (p->mode == CB_MODE_SCORE_FIRST) {
-        ProfMark m(p, s, t, CB_KERNEL_ROW_LSE, 256, (R + 3) / 4);
+        ProfMark m(p, s, t, CB_KERNEL_ROW_LSE, 256, R);
         e = launch_row_lse(sd, p->dtype, R, idx->V, p->d, p->Z, p->Zp, p->n_live, p->ci_of, rows, acc, p->lse_row, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: row log-sum-exp", e);

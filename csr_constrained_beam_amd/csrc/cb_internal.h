@@ -276,7 +276,7 @@ hipError_t launch_wide_small(const StepDev& st, int Q, int K, const int32_t* bea
                              const WideDev& w, int32_t* tok, int32_t* par, int32_t* rows, float* logp, hipStream_t s);
 hipError_t launch_wide_keys(int Q, int K, const float* acc, const WideDev& w, hipStream_t s);
 // Score first on the radix path: the log-sum-exp of each live beam's whole
-// score row (the softmax support of the variant), one wave per beam.
+// score row (the softmax support of the variant), one workgroup per beam.
 hipError_t launch_row_lse(const StepDev& st, cb_dtype dt, int R, int V, int d, const float* Z, const float* Zp,
                           const int32_t* n_live, const int32_t* ci_of, const int32_t* beam_rows, const float* acc,
                           float* lse_row, hipStream_t s);

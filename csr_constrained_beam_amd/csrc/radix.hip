@@ -317,36 +317,79 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
     }
 }
 
-// Log-sum-exp of every live beam's whole score row, one wavefront per beam
-// (four per workgroup): the max, then the sum of exps, over the V columns of
-// the full-codebook scores (summed over the k-slices, if any, in slice
-// order).  Score first takes its softmax over the whole codebook.
+// Log-sum-exp of every live beam's whole score row, one workgroup of 256 per
+// beam.  Thread tid keeps a running (max, sum of exps) over the columns
+// tid + 256 i, taken eight columns at a time (summed over the k-slices, if
+// any, in slice order) so that eight loads are in flight per thread; the 256
+// pairs are then combined in thread order.  Score first takes its softmax over
+// the whole codebook.
+template <bool SPLIT>
+__device__ __forceinline__ void row_lse_scan(const float* __restrict__ zb, int V, int split, int64_t sstride,
+                                             int tid, float& m, float& sm) {
+    constexpr int U = 8;
+    for (int c0 = tid; c0 < V; c0 += 256 * U) {
+        float z[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + 256 * u;
+            z[u] = -INFINITY;
+            if (c < V) z[u] = zb[c];
+        }
+        if (SPLIT) {
+            for (int x = 1; x < split; ++x) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + 256 * u;
+                    if (c < V) z[u] += zb[x * sstride + c];
+                }
+            }
+        }
+        float mx = z[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) mx = fmaxf(mx, z[u]);
+        const float mn = fmaxf(m, mx);  // finite: column c0 < V is in range
+        float s = sm * exp_sm(m - mn);
+#pragma unroll
+        for (int u = 0; u < U; ++u) s += exp_sm(z[u] - mn);  // columns past V add exp(-inf) = 0
+        m = mn;
+        sm = s;
+    }
+}
+
 __global__ __launch_bounds__(256) void k_row_lse(StepDev st, int R, int V, int d, const float* __restrict__ Z,
                                                  const float* __restrict__ Zp, const int32_t* __restrict__ n_live,
                                                  const int32_t* __restrict__ ci_of, int split_ok,
                                                  const int32_t* __restrict__ beam_rows,
                                                  const float* __restrict__ acc, float* __restrict__ lse_row) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int b = blockIdx.x * 4 + threadIdx.x / kWave;
-    if (b >= R) return;  // uniform over the wave
-    if (!beam_live(st, beam_rows[b], acc[b])) {
-        if (lane == 0) lse_row[b] = -INFINITY;
+    __shared__ float pm[256], ps[256];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    if (!beam_live(st, beam_rows[b], acc[b])) {  // uniform over the workgroup
+        if (tid == 0) lse_row[b] = -INFINITY;
         return;
     }
     const int split = split_ok ? gemm_split(*n_live, V, d) : 1;
     const float* zb = split == 1 ? Z + (int64_t)b * V : Zp + (int64_t)ci_of[b] * V;
-    auto zc = [&](int c) {
-        float z = 0.f;
-        for (int x = 0; x < split; ++x) z += zb[(int64_t)x * kSplitRows * V + c];
-        return z;
-    };
-    float m = -INFINITY;
-    for (int c = lane; c < V; c += kWave) m = fmaxf(m, zc(c));
-    m = wave_max(m);
-    float se = 0.f;
-    for (int c = lane; c < V; c += kWave) se += exp_sm(zc(c) - m);
-    se = wave_sum(se);
-    if (lane == 0) lse_row[b] = m + logf(se);
+    float m = -INFINITY, sm = 0.f;
+    if (split == 1)
+        row_lse_scan<false>(zb, V, 1, 0, tid, m, sm);
+    else
+        row_lse_scan<true>(zb, V, split, (int64_t)kSplitRows * V, tid, m, sm);
+    pm[tid] = m;
+    ps[tid] = sm;
+    __syncthreads();
+    if (tid < kWave) {
+        // lane l combines the pairs l, l + 64, l + 128, l + 192, then the wave
+        float M = pm[tid];
+        for (int x = 1; x < 4; ++x) M = fmaxf(M, pm[tid + 64 * x]);
+        float S = 0.f;
+        for (int x = 0; x < 4; ++x) {
+            const float mx = pm[tid + 64 * x];
+            S += mx == -INFINITY ? 0.f : ps[tid + 64 * x] * exp_sm(mx - M);
+        }
+        const float MM = wave_max(M);
+        S = wave_sum(M == -INFINITY ? 0.f : S * exp_sm(M - MM));
+        if (tid == 0) lse_row[b] = MM + logf(S);
+    }
 }
 
 // Keys of every candidate (one chunk per wavefront): the beam's log-sum-exp
@@ -757,8 +800,8 @@ hipError_t launch_row_lse(const StepDev& st, cb_dtype dt, int R, int V, int d, c
                           const int32_t* n_live, const int32_t* ci_of, const int32_t* beam_rows, const float* acc,
                           float* lse_row, hipStream_t s) {
     if (R <= 0) return hipSuccess;
-    CB_LAUNCH(k_row_lse, dim3((R + 3) / 4), dim3(256), 0, s, st, R, V, d, Z, Zp, n_live, ci_of,
-              dt == CB_BF16 ? 1 : 0, beam_rows, acc, lse_row);
+    CB_LAUNCH(k_row_lse, dim3(R), dim3(256), 0, s, st, R, V, d, Z, Zp, n_live, ci_of, dt == CB_BF16 ? 1 : 0,
+              beam_rows, acc, lse_row);
     return hipGetLastError();
 }
 

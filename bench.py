@@ -318,8 +318,9 @@ def main():
                 # radix path: candidates written to HBM as 8-byte keys
                 "radix_score_sparse": R * 8 + idx_bytes + w_bytes + n_exp * 8 + chunks * 8,
                 "radix_score_dense": R * 8 + idx_bytes + n_exp * 4 + n_exp * 8 + chunks * 8,
-                # score first: every live beam's whole score row, once
-                "row_lse": len(live) * V * 4 + R * 12,
+                # score first: every live beam's whole score row, once; unconstrained:
+                # the chunk pairs of the score pass
+                "row_lse": (chunks * 8 + R * 4 if args.mode == "unconstrained" else len(live) * V * 4 + R * 12),
                 "radix_keys": n_exp * 16 + chunks * 8 + len(live) * 4,
                 "radix_refine": n_exp * 8,
                 "radix_collect": n_exp * 8,

@@ -220,7 +220,9 @@ cb_status run_step_radix(cb_plan* p, int t, int Q, int32_t path, const void* hid
         set_error("cb_step: radix workspace missing");
         return CB_EINVAL;
     }
-    const int GS = wide_blocks_per_query(Q) * Q, GH = wide_hist_blocks_per_query(Q) * Q;
+    // candidates a query can hold: K rows of the widest row (every token without a constraint)
+    const int64_t kb = (int64_t)p->K * (p->mode == CB_MODE_UNCONSTRAINED ? idx->V : std::max(idx->steps[(size_t)t].S, 1));
+    const int GS = wide_blocks_per_query(Q) * Q, GH = wide_hist_blocks(Q, kb) * Q;
     const bool dense = path == CB_PATH_DENSE;
     hipError_t e;
     // the one-token pre-pass (sparse scoring only): queries whose live rows
@@ -267,21 +269,30 @@ cb_status run_step_radix(cb_plan* p, int t, int Q, int32_t path, const void* hid
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: radix scores", e);
     }
+    if (p->mode == CB_MODE_UNCONSTRAINED) {
+        // a beam's candidates are its whole row: its log-sum-exp once, from
+        // the chunk pairs, not again for each of its chunks
+        ProfMark m(p, s, t, CB_KERNEL_ROW_LSE, 256, (R + 3) / 4);
+        e = launch_chunk_lse(Q, p->K, w, p->lse_row, s);
+        m.done();
+        if (e != hipSuccess) return hip_fail("cb_step: row log-sum-exp", e);
+        w.lse_row = p->lse_row;
+    }
     {
         ProfMark m(p, s, t, CB_KERNEL_RADIX_KEYS, 256, GH);
-        e = launch_wide_keys(Q, p->K, acc, w, s);
+        e = launch_wide_keys(Q, p->K, kb, acc, w, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: radix keys", e);
     }
     {
         ProfMark m(p, s, t, CB_KERNEL_RADIX_REFINE, 256, GH);
-        e = launch_wide_refine(Q, p->K, w, s);
+        e = launch_wide_refine(Q, p->K, kb, w, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: radix refine", e);
     }
     {
         ProfMark m(p, s, t, CB_KERNEL_RADIX_COLLECT, 256, GH);
-        e = launch_wide_collect(Q, p->K, w, s);
+        e = launch_wide_collect(Q, p->K, kb, w, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: radix collect", e);
     }

@@ -120,7 +120,7 @@ struct WideDev {
     int32_t* done = nullptr;       // [Q_max] 1: the pre-pass (k_wide_small) wrote the query's outputs
     int32_t use_done = 0;          // the kernels skip the queries marked done (set when the pre-pass ran)
     int32_t unc_v = 0;             // unconstrained decoding: every one of the unc_v tokens is a candidate
-    const float* lse_row = nullptr;  // score first: [R] log-sum-exp of each beam's whole score row
+    const float* lse_row = nullptr;  // variants: [R] log-sum-exp of each beam's whole score row
     int64_t cap = 0, chunk_cap = 0;
 };
 }  // namespace cb
@@ -144,7 +144,7 @@ struct cb_plan {
     uint64_t* keys = nullptr;     // [Q_max*K][Kc_max] per-beam survivors (dense path, per-beam sparse form)
     uint64_t* side = nullptr;     // [Q_max*K][Kc_max] their next row << 16 | token (per-beam expansion)
     float* qz = nullptr;          // [Q_max][K*64 + S_max] scores handed between a query's workgroups
-    float* lse_row = nullptr;     // [Q_max*K] whole-row log-sum-exp (score first on the radix path)
+    float* lse_row = nullptr;     // [Q_max*K] whole-row log-sum-exp (the variants on the radix path)
     int32_t* qcnt = nullptr;      // [Q_max] their arrival counts (zero between launches)
     float* Z = nullptr;           // [Q_max*K][V] full-codebook scores (dense path)
     float* Zp = nullptr;          // [k-slices][rows][V] partial scores (dense path, few live beams)
@@ -264,6 +264,9 @@ int wide_surv_cap();
 size_t wide_sel_bytes();
 int wide_blocks_per_query(int Q);
 int wide_hist_blocks_per_query(int Q);
+// Workgroups launched per query by the histogram kernels, for queries of up to
+// keys_bound candidates (each kernel uses as many as its actual count needs).
+int wide_hist_blocks(int Q, int64_t keys_bound);
 size_t wide_score_lds_bytes(int d, bool dense);
 hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, int K, int d, const void* hidden,
                              const void* W, const float* Z, const float* Zp, int64_t ldz, const int32_t* n_live,
@@ -274,14 +277,17 @@ hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, 
 // and leaves the others to the radix kernels (done[q] = 0).
 hipError_t launch_wide_small(const StepDev& st, int Q, int K, const int32_t* beam_rows, const float* acc,
                              const WideDev& w, int32_t* tok, int32_t* par, int32_t* rows, float* logp, hipStream_t s);
-hipError_t launch_wide_keys(int Q, int K, const float* acc, const WideDev& w, hipStream_t s);
+hipError_t launch_wide_keys(int Q, int K, int64_t keys_bound, const float* acc, const WideDev& w, hipStream_t s);
 // Score first on the radix path: the log-sum-exp of each live beam's whole
 // score row (the softmax support of the variant), one workgroup per beam.
 hipError_t launch_row_lse(const StepDev& st, cb_dtype dt, int R, int V, int d, const float* Z, const float* Zp,
                           const int32_t* n_live, const int32_t* ci_of, const int32_t* beam_rows, const float* acc,
                           float* lse_row, hipStream_t s);
-hipError_t launch_wide_refine(int Q, int K, const WideDev& w, hipStream_t s);
-hipError_t launch_wide_collect(int Q, int K, const WideDev& w, hipStream_t s);
+// Unconstrained decoding on the radix path: each live beam's log-sum-exp over
+// all its candidates, once per beam from the chunk pairs of the score pass.
+hipError_t launch_chunk_lse(int Q, int K, const WideDev& w, float* lse_row, hipStream_t s);
+hipError_t launch_wide_refine(int Q, int K, int64_t keys_bound, const WideDev& w, hipStream_t s);
+hipError_t launch_wide_collect(int Q, int K, int64_t keys_bound, const WideDev& w, hipStream_t s);
 hipError_t launch_wide_sort(const StepDev& st, int Q, int K, const int32_t* beam_rows, const WideDev& w,
                             int32_t* tok, int32_t* par, int32_t* rows, float* logp, hipStream_t s);
 

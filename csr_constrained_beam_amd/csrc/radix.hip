@@ -255,8 +255,52 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
         }
     }
     const int nch = ho_s[K];
-    int split = 1;
-    if (DENSE && split_ok) split = gemm_split(*n_live, (int)ldz, d);
+    if constexpr (DENSE) {
+        // full-codebook scores: one chunk per wavefront, each lane reading its
+        // token's column of the score row (no staging, no workgroup barrier)
+        const int split = split_ok ? gemm_split(*n_live, (int)ldz, d) : 1;
+        const int lane = tid & (kWave - 1);
+        constexpr int NWV = kWThreads / kWave;
+        for (int c = g * NWV + tid / kWave; c < nch; c += G * NWV) {
+            const int k = slot_of_chunk(ho_s, K, c);
+            const int64_t b = (int64_t)q * K + k;
+            int32_t r = 0;
+            uint32_t e0 = 0;
+            if (!w.unc_v) {  // without a constraint the tokens are the columns
+                r = beam_rows[b];
+                e0 = st.row_ptr[r];
+            }
+            const int j0 = (c - ho_s[k]) * kWCH;
+            const int cnt = min(kWCH, co_s[k + 1] - co_s[k] - j0);
+            int v = 0;
+            float z = -INFINITY;
+            if (lane < cnt) {
+                v = w.unc_v ? j0 + lane : nth_token(st, r, e0, j0 + lane);
+                if (split == 1) {
+                    z = Z[b * ldz + v];
+                } else {
+                    const float* zb = Zp + (int64_t)ci_of[b] * ldz + v;
+                    z = 0.f;
+                    for (int x = 0; x < split; ++x) z += zb[(int64_t)x * kSplitRows * ldz];
+                }
+            }
+            const float m = wave_max(z);
+            const float sm = wave_sum(lane < cnt ? exp_sm(z - m) : 0.f);
+            if (lane == 0) {
+                float* p = w.cms + ((int64_t)q * w.chunk_cap + c) * 2;
+                p[0] = m;
+                p[1] = sm;
+            }
+            if (lane < cnt) {
+                const uint32_t c_ix = (uint32_t)(co_s[k] + j0 + lane);
+                const int64_t o = (int64_t)q * w.cap + c_ix;
+                w.cand[o] = ((uint64_t)__float_as_uint(z) << 32) | (uint64_t)(0xFFFFFFFFu - c_ix);
+                const uint32_t nxt = w.unc_v ? 0u : e0 + (uint32_t)(j0 + lane);
+                w.info[o] = ((uint64_t)nxt << 32) | ((uint64_t)v << 16) | (uint64_t)k;
+            }
+        }
+        return;
+    }
     int staged = -1;
     for (int c = g; c < nch; c += G) {
         const int k = slot_of_chunk(ho_s, K, c);
@@ -267,26 +311,14 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
         const int j0 = (c - ho_s[k]) * kWCH;
         const int cnt = min(kWCH, n - j0);
         if (tid < cnt) tok_s[tid] = (uint16_t)(w.unc_v ? j0 + tid : nth_token(st, r, e0, j0 + tid));
-        if (!DENSE && staged != k && n > 1) {
+        if (staged != k && n > 1) {
             for (int i = tid; i < d; i += kWThreads) h_s[i] = to_f32(hidden[b * d + i]);
             staged = k;
         }
         __syncthreads();
-        if (!DENSE && n == 1) {
+        if (n == 1) {
             // one valid token: log-softmax 0 whatever the score (no reads)
             if (tid == 0) z_s[0] = 0.f;
-        } else if (DENSE) {
-            if (tid < cnt) {
-                const int v = tok_s[tid];
-                float z = 0.f;
-                if (split == 1) {
-                    z = Z[b * ldz + v];
-                } else {
-                    const float* zb = Zp + (int64_t)ci_of[b] * ldz + v;
-                    for (int x = 0; x < split; ++x) z += zb[(int64_t)x * kSplitRows * ldz];
-                }
-                z_s[tid] = z;
-            }
         } else if constexpr (CH > 0) {
             // every W_t row chunk of 16 tokens per wave in flight at once (the
             // chunk's 64 tokens in one round trip at d <= 1024 bf16)
@@ -392,10 +424,64 @@ __global__ __launch_bounds__(256) void k_row_lse(StepDev st, int R, int V, int d
     }
 }
 
+// Workgroups of a histogram kernel that take part for a query of n keys: the
+// base count, more (up to the G launched) where each would hold more than
+// kHistKeys keys; the others leave at once.
+constexpr int kHistKeys = 16384;
+__device__ __forceinline__ int hist_blocks_used(int G, int Gb, int n) {
+    return min(G, max(Gb, (n + kHistKeys - 1) / kHistKeys));
+}
+
+// LDS histogram increment by the lanes in `on`, one atomic per distinct bin
+// of the wavefront (keys of one chunk mostly share their top digit).  All
+// lanes of the wavefront call.
+__device__ __forceinline__ void wave_hist_add(uint32_t* hs, uint32_t bin, bool on) {
+    uint64_t todo = __ballot(on);
+    while (todo) {
+        const int lead = __ffsll((unsigned long long)todo) - 1;
+        const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, lead);
+        const uint64_t same = __ballot(on && bin == lb);
+        if ((int)(threadIdx.x & (kWave - 1)) == lead) atomicAdd(&hs[lb], (uint32_t)__popcll(same));
+        todo &= ~same;
+    }
+}
+
+// Running (max, sum of exps) over the chunk pairs x, x + 64, ... below end.
+__device__ __forceinline__ void chunk_pairs(const float* __restrict__ cms, int x, int end, float& m, float& s) {
+    for (; x < end; x += kWave) {
+        const float cm = cms[2 * x], cs = cms[2 * x + 1];
+        if (cm > m) {
+            s = s * exp_sm(m - cm) + cs;
+            m = cm;
+        } else {
+            s += cs * exp_sm(cm - m);
+        }
+    }
+}
+
+// Unconstrained decoding: each live beam's log-sum-exp over its candidates
+// (the whole codebook row), combined once from its chunks' pairs, one
+// wavefront per beam; dead beams (no chunks) get -inf.
+__global__ __launch_bounds__(256) void k_chunk_lse(int Q, int K, WideDev w, float* __restrict__ lse_row) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int b = blockIdx.x * (256 / kWave) + (int)threadIdx.x / kWave;
+    if (b >= Q * K) return;  // uniform over the wavefront
+    const int q = b / K, k = b - q * K;
+    if (w.use_done && w.done[q]) return;
+    const int32_t* ho = w.chunk_off + (int64_t)q * (K + 1);
+    const int h0 = ho[k], h1 = ho[k + 1];
+    float m = -INFINITY, s = 0.f;
+    chunk_pairs(w.cms + (int64_t)q * w.chunk_cap * 2, h0 + lane, h1, m, s);
+    const float M = wave_max(m);
+    const float S = wave_sum(m == -INFINITY ? 0.f : s * exp_sm(m - M));
+    if (lane == 0) lse_row[b] = h1 > h0 ? M + logf(S) : -INFINITY;
+}
+
 // Keys of every candidate (one chunk per wavefront): the beam's log-sum-exp
 // from its chunks, score = acc + (z - lse) in float32, and the histogram of
 // the keys' top digit.
-__global__ __launch_bounds__(kWThreads) void k_wide_keys(int K, const float* __restrict__ acc, WideDev w, int G) {
+__global__ __launch_bounds__(kWThreads) void k_wide_keys(int K, const float* __restrict__ acc, WideDev w, int G,
+                                                         int Gb) {
     __shared__ __align__(16) uint32_t hs[kRBins];
     __shared__ int32_t co_s[kMaxKRadix + 1], ho_s[kMaxKRadix + 1];
     const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
@@ -403,6 +489,8 @@ __global__ __launch_bounds__(kWThreads) void k_wide_keys(int K, const float* __r
     const int lane = tid & (kWave - 1), wv = tid / kWave;
     constexpr int NWV = kWThreads / kWave;
     const WideSel* sel = reinterpret_cast<const WideSel*>(w.sel) + q;
+    const int GE = hist_blocks_used(G, Gb, sel->n_cand);
+    if (g >= GE) return;  // uniform over the workgroup
     const bool pending = sel->state == kSelPending;  // uniform over the query's workgroups
     for (int i = tid; i < kRBins; i += kWThreads) hs[i] = 0;
     const int32_t* co = w.cand_off + (int64_t)q * (K + 1);
@@ -415,33 +503,31 @@ __global__ __launch_bounds__(kWThreads) void k_wide_keys(int K, const float* __r
     const int nch = ho_s[K];
     const float* cms = w.cms + (int64_t)q * w.chunk_cap * 2;
     uint64_t* cq = w.cand + (int64_t)q * w.cap;
-    for (int c = g * NWV + wv; c < nch; c += G * NWV) {
+    for (int c = g * NWV + wv; c < nch; c += GE * NWV) {
         const int k = slot_of_chunk(ho_s, K, c);
-        float m = -INFINITY, s = 0.f;
-        for (int x = ho_s[k] + lane; x < ho_s[k + 1]; x += kWave) {
-            const float cm = cms[2 * x], cs = cms[2 * x + 1];
-            if (cm > m) {
-                s = s * exp_sm(m - cm) + cs;
-                m = cm;
-            } else {
-                s += cs * exp_sm(cm - m);
-            }
+        // the softmax support: the candidates (their chunks' pairs), or the
+        // per-beam value of the variants (the whole row)
+        float lse;
+        if (w.lse_row) {
+            lse = w.lse_row[(int64_t)q * K + k];
+        } else {
+            float m = -INFINITY, s = 0.f;
+            chunk_pairs(cms, ho_s[k] + lane, ho_s[k + 1], m, s);
+            const float M = wave_max(m);
+            lse = M + logf(wave_sum(m == -INFINITY ? 0.f : s * exp_sm(m - M)));
         }
-        const float M = wave_max(m);
-        const float S = wave_sum(m == -INFINITY ? 0.f : s * exp_sm(m - M));
-        // the softmax support: the candidates (their chunks), or (score first) the whole row
-        const float lse = w.lse_row ? w.lse_row[(int64_t)q * K + k] : M + logf(S);
         const float a = acc[(int64_t)q * K + k];
         const int j0 = (c - ho_s[k]) * kWCH;
         const int cnt = min(kWCH, co_s[k + 1] - co_s[k] - j0);
+        uint64_t key = 0;
         if (lane < cnt) {
             uint64_t* p = cq + co_s[k] + j0 + lane;
             const uint64_t v = *p;
             const float z = __uint_as_float((uint32_t)(v >> 32));
-            const uint64_t key = ((uint64_t)score_order_bits(a + (z - lse)) << 32) | (v & 0xFFFFFFFFull);
+            key = ((uint64_t)score_order_bits(a + (z - lse)) << 32) | (v & 0xFFFFFFFFull);
             *p = key;
-            if (pending) atomicAdd(&hs[key >> (64 - kRBits)], 1u);
         }
+        if (pending) wave_hist_add(hs, (uint32_t)(key >> (64 - kRBits)), lane < cnt);
     }
     if (!pending) return;
     __syncthreads();
@@ -452,7 +538,7 @@ __global__ __launch_bounds__(kWThreads) void k_wide_keys(int K, const float* __r
 
 // Second digit, over the keys that share the first (queries the first digit
 // left open).
-__global__ __launch_bounds__(kWThreads) void k_wide_refine(int K, WideDev w, int G) {
+__global__ __launch_bounds__(kWThreads) void k_wide_refine(int K, WideDev w, int G, int Gb) {
     __shared__ __align__(16) uint32_t hs[kRBins];
     __shared__ int red_i[kWThreads / kWave];
     __shared__ int pick[3];
@@ -461,15 +547,27 @@ __global__ __launch_bounds__(kWThreads) void k_wide_refine(int K, WideDev w, int
     const WideSel* sel = reinterpret_cast<const WideSel*>(w.sel) + q;
     if (sel->state != kSelPending) return;  // uniform over the query's workgroups
     const int n = sel->n_cand;
+    const int GE = hist_blocks_used(G, Gb, n);
+    if (g >= GE) return;
     const SelView v = resolve_digits<kWThreads>(w, q, K, n, 1, hs, red_i, pick);
     if (v.state != kSelPending) return;
     for (int i = tid; i < kRBins; i += kWThreads) hs[i] = 0;
     __syncthreads();
     const uint64_t pre = v.prefix >> (64 - kRBits);
     const uint64_t* cq = w.cand + (int64_t)q * w.cap;
-    for (int i = g * kWThreads + tid; i < n; i += G * kWThreads) {
-        const uint64_t key = cq[i];
-        if ((key >> (64 - kRBits)) == pre) atomicAdd(&hs[(key >> (64 - 2 * kRBits)) & (kRBins - 1)], 1u);
+    // four keys per thread in flight
+    const int stride = GE * kWThreads;
+    for (int i0 = g * kWThreads + tid; i0 < n; i0 += 4 * stride) {
+        uint64_t k4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * stride;
+            k4[u] = i < n ? cq[i] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (i0 + u * stride < n && (k4[u] >> (64 - kRBits)) == pre)
+                atomicAdd(&hs[(k4[u] >> (64 - 2 * kRBits)) & (kRBins - 1)], 1u);
     }
     __syncthreads();
     uint32_t* h2 = w.hist + (int64_t)q * 2 * kRBins + kRBins;
@@ -479,7 +577,7 @@ __global__ __launch_bounds__(kWThreads) void k_wide_refine(int K, WideDev w, int
 
 // Survivors (keys >= the query's threshold) appended to the query's list;
 // the query's first workgroup records the resolved selection for the sort.
-__global__ __launch_bounds__(kWThreads) void k_wide_collect(int K, WideDev w, int G) {
+__global__ __launch_bounds__(kWThreads) void k_wide_collect(int K, WideDev w, int G, int Gb) {
     __shared__ __align__(16) uint32_t hs[kRBins];
     __shared__ int red_i[kWThreads / kWave];
     __shared__ int pick[3];
@@ -489,6 +587,8 @@ __global__ __launch_bounds__(kWThreads) void k_wide_collect(int K, WideDev w, in
     WideSel* sel = reinterpret_cast<WideSel*>(w.sel) + q;
     const int n = sel->n_cand;
     if (n <= K) return;  // every candidate survives (sel->state is rewritten below, so not read here)
+    const int GE = hist_blocks_used(G, Gb, n);
+    if (g >= GE) return;
     const SelView v = resolve_digits<kWThreads>(w, q, K, n, 2, hs, red_i, pick);
     if (g == 0 && tid == 0) {
         sel->prefix = v.prefix;
@@ -499,17 +599,26 @@ __global__ __launch_bounds__(kWThreads) void k_wide_collect(int K, WideDev w, in
     const uint64_t thr = v.prefix;  // every key >= the prefix with zero low bits survives
     const uint64_t* cq = w.cand + (int64_t)q * w.cap;
     uint64_t* out = w.surv + (int64_t)q * kSurvCap;
-    for (int i0 = g * kWThreads; i0 < n; i0 += G * kWThreads) {
-        const int i = i0 + tid;
-        const uint64_t key = i < n ? cq[i] : 0ull;
-        const bool take = i < n && key >= thr;
-        const uint64_t mask = __ballot(take);
-        int base = 0;
-        if (lane == 0 && mask) base = atomicAdd(&w.surv_n[q], (int)__popcll(mask));
-        base = lane_bcast(base, 0);
-        if (take) {
-            const int pos = base + (int)__popcll(mask & ((1ull << lane) - 1ull));
-            if (pos < kSurvCap) out[pos] = key;
+    // four keys per thread in flight; i0 is uniform over the workgroup
+    const int stride = GE * kWThreads;
+    for (int i0 = g * kWThreads; i0 < n; i0 += 4 * stride) {
+        uint64_t k4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * stride + tid;
+            k4[u] = i < n ? cq[i] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool take = i0 + u * stride + tid < n && k4[u] >= thr;
+            const uint64_t mask = __ballot(take);
+            int base = 0;
+            if (lane == 0 && mask) base = atomicAdd(&w.surv_n[q], (int)__popcll(mask));
+            base = lane_bcast(base, 0);
+            if (take) {
+                const int pos = base + (int)__popcll(mask & ((1ull << lane) - 1ull));
+                if (pos < kSurvCap) out[pos] = k4[u];
+            }
         }
     }
 }
@@ -758,6 +867,12 @@ size_t wide_sel_bytes() { return sizeof(WideSel); }
 // to 1024 workgroups; the histogram kernels use up to 256 (one per CU).
 int wide_blocks_per_query(int Q) { return Q >= 2048 ? 1 : (2048 / (Q > 0 ? Q : 1) > 1024 ? 1024 : 2048 / Q); }
 int wide_hist_blocks_per_query(int Q) { return Q >= 256 ? 1 : 256 / (Q > 0 ? Q : 1); }
+int wide_hist_blocks(int Q, int64_t keys_bound) {
+    const int base = wide_hist_blocks_per_query(Q);
+    const int cap = std::max(base, 2048 / std::max(Q, 1));
+    const int64_t want = (keys_bound + kHistKeys - 1) / kHistKeys;
+    return (int)std::min<int64_t>(cap, std::max<int64_t>(base, want));
+}
 size_t wide_score_lds_bytes(int d, bool dense) { return dense ? 0 : (size_t)d * 4; }
 
 hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, int K, int d, const void* hidden,
@@ -805,24 +920,31 @@ hipError_t launch_row_lse(const StepDev& st, cb_dtype dt, int R, int V, int d, c
     return hipGetLastError();
 }
 
-hipError_t launch_wide_keys(int Q, int K, const float* acc, const WideDev& w, hipStream_t s) {
+hipError_t launch_chunk_lse(int Q, int K, const WideDev& w, float* lse_row, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
-    const int G = wide_hist_blocks_per_query(Q);
-    CB_LAUNCH(k_wide_keys, dim3(Q * G), dim3(kWThreads), 0, s, K, acc, w, G);
+    CB_LAUNCH(k_chunk_lse, dim3((Q * K + 3) / 4), dim3(256), 0, s, Q, K, w, lse_row);
     return hipGetLastError();
 }
 
-hipError_t launch_wide_refine(int Q, int K, const WideDev& w, hipStream_t s) {
+hipError_t launch_wide_keys(int Q, int K, int64_t keys_bound, const float* acc, const WideDev& w,
+                            hipStream_t s) {
     if (Q <= 0) return hipSuccess;
-    const int G = wide_hist_blocks_per_query(Q);
-    CB_LAUNCH(k_wide_refine, dim3(Q * G), dim3(kWThreads), 0, s, K, w, G);
+    const int G = wide_hist_blocks(Q, keys_bound), Gb = wide_hist_blocks_per_query(Q);
+    CB_LAUNCH(k_wide_keys, dim3(Q * G), dim3(kWThreads), 0, s, K, acc, w, G, Gb);
     return hipGetLastError();
 }
 
-hipError_t launch_wide_collect(int Q, int K, const WideDev& w, hipStream_t s) {
+hipError_t launch_wide_refine(int Q, int K, int64_t keys_bound, const WideDev& w, hipStream_t s) {
     if (Q <= 0) return hipSuccess;
-    const int G = wide_hist_blocks_per_query(Q);
-    CB_LAUNCH(k_wide_collect, dim3(Q * G), dim3(kWThreads), 0, s, K, w, G);
+    const int G = wide_hist_blocks(Q, keys_bound), Gb = wide_hist_blocks_per_query(Q);
+    CB_LAUNCH(k_wide_refine, dim3(Q * G), dim3(kWThreads), 0, s, K, w, G, Gb);
+    return hipGetLastError();
+}
+
+hipError_t launch_wide_collect(int Q, int K, int64_t keys_bound, const WideDev& w, hipStream_t s) {
+    if (Q <= 0) return hipSuccess;
+    const int G = wide_hist_blocks(Q, keys_bound), Gb = wide_hist_blocks_per_query(Q);
+    CB_LAUNCH(k_wide_collect, dim3(Q * G), dim3(kWThreads), 0, s, K, w, G, Gb);
     return hipGetLastError();
 }
 

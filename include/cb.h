@@ -409,7 +409,8 @@ typedef enum {
     CB_KERNEL_RADIX_SORT = 12,    /* radix selection: survivors sorted, outputs and next rows */
     CB_KERNEL_DECODE_TAIL = 13,   /* persistent decode of the trailing sparse steps (step = first one) */
     CB_KERNEL_RADIX_SMALL = 14,   /* radix selection: pre-pass finishing the queries whose rows hold one token */
-    CB_KERNEL_ROW_LSE = 15        /* score first on the radix selection: log-sum-exp of every whole score row */
+    CB_KERNEL_ROW_LSE = 15        /* variants on the radix selection: log-sum-exp of every whole score row
+                                     (score first: over the scores; unconstrained: over the chunk pairs) */
 } cb_kernel;
 
 typedef struct {

@@ -120,7 +120,10 @@ def test_variant_argument_errors():
 
 WIDE_CASES = [("small", {"K": 100}, "score_first"), ("small", {"K": 100}, "unconstrained"),
               ("tiny", {"K": 100}, "score_first"), ("tiny", {"V": 5003, "K": 16}, "unconstrained"),
-              ("tiny", {"V": 5003, "K": 16}, "score_first")]
+              ("tiny", {"V": 5003, "K": 16}, "score_first"),
+              # 5M candidates in one query at step 1: the histogram kernels
+              # take more workgroups than their base count
+              ("tiny", {"V": 5003, "K": 1000, "Q": 1}, "unconstrained")]
 
 
 @pytest.mark.parametrize("name,over,mode", WIDE_CASES, ids=lambda x: str(x))

@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--paths", default=None,
                     help="comma-separated path per step (dense/sparse/sparse_split), no tuning: replays a tuned "
                          "choice without the tuning launches (profiler runs)")
+    ap.add_argument("--radix-scoring", default="tuned", choices=["tuned", "chunk", "token"],
+                    help="sparse scoring of the radix-selection steps: as tuned, per beam chunk, or by token")
     ap.add_argument("--mode", default="filter_first", choices=["filter_first", "score_first", "unconstrained"],
                     help="decoding variant (the last two run the dense path)")
     ap.add_argument("--json-out", default=None)
@@ -219,12 +221,16 @@ def main():
     elif args.path in ("dense", "sparse"):
         for t in range(cfg.L):
             plan.set_path(t, args.path)
+    if args.radix_scoring != "tuned":
+        for t in range(cfg.L):
+            plan.set_option(t, "token_major", 2 if args.radix_scoring == "token" else 1)
     paths = [plan.get_path(t) for t in range(cfg.L)]
     forms = [plan.get_option(t, "sparse_form") for t in range(cfg.L)]
     qsplits = [plan.get_option(t, "query_split") for t in range(cfg.L)]
+    tmajor = [plan.get_option(t, "token_major") for t in range(cfg.L)]
     nthreads = [plan.get_option(t, "step_threads") for t in range(cfg.L)]
     log("paths per step:", paths, "sparse form per step (1: per beam):", forms, "workgroups per query:", qsplits,
-        "threads:", nthreads)
+        "threads:", nthreads, "radix scoring (2: by token):", tmajor)
 
     # free-running decode: records every step's inputs; also times the full decode
     rec = plan.decode(q, P, W, trace=True)
@@ -303,6 +309,7 @@ def main():
         w_bytes = live_scored * d * es + len(toks_scored) * d * es  # hidden vectors and distinct W_t rows
         steps.append({
             "t": t, "path": paths[t], "sparse_form": forms[t], "query_split": qsplits[t], "step_threads": nthreads[t],
+            "token_major": tmajor[t],
             "storage": info[t]["storage"], "live_beams": int(len(live)),
             "expansions": n_exp, "max_fanout": S, "mean_fanout": float(fan.mean()) if len(fan) else 0.0,
             "valid_fraction": n_exp / max(1, len(live) * V), "distinct_tokens": len(toks),
@@ -318,9 +325,13 @@ def main():
                 # radix path: candidates written to HBM as 8-byte keys
                 "radix_score_sparse": R * 8 + idx_bytes + w_bytes + n_exp * 8 + chunks * 8,
                 "radix_score_dense": R * 8 + idx_bytes + n_exp * 4 + n_exp * 8 + chunks * 8,
-                # score first: every live beam's whole score row, once; unconstrained:
+                # scores by token: counting sort of the candidates (ranks, lists, offsets),
+                # then each distinct W_t row and each scored beam's hidden vector once
+                "token_lists": R * 8 + idx_bytes + n_exp * 32 + V * 16,
+                "token_score": w_bytes + n_scored * 16,
+                # score first: every live beam's whole score row, once; otherwise
                 # the chunk pairs of the score pass
-                "row_lse": (chunks * 8 + R * 4 if args.mode == "unconstrained" else len(live) * V * 4 + R * 12),
+                "row_lse": (len(live) * V * 4 + R * 12 if args.mode == "score_first" else chunks * 8 + R * 4),
                 "radix_keys": n_exp * 16 + chunks * 8 + len(live) * 4,
                 "radix_refine": n_exp * 8,
                 "radix_collect": n_exp * 8,

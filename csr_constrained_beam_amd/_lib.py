@@ -16,7 +16,7 @@ CB_PATH_AUTO, CB_PATH_DENSE, CB_PATH_SPARSE, CB_PATH_SPARSE_SPLIT = 0, 1, 2, 3
 CB_STORE_AUTO, CB_STORE_CSR, CB_STORE_BITMAP = 0, 1, 2
 CB_SELECT_AUTO, CB_SELECT_LDS, CB_SELECT_RADIX = 0, 1, 2
 STEP_OPTIONS = {"step_threads": 0, "split_rows": 1, "sparse_form": 2, "dense_rows": 3, "radix_prepass": 4,
-                "query_split": 5}
+                "query_split": 5, "token_major": 6}
 
 STATUS_NAMES = {0: "CB_OK", -1: "CB_EINVAL", -2: "CB_ENOMEM", -3: "CB_EHIP", -4: "CB_EUNSUPPORTED",
                 -5: "CB_ECAPACITY"}
@@ -45,7 +45,7 @@ class PhaseTime(ctypes.Structure):
 KERNEL_NAMES = {0: "gemm_bf16", 1: "gemm_f32", 2: "expand_sparse", 3: "expand_dense", 4: "merge",
                 5: "step_query", 6: "live_rows", 7: "radix_score_sparse", 8: "radix_score_dense",
                 9: "radix_keys", 10: "radix_refine", 11: "radix_collect", 12: "radix_sort",
-                13: "decode_tail", 14: "radix_small", 15: "row_lse"}
+                13: "decode_tail", 14: "radix_small", 15: "row_lse", 16: "token_lists", 17: "token_score"}
 
 SIGNATURES = {
     "cb_build_index": (ctypes.c_int, [_P, _I64, _I32, _I32, _I32, _I32, _PP]),

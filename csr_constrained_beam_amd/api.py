@@ -189,7 +189,8 @@ class Plan:
     def set_option(self, t, option, value):
         """Force a form of step t's kernels (cb_set_step_option): option is
         one of "step_threads", "split_rows", "sparse_form", "dense_rows",
-        "radix_prepass", "query_split"; 0 restores the default."""
+        "radix_prepass", "query_split", "token_major"; 0 restores the
+        default."""
         C.check("cb_set_step_option", self._lib.cb_set_step_option(self._h, int(t), C.STEP_OPTIONS[option],
                                                                     int(value)))
 

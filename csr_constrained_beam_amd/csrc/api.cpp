@@ -151,6 +151,59 @@ void wide_release(cb_plan* p) {
     dev_free(w.done);
     w = WideDev();
     p->wide_S = 0;
+    cb::TokDev& tk = p->tok;
+    dev_free(tk.count);
+    dev_free(tk.off);
+    dev_free(tk.units);
+    dev_free(tk.n_units);
+    dev_free(tk.rank);
+    dev_free(tk.list);
+    tk = cb::TokDev();
+    p->tok_n = 0;
+    p->tok_dirty = false;
+}
+
+// Token-major workspace for the radix workspace's capacity (which must exist).
+cb_status tok_alloc(cb_plan* p) {
+    const int64_t n = (int64_t)p->Q_max * p->wide.cap;
+    if (p->tok.list && p->tok_n >= n) return CB_OK;
+    if (n >= (int64_t(1) << 31)) {
+        set_error("token-major scoring: Q_max * K * widest row exceeds 2^31 candidates");
+        return CB_ECAPACITY;
+    }
+    const int V = p->idx->V;
+    cb::TokDev& tk = p->tok;
+    dev_free(tk.count);
+    dev_free(tk.off);
+    dev_free(tk.units);
+    dev_free(tk.n_units);
+    dev_free(tk.rank);
+    dev_free(tk.list);
+    tk = cb::TokDev();
+    p->tok_n = 0;
+    cb_status st = dev_alloc(&tk.count, (size_t)V, "token counts");
+    if (st == CB_OK) st = dev_alloc(&tk.off, (size_t)V + 1, "token offsets");
+    if (st == CB_OK) st = dev_alloc(&tk.units, (size_t)tm_unit_cap(n, V), "token units");
+    if (st == CB_OK) st = dev_alloc(&tk.n_units, 1, "token unit count");
+    if (st == CB_OK) st = dev_alloc(&tk.rank, (size_t)n, "token ranks");
+    if (st == CB_OK) st = dev_alloc(&tk.list, (size_t)n, "token lists");
+    if (st == CB_OK) {
+        const hipError_t e = hipMemset(tk.count, 0, (size_t)V * sizeof(int32_t));
+        if (e != hipSuccess) st = hip_fail("token counts", e);
+    }
+    if (st != CB_OK) {
+        dev_free(tk.count);
+        dev_free(tk.off);
+        dev_free(tk.units);
+        dev_free(tk.n_units);
+        dev_free(tk.rank);
+        dev_free(tk.list);
+        tk = cb::TokDev();
+        return st;
+    }
+    p->tok_n = n;
+    p->tok_dirty = false;
+    return CB_OK;
 }
 
 // Radix-selection workspace sized for the plan's widest row.
@@ -190,6 +243,9 @@ cb_status wide_alloc(cb_plan* p) {
         return st;
     }
     p->wide_S = S;
+    // a step set to score by token keeps its workspace sized with this one
+    for (const int32_t v : p->radix_tm)
+        if (v == 2) return tok_alloc(p);
     return CB_OK;
 }
 
@@ -262,16 +318,61 @@ cb_status run_step_radix(cb_plan* p, int t, int Q, int32_t path, const void* hid
         if (e != hipSuccess) return hip_fail("cb_step: row log-sum-exp", e);
         w.lse_row = p->lse_row;
     }
-    {
+    const cb::StepTable& T = idx->steps[(size_t)t];
+    if (!dense && opt(p->radix_tm, t) == 2 && p->d <= kQueryMaxD) {
+        // scores by token: each W_t row read once for all the beams that hold it
+        cb_status st = tok_alloc(p);
+        if (st != CB_OK) return st;
+        const cb::TokDev& tk = p->tok;
+        if (p->tok_dirty) {
+            e = launch_tm_clear(idx->V, tk, s);
+            if (e != hipSuccess) return hip_fail("cb_step: token counts", e);
+        }
+        p->tok_dirty = true;
+        {
+            ProfMark m(p, s, t, CB_KERNEL_TOKEN_LISTS, 256, GS);
+            e = launch_tm_count(sd, Q, p->K, rows, acc, w, tk, s);
+            m.done();
+            if (e != hipSuccess) return hip_fail("cb_step: token counts", e);
+        }
+        {
+            ProfMark m(p, s, t, CB_KERNEL_TOKEN_LISTS, 1024, 1);
+            e = launch_tm_scan(idx->V, tk, s);
+            m.done();
+            if (e != hipSuccess) return hip_fail("cb_step: token offsets", e);
+        }
+        p->tok_dirty = false;
+        {
+            ProfMark m(p, s, t, CB_KERNEL_TOKEN_LISTS, 256, GS);
+            e = launch_tm_scatter(Q, p->K, w, tk, s);
+            m.done();
+            if (e != hipSuccess) return hip_fail("cb_step: token lists", e);
+        }
+        {
+            ProfMark m(p, s, t, CB_KERNEL_TOKEN_SCORE, 256, tm_score_blocks());
+            e = launch_tm_score(p->dtype, p->K, p->d, hidden, Wt, w, tk, s);
+            m.done();
+            if (e != hipSuccess) return hip_fail("cb_step: scores by token", e);
+        }
+        {
+            ProfMark m(p, s, t, CB_KERNEL_TOKEN_SCORE, 256, GH);
+            e = launch_tm_pairs(Q, p->K, kb, w, s);
+            m.done();
+            if (e != hipSuccess) return hip_fail("cb_step: chunk softmax pairs", e);
+        }
+    } else {
         ProfMark m(p, s, t, dense ? CB_KERNEL_RADIX_SCORE_DENSE : CB_KERNEL_RADIX_SCORE_SPARSE, 256, GS);
         e = launch_wide_score(sd, dense, p->dtype, Q, p->K, p->d, hidden, Wt, p->Z, p->Zp, idx->V, p->n_live,
                               p->ci_of, rows, acc, 0, w, s);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: radix scores", e);
     }
-    if (p->mode == CB_MODE_UNCONSTRAINED) {
-        // a beam's candidates are its whole row: its log-sum-exp once, from
-        // the chunk pairs, not again for each of its chunks
+    if (!w.lse_row && (p->mode == CB_MODE_UNCONSTRAINED ||
+                       (p->mode == CB_MODE_FILTER_FIRST &&
+                        T.n_edges > (int64_t)kChunkLseTokens * std::max<int64_t>(T.n_rows, 1)))) {
+        // rows of many chunks on average (every token without a constraint,
+        // or wide rows): each beam's log-sum-exp once, from its chunk pairs,
+        // not again for each of its chunks
         ProfMark m(p, s, t, CB_KERNEL_ROW_LSE, 256, (R + 3) / 4);
         e = launch_chunk_lse(Q, p->K, w, p->lse_row, s);
         m.done();
@@ -676,6 +777,7 @@ cb_status cb_plan_create(cb_index* idx, int32_t Q_max, int32_t K, int32_t d, cb_
     p->query_nt.assign((size_t)idx->L, 0);
     p->gemm_rows.assign((size_t)idx->L, 0);
     p->radix_pre.assign((size_t)idx->L, 0);
+    p->radix_tm.assign((size_t)idx->L, 0);
     p->split_min.assign((size_t)idx->L, 0);
     p->sparse_form.assign((size_t)idx->L, 0);
     p->query_split.assign((size_t)idx->L, 0);
@@ -887,6 +989,21 @@ cb_status cb_set_step_option(cb_plan* p, int32_t t, cb_step_option o, int32_t va
             if (value != 0 && value != 1 && value != 2 && value != 4) break;
             p->query_split[(size_t)t] = value;
             return CB_OK;
+        case CB_OPT_TOKEN_MAJOR: {
+            if (value < 0 || value > 2) break;
+            if (value == 2) {
+                if (p->d > kQueryMaxD) {
+                    set_error("cb_set_step_option: scores by token hold W_t rows of at most 2048 elements");
+                    return CB_EINVAL;
+                }
+                DeviceGuard g(p->idx->device);
+                cb_status st = wide_alloc(p);
+                if (st == CB_OK) st = tok_alloc(p);
+                if (st != CB_OK) return st;
+            }
+            p->radix_tm[(size_t)t] = value;
+            return CB_OK;
+        }
     }
     set_error("cb_set_step_option: unknown option or value out of range");
     return CB_EINVAL;
@@ -909,6 +1026,7 @@ cb_status cb_get_step_option(const cb_plan* p, int32_t t, cb_step_option o, int3
         case CB_OPT_DENSE_ROWS: *value = gemm_full(p, t) ? 2 : 1; return CB_OK;
         case CB_OPT_RADIX_PREPASS: *value = p->radix_pre[(size_t)t] == 1 ? 1 : 2; return CB_OK;
         case CB_OPT_QUERY_SPLIT: *value = p->query_split[(size_t)t] > 1 ? p->query_split[(size_t)t] : 1; return CB_OK;
+        case CB_OPT_TOKEN_MAJOR: *value = p->radix_tm[(size_t)t] == 2 ? 2 : 1; return CB_OK;
     }
     set_error("cb_get_step_option: unknown option");
     return CB_EINVAL;
@@ -1016,7 +1134,7 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
             float best_us[2] = {-1.f, -1.f};  // dense, sparse (either variant): best over the selections
             float best = -1.f;
             int32_t best_path = 0, best_sel = 0, best_nt = 0, best_rows = 0, best_pre = 0, best_min = 0, best_form = 0,
-                    best_split = 0;
+                    best_split = 0, best_tm = 0;
             const int32_t paths[3] = {CB_PATH_DENSE, CB_PATH_SPARSE, CB_PATH_SPARSE_SPLIT};
             const int32_t sels[2] = {CB_SELECT_LDS, CB_SELECT_RADIX};
             const cb::StepTable& T = idx->steps[(size_t)t];
@@ -1052,18 +1170,28 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
                     const int mins[4] = {kPreMin, kPreMin, 1, 1};
                     // and the plain sparse path with two and four workgroups per query
                     const bool qsplit_var = paths[k] == CB_PATH_SPARSE && per_query;
+                    // and the radix selection's sparse scoring by token (with the pre-pass)
+                    bool tm_var = pre_var && p->d <= kQueryMaxD;
+                    if (tm_var && tok_alloc(p) != CB_OK) {
+                        (void)hipGetLastError();
+                        clear_error();
+                        tm_var = false;
+                    }
                     const int nv0 = split_var ? 4 : per_query || rows_var || pre_var ? 2 : 1;
                     const int nv1 = nv0 + (form_var ? 1 : 0);
-                    const int nv = nv1 + (qsplit_var ? 2 : 0);
+                    const int nv2 = nv1 + (qsplit_var ? 2 : 0);
+                    const int nv = nv2 + (tm_var ? 1 : 0);
                     for (int v = 0; v < nv && st == CB_OK; ++v) {
                         const bool beam_form = form_var && v == nv0;
-                        const int qs = v >= nv1 ? (v == nv1 ? 2 : 4) : 0;
+                        const bool by_token = tm_var && v == nv2;
+                        const int qs = v >= nv1 && v < nv2 ? (v == nv1 ? 2 : 4) : 0;
                         p->sparse_form[(size_t)t] = beam_form ? 1 : 0;
                         p->query_split[(size_t)t] = qs;
                         p->query_nt[(size_t)t] = per_query && !beam_form && v < nv0 ? nts[v] : 0;
                         p->split_min[(size_t)t] = split_var ? mins[v] : 0;
                         p->gemm_rows[(size_t)t] = rows_var ? 1 + v : 0;
-                        p->radix_pre[(size_t)t] = pre_var && !beam_form ? 1 + v : 0;
+                        p->radix_pre[(size_t)t] = by_token ? 2 : pre_var && !beam_form ? 1 + v : 0;
+                        p->radix_tm[(size_t)t] = by_token ? 2 : 0;
                         st = run_step(p, t, Q, paths[k], sels[m], p->h, Wt, p->rows[cur], p->acc[cur],
                                       p->scratch_tok, p->scratch_par, p->scratch_rows, p->scratch_logp, s);
                         if (st != CB_OK) break;
@@ -1091,8 +1219,10 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
                             best_min = p->split_min[(size_t)t];
                             best_form = p->sparse_form[(size_t)t];
                             best_split = p->query_split[(size_t)t];
+                            best_tm = p->radix_tm[(size_t)t];
                         }
                     }
+                    p->radix_tm[(size_t)t] = 0;
                     p->query_nt[(size_t)t] = 0;
                     p->split_min[(size_t)t] = 0;
                     p->gemm_rows[(size_t)t] = 0;
@@ -1112,6 +1242,7 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
             p->split_min[(size_t)t] = best_min;
             p->sparse_form[(size_t)t] = best_form;
             p->query_split[(size_t)t] = best_split;
+            p->radix_tm[(size_t)t] = best_tm;
         }
         st = run_step(p, t, Q, resolve_path(p, t), resolve_select(p, t), p->h, Wt, p->rows[cur], p->acc[cur],
                       p->hist_tok + (size_t)t * R, p->hist_par + (size_t)t * R, p->rows[1 - cur], p->acc[1 - cur], s);

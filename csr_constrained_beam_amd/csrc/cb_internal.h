@@ -99,6 +99,9 @@ constexpr int kMaxK = 64;            // beam width held by the per-query selecti
 constexpr int kQueryMaxD = 2048;     // hidden width the fused per-query sparse step holds in registers
                                      // (wider: per-beam expansion + per-query merge, or the radix path)
 constexpr int kMaxKRadix = 1024;     // beam width of the radix-select path (10-bit parent field of a key)
+constexpr int kChunkLseTokens = 2048;  // radix path: steps whose rows hold more tokens on average get each
+                                       // beam's log-sum-exp in a pass of its own (else the keys kernel
+                                       // combines a beam's chunk pairs again for every chunk)
 constexpr int kMaxLds = 65536;       // LDS one workgroup may use
 constexpr int kPreMin = 16;          // split sparse path: rows above this many tokens scored apart, unless measured
 constexpr int kExpandThreads = 256;  // per-beam expansion workgroup
@@ -122,6 +125,17 @@ struct WideDev {
     int32_t unc_v = 0;             // unconstrained decoding: every one of the unc_v tokens is a candidate
     const float* lse_row = nullptr;  // variants: [R] log-sum-exp of each beam's whole score row
     int64_t cap = 0, chunk_cap = 0;
+};
+
+// Workspace of the token-major scoring of the radix path's sparse steps (the
+// candidates grouped by token: a counting sort per step).
+struct TokDev {
+    int32_t* count = nullptr;    // [V] candidates per token (zero between steps)
+    int32_t* off = nullptr;      // [V + 1] first entry of each token
+    int2* units = nullptr;       // [unit cap] (token | entries << 16, first entry): at most 16 entries of one token
+    int32_t* n_units = nullptr;  // [1]
+    int32_t* rank = nullptr;     // [Q_max][cap] rank among the token's entries (-1: not scored)
+    uint2* list = nullptr;       // [Q_max * cap] (candidate, beam) grouped by token
 };
 }  // namespace cb
 
@@ -154,6 +168,10 @@ struct cb_plan {
     std::vector<int32_t> select;  // per step: CB_SELECT_* set by the caller
     std::vector<int32_t> tuned_select;  // per step: measured choice (0 = none)
     cb::WideDev wide;             // radix-select workspace (allocated when a step may use it)
+    cb::TokDev tok;               // token-major scoring workspace (allocated when a step may use it)
+    int64_t tok_n = 0;            // candidates the token-major workspace holds (Q_max * cap)
+    bool tok_dirty = false;       // per-token counts possibly left nonzero (a step stopped between its kernels)
+    std::vector<int32_t> radix_tm; // per step: radix sparse scoring per chunk (1, default) or by token (2), 0 = default
     int32_t wide_S = 0;           // widest row the radix workspace was sized for
     // decode state
     float* s[2] = {nullptr, nullptr};    // [R][d] float32 state vectors
@@ -272,6 +290,20 @@ hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, 
                              const void* W, const float* Z, const float* Zp, int64_t ldz, const int32_t* n_live,
                              const int32_t* ci_of, const int32_t* beam_rows, const float* acc, int wide_only,
                              const WideDev& w, hipStream_t s);
+// Token-major scoring (sparse steps on the radix selection, d <= 2048): the
+// candidates' tokens and ranks per token, the per-token offsets and work units,
+// the lists, the scores by token, then the chunk pairs of the scores.
+hipError_t launch_tm_count(const StepDev& st, int Q, int K, const int32_t* beam_rows, const float* acc,
+                           const WideDev& w, const TokDev& tk, hipStream_t s);
+hipError_t launch_tm_scan(int V, const TokDev& tk, hipStream_t s);
+hipError_t launch_tm_scatter(int Q, int K, const WideDev& w, const TokDev& tk, hipStream_t s);
+hipError_t launch_tm_score(cb_dtype dt, int K, int d, const void* hidden, const void* W, const WideDev& w,
+                           const TokDev& tk, hipStream_t s);
+hipError_t launch_tm_pairs(int Q, int K, int64_t keys_bound, const WideDev& w, hipStream_t s);
+hipError_t launch_tm_clear(int V, const TokDev& tk, hipStream_t s);
+int tm_score_blocks();
+int64_t tm_unit_cap(int64_t n, int V);
+
 // Pre-pass of the radix selection: one workgroup per query finishes every
 // query whose live rows all hold one token (outputs written, done[q] = 1)
 // and leaves the others to the radix kernels (done[q] = 0).

@@ -56,6 +56,14 @@ constexpr int kSortThreads = 1024;
 
 enum : int32_t { kSelPending = 0, kSelThreshold = 1, kSelUnresolved = 2, kSelAll = 3 };
 
+// Workgroups of a histogram kernel that take part for a query of n keys: the
+// base count, more (up to the G launched) where each would hold more than
+// kHistKeys keys; the others leave at once.
+constexpr int kHistKeys = 16384;
+__device__ __forceinline__ int hist_blocks_used(int G, int Gb, int n) {
+    return min(G, max(Gb, (n + kHistKeys - 1) / kHistKeys));
+}
+
 // Per query, written by the scoring kernel (n_cand, state) and by the collect
 // kernel (the resolved selection) for the sort kernel.
 struct WideSel {
@@ -206,30 +214,13 @@ __device__ SelView resolve_digits(const WideDev& w, int q, int K, int n_cand, in
     return v;
 }
 
-// Scores of every candidate, one chunk per workgroup iteration: z (sparse
-// gather-dot against the beam's hidden vector staged in LDS, or the
-// full-codebook score of the column), stored as z's bits over the key's low
-// half (parent, token), and the chunk's (max, sum exp).  Every workgroup
-// derives the slot offsets itself; the query's first one also publishes them
-// and resets the query's selection state for the kernels that follow.
-// CH: hidden width in 512-element chunks held in registers by the scoring
-// loop (1, 2 or 4: d <= 512 * CH), or 0 for any width (one chunk at a time).
-template <typename DT, bool DENSE, int CH>
-__global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int d, const DT* __restrict__ hidden,
-                                                          const DT* __restrict__ W, const float* __restrict__ Z,
-                                                          const float* __restrict__ Zp, int64_t ldz,
-                                                          const int32_t* __restrict__ n_live,
-                                                          const int32_t* __restrict__ ci_of, int split_ok,
-                                                          const int32_t* __restrict__ beam_rows,
-                                                          const float* __restrict__ acc, int wide_only, WideDev w,
-                                                          int G) {
-    extern __shared__ __align__(16) float h_s[];  // [d], sparse scoring only
-    __shared__ float z_s[kWCH];
-    __shared__ uint16_t tok_s[kWCH];
-    __shared__ int32_t co_s[kMaxKRadix + 1], ho_s[kMaxKRadix + 1];
-    __shared__ int red_i[kWThreads / kWave];
-    const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
-    if (w.use_done && w.done[q]) return;  // finished by the pre-pass (uniform over the workgroup)
+// Start of a scoring pass over query q (every workgroup g of the query): the
+// slot offsets into co_s / ho_s; the query's first workgroup also publishes
+// them and resets the query's selection state for the kernels that follow.
+__device__ void wide_prologue(const StepDev& st, int q, int g, int K, const int32_t* __restrict__ beam_rows,
+                              const float* __restrict__ acc, int wide_only, const WideDev& w, int32_t* co_s,
+                              int32_t* ho_s, int* red_i) {
+    const int tid = threadIdx.x;
     slot_offsets<kWThreads>(st, q, K, beam_rows, acc, wide_only, co_s, ho_s, red_i, w.unc_v);
     if (g == 0 && wide_only) {
         int32_t* co = w.cand_off + (int64_t)q * (K + 1);
@@ -254,6 +245,33 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
             w.surv_n[q] = 0;
         }
     }
+}
+
+// Scores of every candidate, one chunk per workgroup iteration: z (sparse
+// gather-dot against the beam's hidden vector staged in LDS, or the
+// full-codebook score of the column), stored as z's bits over the key's low
+// half (parent, token), and the chunk's (max, sum exp).  Every workgroup
+// derives the slot offsets itself; the query's first one also publishes them
+// and resets the query's selection state for the kernels that follow.
+// CH: hidden width in 512-element chunks held in registers by the scoring
+// loop (1, 2 or 4: d <= 512 * CH), or 0 for any width (one chunk at a time).
+template <typename DT, bool DENSE, int CH>
+__global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int d, const DT* __restrict__ hidden,
+                                                          const DT* __restrict__ W, const float* __restrict__ Z,
+                                                          const float* __restrict__ Zp, int64_t ldz,
+                                                          const int32_t* __restrict__ n_live,
+                                                          const int32_t* __restrict__ ci_of, int split_ok,
+                                                          const int32_t* __restrict__ beam_rows,
+                                                          const float* __restrict__ acc, int wide_only, WideDev w,
+                                                          int G) {
+    extern __shared__ __align__(16) float h_s[];  // [d], sparse scoring only
+    __shared__ float z_s[kWCH];
+    __shared__ uint16_t tok_s[kWCH];
+    __shared__ int32_t co_s[kMaxKRadix + 1], ho_s[kMaxKRadix + 1];
+    __shared__ int red_i[kWThreads / kWave];
+    const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
+    if (w.use_done && w.done[q]) return;  // finished by the pre-pass (uniform over the workgroup)
+    wide_prologue(st, q, g, K, beam_rows, acc, wide_only, w, co_s, ho_s, red_i);
     const int nch = ho_s[K];
     if constexpr (DENSE) {
         // full-codebook scores: one chunk per wavefront, each lane reading its
@@ -349,6 +367,211 @@ __global__ __launch_bounds__(kWThreads) void k_wide_score(StepDev st, int K, int
     }
 }
 
+// Token-major scoring of a sparse step.  The per-chunk scoring above stages a
+// beam's hidden vector and gathers one W_t row per candidate, so a token held
+// by many beams has its row fetched once per beam.  Here the candidates are
+// grouped by token (a counting sort: count, scan, scatter), and each token's
+// row is read once into registers and dotted with the hidden vectors of the
+// beams that hold it (2 KB each at d = 1024 bf16, hit in L2 across the beam's
+// tokens).  The work is cut into units of up to kTmUnit entries of one token,
+// so that a token held by every beam does not serialise one wavefront.
+constexpr int kTmUnit = 16;
+
+// Slot offsets (published as by k_wide_score), every candidate's token, next
+// row and parent slot, and its rank among its token's candidates (one atomic
+// on the token's count); the candidate of a one-token row has log-softmax 0
+// whatever its score, so it is written at once (z = 0) and takes no rank.
+__global__ __launch_bounds__(kWThreads) void k_tm_count(StepDev st, int K, const int32_t* __restrict__ beam_rows,
+                                                        const float* __restrict__ acc, WideDev w, TokDev tk, int G) {
+    __shared__ int32_t co_s[kMaxKRadix + 1], ho_s[kMaxKRadix + 1];
+    __shared__ int red_i[kWThreads / kWave];
+    const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
+    if (w.use_done && w.done[q]) return;  // uniform over the workgroup
+    wide_prologue(st, q, g, K, beam_rows, acc, 0, w, co_s, ho_s, red_i);
+    const int nch = ho_s[K];
+    const int lane = tid & (kWave - 1);
+    constexpr int NWV = kWThreads / kWave;
+    for (int c = g * NWV + tid / kWave; c < nch; c += G * NWV) {
+        const int k = slot_of_chunk(ho_s, K, c);
+        const int32_t r = beam_rows[(int64_t)q * K + k];
+        const uint32_t e0 = st.row_ptr[r];
+        const int n = co_s[k + 1] - co_s[k];
+        const int j0 = (c - ho_s[k]) * kWCH;
+        if (lane < min(kWCH, n - j0)) {
+            const int v = nth_token(st, r, e0, j0 + lane);
+            const uint32_t c_ix = (uint32_t)(co_s[k] + j0 + lane);
+            const int64_t o = (int64_t)q * w.cap + c_ix;
+            w.info[o] = ((uint64_t)(e0 + (uint32_t)(j0 + lane)) << 32) | ((uint64_t)v << 16) | (uint64_t)k;
+            if (n == 1) {
+                w.cand[o] = (uint64_t)(0xFFFFFFFFu - c_ix);  // z = +0.0
+                tk.rank[o] = -1;
+            } else {
+                tk.rank[o] = atomicAdd(&tk.count[v], 1);
+            }
+        }
+    }
+}
+
+// Exclusive prefix sums of the per-token counts (first list entry of each
+// token) and of their units; the unit table (token and entry count in .x,
+// first entry in .y) and the number of units; the counts are cleared for the
+// next step.  One workgroup; thread i takes the PER tokens from i * PER on,
+// loaded 4 at a time, all loads in flight before any is used.
+template <int PER>
+__global__ __launch_bounds__(1024) void k_tm_scan(int V, TokDev tk) {
+    __shared__ int red_i[1024 / kWave];
+    const int v0 = (int)threadIdx.x * PER;
+    int c[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i += 4) {
+        if (v0 + i + 4 <= V) {
+            const int4 x = *reinterpret_cast<const int4*>(tk.count + v0 + i);
+            c[i] = x.x;
+            c[i + 1] = x.y;
+            c[i + 2] = x.z;
+            c[i + 3] = x.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c[i + e] = v0 + i + e < V ? tk.count[v0 + i + e] : 0;
+        }
+    }
+    int se = 0, su = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        se += c[i];
+        su += (c[i] + kTmUnit - 1) / kTmUnit;
+    }
+    int te, tu;
+    int oe = block_exclusive_scan<1024>(se, red_i, &te);
+    int ou = block_exclusive_scan<1024>(su, red_i, &tu);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int v = v0 + i;
+        if (v < V) {
+            tk.off[v] = oe;
+            tk.count[v] = 0;
+            for (int x = 0; x < c[i]; x += kTmUnit) tk.units[ou++] = make_int2(v | (min(kTmUnit, c[i] - x) << 16), oe + x);
+            oe += c[i];
+        }
+    }
+    if (threadIdx.x == 0) {
+        tk.off[V] = te;
+        *tk.n_units = tu;
+    }
+}
+
+// Every candidate that takes a rank into its token's entries: entry
+// off[v] + rank = (candidate, beam).
+__global__ __launch_bounds__(kWThreads) void k_tm_scatter(int K, WideDev w, TokDev tk, int G) {
+    const int q = blockIdx.x / G, g = blockIdx.x % G;
+    if (w.use_done && w.done[q]) return;
+    const int n = reinterpret_cast<const WideSel*>(w.sel)[q].n_cand;
+    const int64_t base = (int64_t)q * w.cap;
+    for (int i = g * kWThreads + (int)threadIdx.x; i < n; i += G * kWThreads) {
+        const int rk = tk.rank[base + i];
+        if (rk < 0) continue;
+        const uint64_t inf = w.info[base + i];
+        const int v = (int)((inf >> 16) & 0xFFFFu), k = (int)(inf & 0xFFFFu);
+        tk.list[tk.off[v] + rk] = make_uint2((uint32_t)(base + i), (uint32_t)(q * K + k));
+    }
+}
+
+// Scores by token: one wavefront per unit holds the token's W_t row in
+// registers (lane l: elements 512 c + 8 l ... + 7), loads the unit's entries
+// one per lane, and takes them eight at a time (their hidden rows all in
+// flight), each a dot product with the entry's beam's hidden vector (fp32
+// products and sums, the wavefront's butterfly last); the candidate's key
+// half gets z's bits.
+template <typename DT, int CH>
+__global__ __launch_bounds__(kWThreads) void k_tm_score(int K, int d, const DT* __restrict__ hidden,
+                                                        const DT* __restrict__ W, WideDev w, TokDev tk) {
+    constexpr int NWV = kWThreads / kWave;
+    constexpr int U = 8;
+    static_assert(kTmUnit <= kWave, "a unit's entries are held one per lane");
+    const int lane = threadIdx.x & (kWave - 1);
+    const int nu = *tk.n_units;
+    for (int u = blockIdx.x * NWV + (int)threadIdx.x / kWave; u < nu; u += gridDim.x * NWV) {
+        const int2 un = tk.units[u];
+        const int v = un.x & 0xFFFF, cnt = un.x >> 16, e0 = un.y;
+        const uint2 mine = tk.list[e0 + min(lane, cnt - 1)];
+        float wr[CH][8];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int i = c * kWave * 8 + lane * 8;
+            if (i < d) load8(W + (int64_t)v * d + i, wr[c]);
+            else
+#pragma unroll
+                for (int x = 0; x < 8; ++x) wr[c][x] = 0.f;
+        }
+        for (int j = 0; j < cnt; j += U) {
+            uint32_t ex[U], eb[U];
+#pragma unroll
+            for (int x = 0; x < U; ++x) {
+                const int jj = min(j + x, cnt - 1);  // uniform over the wavefront
+                ex[x] = (uint32_t)__builtin_amdgcn_readlane((int)mine.x, jj);
+                eb[x] = (uint32_t)__builtin_amdgcn_readlane((int)mine.y, jj);
+            }
+            Raw8<DT> h[U][CH];
+#pragma unroll
+            for (int x = 0; x < U; ++x)
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const int i = c * kWave * 8 + lane * 8;
+                    if (i < d) h[x][c].load(hidden + (int64_t)eb[x] * d + i);
+                    else h[x][c].zero();
+                }
+#pragma unroll
+            for (int x = 0; x < U; ++x) {
+                float sv = 0.f;
+#pragma unroll
+                for (int c = 0; c < CH; ++c) sv = h[x][c].dot(wr[c], sv);
+                const float z = wave_sum(sv);
+                if (lane == 0 && j + x < cnt) {
+                    const int64_t qc = (int64_t)(eb[x] / (uint32_t)K) * w.cap;
+                    const uint32_t c_ix = (uint32_t)((int64_t)ex[x] - qc);
+                    w.cand[ex[x]] = ((uint64_t)__float_as_uint(z) << 32) | (uint64_t)(0xFFFFFFFFu - c_ix);
+                }
+            }
+        }
+    }
+}
+
+// Chunk pairs (max z, sum exp(z - max)) of every chunk of candidates, one
+// wavefront per chunk, from the key halves the token-major scoring wrote; the
+// keys kernel then combines them into each beam's log-sum-exp as after the
+// per-chunk scoring.
+__global__ __launch_bounds__(kWThreads) void k_tm_pairs(int K, WideDev w, int G, int Gb) {
+    __shared__ int32_t co_s[kMaxKRadix + 1], ho_s[kMaxKRadix + 1];
+    const int q = blockIdx.x / G, g = blockIdx.x % G, tid = threadIdx.x;
+    if (w.use_done && w.done[q]) return;
+    const int GE = hist_blocks_used(G, Gb, reinterpret_cast<const WideSel*>(w.sel)[q].n_cand);
+    if (g >= GE) return;  // uniform over the workgroup
+    const int lane = tid & (kWave - 1);
+    constexpr int NWV = kWThreads / kWave;
+    const int32_t* co = w.cand_off + (int64_t)q * (K + 1);
+    const int32_t* ho = w.chunk_off + (int64_t)q * (K + 1);
+    for (int k = tid; k <= K; k += kWThreads) {
+        co_s[k] = co[k];
+        ho_s[k] = ho[k];
+    }
+    __syncthreads();
+    const int nch = ho_s[K];
+    const uint64_t* cq = w.cand + (int64_t)q * w.cap;
+    for (int c = g * NWV + tid / kWave; c < nch; c += GE * NWV) {
+        const int k = slot_of_chunk(ho_s, K, c);
+        const int j0 = (c - ho_s[k]) * kWCH;
+        const int cnt = min(kWCH, co_s[k + 1] - co_s[k] - j0);
+        const float z = lane < cnt ? __uint_as_float((uint32_t)(cq[co_s[k] + j0 + lane] >> 32)) : -INFINITY;
+        const float m = wave_max(z);
+        const float sm = wave_sum(lane < cnt ? exp_sm(z - m) : 0.f);
+        if (lane == 0) {
+            float* p = w.cms + ((int64_t)q * w.chunk_cap + c) * 2;
+            p[0] = m;
+            p[1] = sm;
+        }
+    }
+}
+
 // Log-sum-exp of every live beam's whole score row, one workgroup of 256 per
 // beam.  Thread tid keeps a running (max, sum of exps) over the columns
 // tid + 256 i, taken eight columns at a time (summed over the k-slices, if
@@ -422,14 +645,6 @@ __global__ __launch_bounds__(256) void k_row_lse(StepDev st, int R, int V, int d
         S = wave_sum(M == -INFINITY ? 0.f : S * exp_sm(M - MM));
         if (tid == 0) lse_row[b] = MM + logf(S);
     }
-}
-
-// Workgroups of a histogram kernel that take part for a query of n keys: the
-// base count, more (up to the G launched) where each would hold more than
-// kHistKeys keys; the others leave at once.
-constexpr int kHistKeys = 16384;
-__device__ __forceinline__ int hist_blocks_used(int G, int Gb, int n) {
-    return min(G, max(Gb, (n + kHistKeys - 1) / kHistKeys));
 }
 
 // LDS histogram increment by the lanes in `on`, one atomic per distinct bin
@@ -901,6 +1116,71 @@ hipError_t launch_wide_score(const StepDev& st, bool dense, cb_dtype dt, int Q, 
     }
 #undef CB_WSCORE_CH
 #undef CB_WSCORE
+    return hipGetLastError();
+}
+
+hipError_t launch_tm_count(const StepDev& st, int Q, int K, const int32_t* beam_rows, const float* acc,
+                           const WideDev& w, const TokDev& tk, hipStream_t s) {
+    if (Q <= 0) return hipSuccess;
+    const int G = wide_blocks_per_query(Q);
+    CB_LAUNCH(k_tm_count, dim3(Q * G), dim3(kWThreads), 0, s, st, K, beam_rows, acc, w, tk, G);
+    return hipGetLastError();
+}
+
+hipError_t launch_tm_scan(int V, const TokDev& tk, hipStream_t s) {
+    if (V <= 4096) CB_LAUNCH(k_tm_scan<4>, dim3(1), dim3(1024), 0, s, V, tk);
+    else if (V <= 8192) CB_LAUNCH(k_tm_scan<8>, dim3(1), dim3(1024), 0, s, V, tk);
+    else if (V <= 16384) CB_LAUNCH(k_tm_scan<16>, dim3(1), dim3(1024), 0, s, V, tk);
+    else if (V <= 32768) CB_LAUNCH(k_tm_scan<32>, dim3(1), dim3(1024), 0, s, V, tk);
+    else CB_LAUNCH(k_tm_scan<64>, dim3(1), dim3(1024), 0, s, V, tk);
+    return hipGetLastError();
+}
+
+hipError_t launch_tm_scatter(int Q, int K, const WideDev& w, const TokDev& tk, hipStream_t s) {
+    if (Q <= 0) return hipSuccess;
+    const int G = wide_blocks_per_query(Q);
+    CB_LAUNCH(k_tm_scatter, dim3(Q * G), dim3(kWThreads), 0, s, K, w, tk, G);
+    return hipGetLastError();
+}
+
+int tm_score_blocks() { return 2048; }
+
+// Units of n entries over V tokens: each token's entries in runs of at most
+// kTmUnit, so at most n / kTmUnit + V.
+int64_t tm_unit_cap(int64_t n, int V) { return n / kTmUnit + V + 1; }
+
+__global__ __launch_bounds__(256) void k_tm_clear(int V, TokDev tk) {
+    const int v = blockIdx.x * 256 + (int)threadIdx.x;
+    if (v < V) tk.count[v] = 0;
+}
+
+hipError_t launch_tm_clear(int V, const TokDev& tk, hipStream_t s) {
+    CB_LAUNCH(k_tm_clear, dim3((V + 255) / 256), dim3(256), 0, s, V, tk);
+    return hipGetLastError();
+}
+
+hipError_t launch_tm_score(cb_dtype dt, int K, int d, const void* hidden, const void* W, const WideDev& w,
+                           const TokDev& tk, hipStream_t s) {
+    const dim3 grid(tm_score_blocks());
+#define CB_TMS(DT, CHV) \
+    CB_LAUNCH((k_tm_score<DT, CHV>), grid, dim3(kWThreads), 0, s, K, d, (const DT*)hidden, (const DT*)W, w, tk)
+#define CB_TMS_CH(DT)                          \
+    do {                                       \
+        if (d <= 512) CB_TMS(DT, 1);           \
+        else if (d <= 1024) CB_TMS(DT, 2);     \
+        else CB_TMS(DT, 4);                    \
+    } while (0)
+    if (d > 2048) return hipErrorInvalidValue;
+    if (dt == CB_BF16) CB_TMS_CH(uint16_t); else CB_TMS_CH(float);
+#undef CB_TMS_CH
+#undef CB_TMS
+    return hipGetLastError();
+}
+
+hipError_t launch_tm_pairs(int Q, int K, int64_t keys_bound, const WideDev& w, hipStream_t s) {
+    if (Q <= 0) return hipSuccess;
+    const int G = wide_hist_blocks(Q, keys_bound), Gb = wide_hist_blocks_per_query(Q);
+    CB_LAUNCH(k_tm_pairs, dim3(Q * G), dim3(kWThreads), 0, s, K, w, G, Gb);
     return hipGetLastError();
 }
 

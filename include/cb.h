@@ -237,15 +237,22 @@ cb_status cb_set_path(cb_plan* plan, int32_t t, cb_path path);
  *                         step (ZeroGR summary, "Why fewer scores are not
  *                         automatically faster": beams read uneven numbers
  *                         of weight rows; this spreads a heavy query's reads)
+ *   CB_OPT_TOKEN_MAJOR    sparse scoring on the radix selection: per beam (1,
+ *                         default; the beam's hidden vector staged, one W_t
+ *                         row gathered per candidate) or by token (2; the
+ *                         candidates grouped by token so that each W_t row is
+ *                         read once for every beam holding it; d <= 2048)
  * Errors: CB_EINVAL (unknown option or value), CB_ECAPACITY (the form does not
- * fit the LDS), CB_EUNSUPPORTED (every-slot product of an f32 plan). */
+ * fit the LDS, or the token-major workspace would pass 2^31 candidates),
+ * CB_EUNSUPPORTED (every-slot product of an f32 plan). */
 typedef enum {
     CB_OPT_STEP_THREADS = 0,
     CB_OPT_SPLIT_ROWS = 1,
     CB_OPT_SPARSE_FORM = 2,
     CB_OPT_DENSE_ROWS = 3,
     CB_OPT_RADIX_PREPASS = 4,
-    CB_OPT_QUERY_SPLIT = 5
+    CB_OPT_QUERY_SPLIT = 5,
+    CB_OPT_TOKEN_MAJOR = 6
 } cb_step_option;
 cb_status cb_set_step_option(cb_plan* plan, int32_t t, cb_step_option option, int32_t value);
 
@@ -409,8 +416,13 @@ typedef enum {
     CB_KERNEL_RADIX_SORT = 12,    /* radix selection: survivors sorted, outputs and next rows */
     CB_KERNEL_DECODE_TAIL = 13,   /* persistent decode of the trailing sparse steps (step = first one) */
     CB_KERNEL_RADIX_SMALL = 14,   /* radix selection: pre-pass finishing the queries whose rows hold one token */
-    CB_KERNEL_ROW_LSE = 15        /* variants on the radix selection: log-sum-exp of every whole score row
-                                     (score first: over the scores; unconstrained: over the chunk pairs) */
+    CB_KERNEL_ROW_LSE = 15,       /* radix selection: log-sum-exp of every beam in a pass of its own (score
+                                     first: over the whole score row; unconstrained, and filter first where the
+                                     step's rows hold more than 2,048 tokens on average: over the candidates'
+                                     chunk pairs) */
+    CB_KERNEL_TOKEN_LISTS = 16,   /* scores by token: candidates counted, offsets, lists (three launches) */
+    CB_KERNEL_TOKEN_SCORE = 17    /* scores by token: each W_t row dotted with the hidden vectors of its beams,
+                                     then the chunk softmax pairs (two launches) */
 } cb_kernel;
 
 typedef struct {

@@ -59,12 +59,14 @@ def workload(name, oracle_cls=oracle.Trie, **over):
 
 
 def step_all(plan, w, path, select, K=None):
-    """Teacher-forced steps on the oracle's beam state; returns the exemptions."""
+    """Teacher-forced steps on the oracle's beam state; returns the exemptions.
+    path "sparse_tm": the sparse path with its scores grouped by token."""
     cfg, T, ref = w["cfg"], w["T"], w["ref"]
     K = K or cfg.K
     ex_total = 0
     for t in range(cfg.L):
-        plan.set_path(t, path)
+        plan.set_path(t, "sparse" if path == "sparse_tm" else path)
+        plan.set_option(t, "token_major", 2 if path == "sparse_tm" else 1)
         plan.set_select(t, select)
         print("step", t, plan.get_path(t), plan.get_select(t), flush=True)
         h, rows, acc = ref["trace_h"][t], ref["trace_rows_in"][t], ref["trace_acc_in"][t]
@@ -80,7 +82,7 @@ def step_all(plan, w, path, select, K=None):
 
 
 @pytest.mark.parametrize("name", ["tiny", "small"])
-@pytest.mark.parametrize("path", ["sparse", "dense"])
+@pytest.mark.parametrize("path", ["sparse", "dense", "sparse_tm"])
 @pytest.mark.parametrize("store", ["auto", "bitmap"])
 def test_radix_step_parity_at_workload_width(name, path, store):
     w = workload(name)
@@ -93,7 +95,7 @@ def test_radix_step_parity_at_workload_width(name, path, store):
 
 
 @pytest.mark.parametrize("K", [100, 256, 1000])
-@pytest.mark.parametrize("path", ["sparse", "dense"])
+@pytest.mark.parametrize("path", ["sparse", "dense", "sparse_tm"])
 def test_wide_beam_step_parity(K, path):
     w = workload("small", K=K, Q=6)
     cfg = w["cfg"]
@@ -167,9 +169,10 @@ def test_massive_exact_ties_follow_the_tie_break():
     ref = T.decode(K, q, P, W, bf16=False, trace=True)
     idx = cb.Index(items, V, device=0)
     plan = idx.plan(Q, K, d, "f32")
-    for path in ("sparse", "dense"):
+    for path in ("sparse", "dense", "sparse_tm"):
         for t in range(2):
-            plan.set_path(t, path)
+            plan.set_path(t, "sparse" if path == "sparse_tm" else path)
+            plan.set_option(t, "token_major", 2 if path == "sparse_tm" else 1)
         out = plan.decode(torch.from_numpy(q).to(DEV), torch.from_numpy(P).to(DEV), torch.from_numpy(W).to(DEV))
         torch.cuda.synchronize()
         seqs = out["seqs"].cpu().numpy()
@@ -213,11 +216,12 @@ def test_large_generator_reduced_catalog(K):
     cfg = w["cfg"]
     idx = cb.Index(w["items"], cfg.V, device=0)
     plan = idx.plan(cfg.Q, K, cfg.d, cfg.dtype)
-    for path in ("sparse", "dense"):
+    for path in ("sparse", "dense", "sparse_tm"):
         print("teacher forced", path, flush=True)
         step_all(plan, w, path, "auto", K=K)
     for t in range(cfg.L):
         plan.set_path(t, "auto")
+        plan.set_option(t, "token_major", 0)
     q = torch.from_numpy(w["dense"]["q"]).to(DEV)
     P = torch.from_numpy(w["dense"]["P"]).to(DEV)
     plan.tune(q, P, w["W"], reps=2)
@@ -240,3 +244,40 @@ def test_radix_errors():
     assert e.value.status == -5
     plan.set_select(0, "radix")
     assert plan.get_select(0) == "radix"
+    assert plan.get_option(0, "token_major") == 1
+    plan.set_option(0, "token_major", 2)
+    assert plan.get_option(0, "token_major") == 2
+    with pytest.raises(cb.CbError) as e:
+        plan.set_option(0, "token_major", 3)
+    assert e.value.status == -1
+    wide = idx.plan(1, 100, 2056, cfg.dtype)  # W_t rows wider than the registers hold
+    with pytest.raises(cb.CbError) as e:
+        wide.set_option(0, "token_major", 2)
+    assert e.value.status == -1
+
+
+@pytest.mark.parametrize("prepass", [1, 2])
+def test_token_major_decode_with_and_without_prepass(prepass):
+    """Every step scored by token, with and without the one-token pre-pass,
+    repeated (the per-token counts are cleared between steps): the decode
+    equals the per-chunk scoring's up to near ties and holds to the oracle."""
+    w = workload("small", K=100, Q=6)
+    cfg = w["cfg"]
+    idx = cb.Index(w["items"], cfg.V, device=0)
+    plan = idx.plan(cfg.Q, cfg.K, cfg.d, cfg.dtype)
+    q = torch.from_numpy(w["dense"]["q"]).to(DEV)
+    P = torch.from_numpy(w["dense"]["P"]).to(DEV)
+    for t in range(cfg.L):
+        plan.set_path(t, "sparse")
+        plan.set_option(t, "radix_prepass", prepass)
+        plan.set_option(t, "token_major", 2)
+    first = None
+    for rep in range(2):
+        out = plan.decode(q, P, w["W"], trace=True)
+        torch.cuda.synchronize()
+        check_decode(w, out, cfg.K, plan)
+        if first is None:
+            first = {k: out[k].clone() for k in ("seqs", "logp", "rows")}
+        else:
+            for k in first:
+                assert torch.equal(first[k], out[k]), k

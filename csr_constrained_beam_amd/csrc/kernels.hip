@@ -872,16 +872,47 @@ template <int NT>
 __global__ __launch_bounds__(NT) void k_live_rows(StepDev st, int R, const int32_t* __restrict__ beam_rows,
                                                   const float* __restrict__ acc, int32_t* __restrict__ live,
                                                   int32_t* __restrict__ n_live, int32_t* __restrict__ ci_of) {
-    __shared__ int red_i[NT / kWave];
+    // rounds of U * NT slots: slot r0 + u * NT + tid for u < U (coalesced, all
+    // loads in flight at once); each wavefront's count per u by a ballot, then
+    // one scan over the (u, wavefront) counts in slot order
+    constexpr int U = 8, NW = NT / kWave;
+    static_assert(U * NW <= NT, "one thread per (u, wavefront) count");
+    __shared__ int wc[U * NW];
+    __shared__ int red_i[NW];
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    const uint64_t below = (1ull << lane) - 1ull;
     int base = 0;
-    for (int b0 = 0; b0 < R; b0 += NT) {
-        const int b = b0 + threadIdx.x;
-        const int on = b < R && beam_live(st, beam_rows[b], acc[b]);
+    for (int r0 = 0; r0 < R; r0 += U * NT) {
+        bool x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int b = r0 + u * NT + (int)threadIdx.x;
+            x[u] = b < R && beam_live(st, beam_rows[b], acc[b]);
+        }
+        uint64_t m[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            m[u] = __ballot(x[u]);
+            if (lane == 0) wc[u * NW + wv] = __popcll(m[u]);
+        }
+        __syncthreads();
+        const int c = (int)threadIdx.x < U * NW ? wc[threadIdx.x] : 0;
         int tot;
-        const int pos = base + block_exclusive_scan<NT>(on, red_i, &tot);
-        if (on) live[pos] = b;
-        if (b < R) ci_of[b] = on ? pos : -1;
+        const int o = block_exclusive_scan<NT>(c, red_i, &tot);
+        __syncthreads();  // every count read before it is overwritten
+        if ((int)threadIdx.x < U * NW) wc[threadIdx.x] = o;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int b = r0 + u * NT + (int)threadIdx.x;
+            if (b < R) {
+                const int pos = base + wc[u * NW + wv] + __popcll(m[u] & below);
+                if (x[u]) live[pos] = b;
+                ci_of[b] = x[u] ? pos : -1;
+            }
+        }
         base += tot;
+        __syncthreads();  // wc is rewritten by the next round
     }
     if (threadIdx.x == 0) *n_live = base;
 }

@@ -76,15 +76,19 @@ def test_large_decode_full_size(K):
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("path", ["sparse", "dense"])
+@pytest.mark.parametrize("path", ["sparse", "dense", "sparse_tm"])
 def test_large_teacher_forced_full_size(path):
+    """Every step at full size on the oracle's beam state; sparse_tm: the
+    sparse scores grouped by token."""
     w = large()
     cfg = w["cfg"]
     K = cfg.K
     ref = ref_for(w, K)
     plan = w["idx"].plan(cfg.Q, K, cfg.d, cfg.dtype)
     for t in range(cfg.L):
-        plan.set_path(t, path)
+        plan.set_path(t, "sparse" if path == "sparse_tm" else path)
+        if path == "sparse_tm":
+            plan.set_option(t, "token_major", 2)
         h, rows, acc = ref["trace_h"][t], ref["trace_rows_in"][t], ref["trace_acc_in"][t]
         o = w["T"].step(t, K, h, w["dense"]["W"][t], rows, acc, candidates=True, threads=16)
         got = plan.step(t, dev_h(h, cfg.dtype), w["W"][t], torch.from_numpy(rows.astype(np.int32)).to(DEV),

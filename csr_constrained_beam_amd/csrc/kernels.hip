@@ -851,6 +851,106 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
     if (lane < Kc) out[lane] = best;
 }
 
+// Dense path on a CSR step (filter first): one wavefront per beam, four
+// beams per workgroup.  The row's tokens and their score columns are gathered
+// a window of 64 * U at a time (U per lane, all loads in flight); a first
+// pass takes the log-sum-exp over the row (running max and sum of exps), a
+// second the beam's best min(Kc, n) keys, each window's merged with the best
+// so far (rows of one window keep their scores in registers between the
+// passes).  Keys re-keyed by their place in the beam's list, with side
+// information (next row << 16 | token), as k_beam_expand writes them.
+template <int U>
+__global__ __launch_bounds__(256) void k_expand_csr_wave(StepDev st, int R, int K, int Kc, int d, int64_t ldz,
+                                                         const float* __restrict__ Z, const float* __restrict__ Zp,
+                                                         const int32_t* __restrict__ n_live,
+                                                         const int32_t* __restrict__ ci_of, int split_ok,
+                                                         const int32_t* __restrict__ beam_rows,
+                                                         const float* __restrict__ acc,
+                                                         uint64_t* __restrict__ keys_out,
+                                                         uint64_t* __restrict__ side) {
+    __shared__ uint64_t wl_all[4][kWaveListCap + kWave];
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    const int b = blockIdx.x * 4 + wv;
+    if (b >= R) return;  // uniform over the wavefront
+    uint64_t* out = keys_out + (int64_t)b * Kc;
+    const int32_t r = beam_rows[b];
+    const float a = acc[b];
+    if (!beam_live(st, r, a)) {
+        if (lane < Kc) out[lane] = 0;
+        return;
+    }
+    const uint32_t e0 = st.row_ptr[r];
+    const int n = (int)(st.row_ptr[r + 1] - e0);  // >= 1: every row of a table has a child
+    const int split = split_ok ? gemm_split(*n_live, (int)ldz, d) : 1;
+    const float* zb = split == 1 ? Z + (int64_t)b * ldz : Zp + (int64_t)ci_of[b] * ldz;
+    constexpr int WIN = kWave * U;
+    // positions past the row re-read its last token (in bounds, no branch
+    // around the loads) and are masked
+    auto window = [&](int c0, float (&z)[U]) {
+        int tk[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) tk[u] = st.tok[e0 + min(c0 + u * kWave + lane, n - 1)];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float v = 0.f;
+            for (int x = 0; x < split; ++x) v += zb[(int64_t)x * kSplitRows * ldz + tk[u]];
+            z[u] = c0 + u * kWave + lane < n ? v : -INFINITY;
+        }
+    };
+    float z0[U];
+    float m = -INFINITY, sm = 0.f;
+    for (int c0 = 0; c0 < n; c0 += WIN) {
+        float z[U];
+        window(c0, z);
+        if (c0 == 0)
+#pragma unroll
+            for (int u = 0; u < U; ++u) z0[u] = z[u];
+        float wmx = z[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) wmx = fmaxf(wmx, z[u]);
+        const float mn = fmaxf(m, wave_max(wmx));  // finite: the window holds a token of the row
+        float ws = 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) ws += exp_sm(z[u] - mn);  // masked positions add exp(-inf) = 0
+        sm = sm * exp_sm(m - mn) + wave_sum(ws);
+        m = mn;
+    }
+    const float lse = m + logf(sm);
+    const int parent = b % K;
+    uint64_t best = 0;
+    for (int c0 = 0; c0 < n; c0 += WIN) {
+        float z[U];
+        if (c0 == 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) z[u] = z0[u];
+        } else {
+            window(c0, z);
+        }
+        uint32_t sc[U + 1];
+#pragma unroll
+        for (int u = 0; u < U; ++u) sc[u] = c0 + u * kWave + lane < n ? score_order_bits(a + (z[u] - lse)) : 0u;
+        sc[U] = (uint32_t)(best >> 32);
+        const uint64_t prev = best;
+        best = wave_top<U + 1>(
+            Kc, [&](int i) { return sc[i]; },
+            [&](int i) {
+                return i < U ? ((uint64_t)sc[i] << 32) | ((uint64_t)(1023 - parent) << 16) |
+                                   (uint64_t)(65535 - (c0 + i * kWave + lane))
+                             : prev;
+            },
+            wl_all[wv]);
+    }
+    if (lane < Kc) {
+        uint64_t key = best;
+        if (key) {
+            const int j = 65535 - (int)(key & 0xFFFFu);
+            side[(int64_t)b * Kc + lane] = ((uint64_t)(e0 + (uint32_t)j) << 16) | st.tok[e0 + j];
+            key = (key & ~0xFFFFull) | (uint64_t)(65535 - lane);
+        }
+        out[lane] = key;
+    }
+}
+
 // Dense path, per query: one wavefront per query, four queries per workgroup.
 template <int M>
 __global__ __launch_bounds__(256) void k_query_merge_w(StepDev st, int Q, int K, int Kc,
@@ -1548,6 +1648,12 @@ hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R,
         else CB_EXPAND_BM(64);
 #undef CB_EXPAND_BM
 #undef CB_EXPAND_BM_MODE
+        return hipGetLastError();
+    }
+    if (dense && st.store == CB_STORE_CSR && mode == CB_MODE_FILTER_FIRST) {
+        *sided = true;
+        CB_LAUNCH((k_expand_csr_wave<8>), dim3((R + 3) / 4), dim3(256), 0, s, st, R, K, Kc, d, ldz, Z, Zp, n_live,
+                  ci_of, split_ok, beam_rows, acc, keys, side);
         return hipGetLastError();
     }
     const ExpandLds lay = expand_lds(st.S, d, dense, kExpandThreads);

@@ -76,7 +76,15 @@ def test_step_split_scoring(dtype, d, K, split_rows):
     _run_widths(dtype, d, K, "sparse_split", "lds", split_rows=split_rows)
 
 
-def _run_widths(dtype, d, K, path, select, split_rows=0):
+@pytest.mark.parametrize("dtype,d", [("f32", 200), ("f32", 1024), ("bf16", 520), ("bf16", 1536), ("bf16", 2048)])
+def test_step_token_major_widths(dtype, d):
+    """The radix selection's sparse scores grouped by token at hidden widths
+    of one to four 512-element chunks, partial chunks included, on rows of
+    every scoring phase."""
+    _run_widths(dtype, d, 32, "sparse", "radix", token_major=True)
+
+
+def _run_widths(dtype, d, K, path, select, split_rows=0, token_major=False):
     items, V = catalog(11)
     L, Q = 3, 6
     rng = np.random.default_rng(5)
@@ -101,6 +109,8 @@ def _run_widths(dtype, d, K, path, select, split_rows=0):
             plan.set_option(t, "query_split", 4)
         if split_rows:
             plan.set_split_rows(t, split_rows)
+        if token_major:
+            plan.set_option(t, "token_major", 2)
     for t in range(L):
         print("case", dtype, d, "K", K, path, "step", t, flush=True)
         h = ref["trace_h"][t]

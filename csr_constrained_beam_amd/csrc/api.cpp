@@ -986,7 +986,7 @@ cb_status cb_set_step_option(cb_plan* p, int32_t t, cb_step_option o, int32_t va
             p->radix_pre[(size_t)t] = value;
             return CB_OK;
         case CB_OPT_QUERY_SPLIT:
-            if (value != 0 && value != 1 && value != 2 && value != 4) break;
+            if (value != 0 && value != 1 && value != 2 && value != 4 && value != 8) break;
             p->query_split[(size_t)t] = value;
             return CB_OK;
         case CB_OPT_TOKEN_MAJOR: {
@@ -1168,7 +1168,7 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
                                           expand_lds_bytes(T.S, p->d, false) <= (size_t)kMaxLds;
                     const int nts[4] = {0, 256, 0, 256};
                     const int mins[4] = {kPreMin, kPreMin, 1, 1};
-                    // and the plain sparse path with two and four workgroups per query
+                    // and the plain sparse path with two, four and eight workgroups per query
                     const bool qsplit_var = paths[k] == CB_PATH_SPARSE && per_query;
                     // and the radix selection's sparse scoring by token (with the pre-pass)
                     bool tm_var = pre_var && p->d <= kQueryMaxD;
@@ -1179,12 +1179,12 @@ static cb_status decode_impl(cb_plan* p, int32_t Q, const float* q, const float*
                     }
                     const int nv0 = split_var ? 4 : per_query || rows_var || pre_var ? 2 : 1;
                     const int nv1 = nv0 + (form_var ? 1 : 0);
-                    const int nv2 = nv1 + (qsplit_var ? 2 : 0);
+                    const int nv2 = nv1 + (qsplit_var ? 3 : 0);
                     const int nv = nv2 + (tm_var ? 1 : 0);
                     for (int v = 0; v < nv && st == CB_OK; ++v) {
                         const bool beam_form = form_var && v == nv0;
                         const bool by_token = tm_var && v == nv2;
-                        const int qs = v >= nv1 && v < nv2 ? (v == nv1 ? 2 : 4) : 0;
+                        const int qs = v >= nv1 && v < nv2 ? 2 << (v - nv1) : 0;
                         p->sparse_form[(size_t)t] = beam_form ? 1 : 0;
                         p->query_split[(size_t)t] = qs;
                         p->query_nt[(size_t)t] = per_query && !beam_form && v < nv0 ? nts[v] : 0;

@@ -232,7 +232,7 @@ cb_status cb_set_path(cb_plan* plan, int32_t t, cb_path path);
  *                         pre-pass that finishes queries whose live rows all
  *                         hold one token
  *   CB_OPT_QUERY_SPLIT    workgroups per query of the per-query sparse step:
- *                         1 (default), 2 or 4; each scores a share of the
+ *                         1 (default), 2, 4 or 8; each scores a share of the
  *                         query's rows and the last to finish completes the
  *                         step (ZeroGR summary, "Why fewer scores are not
  *                         automatically faster": beams read uneven numbers

@@ -57,7 +57,7 @@ def gpu_step(plan, t, h, Wt, rows, acc):
 
 @pytest.mark.parametrize("name", ["tiny", "small"])
 @pytest.mark.parametrize("path", ["sparse", "dense", "auto", "sparse_split", "sparse_split_all", "sparse_beam",
-                                  "sparse_qsplit"])
+                                  "sparse_qsplit", "sparse_qsplit8"])
 @pytest.mark.parametrize("store", ["auto", "csr", "bitmap"])
 def test_step_parity_teacher_forced(name, path, store):
     w = workload(name)
@@ -73,9 +73,9 @@ def test_step_parity_teacher_forced(name, path, store):
         elif path == "sparse_beam":  # one workgroup per beam, then the per-query merge
             plan.set_path(t, "sparse")
             force_beam_form(plan, t)
-        elif path == "sparse_qsplit":  # four workgroups per query, the last completes the step
+        elif path in ("sparse_qsplit", "sparse_qsplit8"):  # four or eight workgroups per query
             plan.set_path(t, "sparse")
-            plan.set_option(t, "query_split", 4)
+            plan.set_option(t, "query_split", 8 if path == "sparse_qsplit8" else 4)
         else:
             plan.set_path(t, path)
         h = ref["trace_h"][t]

@@ -134,3 +134,37 @@ def _run_widths(dtype, d, K, path, select, split_rows=0, token_major=False):
     torch.cuda.synchronize()
     for k in ("seqs", "logp", "rows"):
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dense_csr_expansion_rows_across_windows(dtype):
+    """The dense path on a CSR step expands each beam by one wavefront, 512
+    tokens per window: rows of 1 to 1,500 tokens (window boundaries at 512
+    and 1,024 on both sides) against the oracle, teacher forced."""
+    rng = np.random.default_rng(3)
+    V, d, Q, K, L = 2048, 64, 4, 16, 2
+    fan = [1, 2, 63, 64, 65, 511, 512, 513, 1024, 1025, 1500]
+    items = np.array([(a, int(b)) for a, f in enumerate(fan) for b in rng.choice(V, size=f, replace=False)], np.int32)
+    q = rng.standard_normal((Q, d)).astype(np.float32)
+    P = (rng.standard_normal((L - 1, V, d)) / np.sqrt(d)).astype(np.float32)
+    W = (rng.standard_normal((L, V, d)) / np.sqrt(d)).astype(np.float32)
+    Wd = torch.from_numpy(W).to(DEV)
+    if dtype == "bf16":
+        Wd = Wd.bfloat16()
+        W = Wd.float().cpu().numpy()
+    T = oracle.Trie(items, V)
+    ref = T.decode(K, q, P, W, bf16=dtype == "bf16", trace=True, threads=8)
+    idx = cb.Index(items, V, device=0, store="csr")
+    plan = idx.plan(Q, K, d, dtype)
+    for t in range(L):
+        plan.set_path(t, "dense")
+        h, rows, acc = ref["trace_h"][t], ref["trace_rows_in"][t], ref["trace_acc_in"][t]
+        o = T.step(t, K, h, W[t], rows, acc, candidates=True, threads=8)
+        hd = torch.from_numpy(np.ascontiguousarray(h, np.float32)).to(DEV)
+        if dtype == "bf16":
+            hd = hd.to(torch.bfloat16)
+        g = gpu_step(plan, t, hd, Wd[t], torch.from_numpy(rows.astype(np.int32)).to(DEV),
+                     torch.from_numpy(acc).to(DEV))
+        ex, gap, fails = compare_step(o, g, K, dtype)
+        assert not fails, "step %d:\n" % t + "\n".join(fails[:10])
+    assert sorted(len(T.children_of_row(1, r)[0]) for r in range(len(fan))) == sorted(fan)

@@ -475,18 +475,18 @@ cb_status run_step(cb_plan* p, int t, int Q, int32_t path, int32_t sel, const vo
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: full-codebook scores", e);
     }
-    bool sided = false;
+    bool sided = false, solo = false;
     {
         ProfMark m(p, s, t, CB_KERNEL_EXPAND_DENSE, expand_threads(sd), R);
         e = launch_beam_expand(sd, true, p->dtype, R, p->K, Kc, p->d, hidden, Wt, p->Z, p->Zp, idx->V, p->n_live,
-                               p->ci_of, rows, acc, p->keys, p->side, &sided, p->mode, s);
+                               p->ci_of, rows, acc, p->keys, p->side, &sided, p->mode, s, ot, op, orow, ol, &solo);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: beam expansion", e);
     }
     {
         ProfMark m(p, s, t, CB_KERNEL_MERGE, kMergeThreads, Q);
         e = launch_query_merge(sd, Q, p->K, Kc, p->keys, sided ? p->side : nullptr, rows, ot, op, orow, ol, p->mode,
-                               s);
+                               s, solo);
         m.done();
         if (e != hipSuccess) return hip_fail("cb_step: query merge", e);
     }

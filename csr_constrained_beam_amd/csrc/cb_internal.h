@@ -249,10 +249,11 @@ hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R,
                               const void* hidden, const void* W, const float* Z, const float* Zp, int64_t ldz,
                               const int32_t* n_live, const int32_t* ci_of, const int32_t* beam_rows,
                               const float* acc, uint64_t* keys, uint64_t* side, bool* sided, int mode,
-                              hipStream_t s);
+                              hipStream_t s, int32_t* tok = nullptr, int32_t* par = nullptr,
+                              int32_t* orows = nullptr, float* logp = nullptr, bool* solo_done = nullptr);
 hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uint64_t* keys, const uint64_t* side,
                               const int32_t* beam_rows, int32_t* tok, int32_t* par, int32_t* rows, float* logp,
-                              int mode, hipStream_t s);
+                              int mode, hipStream_t s, bool solo_done = false);
 hipError_t launch_decode_init(int Q, int K, int d, cb_dtype dt, const float* q, float* s_out, void* h_out,
                               int32_t* rows, float* acc, hipStream_t st);
 hipError_t launch_hidden_update(int R, int K, int d, cb_dtype dt, const float* s_old, const float* P_t,

@@ -712,7 +712,7 @@ __device__ __forceinline__ void merge_query_wave(const StepDev& st, int q, int K
                                                  const uint64_t* __restrict__ keys,
                                                  const uint64_t* __restrict__ side,
                                                  const int32_t* __restrict__ beam_rows, const MergeOut& mo, int mode,
-                                                 uint64_t* wl) {
+                                                 uint64_t* wl, int solo_done = 0) {
     const int lane = threadIdx.x & (kWave - 1);
     const int n = K * Kc;
     const uint64_t* src = keys + (int64_t)q * n;
@@ -724,6 +724,20 @@ __device__ __forceinline__ void merge_query_wave(const StepDev& st, int q, int K
         const int c = lane + kWave * i;
         const uint64_t v = src[min(c, n - 1)];
         kv[i] = c < n ? v : 0ull;
+    }
+    if (solo_done) {
+        // keys of one parent only: the query's one live beam wrote its outputs
+        float pmin = 2048.f, pmax = -1.f;
+#pragma unroll
+        for (int i = 0; i < M; ++i)
+            if (kv[i]) {
+                const float pf = (float)((kv[i] >> 16) & 1023u);
+                pmin = fminf(pmin, pf);
+                pmax = fmaxf(pmax, pf);
+            }
+        pmin = -wave_max(-pmin);
+        pmax = wave_max(pmax);
+        if (pmax >= 0.f && pmin == pmax) return;  // uniform over the wavefront
     }
     const uint64_t best = wave_top<M>(K, [&](int i) { return (uint32_t)(kv[i] >> 32); }, [&](int i) { return kv[i]; },
                                       wl);
@@ -772,7 +786,8 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
                                                        const int32_t* __restrict__ n_live,
                                                        const int32_t* __restrict__ ci_of,
                                                        const int32_t* __restrict__ beam_rows,
-                                                       const float* __restrict__ acc, uint64_t* __restrict__ keys_out) {
+                                                       const float* __restrict__ acc, uint64_t* __restrict__ keys_out,
+                                                       MergeOut mo) {
     static_assert(M % 4 == 0 && M <= 64, "columns are read 4 at a time, at most 64 per lane");
     constexpr int G = M / 4;
     __shared__ uint64_t wl_all[4][kWaveListCap + kWave];
@@ -785,6 +800,17 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
     if (!beam_live(st, r, a)) {
         if (lane < Kc) out[lane] = 0;
         return;
+    }
+    // the beam alone in its query (the root step of a decode): its best keys
+    // are the query's outputs, written here (the merge then skips the query)
+    const int qb = b / K, parent = b - qb * K;
+    bool solo = false;
+    uint32_t e0 = 0u;
+    if (MODE != CB_MODE_UNCONSTRAINED && mo.tok) {
+        const int32_t rk = lane < K ? beam_rows[(int64_t)qb * K + lane] : -1;
+        const float ak = lane < K ? acc[(int64_t)qb * K + lane] : -INFINITY;
+        solo = __ballot(lane < K && beam_live(st, rk, ak)) == (1ull << parent);
+        e0 = st.row_ptr[r];
     }
     auto col = [&](int i) { return (i >> 2) * (kWave * 4) + lane * 4 + (i & 3); };
     const uint32_t* rb = MODE == CB_MODE_UNCONSTRAINED ? nullptr : st.bits + (int64_t)r * st.words;
@@ -813,10 +839,11 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
     // holds words l and l + 64), then group g's four bits, which lie in word
     // 8g + l/8 at bit 4(l%8), fetched from the lane holding that word
     uint32_t vb[G];
+    uint32_t w0 = 0u, w1 = 0u;
+    const int words = (V + 31) >> 5;
     if constexpr (MODE != CB_MODE_UNCONSTRAINED) {
-        const int words = (V + 31) >> 5;
-        const uint32_t w0 = rb[min(lane, words - 1)];
-        const uint32_t w1 = G > 8 ? rb[min(lane + kWave, words - 1)] : 0u;
+        w0 = rb[min(lane, words - 1)];
+        w1 = G > 8 ? rb[min(lane + kWave, words - 1)] : 0u;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int src = (g * 8 + (lane >> 3)) & (kWave - 1);
@@ -840,7 +867,6 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
 #pragma unroll
     for (int i = 0; i < M; ++i) se += in_lse(i) ? exp_sm(z[i] - m) : 0.f;
     const float lse = m + logf(wave_sum(se));
-    const int parent = b % K;
     uint32_t sc[M];
 #pragma unroll
     for (int i = 0; i < M; ++i) sc[i] = valid(i) ? score_order_bits(a + (z[i] - lse)) : 0u;
@@ -849,6 +875,29 @@ __global__ __launch_bounds__(256) void k_expand_bitmap(StepDev st, int R, int K,
         [&](int i) { return ((uint64_t)sc[i] << 32) | ((uint64_t)(1023 - parent) << 16) | (uint64_t)(65535 - col(i)); },
         wl_all[wv]);
     if (lane < Kc) out[lane] = best;
+    if (solo) {  // uniform over the wavefront
+        // next row of the lane's survivor: the row's first edge plus the set
+        // bits of the row below its column (prefix counts of the words lane l
+        // holds, l and l + 64)
+        const int p0 = lane < words ? __popc(w0) : 0;
+        const int p1 = lane + kWave < words ? __popc(w1) : 0;
+        const int x0 = wave_inclusive_scan(p0) - p0;
+        const int x1 = wave_inclusive_scan(p1) - p1 + lane_bcast(x0 + p0, kWave - 1);
+        const int c = best ? 65535 - (int)(best & 0xFFFFu) : 0;
+        const int wd = c >> 5, src = wd & (kWave - 1);
+        const int pre0 = __shfl(x0, src), pre1 = __shfl(x1, src);
+        const uint32_t bw0 = (uint32_t)__shfl((int)w0, src), bw1 = (uint32_t)__shfl((int)w1, src);
+        const uint32_t bits = wd < kWave ? bw0 : bw1;
+        const int nxt = (int)(e0 + (uint32_t)(wd < kWave ? pre0 : pre1) + (uint32_t)__popc(bits & ((1u << (c & 31)) - 1u)));
+        if (lane < K) {
+            const int64_t o = (int64_t)qb * K + lane;
+            const bool on = lane < Kc && best != 0ull;
+            mo.tok[o] = on ? c : -1;
+            mo.par[o] = on ? parent : -1;
+            mo.rows[o] = on ? nxt : -1;
+            mo.logp[o] = on ? score_from_order_bits((uint32_t)(best >> 32)) : -INFINITY;
+        }
+    }
 }
 
 // Dense path on a CSR step (filter first): one wavefront per beam, four
@@ -956,12 +1005,13 @@ template <int M>
 __global__ __launch_bounds__(256) void k_query_merge_w(StepDev st, int Q, int K, int Kc,
                                                        const uint64_t* __restrict__ keys,
                                                        const uint64_t* __restrict__ side,
-                                                       const int32_t* __restrict__ beam_rows, MergeOut mo, int mode) {
+                                                       const int32_t* __restrict__ beam_rows, MergeOut mo, int mode,
+                                                       int solo_done) {
     __shared__ uint64_t wl_all[4][kWaveListCap + kWave];
     const int wv = threadIdx.x / kWave;
     const int q = blockIdx.x * 4 + wv;
     if (q >= Q) return;
-    merge_query_wave<M>(st, q, K, Kc, keys, side, beam_rows, mo, mode, wl_all[wv]);
+    merge_query_wave<M>(st, q, K, Kc, keys, side, beam_rows, mo, mode, wl_all[wv], solo_done);
 }
 
 // ---- full-codebook scores of the live beams (dense path) ------------------
@@ -1624,17 +1674,23 @@ hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R,
                               const void* hidden, const void* W, const float* Z, const float* Zp, int64_t ldz,
                               const int32_t* n_live, const int32_t* ci_of, const int32_t* beam_rows,
                               const float* acc, uint64_t* keys, uint64_t* side, bool* sided, int mode,
-                              hipStream_t s) {
+                              hipStream_t s, int32_t* tok, int32_t* par, int32_t* orows, float* logp,
+                              bool* solo_done) {
     *sided = false;
+    if (solo_done) *solo_done = false;
     if (R <= 0) return hipSuccess;
     const int split_ok = dt == CB_BF16 ? 1 : 0;
     if (dense && split_ok && (st.store == CB_STORE_BITMAP || mode == CB_MODE_UNCONSTRAINED) &&
         ldz <= 64 * kWave && ldz % 4 == 0) {
         const int M = (int)((ldz + kWave - 1) / kWave);
         const dim3 grid((R + 3) / 4);
+        // a query's one live beam writes the query's outputs itself
+        const bool direct = tok && mode != CB_MODE_UNCONSTRAINED;
+        const MergeOut mo{direct ? tok : nullptr, par, orows, logp};
+        if (solo_done) *solo_done = direct;
 #define CB_EXPAND_BM_MODE(MV, MD)                                                                            \
     CB_LAUNCH((k_expand_bitmap<MV, MD>), grid, dim3(256), 0, s, st, R, K, Kc, (int)ldz, d, Z, Zp, n_live, \
-                       ci_of, beam_rows, acc, keys)
+                       ci_of, beam_rows, acc, keys, mo)
 #define CB_EXPAND_BM(MV)                                                                          \
     do {                                                                                          \
         if (mode == CB_MODE_FILTER_FIRST) CB_EXPAND_BM_MODE(MV, CB_MODE_FILTER_FIRST);            \
@@ -1681,13 +1737,14 @@ hipError_t launch_beam_expand(const StepDev& st, bool dense, cb_dtype dt, int R,
 
 hipError_t launch_query_merge(const StepDev& st, int Q, int K, int Kc, const uint64_t* keys, const uint64_t* side,
                               const int32_t* beam_rows, int32_t* tok, int32_t* par, int32_t* rows, float* logp,
-                              int mode, hipStream_t s) {
+                              int mode, hipStream_t s, bool solo_done) {
     if (Q <= 0) return hipSuccess;
     const int M = (K * Kc + kWave - 1) / kWave;
     const dim3 grid((Q + 3) / 4);
     const MergeOut mo{tok, par, rows, logp};
-#define CB_MERGE(MV)                                                                                      \
-    CB_LAUNCH((k_query_merge_w<MV>), grid, dim3(256), 0, s, st, Q, K, Kc, keys, side, beam_rows, mo, mode)
+    const int sd = solo_done ? 1 : 0;
+#define CB_MERGE(MV)                                                                                          \
+    CB_LAUNCH((k_query_merge_w<MV>), grid, dim3(256), 0, s, st, Q, K, Kc, keys, side, beam_rows, mo, mode, sd)
     if (M <= 1) CB_MERGE(1);
     else if (M <= 4) CB_MERGE(4);
     else if (M <= 16) CB_MERGE(16);
